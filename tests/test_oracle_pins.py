@@ -1,0 +1,487 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+None of these tests call the oracle to produce its own expected values: each
+expected value comes from a library routine (torch's scaled_dot_product
+attention, torch's bf16 / e4m3fn casts), a closed form, an invariant, or a
+hand-derived golden fixture under tests/golden/.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+from attention_online_softmax_flash_amd import workloads as W
+from oracle import fia_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+RTOL = 1e-12
+
+
+def _t(x):
+    return torch.from_numpy(np.ascontiguousarray(x))
+
+
+def sdpa(q, k, v, scale, *, causal=False, mask=None, gqa=False):
+    """torch SDPA in float64; q [Lq, H, D], k/v [Lk, KV, D] -> [Lq, H, D]."""
+    qt = _t(q).permute(1, 0, 2)[None]
+    kt = _t(k).permute(1, 0, 2)[None]
+    vt = _t(v).permute(1, 0, 2)[None]
+    m = None if mask is None else _t(mask)
+    o = F.scaled_dot_product_attention(qt, kt, vt, attn_mask=m, is_causal=causal,
+                                       scale=scale, enable_gqa=gqa)
+    return o[0].permute(1, 0, 2).numpy()
+
+
+def run(q, k, v, **kw):
+    kw.setdefault("dtype", "fp64")
+    kw.setdefault("layout", "BSND")
+    return O.fia(q, k, v, **kw)
+
+
+def rnd(seed, *shape):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# Decoders
+# ---------------------------------------------------------------------------
+def test_bf16_decode_matches_torch():
+    bits = np.random.default_rng(0).integers(0, 1 << 16, size=20000, dtype=np.uint32).astype(np.uint16)
+    bits[:4] = [0x0000, 0x8000, 0x3F80, 0x7F80]
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    got = O.decode_bf16(bits)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def test_e4m3fn_anchors_golden():
+    g = json.load(open(os.path.join(GOLDEN, "e4m3fn_anchors.json")))
+    for code, val in g["anchors"].items():
+        got = float(O.decode_e4m3fn(np.array([int(code, 16)], np.uint8))[0])
+        want = float(val)
+        if math.isnan(want):
+            assert math.isnan(got), code
+        else:
+            assert got == want and math.copysign(1, got) == math.copysign(1, want), code
+
+
+def test_e4m3fn_full_table_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).double().numpy()
+    got = O.decode_e4m3fn(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert int(np.isnan(got).sum()) == 2          # 0x7F and 0xFF only
+
+
+# ---------------------------------------------------------------------------
+# Hand-derived tiny example
+# ---------------------------------------------------------------------------
+def test_tiny_attention_golden():
+    g = json.load(open(os.path.join(GOLDEN, "tiny_attention.json")))
+    q = np.array(g["q"])[None, :, None, :]
+    k = np.array(g["k"])[None, :, None, :]
+    v = np.array(g["v"])[None, :, None, :]
+    for c in g["cases"]:
+        slopes = None if c["slope"] is None else np.array([c["slope"]])
+        out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=1.0,
+                       sparse_mode=c["sparse_mode"], pre_tokens=c.get("pre", 2147483647),
+                       next_tokens=c.get("next", 2147483647), alibi_slopes=slopes)
+        np.testing.assert_allclose(out[0, :, 0, :], np.array(c["out"]), rtol=0, atol=1e-15, err_msg=c["name"])
+        np.testing.assert_allclose(lse[0, 0], np.array(c["lse"]), rtol=0, atol=1e-15, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------------------
+# Base formula, GQA and causal masks against torch SDPA
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("Lq,Lk,D", [(7, 7, 8), (5, 11, 16), (1, 9, 4)])
+def test_base_formula_matches_sdpa(Lq, Lk, D):
+    q, k, v = rnd(1, 1, Lq, 1, D), rnd(2, 1, Lk, 1, D), rnd(3, 1, Lk, 1, D)
+    scale = 0.37
+    out, _ = run(q, k, v, num_heads=1, num_kv_heads=1, scale=scale)
+    ref = sdpa(q[0], k[0], v[0], scale)
+    np.testing.assert_allclose(out[0], ref, rtol=RTOL, atol=1e-13)
+
+
+@pytest.mark.parametrize("Qn,KVn", [(4, 1), (8, 2), (6, 3), (4, 4)])
+def test_gqa_matches_sdpa_enable_gqa(Qn, KVn):
+    Lq, Lk, D = 6, 9, 8
+    q, k, v = rnd(4, 1, Lq, Qn, D), rnd(5, 1, Lk, KVn, D), rnd(6, 1, Lk, KVn, D)
+    out, _ = run(q, k, v, num_heads=Qn, num_kv_heads=KVn, scale=0.5)
+    ref = sdpa(q[0], k[0], v[0], 0.5, gqa=True)
+    np.testing.assert_allclose(out[0], ref, rtol=RTOL, atol=1e-13)
+
+
+@pytest.mark.parametrize("Lq,Lk", [(6, 6), (4, 9), (9, 4)])
+def test_mode2_left_up_causal_is_sdpa_causal(Lq, Lk):
+    q, k, v = rnd(7, 1, Lq, 2, 8), rnd(8, 1, Lk, 2, 8), rnd(9, 1, Lk, 2, 8)
+    out, _ = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.3, sparse_mode=2)
+    ref = sdpa(q[0], k[0], v[0], 0.3, causal=True)   # torch aligns top-left
+    np.testing.assert_allclose(out[0], ref, rtol=RTOL, atol=1e-13)
+
+
+def test_mode3_right_down_causal_is_suffix_of_square_causal():
+    Lq, Lk, D = 4, 10, 8
+    qfull, k, v = rnd(10, Lk, 2, D), rnd(11, Lk, 2, D), rnd(12, Lk, 2, D)
+    q = qfull[Lk - Lq:]
+    out, _ = run(q[None], k[None], v[None], num_heads=2, num_kv_heads=2, scale=0.4, sparse_mode=3)
+    ref = sdpa(qfull, k, v, 0.4, causal=True)[Lk - Lq:]
+    np.testing.assert_allclose(out[0], ref, rtol=RTOL, atol=1e-13)
+
+
+def test_mode3_more_queries_than_keys_first_rows_empty():
+    Lq, Lk, D = 9, 4, 8
+    q, k, v = rnd(13, 1, Lq, 1, D), rnd(14, 1, Lk, 1, D), rnd(15, 1, Lk, 1, D)
+    out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=3)
+    assert np.all(out[0, : Lq - Lk] == 0.0)
+    assert np.all(np.isposinf(lse[0, 0, : Lq - Lk]))
+    ref = sdpa(q[0, Lq - Lk:], k[0], v[0], 0.4, causal=True)
+    np.testing.assert_allclose(out[0, Lq - Lk:], ref, rtol=RTOL, atol=1e-13)
+
+
+def test_band_reductions():
+    Lq, Lk, D = 5, 8, 8
+    q, k, v = rnd(16, 1, Lq, 1, D), rnd(17, 1, Lk, 1, D), rnd(18, 1, Lk, 1, D)
+    big = 2147483647
+    m3, l3 = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=3)
+    b3, lb3 = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=4, pre_tokens=big, next_tokens=0)
+    np.testing.assert_array_equal(m3, b3)
+    np.testing.assert_array_equal(l3, lb3)
+    m0, _ = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=0)
+    ball, _ = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=4, pre_tokens=big, next_tokens=big)
+    np.testing.assert_array_equal(m0, ball)
+    # pre = next = 0: each row sees exactly key i + (Lk - Lq)
+    one, lone = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=4, pre_tokens=0, next_tokens=0)
+    d = Lk - Lq
+    np.testing.assert_array_equal(one[0, :, 0], v[0, d:d + Lq, 0])
+    for i in range(Lq):
+        assert abs(lone[0, 0, i] - 0.4 * float(q[0, i, 0] @ k[0, i + d, 0])) < 1e-13
+
+
+def test_band_general_matches_sdpa_with_enumerated_mask():
+    Lq, Lk, D, pre, nxt = 6, 10, 8, 2, 1
+    q, k, v = rnd(19, 1, Lq, 1, D), rnd(20, 1, Lk, 1, D), rnd(21, 1, Lk, 1, D)
+    out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.4, sparse_mode=4,
+                   pre_tokens=pre, next_tokens=nxt)
+    d = Lk - Lq
+    mask = np.zeros((Lq, Lk), dtype=bool)
+    for i in range(Lq):
+        for j in range(Lk):
+            mask[i, j] = (i + d - pre) <= j <= (i + d + nxt)
+    ref = sdpa(q[0], k[0], v[0], 0.4, mask=mask)
+    np.testing.assert_allclose(out[0], ref, rtol=RTOL, atol=1e-13)
+
+
+def test_band_window_outside_keys_is_empty():
+    q, k, v = rnd(22, 1, 3, 1, 4), rnd(23, 1, 5, 1, 4), rnd(24, 1, 5, 1, 4)
+    out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=1.0, sparse_mode=4,
+                   pre_tokens=-10, next_tokens=20)          # window [i+d+10, i+d+20]
+    assert np.all(out == 0) and np.all(np.isposinf(lse))
+
+
+# ---------------------------------------------------------------------------
+# Closed forms
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [0, 2, 3, 4])
+def test_uniform_v_rows_come_back_unchanged(mode):
+    Lq, Lk, D = 5, 7, 6
+    q, k = rnd(25, 1, Lq, 2, D), rnd(26, 1, Lk, 1, D)
+    u = rnd(27, D)
+    v = np.broadcast_to(u, (1, Lk, 1, D)).copy()
+    out, lse = run(q, k, v, num_heads=2, num_kv_heads=1, scale=0.7, sparse_mode=mode,
+                   pre_tokens=1, next_tokens=0, alibi_slopes=np.array([0.3, 0.9]))
+    for i in range(Lq):
+        for h in range(2):
+            if np.isfinite(lse[0, h, i]):
+                np.testing.assert_allclose(out[0, i, h], u, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("mode", [0, 2, 3])
+def test_zero_query_gives_mean_of_visible_v_and_log_count(mode):
+    Lq, Lk, D = 4, 6, 5
+    q = np.zeros((1, Lq, 1, D))
+    k, v = rnd(28, 1, Lk, 1, D), rnd(29, 1, Lk, 1, D)
+    out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=0.9, sparse_mode=mode)
+    d = Lk - Lq
+    for i in range(Lq):
+        n = {0: Lk, 2: min(Lk, i + 1), 3: min(Lk, i + d + 1)}[mode]
+        np.testing.assert_allclose(out[0, i, 0], v[0, :n, 0].mean(axis=0), rtol=1e-13, atol=1e-14)
+        assert abs(lse[0, 0, i] - math.log(n)) < 1e-13
+
+
+def test_uniform_keys_give_scaled_dot_plus_log_count():
+    Lq, Lk, D, scale = 5, 5, 4, 0.25
+    q = rnd(30, 1, Lq, 1, D)
+    kk = rnd(31, D)
+    k = np.broadcast_to(kk, (1, Lk, 1, D)).copy()
+    v = rnd(32, 1, Lk, 1, D)
+    out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=scale, sparse_mode=2)
+    for i in range(Lq):
+        want = scale * float(np.dot(q[0, i, 0], kk)) + math.log(i + 1)
+        assert abs(lse[0, 0, i] - want) < 1e-12
+        np.testing.assert_allclose(out[0, i, 0], v[0, : i + 1, 0].mean(axis=0), rtol=1e-12)
+
+
+def _geom(r, n):
+    """sum_{k<n} r^k and sum_{k<n} k r^k in closed form."""
+    s0 = (1 - r ** n) / (1 - r)
+    s1 = r * (1 - n * r ** (n - 1) + (n - 1) * r ** n) / (1 - r) ** 2
+    return s0, s1
+
+
+@pytest.mark.parametrize("slope", [0.0625, 0.5, 2.0])
+def test_alibi_zero_query_geometric_closed_form(slope):
+    n, D = 9, 3
+    q = np.zeros((1, n, 1, D))
+    k = rnd(33, 1, n, 1, D)
+    v = np.zeros((1, n, 1, D))
+    v[0, :, 0, 0] = np.arange(n)          # value = key position
+    v[0, :, 0, 1] = 1.0
+    out, lse = run(q, k, v, num_heads=1, num_kv_heads=1, scale=1.0, sparse_mode=2,
+                   alibi_slopes=np.array([slope]))
+    r = math.exp(-slope)
+    for i in range(n):
+        s0, s1 = _geom(r, i + 1)            # weights r^(i-j), k = i - j
+        assert abs(lse[0, 0, i] - math.log(s0)) < 1e-12
+        assert abs(out[0, i, 0, 0] - (i * s0 - s1) / s0) < 1e-12
+        assert abs(out[0, i, 0, 1] - 1.0) < 1e-13
+
+
+def test_alibi_start_offsets_shift_lse_only():
+    Lq = Lk = 6
+    q, k, v = rnd(34, 1, Lq, 2, 4), rnd(35, 1, Lk, 2, 4), rnd(36, 1, Lk, 2, 4)
+    slopes = np.array([0.25, 0.75])
+    base_o, base_l = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.5, sparse_mode=3, alibi_slopes=slopes)
+    same_o, same_l = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.5, sparse_mode=3,
+                         alibi_slopes=slopes, q_start_idx=11, kv_start_idx=11)
+    np.testing.assert_allclose(same_o, base_o, rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(same_l, base_l, rtol=1e-13, atol=1e-13)
+    dlt = 5
+    sh_o, sh_l = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.5, sparse_mode=3,
+                     alibi_slopes=slopes, q_start_idx=0, kv_start_idx=dlt)
+    np.testing.assert_allclose(sh_o, base_o, rtol=1e-12, atol=1e-13)
+    for h in range(2):
+        np.testing.assert_allclose(sh_l[0, h], base_l[0, h] + slopes[h] * dlt, rtol=0, atol=1e-12)
+    zero_o, _ = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.5, sparse_mode=3, alibi_slopes=np.zeros(2))
+    plain_o, _ = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.5, sparse_mode=3)
+    np.testing.assert_array_equal(zero_o, plain_o)
+
+
+def test_alibi_matches_sdpa_with_additive_bias():
+    L, H, D = 7, 2, 4
+    q, k, v = rnd(37, 1, L, H, D), rnd(38, 1, L, H, D), rnd(39, 1, L, H, D)
+    slopes = np.array([0.5, 0.125])
+    out, _ = run(q, k, v, num_heads=H, num_kv_heads=H, scale=0.6, sparse_mode=2, alibi_slopes=slopes)
+    i = np.arange(L)[:, None]
+    j = np.arange(L)[None, :]
+    bias = np.where(j <= i, slopes[:, None, None] * (j - i)[None], -np.inf)[None]
+    ref = sdpa(q[0], k[0], v[0], 0.6, mask=bias)
+    np.testing.assert_allclose(out[0], ref, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Branch rule, lengths, layouts, paging, empty inputs
+# ---------------------------------------------------------------------------
+def test_decode_equals_last_row_of_causal_prefill():
+    B, L, Qn, KVn, D = 3, 12, 8, 2, 8
+    q, k, v = rnd(40, B, L, Qn, D), rnd(41, B, L, KVn, D), rnd(42, B, L, KVn, D)
+    pre_o, pre_l = run(q, k, v, num_heads=Qn, num_kv_heads=KVn, scale=0.3, sparse_mode=3)
+    dec_o, dec_l = run(q[:, -1:], k, v, num_heads=Qn, num_kv_heads=KVn, scale=0.3, sparse_mode=3)
+    np.testing.assert_allclose(dec_o[:, 0], pre_o[:, -1], rtol=1e-13, atol=1e-14)
+    np.testing.assert_allclose(dec_l[:, :, 0], pre_l[:, :, -1], rtol=1e-13, atol=1e-14)
+
+
+def test_actual_lengths_broadcast_and_padding():
+    B, S, D = 3, 6, 4
+    q, k, v = rnd(43, B, S, 1, D), rnd(44, B, S, 1, D), rnd(45, B, S, 1, D)
+    o1, l1 = run(q, k, v, num_heads=1, num_kv_heads=1, scale=1.0, actual_seq_lengths=[4],
+                 actual_seq_lengths_kv=[5])
+    o2, l2 = run(q, k, v, num_heads=1, num_kv_heads=1, scale=1.0, actual_seq_lengths=[4, 4, 4, 1],
+                 actual_seq_lengths_kv=[5, 5, 5, 2])
+    np.testing.assert_array_equal(o1, o2)
+    assert np.all(o1[:, 4:] == 0) and np.all(np.isposinf(l1[:, :, 4:]))
+    for b in range(B):
+        ref = sdpa(q[b, :4], k[b, :5], v[b, :5], 1.0)
+        np.testing.assert_allclose(o1[b, :4], ref, rtol=RTOL, atol=1e-13)
+    with pytest.raises(ValueError):
+        run(q, k, v, num_heads=1, num_kv_heads=1, scale=1.0, actual_seq_lengths=[4, 4])
+
+
+def test_empty_kv_gives_zero_and_inf():
+    q, k, v = rnd(46, 2, 3, 2, 4), rnd(47, 2, 5, 1, 4), rnd(48, 2, 5, 1, 4)
+    out, lse = run(q, k, v, num_heads=2, num_kv_heads=1, scale=1.0, actual_seq_lengths_kv=[0, 0])
+    assert np.all(out == 0) and np.all(np.isposinf(lse))
+    out, lse = run(q, k[:, :0], v[:, :0], num_heads=2, num_kv_heads=1, scale=1.0)
+    assert np.all(out == 0) and np.all(np.isposinf(lse))
+
+
+def test_tnd_equals_bsnd_per_batch():
+    c = W.tnd_case("t", 49, q_lens=[3, 0, 5], kv_lens=[4, 2, 5], Q_N=4, KV_N=2, D=8,
+                   dtype="fp32", sparse_mode=3)
+    out, lse = O.fia_case(c)
+    qo = [0] + c.actual_seq_lengths
+    ko = [0] + c.actual_seq_lengths_kv
+    for b in range(3):
+        qb = c.q[qo[b]:qo[b + 1]][None]
+        kb = c.k[ko[b]:ko[b + 1]][None]
+        vb = c.v[ko[b]:ko[b + 1]][None]
+        if qb.shape[1] == 0:
+            continue
+        ob, lb = O.fia(qb, kb, vb, dtype="fp32", layout="BSND", num_heads=4, num_kv_heads=2,
+                       scale=c.scale, sparse_mode=3)
+        np.testing.assert_array_equal(out[qo[b]:qo[b + 1]], ob[0])
+        np.testing.assert_array_equal(lse[qo[b]:qo[b + 1]], lb[0].T)
+
+
+def test_paged_equals_contiguous():
+    c = W.paged_decode_case("p", 50, B=3, Q_N=4, KV_N=2, D=8, kv_lens=[5, 33, 16],
+                            block_size=16, dtype="bf16", keep_contiguous=True,
+                            poison_tail=True, extra_blocks=2, S1=2, sparse_mode=3)
+    out_p, lse_p = O.fia_case(c)
+    out_c, lse_c = O.fia(c.q, c.k, c.v, dtype="bf16", layout="BSND", num_heads=4, num_kv_heads=2,
+                         scale=c.scale, sparse_mode=3, actual_seq_lengths_kv=c.actual_seq_lengths_kv)
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+    assert np.all(np.isfinite(out_p))
+
+
+def test_split_keys_merge_by_lse_reproduces_full():
+    """Partial results over disjoint key ranges combine through their LSE
+    (V2 softmaxLse restrictions: the ring-attention composition)."""
+    Lq, Lk, D = 4, 12, 6
+    q, k, v = rnd(51, 1, Lq, 2, D), rnd(52, 1, Lk, 2, D), rnd(53, 1, Lk, 2, D)
+    full_o, full_l = run(q, k, v, num_heads=2, num_kv_heads=2, scale=0.5)
+    parts = [(0, 5), (5, 6), (6, 12)]
+    outs, lses = [], []
+    for a, b in parts:
+        o, l = run(q, k[:, a:b], v[:, a:b], num_heads=2, num_kv_heads=2, scale=0.5)
+        outs.append(o)
+        lses.append(l)
+    L = np.logaddexp.reduce(np.stack(lses), axis=0)           # [1, H, Lq]
+    merged = sum(np.exp(l - L).transpose(0, 2, 1)[..., None] * o for o, l in zip(outs, lses))
+    np.testing.assert_allclose(merged, full_o, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L, full_l, rtol=1e-13, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Shared-KV sparse decode
+# ---------------------------------------------------------------------------
+def test_sparse_rows_golden():
+    g = json.load(open(os.path.join(GOLDEN, "sparse_rows.json")))
+    for c in g["cases"]:
+        win, comp = O.sparse_rows(c["Lk"], 1, 0, c["idx"], cmp_ratio=c["ratio"],
+                                  win_left=c["win_left"], win_right=c["win_right"])
+        want_win = c.get("window")
+        if want_win is None:
+            a, b = c["window_range"]
+            want_win = list(range(a, b + 1))
+        assert win == want_win, c
+        assert comp == c["comp"], c
+
+
+def test_packed_row_decode_hand_values():
+    """A row assembled from known codes: rope bf16 1.0 / -2.0, nope e4m3fn
+    codes 0x38 (1.0), 0x7E (448), 0x01 (2^-9), 0xB8 (-1.0), scales 2^-3 .. 2^3."""
+    row = np.zeros(640, np.uint8)
+    rope = np.zeros(64, np.uint16)
+    rope[0], rope[63] = 0x3F80, 0xC000
+    row[0:128] = rope.view(np.uint8)
+    codes = np.zeros(448, np.uint8)
+    codes[0], codes[64], codes[200], codes[447] = 0x38, 0x7E, 0x01, 0xB8
+    row[128:576] = codes
+    scales = np.array([2.0 ** e for e in range(-3, 4)], np.float32)
+    row[576:604] = scales.view(np.uint8)
+    x = O.decode_packed_row(row)
+    want = np.zeros(512)
+    want[0], want[63] = 1.0, -2.0
+    want[64 + 0] = 1.0 * 2.0 ** -3
+    want[64 + 64] = 448.0 * 2.0 ** -2
+    want[64 + 200] = 2.0 ** -9 * 2.0 ** 0          # tile 3
+    want[64 + 447] = -1.0 * 2.0 ** 3               # tile 6
+    np.testing.assert_array_equal(x, want)
+
+
+def _small_sparse(seed=60, B=2, N1=4, lens=(300, 77), K2=16):
+    return W.sparse_case("s", seed, B=B, N1=N1, seqused_kv=list(lens), K2=K2,
+                         block_size1=32, block_size2=16, materialise_all_ori=False)
+
+
+def test_sparse_matches_sdpa_with_sink_key():
+    c = _small_sparse()
+    out = O.sparse_sharedkv(c)
+    for b, L in enumerate(c.seqused_kv):
+        # gather the logical rows independently: window, then selected rows
+        p = L - 1
+        rows = []
+        for j in range(max(0, p - 127), p + 1):
+            rows.append(c.ori_kv[c.ori_block_table[b, j // 32], j % 32, 0])
+        for cc in c.cmp_sparse_indices[b, 0, 0]:
+            if 0 <= cc < L // 4:
+                rows.append(c.cmp_kv[c.cmp_block_table[b, cc // 16], cc % 16, 0])
+        X = np.stack([O.decode_packed_row(r) for r in rows])
+        Xs = np.concatenate([X, np.zeros((1, 512))])         # the sink key/value
+        q = O.decode_bf16(c.q[b, 0])                         # [N1, 512]
+        mask = np.zeros((c.q.shape[2], 1, X.shape[0] + 1))
+        mask[:, 0, -1] = c.sinks.astype(np.float64)          # sink logit
+        ref = sdpa(q[None], np.repeat(Xs[:, None], 1, 1), np.repeat(Xs[:, None], 1, 1),
+                   c.softmax_scale, mask=mask, gqa=True)
+        np.testing.assert_allclose(out[b, 0], ref[0], rtol=1e-11, atol=1e-13)
+
+
+def test_sparse_zero_query_closed_form_and_sink_limit():
+    c = _small_sparse(seed=61)
+    c.q[...] = 0
+    out = O.sparse_sharedkv(c)
+    for b, L in enumerate(c.seqused_kv):
+        win, comp = O.sparse_rows(L, 1, 0, c.cmp_sparse_indices[b, 0, 0], cmp_ratio=4,
+                                  win_left=127, win_right=0)
+        X = [O.decode_packed_row(c.ori_kv[c.ori_block_table[b, j // 32], j % 32, 0]) for j in win]
+        X += [O.decode_packed_row(c.cmp_kv[c.cmp_block_table[b, x // 16], x % 16, 0]) for x in comp]
+        X = np.stack(X)
+        n = X.shape[0]
+        for h in range(c.q.shape[2]):
+            want = X.sum(axis=0) / (n + math.exp(float(c.sinks[h])))
+            np.testing.assert_allclose(out[b, 0, h], want, rtol=1e-12, atol=1e-14)
+    c.sinks[...] = -np.inf
+    out = O.sparse_sharedkv(c)
+    for b, L in enumerate(c.seqused_kv):
+        win, comp = O.sparse_rows(L, 1, 0, c.cmp_sparse_indices[b, 0, 0], cmp_ratio=4,
+                                  win_left=127, win_right=0)
+        X = [O.decode_packed_row(c.ori_kv[c.ori_block_table[b, j // 32], j % 32, 0]) for j in win]
+        X += [O.decode_packed_row(c.cmp_kv[c.cmp_block_table[b, x // 16], x % 16, 0]) for x in comp]
+        np.testing.assert_allclose(out[b, 0, 0], np.mean(X, axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_sparse_poisoned_rows_are_never_read():
+    c = _small_sparse(seed=62, lens=(1000, 129))
+    out = O.sparse_sharedkv(c)
+    assert np.all(np.isfinite(out))
+
+
+# ---------------------------------------------------------------------------
+# Generators: determinism and shapes
+# ---------------------------------------------------------------------------
+def test_generators_are_deterministic():
+    a = W.paged_decode_case("a", 5, B=2, Q_N=4, KV_N=2, D=8, kv_lens=[7, 20], block_size=16)
+    b = W.paged_decode_case("a", 5, B=2, Q_N=4, KV_N=2, D=8, kv_lens=[7, 20], block_size=16)
+    for x, y in [(a.q, b.q), (a.k_pool, b.k_pool), (a.block_table, b.block_table)]:
+        assert x.tobytes() == y.tobytes()
+    assert sorted(a.block_table[a.block_table >= 0].tolist()) == list(range(3))
+
+
+def test_workload_shapes():
+    c = W.c1_tiny_dense()
+    assert c.q.shape == (1, 64, 2, 64) and c.q.dtype == np.float32 and c.scale == 0.125
+    lens = W.c2_lengths()
+    assert len(lens) == 4 and all(512 <= x <= 2048 for x in lens)
+    lens = W.c3_lengths()
+    assert len(lens) == 64 and all(1024 <= x <= 8192 for x in lens)
+    s = W.alibi_slopes(16)
+    assert s[0] == np.float32(2 ** -0.5) and s[15] == np.float32(2 ** -8)
