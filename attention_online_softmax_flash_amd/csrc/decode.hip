@@ -1,0 +1,302 @@
+// Incremental-decode branch (query length 1): split-KV attention over a
+// dense, TND or paged KV cache, and the second-pass LSE merge.
+//
+// Work item = (batch b, KV head, block of up to 16 query heads of that KV
+// head's group, chunk of `chunk` keys).  Chunk boundaries sit at multiples of
+// `chunk` in absolute key position, so how a row is split depends only on that
+// row's own visible range: the result of one batch entry never depends on the
+// rest of the batch.  Four waves split the chunk in four equal key ranges,
+// combine through LDS in a fixed order and either write the final row (the
+// row has one chunk) or a partial (normalised output + log2-sum-exp) that the
+// merge kernel folds in chunk order (aclnnFusedInferAttentionScoreV2,
+// softmaxLse restrictions: partials compose through their max / sum / LSE).
+//
+// Per 32-key wave step, the 16x16x32 bf16 MFMA computes S^T[key][head] with
+// keys on the M axis (lane n reads 16-byte pieces of key row n) and heads on
+// the N axis, so lane (n, g) owns query head n: the running max / sum of the
+// online softmax stay in that lane.  The value product is O^T = V^T P^T; each
+// lane loads 16 bytes of 8 value rows and re-packs them in registers into the
+// MFMA operand (d = 8n + e for product e), so no LDS transpose is needed.
+#include "fia_device.h"
+
+namespace fia {
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
+  constexpr int NC = D / 32;   // 32-wide d chunks of the score product
+  constexpr int DPL = D / 16;  // value columns per lane column (8 for D = 128)
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  int item = blockIdx.x;
+  const int hb = item % a.n_head_blocks;
+  item /= a.n_head_blocks;
+  const int kvh = item % a.KVn;
+  const int cg = item / a.KVn;
+  const int b = a.work[2 * cg];
+  const int c = a.work[2 * cg + 1];
+  const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
+  const int lo = bm[BF_LO], hi = bm[BF_HI];
+  const int nchunk = bm[BF_NCHUNK], chunk0 = bm[BF_CHUNK0];
+  const int kv_off = bm[BF_KVOFF], q_off = bm[BF_QOFF];
+
+  const int C = a.chunk;
+  const int wlen = C >> 2;
+  const int cbase = (lo / C + c) * C;
+  const int ws = cbase + wave * wlen;
+  const int t_lo = max(ws, lo);
+  const int t_hi = min(ws + wlen, hi);
+
+  const int hl = hb * 16 + n;
+  const bool hvalid = hl < a.G;
+  const int h = kvh * a.G + (hvalid ? hl : 0);
+
+  const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)q_off * a.q_ss +
+                       (int64_t)h * a.q_sh;
+  u32x4 qv[NC];
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    qv[cc] = hvalid ? ld16(qp + 32 * cc + 8 * g) : u32x4{0, 0, 0, 0};
+  }
+  const float c_alibi = (a.slopes != nullptr && hvalid) ? a.slopes[h] * kLog2e : 0.f;
+
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  f32x4 o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint16_t* kbase = (const uint16_t*)a.k;
+  const uint16_t* vbase = (const uint16_t*)a.v;
+
+  if (t_hi > t_lo) {
+    const int first = ws + ((t_lo - ws) & ~31);
+    for (int ts = first; ts < t_hi; ts += kDecodeStep) {
+      // Row offsets of the two 16-key halves; within a half the keys share a
+      // page (block sizes are multiples of 16 and halves are 16-aligned).
+      int64_t krow[2], vrow[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int jb = min(ts + 16 * hf, t_hi - 1);
+        krow[hf] = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
+        vrow[hf] = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
+        // Offsets below are relative to key ts + 16 hf.
+        krow[hf] -= (int64_t)(jb - ts - 16 * hf) * a.k_ss;
+        vrow[hf] -= (int64_t)(jb - ts - 16 * hf) * a.v_ss;
+      }
+      // Key operand: key row (16 hf + n), d = 32 cc + 8 g .. +7.
+      u32x4 kr[2][NC];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int j = ts + 16 * hf + n;
+        const bool ok = j >= t_lo && j < t_hi;
+        const uint16_t* p = kbase + krow[hf] + (int64_t)n * a.k_ss + 8 * g;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) kr[hf][cc] = ok ? ld16(p + 32 * cc) : u32x4{0, 0, 0, 0};
+      }
+      // Value rows for k-slot s: key 16 (s/4) + 4 g + s%4, columns DPL n ..
+      u32x4 vr[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int hf = s >> 2;
+        const int t = 4 * g + (s & 3);
+        const int j = ts + 16 * hf + t;
+        const bool ok = j >= t_lo && j < t_hi;
+        const uint16_t* p = vbase + vrow[hf] + (int64_t)t * a.v_ss + DPL * n;
+        if constexpr (DPL == 8) {
+          vr[s] = ok ? ld16(p) : u32x4{0, 0, 0, 0};
+        } else {
+          u32x2 w = ok ? ld8(p) : u32x2{0, 0};
+          vr[s] = u32x4{w.x, w.y, 0, 0};
+        }
+      }
+      // Scores S^T[key 16 hf + 4 g + r][head n].
+      f32x4 sc[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) sc[hf] = mfma16(kr[hf][cc], qv[cc], sc[hf]);
+      }
+      float x[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int j = ts + 16 * (s >> 2) + 4 * g + (s & 3);
+        const bool ok = j >= t_lo && j < t_hi;
+        float v = sc[s >> 2][s & 3] * a.scale_log2;
+        v += c_alibi * (float)(j + a.alibi_delta);
+        x[s] = ok ? v : kNegInf;
+        mx = fmaxf(mx, x[s]);
+      }
+      mx = fmaxf(mx, shfl_xor_f(mx, 16));
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float p[8];
+      float psum = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        p[s] = fast_exp2(x[s] - m_use);
+        psum += p[s];
+      }
+      l_run = l_run * alpha + psum;
+      m_run = m_new;
+      u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                  pack_bf16x2(p[6], p[7])};
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        o[e] *= alpha;
+        const int w = e >> 1;
+        u32x4 av;
+        if (e & 1) {
+          av = u32x4{pick_hi(vr[0][w], vr[1][w]), pick_hi(vr[2][w], vr[3][w]),
+                     pick_hi(vr[4][w], vr[5][w]), pick_hi(vr[6][w], vr[7][w])};
+        } else {
+          av = u32x4{pick_lo(vr[0][w], vr[1][w]), pick_lo(vr[2][w], vr[3][w]),
+                     pick_lo(vr[4][w], vr[5][w]), pick_lo(vr[6][w], vr[7][w])};
+        }
+        o[e] = mfma16(av, pb, o[e]);
+      }
+    }
+  }
+  l_run += shfl_xor_f(l_run, 16);
+  l_run += shfl_xor_f(l_run, 32);
+
+  // Combine the four waves through LDS in wave order.
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_o[4][16][D + 4];
+  if (g == 0) {
+    sm_m[wave][n] = m_run;
+    sm_l[wave][n] = l_run;
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][n][DPL * (4 * g + r) + e] = o[e][r];
+  }
+  __syncthreads();
+
+  constexpr int PER = 16 * D / 256;  // outputs per thread
+  const int hh = threadIdx.x / (D / PER);
+  const int d0 = (threadIdx.x % (D / PER)) * PER;
+  if (hb * 16 + hh >= a.G) return;
+  const int hout = kvh * a.G + hb * 16 + hh;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
+  float wgt[4];
+  float L = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wgt[w] = (sm_m[w][hh] == kNegInf) ? 0.f : fast_exp2(sm_m[w][hh] - M);
+    L += sm_l[w][hh] * wgt[w];
+  }
+  float acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += sm_o[w][hh][d0 + u] * wgt[w];
+    acc[u] = s;
+  }
+  const float inv = 1.f / L;
+  const float lse2 = M + fast_log2(L);
+  if (nchunk == 1) {
+    uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
+                   (int64_t)hout * a.o_sh + d0;
+#pragma unroll
+    for (int u = 0; u < PER; u += 2) {
+      *reinterpret_cast<uint32_t*>(op + u) = pack_bf16x2(acc[u] * inv, acc[u + 1] * inv);
+    }
+    if (a.write_lse && d0 == 0) {
+      a.lse[(int64_t)b * a.lse_sb + (int64_t)hout * a.lse_sh + (int64_t)q_off * a.lse_ss] =
+          lse2 * kLn2;
+    }
+  } else {
+    const int64_t pi = (int64_t)(chunk0 + c) * a.Qn + hout;
+    float* pp = a.part_o + pi * D + d0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) pp[u] = acc[u] * inv;
+    if (d0 == 0) a.part_lse[pi] = lse2;
+  }
+}
+
+// One wave per output row (b, h): fold the row's partials in chunk order, or
+// write the empty-row result (0, LSE +inf) when the row has no visible key.
+template <int D>
+__global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
+  constexpr int PL = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.B * a.Qn) return;
+  const int b = row / a.Qn;
+  const int h = row - b * a.Qn;
+  const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
+  const int nchunk = bm[BF_NCHUNK];
+  if (nchunk == 1) return;
+  const int q_off = bm[BF_QOFF];
+  uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
+                 (int64_t)h * a.o_sh + lane * PL;
+  float* lp = a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)q_off * a.lse_ss;
+  if (nchunk == 0) {
+#pragma unroll
+    for (int u = 0; u < PL; ++u) op[u] = 0;
+    if (a.write_lse && lane == 0) *lp = kPosInf;
+    return;
+  }
+  const int chunk0 = bm[BF_CHUNK0];
+  float M = kNegInf;
+  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, a.part_lse[(int64_t)(chunk0 + c) * a.Qn + h]);
+  float L = 0.f;
+  float acc[PL];
+#pragma unroll
+  for (int u = 0; u < PL; ++u) acc[u] = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const int64_t pi = (int64_t)(chunk0 + c) * a.Qn + h;
+    const float w = fast_exp2(a.part_lse[pi] - M);
+    L += w;
+    const float* pp = a.part_o + pi * D + lane * PL;
+#pragma unroll
+    for (int u = 0; u < PL; ++u) acc[u] += w * pp[u];
+  }
+  const float inv = 1.f / L;
+  if constexpr (PL == 2) {
+    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
+  } else {
+#pragma unroll
+    for (int u = 0; u < PL; ++u) {
+      op[u] = (uint16_t)(pack_bf16x2(acc[u] * inv, 0.f) & 0xffffu);
+    }
+  }
+  if (a.write_lse && lane == 0) *lp = (M + fast_log2(L)) * kLn2;
+}
+
+hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s) {
+  if (n_items > 0) {
+    if (a.D == 128) {
+      decode_split_bf16<128><<<n_items, 256, 0, s>>>(a);
+    } else {
+      decode_split_bf16<64><<<n_items, 256, 0, s>>>(a);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_merge(const AttnArgs& a, hipStream_t s) {
+  const int rows = a.B * a.Qn;
+  if (rows > 0) {
+    if (a.D == 128) {
+      decode_merge<128><<<(rows + 3) / 4, 256, 0, s>>>(a);
+    } else {
+      decode_merge<64><<<(rows + 3) / 4, 256, 0, s>>>(a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fia

@@ -1,0 +1,912 @@
+// Host side of libfia: argument validation (the constraint tiers of the
+// fused-inference-attention pages), branch dispatch, work planning, workspace
+// layout and the C entry points declared in include/fia.h.
+//
+// Phase 1 (fia_get_workspace_size / fia_sparse_get_workspace_size) is pure
+// host code: it never calls into HIP, so it runs without a GPU.
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+#include <string>
+#include <vector>
+
+#include "fia.h"
+#include "fia_internal.h"
+
+using fia::AttnArgs;
+using fia::SparseArgs;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fia_status fail(fia_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+enum Kind { KIND_FILL = 0, KIND_PREFILL = 1, KIND_DECODE = 2, KIND_SPARSE = 3, KIND_FP32 = 4 };
+
+constexpr int kDecodeChunk = 512;     // keys per split-KV chunk (multiple of 128)
+constexpr int64_t kMaxLen = 20971520; // S <= 20M (V2 restrictions when Q_S > 1)
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int dtype_size(int dt) {
+  switch (dt) {
+    case FIA_DT_BF16:
+    case FIA_DT_FP16: return 2;
+    case FIA_DT_FP32:
+    case FIA_DT_INT32: return 4;
+    case FIA_DT_INT64: return 8;
+    case FIA_DT_FP8_E4M3FN:
+    case FIA_DT_UINT8:
+    case FIA_DT_INT8:
+    case FIA_DT_BOOL: return 1;
+    default: return 0;
+  }
+}
+
+const char* dtype_name(int dt) {
+  static const char* names[] = {"bf16", "fp16", "fp32", "fp8_e4m3fn", "int32",
+                                "int64", "uint8", "int8", "bool"};
+  return (dt >= 0 && dt <= 8) ? names[dt] : "unknown";
+}
+
+int64_t numel(const fia_tensor* t) {
+  int64_t n = 1;
+  for (int d = 0; d < t->ndim; ++d) n *= t->shape[d];
+  return n;
+}
+
+std::string shape_str(const fia_tensor* t) {
+  std::string s = "[";
+  for (int d = 0; d < t->ndim; ++d) {
+    if (d) s += ",";
+    s += std::to_string(t->shape[d]);
+  }
+  return s + "]";
+}
+
+fia_status check_tensor(const fia_tensor* t, const char* name, bool allow_empty_null = true) {
+  if (t->ndim < 1 || t->ndim > 5) {
+    return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": ndim must be 1..5");
+  }
+  if (dtype_size(t->dtype) == 0) {
+    return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": unknown dtype");
+  }
+  for (int d = 0; d < t->ndim; ++d) {
+    if (t->shape[d] < 0) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": negative dim");
+  }
+  if (numel(t) > 0) {
+    if (t->data == nullptr) return fail(FIA_ERR_NULLPTR, std::string(name) + ": data is NULL");
+    if (t->stride[t->ndim - 1] != 1 && t->shape[t->ndim - 1] > 1) {
+      return fail(FIA_ERR_UNSUPPORTED, std::string(name) + ": innermost dim must be contiguous");
+    }
+  } else if (!allow_empty_null && t->data == nullptr) {
+    return fail(FIA_ERR_NULLPTR, std::string(name) + ": data is NULL");
+  }
+  return FIA_SUCCESS;
+}
+
+// Canonical (batch, seq, head, dim) view of a query-like tensor.
+struct Canon {
+  int64_t B = 0, S = 0, N = 0, D = 0;
+  int64_t sb = 0, ss = 0, sh = 0;
+};
+
+fia_status canon(const fia_tensor* t, const std::string& layout, int64_t heads, const char* name,
+                 Canon* c) {
+  if (layout == "BSND") {
+    if (t->ndim != 4) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": BSND needs 4 dims");
+    *c = {t->shape[0], t->shape[1], t->shape[2], t->shape[3], t->stride[0], t->stride[1], t->stride[2]};
+  } else if (layout == "BNSD") {
+    if (t->ndim != 4) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": BNSD needs 4 dims");
+    *c = {t->shape[0], t->shape[2], t->shape[1], t->shape[3], t->stride[0], t->stride[2], t->stride[1]};
+  } else if (layout == "BSH") {
+    if (t->ndim != 3) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": BSH needs 3 dims");
+    if (heads <= 0 || t->shape[2] % heads != 0) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": H must be a multiple of N");
+    }
+    const int64_t D = t->shape[2] / heads;
+    *c = {t->shape[0], t->shape[1], heads, D, t->stride[0], t->stride[1], D};
+  } else if (layout == "TND") {
+    if (t->ndim != 3) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": TND needs 3 dims");
+    *c = {1, t->shape[0], t->shape[1], t->shape[2], 0, t->stride[0], t->stride[1]};
+  } else {
+    return fail(FIA_ERR_PARAM_INVALID, "input_layout must be BSND, BSH, BNSD or TND");
+  }
+  return FIA_SUCCESS;
+}
+
+fia::FastDiv make_fastdiv(uint32_t d) {
+  fia::FastDiv f{};
+  f.d = d;
+  uint32_t s = 0;
+  while ((1ull << s) < d) ++s;
+  const unsigned __int128 num = (unsigned __int128)1 << (32 + s);
+  f.mul = (uint64_t)((num + d - 1) / d);
+  f.shift = s;
+  return f;
+}
+
+}  // namespace
+
+struct fia_executor {
+  int kind = KIND_FILL;
+  AttnArgs a{};
+  SparseArgs sp{};
+  std::vector<int32_t> meta;  // uploaded to the start of the workspace
+  size_t meta_bytes = 0;
+  size_t work_off = 0;        // offset (ints) of the work list inside meta
+  size_t part_o_off = 0, part_lse_off = 0;
+  size_t ws_size = 0;
+  int32_t n_items = 0;        // decode workgroups
+  int32_t s2max = 0;
+  bool noop = false;
+  void* pinned = nullptr;
+};
+
+namespace {
+
+fia_status upload_meta(fia_executor* e, void* ws, hipStream_t stream) {
+  if (e->meta_bytes == 0) return FIA_SUCCESS;
+  if (e->pinned == nullptr) {
+    if (hipHostMalloc(&e->pinned, e->meta_bytes, hipHostMallocDefault) != hipSuccess) {
+      e->pinned = nullptr;
+      return fail(FIA_ERR_HIP, "hipHostMalloc of the plan staging buffer failed");
+    }
+    std::memcpy(e->pinned, e->meta.data(), e->meta_bytes);
+  }
+  if (hipMemcpyAsync(ws, e->pinned, e->meta_bytes, hipMemcpyHostToDevice, stream) != hipSuccess) {
+    return fail(FIA_ERR_HIP, "hipMemcpyAsync of the plan failed");
+  }
+  return FIA_SUCCESS;
+}
+
+void bind_workspace(fia_executor* e, void* ws) {
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  e->a.meta = reinterpret_cast<const int32_t*>(base);
+  e->a.work = reinterpret_cast<const int32_t*>(base) + e->work_off;
+  e->a.part_o = reinterpret_cast<float*>(base + e->part_o_off);
+  e->a.part_lse = reinterpret_cast<float*>(base + e->part_lse_off);
+  e->sp.part_o = reinterpret_cast<float*>(base + e->part_o_off);
+  e->sp.part_lse = reinterpret_cast<float*>(base + e->part_lse_off);
+}
+
+fia_status check_ws(const fia_executor* e, void* ws, size_t ws_size) {
+  if (ws_size < e->ws_size) {
+    return fail(FIA_ERR_WORKSPACE, "workspace of " + std::to_string(ws_size) +
+                                       " bytes is smaller than the required " +
+                                       std::to_string(e->ws_size));
+  }
+  if (e->ws_size > 0 && ws == nullptr) return fail(FIA_ERR_WORKSPACE, "workspace is NULL");
+  if (e->ws_size > 0 && (reinterpret_cast<uintptr_t>(ws) % 16) != 0) {
+    return fail(FIA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+  }
+  return FIA_SUCCESS;
+}
+
+// Per-batch lengths from a host array (V2 actualSeqLengths rule).
+fia_status lengths_from(const int64_t* arr, int64_t len, int64_t B, int64_t def, bool tnd,
+                        int64_t total, const char* name, std::vector<int64_t>* out) {
+  out->assign(B, def);
+  if (arr == nullptr) {
+    if (tnd) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " is required for TND");
+    return FIA_SUCCESS;
+  }
+  if (tnd) {
+    if (len != B) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": TND needs exactly B entries");
+    int64_t prev = 0;
+    for (int64_t b = 0; b < B; ++b) {
+      if (arr[b] < prev) {
+        return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": TND entries must be non-decreasing");
+      }
+      (*out)[b] = arr[b] - prev;
+      prev = arr[b];
+    }
+    if (B > 0 && prev != total) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": last TND entry must equal T");
+    }
+    return FIA_SUCCESS;
+  }
+  if (len != 1 && len < B) {
+    return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": length must be 1 or >= B");
+  }
+  for (int64_t b = 0; b < B; ++b) {
+    const int64_t v = (len == 1) ? arr[0] : arr[b];
+    if (v < 0) return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": negative length");
+    if (v > def) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": length " + std::to_string(v) +
+                                             " exceeds the tensor's S " + std::to_string(def));
+    }
+    (*out)[b] = v;
+  }
+  return FIA_SUCCESS;
+}
+
+void visible(int mode, int64_t i, int64_t Lq, int64_t Lk, int64_t pre, int64_t next, int64_t* lo,
+             int64_t* hi) {
+  const int64_t d = Lk - Lq;
+  int64_t l = 0, h = Lk;
+  if (mode == 2) {
+    h = i + 1;
+  } else if (mode == 3) {
+    h = i + d + 1;
+  } else if (mode == 4) {
+    l = i + d - pre;
+    h = i + d + next + 1;
+  }
+  l = std::max<int64_t>(0, std::min(l, Lk));
+  h = std::min(h, Lk);
+  if (h < l) h = l;
+  *lo = l;
+  *hi = h;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fia_last_error(void) { return g_last_error.c_str(); }
+
+int32_t fia_executor_kind(const fia_executor* e) { return e ? e->kind : -1; }
+
+void fia_executor_destroy(fia_executor* e) {
+  if (e == nullptr) return;
+  if (e->pinned) (void)hipHostFree(e->pinned);
+  delete e;
+}
+
+fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
+                                  const fia_tensor* key, const fia_tensor* value,
+                                  const fia_tensor* pse_shift, const fia_tensor* atten_mask,
+                                  const fia_tensor* block_table, const fia_tensor* attention_out,
+                                  const fia_tensor* softmax_lse, size_t* workspace_size,
+                                  fia_executor** executor) {
+  if (!p || !query || !key || !value || !attention_out || !workspace_size || !executor) {
+    return fail(FIA_ERR_NULLPTR, "params, query, key, value, attention_out, workspace_size and "
+                                 "executor must not be NULL");
+  }
+  *executor = nullptr;
+  *workspace_size = 0;
+  fia_status st;
+  if ((st = check_tensor(query, "query")) != FIA_SUCCESS) return st;
+  if ((st = check_tensor(key, "key")) != FIA_SUCCESS) return st;
+  if ((st = check_tensor(value, "value")) != FIA_SUCCESS) return st;
+  if ((st = check_tensor(attention_out, "attention_out")) != FIA_SUCCESS) return st;
+  const std::string layout = p->input_layout ? p->input_layout : "BSND";
+  const bool tnd = layout == "TND";
+  const bool paged = block_table != nullptr;
+  const int64_t Qn = p->num_heads;
+  const int64_t KVn = p->num_key_value_heads == 0 ? Qn : p->num_key_value_heads;
+  if (Qn < 1 || Qn > 256) return fail(FIA_ERR_PARAM_INVALID, "num_heads must be in [1, 256]");
+  if (KVn < 1 || Qn % KVn != 0) {
+    return fail(FIA_ERR_PARAM_INVALID, "num_heads must be a multiple of num_key_value_heads");
+  }
+  if (Qn / KVn > 64) return fail(FIA_ERR_PARAM_INVALID, "num_heads / num_key_value_heads must be <= 64");
+
+  Canon cq, co;
+  if ((st = canon(query, layout, Qn, "query", &cq)) != FIA_SUCCESS) return st;
+  if ((st = canon(attention_out, layout, Qn, "attention_out", &co)) != FIA_SUCCESS) return st;
+  if (cq.N != Qn) return fail(FIA_ERR_PARAM_INVALID, "query N axis must equal num_heads");
+  if (co.B != cq.B || co.S != cq.S || co.N != cq.N || co.D != cq.D) {
+    return fail(FIA_ERR_PARAM_INVALID, "attention_out shape must match query " + shape_str(query));
+  }
+  if (query->dtype != FIA_DT_BF16 && query->dtype != FIA_DT_FP32) {
+    return fail(FIA_ERR_UNSUPPORTED, std::string("query dtype ") + dtype_name(query->dtype) +
+                                         " is not supported (bf16, fp32)");
+  }
+  if (key->dtype != query->dtype || value->dtype != query->dtype) {
+    return fail(FIA_ERR_PARAM_INVALID, "key and value must have the query dtype");
+  }
+  if (attention_out->dtype != query->dtype) {
+    return fail(FIA_ERR_PARAM_INVALID, "attention_out must have the query dtype");
+  }
+  const int64_t D = cq.D;
+  const bool f32 = query->dtype == FIA_DT_FP32;
+
+  // Query batch size and lengths.
+  std::vector<int64_t> qlen, kvlen;
+  int64_t B;
+  std::vector<int64_t> q_cum;
+  if (tnd) {
+    if (!p->actual_seq_lengths) return fail(FIA_ERR_PARAM_INVALID, "TND requires actual_seq_lengths");
+    B = p->actual_seq_lengths_len;
+  } else {
+    B = cq.B;
+  }
+  if (B > 65536) return fail(FIA_ERR_PARAM_INVALID, "B must be <= 65536");
+  if (D > 512) return fail(FIA_ERR_PARAM_INVALID, "D must be <= 512");
+  if (cq.S > kMaxLen) return fail(FIA_ERR_PARAM_INVALID, "S must be <= 20971520");
+
+  // Empty-tensor rule (V4 public constraints): query / output empty -> nothing
+  // to do, and validation is skipped.
+  if (numel(query) == 0 || numel(attention_out) == 0) {
+    fia_executor* e = new fia_executor();
+    e->noop = true;
+    *executor = e;
+    return FIA_SUCCESS;
+  }
+
+  if ((st = lengths_from(p->actual_seq_lengths, p->actual_seq_lengths_len, B, cq.S, tnd, cq.S,
+                         "actual_seq_lengths", &qlen)) != FIA_SUCCESS) {
+    return st;
+  }
+  int64_t max_q = 0;
+  for (auto v : qlen) max_q = std::max(max_q, v);
+
+  // Key / value views.
+  Canon ck{}, cv{};
+  int64_t n_blocks = 0, bs = p->block_size, bt_cols = 0;
+  if (paged) {
+    if ((st = check_tensor(block_table, "block_table")) != FIA_SUCCESS) return st;
+    if (block_table->dtype != FIA_DT_INT32) return fail(FIA_ERR_PARAM_INVALID, "block_table must be int32");
+    if (block_table->ndim != 2 || block_table->shape[0] == 0 || block_table->shape[1] == 0) {
+      return fail(FIA_ERR_PARAM_INVALID, "block_table must be 2-D with non-zero dims");
+    }
+    if (block_table->shape[0] != B) return fail(FIA_ERR_PARAM_INVALID, "block_table dim 0 must equal B");
+    bt_cols = block_table->shape[1];
+    if (bs <= 0) return fail(FIA_ERR_PARAM_INVALID, "block_size must be > 0");
+    const bool d_64_128 = (D == 64 || D == 128);
+    if (bs % 16 != 0 || bs > 1024) {
+      return fail(FIA_ERR_PARAM_INVALID, "block_size must be a multiple of 16 and <= 1024");
+    }
+    if (!d_64_128 && max_q == 1 && bs > 512) {
+      return fail(FIA_ERR_PARAM_INVALID, "block_size must be <= 512 when Q_S == 1");
+    }
+    if (!p->actual_seq_lengths_kv) {
+      return fail(FIA_ERR_PARAM_INVALID, "paged attention requires actual_seq_lengths_kv");
+    }
+    for (const fia_tensor* t : {key, value}) {
+      const bool four = t->ndim == 4 && t->shape[1] == bs && t->shape[2] == KVn && t->shape[3] == D;
+      const bool three = t->ndim == 3 && t->shape[1] == bs && t->shape[2] == KVn * D;
+      if (!four && !three) {
+        return fail(FIA_ERR_PARAM_INVALID, "paged key/value must be [n_blocks, block_size, KV_N, D] "
+                                           "or [n_blocks, block_size, KV_N*D], got " + shape_str(t));
+      }
+    }
+    if (key->shape[0] != value->shape[0]) {
+      return fail(FIA_ERR_PARAM_INVALID, "paged key and value must have the same shape");
+    }
+    n_blocks = key->shape[0];
+    auto pool_view = [&](const fia_tensor* t, Canon* c) {
+      c->B = n_blocks;
+      c->S = bs;
+      c->N = KVn;
+      c->D = D;
+      c->sb = t->stride[0];
+      c->ss = t->stride[1];
+      c->sh = t->ndim == 4 ? t->stride[2] : D;
+    };
+    pool_view(key, &ck);
+    pool_view(value, &cv);
+    std::vector<int64_t> kl;
+    if ((st = lengths_from(p->actual_seq_lengths_kv, p->actual_seq_lengths_kv_len, B,
+                           bt_cols * bs, false, 0, "actual_seq_lengths_kv", &kl)) != FIA_SUCCESS) {
+      return st;
+    }
+    kvlen = kl;
+    int64_t max_kv = 0;
+    for (auto v : kvlen) max_kv = std::max(max_kv, v);
+    if (bt_cols < (max_kv + bs - 1) / bs) {
+      return fail(FIA_ERR_PARAM_INVALID, "block_table dim 1 is smaller than the largest "
+                                         "actual_seq_lengths_kv needs");
+    }
+    if (n_blocks == 0 && max_kv > 0) return fail(FIA_ERR_PARAM_INVALID, "paged key/value pool is empty");
+  } else {
+    if ((st = canon(key, layout, KVn, "key", &ck)) != FIA_SUCCESS) return st;
+    if ((st = canon(value, layout, KVn, "value", &cv)) != FIA_SUCCESS) return st;
+    if (ck.N != KVn || cv.N != KVn) {
+      return fail(FIA_ERR_PARAM_INVALID, "key/value N axis must equal num_key_value_heads");
+    }
+    if (ck.D != D || cv.D != D) {
+      return fail(FIA_ERR_UNSUPPORTED, "query, key and value head dims must be equal");
+    }
+    if (ck.S != cv.S || ck.B != cv.B) return fail(FIA_ERR_PARAM_INVALID, "key and value shapes differ");
+    if (!tnd && ck.B != B) return fail(FIA_ERR_PARAM_INVALID, "key batch must equal query batch");
+    if ((st = lengths_from(p->actual_seq_lengths_kv, p->actual_seq_lengths_kv_len, B, ck.S, tnd,
+                           ck.S, "actual_seq_lengths_kv", &kvlen)) != FIA_SUCCESS) {
+      return st;
+    }
+  }
+  if (ck.S > kMaxLen) return fail(FIA_ERR_PARAM_INVALID, "KV S must be <= 20971520");
+
+  // Mask group.
+  const int mode = p->sparse_mode;
+  if (mode < 0 || mode > 4) return fail(FIA_ERR_PARAM_INVALID, "sparse_mode must be in [0, 4]");
+  if (mode == 1) return fail(FIA_ERR_UNSUPPORTED, "sparse_mode 1 needs an explicit mask tensor");
+  if (atten_mask != nullptr) {
+    if (mode == 0) return fail(FIA_ERR_UNSUPPORTED, "an explicit atten_mask tensor is not supported");
+    const int dt = atten_mask->dtype;
+    if (dt != FIA_DT_BOOL && dt != FIA_DT_INT8 && dt != FIA_DT_UINT8) {
+      return fail(FIA_ERR_PARAM_INVALID, "atten_mask dtype must be bool, int8 or uint8");
+    }
+    const int nd = atten_mask->ndim;
+    bool ok = nd >= 2 && nd <= 4 && atten_mask->shape[nd - 1] == 2048 && atten_mask->shape[nd - 2] == 2048;
+    for (int d = 0; ok && d < nd - 2; ++d) ok = atten_mask->shape[d] == 1;
+    if (!ok) {
+      return fail(FIA_ERR_PARAM_INVALID, "sparse_mode 2/3/4 needs atten_mask of shape (2048,2048), "
+                                         "(1,2048,2048) or (1,1,2048,2048)");
+    }
+  }
+  if (mode == 4 && -p->next_tokens > p->pre_tokens) {
+    return fail(FIA_ERR_PARAM_INVALID, "pre_tokens and next_tokens must satisfy -next_tokens <= pre_tokens");
+  }
+
+  // PSE group.
+  const int pse = p->pse_type;
+  if (pse != 0 && pse != 1 && pse != 2 && pse != 3) {
+    return fail(FIA_ERR_PARAM_INVALID, "pse_type must be 0, 2 or 3");
+  }
+  if (pse == 1) return fail(FIA_ERR_PARAM_INVALID, "pse_type 1 is for training only");
+  if (pse == 3) return fail(FIA_ERR_UNSUPPORTED, "pse_type 3 is not supported");
+  if (pse == 0 && pse_shift != nullptr) {
+    return fail(FIA_ERR_UNSUPPORTED, "an explicit pse_shift bias tensor is not supported");
+  }
+  if (pse == 2) {
+    if (pse_shift == nullptr) return fail(FIA_ERR_PARAM_INVALID, "pse_type 2 requires pse_shift");
+    if ((st = check_tensor(pse_shift, "pse_shift")) != FIA_SUCCESS) return st;
+    if (pse_shift->dtype != FIA_DT_FP32) return fail(FIA_ERR_PARAM_INVALID, "ALiBi pse_shift must be fp32");
+    if (pse_shift->ndim != 1 || pse_shift->shape[0] != Qn) {
+      return fail(FIA_ERR_PARAM_INVALID, "ALiBi pse_shift shape must be (Q_N)");
+    }
+    const int64_t dlt = p->kv_start_idx - p->q_start_idx;
+    if (dlt < -1048576 || dlt > 1048576) {
+      return fail(FIA_ERR_PARAM_INVALID, "kv_start_idx - q_start_idx must be in [-1048576, 1048576]");
+    }
+    const int64_t S2 = paged ? bt_cols * bs : ck.S;
+    if (!paged && !tnd && cq.S != S2) return fail(FIA_ERR_PARAM_INVALID, "ALiBi requires Q_S == KV_S");
+    for (int64_t b = 0; b < B; ++b) {
+      if (qlen[b] != kvlen[b]) {
+        return fail(FIA_ERR_PARAM_INVALID, "ALiBi requires equal actual query and key lengths");
+      }
+    }
+  }
+
+  // SoftmaxLSE group.
+  if (p->softmax_lse_flag) {
+    if (softmax_lse == nullptr) return fail(FIA_ERR_PARAM_INVALID, "softmax_lse_flag needs softmax_lse");
+    if ((st = check_tensor(softmax_lse, "softmax_lse")) != FIA_SUCCESS) return st;
+    if (softmax_lse->dtype != FIA_DT_FP32) return fail(FIA_ERR_PARAM_INVALID, "softmax_lse must be fp32");
+    if (tnd) {
+      if (softmax_lse->ndim != 3 || softmax_lse->shape[0] != cq.S || softmax_lse->shape[1] != Qn ||
+          softmax_lse->shape[2] != 1) {
+        return fail(FIA_ERR_PARAM_INVALID, "softmax_lse must be [T, Q_N, 1] for TND");
+      }
+    } else if (softmax_lse->ndim != 4 || softmax_lse->shape[0] != B || softmax_lse->shape[1] != Qn ||
+               softmax_lse->shape[2] != cq.S || softmax_lse->shape[3] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "softmax_lse must be [B, Q_N, Q_S, 1]");
+    }
+  }
+  if (p->inner_precise < 0 || p->inner_precise > 3) {
+    return fail(FIA_ERR_PARAM_INVALID, "inner_precise must be in [0, 3]");
+  }
+
+  // Kernel-specific requirements.
+  if (f32) {
+    if (D % 32 != 0 || D > 256) return fail(FIA_ERR_UNSUPPORTED, "fp32 path needs D % 32 == 0 and D <= 256");
+  } else if (D != 64 && D != 128) {
+    return fail(FIA_ERR_UNSUPPORTED, "bf16 kernels support head dim 64 and 128");
+  }
+  {
+    const int64_t vec = f32 ? 4 : 8;  // elements per 16-byte access
+    const int64_t strides[] = {cq.ss, cq.sh, co.ss, co.sh, ck.ss, ck.sh, cv.ss, cv.sh,
+                               tnd ? 0 : cq.sb, tnd ? 0 : co.sb, ck.sb, cv.sb};
+    for (int64_t s : strides) {
+      if (s % vec != 0) return fail(FIA_ERR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
+    }
+    const void* ptrs[] = {query->data, attention_out->data, key->data, value->data};
+    for (const void* ptr : ptrs) {
+      if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) {
+        return fail(FIA_ERR_UNSUPPORTED, "tensor data must be 16-byte aligned");
+      }
+    }
+  }
+  for (int64_t b = 0; b < B; ++b) {
+    if (qlen[b] > INT32_MAX || kvlen[b] > INT32_MAX) return fail(FIA_ERR_PARAM_INVALID, "length too large");
+  }
+
+  // Build the executor.
+  fia_executor* e = new fia_executor();
+  AttnArgs& a = e->a;
+  a.q = query->data;
+  a.o = attention_out->data;
+  a.k = key->data;
+  a.v = value->data;
+  a.lse = p->softmax_lse_flag ? static_cast<float*>(softmax_lse->data) : nullptr;
+  a.write_lse = p->softmax_lse_flag ? 1 : 0;
+  a.q_sb = cq.sb; a.q_ss = cq.ss; a.q_sh = cq.sh;
+  a.o_sb = co.sb; a.o_ss = co.ss; a.o_sh = co.sh;
+  a.k_sb = ck.sb; a.k_ss = ck.ss; a.k_sh = ck.sh;
+  a.v_sb = cv.sb; a.v_ss = cv.ss; a.v_sh = cv.sh;
+  if (a.write_lse) {
+    if (tnd) {
+      a.lse_sb = 0; a.lse_ss = softmax_lse->stride[0]; a.lse_sh = softmax_lse->stride[1];
+    } else {
+      a.lse_sb = softmax_lse->stride[0]; a.lse_sh = softmax_lse->stride[1]; a.lse_ss = softmax_lse->stride[2];
+    }
+  }
+  a.paged = paged ? 1 : 0;
+  a.tnd = tnd ? 1 : 0;
+  if (paged) {
+    a.block_table = static_cast<const int32_t*>(block_table->data);
+    a.bt_sb = block_table->stride[0];
+    a.block_size = (int32_t)bs;
+    a.n_blocks = (int32_t)n_blocks;
+    a.bs_div = make_fastdiv((uint32_t)bs);
+  }
+  a.B = (int32_t)B;
+  a.Sq = (int32_t)cq.S;
+  a.Skv = (int32_t)(paged ? bt_cols * bs : ck.S);
+  a.Qn = (int32_t)Qn;
+  a.KVn = (int32_t)KVn;
+  a.G = (int32_t)(Qn / KVn);
+  a.D = (int32_t)D;
+  a.esz = f32 ? 4 : 2;
+  a.scale = (float)p->scale_value;
+  a.scale_log2 = (float)(p->scale_value * 1.4426950408889634);
+  a.mode = mode;
+  a.pre = p->pre_tokens;
+  a.next = p->next_tokens;
+  a.slopes = pse == 2 ? static_cast<const float*>(pse_shift->data) : nullptr;
+  a.alibi_delta = (int32_t)(p->kv_start_idx - p->q_start_idx);
+
+  // Per-batch records.
+  e->meta.assign((size_t)B * fia::BF_COUNT, 0);
+  int64_t qo = 0, ko = 0, max_kv = 0;
+  for (int64_t b = 0; b < B; ++b) {
+    int32_t* r = &e->meta[(size_t)b * fia::BF_COUNT];
+    r[fia::BF_QLEN] = (int32_t)qlen[b];
+    r[fia::BF_KVLEN] = (int32_t)kvlen[b];
+    r[fia::BF_QOFF] = tnd ? (int32_t)qo : 0;
+    r[fia::BF_KVOFF] = tnd ? (int32_t)ko : 0;
+    qo += qlen[b];
+    ko += kvlen[b];
+    max_kv = std::max(max_kv, kvlen[b]);
+  }
+  e->s2max = (int32_t)max_kv;
+  e->work_off = e->meta.size();
+
+  const bool kv_empty = (numel(key) == 0 || numel(value) == 0) || (!paged && ck.S == 0);
+  if (kv_empty) {
+    e->kind = KIND_FILL;
+  } else if (f32) {
+    e->kind = KIND_FP32;
+  } else if (max_q <= 1 && (tnd || cq.S == 1)) {
+    e->kind = KIND_DECODE;
+  } else {
+    e->kind = KIND_PREFILL;
+  }
+
+  if (e->kind == KIND_PREFILL) {
+    struct Item { int64_t cost; int32_t b, h, qt; };
+    std::vector<Item> items;
+    for (int64_t b = 0; b < B; ++b) {
+      const int64_t rows = tnd ? qlen[b] : cq.S;
+      const int64_t nqt = (rows + fia::kPrefillRows - 1) / fia::kPrefillRows;
+      for (int64_t qt = 0; qt < nqt; ++qt) {
+        int64_t cost = 0;
+        const int64_t i0 = qt * fia::kPrefillRows;
+        const int64_t i1 = std::min(i0 + fia::kPrefillRows, qlen[b]);
+        if (i1 > i0) {
+          int64_t l0, h0, l1, h1;
+          visible(mode, i0, qlen[b], kvlen[b], p->pre_tokens, p->next_tokens, &l0, &h0);
+          visible(mode, i1 - 1, qlen[b], kvlen[b], p->pre_tokens, p->next_tokens, &l1, &h1);
+          if (h1 > l0) {
+            cost = (h1 + fia::kPrefillKeys - 1) / fia::kPrefillKeys - l0 / fia::kPrefillKeys;
+          }
+        }
+        for (int64_t h = 0; h < Qn; ++h) items.push_back({cost, (int32_t)b, (int32_t)h, (int32_t)qt});
+      }
+    }
+    if (items.size() > (size_t)INT32_MAX / 2) {
+      delete e;
+      return fail(FIA_ERR_UNSUPPORTED, "too many prefill work items");
+    }
+    // Longest first: the hardware dispatcher hands workgroups out in index
+    // order, so this is a greedy longest-processing-time schedule.
+    std::stable_sort(items.begin(), items.end(),
+                     [](const Item& x, const Item& y) { return x.cost > y.cost; });
+    for (const Item& it : items) {
+      e->meta.push_back(it.b);
+      e->meta.push_back(it.h | (it.qt << 8));
+    }
+    a.n_work = (int32_t)items.size();
+    for (const Item& it : items) {
+      if (it.qt >= (1 << 23)) {
+        delete e;
+        return fail(FIA_ERR_UNSUPPORTED, "query too long for the prefill work encoding");
+      }
+    }
+  } else if (e->kind == KIND_DECODE) {
+    int64_t total_chunks = 0;
+    for (int64_t b = 0; b < B; ++b) {
+      int32_t* r = &e->meta[(size_t)b * fia::BF_COUNT];
+      int64_t lo = 0, hi = 0;
+      if (qlen[b] >= 1) visible(mode, 0, qlen[b], kvlen[b], p->pre_tokens, p->next_tokens, &lo, &hi);
+      const int64_t nch = hi > lo ? (hi + kDecodeChunk - 1) / kDecodeChunk - lo / kDecodeChunk : 0;
+      r[fia::BF_LO] = (int32_t)lo;
+      r[fia::BF_HI] = (int32_t)hi;
+      r[fia::BF_NCHUNK] = (int32_t)nch;
+      r[fia::BF_CHUNK0] = (int32_t)total_chunks;
+      total_chunks += nch;
+    }
+    for (int64_t b = 0; b < B; ++b) {
+      const int32_t nch = e->meta[(size_t)b * fia::BF_COUNT + fia::BF_NCHUNK];
+      for (int32_t c = 0; c < nch; ++c) {
+        e->meta.push_back((int32_t)b);
+        e->meta.push_back(c);
+      }
+    }
+    a.chunk = kDecodeChunk;
+    a.n_head_blocks = (a.G + 15) / 16;
+    const int64_t n_items = total_chunks * KVn * a.n_head_blocks;
+    if (n_items > INT32_MAX) {
+      delete e;
+      return fail(FIA_ERR_UNSUPPORTED, "too many decode work items");
+    }
+    e->n_items = (int32_t)n_items;
+    a.n_work = (int32_t)total_chunks;
+    e->meta_bytes = e->meta.size() * sizeof(int32_t);
+    e->part_o_off = align_up(e->meta_bytes, kAlign);
+    e->part_lse_off = align_up(e->part_o_off + (size_t)total_chunks * Qn * D * sizeof(float), kAlign);
+    e->ws_size = align_up(e->part_lse_off + (size_t)total_chunks * Qn * sizeof(float), kAlign);
+  }
+  if (e->kind != KIND_DECODE) {
+    e->meta_bytes = e->meta.size() * sizeof(int32_t);
+    e->part_o_off = e->part_lse_off = align_up(e->meta_bytes, kAlign);
+    e->ws_size = align_up(e->meta_bytes, kAlign);
+  }
+  *workspace_size = e->ws_size;
+  *executor = e;
+  return FIA_SUCCESS;
+}
+
+fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_tensor* q,
+                                         const fia_tensor* ori_kv, const fia_tensor* cmp_kv,
+                                         const fia_tensor* ori_sparse_indices,
+                                         const fia_tensor* cmp_sparse_indices,
+                                         const fia_tensor* ori_block_table,
+                                         const fia_tensor* cmp_block_table,
+                                         const fia_tensor* seqused_kv, int64_t max_seqused_kv,
+                                         const fia_tensor* sinks, const fia_tensor* metadata,
+                                         const fia_tensor* attention_out, size_t* workspace_size,
+                                         fia_executor** executor) {
+  (void)metadata;
+  if (!p || !q || !ori_kv || !ori_block_table || !seqused_kv || !sinks || !attention_out ||
+      !workspace_size || !executor) {
+    return fail(FIA_ERR_NULLPTR, "params, q, ori_kv, ori_block_table, seqused_kv, sinks, "
+                                 "attention_out, workspace_size and executor must not be NULL");
+  }
+  *executor = nullptr;
+  *workspace_size = 0;
+  fia_status st;
+  const fia_tensor* must[] = {q, ori_kv, ori_block_table, seqused_kv, sinks, attention_out};
+  const char* names[] = {"q", "ori_kv", "ori_block_table", "seqused_kv", "sinks", "attention_out"};
+  for (int i = 0; i < 6; ++i) {
+    if ((st = check_tensor(must[i], names[i])) != FIA_SUCCESS) return st;
+  }
+  const std::string lq = p->layout_q ? p->layout_q : "BSND";
+  const std::string lkv = p->layout_kv ? p->layout_kv : "PA_ND";
+  if (lq == "TND") return fail(FIA_ERR_UNSUPPORTED, "layout_q TND is not supported");
+  if (lq != "BSND") return fail(FIA_ERR_PARAM_INVALID, "layout_q must be BSND or TND");
+  if (lkv != "PA_ND") return fail(FIA_ERR_PARAM_INVALID, "layout_kv must be PA_ND");
+  if (p->kv_quant_mode != 1) return fail(FIA_ERR_PARAM_INVALID, "kv_quant_mode must be 1 (per-tile)");
+  if (p->tile_size != 64) return fail(FIA_ERR_PARAM_INVALID, "tile_size must be 64");
+  if (p->rope_head_dim != 64) return fail(FIA_ERR_PARAM_INVALID, "rope_head_dim must be 64");
+  if (p->ori_mask_mode != 4) return fail(FIA_ERR_PARAM_INVALID, "ori_mask_mode must be 4 (band)");
+  if (p->ori_win_left != 127 || p->ori_win_right != 0) {
+    return fail(FIA_ERR_PARAM_INVALID, "ori_win_left must be 127 and ori_win_right 0");
+  }
+  if (p->return_softmax_lse) return fail(FIA_ERR_PARAM_INVALID, "return_softmax_lse is reserved");
+  if (ori_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "ori_sparse_indices is reserved");
+  if (q->dtype != FIA_DT_BF16) return fail(FIA_ERR_PARAM_INVALID, "q must be bf16");
+  if (q->ndim != 4) return fail(FIA_ERR_PARAM_INVALID, "q must be [B, S1, N1, 512]");
+  const int64_t B = q->shape[0], S1 = q->shape[1], N1 = q->shape[2];
+  if (q->shape[3] != fia::kSparseD) return fail(FIA_ERR_PARAM_INVALID, "q head dim must be 512");
+  if (N1 != 64 && N1 != 128) return fail(FIA_ERR_PARAM_INVALID, "q heads must be 64 or 128");
+  if (S1 != 1) return fail(FIA_ERR_UNSUPPORTED, "query length must be 1");
+  if (attention_out->dtype != FIA_DT_BF16 || attention_out->ndim != 4 ||
+      attention_out->shape[0] != B || attention_out->shape[1] != S1 || attention_out->shape[2] != N1 ||
+      attention_out->shape[3] != fia::kSparseD) {
+    return fail(FIA_ERR_PARAM_INVALID, "attention_out must be bf16 with the shape of q");
+  }
+  auto check_pool = [&](const fia_tensor* t, const char* name, int64_t* nb, int64_t* bs,
+                        int64_t* sb, int64_t* ss) -> fia_status {
+    if (t->dtype != FIA_DT_UINT8 && t->dtype != FIA_DT_FP8_E4M3FN && t->dtype != FIA_DT_INT8) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be a byte tensor (fp8 packed rows)");
+    }
+    const bool four = t->ndim == 4 && t->shape[2] == 1 && t->shape[3] == fia::kRowBytes;
+    const bool three = t->ndim == 3 && t->shape[2] == fia::kRowBytes;
+    if (!four && !three) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be [n_blocks, block_size, 1, 640]");
+    }
+    *nb = t->shape[0];
+    *bs = t->shape[1];
+    *sb = t->stride[0];
+    *ss = t->stride[1];
+    if (*bs % 16 != 0 || *bs > 1024 || *bs <= 0) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": block_size must be a multiple of 16, <= 1024");
+    }
+    if (*sb % 16 != 0 || *ss % 16 != 0 || reinterpret_cast<uintptr_t>(t->data) % 16 != 0) {
+      return fail(FIA_ERR_UNSUPPORTED, std::string(name) + ": rows must be 16-byte aligned");
+    }
+    return FIA_SUCCESS;
+  };
+  int64_t nb1, bs1, osb, oss, nb2 = 0, bs2 = 16, csb = 0, css = 0;
+  if ((st = check_pool(ori_kv, "ori_kv", &nb1, &bs1, &osb, &oss)) != FIA_SUCCESS) return st;
+  const bool has_cmp = cmp_kv != nullptr;
+  if (has_cmp) {
+    if ((st = check_tensor(cmp_kv, "cmp_kv")) != FIA_SUCCESS) return st;
+    if ((st = check_pool(cmp_kv, "cmp_kv", &nb2, &bs2, &csb, &css)) != FIA_SUCCESS) return st;
+    if (cmp_kv->dtype != ori_kv->dtype) return fail(FIA_ERR_PARAM_INVALID, "ori_kv and cmp_kv dtypes differ");
+    if (cmp_sparse_indices == nullptr) {
+      return fail(FIA_ERR_UNSUPPORTED, "compressed KV without top-k indices is not supported");
+    }
+    if (p->cmp_ratio == 128) return fail(FIA_ERR_UNSUPPORTED, "cmp_ratio 128 is not supported");
+    if (p->cmp_ratio != 4) return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 4 with compressed KV");
+    if (p->cmp_mask_mode != 3) return fail(FIA_ERR_PARAM_INVALID, "cmp_mask_mode must be 3");
+    if (cmp_block_table == nullptr) return fail(FIA_ERR_PARAM_INVALID, "cmp_kv needs cmp_block_table");
+  } else {
+    if (cmp_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices needs cmp_kv");
+    if (p->cmp_ratio != 1) return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 1 without compressed KV");
+  }
+  int64_t K2 = 0, idx_sb = 0;
+  if (cmp_sparse_indices != nullptr) {
+    if ((st = check_tensor(cmp_sparse_indices, "cmp_sparse_indices")) != FIA_SUCCESS) return st;
+    const fia_tensor* t = cmp_sparse_indices;
+    if (t->dtype != FIA_DT_INT32 || t->ndim != 4 || t->shape[0] != B || t->shape[1] != S1 ||
+        t->shape[2] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices must be int32 [B, S1, 1, K2]");
+    }
+    K2 = t->shape[3];
+    if (K2 != 512 && K2 != 1024) return fail(FIA_ERR_PARAM_INVALID, "K2 must be 512 or 1024");
+    idx_sb = t->stride[0];
+  }
+  auto check_bt = [&](const fia_tensor* t, const char* name, int64_t need) -> fia_status {
+    fia_status s2 = check_tensor(t, name);
+    if (s2 != FIA_SUCCESS) return s2;
+    if (t->dtype != FIA_DT_INT32 || t->ndim != 2 || t->shape[0] != B || t->shape[1] == 0) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be int32 [B, cols]");
+    }
+    if (t->shape[1] < need) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " has fewer columns than the longest "
+                                                            "sequence needs");
+    }
+    return FIA_SUCCESS;
+  };
+  if (max_seqused_kv < 0) return fail(FIA_ERR_PARAM_INVALID, "max_seqused_kv must be >= 0");
+  if ((st = check_bt(ori_block_table, "ori_block_table", (max_seqused_kv + bs1 - 1) / bs1)) != FIA_SUCCESS) {
+    return st;
+  }
+  if (has_cmp) {
+    const int64_t ncmp = max_seqused_kv / p->cmp_ratio;
+    if ((st = check_bt(cmp_block_table, "cmp_block_table", (ncmp + bs2 - 1) / bs2)) != FIA_SUCCESS) {
+      return st;
+    }
+  }
+  if (seqused_kv->dtype != FIA_DT_INT32 || seqused_kv->ndim != 1 || seqused_kv->shape[0] != B) {
+    return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
+  }
+  if (sinks->dtype != FIA_DT_FP32 || sinks->ndim != 1 || sinks->shape[0] != N1) {
+    return fail(FIA_ERR_PARAM_INVALID, "sinks must be fp32 [N1]");
+  }
+  if (q->stride[1] % 8 || q->stride[2] % 8 || q->stride[0] % 8 || attention_out->stride[0] % 8 ||
+      attention_out->stride[2] % 8 || reinterpret_cast<uintptr_t>(q->data) % 16 ||
+      reinterpret_cast<uintptr_t>(attention_out->data) % 16) {
+    return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
+  }
+
+  fia_executor* e = new fia_executor();
+  e->kind = KIND_SPARSE;
+  SparseArgs& a = e->sp;
+  a.q = static_cast<const uint16_t*>(q->data);
+  a.q_sb = q->stride[0];
+  a.q_sh = q->stride[2];
+  a.o = static_cast<uint16_t*>(attention_out->data);
+  a.o_sb = attention_out->stride[0];
+  a.o_sh = attention_out->stride[2];
+  a.ori = static_cast<const uint8_t*>(ori_kv->data);
+  a.ori_sb = osb;
+  a.ori_ss = oss;
+  a.cmp = has_cmp ? static_cast<const uint8_t*>(cmp_kv->data) : nullptr;
+  a.cmp_sb = csb;
+  a.cmp_ss = css;
+  a.ori_bt = static_cast<const int32_t*>(ori_block_table->data);
+  a.ori_bt_sb = ori_block_table->stride[0];
+  a.cmp_bt = has_cmp ? static_cast<const int32_t*>(cmp_block_table->data) : nullptr;
+  a.cmp_bt_sb = has_cmp ? cmp_block_table->stride[0] : 0;
+  a.idx = cmp_sparse_indices ? static_cast<const int32_t*>(cmp_sparse_indices->data) : nullptr;
+  a.idx_sb = idx_sb;
+  a.seqused = static_cast<const int32_t*>(seqused_kv->data);
+  a.sinks = static_cast<const float*>(sinks->data);
+  a.B = (int32_t)B;
+  a.N1 = (int32_t)N1;
+  a.K2 = (int32_t)K2;
+  a.bs1 = (int32_t)bs1;
+  a.bs2 = (int32_t)bs2;
+  a.nb1 = (int32_t)nb1;
+  a.nb2 = (int32_t)nb2;
+  a.ori_bt_cols = (int32_t)ori_block_table->shape[1];
+  a.cmp_bt_cols = has_cmp ? (int32_t)cmp_block_table->shape[1] : 0;
+  a.cmp_ratio = p->cmp_ratio;
+  a.win_left = p->ori_win_left;
+  a.win_right = p->ori_win_right;
+  a.n_win_slots = (int32_t)align_up((size_t)(a.win_left + a.win_right + 1), fia::kSparseChunk);
+  a.n_slots = a.n_win_slots + a.K2;
+  a.has_cmp = has_cmp ? 1 : 0;
+  a.scale_log2 = (float)(p->softmax_scale * 1.4426950408889634);
+  const int64_t n_chunks = a.n_slots / fia::kSparseChunk;
+  e->part_o_off = 0;
+  e->part_lse_off = align_up((size_t)B * n_chunks * N1 * fia::kSparseD * sizeof(float), kAlign);
+  e->ws_size = align_up(e->part_lse_off + (size_t)B * n_chunks * N1 * sizeof(float), kAlign);
+  *workspace_size = e->ws_size;
+  *executor = e;
+  return FIA_SUCCESS;
+}
+
+fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void* stream) {
+  if (e == nullptr) return fail(FIA_ERR_NULLPTR, "executor is NULL");
+  if (e->noop) return FIA_SUCCESS;
+  fia_status st = check_ws(e, workspace, workspace_size);
+  if (st != FIA_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(e, workspace, s)) != FIA_SUCCESS) return st;
+  bind_workspace(e, workspace);
+  hipError_t err = hipSuccess;
+  switch (e->kind) {
+    case KIND_FILL: err = fia::launch_fill_empty(e->a, s); break;
+    case KIND_FP32: err = fia::launch_attn_fp32(e->a, s); break;
+    case KIND_PREFILL: err = fia::launch_prefill_bf16(e->a, s); break;
+    case KIND_DECODE:
+      err = fia::launch_decode_bf16(e->a, e->n_items, s);
+      if (err == hipSuccess) err = fia::launch_decode_merge(e->a, s);
+      break;
+    case KIND_SPARSE:
+      err = fia::launch_sparse(e->sp, s);
+      if (err == hipSuccess) err = fia::launch_sparse_merge(e->sp, s);
+      break;
+    default: return fail(FIA_ERR_PARAM_INVALID, "corrupt executor");
+  }
+  if (err != hipSuccess) return fail(FIA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
+  return FIA_SUCCESS;
+}
+
+fia_status fia_debug_gather_kv(fia_executor* e, void* workspace, size_t workspace_size,
+                               int32_t which, void* dst, void* stream) {
+  if (e == nullptr || dst == nullptr) return fail(FIA_ERR_NULLPTR, "executor and dst must not be NULL");
+  if (e->noop || e->kind == KIND_SPARSE || e->kind == KIND_FILL) {
+    return fail(FIA_ERR_PARAM_INVALID, "executor has no key/value rows to gather");
+  }
+  if (which != 0 && which != 1) return fail(FIA_ERR_PARAM_INVALID, "which must be 0 or 1");
+  fia_status st = check_ws(e, workspace, workspace_size);
+  if (st != FIA_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = upload_meta(e, workspace, s)) != FIA_SUCCESS) return st;
+  bind_workspace(e, workspace);
+  hipError_t err = fia::launch_debug_gather(e->a, which, dst, e->s2max, s);
+  if (err != hipSuccess) return fail(FIA_ERR_HIP, std::string("gather launch failed: ") + hipGetErrorString(err));
+  return FIA_SUCCESS;
+}
+
+fia_status fia_debug_sparse_rows(fia_executor* e, void* workspace, size_t workspace_size,
+                                 int32_t* ids_out, uint8_t* rows_out, int32_t* n_slots_out,
+                                 void* stream) {
+  if (e == nullptr) return fail(FIA_ERR_NULLPTR, "executor is NULL");
+  if (e->kind != KIND_SPARSE) return fail(FIA_ERR_PARAM_INVALID, "not a sparse executor");
+  if (n_slots_out) *n_slots_out = e->sp.n_slots;
+  if (ids_out == nullptr) return FIA_SUCCESS;
+  if (rows_out == nullptr) return fail(FIA_ERR_NULLPTR, "rows_out must not be NULL");
+  fia_status st = check_ws(e, workspace, workspace_size);
+  if (st != FIA_SUCCESS) return st;
+  bind_workspace(e, workspace);
+  hipError_t err = fia::launch_debug_sparse_rows(e->sp, ids_out, rows_out, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(FIA_ERR_HIP, std::string("launch failed: ") + hipGetErrorString(err));
+  return FIA_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,126 @@
+// Device helpers shared by the gfx950 kernels: vector types, MFMA wrappers,
+// key/value row addressing and small wave-level utilities.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fia_internal.h"
+
+namespace fia {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+constexpr float kPosInf = __builtin_inff();
+
+// D(32x32) += A(32x16) * B(16x32), bf16 in, fp32 accumulate.
+// Lane l supplies A[l%32][8(l/32)+0..7] and B[8(l/32)+0..7][l%32]; it holds
+// C[8(r/4) + 4(l/32) + r%4][l%32] in accumulator slot r.
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D(16x16) += A(16x32) * B(32x16).  Lane l supplies A[l%16][8(l/16)+0..7] and
+// B[8(l/16)+0..7][l%16]; it holds C[4(l/16) + r][l%16] in slot r.
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Two floats -> packed bf16 pair (round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Select the low (sel = 0) or high (sel = 1) bf16 halves of two words into one
+// packed pair {a.half, b.half}.
+__device__ __forceinline__ uint32_t pick_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
+  return (uint32_t)(((uint64_t)n * f.mul) >> (32 + f.shift));
+}
+
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Base of the contiguous head-dim vector of key (or value) row j of batch b,
+// KV head g.  Dense / TND rows are addressed with batch, token and head
+// strides; paged rows through block_table[b][j / block_size], with the block
+// id clamped into [0, n_blocks).  Returns an element offset.
+__device__ __forceinline__ int64_t kv_row_offset(const AttnArgs& a, int64_t sb, int64_t ss,
+                                                 int64_t sh, int b, int j, int g, int kv_off) {
+  if (a.paged) {
+    uint32_t page = fast_div((uint32_t)j, a.bs_div);
+    int slot = j - (int)page * a.block_size;
+    int blk = a.block_table[(int64_t)b * a.bt_sb + page];
+    blk = blk < 0 ? 0 : (blk >= a.n_blocks ? a.n_blocks - 1 : blk);
+    return (int64_t)blk * sb + (int64_t)slot * ss + (int64_t)g * sh;
+  }
+  return (int64_t)b * sb + (int64_t)(kv_off + j) * ss + (int64_t)g * sh;
+}
+
+// Same, for a run of rows known to share one page (paged) -- the block id is
+// looked up once by the caller.
+__device__ __forceinline__ int64_t paged_row_offset(int blk, int slot, int g, int64_t sb,
+                                                    int64_t ss, int64_t sh) {
+  return (int64_t)blk * sb + (int64_t)slot * ss + (int64_t)g * sh;
+}
+
+__device__ __forceinline__ int clamp_block(int blk, int n_blocks) {
+  return blk < 0 ? 0 : (blk >= n_blocks ? n_blocks - 1 : blk);
+}
+
+// Global loads/stores of 16 and 8 bytes.
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ void st8(void* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
+
+// Visible key range [lo, hi) of query row i given Lq, Lk and the mask mode
+// (mode 0: all keys; 2: j <= i; 3: j <= i + Lk - Lq; 4: band around i + Lk - Lq).
+__device__ __forceinline__ void visible_range(const AttnArgs& a, int i, int Lq, int Lk, int& lo,
+                                              int& hi) {
+  int64_t d = (int64_t)Lk - Lq;
+  int64_t l = 0, h = Lk;
+  if (a.mode == 2) {
+    h = (int64_t)i + 1;
+  } else if (a.mode == 3) {
+    h = (int64_t)i + d + 1;
+  } else if (a.mode == 4) {
+    l = (int64_t)i + d - a.pre;
+    h = (int64_t)i + d + a.next + 1;
+  }
+  if (l < 0) l = 0;
+  if (l > Lk) l = Lk;
+  if (h > Lk) h = Lk;
+  if (h < l) h = l;
+  lo = (int)l;
+  hi = (int)h;
+}
+
+}  // namespace fia

@@ -1,0 +1,125 @@
+// Internal interface between the host planner (fia_api.cpp) and the HIP
+// kernels (*.hip).  Plain structs passed by value as kernel arguments.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace fia {
+
+// Per-batch record in the device metadata (int32 each).
+enum BatchField {
+  BF_QLEN = 0,      // actual query length Lq
+  BF_KVLEN = 1,     // actual key/value length Lk
+  BF_QOFF = 2,      // TND: first query token of the batch (else 0)
+  BF_KVOFF = 3,     // TND: first key token of the batch (else 0)
+  BF_LO = 4,        // decode: first visible key
+  BF_HI = 5,        // decode: one past the last visible key
+  BF_NCHUNK = 6,    // decode: number of split-KV chunks
+  BF_CHUNK0 = 7,    // decode: global index of the batch's first chunk
+  BF_COUNT = 8
+};
+
+// Unsigned division by a runtime constant through a 64-bit multiply:
+// n / d == (n * mul) >> (32 + shift) for every n < 2^31 (mul < 2^33).
+struct FastDiv {
+  uint64_t mul;
+  uint32_t shift;
+  uint32_t d;
+};
+
+// Dense / paged attention arguments (prefill, decode and fp32 kernels).
+struct AttnArgs {
+  const void* q;
+  void* o;
+  float* lse;
+  const void* k;
+  const void* v;
+  // strides in elements.  Query / output: batch, token, head.  For TND the
+  // batch stride is 0 and the token index is offset by BF_QOFF.
+  int64_t q_sb, q_ss, q_sh;
+  int64_t o_sb, o_ss, o_sh;
+  int64_t lse_sb, lse_sh, lse_ss;   // lse[b, h, i] (TND: lse[t, h])
+  // key / value: dense -> batch, token, head; paged -> block, slot, head.
+  int64_t k_sb, k_ss, k_sh;
+  int64_t v_sb, v_ss, v_sh;
+  const int32_t* block_table;       // paged only
+  int64_t bt_sb;                    // row stride of the block table
+  int32_t block_size;
+  int32_t n_blocks;
+  FastDiv bs_div;
+  int32_t paged;
+  int32_t tnd;
+  const int32_t* meta;              // [B * BF_COUNT] then the work list
+  const int32_t* work;              // prefill: 2 ints per item; decode: 2 ints per chunk
+  int32_t n_work;
+  int32_t B, Sq, Skv, Qn, KVn, G, D;
+  int32_t esz;                      // bytes per element of q / k / v / o
+  float scale;                      // softmax scale
+  float scale_log2;                 // scale * log2(e)
+  int32_t mode;                     // mask mode 0, 2, 3, 4
+  int64_t pre, next;                // band (mode 4)
+  const float* slopes;              // ALiBi slopes [Qn] or nullptr
+  int32_t alibi_delta;              // kv_start_idx - q_start_idx
+  int32_t write_lse;
+  // decode split-KV
+  int32_t chunk;                    // tokens per chunk (multiple of 128)
+  int32_t n_head_blocks;            // ceil(G / 16)
+  float* part_o;                    // [total_chunks * Qn * D]
+  float* part_lse;                  // [total_chunks * Qn]
+};
+
+// Shared-KV sparse decode arguments.
+struct SparseArgs {
+  const uint16_t* q;                // bf16 [B, 1, N1, 512]
+  int64_t q_sb, q_sh;
+  uint16_t* o;                      // bf16 [B, 1, N1, 512]
+  int64_t o_sb, o_sh;
+  const uint8_t* ori;               // [nb1, bs1, 1, 640]
+  int64_t ori_sb, ori_ss;           // bytes
+  const uint8_t* cmp;
+  int64_t cmp_sb, cmp_ss;
+  const int32_t* ori_bt;
+  int64_t ori_bt_sb;
+  const int32_t* cmp_bt;
+  int64_t cmp_bt_sb;
+  const int32_t* idx;               // [B, 1, 1, K2]
+  int64_t idx_sb;
+  const int32_t* seqused;           // [B]
+  const float* sinks;               // [N1]
+  int32_t B, N1, K2;
+  int32_t bs1, bs2, nb1, nb2;
+  int32_t ori_bt_cols, cmp_bt_cols;
+  int32_t cmp_ratio, win_left, win_right;
+  int32_t n_win_slots;              // window slots (multiple of 64)
+  int32_t n_slots;                  // window slots + K2
+  int32_t has_cmp;
+  float scale_log2;
+  float* part_o;                    // [B * n_chunks * N1 * 512]
+  float* part_lse;                  // [B * n_chunks * N1]
+};
+
+// Launchers (defined next to their kernels).  Return hipGetLastError().
+hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s);
+hipError_t launch_decode_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_fp32(const AttnArgs& a, hipStream_t s);
+hipError_t launch_fill_empty(const AttnArgs& a, hipStream_t s);
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t s);
+hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s);
+hipError_t launch_debug_gather(const AttnArgs& a, int32_t which, void* dst, int32_t s2max,
+                               hipStream_t s);
+hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* rows,
+                                    hipStream_t s);
+
+// Constants shared by planner and kernels.
+constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
+constexpr int kPrefillKeys = 64;    // keys per prefill tile
+constexpr int kDecodeStep = 32;     // keys per decode wave step
+constexpr int kSparseChunk = 64;    // row slots per sparse workgroup
+constexpr int kSparseHeads = 32;    // heads per sparse workgroup
+constexpr int kSparseD = 512;       // logical row width (64 rope + 448 nope)
+constexpr int kRowBytes = 640;
+
+}  // namespace fia

@@ -1,0 +1,328 @@
+// Shared-KV sparse decode (KvQuantSparseAttnSharedkv; sparse_flash_mla CSA
+// mode): O = softmax(Q K~^T * scale) V~ with K~ = V~ = the window rows of the
+// original KV followed by the top-k selected rows of the compressed KV, plus a
+// per-head sink logit.
+//
+// Row list of batch b (query length 1, query at position p = Lk - 1), as fixed
+// slots so a batch's result never depends on the other batch entries:
+//   slots [0, n_win_slots): window row j = p - win_left + s, used when
+//     0 <= j <= min(Lk - 1, p + win_right);
+//   slots [n_win_slots, n_win_slots + K2): compressed row c = idx[b][s - n_win],
+//     used when 0 <= c < floor(Lk / cmp_ratio).
+// Each packed 640-byte row holds bf16 rope x64 | e4m3fn nope x448 | fp32
+// scale x7 (one per 64-wide nope tile); the logical 512-vector is
+// [rope | nope * scale].
+//
+// One workgroup takes 64 slots x 32 heads of one batch entry: it gathers the
+// rows through the block tables, dequantises them into LDS twice (row-major
+// for the score product, transposed for the value product), runs both
+// products on 32x32x16 bf16 MFMA and writes a normalised partial with its
+// log2-sum-exp.  The merge kernel folds the chunks in slot order together with
+// the sink: an extra logit sigma_h whose value vector is zero.
+#include "fia_device.h"
+
+namespace fia {
+
+namespace {
+
+constexpr int X_PITCH = kSparseD * 2 + 16;   // bytes per row-major row
+constexpr int XT_PITCH = kSparseChunk * 2 + 8; // bytes per transposed row
+constexpr int X_BYTES = kSparseChunk * X_PITCH;
+constexpr int XT_BYTES = kSparseD * XT_PITCH;
+constexpr int P_BYTES = 4 * 64 * 16;
+constexpr int SX_BYTES = 2 * 64 * 16 * 4;
+constexpr int LDS_TOTAL = X_BYTES + XT_BYTES + P_BYTES + SX_BYTES + 64 * 4 + 2 * 32 * 4 * 2;
+
+}  // namespace
+
+// OCP e4m3fn code -> float (exact): exponent field 0 is subnormal m * 2^-9,
+// 0x7f / 0xff are NaN, otherwise (1 + m/8) * 2^(e-7).
+__device__ __forceinline__ float e4m3fn_to_f32(uint32_t x) {
+  const uint32_t e = (x >> 3) & 15u;
+  const uint32_t m = x & 7u;
+  float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+  if ((x & 0x7fu) == 0x7fu) mag = __builtin_nanf("");
+  return (x & 0x80u) ? -mag : mag;
+}
+
+// Slot s of batch b -> packed row address (nullptr for an unused slot) and its
+// id: j for window row j, (1 << 30) | c for compressed row c, -1 if unused.
+__device__ __forceinline__ const uint8_t* sparse_slot_row(const SparseArgs& a, int b, int s,
+                                                          int Lk, int32_t* id) {
+  *id = -1;
+  if (s < a.n_win_slots) {
+    const int p = Lk - 1;
+    const int j = p - a.win_left + s;
+    const int jmax = min(Lk - 1, p + a.win_right);
+    if (s > a.win_left + a.win_right || j < 0 || j > jmax) return nullptr;
+    int page = j / a.bs1;
+    const int slot = j - page * a.bs1;
+    if (page >= a.ori_bt_cols) page = a.ori_bt_cols - 1;
+    const int blk = clamp_block(a.ori_bt[(int64_t)b * a.ori_bt_sb + page], a.nb1);
+    *id = j;
+    return a.ori + (int64_t)blk * a.ori_sb + (int64_t)slot * a.ori_ss;
+  }
+  const int k = s - a.n_win_slots;
+  if (!a.has_cmp || k >= a.K2) return nullptr;
+  const int c = a.idx[(int64_t)b * a.idx_sb + k];
+  const int n_cmp = Lk / a.cmp_ratio;
+  if (c < 0 || c >= n_cmp) return nullptr;
+  int page = c / a.bs2;
+  const int slot = c - page * a.bs2;
+  if (page >= a.cmp_bt_cols) page = a.cmp_bt_cols - 1;
+  const int blk = clamp_block(a.cmp_bt[(int64_t)b * a.cmp_bt_sb + page], a.nb2);
+  *id = (1 << 30) | c;
+  return a.cmp + (int64_t)blk * a.cmp_sb + (int64_t)slot * a.cmp_ss;
+}
+
+__device__ __forceinline__ int sparse_len(const SparseArgs& a, int b) {
+  int Lk = a.seqused[b];
+  const int cap = a.ori_bt_cols * a.bs1;
+  return Lk < 0 ? 0 : (Lk > cap ? cap : Lk);
+}
+
+// Grid: (n_slots / 64, N1 / 32, B); 256 threads.
+__global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint8_t* xs = lds;                         // [64][X_PITCH]
+  uint8_t* xts = xs + X_BYTES;               // [512][XT_PITCH]
+  u32x4* ps = reinterpret_cast<u32x4*>(xts + XT_BYTES);      // [4][64]
+  float* sx = reinterpret_cast<float*>(xts + XT_BYTES + P_BYTES);  // [2][64][16]
+  int32_t* ids = reinterpret_cast<int32_t*>(xts + XT_BYTES + P_BYTES + SX_BYTES);  // [64]
+  float* mx_s = reinterpret_cast<float*>(ids + 64);          // [2][32]
+  float* l_s = mx_s + 64;                                    // [2][32]
+
+  const int chunk = blockIdx.x;
+  const int hb = blockIdx.y;
+  const int b = blockIdx.z;
+  const int n_chunks = gridDim.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int n = lane & 31;
+  const int hh = lane >> 5;
+  const int Lk = sparse_len(a, b);
+  const int s0 = chunk * kSparseChunk;
+
+  // 1. Gather and dequantise: thread owns rows 4 rg .. 4 rg + 3 and the
+  // 8-element pieces pc = tid/16 + 16 q of them.
+  {
+    const int rg = tid & 15;
+    const uint8_t* rows[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int32_t id;
+      rows[u] = sparse_slot_row(a, b, s0 + 4 * rg + u, Lk, &id);
+      if ((tid >> 4) == 0) ids[4 * rg + u] = id;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int pc = (tid >> 4) + 16 * q;
+      uint32_t w[4][4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (rows[u] == nullptr) {
+          w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0u;
+        } else if (pc < 8) {
+          const u32x4 v = ld16(rows[u] + 16 * pc);
+          w[u][0] = v.x;
+          w[u][1] = v.y;
+          w[u][2] = v.z;
+          w[u][3] = v.w;
+        } else {
+          const int np = pc - 8;
+          const u32x2 codes = ld8(rows[u] + 128 + 8 * np);
+          const float sc = *reinterpret_cast<const float*>(rows[u] + 576 + 4 * (np >> 3));
+          float f[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            f[e] = e4m3fn_to_f32((codes.x >> (8 * e)) & 0xffu) * sc;
+            f[4 + e] = e4m3fn_to_f32((codes.y >> (8 * e)) & 0xffu) * sc;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[u][e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
+        }
+        *reinterpret_cast<u32x4*>(xs + (4 * rg + u) * X_PITCH + 16 * pc) =
+            u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int ww = e >> 1;
+        u32x2 pr;
+        if (e & 1) {
+          pr = u32x2{pick_hi(w[0][ww], w[1][ww]), pick_hi(w[2][ww], w[3][ww])};
+        } else {
+          pr = u32x2{pick_lo(w[0][ww], w[1][ww]), pick_lo(w[2][ww], w[3][ww])};
+        }
+        *reinterpret_cast<u32x2*>(xts + (8 * pc + e) * XT_PITCH + 8 * rg) = pr;
+      }
+    }
+  }
+  __syncthreads();
+
+  // 2. Scores S^T[slot][head]: wave (sb, dh) = slot block 32 sb, d half dh.
+  const int sb = wave & 1;
+  const int dh = wave >> 1;
+  const int head = hb * kSparseHeads + n;
+  f32x16 s;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = 0.f;
+  {
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh + 256 * dh + 8 * hh;
+#pragma unroll 4
+    for (int c = 0; c < 16; ++c) {
+      const u32x4 bq = ld16(qp + 16 * c);
+      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH +
+                                                       (256 * dh + 16 * c + 8 * hh) * 2);
+      s = mfma32(av, bq, s);
+    }
+  }
+  if (dh == 1) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sx[(sb * 64 + lane) * 16 + r] = s[r];
+  }
+  __syncthreads();
+  float m_loc = kNegInf;
+  if (dh == 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int slot = 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
+      const float x = (s[r] + sx[(sb * 64 + lane) * 16 + r]) * a.scale_log2;
+      s[r] = ids[slot] >= 0 ? x : kNegInf;
+      m_loc = fmaxf(m_loc, s[r]);
+    }
+    m_loc = fmaxf(m_loc, shfl_xor_f(m_loc, 32));
+    if (hh == 0) mx_s[sb * 32 + n] = m_loc;
+  }
+  __syncthreads();
+  const float m_all = fmaxf(mx_s[n], mx_s[32 + n]);
+  const float m_use = (m_all == kNegInf) ? 0.f : m_all;
+  if (dh == 0) {
+    float l = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      float p[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        p[t] = fast_exp2(s[8 * kk + t] - m_use);
+        l += p[t];
+      }
+      ps[(2 * sb + kk) * 64 + lane] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+    }
+    l += shfl_xor_f(l, 32);
+    if (hh == 0) l_s[sb * 32 + n] = l;
+  }
+  __syncthreads();
+
+  // 3. O^T[d][head] for d in [128 wave, 128 wave + 128).
+  f32x16 o[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      const uint8_t* vp = xts + (128 * wave + 32 * mb + n) * XT_PITCH + (16 * kk + 4 * hh) * 2;
+      const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vp);
+      const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vp + 16);
+      o[mb] = mfma32(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[kk * 64 + lane], o[mb]);
+    }
+  }
+  const float l_tot = l_s[n] + l_s[32 + n];
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const int64_t pi = ((int64_t)b * n_chunks + chunk) * a.N1 + head;
+  float* pp = a.part_o + pi * kSparseD + 128 * wave + 4 * hh;
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      *reinterpret_cast<f32x4*>(pp + 32 * mb + 8 * q4) =
+          f32x4{o[mb][4 * q4] * inv, o[mb][4 * q4 + 1] * inv, o[mb][4 * q4 + 2] * inv,
+                o[mb][4 * q4 + 3] * inv};
+    }
+  }
+  if (wave == 0 && hh == 0) a.part_lse[pi] = l_tot > 0.f ? m_use + fast_log2(l_tot) : kNegInf;
+}
+
+// One wave per (b, head): fold the chunks in slot order with the sink logit.
+__global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= a.B * a.N1) return;
+  const int b = row / a.N1;
+  const int h = row - b * a.N1;
+  const int n_chunks = a.n_slots / kSparseChunk;
+  const float sink = a.sinks[h] * kLog2e;
+  float M = sink;
+  for (int c = 0; c < n_chunks; ++c) {
+    M = fmaxf(M, a.part_lse[((int64_t)b * n_chunks + c) * a.N1 + h]);
+  }
+  const float m_use = (M == kNegInf) ? 0.f : M;
+  float L = fast_exp2(sink - m_use);
+  float acc[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    const int64_t pi = ((int64_t)b * n_chunks + c) * a.N1 + h;
+    const float lc = a.part_lse[pi];
+    if (lc == kNegInf) continue;
+    const float w = fast_exp2(lc - m_use);
+    L += w;
+    const f32x4* pp = reinterpret_cast<const f32x4*>(a.part_o + pi * kSparseD + 8 * lane);
+    const f32x4 x0 = pp[0], x1 = pp[1];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] += w * x0[u];
+      acc[4 + u] += w * x1[u];
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + 8 * lane;
+  st16(op, u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
+                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)});
+}
+
+hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
+  if (a.B == 0) return hipSuccess;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)sparse_chunk, hipFuncAttributeMaxDynamicSharedMemorySize,
+                        LDS_TOTAL);
+    attr_set = true;
+  }
+  dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.B);
+  sparse_chunk<<<grid, 256, LDS_TOTAL, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
+  const int rows = a.B * a.N1;
+  if (rows > 0) sparse_merge<<<(rows + 3) / 4, 256, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// Test support: slot ids and raw row bytes, through sparse_slot_row.
+__global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* ids, uint8_t* rows) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)a.B * a.n_slots;
+  if (t >= total) return;
+  const int b = (int)(t / a.n_slots);
+  const int s = (int)(t % a.n_slots);
+  int32_t id;
+  const uint8_t* row = sparse_slot_row(a, b, s, sparse_len(a, b), &id);
+  ids[t] = id;
+  uint32_t* dst = reinterpret_cast<uint32_t*>(rows + t * kRowBytes);
+  for (int w = 0; w < kRowBytes / 4; ++w) {
+    dst[w] = row ? reinterpret_cast<const uint32_t*>(row)[w] : 0u;
+  }
+}
+
+hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* rows,
+                                    hipStream_t s) {
+  const int64_t total = (int64_t)a.B * a.n_slots;
+  if (total > 0) debug_sparse_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a, ids, rows);
+  return hipGetLastError();
+}
+
+}  // namespace fia

@@ -1,0 +1,73 @@
+"""Move seeded workloads (numpy, from ``workloads``) onto the GPU as torch
+tensors and build library plans for them.  Marshalling only."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import fia
+from .workloads import DenseCase, SparseCase
+
+
+def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """bf16 bit patterns (uint16) -> torch.bfloat16; other arrays as they are."""
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(arr))
+    return t.to(device)
+
+
+def dense_tensors(case: DenseCase, device="cuda"):
+    q = to_device(case.q, case.dtype, device)
+    if case.paged:
+        k = to_device(case.k_pool, case.dtype, device)
+        v = to_device(case.v_pool, case.dtype, device)
+        bt = torch.from_numpy(case.block_table).to(device)
+    else:
+        k = to_device(case.k, case.dtype, device)
+        v = to_device(case.v, case.dtype, device)
+        bt = None
+    slopes = None if case.alibi_slopes is None else torch.from_numpy(case.alibi_slopes).to(device)
+    return q, k, v, bt, slopes
+
+
+def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia.AttentionPlan:
+    q, k, v, bt, slopes = tensors if tensors is not None else dense_tensors(case, device)
+    kw = dict(num_heads=case.num_heads, num_key_value_heads=case.num_kv_heads,
+              scale_value=case.scale, input_layout=case.layout, sparse_mode=case.sparse_mode,
+              pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
+              pse_type=2 if slopes is not None else 0, pse_shift=slopes,
+              q_start_idx=case.q_start_idx, kv_start_idx=case.kv_start_idx,
+              block_table=bt, block_size=case.block_size if bt is not None else 0,
+              softmax_lse_flag=case.lse, actual_seq_lengths=case.actual_seq_lengths,
+              actual_seq_lengths_kv=case.actual_seq_lengths_kv)
+    kw.update(overrides)
+    return fia.AttentionPlan(q, k, v, **kw)
+
+
+def sparse_tensors(case: SparseCase, device="cuda"):
+    return dict(
+        q=to_device(case.q, "bf16", device),
+        ori_kv=torch.from_numpy(case.ori_kv).to(device),
+        cmp_kv=torch.from_numpy(case.cmp_kv).to(device),
+        cmp_sparse_indices=torch.from_numpy(case.cmp_sparse_indices).to(device),
+        ori_block_table=torch.from_numpy(case.ori_block_table).to(device),
+        cmp_block_table=torch.from_numpy(case.cmp_block_table).to(device),
+        seqused_kv=torch.tensor(case.seqused_kv, dtype=torch.int32, device=device),
+        sinks=torch.from_numpy(case.sinks).to(device),
+    )
+
+
+def sparse_plan(case: SparseCase, device="cuda", tensors=None) -> fia.SparsePlan:
+    t = tensors if tensors is not None else sparse_tensors(case, device)
+    return fia.SparsePlan(t["q"], t["ori_kv"], t["cmp_kv"], t["cmp_sparse_indices"],
+                          t["ori_block_table"], t["cmp_block_table"], t["seqused_kv"],
+                          t["sinks"], softmax_scale=case.softmax_scale,
+                          max_seqused_kv=max(case.seqused_kv), cmp_ratio=case.cmp_ratio,
+                          ori_win_left=case.win_left, ori_win_right=case.win_right)
+
+
+def bf16_bits(t: torch.Tensor) -> np.ndarray:
+    """torch.bfloat16 tensor -> uint16 bit patterns (numpy, on the host)."""
+    return t.detach().cpu().view(torch.int16).numpy().view(np.uint16)

@@ -47,9 +47,13 @@ def rng_for(seed: int) -> np.random.Generator:
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """Round float32 values to bfloat16 (round to nearest even); return bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    r = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
-    return ((u + r) >> np.uint64(16)).astype(np.uint16)
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    nan = (u & np.uint32(0x7FFFFFFF)) > np.uint32(0x7F800000)
+    r = ((u >> np.uint32(16)) & np.uint32(1)) + np.uint32(0x7FFF)
+    out = ((u + r) >> np.uint32(16)).astype(np.uint16)
+    if nan.any():
+        out[nan] = (u[nan] >> np.uint32(16)).astype(np.uint16) | np.uint16(0x0040)
+    return out
 
 
 def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
@@ -316,6 +320,8 @@ def pack_rows(rng, n_rows: int) -> np.ndarray:
     import torch  # the e4m3fn rounding of the inputs uses torch's CPU cast
 
     out = np.zeros((n_rows, ROW_BYTES), dtype=np.uint8)
+    if n_rows == 0:
+        return out
     rope = normal_bf16(rng, (n_rows, ROPE_DIM))
     out[:, ROPE_OFF:ROPE_OFF + 2 * ROPE_DIM] = rope.view(np.uint8).reshape(n_rows, -1)
     nope = rng.standard_normal((n_rows, N_TILES, TILE), dtype=np.float32)

@@ -1,0 +1,235 @@
+/*
+ * fia.h - fused inference attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfia.so.  Plain pointers and sizes only.
+ *
+ * The operator computes, per batch b, query head h and query row i,
+ *
+ *     out[b,i,h,:] = softmax_j( scale * q[b,i,h,:] . k[b,j,g,:] + bias(h,i,j) ) v[b,j,g,:]
+ *
+ * over the keys j that the mask mode leaves visible, with g = h / (Q_N / KV_N)
+ * (aclnnFusedInferAttentionScoreV5 and V2, "Formula"; V4 "Formula" adds the
+ * ALiBi full mask after scaling; V2 "numKeyValueHeads" restrictions for GQA).
+ * A query length of 1 is the incremental-decode branch, anything else the
+ * prompt branch (V2 function description).  The optional softmax LSE output is
+ * max + ln(sum exp(s - max)) per row (V2, softmaxLse restrictions).
+ *
+ * The call is two-phase, as on the pages (V5 / V2 "function prototype"):
+ *   1. fia_get_workspace_size() validates every argument, classifies the call,
+ *      plans the work and returns the workspace size and an executor;
+ *   2. fia_run() enqueues the kernels on a HIP stream.
+ *
+ * Conventions shared by every entry point
+ *   - Tensor data pointers are DEVICE pointers; the caller owns them and keeps
+ *     them valid until the enqueued work completes.  Host arrays (lengths) are
+ *     copied into the executor during phase 1.
+ *   - fia_tensor strides are in elements; the innermost dimension must be
+ *     contiguous (stride 1).  Any other strides are honoured.
+ *   - Phase 1 never touches the GPU.  It returns FIA_ERR_PARAM_INVALID for an
+ *     argument that breaks a rule stated on the pages, FIA_ERR_UNSUPPORTED for
+ *     a legal feature this library does not implement, FIA_ERR_NULLPTR for a
+ *     missing required pointer.  fia_last_error() describes the failure.
+ *   - fia_run() returns FIA_ERR_WORKSPACE when the workspace is NULL with a
+ *     non-zero required size or smaller than the required size, and
+ *     FIA_ERR_HIP when a HIP call fails.
+ *   - Block ids in block tables are not validated, as on the pages (V2 page
+ *     attention scenario); an id outside [0, n_blocks) is clamped into range,
+ *     so it yields unspecified values but never an out-of-bounds access.
+ *   - Results are deterministic: repeated calls give bitwise-identical output,
+ *     and the output of one batch entry does not depend on the other entries
+ *     (V4 / V2 deterministic computation; sparse_flash_mla batch invariance).
+ *   - An executor may be run any number of times, from one thread at a time,
+ *     until fia_executor_destroy().
+ */
+#ifndef FIA_H_
+#define FIA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FIA_SUCCESS = 0,
+  FIA_ERR_NULLPTR = 1,
+  FIA_ERR_PARAM_INVALID = 2,
+  FIA_ERR_UNSUPPORTED = 3,
+  FIA_ERR_WORKSPACE = 4,
+  FIA_ERR_HIP = 5
+} fia_status;
+
+typedef enum {
+  FIA_DT_BF16 = 0,
+  FIA_DT_FP16 = 1,
+  FIA_DT_FP32 = 2,
+  FIA_DT_FP8_E4M3FN = 3,
+  FIA_DT_INT32 = 4,
+  FIA_DT_INT64 = 5,
+  FIA_DT_UINT8 = 6,
+  FIA_DT_INT8 = 7,
+  FIA_DT_BOOL = 8
+} fia_dtype;
+
+/* A strided view of device memory.  Unused trailing shape/stride slots are
+ * ignored.  data may be NULL only when the tensor holds zero elements. */
+typedef struct {
+  void* data;
+  int32_t dtype;      /* fia_dtype */
+  int32_t ndim;       /* 1..5 */
+  int64_t shape[5];
+  int64_t stride[5];  /* in elements */
+} fia_tensor;
+
+typedef struct fia_executor fia_executor;
+
+/* Attributes of the dense / paged operator (aclnnFusedInferAttentionScoreV5
+ * and V2 parameter lists, restricted to the supported feature groups). */
+typedef struct {
+  /* Layout of query and attention_out, and of key/value when not paged:
+   * "BSND" [B,S,N,D], "BSH" [B,S,N*D], "BNSD" [B,N,S,D] or "TND" [T,N,D].
+   * With TND the actual lengths are cumulative (V5 ActualSeqLen group). */
+  const char* input_layout;
+  int32_t num_heads;            /* Q_N, 1..256 */
+  int32_t num_key_value_heads;  /* KV_N; 0 means Q_N.  Q_N % KV_N == 0, Q_N/KV_N <= 64 */
+  double scale_value;           /* softmax scale, typically 1/sqrt(D) */
+  /* Mask mode (V5 Attention Mask group; V2 sparseMode rules):
+   *   0 all keys visible (no mask tensor)      2 left-up causal   j <= i
+   *   3 right-down causal j <= i + (Lk - Lq)    4 band:
+   *     i + (Lk-Lq) - pre_tokens <= j <= i + (Lk-Lq) + next_tokens
+   * Mode 1 needs an explicit mask tensor and is unsupported.  For modes 2-4
+   * the mask is generated from its definition; an atten_mask tensor, if
+   * passed, must be the 2048x2048 lower-triangular form and is not read. */
+  int32_t sparse_mode;
+  int64_t pre_tokens;           /* default 2147483647 */
+  int64_t next_tokens;          /* default 2147483647; -next_tokens <= pre_tokens */
+  /* pse_type 0: no positional bias (pse_shift must be NULL; an explicit bias
+   * tensor is unsupported).  pse_type 2: ALiBi, pse_shift is fp32 [Q_N]
+   * slopes and bias(h,i,j) = slope[h] * ((kv_start_idx + j) - (q_start_idx + i)),
+   * which requires S1 == S2 and equal per-batch lengths (V5 PSE group).
+   * pse_type 3 is unsupported (no formula on the pages); 1 is training-only. */
+  int32_t pse_type;
+  int64_t q_start_idx;          /* |kv_start_idx - q_start_idx| <= 1048576 */
+  int64_t kv_start_idx;
+  int32_t block_size;           /* paged KV only: > 0, multiple of 16, <= 1024 (<= 512 when S1 == 1 and D is not 64/128) */
+  int32_t inner_precise;        /* 0..3 accepted; softmax always runs in fp32 with invalid-row correction */
+  int32_t softmax_lse_flag;     /* 1: write softmax_lse */
+  /* Host arrays, copied during phase 1 (V2 actualSeqLengths / Kv).  NULL
+   * means every batch uses the tensor's S.  Length 1 broadcasts, length >= B
+   * uses the first B entries; TND requires exactly B cumulative entries. */
+  const int64_t* actual_seq_lengths;
+  int64_t actual_seq_lengths_len;
+  const int64_t* actual_seq_lengths_kv;
+  int64_t actual_seq_lengths_kv_len;
+} fia_params;
+
+/* Phase 1 of the dense / paged operator.
+ *   query           [B,S1,Q_N,D] (per input_layout), bf16 or fp32.
+ *   key, value      same layout [B,S2,KV_N,D]; or, when block_table is given,
+ *                   PA_ND pools [n_blocks, block_size, KV_N, D] (also accepted
+ *                   as [n_blocks, block_size, KV_N*D]); same dtype as query.
+ *                   key and value may be the same tensor.
+ *   pse_shift       NULL, or fp32 [Q_N] slopes when pse_type == 2.
+ *   atten_mask      NULL, or the 2048x2048 causal mask for modes 2-4 (unread).
+ *   block_table     NULL, or int32 [B, >= ceil(max Lk / block_size)]; requires
+ *                   actual_seq_lengths_kv (V5 Paged Attention group).
+ *   attention_out   same shape and layout as query, same dtype.
+ *   softmax_lse     fp32 [B,Q_N,S1,1] (TND: [T,Q_N,1]) when softmax_lse_flag,
+ *                   otherwise ignored (may be NULL).
+ * Rows past a batch's actual query length, and rows with no visible key, are
+ * written as 0 with LSE +inf (V4 empty-tensor rules; V2 invalid-row
+ * correction).  On success *executor must later be destroyed. */
+fia_status fia_get_workspace_size(const fia_params* params,
+                                  const fia_tensor* query, const fia_tensor* key,
+                                  const fia_tensor* value, const fia_tensor* pse_shift,
+                                  const fia_tensor* atten_mask, const fia_tensor* block_table,
+                                  const fia_tensor* attention_out, const fia_tensor* softmax_lse,
+                                  size_t* workspace_size, fia_executor** executor);
+
+/* Attributes of the shared-KV sparse decode operator (KvQuantSparseAttnSharedkv
+ * parameter table; sparse_flash_mla CSA mode). */
+typedef struct {
+  double softmax_scale;
+  int32_t kv_quant_mode;   /* 1: per-tile quantised nope (the only mode) */
+  int32_t tile_size;       /* 64 */
+  int32_t rope_head_dim;   /* 64 */
+  int32_t cmp_ratio;       /* 4 (compressed-sparse) or 1 when cmp_kv is absent */
+  int32_t ori_mask_mode;   /* 4 (band) */
+  int32_t cmp_mask_mode;   /* 3 (right-down causal) */
+  int32_t ori_win_left;    /* 127 */
+  int32_t ori_win_right;   /* 0 */
+  const char* layout_q;    /* "BSND" */
+  const char* layout_kv;   /* "PA_ND" */
+  int32_t return_softmax_lse; /* must be 0 (reserved on the page) */
+} fia_sparse_params;
+
+/* Phase 1 of the shared-KV sparse decode (query length 1).
+ *   q                  bf16 [B,1,N1,512], N1 in {64,128}; logical dim order
+ *                      [rope(64) | nope(448)].
+ *   ori_kv, cmp_kv     uint8 (or fp8_e4m3fn) PA_ND pools [n_blk, bs, 1, 640]:
+ *                      per row bf16 rope x64 | e4m3fn nope x448 | fp32 scale x7
+ *                      (one per 64-wide tile) | zero pad to 640 bytes.
+ *   ori_sparse_indices must be NULL (reserved on the page).
+ *   cmp_sparse_indices int32 [B,1,1,K2], K2 in {512,1024}; entry c is used
+ *                      iff 0 <= c < floor(Lk / cmp_ratio).
+ *   ori_block_table    int32 [B, >= ceil(max Lk / bs1)].
+ *   cmp_block_table    int32 [B, >= ceil(floor(max Lk / cmp_ratio) / bs2)].
+ *   seqused_kv         int32 [B] device, KV length per batch (Lk).
+ *   max_seqused_kv     host upper bound of seqused_kv, for table validation.
+ *   sinks              fp32 [N1]: one extra logit per head with a zero value.
+ *   metadata           ignored (the plan is built here), may be NULL.
+ *   attention_out      bf16 [B,1,N1,512].
+ * K~ = V~ = window rows of ori_kv followed by the selected cmp_kv rows. */
+fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
+                                         const fia_tensor* q, const fia_tensor* ori_kv,
+                                         const fia_tensor* cmp_kv,
+                                         const fia_tensor* ori_sparse_indices,
+                                         const fia_tensor* cmp_sparse_indices,
+                                         const fia_tensor* ori_block_table,
+                                         const fia_tensor* cmp_block_table,
+                                         const fia_tensor* seqused_kv, int64_t max_seqused_kv,
+                                         const fia_tensor* sinks, const fia_tensor* metadata,
+                                         const fia_tensor* attention_out,
+                                         size_t* workspace_size, fia_executor** executor);
+
+/* Phase 2: enqueue the planned work on `stream` (a hipStream_t; NULL is the
+ * default stream).  `workspace` is device memory of at least the size phase 1
+ * returned (may be NULL when that size is 0); it is scratch and its contents
+ * need not survive between calls.  Asynchronous: returns after enqueueing. */
+fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* executor,
+                   void* stream);
+
+/* Release an executor (NULL is ignored). */
+void fia_executor_destroy(fia_executor* executor);
+
+/* Message describing the last non-success status returned on this thread. */
+const char* fia_last_error(void);
+
+/* Which kernel path an executor takes: 0 fill-only (empty input),
+ * 1 prompt (prefill), 2 incremental decode (split-KV), 3 shared-KV sparse,
+ * 4 fp32 reference-precision path. */
+int32_t fia_executor_kind(const fia_executor* executor);
+
+/* Test support: gather through the same device address function the decode
+ * and prefill kernels use.  Writes key (which = 0) or value (which = 1) rows
+ * 0..Lk_b-1 of every batch into dst, a dense [B, S2max, KV_N, D] buffer of
+ * the key dtype (S2max = max Lk); rows past Lk_b are left untouched. */
+fia_status fia_debug_gather_kv(fia_executor* executor, void* workspace, size_t workspace_size,
+                               int32_t which, void* dst, void* stream);
+
+/* Test support for the sparse executor: for every batch, the row list the
+ * kernel attends to, as fixed slots [B, n_slots]: ids_out[b, s] = j for window
+ * row j of ori_kv, (1 << 30) | c for row c of cmp_kv, -1 for an unused slot;
+ * rows_out[b, s, 0..639] = the raw packed bytes of that row (zero when
+ * unused).  n_slots is returned through *n_slots_out (ids_out may be NULL to
+ * query it). */
+fia_status fia_debug_sparse_rows(fia_executor* executor, void* workspace, size_t workspace_size,
+                                 int32_t* ids_out, uint8_t* rows_out, int32_t* n_slots_out,
+                                 void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FIA_H_ */

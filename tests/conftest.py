@@ -10,3 +10,13 @@ if ROOT not in sys.path:
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on stderr before it touches the device, so a run
+    that dies mid-test still says which case was running."""
+    if request.node.get_closest_marker("gpu") is not None:
+        sys.__stderr__.write(f"\n[gpu case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,362 @@
+"""Host-side tests of libfia.so: it loads, exports every entry point the
+header declares, and phase 1 applies the pages' constraint tiers.  Phase 1
+never touches the GPU, so descriptors carry fake (aligned, never
+dereferenced) device addresses."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from attention_online_softmax_flash_amd import fia
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x7F0000000000
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fia.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(fia_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    L = fia.lib()
+    names = header_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(fia.EXPORTED) == names
+
+
+def T(shape, dtype=fia.DT_BF16, data=FAKE, strides=None):
+    d = fia.FiaTensor()
+    d.data = data
+    d.dtype = dtype
+    d.ndim = len(shape)
+    if strides is None:
+        strides, acc = [], 1
+        for s in reversed(shape):
+            strides.insert(0, acc)
+            acc *= s
+    for i, (s, st) in enumerate(zip(shape, strides)):
+        d.shape[i] = s
+        d.stride[i] = st
+    return d
+
+
+def P(**kw):
+    p = fia.FiaParams()
+    p.input_layout = kw.pop("layout", "BSND").encode()
+    p.num_heads = kw.pop("num_heads", 4)
+    p.num_key_value_heads = kw.pop("num_kv_heads", 0)
+    p.scale_value = kw.pop("scale", 0.125)
+    p.sparse_mode = kw.pop("sparse_mode", 0)
+    p.pre_tokens = kw.pop("pre_tokens", 2147483647)
+    p.next_tokens = kw.pop("next_tokens", 2147483647)
+    p.pse_type = kw.pop("pse_type", 0)
+    p.q_start_idx = kw.pop("q_start_idx", 0)
+    p.kv_start_idx = kw.pop("kv_start_idx", 0)
+    p.block_size = kw.pop("block_size", 0)
+    p.inner_precise = kw.pop("inner_precise", 0)
+    p.softmax_lse_flag = kw.pop("lse", 0)
+    keep = []
+    for name in ("actual_seq_lengths", "actual_seq_lengths_kv"):
+        vals = kw.pop(name, None)
+        if vals is not None:
+            arr = (ctypes.c_int64 * len(vals))(*vals)
+            keep.append(arr)
+            setattr(p, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
+            setattr(p, name + "_len", len(vals))
+    assert not kw, kw
+    p._keep = keep
+    return p
+
+
+def plan(p, q, k, v, out, pse=None, mask=None, bt=None, lse=None):
+    ws = ctypes.c_size_t(0)
+    ex = ctypes.c_void_p(None)
+    ptr = lambda d: ctypes.pointer(d) if d is not None else None
+    st = fia.lib().fia_get_workspace_size(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(pse),
+                                          ptr(mask), ptr(bt), ptr(out), ptr(lse),
+                                          ctypes.byref(ws), ctypes.byref(ex))
+    msg = fia.lib().fia_last_error().decode()
+    kind = None
+    if st == 0:
+        kind = fia.KIND_NAMES[fia.lib().fia_executor_kind(ex)]
+        fia.lib().fia_executor_destroy(ex)
+    return st, kind, ws.value, msg
+
+
+def dense(B=2, S1=64, S2=64, N=4, KVN=2, D=128, dt=fia.DT_BF16):
+    q = T((B, S1, N, D), dt)
+    return q, T((B, S2, KVN, D), dt), T((B, S2, KVN, D), dt), T((B, S1, N, D), dt)
+
+
+def test_valid_calls_classify_branches():
+    q, k, v, o = dense()
+    st, kind, ws, msg = plan(P(num_kv_heads=2, sparse_mode=3), q, k, v, o)
+    assert st == 0 and kind == "prefill", msg
+    q1, k1, v1, o1 = dense(S1=1, S2=300)
+    st, kind, ws, msg = plan(P(num_kv_heads=2), q1, k1, v1, o1)
+    assert st == 0 and kind == "decode" and ws > 0, msg
+    q3, k3, v3, o3 = dense(D=64, dt=fia.DT_FP32)
+    st, kind, _, msg = plan(P(num_kv_heads=2), q3, k3, v3, o3)
+    assert st == 0 and kind == "fp32", msg
+    qe, ke, ve, oe = dense(S2=0)
+    st, kind, _, msg = plan(P(num_kv_heads=2), qe, ke, ve, oe)
+    assert st == 0 and kind == "fill", msg
+
+
+def test_paged_decode_plan_and_workspace_grows_with_lengths():
+    q = T((3, 1, 8, 128))
+    o = T((3, 1, 8, 128))
+    pool = T((20, 128, 2, 128))
+    bt = T((3, 8), fia.DT_INT32)
+    st, kind, ws1, msg = plan(P(num_heads=8, num_kv_heads=2, block_size=128,
+                                actual_seq_lengths_kv=[100, 200, 300]), q, pool, pool, o, bt=bt)
+    assert st == 0 and kind == "decode", msg
+    st, kind, ws2, msg = plan(P(num_heads=8, num_kv_heads=2, block_size=128,
+                                actual_seq_lengths_kv=[1000, 1000, 1000]), q, pool, pool, o, bt=bt)
+    assert st == 0 and ws2 > ws1, msg
+
+
+BAD = fia.FIA_ERR_PARAM_INVALID
+UNS = fia.FIA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("desc,kw,expect", [
+    ("Q_N not a multiple of KV_N", dict(num_heads=4, num_kv_heads=3), BAD),
+    ("group ratio above 64", dict(num_heads=130, num_kv_heads=2), BAD),
+    ("sparse_mode out of range", dict(sparse_mode=5), BAD),
+    ("sparse_mode negative", dict(sparse_mode=-1), BAD),
+    ("sparse_mode 1 needs a mask tensor", dict(sparse_mode=1), UNS),
+    ("band with -next > pre", dict(sparse_mode=4, pre_tokens=-3, next_tokens=2), BAD),
+    ("pse_type out of range", dict(pse_type=4), BAD),
+    ("pse_type 1 is training only", dict(pse_type=1), BAD),
+    ("pse_type 3 unsupported", dict(pse_type=3), UNS),
+    ("pse_type 2 without pse_shift", dict(pse_type=2), BAD),
+    ("inner_precise out of range", dict(inner_precise=4), BAD),
+    ("lse flag without lse tensor", dict(lse=1), BAD),
+    ("negative actual length", dict(actual_seq_lengths=[-1, 3]), BAD),
+    ("actual length above S", dict(actual_seq_lengths=[65, 3]), BAD),
+    ("kv length above S2", dict(actual_seq_lengths_kv=[70, 3]), BAD),
+])
+def test_phase1_rejects(desc, kw, expect):
+    q, k, v, o = dense(N=kw.get("num_heads", 4), KVN=kw.get("num_kv_heads", 2) or 4)
+    kw.setdefault("num_kv_heads", 2)
+    st, _, _, msg = plan(P(**kw), q, k, v, o)
+    assert st == expect, (desc, st, msg)
+    assert msg
+
+
+def test_length_array_size_rule():
+    q, k, v, o = dense(B=3)
+    st, _, _, msg = plan(P(num_kv_heads=2, actual_seq_lengths=[5, 6]), q, k, v, o)
+    assert st == BAD and "length" in msg
+    st, _, _, msg = plan(P(num_kv_heads=2, actual_seq_lengths=[5]), q, k, v, o)
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_kv_heads=2, actual_seq_lengths=[5, 6, 7, 8]), q, k, v, o)
+    assert st == 0, msg
+
+
+def test_alibi_rules():
+    q, k, v, o = dense(S1=64, S2=64)
+    slopes = T((4,), fia.DT_FP32)
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2), q, k, v, o, pse=slopes)
+    assert st == 0, msg
+    q2, k2, v2, o2 = dense(S1=32, S2=64)
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2), q2, k2, v2, o2, pse=slopes)
+    assert st == BAD and "Q_S" in msg
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2, actual_seq_lengths=[10, 20],
+                           actual_seq_lengths_kv=[10, 21]), q, k, v, o, pse=slopes)
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2, kv_start_idx=1048577), q, k, v, o, pse=slopes)
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2), q, k, v, o, pse=T((3,), fia.DT_FP32))
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2), q, k, v, o, pse=T((4,), fia.DT_BF16))
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=0), q, k, v, o, pse=T((2, 4, 64, 64)))
+    assert st == UNS
+
+
+def test_mask_tensor_rules():
+    q, k, v, o = dense()
+    good = T((2048, 2048), fia.DT_BOOL)
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=3), q, k, v, o, mask=good)
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=3), q, k, v, o, mask=T((1, 1, 2048, 2048), fia.DT_UINT8))
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=3), q, k, v, o, mask=T((1024, 1024), fia.DT_BOOL))
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=3), q, k, v, o, mask=T((2048, 2048), fia.DT_FP32))
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q, k, v, o, mask=good)
+    assert st == UNS
+
+
+def test_paged_rules():
+    q = T((2, 1, 4, 128))
+    o = T((2, 1, 4, 128))
+    pool = T((10, 128, 2, 128))
+    bt = T((2, 4), fia.DT_INT32)
+    ok = dict(num_heads=4, num_kv_heads=2, block_size=128, actual_seq_lengths_kv=[300, 500])
+    st, _, _, msg = plan(P(**ok), q, pool, pool, o, bt=bt)
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_heads=4, num_kv_heads=2, block_size=128), q, pool, pool, o, bt=bt)
+    assert st == BAD and "actual_seq_lengths_kv" in msg
+    st, _, _, msg = plan(P(**dict(ok, block_size=0)), q, pool, pool, o, bt=bt)
+    assert st == BAD
+    st, _, _, msg = plan(P(**dict(ok, block_size=100)), q, T((10, 100, 2, 128)), T((10, 100, 2, 128)), o, bt=bt)
+    assert st == BAD
+    st, _, _, msg = plan(P(**dict(ok, block_size=2048)), q, T((10, 2048, 2, 128)), T((10, 2048, 2, 128)), o, bt=bt)
+    assert st == BAD
+    st, _, _, msg = plan(P(**ok), q, pool, pool, o, bt=T((3, 4), fia.DT_INT32))
+    assert st == BAD
+    st, _, _, msg = plan(P(**ok), q, pool, pool, o, bt=T((2, 3), fia.DT_INT32))
+    assert st == BAD
+    st, _, _, msg = plan(P(**ok), q, pool, pool, o, bt=T((2, 4), fia.DT_INT64))
+    assert st == BAD
+    st, _, _, msg = plan(P(**ok), q, pool, pool, o, bt=T((8,), fia.DT_INT32))
+    assert st == BAD
+    st, _, _, msg = plan(P(**ok), q, T((10, 64, 2, 128)), T((10, 64, 2, 128)), o, bt=bt)
+    assert st == BAD
+    st, kind, _, msg = plan(P(**ok), q, T((10, 128, 256)), T((10, 128, 256)), o, bt=bt)
+    assert st == 0 and kind == "decode", msg
+
+
+def test_tnd_rules():
+    q = T((10, 4, 128))
+    o = T((10, 4, 128))
+    k = T((12, 2, 128))
+    st, kind, _, msg = plan(P(layout="TND", num_kv_heads=2, actual_seq_lengths=[4, 10],
+                              actual_seq_lengths_kv=[5, 12]), q, k, k, o)
+    assert st == 0 and kind == "prefill", msg
+    st, _, _, msg = plan(P(layout="TND", num_kv_heads=2, actual_seq_lengths=[4, 9],
+                           actual_seq_lengths_kv=[5, 12]), q, k, k, o)
+    assert st == BAD and "T" in msg
+    st, _, _, msg = plan(P(layout="TND", num_kv_heads=2, actual_seq_lengths=[6, 4, 10],
+                           actual_seq_lengths_kv=[5, 6, 12]), q, k, k, o)
+    assert st == BAD and "non-decreasing" in msg
+    st, _, _, msg = plan(P(layout="TND", num_kv_heads=2, actual_seq_lengths_kv=[5, 12]), q, k, k, o)
+    assert st == BAD
+
+
+def test_lse_shape_rules():
+    q, k, v, o = dense()
+    st, _, _, msg = plan(P(num_kv_heads=2, lse=1), q, k, v, o, lse=T((2, 4, 64, 1), fia.DT_FP32))
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_kv_heads=2, lse=1), q, k, v, o, lse=T((2, 4, 64, 1), fia.DT_BF16))
+    assert st == BAD
+    st, _, _, msg = plan(P(num_kv_heads=2, lse=1), q, k, v, o, lse=T((2, 4, 64), fia.DT_FP32))
+    assert st == BAD
+
+
+def test_shape_limits_and_unsupported():
+    q, k, v, o = dense(D=96)
+    st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o)
+    assert st == UNS
+    q, k, v, o = dense(dt=fia.DT_FP16)
+    st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o)
+    assert st == UNS
+    q, k, v, o = dense(N=257, KVN=257)
+    st, _, _, msg = plan(P(num_heads=257, num_kv_heads=257), q, k, v, o)
+    assert st == BAD
+    q, k, v, o = dense()
+    st, _, _, msg = plan(P(num_kv_heads=2, layout="NSD"), q, k, v, o)
+    assert st == BAD
+    q, k, v, o = dense()
+    q.data = FAKE + 2
+    st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o)
+    assert st == UNS and "aligned" in msg
+    q, k, v, o = dense()
+    st, _, _, msg = plan(P(num_kv_heads=2), q, k, T((2, 64, 2, 128), fia.DT_FP32), o)
+    assert st == BAD
+    q, k, v, o = dense()
+    q.data = None
+    st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o)
+    assert st == fia.FIA_ERR_NULLPTR
+
+
+def test_null_arguments_and_run_errors():
+    L = fia.lib()
+    ws = ctypes.c_size_t(0)
+    ex = ctypes.c_void_p(None)
+    st = L.fia_get_workspace_size(None, None, None, None, None, None, None, None, None,
+                                  ctypes.byref(ws), ctypes.byref(ex))
+    assert st == fia.FIA_ERR_NULLPTR
+    assert L.fia_run(None, 0, None, None) == fia.FIA_ERR_NULLPTR
+    L.fia_executor_destroy(None)
+    # A workspace smaller than required is rejected before any HIP call.
+    q, k, v, o = dense(S1=1, S2=2000)
+    p = P(num_kv_heads=2)
+    ptr = lambda d: ctypes.pointer(d)
+    st = L.fia_get_workspace_size(ctypes.byref(p), ptr(q), ptr(k), ptr(v), None, None, None,
+                                  ptr(o), None, ctypes.byref(ws), ctypes.byref(ex))
+    assert st == 0 and ws.value > 0
+    assert L.fia_run(None, ws.value, ex, None) == fia.FIA_ERR_WORKSPACE
+    assert L.fia_run(FAKE, ws.value - 1, ex, None) == fia.FIA_ERR_WORKSPACE
+    L.fia_executor_destroy(ex)
+
+
+def sparse_plan_status(**over):
+    B, N1 = 2, 64
+    t = dict(q=T((B, 1, N1, 512)), ori=T((32, 128, 1, 640), fia.DT_UINT8),
+             cmp=T((16, 128, 1, 640), fia.DT_UINT8), idx=T((B, 1, 1, 512), fia.DT_INT32),
+             obt=T((B, 16), fia.DT_INT32), cbt=T((B, 4), fia.DT_INT32),
+             seq=T((B,), fia.DT_INT32), sinks=T((N1,), fia.DT_FP32), out=T((B, 1, N1, 512)),
+             oidx=None, max_seq=2048)
+    p = fia.FiaSparseParams()
+    p.softmax_scale = 0.0441941738
+    p.kv_quant_mode, p.tile_size, p.rope_head_dim, p.cmp_ratio = 1, 64, 64, 4
+    p.ori_mask_mode, p.cmp_mask_mode, p.ori_win_left, p.ori_win_right = 4, 3, 127, 0
+    p.layout_q, p.layout_kv, p.return_softmax_lse = b"BSND", b"PA_ND", 0
+    for key, val in over.items():
+        if hasattr(p, key) and key not in t:
+            setattr(p, key, val)
+        else:
+            t[key] = val
+    ws = ctypes.c_size_t(0)
+    ex = ctypes.c_void_p(None)
+    ptr = lambda d: ctypes.pointer(d) if d is not None else None
+    st = fia.lib().fia_sparse_get_workspace_size(
+        ctypes.byref(p), ptr(t["q"]), ptr(t["ori"]), ptr(t["cmp"]), ptr(t["oidx"]), ptr(t["idx"]),
+        ptr(t["obt"]), ptr(t["cbt"]), ptr(t["seq"]), t["max_seq"], ptr(t["sinks"]), None,
+        ptr(t["out"]), ctypes.byref(ws), ctypes.byref(ex))
+    msg = fia.lib().fia_last_error().decode()
+    if st == 0:
+        assert fia.KIND_NAMES[fia.lib().fia_executor_kind(ex)] == "sparse"
+        fia.lib().fia_executor_destroy(ex)
+    return st, msg
+
+
+@pytest.mark.parametrize("over,expect", [
+    ({}, 0),
+    (dict(cmp=None, idx=None, cbt=None, cmp_ratio=1), 0),
+    (dict(q=T((2, 1, 64, 576)), out=T((2, 1, 64, 576))), BAD),
+    (dict(q=T((2, 1, 32, 512)), out=T((2, 1, 32, 512)), sinks=T((32,), fia.DT_FP32)), BAD),
+    (dict(tile_size=32), BAD),
+    (dict(rope_head_dim=32), BAD),
+    (dict(kv_quant_mode=0), BAD),
+    (dict(ori_win_left=63), BAD),
+    (dict(ori_win_right=1), BAD),
+    (dict(ori_mask_mode=3), BAD),
+    (dict(cmp_mask_mode=4), BAD),
+    (dict(cmp_ratio=128), UNS),
+    (dict(cmp_ratio=2), BAD),
+    (dict(idx=T((2, 1, 1, 256), fia.DT_INT32)), BAD),
+    (dict(oidx=T((2, 1, 1, 512), fia.DT_INT32)), BAD),
+    (dict(ori=T((32, 100, 1, 640), fia.DT_UINT8)), BAD),
+    (dict(ori=T((32, 128, 1, 656), fia.DT_UINT8)), BAD),
+    (dict(obt=T((2, 15), fia.DT_INT32)), BAD),
+    (dict(cbt=T((2, 3), fia.DT_INT32)), BAD),
+    (dict(return_softmax_lse=1), BAD),
+    (dict(layout_q=b"TND"), UNS),
+    (dict(layout_kv=b"BSND"), BAD),
+    (dict(sinks=T((64,), fia.DT_BF16)), BAD),
+    (dict(q=T((2, 2, 64, 512)), out=T((2, 2, 64, 512)), idx=T((2, 2, 1, 512), fia.DT_INT32)), UNS),
+])
+def test_sparse_phase1(over, expect):
+    st, msg = sparse_plan_status(**over)
+    assert st == expect, (over, msg)

@@ -1,0 +1,377 @@
+"""GPU parity: the HIP library (through the C ABI) against the float64 oracle
+on identical seeded inputs, at the bar of the parity contract:
+bf16 outputs |gpu - ref| <= 1e-2 + 1e-2 |ref|, LSE within 1e-3 absolute with
++inf matching exactly, gathers and sparse row selection bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+from attention_online_softmax_flash_amd import fia
+from attention_online_softmax_flash_amd import torch_io as TI
+from attention_online_softmax_flash_amd import workloads as W
+from oracle import fia_oracle as O
+from parity import check_lse, check_out, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def run_plan(plan):
+    plan.run()
+    torch.cuda.synchronize()
+    return plan
+
+
+def gpu_results(plan):
+    out = to_f64(plan.out)
+    lse = None if plan.lse is None else to_f64(plan.lse)[..., 0]
+    return out, lse
+
+
+def dense_parity(case, expect_kind=None, rows=None, heads=None, **over):
+    plan = run_plan(TI.dense_plan(case, DEV, **over))
+    if expect_kind:
+        assert plan.kind == expect_kind
+    out, lse = gpu_results(plan)
+    ref_o, ref_l = O.fia_case(case, rows=rows, heads=heads)
+    if rows is None and heads is None:
+        check_out(out, ref_o)
+        if lse is not None:
+            check_lse(lse, ref_l)
+    else:
+        hs = list(range(case.num_heads)) if heads is None else list(heads)
+        rs = list(range(case.q.shape[1])) if rows is None else list(rows)
+        sel_o = np.ix_(range(out.shape[0]), rs, hs, range(out.shape[3]))
+        check_out(out[sel_o], ref_o[sel_o])
+        if lse is not None:
+            sel_l = np.ix_(range(out.shape[0]), hs, rs)
+            check_lse(lse[sel_l], ref_l[sel_l])
+    return plan, out, lse
+
+
+# ---------------------------------------------------------------------------
+# The five workloads at full size.
+# ---------------------------------------------------------------------------
+def test_c1_tiny_dense_fp32():
+    case = W.c1_tiny_dense()
+    plan, out, lse = dense_parity(case, "fp32")
+    ref_o, ref_l = O.fia_case(case)
+    # stretch bound for the fp32 path
+    check_out(out, ref_o, atol=1e-4, rtol=1e-4)
+    check_lse(lse, ref_l, atol=1e-4)
+
+
+def test_c2_causal_gqa_prefill_full_with_nan_padding():
+    case = W.c2_causal_gqa(poison_pad=True, lse=True)
+    plan, out, lse = dense_parity(case, "prefill")
+    for b, L in enumerate(case.actual_seq_lengths):
+        assert np.all(out[b, L:] == 0.0)
+        assert np.all(np.isposinf(lse[b, :, L:]))
+
+
+def test_c3_paged_decode_full_with_nan_tails():
+    case = W.c3_paged_decode(poison_tail=True)
+    dense_parity(case, "decode")
+
+
+def test_c4_long_alibi_prefill_sampled():
+    case = W.c4_alibi_prefill(lse=True)
+    rng = np.random.default_rng(4)
+    rows = sorted(set(list(range(0, 130)) + rng.integers(0, 8192, 64).tolist() +
+                      list(range(8192 - 130, 8192))))
+    dense_parity(case, "prefill", rows=rows, heads=[0, 7, 15])
+
+
+def test_c5_sparse_sharedkv_full():
+    case = W.c5_sparse_sharedkv()
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    assert plan.kind == "sparse"
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
+# ---------------------------------------------------------------------------
+# Small sweeps: several tiles, ragged tails, every mask mode.
+# ---------------------------------------------------------------------------
+PREFILL_CASES = [
+    # (B, S1, S2, Qn, KVn, D, mode, pre, nxt, q_lens, kv_lens, alibi)
+    (2, 200, 200, 4, 4, 128, 0, None, None, None, None, False),
+    (2, 200, 200, 8, 2, 128, 2, None, None, [200, 77], [200, 77], False),
+    (2, 200, 300, 8, 2, 128, 3, None, None, [130, 1], [300, 129], False),
+    (1, 257, 257, 4, 1, 128, 3, None, None, None, None, True),
+    (2, 190, 190, 4, 4, 64, 3, None, None, [190, 65], [190, 65], True),
+    (2, 160, 220, 4, 2, 128, 4, 40, 3, [160, 100], [220, 90], False),
+    (1, 300, 100, 2, 2, 64, 3, None, None, None, None, False),
+    (1, 150, 150, 4, 4, 128, 4, 0, 0, None, None, False),
+    (3, 129, 129, 16, 2, 128, 2, None, None, [129, 0, 64], [129, 5, 64], False),
+    (1, 64, 513, 8, 8, 64, 0, None, None, None, None, False),
+    (2, 140, 140, 6, 3, 128, 4, 2147483647, 0, None, None, False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PREFILL_CASES)))
+def test_prefill_sweep(i):
+    B, S1, S2, Qn, KVn, D, mode, pre, nxt, ql, kl, alibi = PREFILL_CASES[i]
+    kw = {}
+    if pre is not None:
+        kw.update(pre_tokens=pre, next_tokens=nxt)
+    case = W.dense_case(f"pre{i}", 100 + i, B=B, S1=S1, S2=S2, Q_N=Qn, KV_N=KVn, D=D,
+                        sparse_mode=mode, q_lens=ql, kv_lens=kl, alibi=alibi, lse=True,
+                        poison_pad=True, **kw)
+    dense_parity(case, "prefill")
+
+
+def test_prefill_alibi_start_offsets():
+    case = W.dense_case("alibi_off", 120, B=1, S1=140, S2=140, Q_N=4, KV_N=4, D=128,
+                        sparse_mode=3, alibi=True, lse=True, q_start_idx=7, kv_start_idx=300)
+    dense_parity(case, "prefill")
+
+
+@pytest.mark.parametrize("layout", ["BNSD", "BSH"])
+def test_prefill_other_layouts(layout):
+    case = W.dense_case("lay", 130, B=2, S1=150, S2=150, Q_N=8, KV_N=2, D=128, sparse_mode=3,
+                        lse=True)
+    q, k, v, bt, slopes = TI.dense_tensors(case, DEV)
+    if layout == "BNSD":
+        tq, tk, tv = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+    else:
+        tq, tk, tv = (x.reshape(x.shape[0], x.shape[1], -1).contiguous() for x in (q, k, v))
+    plan = run_plan(fia.AttentionPlan(tq, tk, tv, num_heads=8, num_key_value_heads=2,
+                                      scale_value=case.scale, input_layout=layout,
+                                      sparse_mode=3, softmax_lse_flag=True))
+    out = plan.out.permute(0, 2, 1, 3) if layout == "BNSD" else plan.out.reshape(q.shape)
+    ref_o, ref_l = O.fia_case(case)
+    check_out(to_f64(out), ref_o)
+    check_lse(to_f64(plan.lse)[..., 0], ref_l)
+
+
+def test_prefill_tnd():
+    case = W.tnd_case("tnd", 140, q_lens=[100, 0, 257, 1], kv_lens=[100, 3, 300, 50],
+                      Q_N=8, KV_N=4, D=128, sparse_mode=3, lse=True)
+    dense_parity(case, "prefill")
+
+
+def test_prefill_over_paged_kv():
+    case = W.paged_decode_case("pp", 150, B=3, Q_N=8, KV_N=2, D=128, kv_lens=[300, 70, 513],
+                               block_size=64, S1=70, sparse_mode=3, lse=True, poison_tail=True,
+                               extra_blocks=3)
+    case.actual_seq_lengths = [70, 70, 70]
+    dense_parity(case, "prefill")
+
+
+DECODE_CASES = [
+    # (B, Qn, KVn, D, kv_lens, block_size or None (dense), mode, pre, nxt)
+    (3, 32, 8, 128, [1, 511, 1300], 128, 0, None, None),
+    (2, 8, 8, 128, [512, 513], 16, 3, None, None),
+    (2, 16, 1, 128, [2048 + 7, 100], 64, 0, None, None),
+    (2, 32, 1, 128, [700, 3], 512, 0, None, None),
+    (1, 64, 1, 128, [1500], 128, 0, None, None),
+    (2, 4, 2, 64, [999, 40], 32, 0, None, None),
+    (3, 8, 2, 128, [0, 600, 17], 128, 0, None, None),
+    (2, 8, 2, 128, [900, 300], None, 0, None, None),
+    (2, 8, 2, 128, [900, 300], 128, 2, None, None),
+    (2, 8, 2, 128, [900, 300], 128, 4, 100, 0),
+    (2, 8, 2, 128, [2000, 300], 128, 4, 1500, 5),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DECODE_CASES)))
+def test_decode_sweep(i):
+    B, Qn, KVn, D, lens, bs, mode, pre, nxt = DECODE_CASES[i]
+    if bs is None:
+        S2 = max(lens)
+        case = W.dense_case(f"dec{i}", 200 + i, B=B, S1=1, S2=S2, Q_N=Qn, KV_N=KVn, D=D,
+                            sparse_mode=mode, kv_lens=lens, lse=True, poison_pad=True)
+    else:
+        case = W.paged_decode_case(f"dec{i}", 200 + i, B=B, Q_N=Qn, KV_N=KVn, D=D, kv_lens=lens,
+                                   block_size=bs, lse=True, poison_tail=True, sparse_mode=mode,
+                                   extra_blocks=2, table_cols=(max(lens) + bs - 1) // bs + 1)
+    if pre is not None:
+        case.pre_tokens, case.next_tokens = pre, nxt
+    dense_parity(case, "decode")
+
+
+def test_decode_tnd():
+    case = W.tnd_case("dtnd", 240, q_lens=[1, 1, 0, 1], kv_lens=[600, 5, 100, 1029], Q_N=8,
+                      KV_N=2, D=128, lse=True)
+    dense_parity(case, "decode")
+
+
+FP32_CASES = [
+    (2, 70, 70, 4, 2, 64, 3, None, None, [70, 33], [70, 33], True),
+    (1, 40, 90, 2, 1, 128, 4, 10, 2, None, None, False),
+    (2, 1, 300, 4, 4, 32, 0, None, None, None, [300, 0], False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(FP32_CASES)))
+def test_fp32_sweep(i):
+    B, S1, S2, Qn, KVn, D, mode, pre, nxt, ql, kl, alibi = FP32_CASES[i]
+    kw = {} if pre is None else dict(pre_tokens=pre, next_tokens=nxt)
+    case = W.dense_case(f"f32_{i}", 300 + i, B=B, S1=S1, S2=S2, Q_N=Qn, KV_N=KVn, D=D,
+                        dtype="fp32", sparse_mode=mode, q_lens=ql, kv_lens=kl, alibi=alibi,
+                        lse=True, poison_pad=True, **kw)
+    plan, out, lse = dense_parity(case, "fp32")
+    ref_o, ref_l = O.fia_case(case)
+    check_out(out, ref_o, atol=1e-4, rtol=1e-4)
+
+
+def test_empty_kv_fills_zero_and_inf():
+    case = W.dense_case("empty", 310, B=2, S1=5, S2=0, Q_N=4, KV_N=2, D=128, lse=True)
+    plan = run_plan(TI.dense_plan(case, DEV))
+    assert plan.kind == "fill"
+    out, lse = gpu_results(plan)
+    assert np.all(out == 0) and np.all(np.isposinf(lse))
+
+
+# ---------------------------------------------------------------------------
+# Shared-KV sparse decode sweep.
+# ---------------------------------------------------------------------------
+SPARSE_CASES = [
+    # (B, N1, lens, K2, n_valid)
+    (3, 64, [1, 5, 130], 512, None),
+    (2, 128, [1000, 4096], 1024, None),
+    (2, 64, [2000, 300], 512, 17),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SPARSE_CASES)))
+def test_sparse_sweep(i):
+    B, N1, lens, K2, nv = SPARSE_CASES[i]
+    case = W.sparse_case(f"sp{i}", 400 + i, B=B, N1=N1, seqused_kv=lens, K2=K2, n_valid=nv,
+                         block_size1=64, block_size2=32, materialise_all_ori=False)
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
+def test_sparse_window_only():
+    case = W.sparse_case("swa", 410, B=2, N1=64, seqused_kv=[300, 50], K2=512,
+                         materialise_all_ori=False)
+    t = TI.sparse_tensors(case, DEV)
+    plan = run_plan(fia.SparsePlan(t["q"], t["ori_kv"], None, None, t["ori_block_table"], None,
+                                   t["seqused_kv"], t["sinks"], softmax_scale=case.softmax_scale,
+                                   max_seqused_kv=300, cmp_ratio=1))
+    case.cmp_sparse_indices[...] = -1
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
+# ---------------------------------------------------------------------------
+# Bit-exact gathers and row selection.
+# ---------------------------------------------------------------------------
+def test_paged_gather_is_bit_exact():
+    case = W.paged_decode_case("g", 500, B=3, Q_N=8, KV_N=2, D=128, kv_lens=[1, 300, 1029],
+                               block_size=16, poison_tail=True, extra_blocks=4)
+    plan = TI.dense_plan(case, DEV)
+    s2 = max(case.actual_seq_lengths_kv)
+    for which, pool in ((0, case.k_pool), (1, case.v_pool)):
+        got = plan.debug_gather(which, s2)
+        torch.cuda.synchronize()
+        got = got.cpu().view(torch.int16).numpy().view(np.uint16)
+        for b, L in enumerate(case.actual_seq_lengths_kv):
+            j = np.arange(L)
+            want = pool[case.block_table[b, j // 16], j % 16]
+            assert np.array_equal(got[b, :L], want), (which, b)
+
+
+def test_sparse_row_selection_is_bit_exact():
+    case = W.sparse_case("sr", 510, B=3, N1=64, seqused_kv=[5, 300, 4000], K2=512, n_valid=100,
+                         block_size1=32, block_size2=16, materialise_all_ori=False)
+    case.cmp_sparse_indices[1, 0, 0, 3] = 10 ** 6      # out of range: must be skipped
+    plan = TI.sparse_plan(case, DEV)
+    ids, rows = plan.debug_rows()
+    torch.cuda.synchronize()
+    ids, rows = ids.cpu().numpy(), rows.cpu().numpy()
+    n_win = 128
+    for b, L in enumerate(case.seqused_kv):
+        win, comp = O.sparse_rows(L, 1, 0, case.cmp_sparse_indices[b, 0, 0], cmp_ratio=4,
+                                  win_left=127, win_right=0)
+        got_win = [int(x) for x in ids[b, :n_win] if x >= 0]
+        assert got_win == win
+        got_comp = [int(x) & ((1 << 30) - 1) for x in ids[b, n_win:] if x >= 0]
+        assert got_comp == comp
+        for s in range(ids.shape[1]):
+            x = int(ids[b, s])
+            if x < 0:
+                assert not rows[b, s].any()
+            elif x >> 30:
+                c = x & ((1 << 30) - 1)
+                want = case.cmp_kv[case.cmp_block_table[b, c // 16], c % 16, 0]
+                assert np.array_equal(rows[b, s], want)
+            else:
+                want = case.ori_kv[case.ori_block_table[b, x // 32], x % 32, 0]
+                assert np.array_equal(rows[b, s], want)
+
+
+# ---------------------------------------------------------------------------
+# Determinism and batch invariance.
+# ---------------------------------------------------------------------------
+def test_repeat_runs_are_bitwise_identical():
+    case = W.paged_decode_case("det", 600, B=4, Q_N=32, KV_N=8, D=128,
+                               kv_lens=[3000, 17, 1200, 4097], block_size=128)
+    plan = run_plan(TI.dense_plan(case, DEV))
+    first = plan.out.clone()
+    first_lse = plan.lse.clone()
+    for _ in range(3):
+        run_plan(plan)
+        assert torch.equal(plan.out, first) and torch.equal(plan.lse, first_lse)
+    pc = W.dense_case("detp", 601, B=2, S1=300, S2=300, Q_N=8, KV_N=2, D=128, sparse_mode=3)
+    pp = run_plan(TI.dense_plan(pc, DEV))
+    f2 = pp.out.clone()
+    run_plan(pp)
+    assert torch.equal(pp.out, f2)
+    sc = W.sparse_case("dets", 602, B=2, N1=64, seqused_kv=[5000, 700], K2=512,
+                       materialise_all_ori=False)
+    sp = run_plan(TI.sparse_plan(sc, DEV))
+    f3 = sp.out.clone()
+    run_plan(sp)
+    assert torch.equal(sp.out, f3)
+
+
+def test_decode_batch_invariance():
+    lens = [4100, 90, 2500, 7000]
+    case = W.dense_case("bi", 610, B=4, S1=1, S2=max(lens), Q_N=16, KV_N=4, D=128, kv_lens=lens,
+                        lse=True)
+    q, k, v, _, _ = TI.dense_tensors(case, DEV)
+    full = run_plan(fia.AttentionPlan(q, k, v, num_heads=16, num_key_value_heads=4,
+                                      scale_value=case.scale, softmax_lse_flag=True,
+                                      actual_seq_lengths_kv=lens))
+    for b in (0, 3):
+        one = run_plan(fia.AttentionPlan(q[b:b + 1].contiguous(), k[b:b + 1].contiguous(),
+                                         v[b:b + 1].contiguous(), num_heads=16,
+                                         num_key_value_heads=4, scale_value=case.scale,
+                                         softmax_lse_flag=True, actual_seq_lengths_kv=[lens[b]]))
+        assert torch.equal(one.out[0], full.out[b])
+        assert torch.equal(one.lse[0], full.lse[b])
+    # reversed batch order
+    perm = [3, 2, 1, 0]
+    rev = run_plan(fia.AttentionPlan(q[perm].contiguous(), k[perm].contiguous(),
+                                     v[perm].contiguous(), num_heads=16, num_key_value_heads=4,
+                                     scale_value=case.scale, softmax_lse_flag=True,
+                                     actual_seq_lengths_kv=[lens[p] for p in perm]))
+    for i, p in enumerate(perm):
+        assert torch.equal(rev.out[i], full.out[p])
+
+
+def test_prefill_batch_invariance():
+    lens = [300, 129, 77]
+    case = W.dense_case("pbi", 620, B=3, S1=300, S2=300, Q_N=8, KV_N=2, D=128, sparse_mode=3,
+                        q_lens=lens, kv_lens=lens)
+    q, k, v, _, _ = TI.dense_tensors(case, DEV)
+    kw = dict(num_heads=8, num_key_value_heads=2, scale_value=case.scale, sparse_mode=3)
+    full = run_plan(fia.AttentionPlan(q, k, v, actual_seq_lengths=lens, actual_seq_lengths_kv=lens, **kw))
+    one = run_plan(fia.AttentionPlan(q[1:2].contiguous(), k[1:2].contiguous(), v[1:2].contiguous(),
+                                     actual_seq_lengths=[lens[1]], actual_seq_lengths_kv=[lens[1]], **kw))
+    assert torch.equal(one.out[0], full.out[1])
+
+
+def test_sparse_batch_invariance():
+    case = W.sparse_case("sbi", 630, B=3, N1=64, seqused_kv=[3000, 600, 5000], K2=512,
+                         materialise_all_ori=False)
+    t = TI.sparse_tensors(case, DEV)
+    full = run_plan(TI.sparse_plan(case, DEV, tensors=t))
+    sub = {k: (v[1:2].contiguous() if k not in ("ori_kv", "cmp_kv", "sinks") else v)
+           for k, v in t.items()}
+    one = run_plan(fia.SparsePlan(sub["q"], sub["ori_kv"], sub["cmp_kv"],
+                                  sub["cmp_sparse_indices"], sub["ori_block_table"],
+                                  sub["cmp_block_table"], sub["seqused_kv"], sub["sinks"],
+                                  softmax_scale=case.softmax_scale, max_seqused_kv=600))
+    assert torch.equal(one.out[0], full.out[1])
