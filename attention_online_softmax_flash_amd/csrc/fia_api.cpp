@@ -147,30 +147,38 @@ struct fia_executor {
   int32_t n_items = 0;        // decode workgroups
   int32_t s2max = 0;
   bool noop = false;
-  void* pinned = nullptr;
+  // Device copy of `meta`, made by the first run on a device and reused by
+  // every later run there (the plan never changes after phase 1).
+  void* dplan = nullptr;
+  int dplan_device = -1;
 };
 
 namespace {
 
-fia_status upload_meta(fia_executor* e, void* ws, hipStream_t stream) {
+fia_status upload_plan(fia_executor* e) {
   if (e->meta_bytes == 0) return FIA_SUCCESS;
-  if (e->pinned == nullptr) {
-    if (hipHostMalloc(&e->pinned, e->meta_bytes, hipHostMallocDefault) != hipSuccess) {
-      e->pinned = nullptr;
-      return fail(FIA_ERR_HIP, "hipHostMalloc of the plan staging buffer failed");
-    }
-    std::memcpy(e->pinned, e->meta.data(), e->meta_bytes);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(FIA_ERR_HIP, "hipGetDevice failed");
+  if (e->dplan != nullptr && e->dplan_device == dev) return FIA_SUCCESS;
+  if (e->dplan != nullptr) {
+    (void)hipFree(e->dplan);
+    e->dplan = nullptr;
   }
-  if (hipMemcpyAsync(ws, e->pinned, e->meta_bytes, hipMemcpyHostToDevice, stream) != hipSuccess) {
-    return fail(FIA_ERR_HIP, "hipMemcpyAsync of the plan failed");
+  if (hipMalloc(&e->dplan, e->meta_bytes) != hipSuccess) {
+    e->dplan = nullptr;
+    return fail(FIA_ERR_HIP, "hipMalloc of the device plan failed");
   }
+  if (hipMemcpy(e->dplan, e->meta.data(), e->meta_bytes, hipMemcpyHostToDevice) != hipSuccess) {
+    return fail(FIA_ERR_HIP, "upload of the device plan failed");
+  }
+  e->dplan_device = dev;
   return FIA_SUCCESS;
 }
 
 void bind_workspace(fia_executor* e, void* ws) {
   uint8_t* base = static_cast<uint8_t*>(ws);
-  e->a.meta = reinterpret_cast<const int32_t*>(base);
-  e->a.work = reinterpret_cast<const int32_t*>(base) + e->work_off;
+  e->a.meta = static_cast<const int32_t*>(e->dplan);
+  e->a.work = static_cast<const int32_t*>(e->dplan) + e->work_off;
   e->a.part_o = reinterpret_cast<float*>(base + e->part_o_off);
   e->a.part_lse = reinterpret_cast<float*>(base + e->part_lse_off);
   e->sp.part_o = reinterpret_cast<float*>(base + e->part_o_off);
@@ -257,7 +265,7 @@ int32_t fia_executor_kind(const fia_executor* e) { return e ? e->kind : -1; }
 
 void fia_executor_destroy(fia_executor* e) {
   if (e == nullptr) return;
-  if (e->pinned) (void)hipHostFree(e->pinned);
+  if (e->dplan) (void)hipFree(e->dplan);
   delete e;
 }
 
@@ -652,14 +660,14 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     e->n_items = (int32_t)n_items;
     a.n_work = (int32_t)total_chunks;
     e->meta_bytes = e->meta.size() * sizeof(int32_t);
-    e->part_o_off = align_up(e->meta_bytes, kAlign);
-    e->part_lse_off = align_up(e->part_o_off + (size_t)total_chunks * Qn * D * sizeof(float), kAlign);
+    e->part_o_off = 0;
+    e->part_lse_off = align_up((size_t)total_chunks * Qn * D * sizeof(float), kAlign);
     e->ws_size = align_up(e->part_lse_off + (size_t)total_chunks * Qn * sizeof(float), kAlign);
   }
   if (e->kind != KIND_DECODE) {
     e->meta_bytes = e->meta.size() * sizeof(int32_t);
-    e->part_o_off = e->part_lse_off = align_up(e->meta_bytes, kAlign);
-    e->ws_size = align_up(e->meta_bytes, kAlign);
+    e->part_o_off = e->part_lse_off = 0;
+    e->ws_size = 0;
   }
   *workspace_size = e->ws_size;
   *executor = e;
@@ -855,7 +863,7 @@ fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void
   fia_status st = check_ws(e, workspace, workspace_size);
   if (st != FIA_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = upload_meta(e, workspace, s)) != FIA_SUCCESS) return st;
+  if ((st = upload_plan(e)) != FIA_SUCCESS) return st;
   bind_workspace(e, workspace);
   hipError_t err = hipSuccess;
   switch (e->kind) {
@@ -886,7 +894,7 @@ fia_status fia_debug_gather_kv(fia_executor* e, void* workspace, size_t workspac
   fia_status st = check_ws(e, workspace, workspace_size);
   if (st != FIA_SUCCESS) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = upload_meta(e, workspace, s)) != FIA_SUCCESS) return st;
+  if ((st = upload_plan(e)) != FIA_SUCCESS) return st;
   bind_workspace(e, workspace);
   hipError_t err = fia::launch_debug_gather(e->a, which, dst, e->s2max, s);
   if (err != hipSuccess) return fail(FIA_ERR_HIP, std::string("gather launch failed: ") + hipGetErrorString(err));

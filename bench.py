@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused inference attention hot path on one MI355X.
+
+Prints ONE JSON line.  The headline workload is the causal GQA prefill
+(B=4, Q_N=32, KV_N=8, D=128, bf16, per-batch lengths in [512, 2048]); a step
+is one run of its plan (fia_run: the prefill kernel).  `value` is its
+algorithmic TFLOP/s (visible (i, j) pairs only, 4*D flops per pair and head)
+over the K timed steps.  The same line carries, as `components`, the other
+hot-path workloads measured the same way: paged GQA decode (HBM GB/s), long
+causal ALiBi prefill (TFLOP/s) and shared-KV sparse decode (GB/s).
+
+Kernel durations come from HIP events recorded on the launch stream around
+each run; `roofline` relates them to MI355X's published peaks.  The
+`cpu_baseline` times the float64 oracle on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+
+
+def visible_pairs(mode, Lq, Lk):
+    """Number of visible (i, j) pairs of one head for mask modes 0 / 2 / 3."""
+    if mode == 0:
+        return Lq * Lk
+    total = 0
+    d = Lk - Lq if mode == 3 else 0
+    # row i sees keys j <= i + d, clipped to [0, Lk)
+    for i in range(Lq):
+        total += max(0, min(Lk, i + d + 1))
+    return total
+
+
+def dense_flops(case):
+    B = case.batch
+    lq = case.actual_seq_lengths or [case.q.shape[1]] * B
+    lk = case.actual_seq_lengths_kv or [case.k.shape[1]] * B
+    pairs = sum(visible_pairs(case.sparse_mode, int(a), int(b)) for a, b in zip(lq, lk))
+    return 4.0 * case.q.shape[-1] * case.num_heads * pairs
+
+
+def decode_bytes(case):
+    """Algorithmic HBM bytes of a paged decode: every visible K and V row once
+    per KV head, plus Q, O, LSE and the block-table entries used."""
+    D, kvn, qn = case.q.shape[-1], case.num_kv_heads, case.num_heads
+    B = case.q.shape[0]
+    L = case.actual_seq_lengths_kv
+    kv = sum(L) * kvn * D * 2 * 2
+    q = B * qn * D * 2
+    o = q
+    lse = B * qn * 4 if case.lse else 0
+    bt = sum(-(-x // case.block_size) for x in L) * 4
+    return kv + q + o + lse + bt
+
+
+def sparse_bytes(case):
+    """640 selected rows per batch at 604 used bytes each, q, out, indices."""
+    B, _, N1, D = case.q.shape
+    rows = 0
+    for b, Lk in enumerate(case.seqused_kv):
+        win = min(Lk, case.win_left + case.win_right + 1)
+        n_cmp = Lk // case.cmp_ratio
+        idx = case.cmp_sparse_indices[b, 0, 0]
+        rows += win + int(((idx >= 0) & (idx < n_cmp)).sum())
+    return rows * 604 + 2 * B * N1 * D * 2 + case.cmp_sparse_indices.nbytes
+
+
+def time_plan(plan, steps, warmup, flush=None):
+    """Run warmup untimed, then `steps` timed runs.  Returns (wall ms per
+    step, mean kernel ms from events on the launch stream, per-step kernel ms)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        plan.run(stream)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    if flush is None:
+        t0 = time.perf_counter()
+        for k in range(steps):
+            starts[k].record(stream)
+            plan.run(stream)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
+    else:
+        wall_ms = None
+        for k in range(steps):
+            flush()
+            starts[k].record(stream)
+            plan.run(stream)
+            ends[k].record(stream)
+        torch.cuda.synchronize()
+    per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return wall_ms, sum(per) / len(per), per
+
+
+def kernel_source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "attention_online_softmax_flash_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    counts, scaled by the copy-kernel calibration; None when no counts were
+    taken for the current kernel source."""
+    try:
+        with open(COUNTERS) as f:
+            data = json.load(f)
+    except (OSError, ValueError):
+        return None
+    entry = data.get(kernel)
+    if not entry:
+        return None
+    if entry.get("source_digest") != kernel_source_digest(entry.get("sources", [])):
+        return None
+    return entry.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(case, flops):
+    from oracle import fia_oracle as O
+
+    threads = None
+    try:
+        import threadpoolctl
+
+        threads = sum(i.get("num_threads", 0) for i in threadpoolctl.threadpool_info()
+                      if i.get("user_api") == "blas") or None
+    except Exception:
+        pass
+    t0 = time.perf_counter()
+    O.fia_case(case)
+    secs = time.perf_counter() - t0
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
+            "kind": "oracle", "seconds": round(secs, 3),
+            "sample": "the whole causal GQA prefill workload (4 batches x 32 heads), float64 "
+                      "numpy with materialised scores"}
+
+
+def roofline(bound, achieved, peak, unit, traffic):
+    return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
+            "frac": round(achieved / peak, 4), "traffic": traffic}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5"], default="all",
+                    help="limit the run to one workload (profiling)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the operator shards by batch / KV head with no exchange; see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_online_softmax_flash_amd import torch_io as TI
+    from attention_online_softmax_flash_amd import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    want = lambda w: args.workload in ("all", w)
+    flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
+    flush = lambda: flush_buf.zero_()
+    components = {}
+    line = None
+
+    if want("c2"):
+        case = W.c2_causal_gqa()
+        flops = dense_flops(case)
+        t0 = time.perf_counter()
+        tensors = TI.dense_tensors(case, dev)
+        t_plan = time.perf_counter()
+        plan = TI.dense_plan(case, dev, tensors=tensors)
+        plan_ms = (time.perf_counter() - t_plan) * 1000.0
+        wall_ms, kern_ms, _ = time_plan(plan, args.steps, args.warmup)
+        value = flops / (wall_ms / 1000.0) / 1e12
+        achieved = flops / (kern_ms / 1000.0) / 1e12
+        line = {
+            "metric": "decode attention HBM GB/s + prefill attention TFLOP/s, bf16, 1 MI355X",
+            "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(wall_ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": {"workload": "causal GQA prefill: B=4, Q_N=32, KV_N=8, D=128, S padded "
+                                   "to 2048, actual lengths " + str(case.actual_seq_lengths) +
+                                   ", right-down causal, scale 1/sqrt(128)",
+                       "global_batch": 4, "seq_len": 2048, "parallelism": "none",
+                       "algorithmic_flop_per_step": flops, "plan_ms": round(plan_ms, 3)},
+            "roofline": roofline("mfma", achieved, PEAK_BF16_TFLOPS, "TFLOP/s",
+                                 measured_traffic("prefill_bf16")),
+        }
+        line["roofline"]["kernel"] = "prefill_bf16<128, false>"
+        line["roofline"]["kernel_ms"] = round(kern_ms, 5)
+        if not args.no_cpu_baseline:
+            line["cpu_baseline"] = cpu_baseline(case, flops)
+        del plan, tensors
+
+    if want("c3"):
+        case = W.c3_paged_decode()
+        nbytes = decode_bytes(case)
+        plan = TI.dense_plan(case, dev)
+        _, kern_ms, _ = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["paged_decode"] = {
+            "workload": "paged GQA decode: B=64, Q_N=32, KV_N=8, D=128, block 128, KV lengths "
+                        "in [1024, 8192], LSE", "unit": "GB/s", "value": round(gbs, 2),
+            "algorithmic_bytes": nbytes, "ms": round(kern_ms, 5),
+            "kernels": "decode_split_bf16<128> + decode_merge<128>",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
+                                 measured_traffic("decode_split_bf16"))}
+        del plan
+
+    if want("c4"):
+        case = W.c4_alibi_prefill()
+        flops = dense_flops(case)
+        plan = TI.dense_plan(case, dev)
+        _, kern_ms, _ = time_plan(plan, min(args.steps, 20), args.warmup)
+        tf = flops / (kern_ms / 1000.0) / 1e12
+        components["long_alibi_prefill"] = {
+            "workload": "causal ALiBi prefill: B=1, Q_N=KV_N=16, S=8192, D=128",
+            "unit": "TFLOP/s", "value": round(tf, 3), "algorithmic_flop": flops,
+            "ms": round(kern_ms, 5), "kernels": "prefill_bf16<128, true>",
+            "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)}
+        del plan
+
+    if want("c5"):
+        case = W.c5_sparse_sharedkv()
+        nbytes = sparse_bytes(case)
+        plan = TI.sparse_plan(case, dev)
+        _, kern_ms, _ = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["sparse_sharedkv_decode"] = {
+            "workload": "shared-KV sparse decode: B=16, Q_N=64, D=512 (fp8 nope + bf16 rope), "
+                        "window 128 + top-512 of ratio-4 compressed KV, sinks",
+            "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
+            "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+        del plan
+
+    if line is None:
+        line = {"metric": "decode attention HBM GB/s + prefill attention TFLOP/s, bf16, 1 MI355X",
+                "value": None, "unit": None, "n_gpus": 1, "steps": args.steps,
+                "warmup": args.warmup, "note": f"partial run: --workload {args.workload}"}
+    line["components"] = components
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -196,7 +196,12 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
 /* Phase 2: enqueue the planned work on `stream` (a hipStream_t; NULL is the
  * default stream).  `workspace` is device memory of at least the size phase 1
  * returned (may be NULL when that size is 0); it is scratch and its contents
- * need not survive between calls.  Asynchronous: returns after enqueueing. */
+ * need not survive between calls.  Asynchronous: returns after enqueueing.
+ * The first run of an executor on a device allocates a small device copy of
+ * the plan (per-batch lengths and the work list) and uploads it
+ * synchronously; later runs on that device only launch kernels, so a run
+ * can be captured into a HIP graph once the executor has run once outside
+ * the capture.  The copy is freed by fia_executor_destroy(). */
 fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* executor,
                    void* stream);
 
