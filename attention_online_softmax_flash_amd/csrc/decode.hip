@@ -74,27 +74,34 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
   if (t_hi > t_lo) {
     const int first = ws + ((t_lo - ws) & ~31);
     for (int ts = first; ts < t_hi; ts += kDecodeStep) {
-      // Row offsets of the two 16-key halves; within a half the keys share a
-      // page (block sizes are multiples of 16 and halves are 16-aligned).
-      int64_t krow[2], vrow[2];
+      // The two 16-key halves each lie inside one page (block sizes are
+      // multiples of 16 and halves are 16-aligned): one bounds-checked
+      // resource per half and operand; rows at or past `hi` (possibly the
+      // unwritten tail of the last page) read as zero.
+      __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int jb = min(ts + 16 * hf, t_hi - 1);
-        krow[hf] = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
-        vrow[hf] = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
-        // Offsets below are relative to key ts + 16 hf.
-        krow[hf] -= (int64_t)(jb - ts - 16 * hf) * a.k_ss;
-        vrow[hf] -= (int64_t)(jb - ts - 16 * hf) * a.v_ss;
+        const int jb = ts + 16 * hf;
+        const int nv = min(16, hi - jb);
+        int64_t ko = 0, vo = 0;
+        uint32_t kbytes = 0, vbytes = 0;
+        if (nv > 0) {
+          ko = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
+          vo = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
+          kbytes = (uint32_t)((nv - 1) * a.k_ss + D) * 2u;
+          vbytes = (uint32_t)((nv - 1) * a.v_ss + D) * 2u;
+        }
+        rk[hf] = make_rsrc(kbase + ko, kbytes);
+        rv[hf] = make_rsrc(vbase + vo, vbytes);
       }
       // Key operand: key row (16 hf + n), d = 32 cc + 8 g .. +7.
       u32x4 kr[2][NC];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int j = ts + 16 * hf + n;
-        const bool ok = j >= t_lo && j < t_hi;
-        const uint16_t* p = kbase + krow[hf] + (int64_t)n * a.k_ss + 8 * g;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) kr[hf][cc] = ok ? ld16(p + 32 * cc) : u32x4{0, 0, 0, 0};
+        for (int cc = 0; cc < NC; ++cc) {
+          kr[hf][cc] = buf_ld16(rk[hf], (uint32_t)(n * a.k_ss + 32 * cc + 8 * g) * 2u);
+        }
       }
       // Value rows for k-slot s: key 16 (s/4) + 4 g + s%4, columns DPL n ..
       u32x4 vr[8];
@@ -102,13 +109,11 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
       for (int s = 0; s < 8; ++s) {
         const int hf = s >> 2;
         const int t = 4 * g + (s & 3);
-        const int j = ts + 16 * hf + t;
-        const bool ok = j >= t_lo && j < t_hi;
-        const uint16_t* p = vbase + vrow[hf] + (int64_t)t * a.v_ss + DPL * n;
+        const uint32_t off = (uint32_t)(t * a.v_ss + DPL * n) * 2u;
         if constexpr (DPL == 8) {
-          vr[s] = ok ? ld16(p) : u32x4{0, 0, 0, 0};
+          vr[s] = buf_ld16(rv[hf], off);
         } else {
-          u32x2 w = ok ? ld8(p) : u32x2{0, 0};
+          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[hf], off, 0, 0));
           vr[s] = u32x4{w.x, w.y, 0, 0};
         }
       }
@@ -228,6 +233,8 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
 
 // One wave per output row (b, h): fold the row's partials in chunk order, or
 // write the empty-row result (0, LSE +inf) when the row has no visible key.
+// Lanes read the chunk LSEs in parallel (64 at a time); the weighted sum then
+// runs over chunks in order with every load independent of the others.
 template <int D>
 __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   constexpr int PL = D / 64;
@@ -251,18 +258,47 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   }
   const int chunk0 = bm[BF_CHUNK0];
   float M = kNegInf;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, a.part_lse[(int64_t)(chunk0 + c) * a.Qn + h]);
+  for (int c0 = 0; c0 < nchunk; c0 += 64) {
+    const int c = c0 + lane;
+    const float lc = c < nchunk ? a.part_lse[(int64_t)(chunk0 + c) * a.Qn + h] : kNegInf;
+    M = fmaxf(M, lc);
+  }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
   float L = 0.f;
   float acc[PL];
 #pragma unroll
   for (int u = 0; u < PL; ++u) acc[u] = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    const int64_t pi = (int64_t)(chunk0 + c) * a.Qn + h;
-    const float w = fast_exp2(a.part_lse[pi] - M);
-    L += w;
-    const float* pp = a.part_o + pi * D + lane * PL;
+  for (int c0 = 0; c0 < nchunk; c0 += 64) {
+    const int c = c0 + lane;
+    const float lc = c < nchunk ? a.part_lse[(int64_t)(chunk0 + c) * a.Qn + h] : kNegInf;
+    const float w = fast_exp2(lc - M);
+    const int cnt = min(64, nchunk - c0);
+    int k = 0;
+    for (; k + 4 <= cnt; k += 4) {
+      float x[4][PL];
+      float wk[4];
 #pragma unroll
-    for (int u = 0; u < PL; ++u) acc[u] += w * pp[u];
+      for (int t = 0; t < 4; ++t) {
+        wk[t] = __shfl(w, k + t, 64);
+        const float* pp = a.part_o + ((int64_t)(chunk0 + c0 + k + t) * a.Qn + h) * D + lane * PL;
+#pragma unroll
+        for (int u = 0; u < PL; ++u) x[t][u] = pp[u];
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        L += wk[t];
+#pragma unroll
+        for (int u = 0; u < PL; ++u) acc[u] += wk[t] * x[t][u];
+      }
+    }
+    for (; k < cnt; ++k) {
+      const float wk = __shfl(w, k, 64);
+      const float* pp = a.part_o + ((int64_t)(chunk0 + c0 + k) * a.Qn + h) * D + lane * PL;
+      L += wk;
+#pragma unroll
+      for (int u = 0; u < PL; ++u) acc[u] += wk * pp[u];
+    }
   }
   const float inv = 1.f / L;
   if constexpr (PL == 2) {

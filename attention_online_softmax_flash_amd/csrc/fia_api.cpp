@@ -490,6 +490,9 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
       return fail(FIA_ERR_PARAM_INVALID, "softmax_lse must be [B, Q_N, Q_S, 1]");
     }
   }
+  if (!(p->scale_value >= 0.0) || std::isinf(p->scale_value)) {
+    return fail(FIA_ERR_UNSUPPORTED, "scale_value must be a finite non-negative number");
+  }
   if (p->inner_precise < 0 || p->inner_precise > 3) {
     return fail(FIA_ERR_PARAM_INVALID, "inner_precise must be in [0, 3]");
   }
@@ -500,16 +503,30 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   } else if (D != 64 && D != 128) {
     return fail(FIA_ERR_UNSUPPORTED, "bf16 kernels support head dim 64 and 128");
   }
+  const bool kv_empty = numel(key) == 0 || numel(value) == 0 || (!paged && ck.S == 0);
   {
+    // Key / value of an empty input are never read; their strides do not matter.
     const int64_t vec = f32 ? 4 : 8;  // elements per 16-byte access
-    const int64_t strides[] = {cq.ss, cq.sh, co.ss, co.sh, ck.ss, ck.sh, cv.ss, cv.sh,
-                               tnd ? 0 : cq.sb, tnd ? 0 : co.sb, ck.sb, cv.sb};
+    const int64_t strides[] = {cq.ss, cq.sh, co.ss, co.sh, tnd ? 0 : cq.sb, tnd ? 0 : co.sb};
+    const int64_t kv_strides[] = {ck.ss, ck.sh, cv.ss, cv.sh, ck.sb, cv.sb};
     for (int64_t s : strides) {
       if (s % vec != 0) return fail(FIA_ERR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
     }
-    const void* ptrs[] = {query->data, attention_out->data, key->data, value->data};
+    const void* ptrs[] = {query->data, attention_out->data};
     for (const void* ptr : ptrs) {
       if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) {
+        return fail(FIA_ERR_UNSUPPORTED, "tensor data must be 16-byte aligned");
+      }
+    }
+    if (!kv_empty) {
+      for (int64_t s : kv_strides) {
+        if (s % vec != 0) return fail(FIA_ERR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
+      }
+      if (ck.ss < D || cv.ss < D) {
+        return fail(FIA_ERR_UNSUPPORTED, "key/value rows must not overlap (token stride >= D)");
+      }
+      if (reinterpret_cast<uintptr_t>(key->data) % 16 != 0 ||
+          reinterpret_cast<uintptr_t>(value->data) % 16 != 0) {
         return fail(FIA_ERR_UNSUPPORTED, "tensor data must be 16-byte aligned");
       }
     }
@@ -555,6 +572,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   a.G = (int32_t)(Qn / KVn);
   a.D = (int32_t)D;
   a.esz = f32 ? 4 : 2;
+  a.tile_contig = (!paged || bs % fia::kPrefillKeys == 0) ? 1 : 0;
   a.scale = (float)p->scale_value;
   a.scale_log2 = (float)(p->scale_value * 1.4426950408889634);
   a.mode = mode;
@@ -579,7 +597,6 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   e->s2max = (int32_t)max_kv;
   e->work_off = e->meta.size();
 
-  const bool kv_empty = (numel(key) == 0 || numel(value) == 0) || (!paged && ck.S == 0);
   if (kv_empty) {
     e->kind = KIND_FILL;
   } else if (f32) {

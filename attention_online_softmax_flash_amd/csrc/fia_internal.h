@@ -51,6 +51,7 @@ struct AttnArgs {
   FastDiv bs_div;
   int32_t paged;
   int32_t tnd;
+  int32_t tile_contig;              // 64-key tiles never straddle a page (dense, or block % 64 == 0)
   const int32_t* meta;              // [B * BF_COUNT] then the work list
   const int32_t* work;              // prefill: 2 ints per item; decode: 2 ints per chunk
   int32_t n_work;

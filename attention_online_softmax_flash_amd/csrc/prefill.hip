@@ -23,6 +23,8 @@
 // (pse type 2) adds slope * ((kv_start + j) - (q_start + i)) after scaling
 // (aclnnFusedInferAttentionScoreV4 formula).  Rows with no visible key and
 // rows past the actual query length are written as 0 with LSE +inf.
+#include <type_traits>
+
 #include "fia_device.h"
 
 namespace fia {
@@ -51,12 +53,22 @@ struct TileRegs {
 
 }  // namespace
 
-template <int D, bool ALIBI>
+// KVM selects how key / value rows are addressed: 0 dense or TND (a tile is
+// one strided run, its base advances by pointer arithmetic), 1 paged with
+// block_size a multiple of 64 (a tile lies in one page, one table lookup per
+// tile), 2 any paged layout (per-row lookup).
+template <int D, bool ALIBI, int KVM>
 __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   using L = PrefillLds<D>;
   constexpr int NQ = D / 16;   // 16-wide d chunks of the score product
   constexpr int NMB = D / 32;  // 32-wide d blocks of the output
   constexpr int DCH = D / 8;   // 16-byte pieces per row
+  constexpr int NK = TileRegs<D>::NK;
+  // PIPE: the score product of tile t+1 is issued together with the softmax
+  // of tile t (needs a second score buffer; too many registers with the ALiBi
+  // bias or per-row paging, which compute each tile's scores up front).
+  constexpr bool PIPE = !ALIBI && KVM != 2;
+  constexpr bool INTERLEAVE = PIPE;
   extern __shared__ __align__(16) uint8_t lds[];
 
   const int tid = threadIdx.x;
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   const int i = iw0 + n;
   const bool row_live = i < Lq;
 
-  // Key range of the whole tile and of this wave.
+  // Key range of the whole tile and of this wave (monotone in the row).
   const int rows_end = min(i0 + BM, Lq);
   int klo = 0, khi = 0;
   if (rows_end > i0) {
@@ -120,50 +132,76 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     const float c_al = ALIBI ? a.slopes[h] * kLog2e : 0.f;
     const uint16_t* kg = (const uint16_t*)a.k;
     const uint16_t* vg = (const uint16_t*)a.v;
+    const uint16_t* kbase0 = kg + (int64_t)b * a.k_sb + (int64_t)kv_off * a.k_ss + (int64_t)kvh * a.k_sh;
+    const uint16_t* vbase0 = vg + (int64_t)b * a.v_sb + (int64_t)kv_off * a.v_ss + (int64_t)kvh * a.v_sh;
 
-    // Thread roles for staging one tile.
-    const int va = tid & 15;   // keys 4 va .. 4 va + 3
+    // Thread roles for staging one tile, with loop-invariant offsets.
+    const int va = tid & 15;   // keys 4 va .. 4 va + 3 of the value tile
     const int vq = tid >> 4;   // 16-byte value column piece
+    uint32_t koffs[NK], ks_addr[NK];
+#pragma unroll
+    for (int q = 0; q < NK; ++q) {
+      const int u = tid + 256 * q;
+      koffs[q] = (uint32_t)((u / DCH) * a.k_ss + 8 * (u % DCH)) * 2u;
+      ks_addr[q] = (uint32_t)((u / DCH) * L::K_PITCH + (u % DCH) * 16);
+    }
+    uint32_t voffs[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) voffs[q] = (uint32_t)((4 * va + q) * a.v_ss + 8 * vq) * 2u;
+    const uint32_t vs_addr = (uint32_t)(L::K_BYTES + 8 * vq * L::V_PITCH + va * 8);
+    const uint32_t kr_addr = (uint32_t)(n * L::K_PITCH + 16 * hh);
+    const uint32_t vr_addr = (uint32_t)(L::K_BYTES + n * L::V_PITCH + 8 * hh);
     TileRegs<D> regs;
 
     auto load_tile = [&](int kt) {
       const int j0 = kt * BN;
+      if constexpr (KVM == 2) {
 #pragma unroll
-      for (int q = 0; q < TileRegs<D>::NK; ++q) {
-        const int u = tid + 256 * q;
-        const int key = u / DCH;
-        const int dch = u % DCH;
-        const int j = j0 + key;
-        u32x4 val = {0, 0, 0, 0};
-        if (j < Lk) {
-          const int64_t off = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, j, kvh, kv_off);
-          val = ld16(kg + off + 8 * dch);
-        }
-        regs.k[q] = val;
-      }
-      if (vq < DCH) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = j0 + 4 * va + q;
+        for (int q = 0; q < NK; ++q) {
+          const int u = tid + 256 * q;
+          const int j = j0 + u / DCH;
           u32x4 val = {0, 0, 0, 0};
-          if (j < Lk) {
-            const int64_t off = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, j, kvh, kv_off);
-            val = ld16(vg + off + 8 * vq);
+          if (j < Lk) val = ld16(kg + kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, j, kvh, kv_off) + 8 * (u % DCH));
+          regs.k[q] = val;
+        }
+        if (vq < DCH) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int j = j0 + 4 * va + q;
+            u32x4 val = {0, 0, 0, 0};
+            if (j < Lk) val = ld16(vg + kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, j, kvh, kv_off) + 8 * vq);
+            regs.v[q] = val;
           }
-          regs.v[q] = val;
+        }
+      } else {
+        const uint16_t* kp;
+        const uint16_t* vp;
+        if constexpr (KVM == 0) {
+          kp = kbase0 + (int64_t)j0 * a.k_ss;
+          vp = vbase0 + (int64_t)j0 * a.v_ss;
+        } else {
+          const uint32_t page = fast_div((uint32_t)j0, a.bs_div);
+          const int blk = clamp_block(a.block_table[(int64_t)b * a.bt_sb + page], a.n_blocks);
+          const int slot = j0 - (int)page * a.block_size;
+          kp = kg + paged_row_offset(blk, slot, kvh, a.k_sb, a.k_ss, a.k_sh);
+          vp = vg + paged_row_offset(blk, slot, kvh, a.v_sb, a.v_ss, a.v_sh);
+        }
+        // Rows >= Lk fall outside the resource and read as zero.
+        const int nvalid = min(BN, Lk - j0);
+        const auto rk = make_rsrc(kp, (uint32_t)((nvalid - 1) * a.k_ss + D) * 2u);
+        const auto rv = make_rsrc(vp, (uint32_t)((nvalid - 1) * a.v_ss + D) * 2u);
+#pragma unroll
+        for (int q = 0; q < NK; ++q) regs.k[q] = buf_ld16(rk, koffs[q]);
+        if (vq < DCH) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) regs.v[q] = buf_ld16(rv, voffs[q]);
         }
       }
     };
     auto store_tile = [&](int stage) {
-      uint8_t* kb = lds + stage * L::STAGE;
-      uint8_t* vb = kb + L::K_BYTES;
+      uint8_t* base = lds + stage * L::STAGE;
 #pragma unroll
-      for (int q = 0; q < TileRegs<D>::NK; ++q) {
-        const int u = tid + 256 * q;
-        const int key = u / DCH;
-        const int dch = u % DCH;
-        *reinterpret_cast<u32x4*>(kb + key * L::K_PITCH + dch * 16) = regs.k[q];
-      }
+      for (int q = 0; q < NK; ++q) *reinterpret_cast<u32x4*>(base + ks_addr[q]) = regs.k[q];
       if (vq < DCH) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -174,95 +212,173 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           } else {
             pr = u32x2{pick_lo(regs.v[0][w], regs.v[1][w]), pick_lo(regs.v[2][w], regs.v[3][w])};
           }
-          *reinterpret_cast<u32x2*>(vb + (8 * vq + e) * L::V_PITCH + va * 8) = pr;
+          *reinterpret_cast<u32x2*>(base + vs_addr + e * L::V_PITCH) = pr;
         }
       }
     };
 
-    const int kt0 = klo / BN;
-    const int kt1 = (khi + BN - 1) / BN;
-    load_tile(kt0);
-    store_tile(0);
-    __syncthreads();
-
-    for (int kt = kt0; kt < kt1; ++kt) {
-      const int stage = (kt - kt0) & 1;
-      const bool more = kt + 1 < kt1;
-      if (more) load_tile(kt + 1);
-
+    // S^T of one tile for this wave: 2 key blocks x 32 query rows.
+    auto compute_s = [&](int stage, f32x16* sv) {
+      const uint8_t* kb = lds + stage * L::STAGE + kr_addr;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const uint8_t* kr = kb + 32 * k2 * L::K_PITCH;
+        sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kr), qreg[0], f32x16{});
+      }
+#pragma unroll
+      for (int c = 1; c < NQ; ++c) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+          const uint8_t* kr = kb + 32 * k2 * L::K_PITCH;
+          sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kr + 32 * c), qreg[c], sv[k2]);
+        }
+      }
+    };
+    auto wave_skip = [&](int kt) {
       const int j0 = kt * BN;
-      const bool wave_skip = (wrows_end <= iw0) || (j0 + BN <= wlo_min) || (j0 >= whi_max);
-      if (!wave_skip) {
-        const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min);
-        const uint8_t* kb = lds + stage * L::STAGE;
-        const uint8_t* vb = kb + L::K_BYTES;
-        f32x16 s[2];
+      return (wrows_end <= iw0) || (j0 + BN <= wlo_min) || (j0 >= whi_max);
+    };
+
+    // Softmax of tile kt (scores in sc), then O += V^T P^T from `stage`.  When
+    // `next_stage` >= 0 the score product of the next tile is issued inside
+    // the same straight-line block, so its MFMAs overlap this tile's VALU work.
+    auto tile_body = [&](auto masked_tag, int kt, int stage, f32x16* sc, int next_stage,
+                         f32x16* sn) {
+      constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr bool PLAIN = !ALIBI && !MASKED;
+      const int j0 = kt * BN;
+      float mx = kNegInf;
+      if constexpr (PLAIN) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) s[k2][r] = 0.f;
-#pragma unroll
-          for (int c = 0; c < NQ; ++c) {
-            const u32x4 av = *reinterpret_cast<const u32x4*>(
-                kb + (32 * k2 + n) * L::K_PITCH + (16 * c + 8 * hh) * 2);
-            s[k2] = mfma32(av, qreg[c], s[k2]);
-          }
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[k2][r]);
         }
-        // Scale, bias, mask.  Key of slot (k2, r): j0 + 32 k2 + 8 (r/4) + 4 hh + r%4.
-        float mx = kNegInf;
+        mx *= a.scale_log2;
+      } else {
         const int jb = j0 + 4 * hh;
-        const float cb = ALIBI ? c_al * (float)(jb - i + a.alibi_delta) : 0.f;
+        // ALiBi distance (kv_start + j) - (q_start + i) = base + koff.  The bias
+        // is c_al * (base + koff), not c_al * base + c_al * koff, so no
+        // loop-invariant products need registers.
+        const float base = (float)(jb - i + a.alibi_delta);
+        const int rel_lo = my_lo - jb;   // visible iff rel_lo <= koff < rel_hi
+        const int rel_hi = my_hi - jb;
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int koff = 32 * k2 + 8 * (r >> 2) + (r & 3);
-            float x = s[k2][r] * a.scale_log2;
-            if (ALIBI) x += __builtin_fmaf(c_al, (float)koff, cb);
-            if (need_mask) {
-              const int j = jb + koff;
-              x = (j >= my_lo && j < my_hi) ? x : kNegInf;
-            }
-            s[k2][r] = x;
+            float x = ALIBI ? __builtin_fmaf(sc[k2][r], a.scale_log2, c_al * (base + (float)koff))
+                            : sc[k2][r] * a.scale_log2;
+            if constexpr (MASKED) x = (koff >= rel_lo && koff < rel_hi) ? x : kNegInf;
+            sc[k2][r] = x;
             mx = fmaxf(mx, x);
           }
         }
-        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+      }
+      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      // Lazy rescale: keep the running max m_run unless a row's new max
+      // exceeds it by more than 8 (probabilities stay <= 2^8).
+      const bool grow = mx > m_run + 8.f;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
         m_run = m_new;
-        float psum = 0.f;
-        u32x4 pb[4];
+        l_run *= alpha;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int k2 = kk >> 1;
-          const int rb = 8 * (kk & 1);
-          float p[8];
+        for (int mb = 0; mb < NMB; ++mb) o[mb] *= alpha;
+      }
+      const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+      if constexpr (PIPE) {
+        if (next_stage >= 0) compute_s(next_stage, sn);
+      }
+      float psum = 0.f;
+      u32x4 pb[4];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) {
-            p[t] = fast_exp2(s[k2][rb + t] - m_use);
-            psum += p[t];
-          }
-          pb[kk] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                         pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      for (int kk = 0; kk < 4; ++kk) {
+        const int k2 = kk >> 1;
+        const int rb = 8 * (kk & 1);
+        float p[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          p[t] = PLAIN ? fast_exp2(__builtin_fmaf(sc[k2][rb + t], a.scale_log2, -m_sub))
+                       : fast_exp2(sc[k2][rb + t] - m_sub);
+          psum += p[t];
         }
-        l_run = l_run * alpha + psum;
+        pb[kk] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+                       pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
+      }
+      l_run += psum;
+      const uint8_t* vb = lds + stage * L::STAGE + vr_addr;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          o[mb] *= alpha;
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const uint8_t* vp = vb + (32 * mb + n) * L::V_PITCH + (16 * kk + 4 * hh) * 2;
-            const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vp);
-            const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vp + 16);
-            const u32x4 av = {lo2.x, lo2.y, hi2.x, hi2.y};
-            o[mb] = mfma32(av, pb[kk], o[mb]);
-          }
+          const uint8_t* vp = vb + 32 * mb * L::V_PITCH + 32 * kk;
+          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vp);
+          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vp + 16);
+          o[mb] = mfma32(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, pb[kk], o[mb]);
         }
       }
-      if (more) store_tile(stage ^ 1);
+      // Interleave: one MFMA, a few VALU, one LDS read, repeated.
+      if constexpr (INTERLEAVE) {
+#pragma unroll
+        for (int g = 0; g < 24; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+      }
+    };
+
+    // Software pipeline over key tiles, two LDS stages.  Iteration kt holds the
+    // scores of tile kt in registers, tile kt+1 in LDS stage `nstage`, and the
+    // global loads of tile kt+2 in flight; it computes softmax(kt) + PV(kt)
+    // together with the score product of tile kt+1, then stores tile kt+2 into
+    // the stage tile kt used.
+    const int kt0 = klo / BN;
+    const int kt1 = (khi + BN - 1) / BN;
+    load_tile(kt0);
+    store_tile(0);
+    if (kt0 + 1 < kt1) load_tile(kt0 + 1);
+    __syncthreads();
+    f32x16 s_a[2], s_b[2];
+    bool cur_skip = wave_skip(kt0);
+    if (PIPE && !cur_skip) compute_s(0, s_a);
+    if (kt0 + 1 < kt1) store_tile(1);
+    __syncthreads();
+
+    // One pipeline step; the loop below is unrolled by two so the roles of
+    // the two score buffers stay static (they live in registers).
+    auto step = [&](int kt, f32x16* sc, f32x16* sn) {
+      const int stage = (kt - kt0) & 1;
+      const bool has_next = kt + 1 < kt1;
+      const bool has_next2 = kt + 2 < kt1;
+      if (has_next2) load_tile(kt + 2);
+      const bool next_skip = has_next ? wave_skip(kt + 1) : true;
+      const int nstage = (!PIPE || next_skip) ? -1 : (stage ^ 1);
+      if (!PIPE && !cur_skip) compute_s(stage, sc);
+      if (!cur_skip) {
+        const int j0 = kt * BN;
+        const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min);
+        if (need_mask) {
+          tile_body(std::true_type{}, kt, stage, sc, nstage, sn);
+        } else {
+          tile_body(std::false_type{}, kt, stage, sc, nstage, sn);
+        }
+      } else if (PIPE && nstage >= 0) {
+        compute_s(nstage, sn);
+      }
+      cur_skip = next_skip;
+      if (has_next2) {
+        __syncthreads();   // every wave is done with this stage
+        store_tile(stage);
+      }
       __syncthreads();
+    };
+    for (int kt = kt0; kt < kt1; kt += 2) {
+      step(kt, s_a, s_b);
+      if (kt + 1 < kt1) step(kt + 1, s_b, s_a);
     }
   }
 
@@ -290,27 +406,34 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   }
 }
 
+template <int D, bool ALIBI, int KVM>
+static void launch_one(const AttnArgs& a, hipStream_t s) {
+  constexpr int lds = PrefillLds<D>::TOTAL;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipFuncSetAttribute((const void*)prefill_bf16<D, ALIBI, KVM>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    attr_set = true;
+  }
+  prefill_bf16<D, ALIBI, KVM><<<a.n_work, 256, lds, s>>>(a);
+}
+
+template <int D, bool ALIBI>
+static void launch_kvm(const AttnArgs& a, hipStream_t s) {
+  if (!a.paged) launch_one<D, ALIBI, 0>(a, s);
+  else if (a.tile_contig) launch_one<D, ALIBI, 1>(a, s);
+  else launch_one<D, ALIBI, 2>(a, s);
+}
+
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   const bool alibi = a.slopes != nullptr;
   if (a.D == 128) {
-    constexpr int lds = PrefillLds<128>::TOTAL;
-    if (alibi) {
-      hipFuncSetAttribute((const void*)prefill_bf16<128, true>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      prefill_bf16<128, true><<<a.n_work, 256, lds, s>>>(a);
-    } else {
-      hipFuncSetAttribute((const void*)prefill_bf16<128, false>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-      prefill_bf16<128, false><<<a.n_work, 256, lds, s>>>(a);
-    }
+    if (alibi) launch_kvm<128, true>(a, s);
+    else launch_kvm<128, false>(a, s);
   } else {
-    constexpr int lds = PrefillLds<64>::TOTAL;
-    if (alibi) {
-      prefill_bf16<64, true><<<a.n_work, 256, lds, s>>>(a);
-    } else {
-      prefill_bf16<64, false><<<a.n_work, 256, lds, s>>>(a);
-    }
+    if (alibi) launch_kvm<64, true>(a, s);
+    else launch_kvm<64, false>(a, s);
   }
   return hipGetLastError();
 }

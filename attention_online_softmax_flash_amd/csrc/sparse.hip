@@ -103,6 +103,18 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
   const int hh = lane >> 5;
   const int Lk = sparse_len(a, b);
   const int s0 = chunk * kSparseChunk;
+  const int sb = wave & 1;
+  const int dh = wave >> 1;
+  const int head = hb * kSparseHeads + n;
+
+  // Query operand for the score product, loaded first so its latency overlaps
+  // the row gather: head n, d = 256 dh + 16 c + 8 hh .. +7.
+  u32x4 qv[16];
+  {
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh + 256 * dh + 8 * hh;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) qv[c] = ld16(qp + 16 * c);
+  }
 
   // 1. Gather and dequantise: thread owns rows 4 rg .. 4 rg + 3 and the
   // 8-element pieces pc = tid/16 + 16 q of them.
@@ -161,21 +173,14 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
   __syncthreads();
 
   // 2. Scores S^T[slot][head]: wave (sb, dh) = slot block 32 sb, d half dh.
-  const int sb = wave & 1;
-  const int dh = wave >> 1;
-  const int head = hb * kSparseHeads + n;
   f32x16 s;
 #pragma unroll
   for (int r = 0; r < 16; ++r) s[r] = 0.f;
-  {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh + 256 * dh + 8 * hh;
-#pragma unroll 4
-    for (int c = 0; c < 16; ++c) {
-      const u32x4 bq = ld16(qp + 16 * c);
-      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH +
-                                                       (256 * dh + 16 * c + 8 * hh) * 2);
-      s = mfma32(av, bq, s);
-    }
+#pragma unroll
+  for (int c = 0; c < 16; ++c) {
+    const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH +
+                                                     (256 * dh + 16 * c + 8 * hh) * 2);
+    s = mfma32(av, qv[c], s);
   }
   if (dh == 1) {
 #pragma unroll
@@ -246,35 +251,57 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
 }
 
 // One wave per (b, head): fold the chunks in slot order with the sink logit.
+// Lanes read the chunk log2-sum-exps in parallel; the weighted sum runs over
+// chunks in order.
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (row >= a.B * a.N1) return;
   const int b = row / a.N1;
   const int h = row - b * a.N1;
-  const int n_chunks = a.n_slots / kSparseChunk;
+  const int n_chunks = a.n_slots / kSparseChunk;   // <= 64 (K2 <= 1024)
   const float sink = a.sinks[h] * kLog2e;
-  float M = sink;
-  for (int c = 0; c < n_chunks; ++c) {
-    M = fmaxf(M, a.part_lse[((int64_t)b * n_chunks + c) * a.N1 + h]);
-  }
+  const float lc = lane < n_chunks ? a.part_lse[((int64_t)b * n_chunks + lane) * a.N1 + h] : kNegInf;
+  float M = fmaxf(lc, sink);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
   const float m_use = (M == kNegInf) ? 0.f : M;
+  const float w = (lc == kNegInf) ? 0.f : fast_exp2(lc - m_use);
   float L = fast_exp2(sink - m_use);
   float acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const int64_t pi = ((int64_t)b * n_chunks + c) * a.N1 + h;
-    const float lc = a.part_lse[pi];
-    if (lc == kNegInf) continue;
-    const float w = fast_exp2(lc - m_use);
-    L += w;
-    const f32x4* pp = reinterpret_cast<const f32x4*>(a.part_o + pi * kSparseD + 8 * lane);
-    const f32x4 x0 = pp[0], x1 = pp[1];
+  int c = 0;
+  for (; c + 2 <= n_chunks; c += 2) {
+    const float w0 = __shfl(w, c, 64), w1 = __shfl(w, c + 1, 64);
+    const f32x4* p0 = reinterpret_cast<const f32x4*>(
+        a.part_o + (((int64_t)b * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
+    const f32x4* p1 = reinterpret_cast<const f32x4*>(
+        a.part_o + (((int64_t)b * n_chunks + c + 1) * a.N1 + h) * kSparseD + 8 * lane);
+    const f32x4 x0 = p0[0], x1 = p0[1], y0 = p1[0], y1 = p1[1];
+    L += w0;
+    L += w1;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      acc[u] += w * x0[u];
-      acc[4 + u] += w * x1[u];
+      acc[u] += w0 * x0[u];
+      acc[4 + u] += w0 * x1[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] += w1 * y0[u];
+      acc[4 + u] += w1 * y1[u];
+    }
+  }
+  for (; c < n_chunks; ++c) {
+    const float w0 = __shfl(w, c, 64);
+    const f32x4* p0 = reinterpret_cast<const f32x4*>(
+        a.part_o + (((int64_t)b * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
+    const f32x4 x0 = p0[0], x1 = p0[1];
+    L += w0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      acc[u] += w0 * x0[u];
+      acc[4 + u] += w0 * x1[u];
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;

@@ -164,8 +164,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5"], default="all",
-                    help="limit the run to one workload (profiling)")
+    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "copy"], default="all",
+                    help="limit the run to one workload (profiling); 'copy' runs a plain 1 GiB "
+                         "device copy, the calibration of the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -181,6 +182,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = "cuda"
+    if args.workload == "copy":
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "copy", "bytes_read": 1 << 30, "bytes_written": 1 << 30,
+                          "launches": 3}), flush=True)
+        return
     want = lambda w: args.workload in ("all", w)
     flush_buf = torch.empty(512 * 1024 * 1024, dtype=torch.uint8, device=dev)
     flush = lambda: flush_buf.zero_()
