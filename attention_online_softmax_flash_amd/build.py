@@ -40,9 +40,14 @@ def common_flags() -> list:
     ]
 
 
+# Extra flags per source (none at present).
+EXTRA_FLAGS: dict = {}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = ([hipcc()] + common_flags() + EXTRA_FLAGS.get(src, []) +
+           ["-c", os.path.join(CSRC, src), "-o", obj])
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide d chunks of the score product
   constexpr int DPL = D / 16;  // value columns per lane column (8 for D = 128)
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = uniform(threadIdx.x >> 6);   // wave-uniform: scalar bookkeeping
   const int n = lane & 15;
   const int g = lane >> 4;
 

@@ -109,6 +109,14 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
+// 16 bytes per lane from a buffer straight into LDS (no staging registers):
+// lane l's bytes land at lds + 16 l.  Kept out of kernel templates: the
+// address-space cast is device-only.
+__device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, 0);
+}
+
 // Global loads/stores of 16 and 8 bytes.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

@@ -121,11 +121,13 @@ hipError_t launch_attn_fp32(const AttnArgs& a, hipStream_t s) {
     case 1: attn_fp32<1><<<grid, 256, lds, s>>>(a); break;
     case 2: attn_fp32<2><<<grid, 256, lds, s>>>(a); break;
     case 4: attn_fp32<4><<<grid, 256, lds, s>>>(a); break;
-    case 8:
-      hipFuncSetAttribute((const void*)attn_fp32<8>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                          (int)lds);
+    case 8: {
+      const hipError_t attr = hipFuncSetAttribute(
+          (const void*)attn_fp32<8>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (attr != hipSuccess) return attr;
       attn_fp32<8><<<grid, 256, lds, s>>>(a);
       break;
+    }
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

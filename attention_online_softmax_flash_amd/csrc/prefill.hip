@@ -407,35 +407,34 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 }
 
 template <int D, bool ALIBI, int KVM>
-static void launch_one(const AttnArgs& a, hipStream_t s) {
+static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
   constexpr int lds = PrefillLds<D>::TOTAL;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)prefill_bf16<D, ALIBI, KVM>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    attr_set = true;
-  }
+  // Dynamic LDS above the default limit must be enabled for the kernel (on
+  // the current device); the call is cheap, so it is made on every launch.
+  const hipError_t attr = hipFuncSetAttribute((const void*)prefill_bf16<D, ALIBI, KVM>,
+                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
   prefill_bf16<D, ALIBI, KVM><<<a.n_work, 256, lds, s>>>(a);
+  return hipSuccess;
 }
 
 template <int D, bool ALIBI>
-static void launch_kvm(const AttnArgs& a, hipStream_t s) {
-  if (!a.paged) launch_one<D, ALIBI, 0>(a, s);
-  else if (a.tile_contig) launch_one<D, ALIBI, 1>(a, s);
-  else launch_one<D, ALIBI, 2>(a, s);
+static hipError_t launch_kvm(const AttnArgs& a, hipStream_t s) {
+  if (!a.paged) return launch_one<D, ALIBI, 0>(a, s);
+  if (a.tile_contig) return launch_one<D, ALIBI, 1>(a, s);
+  return launch_one<D, ALIBI, 2>(a, s);
 }
 
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s) {
   if (a.n_work <= 0) return hipSuccess;
   const bool alibi = a.slopes != nullptr;
+  hipError_t e;
   if (a.D == 128) {
-    if (alibi) launch_kvm<128, true>(a, s);
-    else launch_kvm<128, false>(a, s);
+    e = alibi ? launch_kvm<128, true>(a, s) : launch_kvm<128, false>(a, s);
   } else {
-    if (alibi) launch_kvm<64, true>(a, s);
-    else launch_kvm<64, false>(a, s);
+    e = alibi ? launch_kvm<64, true>(a, s) : launch_kvm<64, false>(a, s);
   }
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 }  // namespace fia

@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
   const int n_chunks = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);   // wave-uniform: scalar bookkeeping
   const int n = lane & 31;
   const int hh = lane >> 5;
   const int Lk = sparse_len(a, b);
@@ -312,12 +312,11 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
   if (a.B == 0) return hipSuccess;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipFuncSetAttribute((const void*)sparse_chunk, hipFuncAttributeMaxDynamicSharedMemorySize,
-                        LDS_TOTAL);
-    attr_set = true;
-  }
+  // Dynamic LDS above the default limit must be enabled for the kernel (on
+  // the current device); the call is cheap, so it is made on every launch.
+  const hipError_t attr = hipFuncSetAttribute(
+      (const void*)sparse_chunk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+  if (attr != hipSuccess) return attr;
   dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.B);
   sparse_chunk<<<grid, 256, LDS_TOTAL, s>>>(a);
   return hipGetLastError();
