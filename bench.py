@@ -145,13 +145,20 @@ def cpu_baseline(case, flops):
                       if i.get("user_api") == "blas") or None
     except Exception:
         pass
+    # Whole passes of the oracle over the workload until at least 10 s of CPU
+    # work (at most 30 passes), so the figure is not a one-shot timing.
     t0 = time.perf_counter()
-    O.fia_case(case)
-    secs = time.perf_counter() - t0
-    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": threads or os.cpu_count(),
-            "kind": "oracle", "seconds": round(secs, 3),
-            "sample": "the whole causal GQA prefill workload (4 batches x 32 heads), float64 "
-                      "numpy with materialised scores"}
+    passes = 0
+    while True:
+        O.fia_case(case)
+        passes += 1
+        secs = time.perf_counter() - t0
+        if secs >= 10.0 or passes >= 30:
+            break
+    return {"value": passes * flops / secs / 1e12, "unit": "TFLOP/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle", "seconds": round(secs, 3),
+            "sample": f"{passes} whole passes of the causal GQA prefill workload (4 batches x 32 "
+                      "heads), float64 numpy with materialised scores"}
 
 
 def roofline(bound, achieved, peak, unit, traffic):
