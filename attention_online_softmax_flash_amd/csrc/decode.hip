@@ -21,8 +21,16 @@
 
 namespace fia {
 
+// Slot of 16-byte piece q of staged key row r is q ^ key_swz(r): with PR
+// pieces per row, the 16 rows one operand read touches land in 16 distinct
+// 16-byte groups of the 256-byte bank window.
+template <int PR>
+__device__ __forceinline__ int key_swz(int r) {
+  return (r / (16 / PR)) % PR;
+}
+
 template <int D>
-__global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
+__global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide d chunks of the score product
   constexpr int DPL = D / 16;  // value columns per lane column (8 for D = 128)
   const int lane = threadIdx.x & 63;
@@ -68,6 +76,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Each wave stages its 32-key step of K in its own slice of the combine
+  // buffer (free until the loop ends).  The XOR swizzle makes the operand
+  // reads (16 rows, one piece each) hit 16 distinct 16-byte bank groups.
+  constexpr int PR = D / 8;       // 16-byte pieces per key row
+  constexpr int RPI = 64 / PR;    // key rows per 64-lane load
+  constexpr int NDMA = 32 / RPI;  // loads per 32-key step
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][D + 4];
+  static_assert(sizeof(sm_o[0]) >= 32 * 2 * D, "key slot does not fit");
+  char* kbuf = reinterpret_cast<char*>(&sm_o[wave][0][0]);
+
   const uint16_t* kbase = (const uint16_t*)a.k;
   const uint16_t* vbase = (const uint16_t*)a.v;
 
@@ -94,14 +112,14 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
         rk[hf] = make_rsrc(kbase + ko, kbytes);
         rv[hf] = make_rsrc(vbase + vo, vbytes);
       }
-      // Key operand: key row (16 hf + n), d = 32 cc + 8 g .. +7.
-      u32x4 kr[2][NC];
+      // The 32 key rows go to the wave's LDS slot, whole rows per load
+      // (RPI rows of 16 * PR bytes), piece q of row r stored at q ^ key_swz<PR>(r).
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          kr[hf][cc] = buf_ld16(rk[hf], (uint32_t)(n * a.k_ss + 32 * cc + 8 * g) * 2u);
-        }
+      for (int i = 0; i < NDMA; ++i) {
+        const int r = RPI * i + lane / PR;
+        const int gp = (lane % PR) ^ key_swz<PR>(r);
+        buf_ld16_lds_nt(rk[(RPI * i) >> 4], kbuf + 1024 * i,
+                        (uint32_t)((r & 15) * a.k_ss + 8 * gp) * 2u);
       }
       // Value rows for k-slot s: key 16 (s/4) + 4 g + s%4, columns DPL n ..
       u32x4 vr[8];
@@ -111,19 +129,28 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
         const int t = 4 * g + (s & 3);
         const uint32_t off = (uint32_t)(t * a.v_ss + DPL * n) * 2u;
         if constexpr (DPL == 8) {
-          vr[s] = buf_ld16(rv[hf], off);
+          vr[s] = buf_ld16_nt(rv[hf], off);
         } else {
-          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[hf], off, 0, 0));
+          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[hf], off, 0, 2));
           vr[s] = u32x4{w.x, w.y, 0, 0};
         }
       }
-      // Scores S^T[key 16 hf + 4 g + r][head n].
+      // Every load of the step is in flight before the first staged-key read,
+      // so one wait (the value loads still outstanding) covers the key rows.
+      __builtin_amdgcn_sched_barrier(0);
+      // Scores S^T[key 16 hf + 4 g + r][head n]; key operand: row 16 hf + n,
+      // d = 32 cc + 8 g .. +7 (piece 4 cc + g).
       f32x4 sc[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * hf + n;
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) sc[hf] = mfma16(kr[hf][cc], qv[cc], sc[hf]);
+        for (int cc = 0; cc < NC; ++cc) {
+          const u32x4 kr = *reinterpret_cast<const u32x4*>(kbuf + 16 * PR * r +
+                                                           16 * ((4 * cc + g) ^ key_swz<PR>(r)));
+          sc[hf] = mfma16(kr, qv[cc], sc[hf]);
+        }
       }
       float x[8];
       float mx = kNegInf;
@@ -174,7 +201,6 @@ __global__ __launch_bounds__(256, 2) void decode_split_bf16(AttnArgs a) {
   // Combine the four waves through LDS in wave order.
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
-  __shared__ float sm_o[4][16][D + 4];
   if (g == 0) {
     sm_m[wave][n] = m_run;
     sm_l[wave][n] = l_run;

@@ -108,6 +108,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// Same, with the non-temporal hint (data read once: streamed past the caches).
+__device__ __forceinline__ u32x4 buf_ld16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
 
 // 16 bytes per lane from a buffer straight into LDS (no staging registers):
 // lane l's bytes land at lds + 16 l.  Kept out of kernel templates: the
@@ -115,6 +119,11 @@ __device__ __forceinline__ u32x4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
 __device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
                                            0, 0, 0);
+}
+// Same, with the non-temporal hint.
+__device__ __forceinline__ void buf_ld16_lds_nt(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
+                                           0, 0, 2);
 }
 
 // Global loads/stores of 16 and 8 bytes.
