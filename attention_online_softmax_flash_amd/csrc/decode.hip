@@ -163,8 +163,7 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
         x[s] = ok ? v : kNegInf;
         mx = fmaxf(mx, x[s]);
       }
-      mx = fmaxf(mx, shfl_xor_f(mx, 16));
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx = pair32_max(pair16_max(mx));
       const float m_new = fmaxf(m_run, mx);
       const float m_use = (m_new == kNegInf) ? 0.f : m_new;
       const float alpha = fast_exp2(m_run - m_use);
@@ -195,8 +194,7 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
       }
     }
   }
-  l_run += shfl_xor_f(l_run, 16);
-  l_run += shfl_xor_f(l_run, 32);
+  l_run = pair32_sum(pair16_sum(l_run));
 
   // Combine the four waves through LDS in wave order.
   __shared__ float sm_m[4][16];

@@ -62,6 +62,27 @@ __device__ __forceinline__ uint32_t pick_hi(uint32_t a, uint32_t b) {
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
+// Max / sum over lane pairs (l, l ^ 32) and (l, l ^ 16) by register lane swaps
+// (v_permlane32_swap / v_permlane16_swap) instead of an LDS permute: with the
+// same value in both operands, lane l ends up with its own value in one result
+// and its partner's in the other.
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 __device__ __forceinline__ uint32_t fast_div(uint32_t n, const FastDiv& f) {
   return (uint32_t)(((uint64_t)n * f.mul) >> (32 + f.shift));
 }

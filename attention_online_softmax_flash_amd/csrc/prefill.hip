@@ -37,7 +37,7 @@ constexpr int BN = kPrefillKeys;  // 64
 template <int D>
 struct PrefillLds {
   static constexpr int K_PITCH = D * 2 + 16;    // bytes per key row
-  static constexpr int V_PITCH = BN * 2 + 8;    // bytes per transposed value row
+  static constexpr int V_PITCH = BN * 2 + 16;   // bytes per transposed value row
   static constexpr int K_BYTES = BN * K_PITCH;
   static constexpr int V_BYTES = D * V_PITCH;
   static constexpr int STAGE = K_BYTES + V_BYTES;
@@ -148,9 +148,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     uint32_t voffs[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) voffs[q] = (uint32_t)((4 * va + q) * a.v_ss + 8 * vq) * 2u;
-    const uint32_t vs_addr = (uint32_t)(L::K_BYTES + 8 * vq * L::V_PITCH + va * 8);
+    // Transposed value rows keep keys in the order the score accumulators
+    // hold them: inside each 16-key group, key 8 b3 + 4 b2 + (0..3) sits at
+    // 8 b2 + 4 b3 + (0..3), so the 8 keys one lane feeds to a k-step of the
+    // value product are one contiguous 16-byte piece.
+    const int va_pos = 4 * (va & ~3) + 4 * (((va & 1) << 1) | ((va >> 1) & 1));
+    const uint32_t vs_addr = (uint32_t)(L::K_BYTES + 8 * vq * L::V_PITCH + va_pos * 2);
     const uint32_t kr_addr = (uint32_t)(n * L::K_PITCH + 16 * hh);
-    const uint32_t vr_addr = (uint32_t)(L::K_BYTES + n * L::V_PITCH + 8 * hh);
+    const uint32_t vr_addr = (uint32_t)(L::K_BYTES + n * L::V_PITCH + 16 * hh);
     TileRegs<D> regs;
 
     auto load_tile = [&](int kt) {
@@ -276,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           }
         }
       }
-      mx = fmaxf(mx, shfl_xor_f(mx, 32));
+      mx = pair32_max(mx);
       // Lazy rescale: keep the running max m_run unless a row's new max
       // exceeds it by more than 8 (probabilities stay <= 2^8).
       const bool grow = mx > m_run + 8.f;
@@ -315,9 +320,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
           const uint8_t* vp = vb + 32 * mb * L::V_PITCH + 32 * kk;
-          const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vp);
-          const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vp + 16);
-          o[mb] = mfma32(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, pb[kk], o[mb]);
+          o[mb] = mfma32(*reinterpret_cast<const u32x4*>(vp), pb[kk], o[mb]);
         }
       }
       // Interleave: one MFMA, a few VALU, one LDS read, repeated.
@@ -383,7 +386,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   }
 
   // Epilogue: normalise and write this lane's row.
-  const float l_tot = l_run + shfl_xor_f(l_run, 32);
+  const float l_tot = pair32_sum(l_run);
   const bool has = row_live && m_run != kNegInf && l_tot > 0.f;
   const float inv = has ? 1.f / l_tot : 0.f;
   if (i < write_rows) {

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
       s[r] = ids[slot] >= 0 ? x : kNegInf;
       m_loc = fmaxf(m_loc, s[r]);
     }
-    m_loc = fmaxf(m_loc, shfl_xor_f(m_loc, 32));
+    m_loc = pair32_max(m_loc);
     if (hh == 0) mx_s[sb * 32 + n] = m_loc;
   }
   __syncthreads();
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
       ps[(2 * sb + kk) * 64 + lane] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                                            pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
     }
-    l += shfl_xor_f(l, 32);
+    l = pair32_sum(l);
     if (hh == 0) l_s[sb * 32 + n] = l;
   }
   __syncthreads();
