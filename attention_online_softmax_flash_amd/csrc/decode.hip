@@ -21,14 +21,6 @@
 
 namespace fia {
 
-// Slot of 16-byte piece q of staged key row r is q ^ key_swz(r): with PR
-// pieces per row, the 16 rows one operand read touches land in 16 distinct
-// 16-byte groups of the 256-byte bank window.
-template <int PR>
-__device__ __forceinline__ int key_swz(int r) {
-  return (r / (16 / PR)) % PR;
-}
-
 template <int D>
 __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide d chunks of the score product

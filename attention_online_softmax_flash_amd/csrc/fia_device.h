@@ -7,6 +7,10 @@
 
 #include "fia_internal.h"
 
+// Helper lambdas inside kernels are force-inlined: their captures then stay
+// in registers instead of going through private memory.
+#define FIA_INLINE __attribute__((always_inline))
+
 namespace fia {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -145,6 +149,15 @@ __device__ __forceinline__ void buf_ld16_lds(__amdgpu_buffer_rsrc_t r, void* lds
 __device__ __forceinline__ void buf_ld16_lds_nt(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off,
                                            0, 0, 2);
+}
+
+// XOR swizzle of key rows staged in LDS without padding: 16-byte piece q of
+// row r sits in slot q ^ key_swz<PR>(r), PR = pieces per row.  The 16 rows
+// that one 16-lane group of an MFMA operand read touches (same piece) then
+// land in 16 distinct 16-byte groups of the 256-byte bank window.
+template <int PR>
+__device__ __forceinline__ int key_swz(int r) {
+  return (r / (16 / PR)) % PR;
 }
 
 // Global loads/stores of 16 and 8 bytes.

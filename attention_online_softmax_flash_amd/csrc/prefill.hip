@@ -36,12 +36,10 @@ constexpr int BN = kPrefillKeys;  // 64
 
 template <int D>
 struct PrefillLds {
-  static constexpr int K_PITCH = D * 2 + 16;    // bytes per key row
+  static constexpr int K_ROW = D * 2;           // bytes per key row (swizzled, no padding)
+  static constexpr int K_BYTES = BN * K_ROW;
   static constexpr int V_PITCH = BN * 2 + 16;   // bytes per transposed value row
-  static constexpr int K_BYTES = BN * K_PITCH;
   static constexpr int V_BYTES = D * V_PITCH;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int TOTAL = 2 * STAGE;
 };
 
 template <int D>
@@ -57,6 +55,11 @@ struct TileRegs {
 // one strided run, its base advances by pointer arithmetic), 1 paged with
 // block_size a multiple of 64 (a tile lies in one page, one table lookup per
 // tile), 2 any paged layout (per-row lookup).
+//
+// Key tiles go global -> LDS by buffer-to-LDS loads (KVM 0 / 1) or through
+// registers (KVM 2); value tiles go through registers, transposed on the way
+// in.  Each stage is its own LDS array, so the compiler's wait for an
+// outstanding buffer-to-LDS load only guards reads of that stage.
 template <int D, bool ALIBI, int KVM>
 __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   using L = PrefillLds<D>;
@@ -64,12 +67,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   constexpr int NMB = D / 32;  // 32-wide d blocks of the output
   constexpr int DCH = D / 8;   // 16-byte pieces per row
   constexpr int NK = TileRegs<D>::NK;
+  constexpr int RPI = 64 / DCH;   // key rows per 64-lane buffer-to-LDS load
+  constexpr bool DMA_K = KVM != 2;
   // PIPE: the score product of tile t+1 is issued together with the softmax
   // of tile t (needs a second score buffer; too many registers with the ALiBi
   // bias or per-row paging, which compute each tile's scores up front).
   constexpr bool PIPE = !ALIBI && KVM != 2;
   constexpr bool INTERLEAVE = PIPE;
-  extern __shared__ __align__(16) uint8_t lds[];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[L::K_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[L::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[L::V_BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -135,16 +143,35 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     const uint16_t* kbase0 = kg + (int64_t)b * a.k_sb + (int64_t)kv_off * a.k_ss + (int64_t)kvh * a.k_sh;
     const uint16_t* vbase0 = vg + (int64_t)b * a.v_sb + (int64_t)kv_off * a.v_ss + (int64_t)kvh * a.v_sh;
 
-    // Thread roles for staging one tile, with loop-invariant offsets.
-    const int va = tid & 15;   // keys 4 va .. 4 va + 3 of the value tile
-    const int vq = tid >> 4;   // 16-byte value column piece
-    uint32_t koffs[NK], ks_addr[NK];
+    // Key staging.  Buffer-to-LDS load q of wave w fills rows RPI (4 q + w)
+    // .. + RPI - 1 of the tile (1 KiB, lane l -> slot l % DCH of row
+    // l / DCH), fetching the global piece that belongs in that slot.  With
+    // registers (KVM 2), thread u = tid + 256 q holds piece u % DCH of row
+    // u / DCH and stores it into its slot.
+    uint32_t koffs[NK];
 #pragma unroll
     for (int q = 0; q < NK; ++q) {
-      const int u = tid + 256 * q;
-      koffs[q] = (uint32_t)((u / DCH) * a.k_ss + 8 * (u % DCH)) * 2u;
-      ks_addr[q] = (uint32_t)((u / DCH) * L::K_PITCH + (u % DCH) * 16);
+      if constexpr (DMA_K) {
+        const int r = RPI * (4 * q + wave) + lane / DCH;
+        const int gp = (lane % DCH) ^ key_swz<DCH>(r);
+        koffs[q] = (uint32_t)(r * a.k_ss + 8 * gp) * 2u;
+      } else {
+        const int u = tid + 256 * q;
+        const int r = u / DCH;
+        koffs[q] = (uint32_t)(r * L::K_ROW + 16 * ((u % DCH) ^ key_swz<DCH>(r)));
+      }
     }
+    // Score-operand reads: lane (n, hh) reads piece 2 c + hh of key rows
+    // 32 k2 + n, which all share the swizzle of row n.
+    uint32_t kr_addr[NQ];
+    {
+      const int sw = key_swz<DCH>(n);
+#pragma unroll
+      for (int c = 0; c < NQ; ++c) kr_addr[c] = (uint32_t)(n * L::K_ROW + 16 * ((2 * c + hh) ^ sw));
+    }
+    // Thread roles for the value tile.
+    const int va = tid & 15;   // keys 4 va .. 4 va + 3 of the value tile
+    const int vq = tid >> 4;   // 16-byte value column piece
     uint32_t voffs[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) voffs[q] = (uint32_t)((4 * va + q) * a.v_ss + 8 * vq) * 2u;
@@ -153,12 +180,33 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     // 8 b2 + 4 b3 + (0..3), so the 8 keys one lane feeds to a k-step of the
     // value product are one contiguous 16-byte piece.
     const int va_pos = 4 * (va & ~3) + 4 * (((va & 1) << 1) | ((va >> 1) & 1));
-    const uint32_t vs_addr = (uint32_t)(L::K_BYTES + 8 * vq * L::V_PITCH + va_pos * 2);
-    const uint32_t kr_addr = (uint32_t)(n * L::K_PITCH + 16 * hh);
-    const uint32_t vr_addr = (uint32_t)(L::K_BYTES + n * L::V_PITCH + 16 * hh);
+    const uint32_t vs_addr = (uint32_t)(8 * vq * L::V_PITCH + va_pos * 2);
+    const uint32_t vr_addr = (uint32_t)(n * L::V_PITCH + 16 * hh);
     TileRegs<D> regs;
 
-    auto load_tile = [&](int kt) {
+    // Resources (or, for KVM 2, register loads) of key / value tile kt.
+    // Rows >= Lk fall outside the resources and read as zero.
+    auto tile_rsrc = [&](int kt, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) FIA_INLINE {
+      const int j0 = kt * BN;
+      const uint16_t* kp;
+      const uint16_t* vp;
+      if constexpr (KVM == 0) {
+        kp = kbase0 + (int64_t)j0 * a.k_ss;
+        vp = vbase0 + (int64_t)j0 * a.v_ss;
+      } else {
+        const uint32_t page = fast_div((uint32_t)j0, a.bs_div);
+        const int blk = clamp_block(a.block_table[(int64_t)b * a.bt_sb + page], a.n_blocks);
+        const int slot = j0 - (int)page * a.block_size;
+        kp = kg + paged_row_offset(blk, slot, kvh, a.k_sb, a.k_ss, a.k_sh);
+        vp = vg + paged_row_offset(blk, slot, kvh, a.v_sb, a.v_ss, a.v_sh);
+      }
+      const int nvalid = min(BN, Lk - j0);
+      rk = make_rsrc(kp, (uint32_t)((nvalid - 1) * a.k_ss + D) * 2u);
+      rv = make_rsrc(vp, (uint32_t)((nvalid - 1) * a.v_ss + D) * 2u);
+    };
+    // Global loads of tile kt: keys straight into stage `kdst` (KVM 0 / 1)
+    // or into registers, values into registers.
+    auto load_tile = [&](int kt, uint8_t* kdst) FIA_INLINE {
       const int j0 = kt * BN;
       if constexpr (KVM == 2) {
 #pragma unroll
@@ -179,34 +227,31 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           }
         }
       } else {
-        const uint16_t* kp;
-        const uint16_t* vp;
-        if constexpr (KVM == 0) {
-          kp = kbase0 + (int64_t)j0 * a.k_ss;
-          vp = vbase0 + (int64_t)j0 * a.v_ss;
-        } else {
-          const uint32_t page = fast_div((uint32_t)j0, a.bs_div);
-          const int blk = clamp_block(a.block_table[(int64_t)b * a.bt_sb + page], a.n_blocks);
-          const int slot = j0 - (int)page * a.block_size;
-          kp = kg + paged_row_offset(blk, slot, kvh, a.k_sb, a.k_ss, a.k_sh);
-          vp = vg + paged_row_offset(blk, slot, kvh, a.v_sb, a.v_ss, a.v_sh);
-        }
-        // Rows >= Lk fall outside the resource and read as zero.
-        const int nvalid = min(BN, Lk - j0);
-        const auto rk = make_rsrc(kp, (uint32_t)((nvalid - 1) * a.k_ss + D) * 2u);
-        const auto rv = make_rsrc(vp, (uint32_t)((nvalid - 1) * a.v_ss + D) * 2u);
+        __amdgpu_buffer_rsrc_t rk, rv;
+        tile_rsrc(kt, rk, rv);
+        if (kdst != nullptr) {
 #pragma unroll
-        for (int q = 0; q < NK; ++q) regs.k[q] = buf_ld16(rk, koffs[q]);
+          for (int q = 0; q < NK; ++q) buf_ld16_lds(rk, kdst + 1024 * (4 * q + wave), koffs[q]);
+        }
         if (vq < DCH) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) regs.v[q] = buf_ld16(rv, voffs[q]);
         }
       }
     };
-    auto store_tile = [&](int stage) {
-      uint8_t* base = lds + stage * L::STAGE;
+    // Keys of tile kt into stage `kdst` by buffer-to-LDS loads alone.
+    auto load_k_lds = [&](int kt, uint8_t* kdst) FIA_INLINE {
+      __amdgpu_buffer_rsrc_t rk, rv;
+      tile_rsrc(kt, rk, rv);
 #pragma unroll
-      for (int q = 0; q < NK; ++q) *reinterpret_cast<u32x4*>(base + ks_addr[q]) = regs.k[q];
+      for (int q = 0; q < NK; ++q) buf_ld16_lds(rk, kdst + 1024 * (4 * q + wave), koffs[q]);
+    };
+    // Register-staged parts of a tile into their stages.
+    auto store_tile = [&](uint8_t* kst, uint8_t* vst) FIA_INLINE {
+      if constexpr (KVM == 2) {
+#pragma unroll
+        for (int q = 0; q < NK; ++q) *reinterpret_cast<u32x4*>(kst + koffs[q]) = regs.k[q];
+      }
       if (vq < DCH) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -217,38 +262,38 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           } else {
             pr = u32x2{pick_lo(regs.v[0][w], regs.v[1][w]), pick_lo(regs.v[2][w], regs.v[3][w])};
           }
-          *reinterpret_cast<u32x2*>(base + vs_addr + e * L::V_PITCH) = pr;
+          *reinterpret_cast<u32x2*>(vst + vs_addr + e * L::V_PITCH) = pr;
         }
       }
     };
 
     // S^T of one tile for this wave: 2 key blocks x 32 query rows.
-    auto compute_s = [&](int stage, f32x16* sv) {
-      const uint8_t* kb = lds + stage * L::STAGE + kr_addr;
+    auto compute_s = [&](const uint8_t* kst, f32x16* sv) FIA_INLINE {
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        const uint8_t* kr = kb + 32 * k2 * L::K_PITCH;
-        sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kr), qreg[0], f32x16{});
+        sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[0] + 32 * k2 * L::K_ROW), qreg[0],
+                        f32x16{});
       }
 #pragma unroll
       for (int c = 1; c < NQ; ++c) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          const uint8_t* kr = kb + 32 * k2 * L::K_PITCH;
-          sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kr + 32 * c), qreg[c], sv[k2]);
+          sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[c] + 32 * k2 * L::K_ROW),
+                          qreg[c], sv[k2]);
         }
       }
     };
-    auto wave_skip = [&](int kt) {
+    auto wave_skip = [&](int kt) FIA_INLINE {
       const int j0 = kt * BN;
       return (wrows_end <= iw0) || (j0 + BN <= wlo_min) || (j0 >= whi_max);
     };
 
-    // Softmax of tile kt (scores in sc), then O += V^T P^T from `stage`.  When
-    // `next_stage` >= 0 the score product of the next tile is issued inside
-    // the same straight-line block, so its MFMAs overlap this tile's VALU work.
-    auto tile_body = [&](auto masked_tag, int kt, int stage, f32x16* sc, int next_stage,
-                         f32x16* sn) {
+    // Softmax of tile kt (scores in sc), then O += V^T P^T from `vst`.  With
+    // `knext` set the score product of the next tile (keys in `knext`) is
+    // issued inside the same straight-line block, so its MFMAs overlap this
+    // tile's VALU work.
+    auto tile_body = [&](auto masked_tag, int kt, const uint8_t* vst, f32x16* sc,
+                         const uint8_t* knext, f32x16* sn) FIA_INLINE {
       constexpr bool MASKED = decltype(masked_tag)::value;
       constexpr bool PLAIN = !ALIBI && !MASKED;
       const int j0 = kt * BN;
@@ -295,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       }
       const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
       if constexpr (PIPE) {
-        if (next_stage >= 0) compute_s(next_stage, sn);
+        if (knext != nullptr) compute_s(knext, sn);
       }
       float psum = 0.f;
       u32x4 pb[4];
@@ -314,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
       }
       l_run += psum;
-      const uint8_t* vb = lds + stage * L::STAGE + vr_addr;
+      const uint8_t* vb = vst + vr_addr;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
@@ -334,54 +379,61 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       }
     };
 
-    // Software pipeline over key tiles, two LDS stages.  Iteration kt holds the
-    // scores of tile kt in registers, tile kt+1 in LDS stage `nstage`, and the
-    // global loads of tile kt+2 in flight; it computes softmax(kt) + PV(kt)
-    // together with the score product of tile kt+1, then stores tile kt+2 into
-    // the stage tile kt used.
+    // Software pipeline over key tiles, two stages (stage of tile kt:
+    // (kt - kt0) & 1).  Step kt holds the scores of tile kt in registers
+    // (with PIPE), issues the loads of tile kt + 2 and computes softmax(kt) +
+    // PV(kt) together with the score product of tile kt + 1; one barrier
+    // ends it, after which tile kt + 2's register-staged parts are stored
+    // into the stage tile kt used.  With PIPE the keys of tile kt were
+    // consumed one step earlier, so their stage is refilled from the start of
+    // step kt; otherwise the key loads go out after the barrier.
     const int kt0 = klo / BN;
     const int kt1 = (khi + BN - 1) / BN;
-    load_tile(kt0);
-    store_tile(0);
-    if (kt0 + 1 < kt1) load_tile(kt0 + 1);
+    const bool has1 = kt0 + 1 < kt1;
+    load_tile(kt0, lds_k0);
+    if (PIPE && DMA_K && has1) load_k_lds(kt0 + 1, lds_k1);
+    __syncthreads();   // waits for every load so far
+    store_tile(lds_k0, lds_v0);
+    if (has1) load_tile(kt0 + 1, (!PIPE && DMA_K) ? lds_k1 : nullptr);
     __syncthreads();
     f32x16 s_a[2], s_b[2];
     bool cur_skip = wave_skip(kt0);
-    if (PIPE && !cur_skip) compute_s(0, s_a);
-    if (kt0 + 1 < kt1) store_tile(1);
+    if (PIPE && !cur_skip) compute_s(lds_k0, s_a);
+    if (has1) store_tile(lds_k1, lds_v1);
     __syncthreads();
 
-    // One pipeline step; the loop below is unrolled by two so the roles of
-    // the two score buffers stay static (they live in registers).
-    auto step = [&](int kt, f32x16* sc, f32x16* sn) {
-      const int stage = (kt - kt0) & 1;
+    auto step = [&](auto stage_tag, int kt, f32x16* sc, f32x16* sn) FIA_INLINE {
+      constexpr int S = decltype(stage_tag)::value;
+      uint8_t* kst = S ? lds_k1 : lds_k0;
+      uint8_t* vst = S ? lds_v1 : lds_v0;
+      uint8_t* knx = S ? lds_k0 : lds_k1;
       const bool has_next = kt + 1 < kt1;
       const bool has_next2 = kt + 2 < kt1;
-      if (has_next2) load_tile(kt + 2);
+      if (has_next2) load_tile(kt + 2, (PIPE && DMA_K) ? kst : nullptr);
       const bool next_skip = has_next ? wave_skip(kt + 1) : true;
-      const int nstage = (!PIPE || next_skip) ? -1 : (stage ^ 1);
-      if (!PIPE && !cur_skip) compute_s(stage, sc);
+      const uint8_t* knext = (!PIPE || next_skip) ? nullptr : knx;
+      if (!PIPE && !cur_skip) compute_s(kst, sc);
       if (!cur_skip) {
         const int j0 = kt * BN;
         const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min);
         if (need_mask) {
-          tile_body(std::true_type{}, kt, stage, sc, nstage, sn);
+          tile_body(std::true_type{}, kt, vst, sc, knext, sn);
         } else {
-          tile_body(std::false_type{}, kt, stage, sc, nstage, sn);
+          tile_body(std::false_type{}, kt, vst, sc, knext, sn);
         }
-      } else if (PIPE && nstage >= 0) {
-        compute_s(nstage, sn);
+      } else if (PIPE && knext != nullptr) {
+        compute_s(knext, sn);
       }
       cur_skip = next_skip;
+      __syncthreads();   // loads of tile kt + 2 landed; every wave is done with tile kt
       if (has_next2) {
-        __syncthreads();   // every wave is done with this stage
-        store_tile(stage);
+        if constexpr (!PIPE && DMA_K) load_k_lds(kt + 2, kst);
+        store_tile(kst, vst);
       }
-      __syncthreads();
     };
     for (int kt = kt0; kt < kt1; kt += 2) {
-      step(kt, s_a, s_b);
-      if (kt + 1 < kt1) step(kt + 1, s_b, s_a);
+      step(std::integral_constant<int, 0>{}, kt, s_a, s_b);
+      if (kt + 1 < kt1) step(std::integral_constant<int, 1>{}, kt + 1, s_b, s_a);
     }
   }
 
@@ -411,13 +463,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 
 template <int D, bool ALIBI, int KVM>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  constexpr int lds = PrefillLds<D>::TOTAL;
-  // Dynamic LDS above the default limit must be enabled for the kernel (on
-  // the current device); the call is cheap, so it is made on every launch.
-  const hipError_t attr = hipFuncSetAttribute((const void*)prefill_bf16<D, ALIBI, KVM>,
-                                              hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (attr != hipSuccess) return attr;
-  prefill_bf16<D, ALIBI, KVM><<<a.n_work, 256, lds, s>>>(a);
+  prefill_bf16<D, ALIBI, KVM><<<a.n_work, 256, 0, s>>>(a);
   return hipSuccess;
 }
 
