@@ -14,10 +14,10 @@
 // [rope | nope * scale].
 //
 // One workgroup takes 64 slots x 32 heads of one batch entry: it gathers the
-// rows through the block tables, dequantises them into LDS twice (row-major
-// for the score product, transposed for the value product), runs both
-// products on 32x32x16 bf16 MFMA and writes a normalised partial with its
-// log2-sum-exp.  The merge kernel folds the chunks in slot order together with
+// rows through the block tables, dequantises them into LDS once (row-major),
+// runs both products on 32x32x16 bf16 MFMA (the value product reads its
+// transposed operand with LDS transpose reads) and writes a normalised
+// partial with its log2-sum-exp.  The merge kernel folds the chunks in slot order together with
 // the sink: an extra logit sigma_h whose value vector is zero.
 #include "fia_device.h"
 
@@ -26,53 +26,73 @@ namespace fia {
 namespace {
 
 constexpr int X_PITCH = kSparseD * 2 + 16;   // bytes per row-major row
-constexpr int XT_PITCH = kSparseChunk * 2 + 8; // bytes per transposed row
 constexpr int X_BYTES = kSparseChunk * X_PITCH;
-constexpr int XT_BYTES = kSparseD * XT_PITCH;
 constexpr int P_BYTES = 4 * 64 * 16;
 constexpr int SX_BYTES = 2 * 64 * 16 * 4;
-constexpr int LDS_TOTAL = X_BYTES + XT_BYTES + P_BYTES + SX_BYTES + 64 * 4 + 2 * 32 * 4 * 2;
+constexpr int LDS_TOTAL = X_BYTES + P_BYTES + SX_BYTES + 64 * 4 + 2 * 32 * 4 * 2;
 
 }  // namespace
 
-// OCP e4m3fn code -> float (exact): exponent field 0 is subnormal m * 2^-9,
-// 0x7f / 0xff are NaN, otherwise (1 + m/8) * 2^(e-7).
-__device__ __forceinline__ float e4m3fn_to_f32(uint32_t x) {
-  const uint32_t e = (x >> 3) & 15u;
-  const uint32_t m = x & 7u;
-  float mag = (e == 0u) ? (float)m * 0.001953125f : __uint_as_float(((e + 120u) << 23) | (m << 20));
-  if ((x & 0x7fu) == 0x7fu) mag = __builtin_nanf("");
-  return (x & 0x80u) ? -mag : mag;
+// Four OCP e4m3fn codes (one dword) -> floats, by the hardware conversion
+// (v_cvt_pk_f32_fp8; exact: subnormals m * 2^-9, 0x7f / 0xff are NaN).
+__device__ __forceinline__ void e4m3fn_x4(uint32_t w, float* f) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+  f[0] = lo[0];
+  f[1] = lo[1];
+  f[2] = hi[0];
+  f[3] = hi[1];
 }
 
-// Slot s of batch b -> packed row address (nullptr for an unused slot) and its
-// id: j for window row j, (1 << 30) | c for compressed row c, -1 if unused.
-__device__ __forceinline__ const uint8_t* sparse_slot_row(const SparseArgs& a, int b, int s,
-                                                          int Lk, int32_t* id) {
-  *id = -1;
-  if (s < a.n_win_slots) {
-    const int p = Lk - 1;
-    const int j = p - a.win_left + s;
-    const int jmax = min(Lk - 1, p + a.win_right);
-    if (s > a.win_left + a.win_right || j < 0 || j > jmax) return nullptr;
-    int page = j / a.bs1;
-    const int slot = j - page * a.bs1;
-    if (page >= a.ori_bt_cols) page = a.ori_bt_cols - 1;
-    const int blk = clamp_block(a.ori_bt[(int64_t)b * a.ori_bt_sb + page], a.nb1);
-    *id = j;
-    return a.ori + (int64_t)blk * a.ori_sb + (int64_t)slot * a.ori_ss;
-  }
-  const int k = s - a.n_win_slots;
-  if (!a.has_cmp || k >= a.K2) return nullptr;
-  const int c = a.idx[(int64_t)b * a.idx_sb + k];
+// Slots s[0..N) of batch b -> packed row addresses (nullptr for an unused
+// slot) and ids: j for window row j, (1 << 30) | c for compressed row c, -1
+// if unused.  No read depends on a branch: every table read goes to an
+// in-bounds address (a clamped position), so the N index reads, then the N
+// block-table reads, are each in flight together.
+template <int N>
+__device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int b, const int* s, int Lk,
+                                                 const uint8_t** row, int32_t* id) {
+  const int p = Lk - 1;
+  const int jmax = min(Lk - 1, p + a.win_right);
   const int n_cmp = Lk / a.cmp_ratio;
-  if (c < 0 || c >= n_cmp) return nullptr;
-  int page = c / a.bs2;
-  const int slot = c - page * a.bs2;
-  if (page >= a.cmp_bt_cols) page = a.cmp_bt_cols - 1;
-  const int blk = clamp_block(a.cmp_bt[(int64_t)b * a.cmp_bt_sb + page], a.nb2);
-  *id = (1 << 30) | c;
-  return a.cmp + (int64_t)blk * a.cmp_sb + (int64_t)slot * a.cmp_ss;
+  const bool cmp_on = a.has_cmp && a.K2 > 0;
+  int c[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const int k = min(max(s[u] - a.n_win_slots, 0), a.K2 > 0 ? a.K2 - 1 : 0);
+    c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + k] : -1;
+  }
+  int raw[N], slot[N];
+  bool win[N], ok[N];
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    win[u] = s[u] < a.n_win_slots;
+    const int j = p - a.win_left + s[u];
+    const int k = s[u] - a.n_win_slots;
+    const bool wok = s[u] <= a.win_left + a.win_right && j >= 0 && j <= jmax;
+    const bool cok = cmp_on && k < a.K2 && c[u] >= 0 && c[u] < n_cmp;
+    ok[u] = win[u] ? wok : cok;
+    const int r = ok[u] ? (win[u] ? j : c[u]) : 0;
+    const int bs = win[u] ? a.bs1 : a.bs2;
+    const int page = r / bs;
+    slot[u] = r - page * bs;
+    // Compressed slots read the compressed table only when there is one.
+    const bool use_cmp = !win[u] && cmp_on;
+    const int cols = use_cmp ? a.cmp_bt_cols : a.ori_bt_cols;
+    const int32_t* bt = use_cmp ? a.cmp_bt + (int64_t)b * a.cmp_bt_sb : a.ori_bt + (int64_t)b * a.ori_bt_sb;
+    raw[u] = bt[min(page, cols - 1)];
+    id[u] = ok[u] ? (win[u] ? j : ((1 << 30) | c[u])) : -1;
+  }
+#pragma unroll
+  for (int u = 0; u < N; ++u) {
+    const uint8_t* r;
+    if (win[u]) {
+      r = a.ori + (int64_t)clamp_block(raw[u], a.nb1) * a.ori_sb + (int64_t)slot[u] * a.ori_ss;
+    } else {
+      r = a.cmp + (int64_t)clamp_block(raw[u], a.nb2) * a.cmp_sb + (int64_t)slot[u] * a.cmp_ss;
+    }
+    row[u] = ok[u] ? r : nullptr;
+  }
 }
 
 __device__ __forceinline__ int sparse_len(const SparseArgs& a, int b) {
@@ -81,14 +101,23 @@ __device__ __forceinline__ int sparse_len(const SparseArgs& a, int b) {
   return Lk < 0 ? 0 : (Lk > cap ? cap : Lk);
 }
 
+// Four 16-bit values by an LDS transpose read (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane i receives value t from position i % 4 of the
+// 8-byte piece addressed by lane 4 t + i / 4 of the group.
+__device__ __forceinline__ u32x2 lds_tr16(const void* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Grid: (n_slots / 64, N1 / 32, B); 256 threads.
-__global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
+__global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xs = lds;                         // [64][X_PITCH]
-  uint8_t* xts = xs + X_BYTES;               // [512][XT_PITCH]
-  u32x4* ps = reinterpret_cast<u32x4*>(xts + XT_BYTES);      // [4][64]
-  float* sx = reinterpret_cast<float*>(xts + XT_BYTES + P_BYTES);  // [2][64][16]
-  int32_t* ids = reinterpret_cast<int32_t*>(xts + XT_BYTES + P_BYTES + SX_BYTES);  // [64]
+  u32x4* ps = reinterpret_cast<u32x4*>(xs + X_BYTES);        // [4][64]
+  float* sx = reinterpret_cast<float*>(xs + X_BYTES + P_BYTES);  // [2][64][16]
+  int32_t* ids = reinterpret_cast<int32_t*>(xs + X_BYTES + P_BYTES + SX_BYTES);  // [64]
   float* mx_s = reinterpret_cast<float*>(ids + 64);          // [2][32]
   float* l_s = mx_s + 64;                                    // [2][32]
 
@@ -117,56 +146,64 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
   }
 
   // 1. Gather and dequantise: thread owns rows 4 rg .. 4 rg + 3 and the
-  // 8-element pieces pc = tid/16 + 16 q of them.
+  // 16-byte pieces pc = tid/16 + 16 q of their bf16 form (pieces 0..7 rope,
+  // 8..63 nope: 8 fp8 codes and their tile scale).  Every load is issued
+  // before the first conversion; unused slots read row 0 of the original KV
+  // (in bounds) and are zeroed.
   {
     const int rg = tid & 15;
+    const int pc0 = tid >> 4;
+    const bool rope0 = pc0 < 8;   // wave-uniform: waves 0, 1
+    int sl[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) sl[u] = s0 + 4 * rg + u;
     const uint8_t* rows[4];
+    int32_t rid[4];
+    sparse_slot_rows<4>(a, b, sl, Lk, rows, rid);
+    if (pc0 == 0) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) ids[4 * rg + u] = rid[u];
+    }
+    u32x4 raw0[4];
+    float sc0[4];
+    u32x2 codes[3][4];
+    float scl[3][4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      int32_t id;
-      rows[u] = sparse_slot_row(a, b, s0 + 4 * rg + u, Lk, &id);
-      if ((tid >> 4) == 0) ids[4 * rg + u] = id;
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int pc = (tid >> 4) + 16 * q;
-      uint32_t w[4][4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (rows[u] == nullptr) {
-          w[u][0] = w[u][1] = w[u][2] = w[u][3] = 0u;
-        } else if (pc < 8) {
-          const u32x4 v = ld16(rows[u] + 16 * pc);
-          w[u][0] = v.x;
-          w[u][1] = v.y;
-          w[u][2] = v.z;
-          w[u][3] = v.w;
-        } else {
-          const int np = pc - 8;
-          const u32x2 codes = ld8(rows[u] + 128 + 8 * np);
-          const float sc = *reinterpret_cast<const float*>(rows[u] + 576 + 4 * (np >> 3));
-          float f[8];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            f[e] = e4m3fn_to_f32((codes.x >> (8 * e)) & 0xffu) * sc;
-            f[4 + e] = e4m3fn_to_f32((codes.y >> (8 * e)) & 0xffu) * sc;
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) w[u][e] = pack_bf16x2(f[2 * e], f[2 * e + 1]);
-        }
-        *reinterpret_cast<u32x4*>(xs + (4 * rg + u) * X_PITCH + 16 * pc) =
-            u32x4{w[u][0], w[u][1], w[u][2], w[u][3]};
+      const uint8_t* rp = rows[u] != nullptr ? rows[u] : a.ori;
+      if (rope0) {
+        raw0[u] = ld16(rp + 16 * pc0);
+        sc0[u] = 0.f;
+      } else {
+        const u32x2 cw = ld8(rp + 128 + 8 * (pc0 - 8));
+        raw0[u] = u32x4{cw.x, cw.y, 0u, 0u};
+        sc0[u] = *reinterpret_cast<const float*>(rp + 576 + 4 * ((pc0 - 8) >> 3));
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int ww = e >> 1;
-        u32x2 pr;
-        if (e & 1) {
-          pr = u32x2{pick_hi(w[0][ww], w[1][ww]), pick_hi(w[2][ww], w[3][ww])};
-        } else {
-          pr = u32x2{pick_lo(w[0][ww], w[1][ww]), pick_lo(w[2][ww], w[3][ww])};
-        }
-        *reinterpret_cast<u32x2*>(xts + (8 * pc + e) * XT_PITCH + 8 * rg) = pr;
+      for (int q = 1; q < 4; ++q) {
+        const int np = pc0 + 16 * q - 8;
+        codes[q - 1][u] = ld8(rp + 128 + 8 * np);
+        scl[q - 1][u] = *reinterpret_cast<const float*>(rp + 576 + 4 * (np >> 3));
+      }
+    }
+    auto dequant = [&](u32x2 cw, float sc) FIA_INLINE {
+      float f[8];
+      e4m3fn_x4(cw.x, f);
+      e4m3fn_x4(cw.y, f + 4);
+      return u32x4{pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
+                   pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)};
+    };
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      uint8_t* xr = xs + (4 * rg + u) * X_PITCH;
+      const bool live = rows[u] != nullptr;
+      const u32x4 w0 = rope0 ? raw0[u] : dequant(u32x2{raw0[u].x, raw0[u].y}, sc0[u]);
+      *reinterpret_cast<u32x4*>(xr + 16 * pc0) = live ? w0 : zero;
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        const u32x4 w = dequant(codes[q - 1][u], scl[q - 1][u]);
+        *reinterpret_cast<u32x4*>(xr + 16 * (pc0 + 16 * q)) = live ? w : zero;
       }
     }
   }
@@ -220,18 +257,28 @@ __global__ __launch_bounds__(256, 1) void sparse_chunk(SparseArgs a) {
   }
   __syncthreads();
 
-  // 3. O^T[d][head] for d in [128 wave, 128 wave + 128).
+  // 3. O^T[d][head] for d in [128 wave, 128 wave + 128).  Lane (n, hh)
+  // feeds k-step kk the slots 16 kk + 8 r + 4 hh + (0..3), r = 0, 1 (the
+  // order of the score accumulators) of column d = n: in 16-lane group g,
+  // lane j addresses slot 16 kk + 8 r + 4 (g / 2) + j / 4 at columns
+  // 16 (g % 2) + 4 (j % 4) .. + 3 of the 32-wide d block.
   f32x16 o[4];
+  {
+    const int g16 = lane >> 4;
+    const int j = lane & 15;
+    const uint8_t* tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH +
+                        (128 * wave + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const uint8_t* vp = xts + (128 * wave + 32 * mb + n) * XT_PITCH + (16 * kk + 4 * hh) * 2;
-      const u32x2 lo2 = *reinterpret_cast<const u32x2*>(vp);
-      const u32x2 hi2 = *reinterpret_cast<const u32x2*>(vp + 16);
-      o[mb] = mfma32(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[kk * 64 + lane], o[mb]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const uint8_t* vp = tb + 16 * kk * X_PITCH + 64 * mb;
+        const u32x2 lo2 = lds_tr16(vp);
+        const u32x2 hi2 = lds_tr16(vp + 8 * X_PITCH);
+        o[mb] = mfma32(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[kk * 64 + lane], o[mb]);
+      }
     }
   }
   const float l_tot = l_s[n] + l_s[32 + n];
@@ -328,7 +375,7 @@ hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Test support: slot ids and raw row bytes, through sparse_slot_row.
+// Test support: slot ids and raw row bytes, through sparse_slot_rows.
 __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* ids, uint8_t* rows) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.B * a.n_slots;
@@ -336,7 +383,8 @@ __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* 
   const int b = (int)(t / a.n_slots);
   const int s = (int)(t % a.n_slots);
   int32_t id;
-  const uint8_t* row = sparse_slot_row(a, b, s, sparse_len(a, b), &id);
+  const uint8_t* row;
+  sparse_slot_rows<1>(a, b, &s, sparse_len(a, b), &row, &id);
   ids[t] = id;
   uint32_t* dst = reinterpret_cast<uint32_t*>(rows + t * kRowBytes);
   for (int w = 0; w < kRowBytes / 4; ++w) {
