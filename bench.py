@@ -80,33 +80,39 @@ def sparse_bytes(case):
 
 def time_plan(plan, steps, warmup, flush=None):
     """Run warmup untimed, then `steps` timed runs.  Returns (wall ms per
-    step, mean kernel ms from events on the launch stream, per-step kernel ms)."""
+    step, mean device ms per run from HIP events on the launch stream).
+
+    Without `flush` the runs go back to back between one pair of events, so
+    the per-run figure carries no event overhead.  With `flush` (a cache
+    scrub between runs, for working sets that fit in the caches) every run
+    is bracketed by its own events and the wall figure is not taken."""
     import torch
 
     stream = torch.cuda.current_stream()
     for _ in range(warmup):
         plan.run(stream)
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     if flush is None:
+        start = torch.cuda.Event(enable_timing=True)
+        end = torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
-        for k in range(steps):
-            starts[k].record(stream)
+        start.record(stream)
+        for _ in range(steps):
             plan.run(stream)
-            ends[k].record(stream)
+        end.record(stream)
         torch.cuda.synchronize()
         wall_ms = (time.perf_counter() - t0) * 1000.0 / steps
-    else:
-        wall_ms = None
-        for k in range(steps):
-            flush()
-            starts[k].record(stream)
-            plan.run(stream)
-            ends[k].record(stream)
-        torch.cuda.synchronize()
+        return wall_ms, start.elapsed_time(end) / steps
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for k in range(steps):
+        flush()
+        starts[k].record(stream)
+        plan.run(stream)
+        ends[k].record(stream)
+    torch.cuda.synchronize()
     per = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall_ms, sum(per) / len(per), per
+    return None, sum(per) / len(per)
 
 
 def kernel_source_digest(names):
@@ -212,7 +218,7 @@ def main():
         t_plan = time.perf_counter()
         plan = TI.dense_plan(case, dev, tensors=tensors)
         plan_ms = (time.perf_counter() - t_plan) * 1000.0
-        wall_ms, kern_ms, _ = time_plan(plan, args.steps, args.warmup)
+        wall_ms, kern_ms = time_plan(plan, args.steps, args.warmup)
         value = flops / (wall_ms / 1000.0) / 1e12
         achieved = flops / (kern_ms / 1000.0) / 1e12
         line = {
@@ -238,7 +244,9 @@ def main():
         case = W.c3_paged_decode()
         nbytes = decode_bytes(case)
         plan = TI.dense_plan(case, dev)
-        _, kern_ms, _ = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        # The KV cache (1.1 GB) is far larger than the L2 and last-level
+        # caches, so back-to-back runs stream it from HBM every time.
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
         gbs = nbytes / (kern_ms / 1000.0) / 1e9
         components["paged_decode"] = {
             "workload": "paged GQA decode: B=64, Q_N=32, KV_N=8, D=128, block 128, KV lengths "
@@ -253,7 +261,7 @@ def main():
         case = W.c4_alibi_prefill()
         flops = dense_flops(case)
         plan = TI.dense_plan(case, dev)
-        _, kern_ms, _ = time_plan(plan, min(args.steps, 20), args.warmup)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
         tf = flops / (kern_ms / 1000.0) / 1e12
         components["long_alibi_prefill"] = {
             "workload": "causal ALiBi prefill: B=1, Q_N=KV_N=16, S=8192, D=128",
@@ -266,7 +274,8 @@ def main():
         case = W.c5_sparse_sharedkv()
         nbytes = sparse_bytes(case)
         plan = TI.sparse_plan(case, dev)
-        _, kern_ms, _ = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        # 8 MB of rows would stay cached between runs: scrub the caches.
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
         gbs = nbytes / (kern_ms / 1000.0) / 1e9
         components["sparse_sharedkv_decode"] = {
             "workload": "shared-KV sparse decode: B=16, Q_N=64, D=512 (fp8 nope + bf16 rope), "
