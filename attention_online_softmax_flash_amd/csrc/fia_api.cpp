@@ -636,6 +636,38 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     // order, so this is a greedy longest-processing-time schedule.
     std::stable_sort(items.begin(), items.end(),
                      [](const Item& x, const Item& y) { return x.cost > y.cost; });
+    // Workgroups go round-robin to the 8 XCDs, each with its own L2.  Inside
+    // each run of one (batch, query tile) (Qn items of equal cost, adjacent
+    // after the stable sort), the query heads of one KV head are moved to
+    // positions congruent mod 8, so they run on one XCD and share its L2
+    // copy of the key / value tiles.
+    {
+      const int64_t G = Qn / KVn;
+      std::vector<Item> run;
+      std::vector<std::vector<Item>> lanes(8);
+      for (size_t k0 = 0; k0 < items.size();) {
+        size_t k1 = k0;
+        while (k1 < items.size() && items[k1].b == items[k0].b && items[k1].qt == items[k0].qt) ++k1;
+        if ((int64_t)(k1 - k0) == Qn) {
+          for (auto& l : lanes) l.clear();
+          for (size_t k = k0; k < k1; ++k) lanes[(size_t)((items[k].h / G) % 8)].push_back(items[k]);
+          run.clear();
+          for (size_t pos = 0; run.size() < (size_t)Qn; ++pos) {
+            // take the next item of lane pos % 8, or of the next non-empty lane
+            for (size_t t = 0; t < 8; ++t) {
+              std::vector<Item>& l = lanes[(pos + t) % 8];
+              if (!l.empty()) {
+                run.push_back(l.front());
+                l.erase(l.begin());
+                break;
+              }
+            }
+          }
+          std::copy(run.begin(), run.end(), items.begin() + (int64_t)k0);
+        }
+        k0 = k1;
+      }
+    }
     for (const Item& it : items) {
       e->meta.push_back(it.b);
       e->meta.push_back(it.h | (it.qt << 8));
