@@ -160,6 +160,16 @@ __device__ __forceinline__ int key_swz(int r) {
   return (r / (16 / PR)) % PR;
 }
 
+// Four 16-bit values by an LDS transpose read (ds_read_b64_tr_b16).  Within
+// each group of 16 lanes, lane i receives value t from position i % 4 of the
+// 8-byte piece addressed by lane 4 t + i / 4 of the group.
+__device__ __forceinline__ u32x2 lds_tr16(const void* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 // Global loads/stores of 16 and 8 bytes.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

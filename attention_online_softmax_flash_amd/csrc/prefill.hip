@@ -339,6 +339,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         for (int mb = 0; mb < NMB; ++mb) o[mb] *= alpha;
       }
       const float m_sub = (m_run == kNegInf) ? 0.f : m_run;
+      // Raised wave priority from here to the end of the value product: the
+      // arbiter then favours this wave's MFMA / LDS stream over the softmax
+      // VALU work of the other wave on the SIMD.
+      __builtin_amdgcn_s_setprio(1);
       if constexpr (PIPE) {
         if (knext != nullptr) compute_s(knext, sn);
       }
@@ -368,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           o[mb] = mfma32(*reinterpret_cast<const u32x4*>(vp), pb[kk], o[mb]);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
       // Interleave: one MFMA, a few VALU, one LDS read, repeated.
       if constexpr (INTERLEAVE) {
 #pragma unroll

@@ -101,16 +101,6 @@ __device__ __forceinline__ int sparse_len(const SparseArgs& a, int b) {
   return Lk < 0 ? 0 : (Lk > cap ? cap : Lk);
 }
 
-// Four 16-bit values by an LDS transpose read (ds_read_b64_tr_b16).  Within
-// each group of 16 lanes, lane i receives value t from position i % 4 of the
-// 8-byte piece addressed by lane 4 t + i / 4 of the group.
-__device__ __forceinline__ u32x2 lds_tr16(const void* p) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
-  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4*)(p));
-  return __builtin_bit_cast(u32x2, v);
-}
-
 // Grid: (n_slots / 64, N1 / 32, B); 256 threads.
 __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
