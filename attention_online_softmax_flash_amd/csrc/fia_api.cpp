@@ -369,7 +369,19 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     if (!p->actual_seq_lengths_kv) {
       return fail(FIA_ERR_PARAM_INVALID, "paged attention requires actual_seq_lengths_kv");
     }
+    const std::string kvl = p->kv_layout ? p->kv_layout : "PA_ND";
+    const bool bnnbsd = kvl == "BnNBsD";
+    if (!bnnbsd && kvl != "PA_ND" && kvl != "BnBsH") {
+      return fail(FIA_ERR_PARAM_INVALID, "kv_layout must be PA_ND, BnBsH or BnNBsD");
+    }
     for (const fia_tensor* t : {key, value}) {
+      if (bnnbsd) {
+        if (!(t->ndim == 4 && t->shape[1] == KVn && t->shape[2] == bs && t->shape[3] == D)) {
+          return fail(FIA_ERR_PARAM_INVALID, "BnNBsD key/value must be [n_blocks, KV_N, block_size, D], "
+                                             "got " + shape_str(t));
+        }
+        continue;
+      }
       const bool four = t->ndim == 4 && t->shape[1] == bs && t->shape[2] == KVn && t->shape[3] == D;
       const bool three = t->ndim == 3 && t->shape[1] == bs && t->shape[2] == KVn * D;
       if (!four && !three) {
@@ -387,8 +399,13 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
       c->N = KVn;
       c->D = D;
       c->sb = t->stride[0];
-      c->ss = t->stride[1];
-      c->sh = t->ndim == 4 ? t->stride[2] : D;
+      if (bnnbsd) {
+        c->ss = t->stride[2];
+        c->sh = t->stride[1];
+      } else {
+        c->ss = t->stride[1];
+        c->sh = t->ndim == 4 ? t->stride[2] : D;
+      }
     };
     pool_view(key, &ck);
     pool_view(value, &cv);

@@ -72,6 +72,7 @@ class FiaParams(ctypes.Structure):
         ("actual_seq_lengths_len", ctypes.c_int64),
         ("actual_seq_lengths_kv", ctypes.POINTER(ctypes.c_int64)),
         ("actual_seq_lengths_kv_len", ctypes.c_int64),
+        ("kv_layout", ctypes.c_char_p),
     ]
 
 
@@ -209,7 +210,8 @@ class AttentionPlan(_Plan):
                  next_tokens=2147483647, pse_type=0, pse_shift=None, q_start_idx=0,
                  kv_start_idx=0, atten_mask=None, block_table=None, block_size=0,
                  inner_precise=0, softmax_lse_flag=False, actual_seq_lengths=None,
-                 actual_seq_lengths_kv=None, attention_out=None, softmax_lse=None):
+                 actual_seq_lengths_kv=None, attention_out=None, softmax_lse=None,
+                 kv_layout="PA_ND"):
         L = lib()
         if attention_out is None:
             attention_out = torch.empty_like(query)
@@ -240,6 +242,7 @@ class AttentionPlan(_Plan):
         p.block_size = block_size
         p.inner_precise = inner_precise
         p.softmax_lse_flag = 1 if softmax_lse_flag else 0
+        p.kv_layout = kv_layout.encode()
         if self._lens[0] is not None:
             p.actual_seq_lengths = ctypes.cast(self._lens[0], ctypes.POINTER(ctypes.c_int64))
             p.actual_seq_lengths_len = self._lens[1]

@@ -41,7 +41,7 @@ def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia
               q_start_idx=case.q_start_idx, kv_start_idx=case.kv_start_idx,
               block_table=bt, block_size=case.block_size if bt is not None else 0,
               softmax_lse_flag=case.lse, actual_seq_lengths=case.actual_seq_lengths,
-              actual_seq_lengths_kv=case.actual_seq_lengths_kv)
+              actual_seq_lengths_kv=case.actual_seq_lengths_kv, kv_layout=case.kv_layout)
     kw.update(overrides)
     return fia.AttentionPlan(q, k, v, **kw)
 

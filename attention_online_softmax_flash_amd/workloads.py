@@ -66,7 +66,8 @@ class DenseCase:
 
     q: [B, S1, Q_N, D] (BSND) or [T, Q_N, D] (TND).
     k, v: [B, S2, KV_N, D] (BSND), [T_kv, KV_N, D] (TND), or None when paged.
-    k_pool, v_pool: [n_blocks, block_size, KV_N, D] (PA_ND) when paged.
+    k_pool, v_pool: [n_blocks, block_size, KV_N, D] (PA_ND) when paged, or
+    [n_blocks, KV_N, block_size, D] when kv_layout is "BnNBsD".
     """
     name: str
     dtype: str                      # "bf16" | "fp32"
@@ -89,6 +90,7 @@ class DenseCase:
     block_size: int = 0
     k_pool: Optional[np.ndarray] = None
     v_pool: Optional[np.ndarray] = None
+    kv_layout: str = "PA_ND"
     lse: bool = False
     seed: int = 0
 
@@ -101,6 +103,16 @@ class DenseCase:
         if self.layout == "TND":
             return len(self.actual_seq_lengths)
         return self.q.shape[0]
+
+
+def as_bnnbsd(case: DenseCase) -> DenseCase:
+    """The same paged case with its pools stored BnNBsD [n_blocks, KV_N,
+    block_size, D] (the values of every (block, slot, head) row unchanged)."""
+    assert case.paged and case.kv_layout == "PA_ND"
+    return dataclasses.replace(
+        case, name=case.name + "_bnnbsd", kv_layout="BnNBsD",
+        k_pool=np.ascontiguousarray(case.k_pool.transpose(0, 2, 1, 3)),
+        v_pool=np.ascontiguousarray(case.v_pool.transpose(0, 2, 1, 3)))
 
 
 def _draw(rng, shape, dtype):

@@ -256,6 +256,18 @@ def main():
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s",
                                  measured_traffic("decode_split_bf16"))}
         del plan
+        # The same cache stored BnNBsD: each KV head's rows of a page contiguous.
+        case_b = W.as_bnnbsd(case)
+        plan = TI.dense_plan(case_b, dev)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["paged_decode_bnnbsd"] = {
+            "workload": "the paged GQA decode above with the KV pools in BnNBsD order "
+                        "[n_blocks, KV_N, 128, D]", "unit": "GB/s", "value": round(gbs, 2),
+            "algorithmic_bytes": nbytes, "ms": round(kern_ms, 5),
+            "kernels": "decode_split_bf16<128> + decode_merge<128>",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+        del plan, case_b
 
     if want("c4"):
         case = W.c4_alibi_prefill()

@@ -122,13 +122,21 @@ typedef struct {
   int64_t actual_seq_lengths_len;
   const int64_t* actual_seq_lengths_kv;
   int64_t actual_seq_lengths_kv_len;
+  /* Memory order of the paged key / value pools (V5 Paged Attention group,
+   * KV cache layouts); ignored without block_table.  NULL or "PA_ND" (also
+   * "BnBsH"): [n_blocks, block_size, KV_N, D] or [n_blocks, block_size,
+   * KV_N*D].  "BnNBsD": [n_blocks, KV_N, block_size, D], each KV head's rows
+   * of a block contiguous. */
+  const char* kv_layout;
 } fia_params;
 
 /* Phase 1 of the dense / paged operator.
  *   query           [B,S1,Q_N,D] (per input_layout), bf16 or fp32.
  *   key, value      same layout [B,S2,KV_N,D]; or, when block_table is given,
- *                   PA_ND pools [n_blocks, block_size, KV_N, D] (also accepted
- *                   as [n_blocks, block_size, KV_N*D]); same dtype as query.
+ *                   pools in params->kv_layout: PA_ND [n_blocks, block_size,
+ *                   KV_N, D] (also accepted as [n_blocks, block_size,
+ *                   KV_N*D]) or BnNBsD [n_blocks, KV_N, block_size, D]; same
+ *                   dtype as query.
  *                   key and value may be the same tensor.
  *   pse_shift       NULL, or fp32 [Q_N] slopes when pse_type == 2.
  *   atten_mask      NULL, or the 2048x2048 causal mask for modes 2-4 (unread).

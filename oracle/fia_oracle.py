@@ -18,7 +18,9 @@ What it computes, and where each step is stated on the pages:
   length >= B -> first B entries) (V2, actualSeqLengths / actualSeqLengthsKv);
   TND lengths are cumulative (V5, ActualSeqLen parameter group).
 * Paged KV: row j of batch b lives at pool[blockTable[b][j // bs], j % bs]
-  (V2 / V5, page attention scenario).
+  (V2 / V5, page attention scenario); with the BnNBsD pool order
+  [n_blocks, KV_N, bs, D] (V5 paged-attention KV cache layouts) the row of
+  KV head n is pool[blockTable[b][j // bs], n, j % bs].
 * Mask modes (V5 Attention Mask parameter group; V2 sparseMode rules), with
   delta = Lk - Lq.  Reading (the mode table itself is not legible):
   0 -> all keys j < Lk, 2 -> j <= i (left-up causal),
@@ -156,10 +158,16 @@ def softmax_rows(s: np.ndarray, mask: np.ndarray, v: np.ndarray,
 # ---------------------------------------------------------------------------
 # Dense / paged fused inference attention.
 # ---------------------------------------------------------------------------
-def gather_paged(pool: np.ndarray, table_row: np.ndarray, L: int, bs: int) -> np.ndarray:
-    """Rows 0..L-1 of one batch from a PA_ND pool [n_blk, bs, KV_N, D]."""
+def gather_paged(pool: np.ndarray, table_row: np.ndarray, L: int, bs: int,
+                 kv_layout: str = "PA_ND") -> np.ndarray:
+    """Rows 0..L-1 of one batch, [L, KV_N, D], from a PA_ND pool
+    [n_blk, bs, KV_N, D] or a BnNBsD pool [n_blk, KV_N, bs, D]."""
     j = np.arange(L)
     blocks = np.asarray(table_row, dtype=np.int64)[j // bs]
+    if kv_layout == "BnNBsD":
+        return pool[blocks, :, j % bs]
+    if kv_layout != "PA_ND":
+        raise ValueError(kv_layout)
     return pool[blocks, j % bs]
 
 
@@ -168,13 +176,15 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
         next_tokens: int = 2147483647, alibi_slopes=None, q_start_idx: int = 0,
         kv_start_idx: int = 0, actual_seq_lengths=None, actual_seq_lengths_kv=None,
         block_table=None, block_size: int = 0, k_pool=None, v_pool=None,
+        kv_layout: str = "PA_ND",
         batches: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
         rows: Optional[Sequence[int]] = None, row_chunk: int = 1024):
     """Fused inference attention, float64.
 
     q: BSND [B, S1, Q_N, D] or TND [T, Q_N, D] (raw bits or floats per
     ``dtype``); k, v: [B, S2, KV_N, D] / [T_kv, KV_N, D]; or k_pool, v_pool
-    PA_ND [n_blk, bs, KV_N, D] with ``block_table`` [B, >= max pages].
+    PA_ND [n_blk, bs, KV_N, D] (``kv_layout`` "BnNBsD": [n_blk, KV_N, bs, D])
+    with ``block_table`` [B, >= max pages].
 
     Returns (out, lse) with out in the query layout (float64) and lse
     [B, Q_N, S1] (BSND) or [T, Q_N] (TND).  ``batches``/``heads``/``rows``
@@ -197,7 +207,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
         lse = np.full((q.shape[0], num_heads), np.nan, dtype=np.float64)
     else:
         B, S1 = q.shape[0], q.shape[1]
-        S2 = k_pool.shape[1] * block_table.shape[1] if paged else k.shape[1]
+        S2 = block_size * block_table.shape[1] if paged else k.shape[1]
         q_len = per_batch_lengths(actual_seq_lengths, B, S1)
         kv_len = per_batch_lengths(actual_seq_lengths_kv, B, S2 if not paged else 0)
         out = np.full(q.shape, np.nan, dtype=np.float64)
@@ -209,8 +219,8 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
     for b in (range(B) if batches is None else batches):
         Lq, Lk = q_len[b], kv_len[b]
         if paged:
-            kb = to_f64(gather_paged(k_pool, block_table[b], Lk, block_size), dtype)
-            vb = to_f64(gather_paged(v_pool, block_table[b], Lk, block_size), dtype)
+            kb = to_f64(gather_paged(k_pool, block_table[b], Lk, block_size, kv_layout), dtype)
+            vb = to_f64(gather_paged(v_pool, block_table[b], Lk, block_size, kv_layout), dtype)
         elif tnd:
             kb = to_f64(k[kv_off[b]:kv_off[b + 1]], dtype)
             vb = to_f64(v[kv_off[b]:kv_off[b + 1]], dtype)
@@ -260,7 +270,8 @@ def fia_case(case, **kw):
                actual_seq_lengths=case.actual_seq_lengths,
                actual_seq_lengths_kv=case.actual_seq_lengths_kv,
                block_table=case.block_table, block_size=case.block_size,
-               k_pool=case.k_pool, v_pool=case.v_pool, **kw)
+               k_pool=case.k_pool, v_pool=case.v_pool,
+               kv_layout=getattr(case, "kv_layout", "PA_ND"), **kw)
 
 
 # ---------------------------------------------------------------------------

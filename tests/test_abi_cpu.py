@@ -60,6 +60,9 @@ def P(**kw):
     p.block_size = kw.pop("block_size", 0)
     p.inner_precise = kw.pop("inner_precise", 0)
     p.softmax_lse_flag = kw.pop("lse", 0)
+    kvl = kw.pop("kv_layout", None)
+    if kvl is not None:
+        p.kv_layout = kvl.encode()
     keep = []
     for name in ("actual_seq_lengths", "actual_seq_lengths_kv"):
         vals = kw.pop(name, None)
@@ -224,6 +227,32 @@ def test_paged_rules():
     assert st == BAD
     st, kind, _, msg = plan(P(**ok), q, T((10, 128, 256)), T((10, 128, 256)), o, bt=bt)
     assert st == 0 and kind == "decode", msg
+
+
+def test_bnnbsd_paged_rules():
+    q = T((2, 1, 4, 128))
+    o = T((2, 1, 4, 128))
+    bt = T((2, 4), fia.DT_INT32)
+    ok = dict(num_heads=4, num_kv_heads=2, block_size=128, actual_seq_lengths_kv=[300, 500])
+    pool = T((10, 2, 128, 128))
+    st, kind, _, msg = plan(P(kv_layout="BnNBsD", **ok), q, pool, pool, o, bt=bt)
+    assert st == 0 and kind == "decode", msg
+    # the same pool read as PA_ND has the wrong shape
+    st, _, _, msg = plan(P(**ok), q, pool, pool, o, bt=bt)
+    assert st == BAD
+    # PA_ND pool under BnNBsD: rejected
+    st, _, _, msg = plan(P(kv_layout="BnNBsD", **ok), q, T((10, 128, 2, 128)), T((10, 128, 2, 128)),
+                         o, bt=bt)
+    assert st == BAD and "BnNBsD" in msg
+    st, _, _, msg = plan(P(kv_layout="BnNBsD", **ok), q, T((10, 128, 256)), T((10, 128, 256)), o, bt=bt)
+    assert st == BAD
+    st, _, _, msg = plan(P(kv_layout="NZ", **ok), q, pool, pool, o, bt=bt)
+    assert st == BAD and "kv_layout" in msg
+    # prefill over a BnNBsD pool
+    q2 = T((2, 64, 4, 128))
+    o2 = T((2, 64, 4, 128))
+    st, kind, _, msg = plan(P(kv_layout="BnNBsD", sparse_mode=3, **ok), q2, pool, pool, o2, bt=bt)
+    assert st == 0 and kind == "prefill", msg
 
 
 def test_tnd_rules():

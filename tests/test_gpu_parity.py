@@ -158,6 +158,33 @@ def test_prefill_over_paged_kv():
     dense_parity(case, "prefill")
 
 
+@pytest.mark.parametrize("bs", [64, 16])
+def test_prefill_over_paged_kv_bnnbsd(bs):
+    case = W.paged_decode_case("ppb", 151, B=3, Q_N=8, KV_N=2, D=128, kv_lens=[300, 70, 513],
+                               block_size=bs, S1=70, sparse_mode=3, lse=True, poison_tail=True,
+                               extra_blocks=3)
+    case.actual_seq_lengths = [70, 70, 70]
+    dense_parity(W.as_bnnbsd(case), "prefill")
+
+
+BNNBSD_DECODE_CASES = [
+    # (B, Qn, KVn, D, kv_lens, block_size)
+    (3, 32, 8, 128, [1, 511, 1300], 128),
+    (2, 8, 8, 128, [512, 513], 16),
+    (2, 4, 2, 64, [999, 40], 32),
+    (2, 16, 1, 128, [2048 + 7, 100], 64),
+]
+
+
+@pytest.mark.parametrize("i", range(len(BNNBSD_DECODE_CASES)))
+def test_decode_bnnbsd(i):
+    B, Qn, KVn, D, lens, bs = BNNBSD_DECODE_CASES[i]
+    case = W.paged_decode_case(f"decb{i}", 260 + i, B=B, Q_N=Qn, KV_N=KVn, D=D, kv_lens=lens,
+                               block_size=bs, lse=True, poison_tail=True, extra_blocks=2,
+                               table_cols=(max(lens) + bs - 1) // bs + 1)
+    dense_parity(W.as_bnnbsd(case), "decode")
+
+
 DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size or None (dense), mode, pre, nxt)
     (3, 32, 8, 128, [1, 511, 1300], 128, 0, None, None),

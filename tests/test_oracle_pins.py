@@ -352,6 +352,39 @@ def test_paged_equals_contiguous():
     assert np.all(np.isfinite(out_p))
 
 
+def test_bnnbsd_pool_equals_contiguous():
+    """The BnNBsD pool order changes only where rows live: the paged result
+    over a BnNBsD pool equals the contiguous one (poisoned tails unread)."""
+    c = W.paged_decode_case("pb", 51, B=3, Q_N=4, KV_N=2, D=8, kv_lens=[5, 33, 16],
+                            block_size=16, dtype="bf16", keep_contiguous=True,
+                            poison_tail=True, extra_blocks=2, S1=2, sparse_mode=3)
+    cb = W.as_bnnbsd(c)
+    assert cb.k_pool.shape == (c.k_pool.shape[0], 2, 16, 8)
+    out_p, lse_p = O.fia_case(cb)
+    out_c, lse_c = O.fia(c.q, c.k, c.v, dtype="bf16", layout="BSND", num_heads=4, num_kv_heads=2,
+                         scale=c.scale, sparse_mode=3, actual_seq_lengths_kv=c.actual_seq_lengths_kv)
+    np.testing.assert_array_equal(out_p, out_c)
+    np.testing.assert_array_equal(lse_p, lse_c)
+
+
+def test_bnnbsd_gather_index_order():
+    """Row j of KV head n is pool[table[j // bs], n, j % bs]: a pool whose
+    every element encodes its own (block, head, slot) is gathered back to
+    the expected codes."""
+    n_blk, kvn, bs, d = 5, 3, 4, 2
+    pool = np.zeros((n_blk, kvn, bs, d))
+    for blk in range(n_blk):
+        for hd in range(kvn):
+            for sl in range(bs):
+                pool[blk, hd, sl, :] = 1000 * blk + 100 * hd + sl
+    table = np.array([3, 0, 4], dtype=np.int32)
+    rows = O.gather_paged(pool, table, 10, bs, "BnNBsD")
+    assert rows.shape == (10, kvn, d)
+    for j in range(10):
+        for hd in range(kvn):
+            assert rows[j, hd, 0] == 1000 * table[j // bs] + 100 * hd + j % bs
+
+
 def test_split_keys_merge_by_lse_reproduces_full():
     """Partial results over disjoint key ranges combine through their LSE
     (V2 softmaxLse restrictions: the ring-attention composition)."""
