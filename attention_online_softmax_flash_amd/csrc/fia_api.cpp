@@ -818,11 +818,15 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
     if ((st = check_tensor(cmp_kv, "cmp_kv")) != FIA_SUCCESS) return st;
     if ((st = check_pool(cmp_kv, "cmp_kv", &nb2, &bs2, &csb, &css)) != FIA_SUCCESS) return st;
     if (cmp_kv->dtype != ori_kv->dtype) return fail(FIA_ERR_PARAM_INVALID, "ori_kv and cmp_kv dtypes differ");
-    if (cmp_sparse_indices == nullptr) {
-      return fail(FIA_ERR_UNSUPPORTED, "compressed KV without top-k indices is not supported");
+    // CSA: top-k indices into a ratio-4 compressed sequence; HCA: no indices,
+    // every row of a ratio-128 compressed sequence.
+    if (cmp_sparse_indices != nullptr && p->cmp_ratio != 4) {
+      return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 4 with cmp_sparse_indices (compressed-sparse)");
     }
-    if (p->cmp_ratio == 128) return fail(FIA_ERR_UNSUPPORTED, "cmp_ratio 128 is not supported");
-    if (p->cmp_ratio != 4) return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 4 with compressed KV");
+    if (cmp_sparse_indices == nullptr && p->cmp_ratio != 128) {
+      return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 128 without cmp_sparse_indices "
+                                         "(heavily compressed)");
+    }
     if (p->cmp_mask_mode != 3) return fail(FIA_ERR_PARAM_INVALID, "cmp_mask_mode must be 3");
     if (cmp_block_table == nullptr) return fail(FIA_ERR_PARAM_INVALID, "cmp_kv needs cmp_block_table");
   } else {
@@ -857,10 +861,19 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   if ((st = check_bt(ori_block_table, "ori_block_table", (max_seqused_kv + bs1 - 1) / bs1)) != FIA_SUCCESS) {
     return st;
   }
+  const bool hca = has_cmp && cmp_sparse_indices == nullptr;
   if (has_cmp) {
     const int64_t ncmp = max_seqused_kv / p->cmp_ratio;
     if ((st = check_bt(cmp_block_table, "cmp_block_table", (ncmp + bs2 - 1) / bs2)) != FIA_SUCCESS) {
       return st;
+    }
+    if (hca) {
+      // One slot per compressed row of the longest sequence; the merge folds
+      // at most 64 chunks of 64 slots.
+      K2 = (int64_t)align_up((size_t)ncmp, fia::kSparseChunk);
+      if (K2 + 128 > 64 * fia::kSparseChunk) {
+        return fail(FIA_ERR_UNSUPPORTED, "max_seqused_kv too large for the heavily compressed mode");
+      }
     }
   }
   if (seqused_kv->dtype != FIA_DT_INT32 || seqused_kv->ndim != 1 || seqused_kv->shape[0] != B) {
@@ -913,6 +926,7 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   a.n_win_slots = (int32_t)align_up((size_t)(a.win_left + a.win_right + 1), fia::kSparseChunk);
   a.n_slots = a.n_win_slots + a.K2;
   a.has_cmp = has_cmp ? 1 : 0;
+  a.cmp_direct = hca ? 1 : 0;
   a.scale_log2 = (float)(p->softmax_scale * 1.4426950408889634);
   const int64_t n_chunks = a.n_slots / fia::kSparseChunk;
   e->part_o_off = 0;

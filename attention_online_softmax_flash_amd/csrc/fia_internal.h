@@ -96,6 +96,7 @@ struct SparseArgs {
   int32_t n_win_slots;              // window slots (multiple of 64)
   int32_t n_slots;                  // window slots + K2
   int32_t has_cmp;
+  int32_t cmp_direct;               // no indices: compressed slot k is row k
   float scale_log2;
   float* part_o;                    // [B * n_chunks * N1 * 512]
   float* part_lse;                  // [B * n_chunks * N1]

@@ -1,5 +1,5 @@
 // Shared-KV sparse decode (KvQuantSparseAttnSharedkv; sparse_flash_mla CSA
-// mode): O = softmax(Q K~^T * scale) V~ with K~ = V~ = the window rows of the
+// and HCA modes): O = softmax(Q K~^T * scale) V~ with K~ = V~ = the window rows of the
 // original KV followed by the top-k selected rows of the compressed KV, plus a
 // per-head sink logit.
 //
@@ -7,8 +7,9 @@
 // slots so a batch's result never depends on the other batch entries:
 //   slots [0, n_win_slots): window row j = p - win_left + s, used when
 //     0 <= j <= min(Lk - 1, p + win_right);
-//   slots [n_win_slots, n_win_slots + K2): compressed row c = idx[b][s - n_win],
-//     used when 0 <= c < floor(Lk / cmp_ratio).
+//   slots [n_win_slots, n_win_slots + K2): compressed row c = idx[b][s - n_win]
+//     (compressed-sparse) or c = s - n_win (heavily compressed: the whole
+//     compressed sequence, no indices), used when 0 <= c < floor(Lk / cmp_ratio).
 // Each packed 640-byte row holds bf16 rope x64 | e4m3fn nope x448 | fp32
 // scale x7 (one per 64-wide nope tile); the logical 512-vector is
 // [rope | nope * scale].
@@ -46,7 +47,8 @@ __device__ __forceinline__ void e4m3fn_x4(uint32_t w, float* f) {
 
 // Slots s[0..N) of batch b -> packed row addresses (nullptr for an unused
 // slot) and ids: j for window row j, (1 << 30) | c for compressed row c, -1
-// if unused.  No read depends on a branch: every table read goes to an
+// if unused.  Compressed slot k holds row idx[b][k] (compressed-sparse) or
+// row k itself (heavily compressed, no indices).  No read depends on a branch: every table read goes to an
 // in-bounds address (a clamped position), so the N index reads, then the N
 // block-table reads, are each in flight together.
 template <int N>
@@ -60,7 +62,11 @@ __device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int b, con
 #pragma unroll
   for (int u = 0; u < N; ++u) {
     const int k = min(max(s[u] - a.n_win_slots, 0), a.K2 > 0 ? a.K2 - 1 : 0);
-    c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + k] : -1;
+    if (a.cmp_direct) {
+      c[u] = cmp_on ? s[u] - a.n_win_slots : -1;
+    } else {
+      c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + k] : -1;
+    }
   }
   int raw[N], slot[N];
   bool win[N], ok[N];

@@ -51,7 +51,8 @@ def sparse_tensors(case: SparseCase, device="cuda"):
         q=to_device(case.q, "bf16", device),
         ori_kv=torch.from_numpy(case.ori_kv).to(device),
         cmp_kv=torch.from_numpy(case.cmp_kv).to(device),
-        cmp_sparse_indices=torch.from_numpy(case.cmp_sparse_indices).to(device),
+        cmp_sparse_indices=(None if case.cmp_sparse_indices is None
+                            else torch.from_numpy(case.cmp_sparse_indices).to(device)),
         ori_block_table=torch.from_numpy(case.ori_block_table).to(device),
         cmp_block_table=torch.from_numpy(case.cmp_block_table).to(device),
         seqused_kv=torch.tensor(case.seqused_kv, dtype=torch.int32, device=device),

@@ -315,7 +315,7 @@ class SparseCase:
     cmp_kv: np.ndarray             # uint8 [nb2, bs2, 1, 640]
     ori_block_table: np.ndarray    # int32 [B, >= ceil(max S2 / bs1)]
     cmp_block_table: np.ndarray    # int32 [B, >= ceil(floor(max S2 / ratio) / bs2)]
-    cmp_sparse_indices: np.ndarray  # int32 [B, S1, 1, K2]; -1 = invalid
+    cmp_sparse_indices: Optional[np.ndarray]  # int32 [B, S1, 1, K2]; -1 = invalid; None: every compressed row
     seqused_kv: list
     sinks: np.ndarray              # float32 [N1]
     softmax_scale: float
@@ -368,14 +368,17 @@ def _paged_pool_of_rows(rng, rows_per_batch, block_size, extra_blocks=0):
 
 def sparse_case(name, seed, *, B, N1, seqused_kv, K2=512, block_size1=128,
                 block_size2=128, cmp_ratio=4, n_valid=None,
-                materialise_all_ori=True) -> SparseCase:
+                materialise_all_ori=True, heavily_compressed=False) -> SparseCase:
     """Shared-KV sparse decode inputs (S1 = 1).
 
     ori rows: every logical row < L_b is materialised, or, when
     ``materialise_all_ori`` is False, only the last 128 (the rest are NaN);
     cmp rows: floor(L_b / cmp_ratio) rows per batch; top-K2 indices drawn
     uniformly without replacement from [0, n_cmp), padded with -1 when fewer
-    are valid (valid entries first)."""
+    are valid (valid entries first).  ``heavily_compressed``: no indices
+    (every compressed row is used), cmp_ratio 128."""
+    if heavily_compressed:
+        cmp_ratio = 128
     rng = rng_for(seed)
     q = normal_bf16(rng, (B, 1, N1, SPARSE_D))
     ori_rows, cmp_rows = [], []
@@ -400,6 +403,8 @@ def sparse_case(name, seed, *, B, N1, seqused_kv, K2=512, block_size1=128,
         nv = min(K2, n_cmp) if n_valid is None else min(n_valid, K2, n_cmp)
         if nv > 0:
             idx[b, 0, 0, :nv] = rng.choice(n_cmp, size=nv, replace=False).astype(np.int32)
+    if heavily_compressed:
+        idx = None
     sinks = rng.standard_normal(N1, dtype=np.float32)
     return SparseCase(name=name, q=q, ori_kv=ori_kv, cmp_kv=cmp_kv,
                       ori_block_table=ori_bt, cmp_block_table=cmp_bt,

@@ -156,13 +156,15 @@ fia_status fia_get_workspace_size(const fia_params* params,
                                   size_t* workspace_size, fia_executor** executor);
 
 /* Attributes of the shared-KV sparse decode operator (KvQuantSparseAttnSharedkv
- * parameter table; sparse_flash_mla CSA mode). */
+ * parameter table; sparse_flash_mla SWA / CSA / HCA modes). */
 typedef struct {
   double softmax_scale;
   int32_t kv_quant_mode;   /* 1: per-tile quantised nope (the only mode) */
   int32_t tile_size;       /* 64 */
   int32_t rope_head_dim;   /* 64 */
-  int32_t cmp_ratio;       /* 4 (compressed-sparse) or 1 when cmp_kv is absent */
+  int32_t cmp_ratio;       /* 4: compressed-sparse (cmp_kv + cmp_sparse_indices);
+                            * 128: heavily compressed (cmp_kv, no indices);
+                            * 1: sliding window only (no cmp_kv) */
   int32_t ori_mask_mode;   /* 4 (band) */
   int32_t cmp_mask_mode;   /* 3 (right-down causal) */
   int32_t ori_win_left;    /* 127 */
@@ -172,7 +174,9 @@ typedef struct {
   int32_t return_softmax_lse; /* must be 0 (reserved on the page) */
 } fia_sparse_params;
 
-/* Phase 1 of the shared-KV sparse decode (query length 1).
+/* Phase 1 of the shared-KV sparse decode (query length 1): attention over
+ * the sliding window of ori_kv (SWA), plus the top-k selected rows of cmp_kv
+ * (CSA), or plus every row of the compressed sequence (HCA).
  *   q                  bf16 [B,1,N1,512], N1 in {64,128}; logical dim order
  *                      [rope(64) | nope(448)].
  *   ori_kv, cmp_kv     uint8 (or fp8_e4m3fn) PA_ND pools [n_blk, bs, 1, 640]:
@@ -180,7 +184,10 @@ typedef struct {
  *                      (one per 64-wide tile) | zero pad to 640 bytes.
  *   ori_sparse_indices must be NULL (reserved on the page).
  *   cmp_sparse_indices int32 [B,1,1,K2], K2 in {512,1024}; entry c is used
- *                      iff 0 <= c < floor(Lk / cmp_ratio).
+ *                      iff 0 <= c < floor(Lk / cmp_ratio).  NULL with cmp_kv:
+ *                      heavily compressed mode, rows 0 .. floor(Lk / 128) - 1
+ *                      of the compressed sequence are all used (max_seqused_kv
+ *                      / 128 + 128 <= 4096).
  *   ori_block_table    int32 [B, >= ceil(max Lk / bs1)].
  *   cmp_block_table    int32 [B, >= ceil(floor(max Lk / cmp_ratio) / bs2)].
  *   seqused_kv         int32 [B] device, KV length per batch (Lk).
@@ -188,7 +195,7 @@ typedef struct {
  *   sinks              fp32 [N1]: one extra logit per head with a zero value.
  *   metadata           ignored (the plan is built here), may be NULL.
  *   attention_out      bf16 [B,1,N1,512].
- * K~ = V~ = window rows of ori_kv followed by the selected cmp_kv rows. */
+ * K~ = V~ = window rows of ori_kv followed by the used cmp_kv rows. */
 fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
                                          const fia_tensor* q, const fia_tensor* ori_kv,
                                          const fia_tensor* cmp_kv,

@@ -302,13 +302,18 @@ def sparse_rows(Lk: int, S1: int, t: int, idx_row, *, cmp_ratio: int,
     Window: p = Lk - S1 + t (the query sits at the end of its KV sequence),
     rows max(0, p - win_left) .. min(Lk - 1, p + win_right).
     Compressed: entries c of the index row with 0 <= c < floor(Lk / ratio),
-    in index order.
+    in index order (compressed-sparse mode); with no index row (heavily
+    compressed mode, sparse_flash_mla HCA: the window plus the contiguous
+    compressed KV segment) every compressed row 0 .. floor(Lk / ratio) - 1.
     """
     p = Lk - S1 + t
     lo, hi = max(0, p - win_left), min(Lk - 1, p + win_right)
     window = list(range(lo, hi + 1)) if hi >= lo else []
     n_cmp = Lk // cmp_ratio
-    comp = [int(c) for c in idx_row if 0 <= int(c) < n_cmp]
+    if idx_row is None:
+        comp = list(range(n_cmp))
+    else:
+        comp = [int(c) for c in idx_row if 0 <= int(c) < n_cmp]
     return window, comp
 
 
@@ -330,7 +335,8 @@ def sparse_sharedkv(case, *, batches=None):
     sinks = np.asarray(case.sinks, dtype=np.float32).astype(np.float64)
     for b in (range(B) if batches is None else batches):
         Lk = int(case.seqused_kv[b])
-        win, comp = sparse_rows(Lk, S1, 0, case.cmp_sparse_indices[b, 0, 0],
+        idx_row = None if case.cmp_sparse_indices is None else case.cmp_sparse_indices[b, 0, 0]
+        win, comp = sparse_rows(Lk, S1, 0, idx_row,
                                 cmp_ratio=case.cmp_ratio, win_left=case.win_left,
                                 win_right=case.win_right)
         X = []

@@ -372,7 +372,12 @@ def sparse_plan_status(**over):
     (dict(ori_win_right=1), BAD),
     (dict(ori_mask_mode=3), BAD),
     (dict(cmp_mask_mode=4), BAD),
-    (dict(cmp_ratio=128), UNS),
+    (dict(cmp_ratio=128), BAD),                       # indices need ratio 4
+    (dict(idx=None, cmp_ratio=128), 0),               # heavily compressed mode
+    (dict(idx=None), BAD),                            # no indices needs ratio 128
+    (dict(idx=None, cmp_ratio=128, cmp_mask_mode=4), BAD),
+    (dict(idx=None, cmp_ratio=128, max_seq=600000, obt=T((2, 4688), fia.DT_INT32),
+          cbt=T((2, 40), fia.DT_INT32)), UNS),        # too many compressed rows
     (dict(cmp_ratio=2), BAD),
     (dict(idx=T((2, 1, 1, 256), fia.DT_INT32)), BAD),
     (dict(oidx=T((2, 1, 1, 512), fia.DT_INT32)), BAD),

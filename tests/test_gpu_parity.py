@@ -281,6 +281,37 @@ def test_sparse_window_only():
     check_out(to_f64(plan.out), O.sparse_sharedkv(case))
 
 
+def test_sparse_heavily_compressed():
+    case = W.sparse_case("hca", 420, B=4, N1=64, seqused_kv=[100, 1000, 16384, 5000],
+                         block_size1=64, block_size2=16, heavily_compressed=True,
+                         materialise_all_ori=False)
+    assert case.cmp_sparse_indices is None and case.cmp_ratio == 128
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
+def test_sparse_heavily_compressed_rows_are_bit_exact():
+    case = W.sparse_case("hcr", 421, B=2, N1=64, seqused_kv=[300, 2000], block_size1=32,
+                         block_size2=16, heavily_compressed=True, materialise_all_ori=False)
+    plan = TI.sparse_plan(case, DEV)
+    ids, rows = plan.debug_rows()
+    torch.cuda.synchronize()
+    ids, rows = ids.cpu().numpy(), rows.cpu().numpy()
+    n_win = 128
+    for b, L in enumerate(case.seqused_kv):
+        win, comp = O.sparse_rows(L, 1, 0, None, cmp_ratio=128, win_left=127, win_right=0)
+        assert [int(x) for x in ids[b, :n_win] if x >= 0] == win
+        assert [int(x) & ((1 << 30) - 1) for x in ids[b, n_win:] if x >= 0] == comp
+        for s in range(n_win, ids.shape[1]):
+            x = int(ids[b, s])
+            if x < 0:
+                assert not rows[b, s].any()
+            else:
+                c = x & ((1 << 30) - 1)
+                want = case.cmp_kv[case.cmp_block_table[b, c // 16], c % 16, 0]
+                assert np.array_equal(rows[b, s], want)
+
+
 # ---------------------------------------------------------------------------
 # Bit-exact gathers and row selection.
 # ---------------------------------------------------------------------------

@@ -385,6 +385,17 @@ def test_bnnbsd_gather_index_order():
             assert rows[j, hd, 0] == 1000 * table[j // bs] + 100 * hd + j % bs
 
 
+def test_heavily_compressed_rows_hand_values():
+    """HCA (no indices): the window plus every compressed row; worked by hand
+    for Lk = 300, ratio 128 (2 compressed rows) and Lk = 100 (none)."""
+    win, comp = O.sparse_rows(300, 1, 0, None, cmp_ratio=128, win_left=127, win_right=0)
+    assert win == list(range(172, 300)) and comp == [0, 1]
+    win, comp = O.sparse_rows(100, 1, 0, None, cmp_ratio=128, win_left=127, win_right=0)
+    assert win == list(range(0, 100)) and comp == []
+    win, comp = O.sparse_rows(1024, 1, 0, None, cmp_ratio=128, win_left=127, win_right=0)
+    assert comp == list(range(8))
+
+
 def test_split_keys_merge_by_lse_reproduces_full():
     """Partial results over disjoint key ranges combine through their LSE
     (V2 softmaxLse restrictions: the ring-attention composition)."""
