@@ -21,7 +21,9 @@
 
 namespace fia {
 
-template <int D>
+// MASKT: an explicit mask tensor (modes 0 / 1) removes keys whose mask byte
+// (query row 0 of the batch) is non-zero.
+template <int D, bool MASKT>
 __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide d chunks of the score product
   constexpr int DPL = D / 16;  // value columns per lane column (8 for D = 128)
@@ -78,6 +80,7 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   static_assert(sizeof(sm_o[0]) >= 32 * 2 * D, "key slot does not fit");
   char* kbuf = reinterpret_cast<char*>(&sm_o[wave][0][0]);
 
+  const uint8_t* mrow = MASKT ? a.mask + (int64_t)b * a.mask_sb : nullptr;
   const uint16_t* kbase = (const uint16_t*)a.k;
   const uint16_t* vbase = (const uint16_t*)a.v;
 
@@ -144,12 +147,24 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
           sc[hf] = mfma16(kr, qv[cc], sc[hf]);
         }
       }
+      // Mask bytes of keys ts + 16 hf + 4 g .. + 3 (4-aligned; a group past
+      // the mask width lies past every visible key, so its address is
+      // clamped and its bytes unused).
+      uint32_t mw[2] = {0u, 0u};
+      if constexpr (MASKT) {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int j4 = min(ts + 16 * hf + 4 * g, a.mask_cols - 4);
+          mw[hf] = *reinterpret_cast<const uint32_t*>(mrow + j4);
+        }
+      }
       float x[8];
       float mx = kNegInf;
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
         const int j = ts + 16 * (s >> 2) + 4 * g + (s & 3);
-        const bool ok = j >= t_lo && j < t_hi;
+        bool ok = j >= t_lo && j < t_hi;
+        if constexpr (MASKT) ok = ok && ((mw[s >> 2] >> (8 * (s & 3))) & 0xffu) == 0u;
         float v = sc[s >> 2][s & 3] * a.scale_log2;
         v += c_alibi * (float)(j + a.alibi_delta);
         x[s] = ok ? v : kNegInf;
@@ -225,8 +240,11 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
     for (int w = 0; w < 4; ++w) s += sm_o[w][hh][d0 + u] * wgt[w];
     acc[u] = s;
   }
-  const float inv = 1.f / L;
-  const float lse2 = M + fast_log2(L);
+  // A chunk can hold no visible key under an explicit mask: output 0 and a
+  // log2-sum-exp of -inf (the row's LSE +inf when it is the only chunk).
+  const bool any = L > 0.f;
+  const float inv = any ? 1.f / L : 0.f;
+  const float lse2 = any ? M + fast_log2(L) : kNegInf;
   if (nchunk == 1) {
     uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
                    (int64_t)hout * a.o_sh + d0;
@@ -236,7 +254,7 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
     }
     if (a.write_lse && d0 == 0) {
       a.lse[(int64_t)b * a.lse_sb + (int64_t)hout * a.lse_sh + (int64_t)q_off * a.lse_ss] =
-          lse2 * kLn2;
+          any ? lse2 * kLn2 : kPosInf;
     }
   } else {
     const int64_t pi = (int64_t)(chunk0 + c) * a.Qn + hout;
@@ -281,6 +299,12 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  if (M == kNegInf) {   // every chunk empty (explicit mask): 0 and LSE +inf
+#pragma unroll
+    for (int u = 0; u < PL; ++u) op[u] = 0;
+    if (a.write_lse && lane == 0) *lp = kPosInf;
+    return;
+  }
   float L = 0.f;
   float acc[PL];
 #pragma unroll
@@ -330,10 +354,13 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
 
 hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s) {
   if (n_items > 0) {
+    const bool m = a.mask != nullptr;
     if (a.D == 128) {
-      decode_split_bf16<128><<<n_items, 256, 0, s>>>(a);
+      if (m) decode_split_bf16<128, true><<<n_items, 256, 0, s>>>(a);
+      else decode_split_bf16<128, false><<<n_items, 256, 0, s>>>(a);
     } else {
-      decode_split_bf16<64><<<n_items, 256, 0, s>>>(a);
+      if (m) decode_split_bf16<64, true><<<n_items, 256, 0, s>>>(a);
+      else decode_split_bf16<64, false><<<n_items, 256, 0, s>>>(a);
     }
   }
   return hipGetLastError();

@@ -443,9 +443,44 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   // Mask group.
   const int mode = p->sparse_mode;
   if (mode < 0 || mode > 4) return fail(FIA_ERR_PARAM_INVALID, "sparse_mode must be in [0, 4]");
-  if (mode == 1) return fail(FIA_ERR_UNSUPPORTED, "sparse_mode 1 needs an explicit mask tensor");
-  if (atten_mask != nullptr) {
-    if (mode == 0) return fail(FIA_ERR_UNSUPPORTED, "an explicit atten_mask tensor is not supported");
+  if (mode == 1 && atten_mask == nullptr) {
+    return fail(FIA_ERR_PARAM_INVALID, "sparse_mode 1 needs an explicit atten_mask tensor");
+  }
+  // Explicit mask (modes 0 / 1): [B or 1, >= Q_S, >= KV_S], [B or 1, 1, >= Q_S,
+  // >= KV_S] or [>= Q_S, >= KV_S]; element != 0 masks the key out.
+  const bool explicit_mask = atten_mask != nullptr && (mode == 0 || mode == 1);
+  int64_t mask_sb = 0, mask_ss = 0, mask_rows = 0, mask_cols = 0;
+  if (explicit_mask) {
+    if ((st = check_tensor(atten_mask, "atten_mask")) != FIA_SUCCESS) return st;
+    const int dt = atten_mask->dtype;
+    if (dt != FIA_DT_BOOL && dt != FIA_DT_INT8 && dt != FIA_DT_UINT8) {
+      return fail(FIA_ERR_PARAM_INVALID, "atten_mask dtype must be bool, int8 or uint8");
+    }
+    if (tnd) return fail(FIA_ERR_UNSUPPORTED, "an explicit atten_mask with TND is not supported");
+    const int nd = atten_mask->ndim;
+    if (nd < 2 || nd > 4) return fail(FIA_ERR_PARAM_INVALID, "atten_mask must have 2, 3 or 4 dims");
+    if (nd == 4 && atten_mask->shape[1] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "a 4-dim atten_mask must be [B or 1, 1, Q_S, KV_S]");
+    }
+    const int64_t mb = nd >= 3 ? atten_mask->shape[0] : 1;
+    if (mb != 1 && mb != B) return fail(FIA_ERR_PARAM_INVALID, "atten_mask dim 0 must be B or 1");
+    mask_rows = atten_mask->shape[nd - 2];
+    mask_cols = atten_mask->shape[nd - 1];
+    const int64_t S2m = paged ? bt_cols * bs : ck.S;
+    if (mask_rows < cq.S || mask_cols < S2m) {
+      return fail(FIA_ERR_PARAM_INVALID, "atten_mask must cover [Q_S, KV_S]");
+    }
+    if (atten_mask->stride[nd - 1] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "atten_mask rows must be contiguous");
+    }
+    mask_ss = atten_mask->stride[nd - 2];
+    mask_sb = (nd >= 3 && mb > 1) ? atten_mask->stride[0] : 0;
+    if (mask_ss % 4 || mask_sb % 4 || mask_cols % 4 ||
+        reinterpret_cast<uintptr_t>(atten_mask->data) % 4) {
+      return fail(FIA_ERR_UNSUPPORTED, "atten_mask rows must be 4-byte aligned (pad KV_S to a "
+                                       "multiple of 4)");
+    }
+  } else if (atten_mask != nullptr) {
     const int dt = atten_mask->dtype;
     if (dt != FIA_DT_BOOL && dt != FIA_DT_INT8 && dt != FIA_DT_UINT8) {
       return fail(FIA_ERR_PARAM_INVALID, "atten_mask dtype must be bool, int8 or uint8");
@@ -597,6 +632,11 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   a.next = p->next_tokens;
   a.slopes = pse == 2 ? static_cast<const float*>(pse_shift->data) : nullptr;
   a.alibi_delta = (int32_t)(p->kv_start_idx - p->q_start_idx);
+  a.mask = explicit_mask ? static_cast<const uint8_t*>(atten_mask->data) : nullptr;
+  a.mask_sb = mask_sb;
+  a.mask_ss = mask_ss;
+  a.mask_rows = (int32_t)mask_rows;
+  a.mask_cols = (int32_t)mask_cols;
 
   // Per-batch records.
   e->meta.assign((size_t)B * fia::BF_COUNT, 0);

@@ -170,6 +170,15 @@ __device__ __forceinline__ u32x2 lds_tr16(const void* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// Workgroup barrier that also publishes buffer-to-LDS loads: each wave first
+// waits for all of its own outstanding vector-memory operations.  The
+// workgroup-scope fence of __syncthreads does not reliably wait for them, so
+// another wave could otherwise read LDS rows whose load is still in flight.
+__device__ __forceinline__ void barrier_after_loads() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt, lgkmcnt unconstrained
+  __syncthreads();
+}
+
 // Global loads/stores of 16 and 8 bytes.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u32x2 ld8(const void* p) { return *reinterpret_cast<const u32x2*>(p); }

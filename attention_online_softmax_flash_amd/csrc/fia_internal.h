@@ -63,6 +63,12 @@ struct AttnArgs {
   int64_t pre, next;                // band (mode 4)
   const float* slopes;              // ALiBi slopes [Qn] or nullptr
   int32_t alibi_delta;              // kv_start_idx - q_start_idx
+  // Explicit mask (modes 0 / 1) or nullptr: key j of query row i of batch b
+  // is masked out when mask[b * mask_sb + i * mask_ss + j] != 0.  Rows and
+  // mask_sb are multiples of 4 bytes; mask_cols >= the KV extent.
+  const uint8_t* mask;
+  int64_t mask_sb, mask_ss;
+  int32_t mask_rows, mask_cols;
   int32_t write_lse;
   // decode split-KV
   int32_t chunk;                    // tokens per chunk (multiple of 128)

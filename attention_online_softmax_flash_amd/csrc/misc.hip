@@ -57,6 +57,10 @@ __global__ __launch_bounds__(256) void attn_fp32(AttnArgs a) {
     khi = h1;
   }
   const float slope = a.slopes != nullptr ? a.slopes[h] * kLog2e : 0.f;
+  // Explicit mask row (modes 0 / 1); rows i < Lq <= mask_rows when live.
+  const uint8_t* mrow = a.mask != nullptr
+                            ? a.mask + (int64_t)b * a.mask_sb + (int64_t)min(i, a.mask_rows - 1) * a.mask_ss
+                            : nullptr;
   float m_run = kNegInf, l_run = 0.f;
   const float* kg = (const float*)a.k;
   const float* vg = (const float*)a.v;
@@ -87,6 +91,7 @@ __global__ __launch_bounds__(256) void attn_fp32(AttnArgs a) {
 #pragma unroll
       for (int msk = 1; msk < T; msk <<= 1) dot += __shfl_xor(dot, msk, 64);
       if (j < lo || j >= hi) continue;
+      if (mrow != nullptr && mrow[j] != 0) continue;
       const float x = dot * a.scale_log2 + slope * (float)(j - i + a.alibi_delta);
       const float m_new = fmaxf(m_run, x);
       const float alpha = fast_exp2(m_run - m_new);

@@ -60,7 +60,10 @@ struct TileRegs {
 // registers (KVM 2); value tiles go through registers, transposed on the way
 // in.  Each stage is its own LDS array, so the compiler's wait for an
 // outstanding buffer-to-LDS load only guards reads of that stage.
-template <int D, bool ALIBI, int KVM>
+//
+// MASKT: an explicit mask tensor (modes 0 / 1); every tile takes the
+// per-element path and also drops keys whose mask byte is non-zero.
+template <int D, bool ALIBI, int KVM, bool MASKT>
 __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   using L = PrefillLds<D>;
   constexpr int NQ = D / 16;   // 16-wide d chunks of the score product
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   // PIPE: the score product of tile t+1 is issued together with the softmax
   // of tile t (needs a second score buffer; too many registers with the ALiBi
   // bias or per-row paging, which compute each tile's scores up front).
-  constexpr bool PIPE = !ALIBI && KVM != 2;
+  constexpr bool PIPE = !ALIBI && !MASKT && KVM != 2;
   constexpr bool INTERLEAVE = PIPE;
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[L::K_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_k1[L::K_BYTES];
@@ -138,6 +141,26 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     for (int c = 0; c < NQ; ++c) qreg[c] = row_live ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
 
     const float c_al = ALIBI ? a.slopes[h] * kLog2e : 0.f;
+    // Explicit mask row of this lane's query row (rows past Q_S are dead;
+    // their index is clamped into the mask).
+    const uint8_t* mrow = MASKT ? a.mask + (int64_t)b * a.mask_sb +
+                                      (int64_t)min(i, a.mask_rows - 1) * a.mask_ss
+                                : nullptr;
+    uint32_t mw[8];
+    // Mask bytes of keys j0 + 4 hh + 32 k2 + 8 g .. + 3 (4-aligned; a group
+    // past the mask width lies past every visible key: address clamped).
+    auto load_mask = [&](int kt) FIA_INLINE {
+      if constexpr (MASKT) {
+#pragma unroll
+        for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int j4 = min(kt * BN + 4 * hh + 32 * k2 + 8 * g4, a.mask_cols - 4);
+            mw[4 * k2 + g4] = *reinterpret_cast<const uint32_t*>(mrow + j4);
+          }
+        }
+      }
+    };
     const uint16_t* kg = (const uint16_t*)a.k;
     const uint16_t* vg = (const uint16_t*)a.v;
     const uint16_t* kbase0 = kg + (int64_t)b * a.k_sb + (int64_t)kv_off * a.k_ss + (int64_t)kvh * a.k_sh;
@@ -320,7 +343,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
             const int koff = 32 * k2 + 8 * (r >> 2) + (r & 3);
             float x = ALIBI ? __builtin_fmaf(sc[k2][r], a.scale_log2, c_al * (base + (float)koff))
                             : sc[k2][r] * a.scale_log2;
-            if constexpr (MASKED) x = (koff >= rel_lo && koff < rel_hi) ? x : kNegInf;
+            if constexpr (MASKED) {
+              bool keep = koff >= rel_lo && koff < rel_hi;
+              if constexpr (MASKT) keep = keep && ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) == 0u;
+              x = keep ? x : kNegInf;
+            }
             sc[k2][r] = x;
             mx = fmaxf(mx, x);
           }
@@ -397,10 +424,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     const bool has1 = kt0 + 1 < kt1;
     load_tile(kt0, lds_k0);
     if (PIPE && DMA_K && has1) load_k_lds(kt0 + 1, lds_k1);
-    __syncthreads();   // waits for every load so far
+    barrier_after_loads();
     store_tile(lds_k0, lds_v0);
     if (has1) load_tile(kt0 + 1, (!PIPE && DMA_K) ? lds_k1 : nullptr);
-    __syncthreads();
+    barrier_after_loads();
     f32x16 s_a[2], s_b[2];
     bool cur_skip = wave_skip(kt0);
     if (PIPE && !cur_skip) compute_s(lds_k0, s_a);
@@ -417,10 +444,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       if (has_next2) load_tile(kt + 2, (PIPE && DMA_K) ? kst : nullptr);
       const bool next_skip = has_next ? wave_skip(kt + 1) : true;
       const uint8_t* knext = (!PIPE || next_skip) ? nullptr : knx;
+      if (MASKT && !cur_skip) load_mask(kt);
       if (!PIPE && !cur_skip) compute_s(kst, sc);
       if (!cur_skip) {
         const int j0 = kt * BN;
-        const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min);
+        const bool need_mask = MASKT || !(j0 >= wlo_max && j0 + BN <= whi_min);
         if (need_mask) {
           tile_body(std::true_type{}, kt, vst, sc, knext, sn);
         } else {
@@ -430,7 +458,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         compute_s(knext, sn);
       }
       cur_skip = next_skip;
-      __syncthreads();   // loads of tile kt + 2 landed; every wave is done with tile kt
+      barrier_after_loads();   // loads of tile kt + 2 landed; every wave is done with tile kt
       if (has_next2) {
         if constexpr (!PIPE && DMA_K) load_k_lds(kt + 2, kst);
         store_tile(kst, vst);
@@ -468,7 +496,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 
 template <int D, bool ALIBI, int KVM>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  prefill_bf16<D, ALIBI, KVM><<<a.n_work, 256, 0, s>>>(a);
+  if (a.mask != nullptr) {
+    prefill_bf16<D, ALIBI, KVM, true><<<a.n_work, 256, 0, s>>>(a);
+  } else {
+    prefill_bf16<D, ALIBI, KVM, false><<<a.n_work, 256, 0, s>>>(a);
+  }
   return hipSuccess;
 }
 

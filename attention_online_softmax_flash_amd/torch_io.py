@@ -32,6 +32,10 @@ def dense_tensors(case: DenseCase, device="cuda"):
     return q, k, v, bt, slopes
 
 
+def mask_tensor(case: DenseCase, device="cuda"):
+    return None if case.atten_mask is None else torch.from_numpy(case.atten_mask).to(device)
+
+
 def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia.AttentionPlan:
     q, k, v, bt, slopes = tensors if tensors is not None else dense_tensors(case, device)
     kw = dict(num_heads=case.num_heads, num_key_value_heads=case.num_kv_heads,
@@ -41,7 +45,8 @@ def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia
               q_start_idx=case.q_start_idx, kv_start_idx=case.kv_start_idx,
               block_table=bt, block_size=case.block_size if bt is not None else 0,
               softmax_lse_flag=case.lse, actual_seq_lengths=case.actual_seq_lengths,
-              actual_seq_lengths_kv=case.actual_seq_lengths_kv, kv_layout=case.kv_layout)
+              actual_seq_lengths_kv=case.actual_seq_lengths_kv, kv_layout=case.kv_layout,
+              atten_mask=mask_tensor(case, device))
     kw.update(overrides)
     return fia.AttentionPlan(q, k, v, **kw)
 

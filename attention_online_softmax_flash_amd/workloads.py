@@ -91,6 +91,7 @@ class DenseCase:
     k_pool: Optional[np.ndarray] = None
     v_pool: Optional[np.ndarray] = None
     kv_layout: str = "PA_ND"
+    atten_mask: Optional[np.ndarray] = None     # uint8 / bool, modes 0 / 1; != 0 masks out
     lse: bool = False
     seed: int = 0
 
@@ -103,6 +104,28 @@ class DenseCase:
         if self.layout == "TND":
             return len(self.actual_seq_lengths)
         return self.q.shape[0]
+
+
+def with_random_mask(case: DenseCase, seed: int, *, p_masked=0.3, dims=3, per_batch=True,
+                     dead_rows=(), mode=0) -> DenseCase:
+    """The case with an explicit uint8 mask (1 = masked out), shape
+    [B or 1, Q_S, KV_S'] (dims 3), [B or 1, 1, Q_S, KV_S'] (dims 4) or
+    [Q_S, KV_S'] (dims 2), KV_S' = KV_S rounded up to a multiple of 4 (the
+    padding columns are 1).  ``dead_rows`` are fully masked."""
+    rng = rng_for(seed)
+    B, S1 = case.q.shape[0], case.q.shape[1]
+    S2 = case.block_size * case.block_table.shape[1] if case.paged else case.k.shape[1]
+    S2p = -(-S2 // 4) * 4
+    nb = B if (per_batch and dims != 2) else 1
+    m = (rng.random((nb, S1, S2p)) < p_masked).astype(np.uint8)
+    m[:, :, S2:] = 1
+    for r in dead_rows:
+        m[:, r, :] = 1
+    if dims == 2:
+        m = m[0]
+    elif dims == 4:
+        m = m[:, None]
+    return dataclasses.replace(case, name=case.name + "_mask", atten_mask=m, sparse_mode=mode)
 
 
 def as_bnnbsd(case: DenseCase) -> DenseCase:

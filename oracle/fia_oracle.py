@@ -23,7 +23,9 @@ What it computes, and where each step is stated on the pages:
   KV head n is pool[blockTable[b][j // bs], n, j % bs].
 * Mask modes (V5 Attention Mask parameter group; V2 sparseMode rules), with
   delta = Lk - Lq.  Reading (the mode table itself is not legible):
-  0 -> all keys j < Lk, 2 -> j <= i (left-up causal),
+  0 -> all keys j < Lk (with an explicit atten_mask tensor, modes 0 and 1:
+  the keys j < Lk whose mask element [b or 0][i][j] is 0; 1 = masked out),
+  2 -> j <= i (left-up causal),
   3 -> j <= i + delta (right-down causal, the "lower triangle anchored at the
   right vertex" of KvQuantSparseAttnSharedkv cmp_mask_mode),
   4 -> i + delta - pre <= j <= i + delta + next (band).
@@ -176,7 +178,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
         next_tokens: int = 2147483647, alibi_slopes=None, q_start_idx: int = 0,
         kv_start_idx: int = 0, actual_seq_lengths=None, actual_seq_lengths_kv=None,
         block_table=None, block_size: int = 0, k_pool=None, v_pool=None,
-        kv_layout: str = "PA_ND",
+        kv_layout: str = "PA_ND", atten_mask=None,
         batches: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
         rows: Optional[Sequence[int]] = None, row_chunk: int = 1024):
     """Fused inference attention, float64.
@@ -245,7 +247,13 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
                         jpos = (kv_start_idx + np.arange(Lk))[None, :]
                         ipos = (q_start_idx + live)[:, None]
                         s = s + slopes[h] * (jpos - ipos)
-                    vis = visible(sparse_mode, Lq, Lk, pre_tokens, next_tokens)[live]
+                    if atten_mask is not None and sparse_mode in (0, 1):
+                        m = np.asarray(atten_mask)
+                        m2 = m.reshape(m.shape[-2], m.shape[-1]) if m.ndim == 2 else \
+                            m.reshape(m.shape[0], m.shape[-2], m.shape[-1])[b if m.shape[0] > 1 else 0]
+                        vis = (m2[:Lq, :Lk] == 0)[live]
+                    else:
+                        vis = visible(sparse_mode, Lq, Lk, pre_tokens, next_tokens)[live]
                     o_live, l_live = softmax_rows(s, vis, V)
                     pos = np.searchsorted(idx, live)
                     o_blk[pos] = o_live
@@ -271,7 +279,8 @@ def fia_case(case, **kw):
                actual_seq_lengths_kv=case.actual_seq_lengths_kv,
                block_table=case.block_table, block_size=case.block_size,
                k_pool=case.k_pool, v_pool=case.v_pool,
-               kv_layout=getattr(case, "kv_layout", "PA_ND"), **kw)
+               kv_layout=getattr(case, "kv_layout", "PA_ND"),
+               atten_mask=getattr(case, "atten_mask", None), **kw)
 
 
 # ---------------------------------------------------------------------------

@@ -133,7 +133,7 @@ UNS = fia.FIA_ERR_UNSUPPORTED
     ("group ratio above 64", dict(num_heads=130, num_kv_heads=2), BAD),
     ("sparse_mode out of range", dict(sparse_mode=5), BAD),
     ("sparse_mode negative", dict(sparse_mode=-1), BAD),
-    ("sparse_mode 1 needs a mask tensor", dict(sparse_mode=1), UNS),
+    ("sparse_mode 1 needs a mask tensor", dict(sparse_mode=1), BAD),
     ("band with -next > pre", dict(sparse_mode=4, pre_tokens=-3, next_tokens=2), BAD),
     ("pse_type out of range", dict(pse_type=4), BAD),
     ("pse_type 1 is training only", dict(pse_type=1), BAD),
@@ -195,8 +195,9 @@ def test_mask_tensor_rules():
     assert st == BAD
     st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=3), q, k, v, o, mask=T((2048, 2048), fia.DT_FP32))
     assert st == BAD
+    # mode 0 reads an explicit mask; a 2048 x 2048 one covers this problem
     st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q, k, v, o, mask=good)
-    assert st == UNS
+    assert st == 0, msg
 
 
 def test_paged_rules():
@@ -253,6 +254,37 @@ def test_bnnbsd_paged_rules():
     o2 = T((2, 64, 4, 128))
     st, kind, _, msg = plan(P(kv_layout="BnNBsD", sparse_mode=3, **ok), q2, pool, pool, o2, bt=bt)
     assert st == 0 and kind == "prefill", msg
+
+
+def test_explicit_mask_rules():
+    q, k, v, o = dense(B=2, S1=64, S2=64)
+    for shape in [(2, 64, 64), (1, 64, 64), (64, 64), (2, 1, 64, 64), (2, 80, 128)]:
+        for mode in (0, 1):
+            st, kind, _, msg = plan(P(num_kv_heads=2, sparse_mode=mode), q, k, v, o,
+                                    mask=T(shape, fia.DT_UINT8))
+            assert st == 0 and kind == "prefill", (shape, mode, msg)
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q, k, v, o, mask=T((2, 64, 64), fia.DT_BOOL))
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=1), q, k, v, o)
+    assert st == BAD and "atten_mask" in msg
+    bad = [((3, 64, 64), fia.DT_UINT8), ((2, 63, 64), fia.DT_UINT8), ((2, 64, 60), fia.DT_UINT8),
+           ((2, 2, 64, 64), fia.DT_UINT8), ((2, 64, 64), fia.DT_FP32), ((64,), fia.DT_UINT8)]
+    for shape, dt in bad:
+        st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q, k, v, o, mask=T(shape, dt))
+        assert st == BAD, (shape, dt, msg)
+    # rows not 4-byte aligned
+    q2, k2, v2, o2 = dense(B=2, S1=8, S2=62)
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q2, k2, v2, o2,
+                         mask=T((2, 8, 62), fia.DT_UINT8))
+    assert st == UNS and "aligned" in msg
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q2, k2, v2, o2,
+                         mask=T((2, 8, 64), fia.DT_UINT8))
+    assert st == 0, msg
+    # decode with a mask
+    q1, k1, v1, o1 = dense(S1=1, S2=300)
+    st, kind, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q1, k1, v1, o1,
+                            mask=T((2, 1, 300), fia.DT_INT8))
+    assert st == 0 and kind == "decode", msg
 
 
 def test_tnd_rules():

@@ -167,6 +167,45 @@ def test_prefill_over_paged_kv_bnnbsd(bs):
     dense_parity(W.as_bnnbsd(case), "prefill")
 
 
+MASK_PREFILL_CASES = [
+    # (B, S1, S2, Qn, KVn, D, dims, per_batch, mode, q_lens, kv_lens)
+    (2, 200, 300, 8, 2, 128, 3, True, 0, [200, 150], [300, 290]),
+    (1, 130, 130, 4, 4, 128, 2, False, 1, None, None),
+    (2, 70, 97, 8, 4, 64, 4, True, 0, [70, 33], [97, 60]),
+]
+
+
+@pytest.mark.parametrize("i", range(len(MASK_PREFILL_CASES)))
+def test_prefill_explicit_mask(i):
+    B, S1, S2, Qn, KVn, D, dims, pb, mode, ql, kl = MASK_PREFILL_CASES[i]
+    case = W.dense_case(f"mp{i}", 700 + i, B=B, S1=S1, S2=S2, Q_N=Qn, KV_N=KVn, D=D,
+                        q_lens=ql, kv_lens=kl, lse=True, poison_pad=True)
+    case = W.with_random_mask(case, 710 + i, dims=dims, per_batch=pb, dead_rows=(5,), mode=mode)
+    dense_parity(case, "prefill")
+
+
+def test_prefill_explicit_mask_paged():
+    case = W.paged_decode_case("mpp", 720, B=2, Q_N=8, KV_N=2, D=128, kv_lens=[300, 129],
+                               block_size=64, S1=40, lse=True, poison_tail=True, extra_blocks=2)
+    case.actual_seq_lengths = [40, 40]
+    dense_parity(W.with_random_mask(case, 721, dead_rows=(0,)), "prefill")
+
+
+def test_decode_explicit_mask():
+    case = W.paged_decode_case("mdp", 730, B=3, Q_N=32, KV_N=8, D=128, kv_lens=[1, 700, 1500],
+                               block_size=128, lse=True, poison_tail=True, extra_blocks=2)
+    dense_parity(W.with_random_mask(case, 731, p_masked=0.5), "decode")
+    case = W.dense_case("mdd", 732, B=2, S1=1, S2=900, Q_N=8, KV_N=2, D=64, kv_lens=[900, 40],
+                        lse=True, poison_pad=True)
+    dense_parity(W.with_random_mask(case, 733, dims=2, per_batch=False, mode=1), "decode")
+
+
+def test_fp32_explicit_mask():
+    case = W.dense_case("mf", 740, B=2, S1=37, S2=50, Q_N=4, KV_N=2, D=64, dtype="fp32",
+                        lse=True, poison_pad=True)
+    plan, out, lse = dense_parity(W.with_random_mask(case, 741, dead_rows=(2,)), "fp32")
+
+
 BNNBSD_DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size)
     (3, 32, 8, 128, [1, 511, 1300], 128),

@@ -5,6 +5,7 @@ expected value comes from a library routine (torch's scaled_dot_product
 attention, torch's bf16 / e4m3fn casts), a closed form, an invariant, or a
 hand-derived golden fixture under tests/golden/.
 """
+import dataclasses
 import json
 import math
 import os
@@ -394,6 +395,51 @@ def test_heavily_compressed_rows_hand_values():
     assert win == list(range(0, 100)) and comp == []
     win, comp = O.sparse_rows(1024, 1, 0, None, cmp_ratio=128, win_left=127, win_right=0)
     assert comp == list(range(8))
+
+
+def test_explicit_mask_reduces_to_analytic_modes():
+    """An explicit mask equal to the left-up causal pattern reproduces mode 2,
+    an all-zero mask reproduces mode 0, and a fully masked row is empty."""
+    c = W.dense_case("em", 60, B=2, S1=9, S2=12, Q_N=4, KV_N=2, D=16, lse=True)
+    i = np.arange(9)[:, None]
+    j = np.arange(12)[None, :]
+    causal = (j > i).astype(np.uint8)                  # 1 = masked out
+    m = np.broadcast_to(causal, (2, 9, 12)).copy()
+    o2, l2 = O.fia_case(dataclasses.replace(c, sparse_mode=2))
+    om, lm = O.fia_case(dataclasses.replace(c, sparse_mode=1, atten_mask=m))
+    np.testing.assert_array_equal(om, o2)
+    np.testing.assert_array_equal(lm, l2)
+    o0, l0 = O.fia_case(c)
+    oz, lz = O.fia_case(dataclasses.replace(c, sparse_mode=0, atten_mask=np.zeros((9, 12), np.uint8)))
+    np.testing.assert_array_equal(oz, o0)
+    m[1, 3, :] = 1
+    od, ld = O.fia_case(dataclasses.replace(c, sparse_mode=0, atten_mask=m))
+    assert np.all(od[1, 3] == 0) and np.all(np.isposinf(ld[1, :, 3]))
+
+
+def test_explicit_mask_brute_force():
+    """A random 4-dim mask against a direct evaluation of softmax over the
+    kept keys only (pure Python loops)."""
+    c = W.dense_case("eb", 61, B=2, S1=3, S2=5, Q_N=2, KV_N=1, D=4, dtype="fp32", lse=True)
+    rng = np.random.default_rng(7)
+    m = (rng.random((2, 1, 3, 8)) < 0.4).astype(np.uint8)
+    out, lse = O.fia_case(dataclasses.replace(c, sparse_mode=0, atten_mask=m))
+    for b in range(2):
+        for h in range(2):
+            for i in range(3):
+                keep = [jj for jj in range(5) if m[b, 0, i, jj] == 0]
+                if not keep:
+                    assert np.all(out[b, i, h] == 0) and math.isinf(lse[b, h, i])
+                    continue
+                s = [c.scale * sum(float(c.q[b, i, h, d]) * float(c.k[b, jj, 0, d]) for d in range(4))
+                     for jj in keep]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                den = sum(w)
+                for d in range(4):
+                    want = sum(wk * float(c.v[b, jj, 0, d]) for wk, jj in zip(w, keep)) / den
+                    assert abs(out[b, i, h, d] - want) < 1e-12
+                assert abs(lse[b, h, i] - (mx + math.log(den))) < 1e-12
 
 
 def test_split_keys_merge_by_lse_reproduces_full():
