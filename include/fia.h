@@ -98,9 +98,11 @@ typedef struct {
    *   0 all keys visible (no mask tensor)      2 left-up causal   j <= i
    *   3 right-down causal j <= i + (Lk - Lq)    4 band:
    *     i + (Lk-Lq) - pre_tokens <= j <= i + (Lk-Lq) + next_tokens
-   * Mode 1 needs an explicit mask tensor and is unsupported.  For modes 2-4
-   * the mask is generated from its definition; an atten_mask tensor, if
-   * passed, must be the 2048x2048 lower-triangular form and is not read. */
+   * Modes 0 and 1 with an atten_mask tensor: key j of query row i is kept
+   * only when mask[b or 0][i][j] == 0 (1 = masked out); mode 1 requires the
+   * tensor, mode 0 without it keeps every key j < Lk.  For modes 2-4 the mask
+   * is generated from its definition; an atten_mask tensor, if passed, must
+   * be the 2048x2048 lower-triangular form and is not read. */
   int32_t sparse_mode;
   int64_t pre_tokens;           /* default 2147483647 */
   int64_t next_tokens;          /* default 2147483647; -next_tokens <= pre_tokens */
@@ -139,7 +141,12 @@ typedef struct {
  *                   dtype as query.
  *                   key and value may be the same tensor.
  *   pse_shift       NULL, or fp32 [Q_N] slopes when pse_type == 2.
- *   atten_mask      NULL, or the 2048x2048 causal mask for modes 2-4 (unread).
+ *   atten_mask      modes 0 / 1: NULL or int8 / uint8 / bool [B or 1, >= Q_S,
+ *                   >= KV_S], [B or 1, 1, >= Q_S, >= KV_S] or [>= Q_S, >= KV_S]
+ *                   (KV_S = block_table cols * block_size when paged), rows
+ *                   contiguous and 4-byte aligned (KV extent padded to a
+ *                   multiple of 4); not with TND.  Modes 2-4: NULL or the
+ *                   2048x2048 causal mask (unread).
  *   block_table     NULL, or int32 [B, >= ceil(max Lk / block_size)]; requires
  *                   actual_seq_lengths_kv (V5 Paged Attention group).
  *   attention_out   same shape and layout as query, same dtype.
