@@ -21,9 +21,10 @@
 
 namespace fia {
 
-// MASKT: an explicit mask tensor (modes 0 / 1) removes keys whose mask byte
-// (query row 0 of the batch) is non-zero.
-template <int D, bool MASKT>
+// EXT: an explicit mask tensor (modes 0 / 1) removes keys whose mask byte
+// (query row 0 of the batch) is non-zero; a bias tensor (pse type 0) adds
+// row 0 of the head's bias to the scaled scores.
+template <int D, bool EXT>
 __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide d chunks of the score product
   constexpr int DPL = D / 16;  // value columns per lane column (8 for D = 128)
@@ -80,7 +81,11 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   static_assert(sizeof(sm_o[0]) >= 32 * 2 * D, "key slot does not fit");
   char* kbuf = reinterpret_cast<char*>(&sm_o[wave][0][0]);
 
-  const uint8_t* mrow = MASKT ? a.mask + (int64_t)b * a.mask_sb : nullptr;
+  const bool has_mask = EXT && a.mask != nullptr;
+  const bool has_pse = EXT && a.pse != nullptr;
+  const uint8_t* mrow = has_mask ? a.mask + (int64_t)b * a.mask_sb : nullptr;
+  const uint16_t* prow = has_pse ? (const uint16_t*)a.pse + (int64_t)b * a.pse_sb + (int64_t)h * a.pse_sh
+                                 : nullptr;
   const uint16_t* kbase = (const uint16_t*)a.k;
   const uint16_t* vbase = (const uint16_t*)a.v;
 
@@ -147,15 +152,17 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
           sc[hf] = mfma16(kr, qv[cc], sc[hf]);
         }
       }
-      // Mask bytes of keys ts + 16 hf + 4 g .. + 3 (4-aligned; a group past
-      // the mask width lies past every visible key, so its address is
-      // clamped and its bytes unused).
+      // Mask bytes and bias values of keys ts + 16 hf + 4 g .. + 3
+      // (4-aligned; a group past the tensor's width lies past every visible
+      // key, so its address is clamped and its values unused).
       uint32_t mw[2] = {0u, 0u};
-      if constexpr (MASKT) {
+      u32x2 pw[2] = {u32x2{0u, 0u}, u32x2{0u, 0u}};
+      if constexpr (EXT) {
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int j4 = min(ts + 16 * hf + 4 * g, a.mask_cols - 4);
-          mw[hf] = *reinterpret_cast<const uint32_t*>(mrow + j4);
+          const int j = ts + 16 * hf + 4 * g;
+          if (has_mask) mw[hf] = *reinterpret_cast<const uint32_t*>(mrow + min(j, a.mask_cols - 4));
+          if (has_pse) pw[hf] = *reinterpret_cast<const u32x2*>(prow + min(j, a.pse_cols - 4));
         }
       }
       float x[8];
@@ -164,9 +171,13 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
       for (int s = 0; s < 8; ++s) {
         const int j = ts + 16 * (s >> 2) + 4 * g + (s & 3);
         bool ok = j >= t_lo && j < t_hi;
-        if constexpr (MASKT) ok = ok && ((mw[s >> 2] >> (8 * (s & 3))) & 0xffu) == 0u;
+        if constexpr (EXT) ok = ok && ((mw[s >> 2] >> (8 * (s & 3))) & 0xffu) == 0u;
         float v = sc[s >> 2][s & 3] * a.scale_log2;
         v += c_alibi * (float)(j + a.alibi_delta);
+        if constexpr (EXT) {
+          const uint32_t pv = pw[s >> 2][(s >> 1) & 1];
+          v = __builtin_fmaf(__builtin_bit_cast(float, (s & 1) ? (pv & 0xffff0000u) : (pv << 16)), kLog2e, v);
+        }
         x[s] = ok ? v : kNegInf;
         mx = fmaxf(mx, x[s]);
       }
@@ -354,7 +365,7 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
 
 hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s) {
   if (n_items > 0) {
-    const bool m = a.mask != nullptr;
+    const bool m = a.mask != nullptr || a.pse != nullptr;
     if (a.D == 128) {
       if (m) decode_split_bf16<128, true><<<n_items, 256, 0, s>>>(a);
       else decode_split_bf16<128, false><<<n_items, 256, 0, s>>>(a);

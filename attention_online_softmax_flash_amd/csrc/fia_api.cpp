@@ -504,8 +504,35 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   }
   if (pse == 1) return fail(FIA_ERR_PARAM_INVALID, "pse_type 1 is for training only");
   if (pse == 3) return fail(FIA_ERR_UNSUPPORTED, "pse_type 3 is not supported");
-  if (pse == 0 && pse_shift != nullptr) {
-    return fail(FIA_ERR_UNSUPPORTED, "an explicit pse_shift bias tensor is not supported");
+  // pseType 0 with a tensor: bias [B or 1, Q_N, >= Q_S or 1, >= KV_S] in the
+  // query's dtype, added to the scaled scores (V5 PSE group).
+  int64_t pse_sb = 0, pse_sh = 0, pse_ss = 0, pse_rows = 0, pse_cols = 0;
+  const bool pse_tensor = pse == 0 && pse_shift != nullptr;
+  if (pse_tensor) {
+    if ((st = check_tensor(pse_shift, "pse_shift")) != FIA_SUCCESS) return st;
+    if (pse_shift->dtype != query->dtype) {
+      return fail(FIA_ERR_PARAM_INVALID, "pse_shift must have the query's dtype");
+    }
+    if (tnd) return fail(FIA_ERR_UNSUPPORTED, "a pse_shift tensor with TND is not supported");
+    if (pse_shift->ndim != 4) return fail(FIA_ERR_PARAM_INVALID, "pse_shift must have 4 dims");
+    const int64_t pb = pse_shift->shape[0];
+    pse_rows = pse_shift->shape[2];
+    pse_cols = pse_shift->shape[3];
+    const int64_t S2p = paged ? bt_cols * bs : ck.S;
+    if ((pb != 1 && pb != B) || pse_shift->shape[1] != Qn || (pse_rows != 1 && pse_rows < cq.S) ||
+        pse_cols < S2p) {
+      return fail(FIA_ERR_PARAM_INVALID, "pse_shift must be [B or 1, Q_N, >= Q_S or 1, >= KV_S]");
+    }
+    if (pse_shift->stride[3] != 1) return fail(FIA_ERR_PARAM_INVALID, "pse_shift rows must be contiguous");
+    pse_sb = pb > 1 ? pse_shift->stride[0] : 0;
+    pse_sh = pse_shift->stride[1];
+    pse_ss = pse_rows > 1 ? pse_shift->stride[2] : 0;
+    const int64_t esz = query->dtype == FIA_DT_FP32 ? 4 : 2;
+    if (pse_sb % 4 || pse_sh % 4 || pse_ss % 4 || pse_cols % 4 ||
+        reinterpret_cast<uintptr_t>(pse_shift->data) % (4 * esz)) {
+      return fail(FIA_ERR_UNSUPPORTED, "pse_shift rows must be aligned to 4 elements (pad KV_S to a "
+                                       "multiple of 4)");
+    }
   }
   if (pse == 2) {
     if (pse_shift == nullptr) return fail(FIA_ERR_PARAM_INVALID, "pse_type 2 requires pse_shift");
@@ -632,6 +659,12 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   a.next = p->next_tokens;
   a.slopes = pse == 2 ? static_cast<const float*>(pse_shift->data) : nullptr;
   a.alibi_delta = (int32_t)(p->kv_start_idx - p->q_start_idx);
+  a.pse = pse_tensor ? pse_shift->data : nullptr;
+  a.pse_sb = pse_sb;
+  a.pse_sh = pse_sh;
+  a.pse_ss = pse_ss;
+  a.pse_rows = (int32_t)pse_rows;
+  a.pse_cols = (int32_t)pse_cols;
   a.mask = explicit_mask ? static_cast<const uint8_t*>(atten_mask->data) : nullptr;
   a.mask_sb = mask_sb;
   a.mask_ss = mask_ss;

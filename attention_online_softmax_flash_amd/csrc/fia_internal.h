@@ -69,6 +69,13 @@ struct AttnArgs {
   const uint8_t* mask;
   int64_t mask_sb, mask_ss;
   int32_t mask_rows, mask_cols;
+  // Bias tensor (pse type 0) or nullptr, in the element type of q: added to
+  // the scaled score of (b, h, i, j) at pse[b * pse_sb + h * pse_sh +
+  // i * pse_ss + j] (pse_ss = 0: one row for every query row).  Strides in
+  // elements, multiples of 4; pse_cols >= the KV extent.
+  const void* pse;
+  int64_t pse_sb, pse_sh, pse_ss;
+  int32_t pse_rows, pse_cols;
   int32_t write_lse;
   // decode split-KV
   int32_t chunk;                    // tokens per chunk (multiple of 128)

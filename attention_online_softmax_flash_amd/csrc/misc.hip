@@ -61,6 +61,10 @@ __global__ __launch_bounds__(256) void attn_fp32(AttnArgs a) {
   const uint8_t* mrow = a.mask != nullptr
                             ? a.mask + (int64_t)b * a.mask_sb + (int64_t)min(i, a.mask_rows - 1) * a.mask_ss
                             : nullptr;
+  // Bias row (pse type 0), fp32 like the query.
+  const float* prow = a.pse != nullptr ? (const float*)a.pse + (int64_t)b * a.pse_sb + (int64_t)h * a.pse_sh +
+                                             (int64_t)min(i, a.pse_rows - 1) * a.pse_ss
+                                       : nullptr;
   float m_run = kNegInf, l_run = 0.f;
   const float* kg = (const float*)a.k;
   const float* vg = (const float*)a.v;
@@ -92,7 +96,8 @@ __global__ __launch_bounds__(256) void attn_fp32(AttnArgs a) {
       for (int msk = 1; msk < T; msk <<= 1) dot += __shfl_xor(dot, msk, 64);
       if (j < lo || j >= hi) continue;
       if (mrow != nullptr && mrow[j] != 0) continue;
-      const float x = dot * a.scale_log2 + slope * (float)(j - i + a.alibi_delta);
+      float x = dot * a.scale_log2 + slope * (float)(j - i + a.alibi_delta);
+      if (prow != nullptr) x = __builtin_fmaf(prow[j], kLog2e, x);
       const float m_new = fmaxf(m_run, x);
       const float alpha = fast_exp2(m_run - m_new);
       const float p = fast_exp2(x - m_new);

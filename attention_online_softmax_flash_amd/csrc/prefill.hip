@@ -61,9 +61,10 @@ struct TileRegs {
 // in.  Each stage is its own LDS array, so the compiler's wait for an
 // outstanding buffer-to-LDS load only guards reads of that stage.
 //
-// MASKT: an explicit mask tensor (modes 0 / 1); every tile takes the
-// per-element path and also drops keys whose mask byte is non-zero.
-template <int D, bool ALIBI, int KVM, bool MASKT>
+// EXT: an explicit mask tensor (modes 0 / 1) and / or a bias tensor (pse
+// type 0); every tile takes the per-element path, drops keys whose mask byte
+// is non-zero and adds the bias to the scaled scores.
+template <int D, bool ALIBI, int KVM, bool EXT>
 __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   using L = PrefillLds<D>;
   constexpr int NQ = D / 16;   // 16-wide d chunks of the score product
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   // PIPE: the score product of tile t+1 is issued together with the softmax
   // of tile t (needs a second score buffer; too many registers with the ALiBi
   // bias or per-row paging, which compute each tile's scores up front).
-  constexpr bool PIPE = !ALIBI && !MASKT && KVM != 2;
+  constexpr bool PIPE = !ALIBI && !EXT && KVM != 2;
   constexpr bool INTERLEAVE = PIPE;
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[L::K_BYTES];
   __shared__ __attribute__((aligned(16))) uint8_t lds_k1[L::K_BYTES];
@@ -141,22 +142,32 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     for (int c = 0; c < NQ; ++c) qreg[c] = row_live ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
 
     const float c_al = ALIBI ? a.slopes[h] * kLog2e : 0.f;
-    // Explicit mask row of this lane's query row (rows past Q_S are dead;
-    // their index is clamped into the mask).
-    const uint8_t* mrow = MASKT ? a.mask + (int64_t)b * a.mask_sb +
-                                      (int64_t)min(i, a.mask_rows - 1) * a.mask_ss
-                                : nullptr;
+    // Explicit mask and bias rows of this lane's query row (rows past Q_S
+    // are dead; their index is clamped into the tensor).
+    const bool has_mask = EXT && a.mask != nullptr;
+    const bool has_pse = EXT && a.pse != nullptr;
+    const uint8_t* mrow = has_mask ? a.mask + (int64_t)b * a.mask_sb +
+                                         (int64_t)min(i, a.mask_rows - 1) * a.mask_ss
+                                   : nullptr;
+    const uint16_t* prow = has_pse ? (const uint16_t*)a.pse + (int64_t)b * a.pse_sb +
+                                         (int64_t)h * a.pse_sh +
+                                         (int64_t)min(i, a.pse_rows - 1) * a.pse_ss
+                                   : nullptr;
     uint32_t mw[8];
-    // Mask bytes of keys j0 + 4 hh + 32 k2 + 8 g .. + 3 (4-aligned; a group
-    // past the mask width lies past every visible key: address clamped).
-    auto load_mask = [&](int kt) FIA_INLINE {
-      if constexpr (MASKT) {
+    u32x2 pw[8];
+    // Mask bytes and bias values of keys j0 + 4 hh + 32 k2 + 8 g .. + 3
+    // (4-aligned; a group past the tensor's width lies past every visible
+    // key: address clamped, values unused).
+    auto load_ext = [&](int kt) FIA_INLINE {
+      if constexpr (EXT) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const int j4 = min(kt * BN + 4 * hh + 32 * k2 + 8 * g4, a.mask_cols - 4);
-            mw[4 * k2 + g4] = *reinterpret_cast<const uint32_t*>(mrow + j4);
+            const int j = kt * BN + 4 * hh + 32 * k2 + 8 * g4;
+            mw[4 * k2 + g4] = has_mask ? *reinterpret_cast<const uint32_t*>(mrow + min(j, a.mask_cols - 4)) : 0u;
+            pw[4 * k2 + g4] = has_pse ? *reinterpret_cast<const u32x2*>(prow + min(j, a.pse_cols - 4))
+                                      : u32x2{0u, 0u};
           }
         }
       }
@@ -343,9 +354,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
             const int koff = 32 * k2 + 8 * (r >> 2) + (r & 3);
             float x = ALIBI ? __builtin_fmaf(sc[k2][r], a.scale_log2, c_al * (base + (float)koff))
                             : sc[k2][r] * a.scale_log2;
+            if constexpr (EXT) {
+              // bf16 bias of key koff: half (r & 1) of word (r >> 1) & 1.
+              const uint32_t pv = pw[4 * k2 + (r >> 2)][(r >> 1) & 1];
+              const float bias = __builtin_bit_cast(float, (r & 1) ? (pv & 0xffff0000u) : (pv << 16));
+              x = __builtin_fmaf(bias, kLog2e, x);
+            }
             if constexpr (MASKED) {
               bool keep = koff >= rel_lo && koff < rel_hi;
-              if constexpr (MASKT) keep = keep && ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) == 0u;
+              if constexpr (EXT) keep = keep && ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) == 0u;
               x = keep ? x : kNegInf;
             }
             sc[k2][r] = x;
@@ -444,11 +461,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       if (has_next2) load_tile(kt + 2, (PIPE && DMA_K) ? kst : nullptr);
       const bool next_skip = has_next ? wave_skip(kt + 1) : true;
       const uint8_t* knext = (!PIPE || next_skip) ? nullptr : knx;
-      if (MASKT && !cur_skip) load_mask(kt);
+      if (EXT && !cur_skip) load_ext(kt);
       if (!PIPE && !cur_skip) compute_s(kst, sc);
       if (!cur_skip) {
         const int j0 = kt * BN;
-        const bool need_mask = MASKT || !(j0 >= wlo_max && j0 + BN <= whi_min);
+        const bool need_mask = EXT || !(j0 >= wlo_max && j0 + BN <= whi_min);
         if (need_mask) {
           tile_body(std::true_type{}, kt, vst, sc, knext, sn);
         } else {
@@ -496,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 
 template <int D, bool ALIBI, int KVM>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-  if (a.mask != nullptr) {
+  if (a.mask != nullptr || a.pse != nullptr) {
     prefill_bf16<D, ALIBI, KVM, true><<<a.n_work, 256, 0, s>>>(a);
   } else {
     prefill_bf16<D, ALIBI, KVM, false><<<a.n_work, 256, 0, s>>>(a);

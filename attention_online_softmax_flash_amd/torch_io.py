@@ -32,6 +32,10 @@ def dense_tensors(case: DenseCase, device="cuda"):
     return q, k, v, bt, slopes
 
 
+def pse_tensor(case: DenseCase, device="cuda"):
+    return None if case.pse_bias is None else to_device(case.pse_bias, case.dtype, device)
+
+
 def mask_tensor(case: DenseCase, device="cuda"):
     return None if case.atten_mask is None else torch.from_numpy(case.atten_mask).to(device)
 
@@ -41,7 +45,8 @@ def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia
     kw = dict(num_heads=case.num_heads, num_key_value_heads=case.num_kv_heads,
               scale_value=case.scale, input_layout=case.layout, sparse_mode=case.sparse_mode,
               pre_tokens=case.pre_tokens, next_tokens=case.next_tokens,
-              pse_type=2 if slopes is not None else 0, pse_shift=slopes,
+              pse_type=2 if slopes is not None else 0,
+              pse_shift=slopes if slopes is not None else pse_tensor(case, device),
               q_start_idx=case.q_start_idx, kv_start_idx=case.kv_start_idx,
               block_table=bt, block_size=case.block_size if bt is not None else 0,
               softmax_lse_flag=case.lse, actual_seq_lengths=case.actual_seq_lengths,

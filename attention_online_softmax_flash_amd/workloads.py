@@ -92,6 +92,7 @@ class DenseCase:
     v_pool: Optional[np.ndarray] = None
     kv_layout: str = "PA_ND"
     atten_mask: Optional[np.ndarray] = None     # uint8 / bool, modes 0 / 1; != 0 masks out
+    pse_bias: Optional[np.ndarray] = None       # [B or 1, Q_N, Q_S or 1, KV_S'] (pseType 0), q's dtype
     lse: bool = False
     seed: int = 0
 
@@ -126,6 +127,21 @@ def with_random_mask(case: DenseCase, seed: int, *, p_masked=0.3, dims=3, per_ba
     elif dims == 4:
         m = m[:, None]
     return dataclasses.replace(case, name=case.name + "_mask", atten_mask=m, sparse_mode=mode)
+
+
+def with_random_bias(case: DenseCase, seed: int, *, per_batch=True, one_row=False,
+                     std=1.0) -> DenseCase:
+    """The case with a pseType 0 bias tensor of normal values (mean 0, ``std``)
+    in the query's dtype, shape [B or 1, Q_N, Q_S or 1, KV_S'], KV_S' = KV_S
+    rounded up to a multiple of 4 (the padding columns lie past every key)."""
+    rng = rng_for(seed)
+    B, S1 = case.q.shape[0], case.q.shape[1]
+    S2 = case.block_size * case.block_table.shape[1] if case.paged else case.k.shape[1]
+    S2p = -(-S2 // 4) * 4
+    shape = (B if per_batch else 1, case.num_heads, 1 if one_row else S1, S2p)
+    x = (rng.standard_normal(shape) * std).astype(np.float32)
+    bits = f32_to_bf16_bits(x) if case.dtype == "bf16" else x
+    return dataclasses.replace(case, name=case.name + "_pse", pse_bias=bits)
 
 
 def as_bnnbsd(case: DenseCase) -> DenseCase:

@@ -106,8 +106,9 @@ typedef struct {
   int32_t sparse_mode;
   int64_t pre_tokens;           /* default 2147483647 */
   int64_t next_tokens;          /* default 2147483647; -next_tokens <= pre_tokens */
-  /* pse_type 0: no positional bias (pse_shift must be NULL; an explicit bias
-   * tensor is unsupported).  pse_type 2: ALiBi, pse_shift is fp32 [Q_N]
+  /* pse_type 0: no positional bias, or, with a pse_shift tensor, that
+   * tensor added element-wise to the scaled scores (V5 PSE group; see
+   * pse_shift below).  pse_type 2: ALiBi, pse_shift is fp32 [Q_N]
    * slopes and bias(h,i,j) = slope[h] * ((kv_start_idx + j) - (q_start_idx + i)),
    * which requires S1 == S2 and equal per-batch lengths (V5 PSE group).
    * pse_type 3 is unsupported (no formula on the pages); 1 is training-only. */
@@ -140,7 +141,14 @@ typedef struct {
  *                   KV_N*D]) or BnNBsD [n_blocks, KV_N, block_size, D]; same
  *                   dtype as query.
  *                   key and value may be the same tensor.
- *   pse_shift       NULL, or fp32 [Q_N] slopes when pse_type == 2.
+ *   pse_shift       NULL, or fp32 [Q_N] slopes when pse_type == 2, or, when
+ *                   pse_type == 0, a bias [B or 1, Q_N, P_S1, >= KV_S] in
+ *                   the query's dtype with P_S1 >= Q_S or P_S1 == 1 (one row
+ *                   for every query row); score(b,h,i,j) = scale * q.k +
+ *                   pse[b or 0][h][i or 0][j], indexed by the position inside
+ *                   the actual lengths.  Last dim contiguous; batch, head and
+ *                   row strides, the last extent and the base (in elements)
+ *                   multiples of 4, else FIA_ERR_UNSUPPORTED; not with TND.
  *   atten_mask      modes 0 / 1: NULL or int8 / uint8 / bool [B or 1, >= Q_S,
  *                   >= KV_S], [B or 1, 1, >= Q_S, >= KV_S] or [>= Q_S, >= KV_S]
  *                   (KV_S = block_table cols * block_size when paged), rows

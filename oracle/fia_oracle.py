@@ -12,6 +12,10 @@ What it computes, and where each step is stated on the pages:
 * Attention(Q,K,V) = softmax(Q K^T * scale + bias) V, row-wise softmax
   (aclnnFusedInferAttentionScoreV5 / V2, "Formula"); the ALiBi bias is added
   after scaling (aclnnFusedInferAttentionScoreV4, "Formula", FullMask term).
+* pseType 0 bias tensor (V5 PSE parameter group): shape [B or 1, Q_N,
+  P_S1, >= KV_S] with P_S1 >= Q_S or P_S1 = 1, in the query's dtype.
+  Reading (no formula places it): like the full-mask ALiBi term it is added
+  to the scaled scores, element [b or 0][h][i or 0][j] to score (i, j).
 * GQA: Q_N a multiple of KV_N (V2, numKeyValueHeads restrictions).  Reading:
   query head h uses KV head floor(h / (Q_N / KV_N)).
 * Per-batch actual lengths, broadcast rule (length-1 array -> every batch;
@@ -178,7 +182,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
         next_tokens: int = 2147483647, alibi_slopes=None, q_start_idx: int = 0,
         kv_start_idx: int = 0, actual_seq_lengths=None, actual_seq_lengths_kv=None,
         block_table=None, block_size: int = 0, k_pool=None, v_pool=None,
-        kv_layout: str = "PA_ND", atten_mask=None,
+        kv_layout: str = "PA_ND", atten_mask=None, pse_shift=None,
         batches: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
         rows: Optional[Sequence[int]] = None, row_chunk: int = 1024):
     """Fused inference attention, float64.
@@ -186,7 +190,8 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
     q: BSND [B, S1, Q_N, D] or TND [T, Q_N, D] (raw bits or floats per
     ``dtype``); k, v: [B, S2, KV_N, D] / [T_kv, KV_N, D]; or k_pool, v_pool
     PA_ND [n_blk, bs, KV_N, D] (``kv_layout`` "BnNBsD": [n_blk, KV_N, bs, D])
-    with ``block_table`` [B, >= max pages].
+    with ``block_table`` [B, >= max pages].  ``pse_shift``: pseType 0 bias
+    [B or 1, Q_N, Q_S or 1, >= KV_S], encoded like q (``dtype``).
 
     Returns (out, lse) with out in the query layout (float64) and lse
     [B, Q_N, S1] (BSND) or [T, Q_N] (TND).  ``batches``/``heads``/``rows``
@@ -247,6 +252,9 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
                         jpos = (kv_start_idx + np.arange(Lk))[None, :]
                         ipos = (q_start_idx + live)[:, None]
                         s = s + slopes[h] * (jpos - ipos)
+                    if pse_shift is not None:
+                        pb = to_f64(np.asarray(pse_shift)[b if pse_shift.shape[0] > 1 else 0, h], dtype)
+                        s = s + (pb[np.zeros_like(live)] if pb.shape[0] == 1 else pb[live])[:, :Lk]
                     if atten_mask is not None and sparse_mode in (0, 1):
                         m = np.asarray(atten_mask)
                         m2 = m.reshape(m.shape[-2], m.shape[-1]) if m.ndim == 2 else \
@@ -280,7 +288,8 @@ def fia_case(case, **kw):
                block_table=case.block_table, block_size=case.block_size,
                k_pool=case.k_pool, v_pool=case.v_pool,
                kv_layout=getattr(case, "kv_layout", "PA_ND"),
-               atten_mask=getattr(case, "atten_mask", None), **kw)
+               atten_mask=getattr(case, "atten_mask", None),
+               pse_shift=getattr(case, "pse_bias", None), **kw)
 
 
 # ---------------------------------------------------------------------------

@@ -181,7 +181,7 @@ def test_alibi_rules():
     st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2), q, k, v, o, pse=T((4,), fia.DT_BF16))
     assert st == BAD
     st, _, _, msg = plan(P(num_kv_heads=2, pse_type=0), q, k, v, o, pse=T((2, 4, 64, 64)))
-    assert st == UNS
+    assert st == 0, msg   # pse_type 0 takes a bias tensor
 
 
 def test_mask_tensor_rules():
@@ -285,6 +285,50 @@ def test_explicit_mask_rules():
     st, kind, _, msg = plan(P(num_kv_heads=2, sparse_mode=0), q1, k1, v1, o1,
                             mask=T((2, 1, 300), fia.DT_INT8))
     assert st == 0 and kind == "decode", msg
+
+
+def test_pse_bias_rules():
+    """pseType 0 bias tensor: 4 dims [B or 1, Q_N, >= Q_S or 1, >= KV_S] in the
+    query's dtype (V5 PSE parameter group)."""
+    q, k, v, o = dense(B=2, S1=64, S2=64)
+    for shape in [(2, 4, 64, 64), (1, 4, 64, 64), (2, 4, 1, 64), (1, 4, 80, 128)]:
+        for mode in (0, 2, 3):
+            st, kind, _, msg = plan(P(num_kv_heads=2, sparse_mode=mode), q, k, v, o, pse=T(shape))
+            assert st == 0 and kind == "prefill", (shape, mode, msg)
+    bad = [((3, 4, 64, 64), fia.DT_BF16), ((2, 2, 64, 64), fia.DT_BF16), ((2, 4, 32, 64), fia.DT_BF16),
+           ((2, 4, 64, 60), fia.DT_BF16), ((2, 4, 64, 64), fia.DT_FP32), ((2, 4, 64), fia.DT_BF16),
+           ((4,), fia.DT_BF16)]
+    for shape, dt in bad:
+        st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o, pse=T(shape, dt))
+        assert st == BAD, (shape, dt, msg)
+    # bias with an explicit mask
+    st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=1), q, k, v, o, pse=T((2, 4, 64, 64)),
+                         mask=T((2, 64, 64), fia.DT_UINT8))
+    assert st == 0, msg
+    # rows not aligned to 4 elements
+    q2, k2, v2, o2 = dense(B=2, S1=8, S2=62)
+    st, _, _, msg = plan(P(num_kv_heads=2), q2, k2, v2, o2, pse=T((2, 4, 8, 62)))
+    assert st == UNS and "aligned" in msg
+    st, _, _, msg = plan(P(num_kv_heads=2), q2, k2, v2, o2, pse=T((2, 4, 8, 64)))
+    assert st == 0, msg
+    # fp32 query takes an fp32 bias; decode takes one row
+    q3, k3, v3, o3 = dense(D=64, dt=fia.DT_FP32)
+    st, kind, _, msg = plan(P(num_kv_heads=2), q3, k3, v3, o3, pse=T((2, 4, 64, 64), fia.DT_FP32))
+    assert st == 0 and kind == "fp32", msg
+    q1, k1, v1, o1 = dense(S1=1, S2=300)
+    st, kind, _, msg = plan(P(num_kv_heads=2), q1, k1, v1, o1, pse=T((2, 4, 1, 300)))
+    assert st == 0 and kind == "decode", msg
+    # paged: the last dim covers the block table's pages
+    pool = T((20, 128, 2, 128))
+    bt = T((2, 4), fia.DT_INT32)
+    st, _, _, msg = plan(P(num_kv_heads=2, block_size=128, actual_seq_lengths_kv=[300, 400]),
+                         q1, pool, pool, o1, bt=bt,
+                         pse=T((2, 4, 1, 512)))
+    assert st == 0, msg
+    st, _, _, msg = plan(P(num_kv_heads=2, block_size=128, actual_seq_lengths_kv=[300, 400]),
+                         q1, pool, pool, o1, bt=bt,
+                         pse=T((2, 4, 1, 508)))
+    assert st == BAD, msg
 
 
 def test_tnd_rules():

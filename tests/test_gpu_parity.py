@@ -206,6 +206,51 @@ def test_fp32_explicit_mask():
     plan, out, lse = dense_parity(W.with_random_mask(case, 741, dead_rows=(2,)), "fp32")
 
 
+PSE_PREFILL_CASES = [
+    # (B, S1, S2, Qn, KVn, D, mode, per_batch, one_row, q_lens, kv_lens, with_mask)
+    (2, 200, 300, 8, 2, 128, 3, True, False, [200, 150], [300, 290], False),
+    (1, 130, 130, 4, 4, 128, 0, False, True, None, None, False),
+    (2, 70, 97, 8, 4, 64, 0, True, False, [70, 33], [97, 60], True),
+    (1, 257, 257, 8, 1, 128, 2, False, False, None, None, False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(PSE_PREFILL_CASES)))
+def test_prefill_pse_bias(i):
+    """pseType 0 bias tensor [B or 1, Q_N, Q_S or 1, KV_S'] in bf16."""
+    B, S1, S2, Qn, KVn, D, mode, pb, one, ql, kl, wm = PSE_PREFILL_CASES[i]
+    case = W.dense_case(f"pp{i}", 750 + i, B=B, S1=S1, S2=S2, Q_N=Qn, KV_N=KVn, D=D, sparse_mode=mode,
+                        q_lens=ql, kv_lens=kl, lse=True, poison_pad=True)
+    if wm:
+        case = W.with_random_mask(case, 760 + i, dead_rows=(3,), mode=mode)
+    dense_parity(W.with_random_bias(case, 770 + i, per_batch=pb, one_row=one), "prefill")
+
+
+@pytest.mark.parametrize("bs", [64, 16])
+def test_prefill_pse_bias_paged(bs):
+    case = W.paged_decode_case("ppp", 780, B=2, Q_N=8, KV_N=2, D=128, kv_lens=[300, 129],
+                               block_size=bs, S1=40, sparse_mode=3, lse=True, poison_tail=True,
+                               extra_blocks=2)
+    case.actual_seq_lengths = [40, 40]
+    dense_parity(W.with_random_bias(case, 781), "prefill")
+
+
+def test_decode_pse_bias():
+    case = W.paged_decode_case("pdp", 790, B=3, Q_N=32, KV_N=8, D=128, kv_lens=[1, 700, 1500],
+                               block_size=128, lse=True, poison_tail=True, extra_blocks=2)
+    dense_parity(W.with_random_bias(case, 791, one_row=True), "decode")
+    case = W.dense_case("pdd", 792, B=2, S1=1, S2=900, Q_N=8, KV_N=2, D=64, kv_lens=[900, 40],
+                        lse=True, poison_pad=True)
+    case = W.with_random_mask(case, 793, dims=2, per_batch=False, mode=1)
+    dense_parity(W.with_random_bias(case, 794, per_batch=False, std=3.0), "decode")
+
+
+def test_fp32_pse_bias():
+    case = W.dense_case("pf", 795, B=2, S1=37, S2=50, Q_N=4, KV_N=2, D=64, dtype="fp32",
+                        sparse_mode=3, lse=True, poison_pad=True)
+    dense_parity(W.with_random_bias(case, 796), "fp32")
+
+
 BNNBSD_DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size)
     (3, 32, 8, 128, [1, 511, 1300], 128),

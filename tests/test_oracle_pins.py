@@ -442,6 +442,80 @@ def test_explicit_mask_brute_force():
                 assert abs(lse[b, h, i] - (mx + math.log(den))) < 1e-12
 
 
+@pytest.mark.parametrize("mode,per_batch", [(0, True), (3, False), (2, True)])
+def test_pse_bias_matches_sdpa_float_mask(mode, per_batch):
+    """pseType 0 bias tensor: torch SDPA with a float attn_mask adds it to the
+    scaled scores; with GQA, ragged-free BSND, S1 != S2, per-batch or shared."""
+    c = W.dense_case("pb", 81, B=2, S1=5, S2=7, Q_N=4, KV_N=2, D=6, dtype="fp32",
+                     scale=0.37, sparse_mode=mode, lse=True)
+    c = W.with_random_bias(c, 82, per_batch=per_batch, std=2.0)
+    out, _ = O.fia_case(c)
+    i = np.arange(5)[:, None]
+    j = np.arange(7)[None, :]
+    vis = {0: np.ones((5, 7), bool), 2: j <= i, 3: j <= i + 2}[mode]
+    for b in range(2):
+        bias = c.pse_bias[b if per_batch else 0][:, :, :7].astype(np.float64)
+        m = np.where(vis[None], bias, -np.inf)
+        want = sdpa(c.q[b].astype(np.float64), c.k[b].astype(np.float64), c.v[b].astype(np.float64),
+                    0.37, mask=m, gqa=True)
+        np.testing.assert_allclose(out[b], want, rtol=1e-11, atol=1e-12)
+
+
+def test_pse_bias_one_row_broadcasts_over_queries():
+    """P_S1 = 1: the single bias row applies to every query row."""
+    c = W.dense_case("p1", 83, B=1, S1=4, S2=9, Q_N=2, KV_N=1, D=5, dtype="fp32", lse=True)
+    c1 = W.with_random_bias(c, 84, one_row=True)
+    full = np.repeat(c1.pse_bias, 4, axis=2)
+    o1, l1 = O.fia_case(c1)
+    o2, l2 = O.fia_case(dataclasses.replace(c1, pse_bias=full))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_pse_full_alibi_matrix_equals_alibi():
+    """The ALiBi full-mask form carried as a pseType 0 tensor: slope_h *
+    ((kv_start + j) - (q_start + i)) as a bias equals pseType 2 with the
+    slopes (V4 alibi full-mask constraints)."""
+    c = W.dense_case("pa", 85, B=2, S1=6, S2=6, Q_N=4, KV_N=2, D=8, dtype="fp32",
+                     sparse_mode=3, alibi=True, q_start_idx=3, kv_start_idx=5, lse=True)
+    sl = c.alibi_slopes.astype(np.float64)
+    rel = (5 + np.arange(8))[None, :] - (3 + np.arange(6))[:, None]
+    bias = np.broadcast_to((sl[:, None, None] * rel[None])[None], (2, 4, 6, 8)).copy()
+    o_al, l_al = O.fia_case(c)
+    o_ps, l_ps = O.fia(c.q, c.k, c.v, dtype="fp32", layout="BSND", num_heads=4, num_kv_heads=2,
+                       scale=c.scale, sparse_mode=3, pse_shift=bias.astype(np.float32))
+    tol = 4 * np.abs(bias).max() * 2.0 ** -24   # float32 storage of the bias
+    np.testing.assert_allclose(o_ps, o_al, rtol=0, atol=tol * 4)
+    np.testing.assert_allclose(l_ps, l_al, rtol=0, atol=tol * 4)
+
+
+def test_pse_bias_and_mask_brute_force():
+    """Bias plus an explicit mask against pure-Python loops (bias added after
+    scaling, indexed [b][h][i][j])."""
+    c = W.dense_case("pm", 86, B=2, S1=3, S2=5, Q_N=2, KV_N=1, D=4, dtype="fp32", scale=0.6, lse=True)
+    c = W.with_random_bias(c, 87)
+    rng = np.random.default_rng(8)
+    m = (rng.random((2, 3, 8)) < 0.3).astype(np.uint8)
+    out, lse = O.fia_case(dataclasses.replace(c, sparse_mode=1, atten_mask=m))
+    pb = c.pse_bias
+    for b in range(2):
+        for h in range(2):
+            for i in range(3):
+                keep = [jj for jj in range(5) if m[b, i, jj] == 0]
+                if not keep:
+                    assert np.all(out[b, i, h] == 0) and math.isinf(lse[b, h, i])
+                    continue
+                s = [0.6 * sum(float(c.q[b, i, h, d]) * float(c.k[b, jj, 0, d]) for d in range(4))
+                     + float(pb[b, h, i, jj]) for jj in keep]
+                mx = max(s)
+                w = [math.exp(x - mx) for x in s]
+                den = sum(w)
+                for d in range(4):
+                    want = sum(wk * float(c.v[b, jj, 0, d]) for wk, jj in zip(w, keep)) / den
+                    assert abs(out[b, i, h, d] - want) < 1e-12
+                assert abs(lse[b, h, i] - (mx + math.log(den))) < 1e-12
+
+
 def test_split_keys_merge_by_lse_reproduces_full():
     """Partial results over disjoint key ranges combine through their LSE
     (V2 softmaxLse restrictions: the ring-attention composition)."""
