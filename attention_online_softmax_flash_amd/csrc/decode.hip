@@ -253,9 +253,19 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   }
   // A chunk can hold no visible key under an explicit mask: output 0 and a
   // log2-sum-exp of -inf (the row's LSE +inf when it is the only chunk).
-  const bool any = L > 0.f;
-  const float inv = any ? 1.f / L : 0.f;
-  const float lse2 = any ? M + fast_log2(L) : kNegInf;
+  bool any = L > 0.f;
+  float inv = any ? 1.f / L : 0.f;
+  float lse2 = any ? M + fast_log2(L) : kNegInf;
+  if (nchunk == 1 && a.sink != nullptr) {
+    // The sink: one more softmax term with a zero value vector.
+    const float z = bf16_to_f32(a.sink[hout]) * kLog2e;
+    const float m_new = fmaxf(M, z);
+    const float w = any ? fast_exp2(M - m_new) : 0.f;
+    const float Ls = L * w + fast_exp2(z - m_new);
+    inv = w / Ls;
+    lse2 = m_new + fast_log2(Ls);
+    any = true;
+  }
   if (nchunk == 1) {
     uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
                    (int64_t)hout * a.o_sh + d0;
@@ -295,10 +305,12 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
                  (int64_t)h * a.o_sh + lane * PL;
   float* lp = a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)q_off * a.lse_ss;
+  // Learnable sink (log2 units): one more term with a zero value vector.
+  const float z = a.sink != nullptr ? bf16_to_f32(a.sink[h]) * kLog2e : kNegInf;
   if (nchunk == 0) {
 #pragma unroll
     for (int u = 0; u < PL; ++u) op[u] = 0;
-    if (a.write_lse && lane == 0) *lp = kPosInf;
+    if (a.write_lse && lane == 0) *lp = a.sink != nullptr ? z * kLn2 : kPosInf;
     return;
   }
   const int chunk0 = bm[BF_CHUNK0];
@@ -310,12 +322,13 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   }
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  if (M == kNegInf) {   // every chunk empty (explicit mask): 0 and LSE +inf
+  if (M == kNegInf) {   // every chunk empty (explicit mask): 0 and LSE +inf, or the sink's
 #pragma unroll
     for (int u = 0; u < PL; ++u) op[u] = 0;
-    if (a.write_lse && lane == 0) *lp = kPosInf;
+    if (a.write_lse && lane == 0) *lp = a.sink != nullptr ? z * kLn2 : kPosInf;
     return;
   }
+  M = fmaxf(M, z);
   float L = 0.f;
   float acc[PL];
 #pragma unroll
@@ -351,6 +364,7 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
       for (int u = 0; u < PL; ++u) acc[u] += wk * pp[u];
     }
   }
+  if (a.sink != nullptr) L += fast_exp2(z - M);
   const float inv = 1.f / L;
   if constexpr (PL == 2) {
     *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);

@@ -534,6 +534,27 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
                                        "multiple of 4)");
     }
   }
+  // LearnableSink group (V5): [Q_N] in the query's dtype (bf16 / fp16 only).
+  const fia_tensor* sink = p->learnable_sink;
+  if (sink != nullptr) {
+    if ((st = check_tensor(sink, "learnable_sink")) != FIA_SUCCESS) return st;
+    if (sink->dtype != FIA_DT_BF16 && sink->dtype != FIA_DT_FP16) {
+      return fail(FIA_ERR_PARAM_INVALID, "learnable_sink dtype must be float16 or bfloat16");
+    }
+    if (sink->dtype != query->dtype) {
+      return fail(FIA_ERR_PARAM_INVALID, "learnable_sink must have the query's dtype");
+    }
+    if (sink->ndim != 1 || sink->shape[0] != Qn) {
+      return fail(FIA_ERR_PARAM_INVALID, "learnable_sink shape must be (Q_N)");
+    }
+    if (sink->stride[0] != 1) return fail(FIA_ERR_PARAM_INVALID, "learnable_sink must be contiguous");
+    if (p->inner_precise != 0) {
+      return fail(FIA_ERR_PARAM_INVALID, "learnable_sink requires inner_precise 0");
+    }
+    if (pse == 2 || pse_tensor) {
+      return fail(FIA_ERR_PARAM_INVALID, "learnable_sink does not combine with pse or ALiBi");
+    }
+  }
   if (pse == 2) {
     if (pse_shift == nullptr) return fail(FIA_ERR_PARAM_INVALID, "pse_type 2 requires pse_shift");
     if ((st = check_tensor(pse_shift, "pse_shift")) != FIA_SUCCESS) return st;
@@ -660,6 +681,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   a.slopes = pse == 2 ? static_cast<const float*>(pse_shift->data) : nullptr;
   a.alibi_delta = (int32_t)(p->kv_start_idx - p->q_start_idx);
   a.pse = pse_tensor ? pse_shift->data : nullptr;
+  a.sink = sink != nullptr ? static_cast<const uint16_t*>(sink->data) : nullptr;
   a.pse_sb = pse_sb;
   a.pse_sh = pse_sh;
   a.pse_ss = pse_ss;

@@ -45,6 +45,11 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// bf16 bit pattern -> float (exact).
+__device__ __forceinline__ float bf16_to_f32(uint16_t u) {
+  return __builtin_bit_cast(float, (uint32_t)u << 16);
+}
+
 // Two floats -> packed bf16 pair (round to nearest even).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   f32x2 v = {lo, hi};

@@ -76,6 +76,9 @@ struct AttnArgs {
   const void* pse;
   int64_t pse_sb, pse_sh, pse_ss;
   int32_t pse_rows, pse_cols;
+  // Learnable sink: bf16 logit per query head or nullptr; one more softmax
+  // term with a zero value vector, not scaled.
+  const uint16_t* sink;
   int32_t write_lse;
   // decode split-KV
   int32_t chunk;                    // tokens per chunk (multiple of 128)

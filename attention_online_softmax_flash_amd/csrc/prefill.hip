@@ -488,9 +488,19 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   }
 
   // Epilogue: normalise and write this lane's row.
-  const float l_tot = pair32_sum(l_run);
-  const bool has = row_live && m_run != kNegInf && l_tot > 0.f;
-  const float inv = has ? 1.f / l_tot : 0.f;
+  float l_tot = pair32_sum(l_run);
+  bool has = row_live && m_run != kNegInf && l_tot > 0.f;
+  float o_scale = 1.f;
+  if (a.sink != nullptr && row_live) {
+    // The sink: one more softmax term with a zero value vector.
+    const float z = bf16_to_f32(a.sink[h]) * kLog2e;
+    const float m_new = fmaxf(m_run, z);
+    o_scale = (m_run == kNegInf) ? 0.f : fast_exp2(m_run - m_new);
+    l_tot = l_tot * o_scale + fast_exp2(z - m_new);
+    m_run = m_new;
+    has = true;
+  }
+  const float inv = has ? o_scale / l_tot : 0.f;
   if (i < write_rows) {
     uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)(q_off + i) * a.o_ss +
                    (int64_t)h * a.o_sh;

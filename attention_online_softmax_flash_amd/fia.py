@@ -73,6 +73,7 @@ class FiaParams(ctypes.Structure):
         ("actual_seq_lengths_kv", ctypes.POINTER(ctypes.c_int64)),
         ("actual_seq_lengths_kv_len", ctypes.c_int64),
         ("kv_layout", ctypes.c_char_p),
+        ("learnable_sink", ctypes.POINTER(FiaTensor)),
     ]
 
 
@@ -211,7 +212,7 @@ class AttentionPlan(_Plan):
                  kv_start_idx=0, atten_mask=None, block_table=None, block_size=0,
                  inner_precise=0, softmax_lse_flag=False, actual_seq_lengths=None,
                  actual_seq_lengths_kv=None, attention_out=None, softmax_lse=None,
-                 kv_layout="PA_ND"):
+                 kv_layout="PA_ND", learnable_sink=None):
         L = lib()
         if attention_out is None:
             attention_out = torch.empty_like(query)
@@ -243,6 +244,10 @@ class AttentionPlan(_Plan):
         p.inner_precise = inner_precise
         p.softmax_lse_flag = 1 if softmax_lse_flag else 0
         p.kv_layout = kv_layout.encode()
+        self.learnable_sink = learnable_sink
+        self._sink_desc = describe(learnable_sink) if learnable_sink is not None else None
+        if self._sink_desc is not None:
+            p.learnable_sink = ctypes.pointer(self._sink_desc)
         if self._lens[0] is not None:
             p.actual_seq_lengths = ctypes.cast(self._lens[0], ctypes.POINTER(ctypes.c_int64))
             p.actual_seq_lengths_len = self._lens[1]

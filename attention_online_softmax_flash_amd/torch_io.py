@@ -51,7 +51,9 @@ def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia
               block_table=bt, block_size=case.block_size if bt is not None else 0,
               softmax_lse_flag=case.lse, actual_seq_lengths=case.actual_seq_lengths,
               actual_seq_lengths_kv=case.actual_seq_lengths_kv, kv_layout=case.kv_layout,
-              atten_mask=mask_tensor(case, device))
+              atten_mask=mask_tensor(case, device),
+              learnable_sink=(None if case.learnable_sink is None
+                              else to_device(case.learnable_sink, "bf16", device)))
     kw.update(overrides)
     return fia.AttentionPlan(q, k, v, **kw)
 

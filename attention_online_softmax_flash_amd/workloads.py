@@ -93,6 +93,7 @@ class DenseCase:
     kv_layout: str = "PA_ND"
     atten_mask: Optional[np.ndarray] = None     # uint8 / bool, modes 0 / 1; != 0 masks out
     pse_bias: Optional[np.ndarray] = None       # [B or 1, Q_N, Q_S or 1, KV_S'] (pseType 0), q's dtype
+    learnable_sink: Optional[np.ndarray] = None  # bf16 bits [Q_N]
     lse: bool = False
     seed: int = 0
 
@@ -142,6 +143,14 @@ def with_random_bias(case: DenseCase, seed: int, *, per_batch=True, one_row=Fals
     x = (rng.standard_normal(shape) * std).astype(np.float32)
     bits = f32_to_bf16_bits(x) if case.dtype == "bf16" else x
     return dataclasses.replace(case, name=case.name + "_pse", pse_bias=bits)
+
+
+def with_random_sink(case: DenseCase, seed: int, *, mean=0.0, std=2.0) -> DenseCase:
+    """The case with a learnable sink: one bf16 logit per query head, normal
+    values (``mean``, ``std``)."""
+    rng = rng_for(seed)
+    x = (mean + std * rng.standard_normal(case.num_heads)).astype(np.float32)
+    return dataclasses.replace(case, name=case.name + "_sink", learnable_sink=f32_to_bf16_bits(x))
 
 
 def as_bnnbsd(case: DenseCase) -> DenseCase:

@@ -131,6 +131,15 @@ typedef struct {
    * KV_N*D].  "BnNBsD": [n_blocks, KV_N, block_size, D], each KV head's rows
    * of a block contiguous. */
   const char* kv_layout;
+  /* NULL, or the learnable sink (V5 LearnableSink group): one logit per
+   * query head, bf16 [Q_N] like the query, contiguous.  It joins every
+   * row's softmax as one more term with a zero value vector and is not
+   * multiplied by the scale: out = sum_j e^(s_j) v_j / (sum_j e^(s_j) +
+   * e^(sink[h])), and the LSE includes it (a live row with no visible key
+   * then gives 0 and LSE sink[h]; an empty key / value tensor still gives 0
+   * and +inf).  Requires inner_precise 0 and no pse (pse_type 0 without a
+   * pse_shift tensor).  Device memory, read during phase 2. */
+  const fia_tensor* learnable_sink;
 } fia_params;
 
 /* Phase 1 of the dense / paged operator.

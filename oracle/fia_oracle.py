@@ -16,6 +16,10 @@ What it computes, and where each step is stated on the pages:
   P_S1, >= KV_S] with P_S1 >= Q_S or P_S1 = 1, in the query's dtype.
   Reading (no formula places it): like the full-mask ALiBi term it is added
   to the scaled scores, element [b or 0][h][i or 0][j] to score (i, j).
+* Learnable sink (V5 LearnableSink group: [Q_N], the query's dtype).  Same
+  reading as the shared-KV sink: one extra logit per head with a zero value
+  vector, not multiplied by the scale; the LSE includes it, so a live row
+  with no visible key (or a batch with Lk = 0) gives out 0 and LSE = sink.
 * GQA: Q_N a multiple of KV_N (V2, numKeyValueHeads restrictions).  Reading:
   query head h uses KV head floor(h / (Q_N / KV_N)).
 * Per-batch actual lengths, broadcast rule (length-1 array -> every batch;
@@ -182,7 +186,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
         next_tokens: int = 2147483647, alibi_slopes=None, q_start_idx: int = 0,
         kv_start_idx: int = 0, actual_seq_lengths=None, actual_seq_lengths_kv=None,
         block_table=None, block_size: int = 0, k_pool=None, v_pool=None,
-        kv_layout: str = "PA_ND", atten_mask=None, pse_shift=None,
+        kv_layout: str = "PA_ND", atten_mask=None, pse_shift=None, learnable_sink=None,
         batches: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
         rows: Optional[Sequence[int]] = None, row_chunk: int = 1024):
     """Fused inference attention, float64.
@@ -192,6 +196,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
     PA_ND [n_blk, bs, KV_N, D] (``kv_layout`` "BnNBsD": [n_blk, KV_N, bs, D])
     with ``block_table`` [B, >= max pages].  ``pse_shift``: pseType 0 bias
     [B or 1, Q_N, Q_S or 1, >= KV_S], encoded like q (``dtype``).
+    ``learnable_sink``: [Q_N] logits, encoded like q.
 
     Returns (out, lse) with out in the query layout (float64) and lse
     [B, Q_N, S1] (BSND) or [T, Q_N] (TND).  ``batches``/``heads``/``rows``
@@ -222,6 +227,9 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
     D = q.shape[-1]
     Dv = (v_pool if paged else v).shape[-1]
     slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, np.float64)
+    sink = None if learnable_sink is None else to_f64(learnable_sink, dtype)
+    # Empty key / value tensors are the empty-tensor case: 0 and +inf everywhere.
+    kv_tensor_empty = np.asarray(k_pool if paged else k).size == 0
 
     for b in (range(B) if batches is None else batches):
         Lq, Lk = q_len[b], kv_len[b]
@@ -246,7 +254,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
                 o_blk = np.zeros((idx.size, Dv))
                 l_blk = np.full(idx.size, POS_INF)
                 live = idx[idx < Lq]          # padded rows i >= Lq stay 0 / +inf
-                if live.size and Lk > 0:
+                if live.size and (Lk > 0 or (sink is not None and not kv_tensor_empty)):
                     s = scale * (qb[live, h, :] @ K.T)
                     if slopes is not None:
                         jpos = (kv_start_idx + np.arange(Lk))[None, :]
@@ -262,7 +270,7 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
                         vis = (m2[:Lq, :Lk] == 0)[live]
                     else:
                         vis = visible(sparse_mode, Lq, Lk, pre_tokens, next_tokens)[live]
-                    o_live, l_live = softmax_rows(s, vis, V)
+                    o_live, l_live = softmax_rows(s, vis, V, None if sink is None else float(sink[h]))
                     pos = np.searchsorted(idx, live)
                     o_blk[pos] = o_live
                     l_blk[pos] = l_live
@@ -289,7 +297,8 @@ def fia_case(case, **kw):
                k_pool=case.k_pool, v_pool=case.v_pool,
                kv_layout=getattr(case, "kv_layout", "PA_ND"),
                atten_mask=getattr(case, "atten_mask", None),
-               pse_shift=getattr(case, "pse_bias", None), **kw)
+               pse_shift=getattr(case, "pse_bias", None),
+               learnable_sink=getattr(case, "learnable_sink", None), **kw)
 
 
 # ---------------------------------------------------------------------------

@@ -71,6 +71,10 @@ def P(**kw):
             keep.append(arr)
             setattr(p, name, ctypes.cast(arr, ctypes.POINTER(ctypes.c_int64)))
             setattr(p, name + "_len", len(vals))
+    sink = kw.pop("learnable_sink", None)
+    if sink is not None:
+        keep.append(sink)
+        p.learnable_sink = ctypes.pointer(sink)
     assert not kw, kw
     p._keep = keep
     return p
@@ -328,6 +332,33 @@ def test_pse_bias_rules():
     st, _, _, msg = plan(P(num_kv_heads=2, block_size=128, actual_seq_lengths_kv=[300, 400]),
                          q1, pool, pool, o1, bt=bt,
                          pse=T((2, 4, 1, 508)))
+    assert st == BAD, msg
+
+
+def test_learnable_sink_rules():
+    """V5 LearnableSink group: [Q_N] in the query's dtype (float16 / bfloat16),
+    innerPrecise 0, no pse / ALiBi."""
+    q, k, v, o = dense(B=2, S1=64, S2=64)
+    st, kind, _, msg = plan(P(num_kv_heads=2, sparse_mode=3, learnable_sink=T((4,))), q, k, v, o)
+    assert st == 0 and kind == "prefill", msg
+    q1, k1, v1, o1 = dense(S1=1, S2=300)
+    st, kind, _, msg = plan(P(num_kv_heads=2, learnable_sink=T((4,))), q1, k1, v1, o1)
+    assert st == 0 and kind == "decode", msg
+    bad = [dict(learnable_sink=T((3,))), dict(learnable_sink=T((1, 4))),
+           dict(learnable_sink=T((4,), fia.DT_FP32)), dict(learnable_sink=T((4,), fia.DT_FP16)),
+           dict(learnable_sink=T((4,)), inner_precise=1)]
+    for kw in bad:
+        st, _, _, msg = plan(P(num_kv_heads=2, **kw), q, k, v, o)
+        assert st == BAD, (kw, msg)
+    st, _, _, msg = plan(P(num_kv_heads=2, learnable_sink=T((4,), strides=[2])), q, k, v, o)
+    assert st == UNS and "contiguous" in msg
+    st, _, _, msg = plan(P(num_kv_heads=2, pse_type=2, learnable_sink=T((4,))), q, k, v, o,
+                         pse=T((4,), fia.DT_FP32))
+    assert st == BAD and "pse" in msg
+    st, _, _, msg = plan(P(num_kv_heads=2, learnable_sink=T((4,))), q, k, v, o, pse=T((2, 4, 64, 64)))
+    assert st == BAD and "pse" in msg
+    q3, k3, v3, o3 = dense(D=64, dt=fia.DT_FP32)
+    st, _, _, msg = plan(P(num_kv_heads=2, learnable_sink=T((4,), fia.DT_FP32)), q3, k3, v3, o3)
     assert st == BAD, msg
 
 

@@ -251,6 +251,35 @@ def test_fp32_pse_bias():
     dense_parity(W.with_random_bias(case, 796), "fp32")
 
 
+SINK_PREFILL_CASES = [
+    # (B, S1, S2, Qn, KVn, D, mode, q_lens, kv_lens, with_mask, sink_mean)
+    (2, 200, 300, 8, 2, 128, 3, [200, 150], [300, 290], False, 0.0),
+    (2, 70, 97, 8, 4, 64, 0, [70, 33], [97, 60], True, 3.0),
+    (3, 130, 130, 4, 4, 128, 2, None, [130, 0, 77], False, -1.0),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SINK_PREFILL_CASES)))
+def test_prefill_learnable_sink(i):
+    B, S1, S2, Qn, KVn, D, mode, ql, kl, wm, mean = SINK_PREFILL_CASES[i]
+    case = W.dense_case(f"sp{i}", 800 + i, B=B, S1=S1, S2=S2, Q_N=Qn, KV_N=KVn, D=D, sparse_mode=mode,
+                        q_lens=ql, kv_lens=kl, lse=True, poison_pad=True)
+    if wm:
+        case = W.with_random_mask(case, 810 + i, dead_rows=(3,), mode=mode)
+    dense_parity(W.with_random_sink(case, 820 + i, mean=mean), "prefill")
+
+
+def test_decode_learnable_sink():
+    # single-chunk rows, multi-chunk merges and a batch with no key
+    case = W.paged_decode_case("sdp", 830, B=4, Q_N=32, KV_N=8, D=128, kv_lens=[1, 700, 5000, 0],
+                               block_size=128, lse=True, poison_tail=True, extra_blocks=2)
+    dense_parity(W.with_random_sink(case, 831), "decode")
+    case = W.dense_case("sdd", 832, B=2, S1=1, S2=900, Q_N=8, KV_N=2, D=64, kv_lens=[900, 40],
+                        lse=True, poison_pad=True)
+    case = W.with_random_mask(case, 833, p_masked=0.995, dims=2, per_batch=False)
+    dense_parity(W.with_random_sink(case, 834, mean=2.0), "decode")
+
+
 BNNBSD_DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size)
     (3, 32, 8, 128, [1, 511, 1300], 128),

@@ -516,6 +516,68 @@ def test_pse_bias_and_mask_brute_force():
                 assert abs(lse[b, h, i] - (mx + math.log(den))) < 1e-12
 
 
+@pytest.mark.parametrize("mode", [0, 3])
+def test_learnable_sink_matches_sdpa_with_zero_key(mode):
+    """The sink as torch SDPA over one appended key with a zero key vector
+    (score 0), a zero value vector and float-mask bias sink[h] on that
+    column; the LSE as torch.logsumexp over the explicit scores."""
+    c = W.dense_case("ls", 91, B=2, S1=5, S2=7, Q_N=4, KV_N=2, D=6, dtype="bf16", scale=0.41,
+                     sparse_mode=mode, lse=True)
+    c = W.with_random_sink(c, 92)
+    out, lse = O.fia_case(c)
+    z = O.decode_bf16(c.learnable_sink)
+    i = np.arange(5)[:, None]
+    j = np.arange(7)[None, :]
+    vis = np.ones((5, 7), bool) if mode == 0 else (j <= i + 2)
+    for b in range(2):
+        q = O.decode_bf16(c.q[b])
+        k = np.concatenate([O.decode_bf16(c.k[b]), np.zeros((1, 2, 6))], axis=0)
+        v = np.concatenate([O.decode_bf16(c.v[b]), np.zeros((1, 2, 6))], axis=0)
+        m = np.zeros((4, 5, 8))
+        m[:, :, :7] = np.where(vis, 0.0, -np.inf)[None]
+        m[:, :, 7] = z[:, None]
+        want = sdpa(q, k, v, 0.41, mask=m, gqa=True)
+        np.testing.assert_allclose(out[b], want, rtol=1e-11, atol=1e-12)
+        kk = torch.repeat_interleave(_t(k).permute(1, 0, 2), 2, dim=0)   # [H, 8, D]
+        sc = 0.41 * torch.einsum("hid,hjd->hij", _t(q).permute(1, 0, 2), kk) + _t(m)
+        np.testing.assert_allclose(lse[b], torch.logsumexp(sc, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+
+
+def test_learnable_sink_single_key_closed_form():
+    """One key: out = v * e^s / (e^s + e^z), lse = log(e^s + e^z)."""
+    q = np.array([[[0.5, -1.0]]])            # [1, 1, 1, 2]
+    k = np.array([[[1.0, 0.25]]])
+    v = np.array([[[2.0, -3.0]]])
+    for z in (-3.0, 0.0, 0.0625, 4.0):
+        out, lse = O.fia(q[None], k[None], v[None], dtype="fp64", layout="BSND", num_heads=1,
+                         num_kv_heads=1, scale=0.5, learnable_sink=np.array([z]))
+        s = 0.5 * (0.5 * 1.0 + (-1.0) * 0.25)
+        w = math.exp(s) / (math.exp(s) + math.exp(z))
+        assert abs(out[0, 0, 0, 0] - 2.0 * w) < 1e-15 and abs(out[0, 0, 0, 1] + 3.0 * w) < 1e-15
+        assert abs(lse[0, 0, 0] - math.log(math.exp(s) + math.exp(z))) < 1e-15
+
+
+def test_learnable_sink_empty_rows_give_zero_and_the_sink():
+    """A live row with no visible key (fully masked, or Lk = 0) holds only
+    the sink: output 0, LSE = sink.  Padded rows and an empty key tensor keep
+    0 / +inf."""
+    c = W.dense_case("le", 93, B=2, S1=4, S2=8, Q_N=2, KV_N=1, D=4, dtype="fp32",
+                     q_lens=[4, 3], kv_lens=[8, 0], lse=True)
+    sink_bits = np.array([0.5, -2.0], np.float32)
+    m = np.zeros((2, 4, 8), np.uint8)
+    m[0, 1, :] = 1
+    out, lse = O.fia(c.q, c.k, c.v, dtype="fp32", layout="BSND", num_heads=2, num_kv_heads=1,
+                     scale=c.scale, actual_seq_lengths=[4, 3], actual_seq_lengths_kv=[8, 0],
+                     atten_mask=m, learnable_sink=sink_bits)
+    assert np.all(out[0, 1] == 0) and np.all(out[1, :3] == 0)
+    np.testing.assert_array_equal(lse[0, :, 1], [0.5, -2.0])
+    np.testing.assert_array_equal(lse[1, :, :3], [[0.5] * 3, [-2.0] * 3])
+    assert np.all(out[1, 3] == 0) and np.all(np.isposinf(lse[1, :, 3]))
+    out_e, lse_e = O.fia(c.q, c.k[:, :0], c.v[:, :0], dtype="fp32", layout="BSND", num_heads=2,
+                         num_kv_heads=1, scale=c.scale, learnable_sink=sink_bits)
+    assert np.all(out_e == 0) and np.all(np.isposinf(lse_e))
+
+
 def test_split_keys_merge_by_lse_reproduces_full():
     """Partial results over disjoint key ranges combine through their LSE
     (V2 softmaxLse restrictions: the ring-attention composition)."""
