@@ -510,6 +510,11 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   const bool pse_tensor = pse == 0 && pse_shift != nullptr;
   if (pse_tensor) {
     if ((st = check_tensor(pse_shift, "pse_shift")) != FIA_SUCCESS) return st;
+    // The prefill kernel folds the bias into its score accumulators as
+    // bias / scale.
+    if (!(p->scale_value > 0.0)) {
+      return fail(FIA_ERR_UNSUPPORTED, "a pse_shift tensor needs scale_value > 0");
+    }
     if (pse_shift->dtype != query->dtype) {
       return fail(FIA_ERR_PARAM_INVALID, "pse_shift must have the query's dtype");
     }
@@ -675,6 +680,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   a.tile_contig = (!paged || bs % fia::kPrefillKeys == 0) ? 1 : 0;
   a.scale = (float)p->scale_value;
   a.scale_log2 = (float)(p->scale_value * 1.4426950408889634);
+  a.inv_scale = p->scale_value > 0.0 ? (float)(1.0 / p->scale_value) : 0.f;
   a.mode = mode;
   a.pre = p->pre_tokens;
   a.next = p->next_tokens;

@@ -76,6 +76,7 @@ struct AttnArgs {
   const void* pse;
   int64_t pse_sb, pse_sh, pse_ss;
   int32_t pse_rows, pse_cols;
+  float inv_scale;                  // 1 / scale (> 0 whenever pse is set)
   // Learnable sink: bf16 logit per query head or nullptr; one more softmax
   // term with a zero value vector, not scaled.
   const uint16_t* sink;

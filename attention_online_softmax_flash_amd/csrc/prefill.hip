@@ -62,8 +62,11 @@ struct TileRegs {
 // outstanding buffer-to-LDS load only guards reads of that stage.
 //
 // EXT: an explicit mask tensor (modes 0 / 1) and / or a bias tensor (pse
-// type 0); every tile takes the per-element path, drops keys whose mask byte
-// is non-zero and adds the bias to the scaled scores.
+// type 0); every tile takes the per-element path.  Both enter through the
+// initial value of the score accumulators: -inf for a masked key, bias /
+// scale otherwise (the scaled score is then q.k * scale + bias).  Their
+// loads for tile t + 1 go out at the end of step t, so they are in
+// registers only between the steps.
 template <int D, bool ALIBI, int KVM, bool EXT>
 __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   using L = PrefillLds<D>;
@@ -155,6 +158,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
                                    : nullptr;
     uint32_t mw[8];
     u32x2 pw[8];
+    const float inv_scale = EXT ? a.inv_scale : 0.f;
     // Mask bytes and bias values of keys j0 + 4 hh + 32 k2 + 8 g .. + 3
     // (4-aligned; a group past the tensor's width lies past every visible
     // key: address clamped, values unused).
@@ -301,12 +305,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       }
     };
 
-    // S^T of one tile for this wave: 2 key blocks x 32 query rows.
-    auto compute_s = [&](const uint8_t* kst, f32x16* sv) FIA_INLINE {
+    // Score accumulators of tile kt with the mask and bias folded in (from
+    // the mask words / bias values loaded by load_ext).
+    auto init_ext = [&](f32x16* sv) FIA_INLINE {
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t pv = pw[4 * k2 + (r >> 2)][(r >> 1) & 1];
+          const float bias = __builtin_bit_cast(float, (r & 1) ? (pv & 0xffff0000u) : (pv << 16));
+          const bool off = ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) != 0u;
+          sv[k2][r] = off ? kNegInf : bias * inv_scale;
+        }
+      }
+    };
+    // S^T of one tile for this wave: 2 key blocks x 32 query rows, added to
+    // the accumulators' initial value with ACC (else from zero).
+    auto compute_s = [&](auto acc_tag, const uint8_t* kst, f32x16* sv) FIA_INLINE {
+      constexpr bool ACC = decltype(acc_tag)::value;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
         sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[0] + 32 * k2 * L::K_ROW), qreg[0],
-                        f32x16{});
+                        ACC ? sv[k2] : f32x16{});
       }
 #pragma unroll
       for (int c = 1; c < NQ; ++c) {
@@ -323,11 +343,11 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     };
 
     // Softmax of tile kt (scores in sc), then O += V^T P^T from `vst`.  With
-    // `knext` set the score product of the next tile (keys in `knext`) is
+    // `do_next` the score product of the next tile (keys in stage `knx`) is
     // issued inside the same straight-line block, so its MFMAs overlap this
     // tile's VALU work.
     auto tile_body = [&](auto masked_tag, int kt, const uint8_t* vst, f32x16* sc,
-                         const uint8_t* knext, f32x16* sn) FIA_INLINE {
+                         bool do_next, const uint8_t* knx, f32x16* sn) FIA_INLINE {
       constexpr bool MASKED = decltype(masked_tag)::value;
       constexpr bool PLAIN = !ALIBI && !MASKED;
       const int j0 = kt * BN;
@@ -354,15 +374,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
             const int koff = 32 * k2 + 8 * (r >> 2) + (r & 3);
             float x = ALIBI ? __builtin_fmaf(sc[k2][r], a.scale_log2, c_al * (base + (float)koff))
                             : sc[k2][r] * a.scale_log2;
-            if constexpr (EXT) {
-              // bf16 bias of key koff: half (r & 1) of word (r >> 1) & 1.
-              const uint32_t pv = pw[4 * k2 + (r >> 2)][(r >> 1) & 1];
-              const float bias = __builtin_bit_cast(float, (r & 1) ? (pv & 0xffff0000u) : (pv << 16));
-              x = __builtin_fmaf(bias, kLog2e, x);
-            }
             if constexpr (MASKED) {
               bool keep = koff >= rel_lo && koff < rel_hi;
-              if constexpr (EXT) keep = keep && ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) == 0u;
+              if constexpr (EXT) keep = keep && sc[k2][r] != kNegInf;   // masked-out key
               x = keep ? x : kNegInf;
             }
             sc[k2][r] = x;
@@ -388,7 +402,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       // VALU work of the other wave on the SIMD.
       __builtin_amdgcn_s_setprio(1);
       if constexpr (PIPE) {
-        if (knext != nullptr) compute_s(knext, sn);
+        if (do_next) compute_s(std::false_type{}, knx, sn);
       }
       float psum = 0.f;
       u32x4 pb[4];
@@ -447,7 +461,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     barrier_after_loads();
     f32x16 s_a[2], s_b[2];
     bool cur_skip = wave_skip(kt0);
-    if (PIPE && !cur_skip) compute_s(lds_k0, s_a);
+    if (PIPE && !cur_skip) compute_s(std::false_type{}, lds_k0, s_a);
+    if (EXT && !cur_skip) load_ext(kt0);
     if (has1) store_tile(lds_k1, lds_v1);
     __syncthreads();
 
@@ -460,19 +475,28 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       const bool has_next2 = kt + 2 < kt1;
       if (has_next2) load_tile(kt + 2, (PIPE && DMA_K) ? kst : nullptr);
       const bool next_skip = has_next ? wave_skip(kt + 1) : true;
-      const uint8_t* knext = (!PIPE || next_skip) ? nullptr : knx;
-      if (EXT && !cur_skip) load_ext(kt);
-      if (!PIPE && !cur_skip) compute_s(kst, sc);
+      // The next tile's keys are always read from the other stage array
+      // itself (not through a pointer chosen at run time), so the compiler
+      // sees that they cannot alias this step's buffer-to-LDS loads.
+      const bool do_next = PIPE && !next_skip;
+      if constexpr (EXT) {
+        if (!cur_skip) {
+          init_ext(sc);
+          compute_s(std::true_type{}, kst, sc);
+        }
+      } else if (!PIPE && !cur_skip) {
+        compute_s(std::false_type{}, kst, sc);
+      }
       if (!cur_skip) {
         const int j0 = kt * BN;
         const bool need_mask = EXT || !(j0 >= wlo_max && j0 + BN <= whi_min);
         if (need_mask) {
-          tile_body(std::true_type{}, kt, vst, sc, knext, sn);
+          tile_body(std::true_type{}, kt, vst, sc, do_next, knx, sn);
         } else {
-          tile_body(std::false_type{}, kt, vst, sc, knext, sn);
+          tile_body(std::false_type{}, kt, vst, sc, do_next, knx, sn);
         }
-      } else if (PIPE && knext != nullptr) {
-        compute_s(knext, sn);
+      } else if (do_next) {
+        compute_s(std::false_type{}, knx, sn);
       }
       cur_skip = next_skip;
       barrier_after_loads();   // loads of tile kt + 2 landed; every wave is done with tile kt
@@ -480,6 +504,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         if constexpr (!PIPE && DMA_K) load_k_lds(kt + 2, kst);
         store_tile(kst, vst);
       }
+      if (EXT && !next_skip) load_ext(kt + 1);
     };
     for (int kt = kt0; kt < kt1; kt += 2) {
       step(std::integral_constant<int, 0>{}, kt, s_a, s_b);

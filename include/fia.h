@@ -158,6 +158,8 @@ typedef struct {
  *                   the actual lengths.  Last dim contiguous; batch, head and
  *                   row strides, the last extent and the base (in elements)
  *                   multiples of 4, else FIA_ERR_UNSUPPORTED; not with TND.
+ *                   Needs scale_value > 0 (the prefill kernel carries the
+ *                   bias as bias / scale in its fp32 score accumulators).
  *   atten_mask      modes 0 / 1: NULL or int8 / uint8 / bool [B or 1, >= Q_S,
  *                   >= KV_S], [B or 1, 1, >= Q_S, >= KV_S] or [>= Q_S, >= KV_S]
  *                   (KV_S = block_table cols * block_size when paged), rows

@@ -305,6 +305,8 @@ def test_pse_bias_rules():
     for shape, dt in bad:
         st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o, pse=T(shape, dt))
         assert st == BAD, (shape, dt, msg)
+    st, _, _, msg = plan(P(num_kv_heads=2, scale=0.0), q, k, v, o, pse=T((2, 4, 64, 64)))
+    assert st == UNS and "scale" in msg
     # bias with an explicit mask
     st, _, _, msg = plan(P(num_kv_heads=2, sparse_mode=1), q, k, v, o, pse=T((2, 4, 64, 64)),
                          mask=T((2, 64, 64), fia.DT_UINT8))
