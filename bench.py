@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
+SEEDS_HCA = 1006
 
 
 def visible_pairs(mode, Lq, Lk):
@@ -48,7 +49,14 @@ def dense_flops(case):
     B = case.batch
     lq = case.actual_seq_lengths or [case.q.shape[1]] * B
     lk = case.actual_seq_lengths_kv or [case.k.shape[1]] * B
-    pairs = sum(visible_pairs(case.sparse_mode, int(a), int(b)) for a, b in zip(lq, lk))
+    m = getattr(case, "atten_mask", None)
+    if m is not None and case.sparse_mode in (0, 1):
+        # explicit mask: the unmasked pairs of each batch's [Lq, Lk] corner
+        m3 = m.reshape(-1, m.shape[-2], m.shape[-1])
+        pairs = sum(int((m3[b if m3.shape[0] > 1 else 0, :int(a), :int(c)] == 0).sum())
+                    for b, (a, c) in enumerate(zip(lq, lk)))
+    else:
+        pairs = sum(visible_pairs(case.sparse_mode, int(a), int(b)) for a, b in zip(lq, lk))
     return 4.0 * case.q.shape[-1] * case.num_heads * pairs
 
 
@@ -73,9 +81,13 @@ def sparse_bytes(case):
     for b, Lk in enumerate(case.seqused_kv):
         win = min(Lk, case.win_left + case.win_right + 1)
         n_cmp = Lk // case.cmp_ratio
-        idx = case.cmp_sparse_indices[b, 0, 0]
-        rows += win + int(((idx >= 0) & (idx < n_cmp)).sum())
-    return rows * 604 + 2 * B * N1 * D * 2 + case.cmp_sparse_indices.nbytes
+        if case.cmp_sparse_indices is None:     # heavily compressed: every compressed row
+            rows += win + n_cmp
+        else:
+            idx = case.cmp_sparse_indices[b, 0, 0]
+            rows += win + int(((idx >= 0) & (idx < n_cmp)).sum())
+    idx_bytes = 0 if case.cmp_sparse_indices is None else case.cmp_sparse_indices.nbytes
+    return rows * 604 + 2 * B * N1 * D * 2 + idx_bytes
 
 
 def time_plan(plan, steps, warmup, flush=None):
@@ -177,7 +189,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "copy"], default="all",
+    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "next", "copy"], default="all",
                     help="limit the run to one workload (profiling); 'copy' runs a plain 1 GiB "
                          "device copy, the calibration of the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -292,6 +304,45 @@ def main():
         components["sparse_sharedkv_decode"] = {
             "workload": "shared-KV sparse decode: B=16, Q_N=64, D=512 (fp8 nope + bf16 rope), "
                         "window 128 + top-512 of ratio-4 compressed KV, sinks",
+            "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
+            "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+        del plan
+
+    if want("next"):
+        # The causal GQA prefill workload with the inputs of the mask / bias /
+        # sink parameter groups, and the heavily compressed sparse mode.
+        base = W.c2_causal_gqa()
+        variants = [
+            ("prefill_explicit_mask", W.with_random_mask(base, 41, p_masked=0.1, mode=0),
+             "causal GQA prefill shapes, sparse_mode 0 with a uint8 mask [4, 2048, 2048] "
+             "(10 % of keys masked out, every key of the actual lengths otherwise)"),
+            ("prefill_pse_bias", W.with_random_bias(base, 42, per_batch=False),
+             "causal GQA prefill with a bf16 pse_shift bias [1, 32, 2048, 2048]"),
+            ("prefill_learnable_sink", W.with_random_sink(base, 43),
+             "causal GQA prefill with a bf16 learnable sink [32]"),
+        ]
+        for key, case, text in variants:
+            flops = dense_flops(case)
+            plan = TI.dense_plan(case, dev)
+            _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
+            tf = flops / (kern_ms / 1000.0) / 1e12
+            components[key] = {
+                "workload": text, "unit": "TFLOP/s", "value": round(tf, 3),
+                "algorithmic_flop": flops, "ms": round(kern_ms, 5),
+                "kernels": "prefill_bf16<128, false, 0, true>" if key != "prefill_learnable_sink"
+                           else "prefill_bf16<128, false, 0, false>",
+                "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)}
+            del plan, case
+        case = W.sparse_case("hca", SEEDS_HCA, B=16, N1=64, seqused_kv=[16384] * 16,
+                             materialise_all_ori=False, heavily_compressed=True)
+        nbytes = sparse_bytes(case)
+        plan = TI.sparse_plan(case, dev)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["sparse_heavily_compressed"] = {
+            "workload": "shared-KV sparse decode, heavily compressed: B=16, Q_N=64, D=512, "
+                        "window 128 + every row of the ratio-128 compressed KV (128 rows), sinks",
             "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
             "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
