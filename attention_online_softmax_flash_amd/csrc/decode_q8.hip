@@ -1,0 +1,391 @@
+// Incremental decode over a fake-quantised KV cache (aclnnFusedInferAttentionScoreV5,
+// quantisation parameter group, fake-quant scenario): key and value rows are
+// int8 or float8 e4m3fn codes, the query bf16.  A value is dequantised as
+// scale * (code + offset), with the scale / offset either per channel
+// ([KV_N, D], or one value for the whole tensor) or per token ([B, S2],
+// shared by the KV heads).
+//
+// Same work split, chunking, wave combine and partial format as the bf16
+// split-KV kernel, so the bf16 merge kernel folds the partials.  The scales
+// and offsets are moved out of the MFMA operands:
+//   * key, per channel:  s_j = sum_d (q_d ks_d) c_jd + sum_d q_d ks_d ko_d.  The
+//     first term is an MFMA of the codes (exact in bf16) against q * ks split
+//     into a bf16 high and low part (two products, so the scaled query keeps
+//     about 16 bits); the second is one constant per head.
+//   * key, per token:    s_j = ks_j (q . c_j + ko_j sum_d q_d).
+//   * value, per channel: o_d = vs_d (sum_j p_j c_jd / l + vo_d), applied to the
+//     normalised chunk result (the merge is a convex combination, so it
+//     commutes with this per-channel affine map).
+//   * value, per token:  o_d = (sum_j (p_j vs_j) c_jd + sum_j p_j vs_j vo_j) / l;
+//     p_j vs_j is the bf16 operand, the offset sum one fp32 value per head.
+// Lane (n, g) of the score product holds d = (D / 4) g + 8 cc + e of both the
+// key codes and the query (one permutation of d on both operands), so each
+// lane loads D / 4 contiguous bytes of its key row.
+#include "fia_device.h"
+
+namespace fia {
+
+namespace {
+
+// Element i of a per-channel scale / offset (bf16 or fp32; one element for
+// the whole tensor when `scalar`), 0 without a tensor.
+__device__ __forceinline__ float chan_val(const void* p, int is_f32, int scalar, int i) {
+  if (p == nullptr) return 0.f;
+  const int k = scalar ? 0 : i;
+  return is_f32 ? static_cast<const float*>(p)[k] : bf16_to_f32(static_cast<const uint16_t*>(p)[k]);
+}
+
+// Byte K of the 4-byte word w as a float (int8 or e4m3fn code, exact).
+template <bool FP8, int K>
+__device__ __forceinline__ float code_byte(uint32_t w) {
+  if constexpr (FP8) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)w, K);
+  } else {
+    return (float)(int8_t)(w >> (8 * K));
+  }
+}
+// Same with the byte index known after unrolling.
+template <bool FP8>
+__device__ __forceinline__ float code_f32(uint32_t w, int k) {
+  switch (k) {
+    case 0: return code_byte<FP8, 0>(w);
+    case 1: return code_byte<FP8, 1>(w);
+    case 2: return code_byte<FP8, 2>(w);
+    default: return code_byte<FP8, 3>(w);
+  }
+}
+
+// Split x into a bf16 high part and a bf16 low part (x - hi), as bits.
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
+  hi = h;
+  lo = pack_bf16x2(x - bf16_to_f32((uint16_t)h), 0.f) & 0xffffu;
+}
+
+}  // namespace
+
+// KPT / VPT: key / value scales per token (else per channel).
+template <int D, bool FP8, bool KPT, bool VPT>
+__global__ __launch_bounds__(256, 2) void decode_split_q8(AttnArgs a) {
+  constexpr int NC = D / 32;   // 32-wide k-steps of the score product per 16-key half
+  constexpr int DPL = D / 16;  // value columns per lane column
+  constexpr int KB = D / 4;    // key bytes per lane and row
+  const int lane = threadIdx.x & 63;
+  const int wave = uniform(threadIdx.x >> 6);
+  const int n = lane & 15;
+  const int g = lane >> 4;
+
+  int item = blockIdx.x;
+  const int hb = item % a.n_head_blocks;
+  item /= a.n_head_blocks;
+  const int kvh = item % a.KVn;
+  const int cg = item / a.KVn;
+  const int b = a.work[2 * cg];
+  const int c = a.work[2 * cg + 1];
+  const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
+  const int lo = bm[BF_LO], hi = bm[BF_HI];
+  const int nchunk = bm[BF_NCHUNK], chunk0 = bm[BF_CHUNK0];
+  const int kv_off = bm[BF_KVOFF], q_off = bm[BF_QOFF];
+
+  const int C = a.chunk;
+  const int wlen = C >> 2;
+  const int cbase = (lo / C + c) * C;
+  const int ws = cbase + wave * wlen;
+  const int t_lo = max(ws, lo);
+  const int t_hi = min(ws + wlen, hi);
+
+  const int hl = hb * 16 + n;
+  const bool hvalid = hl < a.G;
+  const int h = kvh * a.G + (hvalid ? hl : 0);
+
+  // Query of head n at d = KB g + 8 cc + e, as the B operand: the bf16 query
+  // itself (key per token), or q * ks split into high and low parts (key per
+  // channel).  qc: the per-head constant of the scores (log2 units), or, per
+  // token, sum_d q_d.
+  const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)q_off * a.q_ss +
+                       (int64_t)h * a.q_sh + KB * g;
+  u32x4 qh[NC], ql[NC];
+  float qc = 0.f;
+#pragma unroll
+  for (int cc = 0; cc < NC; ++cc) {
+    const u32x4 raw = hvalid ? ld16(qp + 8 * cc) : u32x4{0, 0, 0, 0};
+    if constexpr (KPT) {
+      qh[cc] = raw;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = raw[e >> 1];
+        qc += bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+      }
+    } else {
+      uint32_t hbits[8], lbits[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t w = raw[e >> 1];
+        const float qd = bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+        const int ch = kvh * D + KB * g + 8 * cc + e;
+        const float qs = qd * chan_val(a.kq_scale, a.kq_f32, a.kq_scalar, ch);
+        split_bf16(qs, hbits[e], lbits[e]);
+        qc += qs * chan_val(a.kq_off, a.kq_f32, a.kq_scalar, ch);
+      }
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        qh[cc][w] = hbits[2 * w] | (hbits[2 * w + 1] << 16);
+        ql[cc][w] = lbits[2 * w] | (lbits[2 * w + 1] << 16);
+      }
+    }
+  }
+  // Sum over the four lanes of head n (lanes n, n + 16, n + 32, n + 48).
+  qc += shfl_xor_f(qc, 16);
+  qc += shfl_xor_f(qc, 32);
+  const float c_shift = KPT ? 0.f : qc * a.scale_log2;
+
+  float m_run = kNegInf;
+  float l_run = 0.f;
+  float t_run = 0.f;   // value per token: sum_j p_j vs_j vo_j
+  f32x4 o[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) o[e] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const uint8_t* kbase = (const uint8_t*)a.k;
+  const uint8_t* vbase = (const uint8_t*)a.v;
+  const float* ksp = KPT ? (const float*)a.kq_scale + (int64_t)b * a.kq_sb : nullptr;
+  const float* kop = KPT && a.kq_off ? (const float*)a.kq_off + (int64_t)b * a.kq_sb : nullptr;
+  const float* vsp = VPT ? (const float*)a.vq_scale + (int64_t)b * a.vq_sb : nullptr;
+  const float* vop = VPT && a.vq_off ? (const float*)a.vq_off + (int64_t)b * a.vq_sb : nullptr;
+
+  if (t_hi > t_lo) {
+    const int first = ws + ((t_lo - ws) & ~31);
+    for (int ts = first; ts < t_hi; ts += kDecodeStep) {
+      // The two 16-key halves each lie inside one page (block sizes are
+      // multiples of 32); rows at or past `hi` read as zero.
+      __amdgpu_buffer_rsrc_t rk[2], rv[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int jb = ts + 16 * hf;
+        const int nv = min(16, hi - jb);
+        int64_t ko = 0, vo = 0;
+        uint32_t kbytes = 0, vbytes = 0;
+        if (nv > 0) {
+          ko = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
+          vo = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
+          kbytes = (uint32_t)((nv - 1) * a.k_ss + D);
+          vbytes = (uint32_t)((nv - 1) * a.v_ss + D);
+        }
+        rk[hf] = make_rsrc(kbase + ko, kbytes);
+        rv[hf] = make_rsrc(vbase + vo, vbytes);
+      }
+      // Key codes: row 16 hf + n, bytes KB g .. KB g + KB - 1.
+      u32x4 kw[2][KB / 16];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+        for (int i = 0; i < KB / 16; ++i) {
+          kw[hf][i] = buf_ld16_nt(rk[hf], (uint32_t)(n * a.k_ss + KB * g + 16 * i));
+        }
+      }
+      // Value codes for k-slot s: key 16 (s / 4) + 4 g + s % 4, columns DPL n ..
+      uint32_t vr[8][DPL / 4];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int hf = s >> 2;
+        const int t = 4 * g + (s & 3);
+        const uint32_t off = (uint32_t)(t * a.v_ss + DPL * n);
+        if constexpr (DPL == 8) {
+          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[hf], off, 0, 2));
+          vr[s][0] = w.x;
+          vr[s][1] = w.y;
+        } else {
+          vr[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rv[hf], off, 0, 2);
+        }
+      }
+      // Per-token scales / offsets of the lane's keys ts + 16 hf + 4 g + r
+      // (4-aligned groups; a group past the tensor's width lies past every
+      // visible key, so its index is clamped).
+      f32x4 ks[2], kq[2], vs[2], vq[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int j4 = ts + 16 * hf + 4 * g;
+        ks[hf] = kq[hf] = vs[hf] = vq[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (KPT) {
+          const int jk = min(j4, a.kq_cols - 4);
+          ks[hf] = *reinterpret_cast<const f32x4*>(ksp + jk);
+          if (kop != nullptr) kq[hf] = *reinterpret_cast<const f32x4*>(kop + jk);
+        }
+        if constexpr (VPT) {
+          const int jv = min(j4, a.vq_cols - 4);
+          vs[hf] = *reinterpret_cast<const f32x4*>(vsp + jv);
+          if (vop != nullptr) vq[hf] = *reinterpret_cast<const f32x4*>(vop + jv);
+        }
+      }
+
+      // Scores S^T[key 16 hf + 4 g + r][head n].
+      f32x4 sc[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc) {
+          // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
+          const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
+          const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
+          const u32x4 kop8 = {pack_bf16x2(code_f32<FP8>(w0, 0), code_f32<FP8>(w0, 1)),
+                              pack_bf16x2(code_f32<FP8>(w0, 2), code_f32<FP8>(w0, 3)),
+                              pack_bf16x2(code_f32<FP8>(w1, 0), code_f32<FP8>(w1, 1)),
+                              pack_bf16x2(code_f32<FP8>(w1, 2), code_f32<FP8>(w1, 3))};
+          sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
+          if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
+        }
+      }
+      float x[8];
+      float mx = kNegInf;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        const int hf = s >> 2, r = s & 3;
+        const int j = ts + 16 * hf + 4 * g + r;
+        const bool ok = j >= t_lo && j < t_hi;
+        float v;
+        if constexpr (KPT) {
+          v = ks[hf][r] * __builtin_fmaf(kq[hf][r], qc, sc[hf][r]) * a.scale_log2;
+        } else {
+          v = __builtin_fmaf(sc[hf][r], a.scale_log2, c_shift);
+        }
+        x[s] = ok ? v : kNegInf;
+        mx = fmaxf(mx, x[s]);
+      }
+      mx = pair32_max(pair16_max(mx));
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float p[8];
+      float psum = 0.f, tsum = 0.f;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        p[s] = fast_exp2(x[s] - m_use);
+        psum += p[s];
+      }
+      if constexpr (VPT) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const float pv = p[s] * vs[s >> 2][s & 3];
+          tsum = __builtin_fmaf(pv, vq[s >> 2][s & 3], tsum);
+          p[s] = pv;
+        }
+      }
+      l_run = l_run * alpha + psum;
+      t_run = t_run * alpha + tsum;
+      m_run = m_new;
+      const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                        pack_bf16x2(p[6], p[7])};
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) {
+        o[e] *= alpha;
+        // byte e of the lane's DPL value bytes of each of the 8 keys
+        const int w = e >> 2, k = e & 3;
+        const u32x4 av = {pack_bf16x2(code_f32<FP8>(vr[0][w], k), code_f32<FP8>(vr[1][w], k)),
+                          pack_bf16x2(code_f32<FP8>(vr[2][w], k), code_f32<FP8>(vr[3][w], k)),
+                          pack_bf16x2(code_f32<FP8>(vr[4][w], k), code_f32<FP8>(vr[5][w], k)),
+                          pack_bf16x2(code_f32<FP8>(vr[6][w], k), code_f32<FP8>(vr[7][w], k))};
+        o[e] = mfma16(av, pb, o[e]);
+      }
+    }
+  }
+  l_run = pair32_sum(pair16_sum(l_run));
+  t_run = pair32_sum(pair16_sum(t_run));
+
+  // Combine the four waves through LDS in wave order.
+  __shared__ float sm_m[4][16];
+  __shared__ float sm_l[4][16];
+  __shared__ float sm_t[4][16];
+  __shared__ __attribute__((aligned(16))) float sm_o[4][16][D + 4];
+  if (g == 0) {
+    sm_m[wave][n] = m_run;
+    sm_l[wave][n] = l_run;
+    sm_t[wave][n] = t_run;
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sm_o[wave][n][DPL * (4 * g + r) + e] = o[e][r];
+  }
+  __syncthreads();
+
+  constexpr int PER = 16 * D / 256;  // outputs per thread
+  const int hh = threadIdx.x / (D / PER);
+  const int d0 = (threadIdx.x % (D / PER)) * PER;
+  if (hb * 16 + hh >= a.G) return;
+  const int hout = kvh * a.G + hb * 16 + hh;
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
+  float wgt[4];
+  float L = 0.f, T = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    wgt[w] = (sm_m[w][hh] == kNegInf) ? 0.f : fast_exp2(sm_m[w][hh] - M);
+    L += sm_l[w][hh] * wgt[w];
+    T += sm_t[w][hh] * wgt[w];
+  }
+  const bool any = L > 0.f;
+  const float inv = any ? 1.f / L : 0.f;
+  const float lse2 = any ? M + fast_log2(L) : kNegInf;
+  float val[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) s += sm_o[w][hh][d0 + u] * wgt[w];
+    if constexpr (VPT) {
+      val[u] = (s + T) * inv;
+    } else {
+      const int ch = kvh * D + d0 + u;
+      val[u] = any ? chan_val(a.vq_scale, a.vq_f32, a.vq_scalar, ch) *
+                         (s * inv + chan_val(a.vq_off, a.vq_f32, a.vq_scalar, ch))
+                   : 0.f;
+    }
+  }
+  if (nchunk == 1) {
+    uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
+                   (int64_t)hout * a.o_sh + d0;
+#pragma unroll
+    for (int u = 0; u < PER; u += 2) {
+      *reinterpret_cast<uint32_t*>(op + u) = pack_bf16x2(val[u], val[u + 1]);
+    }
+    if (a.write_lse && d0 == 0) {
+      a.lse[(int64_t)b * a.lse_sb + (int64_t)hout * a.lse_sh + (int64_t)q_off * a.lse_ss] =
+          any ? lse2 * kLn2 : kPosInf;
+    }
+  } else {
+    const int64_t pi = (int64_t)(chunk0 + c) * a.Qn + hout;
+    float* pp = a.part_o + pi * D + d0;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) pp[u] = val[u];
+    if (d0 == 0) a.part_lse[pi] = lse2;
+  }
+}
+
+template <int D, bool FP8>
+static void launch_q8_modes(const AttnArgs& a, int32_t n_items, hipStream_t s) {
+  if (a.kq_mode == 1) {
+    decode_split_q8<D, FP8, true, true><<<n_items, 256, 0, s>>>(a);
+  } else if (a.vq_mode == 1) {
+    decode_split_q8<D, FP8, false, true><<<n_items, 256, 0, s>>>(a);
+  } else {
+    decode_split_q8<D, FP8, false, false><<<n_items, 256, 0, s>>>(a);
+  }
+}
+
+hipError_t launch_decode_q8(const AttnArgs& a, int32_t n_items, hipStream_t s) {
+  if (n_items > 0) {
+    const bool fp8 = a.kvq == 2;
+    if (a.D == 128) {
+      if (fp8) launch_q8_modes<128, true>(a, n_items, s);
+      else launch_q8_modes<128, false>(a, n_items, s);
+    } else {
+      if (fp8) launch_q8_modes<64, true>(a, n_items, s);
+      else launch_q8_modes<64, false>(a, n_items, s);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fia

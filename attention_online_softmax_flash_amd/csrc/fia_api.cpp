@@ -308,7 +308,14 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     return fail(FIA_ERR_UNSUPPORTED, std::string("query dtype ") + dtype_name(query->dtype) +
                                          " is not supported (bf16, fp32)");
   }
-  if (key->dtype != query->dtype || value->dtype != query->dtype) {
+  // Fake-quantised key / value: int8 or e4m3fn codes with a bf16 query.
+  const bool kvq = query->dtype == FIA_DT_BF16 &&
+                   (key->dtype == FIA_DT_INT8 || key->dtype == FIA_DT_FP8_E4M3FN);
+  if (kvq) {
+    if (value->dtype != key->dtype) {
+      return fail(FIA_ERR_PARAM_INVALID, "fake-quantised key and value must have the same dtype");
+    }
+  } else if (key->dtype != query->dtype || value->dtype != query->dtype) {
     return fail(FIA_ERR_PARAM_INVALID, "key and value must have the query dtype");
   }
   if (attention_out->dtype != query->dtype) {
@@ -560,6 +567,131 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
       return fail(FIA_ERR_PARAM_INVALID, "learnable_sink does not combine with pse or ALiBi");
     }
   }
+  // Fake-quant group (V5 quantisation parameters, fake-quant scenario).
+  struct AqView {
+    const void* scale = nullptr;
+    const void* off = nullptr;
+    int32_t f32 = 0, scalar = 0, cols = 0;
+    int64_t sb = 0;
+  } aqk, aqv;
+  const int kmode = p->key_antiquant_mode, vmode = p->value_antiquant_mode;
+  if (kvq) {
+    if (kmode < 0 || kmode > 6 || vmode < 0 || vmode > 6) {
+      return fail(FIA_ERR_PARAM_INVALID, "key/value_antiquant_mode must be in [0, 6]");
+    }
+    if (kmode != vmode && !(kmode == 0 && vmode == 1)) {
+      return fail(FIA_ERR_PARAM_INVALID, "key and value antiquant modes must be equal, or key per "
+                                         "channel (0) with value per token (1)");
+    }
+    if (kmode > 1 || vmode > 1) {
+      return fail(FIA_ERR_UNSUPPORTED, "antiquant modes 2-6 are not supported");
+    }
+    if (max_q > 1 || (!tnd && cq.S != 1)) {
+      return fail(FIA_ERR_UNSUPPORTED, "fake-quantised key/value are supported for query length 1");
+    }
+    if (D != 64 && D != 128) return fail(FIA_ERR_UNSUPPORTED, "fake-quantised key/value need D 64 or 128");
+    if (pse == 2 || pse_tensor || explicit_mask || sink != nullptr) {
+      return fail(FIA_ERR_UNSUPPORTED, "fake-quantised key/value do not combine with pse, an explicit "
+                                       "mask or a learnable sink");
+    }
+    if (paged && (bs % 32 != 0 || bs > 512)) {
+      return fail(FIA_ERR_PARAM_INVALID, "fake-quant paged attention needs block_size % 32 == 0, <= 512");
+    }
+    const fia_tensor* ksc = p->key_antiquant_scale;
+    const fia_tensor* vsc = p->value_antiquant_scale;
+    const fia_tensor* kof = p->key_antiquant_offset;
+    const fia_tensor* vof = p->value_antiquant_offset;
+    if (ksc == nullptr || vsc == nullptr) {
+      return fail(FIA_ERR_PARAM_INVALID, "fake quant needs key_antiquant_scale and value_antiquant_scale");
+    }
+    if ((kof == nullptr) != (vof == nullptr)) {
+      return fail(FIA_ERR_PARAM_INVALID, "key_antiquant_offset and value_antiquant_offset go together");
+    }
+    if (kof != nullptr && key->dtype != FIA_DT_INT8) {
+      return fail(FIA_ERR_PARAM_INVALID, "antiquant offsets are for int8 key/value only");
+    }
+    // Key length of the per-token tables: the padded S2, or with TND the
+    // longest actual key length.
+    int64_t S2q = paged ? bt_cols * bs : ck.S;
+    if (tnd) {
+      S2q = 0;
+      for (auto v : kvlen) S2q = std::max(S2q, v);
+    }
+    auto view = [&](const fia_tensor* sc, const fia_tensor* of, int m, bool f32_chan, const char* what,
+                    AqView* out) -> fia_status {
+      fia_status s2;
+      for (const fia_tensor* t : {sc, of}) {
+        if (t == nullptr) continue;
+        if ((s2 = check_tensor(t, what)) != FIA_SUCCESS) return s2;
+        if (of != nullptr && (t->dtype != sc->dtype || t->ndim != sc->ndim)) {
+          return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": offset must match the scale");
+        }
+        for (int d = 0; of != nullptr && d < t->ndim; ++d) {
+          if (of->shape[d] != sc->shape[d] || of->stride[d] != sc->stride[d]) {
+            return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": offset must match the scale");
+          }
+        }
+      }
+      out->scale = sc->data;
+      out->off = of ? of->data : nullptr;
+      if (m == 0) {
+        const int want = f32_chan ? FIA_DT_FP32 : FIA_DT_BF16;
+        if (sc->dtype != want) {
+          return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": per-channel scale dtype must be " +
+                                                 (f32_chan ? "fp32" : "the query's"));
+        }
+        if (numel(sc) == 1 && sc->ndim == 1) {
+          if (key->dtype != FIA_DT_INT8 || f32_chan) {
+            return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": per-tensor scale is for int8 "
+                                                                   "with equal modes");
+          }
+          out->scalar = 1;
+        } else {
+          // (1, N, 1, D), (1, N, D), (1, H), (N, 1, D), (N, D), (H): N * D
+          // contiguous values.
+          bool ok = numel(sc) == KVn * D && sc->shape[sc->ndim - 1] % D == 0;
+          if (sc->ndim == 4) ok = ok && sc->shape[0] == 1 && sc->shape[2] == 1 && sc->shape[3] == D;
+          if (sc->ndim == 3) ok = ok && sc->shape[2] == D && (sc->shape[0] == 1 || sc->shape[1] == 1);
+          int64_t acc = 1;
+          for (int d = sc->ndim - 1; ok && d >= 0; --d) {
+            if (sc->shape[d] > 1 && sc->stride[d] != acc) ok = false;
+            acc *= sc->shape[d];
+          }
+          if (!ok) {
+            return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": per-channel scale must be (1, N, 1, D), "
+                                                   "(1, N, D), (1, H), (N, 1, D), (N, D) or (H), contiguous");
+          }
+        }
+        out->f32 = f32_chan ? 1 : 0;
+      } else {
+        if (sc->dtype != FIA_DT_FP32) {
+          return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": per-token scale must be fp32");
+        }
+        const bool two = sc->ndim == 2 && sc->shape[0] == B;
+        const bool three = sc->ndim == 3 && sc->shape[0] == 1 && sc->shape[1] == B;
+        if ((!two && !three) || sc->shape[sc->ndim - 1] < S2q) {
+          return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": per-token scale must be (B, >= S2) or "
+                                                                 "(1, B, >= S2)");
+        }
+        out->sb = sc->stride[sc->ndim - 2];
+        const int64_t cols = sc->shape[sc->ndim - 1];
+        if (cols > INT32_MAX) return fail(FIA_ERR_PARAM_INVALID, std::string(what) + ": too long");
+        out->cols = (int32_t)cols;
+        if (out->sb % 4 || cols % 4 || reinterpret_cast<uintptr_t>(sc->data) % 16 ||
+            (of && reinterpret_cast<uintptr_t>(of->data) % 16)) {
+          return fail(FIA_ERR_UNSUPPORTED, std::string(what) + ": per-token rows must be 16-byte aligned "
+                                                               "(pad S2 to a multiple of 4)");
+        }
+      }
+      return FIA_SUCCESS;
+    };
+    const bool mixed = kmode == 0 && vmode == 1;
+    if ((st = view(ksc, kof, kmode, mixed, "key_antiquant_scale", &aqk)) != FIA_SUCCESS) return st;
+    if ((st = view(vsc, vof, vmode, false, "value_antiquant_scale", &aqv)) != FIA_SUCCESS) return st;
+  } else if (p->key_antiquant_scale || p->value_antiquant_scale || p->key_antiquant_offset ||
+             p->value_antiquant_offset) {
+    return fail(FIA_ERR_PARAM_INVALID, "antiquant scales / offsets need int8 or fp8 key/value");
+  }
   if (pse == 2) {
     if (pse_shift == nullptr) return fail(FIA_ERR_PARAM_INVALID, "pse_type 2 requires pse_shift");
     if ((st = check_tensor(pse_shift, "pse_shift")) != FIA_SUCCESS) return st;
@@ -612,6 +744,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   {
     // Key / value of an empty input are never read; their strides do not matter.
     const int64_t vec = f32 ? 4 : 8;  // elements per 16-byte access
+    const int64_t kv_vec = kvq ? 16 : vec;
     const int64_t strides[] = {cq.ss, cq.sh, co.ss, co.sh, tnd ? 0 : cq.sb, tnd ? 0 : co.sb};
     const int64_t kv_strides[] = {ck.ss, ck.sh, cv.ss, cv.sh, ck.sb, cv.sb};
     for (int64_t s : strides) {
@@ -625,7 +758,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     }
     if (!kv_empty) {
       for (int64_t s : kv_strides) {
-        if (s % vec != 0) return fail(FIA_ERR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
+        if (s % kv_vec != 0) return fail(FIA_ERR_UNSUPPORTED, "row strides must be multiples of 16 bytes");
       }
       if (ck.ss < D || cv.ss < D) {
         return fail(FIA_ERR_UNSUPPORTED, "key/value rows must not overlap (token stride >= D)");
@@ -688,6 +821,13 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   a.alibi_delta = (int32_t)(p->kv_start_idx - p->q_start_idx);
   a.pse = pse_tensor ? pse_shift->data : nullptr;
   a.sink = sink != nullptr ? static_cast<const uint16_t*>(sink->data) : nullptr;
+  a.kvq = kvq ? (key->dtype == FIA_DT_INT8 ? 1 : 2) : 0;
+  a.kq_mode = kmode;
+  a.vq_mode = vmode;
+  a.kq_scale = aqk.scale; a.kq_off = aqk.off; a.kq_f32 = aqk.f32; a.kq_scalar = aqk.scalar;
+  a.kq_sb = aqk.sb; a.kq_cols = aqk.cols;
+  a.vq_scale = aqv.scale; a.vq_off = aqv.off; a.vq_f32 = aqv.f32; a.vq_scalar = aqv.scalar;
+  a.vq_sb = aqv.sb; a.vq_cols = aqv.cols;
   a.pse_sb = pse_sb;
   a.pse_sh = pse_sh;
   a.pse_ss = pse_ss;
@@ -1052,7 +1192,8 @@ fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void
     case KIND_FP32: err = fia::launch_attn_fp32(e->a, s); break;
     case KIND_PREFILL: err = fia::launch_prefill_bf16(e->a, s); break;
     case KIND_DECODE:
-      err = fia::launch_decode_bf16(e->a, e->n_items, s);
+      err = e->a.kvq ? fia::launch_decode_q8(e->a, e->n_items, s)
+                     : fia::launch_decode_bf16(e->a, e->n_items, s);
       if (err == hipSuccess) err = fia::launch_decode_merge(e->a, s);
       break;
     case KIND_SPARSE:

@@ -77,6 +77,21 @@ struct AttnArgs {
   int64_t pse_sb, pse_sh, pse_ss;
   int32_t pse_rows, pse_cols;
   float inv_scale;                  // 1 / scale (> 0 whenever pse is set)
+  // Fake-quantised key / value (decode only): rows of int8 (kvq 1) or e4m3fn
+  // (kvq 2) codes, dequantised as scale * (code + offset).  Mode 0: per
+  // channel, element kvh * D + d of a bf16 (or fp32, *_f32) tensor, or its
+  // only element (*_scalar); mode 1: per token, fp32 element b * *_sb + j
+  // (j < *_cols, *_cols and *_sb multiples of 4).  Offsets (nullable) share
+  // the scale's layout.
+  int32_t kvq;
+  int32_t kq_mode, vq_mode;
+  const void* kq_scale;
+  const void* kq_off;
+  const void* vq_scale;
+  const void* vq_off;
+  int32_t kq_f32, kq_scalar, vq_f32, vq_scalar;
+  int64_t kq_sb, vq_sb;
+  int32_t kq_cols, vq_cols;
   // Learnable sink: bf16 logit per query head or nullptr; one more softmax
   // term with a zero value vector, not scaled.
   const uint16_t* sink;
@@ -123,6 +138,7 @@ struct SparseArgs {
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s);
 hipError_t launch_decode_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_q8(const AttnArgs& a, int32_t n_items, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fill_empty(const AttnArgs& a, hipStream_t s);
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t s);

@@ -74,6 +74,12 @@ class FiaParams(ctypes.Structure):
         ("actual_seq_lengths_kv_len", ctypes.c_int64),
         ("kv_layout", ctypes.c_char_p),
         ("learnable_sink", ctypes.POINTER(FiaTensor)),
+        ("key_antiquant_mode", ctypes.c_int32),
+        ("value_antiquant_mode", ctypes.c_int32),
+        ("key_antiquant_scale", ctypes.POINTER(FiaTensor)),
+        ("value_antiquant_scale", ctypes.POINTER(FiaTensor)),
+        ("key_antiquant_offset", ctypes.POINTER(FiaTensor)),
+        ("value_antiquant_offset", ctypes.POINTER(FiaTensor)),
     ]
 
 
@@ -212,7 +218,9 @@ class AttentionPlan(_Plan):
                  kv_start_idx=0, atten_mask=None, block_table=None, block_size=0,
                  inner_precise=0, softmax_lse_flag=False, actual_seq_lengths=None,
                  actual_seq_lengths_kv=None, attention_out=None, softmax_lse=None,
-                 kv_layout="PA_ND", learnable_sink=None):
+                 kv_layout="PA_ND", learnable_sink=None, key_antiquant_mode=0,
+                 value_antiquant_mode=0, key_antiquant_scale=None, value_antiquant_scale=None,
+                 key_antiquant_offset=None, value_antiquant_offset=None):
         L = lib()
         if attention_out is None:
             attention_out = torch.empty_like(query)
@@ -248,6 +256,15 @@ class AttentionPlan(_Plan):
         self._sink_desc = describe(learnable_sink) if learnable_sink is not None else None
         if self._sink_desc is not None:
             p.learnable_sink = ctypes.pointer(self._sink_desc)
+        p.key_antiquant_mode = key_antiquant_mode
+        p.value_antiquant_mode = value_antiquant_mode
+        self._aq = (key_antiquant_scale, value_antiquant_scale, key_antiquant_offset,
+                    value_antiquant_offset)
+        self._aq_descs = [describe(t) if t is not None else None for t in self._aq]
+        for name, d in zip(("key_antiquant_scale", "value_antiquant_scale", "key_antiquant_offset",
+                            "value_antiquant_offset"), self._aq_descs):
+            if d is not None:
+                setattr(p, name, ctypes.pointer(d))
         if self._lens[0] is not None:
             p.actual_seq_lengths = ctypes.cast(self._lens[0], ctypes.POINTER(ctypes.c_int64))
             p.actual_seq_lengths_len = self._lens[1]

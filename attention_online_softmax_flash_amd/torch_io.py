@@ -18,15 +18,41 @@ def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
     return t.to(device)
 
 
+def kv_to_device(arr: np.ndarray, case: DenseCase, device) -> torch.Tensor:
+    """Key / value rows: the query dtype, or fake-quantised int8 / e4m3fn codes."""
+    if case.kv_quant is None:
+        return to_device(arr, case.dtype, device)
+    t = torch.from_numpy(np.ascontiguousarray(arr))
+    if case.kv_quant["kind"] == "fp8":
+        t = t.view(torch.float8_e4m3fn)
+    return t.to(device)
+
+
+def antiquant_kwargs(case: DenseCase, device="cuda") -> dict:
+    """AttentionPlan keyword arguments of a fake-quantised case."""
+    aq = case.kv_quant
+    if aq is None:
+        return {}
+
+    def tens(x):
+        if x is None:
+            return None
+        return to_device(x, "bf16", device) if x.dtype == np.uint16 else torch.from_numpy(x).to(device)
+
+    return dict(key_antiquant_mode=aq["kmode"], value_antiquant_mode=aq["vmode"],
+                key_antiquant_scale=tens(aq["kscale"]), value_antiquant_scale=tens(aq["vscale"]),
+                key_antiquant_offset=tens(aq["koff"]), value_antiquant_offset=tens(aq["voff"]))
+
+
 def dense_tensors(case: DenseCase, device="cuda"):
     q = to_device(case.q, case.dtype, device)
     if case.paged:
-        k = to_device(case.k_pool, case.dtype, device)
-        v = to_device(case.v_pool, case.dtype, device)
+        k = kv_to_device(case.k_pool, case, device)
+        v = kv_to_device(case.v_pool, case, device)
         bt = torch.from_numpy(case.block_table).to(device)
     else:
-        k = to_device(case.k, case.dtype, device)
-        v = to_device(case.v, case.dtype, device)
+        k = kv_to_device(case.k, case, device)
+        v = kv_to_device(case.v, case, device)
         bt = None
     slopes = None if case.alibi_slopes is None else torch.from_numpy(case.alibi_slopes).to(device)
     return q, k, v, bt, slopes
@@ -53,7 +79,8 @@ def dense_plan(case: DenseCase, device="cuda", tensors=None, **overrides) -> fia
               actual_seq_lengths_kv=case.actual_seq_lengths_kv, kv_layout=case.kv_layout,
               atten_mask=mask_tensor(case, device),
               learnable_sink=(None if case.learnable_sink is None
-                              else to_device(case.learnable_sink, "bf16", device)))
+                              else to_device(case.learnable_sink, "bf16", device)),
+              **antiquant_kwargs(case, device))
     kw.update(overrides)
     return fia.AttentionPlan(q, k, v, **kw)
 

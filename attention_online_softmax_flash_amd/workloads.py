@@ -94,6 +94,9 @@ class DenseCase:
     atten_mask: Optional[np.ndarray] = None     # uint8 / bool, modes 0 / 1; != 0 masks out
     pse_bias: Optional[np.ndarray] = None       # [B or 1, Q_N, Q_S or 1, KV_S'] (pseType 0), q's dtype
     learnable_sink: Optional[np.ndarray] = None  # bf16 bits [Q_N]
+    # Fake-quantised key / value: k / v (or the pools) hold int8 or e4m3fn
+    # (uint8) codes; dict(kind, kmode, vmode, kscale, vscale, koff, voff).
+    kv_quant: Optional[dict] = None
     lse: bool = False
     seed: int = 0
 
@@ -151,6 +154,63 @@ def with_random_sink(case: DenseCase, seed: int, *, mean=0.0, std=2.0) -> DenseC
     rng = rng_for(seed)
     x = (mean + std * rng.standard_normal(case.num_heads)).astype(np.float32)
     return dataclasses.replace(case, name=case.name + "_sink", learnable_sink=f32_to_bf16_bits(x))
+
+
+def with_kv_quant(case: DenseCase, seed: int, *, kind="int8", kmode=0, vmode=0, offsets=False,
+                  per_tensor=False) -> DenseCase:
+    """The case with its key / value replaced by fake-quantised codes of the
+    same shape: int8 codes round(30 N(0,1)) clipped to [-128, 127], or e4m3fn
+    codes of 8 N(0,1); rows that were NaN-poisoned get code 127 (int8) or
+    0x7f (e4m3fn NaN).  Scales U(0.5, 1.5) / 32: per channel [KV_N, D] in
+    bf16 bits (fp32 when the key is per channel and the value per token), one
+    value (``per_tensor``), or per token fp32 [B, S2'] (S2' = S2 rounded up to
+    a multiple of 4).  ``offsets`` (int8 only): N(0, 3) in the scale's
+    layout and dtype."""
+    import torch  # e4m3fn encoding of the fp8 codes uses torch's CPU cast
+    rng = rng_for(seed)
+    B = case.batch
+    KVn, D = case.num_kv_heads, case.q.shape[-1]
+    if case.layout == "TND":
+        cum = [0] + [int(x) for x in case.actual_seq_lengths_kv]
+        S2 = max(cum[i + 1] - cum[i] for i in range(B))
+    else:
+        S2 = case.block_size * case.block_table.shape[1] if case.paged else case.k.shape[1]
+    S2p = max(4, -(-S2 // 4) * 4)
+
+    def codes(orig):
+        shape = orig.shape
+        if kind == "int8":
+            c = np.clip(np.rint(rng.standard_normal(shape) * 30.0), -128, 127).astype(np.int8)
+        else:
+            x = torch.from_numpy((rng.standard_normal(shape) * 8.0).astype(np.float32))
+            c = x.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+        if orig.dtype == np.uint16:
+            bad = (orig & np.uint16(0x7FFF)) > np.uint16(0x7F80)
+            c[bad] = 127 if kind == "int8" else 0x7F
+        return c
+
+    def table(mode, f32_chan):
+        if mode == 1:
+            sc = (rng.uniform(0.5, 1.5, (B, S2p)) / 32.0).astype(np.float32)
+            off = rng.normal(0.0, 3.0, (B, S2p)).astype(np.float32) if offsets else None
+            return sc, off
+        shape = (1,) if per_tensor else (KVn, D)
+        sc = (rng.uniform(0.5, 1.5, shape) / 32.0).astype(np.float32)
+        off = rng.normal(0.0, 3.0, shape).astype(np.float32) if offsets else None
+        if not f32_chan:
+            sc = f32_to_bf16_bits(sc)
+            off = None if off is None else f32_to_bf16_bits(off)
+        return sc, off
+
+    mixed = kmode == 0 and vmode == 1
+    kscale, koff = table(kmode, mixed)
+    vscale, voff = table(vmode, False)
+    q = dict(kind=kind, kmode=kmode, vmode=vmode, kscale=kscale, vscale=vscale, koff=koff, voff=voff)
+    if case.paged:
+        return dataclasses.replace(case, name=case.name + "_" + kind, k_pool=codes(case.k_pool),
+                                   v_pool=codes(case.v_pool), kv_quant=q)
+    return dataclasses.replace(case, name=case.name + "_" + kind, k=codes(case.k), v=codes(case.v),
+                               kv_quant=q)
 
 
 def as_bnnbsd(case: DenseCase) -> DenseCase:

@@ -140,6 +140,28 @@ typedef struct {
    * and +inf).  Requires inner_precise 0 and no pse (pse_type 0 without a
    * pse_shift tensor).  Device memory, read during phase 2. */
   const fia_tensor* learnable_sink;
+  /* Fake-quantised key / value (V5 quantisation parameter group, fake-quant
+   * scenario): key and value hold int8 or float8 e4m3fn codes (both the
+   * same), the query bf16; a code c is used as scale * (c + offset).
+   * Supported for query length 1 (the decode branch), D 64 / 128, without
+   * pse, explicit mask or learnable sink.  Modes (key, value): (0, 0) per
+   * channel, (1, 1) per token, (0, 1) key per channel and value per token;
+   * modes 2-6 are FIA_ERR_UNSUPPORTED.
+   *   per channel: scale bf16 (fp32 in mode (0, 1)) of shape (1, N, 1, D),
+   *     (1, N, D), (1, H), (N, 1, D), (N, D) or (H) with N = KV_N, H = KV_N*D,
+   *     contiguous; or (1): one scale for the whole tensor (int8 only).
+   *   per token: scale fp32 (B, >= S2) or (1, B, >= S2), S2 the key length
+   *     (block_table cols * block_size when paged), shared by the KV heads;
+   *     the last dim contiguous, the batch stride and the last extent
+   *     multiples of 4 and the data 16-byte aligned (else UNSUPPORTED).
+   * Offsets: NULL or the scale's dtype and shape, both key and value or
+   * neither, int8 only.  Paged: block_size a multiple of 32, <= 512. */
+  int32_t key_antiquant_mode;
+  int32_t value_antiquant_mode;
+  const fia_tensor* key_antiquant_scale;
+  const fia_tensor* value_antiquant_scale;
+  const fia_tensor* key_antiquant_offset;
+  const fia_tensor* value_antiquant_offset;
 } fia_params;
 
 /* Phase 1 of the dense / paged operator.

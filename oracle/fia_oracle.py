@@ -16,6 +16,12 @@ What it computes, and where each step is stated on the pages:
   P_S1, >= KV_S] with P_S1 >= Q_S or P_S1 = 1, in the query's dtype.
   Reading (no formula places it): like the full-mask ALiBi term it is added
   to the scaled scores, element [b or 0][h][i or 0][j] to score (i, j).
+* Fake-quantised key / value (V5 quantisation parameter group, fake-quant
+  scenario): int8 or e4m3fn codes c with per-channel scales / offsets
+  ([KV_N, D], or one value) or per-token ones ([B, S2], index = position
+  inside the batch's key sequence, shared by the KV heads).  Reading (the
+  dequantisation formula is not legible on the pages): value = scale *
+  (c + offset).
 * Learnable sink (V5 LearnableSink group: [Q_N], the query's dtype).  Same
   reading as the shared-KV sink: one extra logit per head with a zero value
   vector, not multiplied by the scale; the LSE includes it, so a live row
@@ -181,13 +187,49 @@ def gather_paged(pool: np.ndarray, table_row: np.ndarray, L: int, bs: int,
     return pool[blocks, j % bs]
 
 
+def decode_codes(c: np.ndarray, kind: str) -> np.ndarray:
+    """int8 or e4m3fn (uint8) codes -> float64, exactly."""
+    if kind == "int8":
+        return np.asarray(c, dtype=np.int8).astype(np.float64)
+    if kind == "fp8":
+        return decode_e4m3fn(np.asarray(c, dtype=np.uint8))
+    raise ValueError(kind)
+
+
+def _table_f64(x) -> np.ndarray:
+    """Scale / offset table: bf16 bit patterns (uint16) or fp32 values."""
+    x = np.asarray(x)
+    return decode_bf16(x) if x.dtype == np.uint16 else x.astype(np.float64)
+
+
+def dequant_rows(codes: np.ndarray, kind: str, mode: int, scale, offset, b: int) -> np.ndarray:
+    """Key / value codes [Lk, KV_N, D] of batch b -> scale * (code + offset),
+    float64.  mode 1: per token, scale[b][j] for the row at position j; mode
+    0: per channel scale[n][d], or the single value of a one-element table."""
+    c = decode_codes(codes, kind)
+    Lk, N, D = c.shape
+    sc = _table_f64(scale)
+    of = None if offset is None else _table_f64(offset)
+    if mode == 1:
+        sc2 = sc.reshape(-1, sc.shape[-1])
+        s = sc2[b, :Lk][:, None, None]
+        o = 0.0 if of is None else of.reshape(-1, of.shape[-1])[b, :Lk][:, None, None]
+    elif sc.size == 1:
+        s = float(sc.reshape(()))
+        o = 0.0 if of is None else float(of.reshape(()))
+    else:
+        s = sc.reshape(N, D)[None]
+        o = 0.0 if of is None else of.reshape(N, D)[None]
+    return s * (c + o)
+
+
 def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
         scale: float, sparse_mode: int = 0, pre_tokens: int = 2147483647,
         next_tokens: int = 2147483647, alibi_slopes=None, q_start_idx: int = 0,
         kv_start_idx: int = 0, actual_seq_lengths=None, actual_seq_lengths_kv=None,
         block_table=None, block_size: int = 0, k_pool=None, v_pool=None,
         kv_layout: str = "PA_ND", atten_mask=None, pse_shift=None, learnable_sink=None,
-        batches: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
+        kv_quant=None, batches: Optional[Sequence[int]] = None, heads: Optional[Sequence[int]] = None,
         rows: Optional[Sequence[int]] = None, row_chunk: int = 1024):
     """Fused inference attention, float64.
 
@@ -196,7 +238,8 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
     PA_ND [n_blk, bs, KV_N, D] (``kv_layout`` "BnNBsD": [n_blk, KV_N, bs, D])
     with ``block_table`` [B, >= max pages].  ``pse_shift``: pseType 0 bias
     [B or 1, Q_N, Q_S or 1, >= KV_S], encoded like q (``dtype``).
-    ``learnable_sink``: [Q_N] logits, encoded like q.
+    ``learnable_sink``: [Q_N] logits, encoded like q.  ``kv_quant``: dict(kind,
+    kmode, vmode, kscale, vscale, koff, voff) when k / v hold codes.
 
     Returns (out, lse) with out in the query layout (float64) and lse
     [B, Q_N, S1] (BSND) or [T, Q_N] (TND).  ``batches``/``heads``/``rows``
@@ -234,14 +277,20 @@ def fia(q, k, v, *, dtype: str, layout: str, num_heads: int, num_kv_heads: int,
     for b in (range(B) if batches is None else batches):
         Lq, Lk = q_len[b], kv_len[b]
         if paged:
-            kb = to_f64(gather_paged(k_pool, block_table[b], Lk, block_size, kv_layout), dtype)
-            vb = to_f64(gather_paged(v_pool, block_table[b], Lk, block_size, kv_layout), dtype)
+            kr = gather_paged(k_pool, block_table[b], Lk, block_size, kv_layout)
+            vr = gather_paged(v_pool, block_table[b], Lk, block_size, kv_layout)
         elif tnd:
-            kb = to_f64(k[kv_off[b]:kv_off[b + 1]], dtype)
-            vb = to_f64(v[kv_off[b]:kv_off[b + 1]], dtype)
+            kr = k[kv_off[b]:kv_off[b + 1]]
+            vr = v[kv_off[b]:kv_off[b + 1]]
         else:
-            kb = to_f64(k[b, :Lk], dtype)
-            vb = to_f64(v[b, :Lk], dtype)
+            kr = k[b, :Lk]
+            vr = v[b, :Lk]
+        if kv_quant is None:
+            kb, vb = to_f64(kr, dtype), to_f64(vr, dtype)
+        else:
+            aq = kv_quant
+            kb = dequant_rows(kr, aq["kind"], aq["kmode"], aq["kscale"], aq["koff"], b)
+            vb = dequant_rows(vr, aq["kind"], aq["vmode"], aq["vscale"], aq["voff"], b)
         qb = to_f64(q[q_off[b]:q_off[b + 1]] if tnd else q[b], dtype)   # [S, Q_N, D]
         S_rows = qb.shape[0]
         want = range(S_rows) if rows is None else [r for r in rows if r < S_rows]
@@ -298,7 +347,8 @@ def fia_case(case, **kw):
                kv_layout=getattr(case, "kv_layout", "PA_ND"),
                atten_mask=getattr(case, "atten_mask", None),
                pse_shift=getattr(case, "pse_bias", None),
-               learnable_sink=getattr(case, "learnable_sink", None), **kw)
+               learnable_sink=getattr(case, "learnable_sink", None),
+               kv_quant=getattr(case, "kv_quant", None), **kw)
 
 
 # ---------------------------------------------------------------------------

@@ -75,6 +75,14 @@ def P(**kw):
     if sink is not None:
         keep.append(sink)
         p.learnable_sink = ctypes.pointer(sink)
+    p.key_antiquant_mode = kw.pop("kmode", 0)
+    p.value_antiquant_mode = kw.pop("vmode", 0)
+    for name in ("key_antiquant_scale", "value_antiquant_scale", "key_antiquant_offset",
+                 "value_antiquant_offset"):
+        t = kw.pop(name, None)
+        if t is not None:
+            keep.append(t)
+            setattr(p, name, ctypes.pointer(t))
     assert not kw, kw
     p._keep = keep
     return p
@@ -362,6 +370,75 @@ def test_learnable_sink_rules():
     q3, k3, v3, o3 = dense(D=64, dt=fia.DT_FP32)
     st, _, _, msg = plan(P(num_kv_heads=2, learnable_sink=T((4,), fia.DT_FP32)), q3, k3, v3, o3)
     assert st == BAD, msg
+
+
+def test_fake_quant_kv_rules():
+    """V5 fake-quant group: int8 / e4m3fn key/value with a bf16 query, scales
+    per channel (query dtype; fp32 in the key-channel / value-token mode),
+    per tensor (int8) or per token (fp32 [B, >= S2]); offsets int8 only."""
+    B, S2, KVN, D = 2, 300, 2, 128
+    q = T((B, 1, 4, D))
+    o = T((B, 1, 4, D))
+    k8 = T((B, S2, KVN, D), fia.DT_INT8)
+    f8 = T((B, S2, KVN, D), fia.DT_FP8_E4M3FN)
+    chan = lambda dt=fia.DT_BF16: T((KVN, D), dt)
+    tok = lambda cols=300: T((B, cols), fia.DT_FP32)
+    ok = [
+        (k8, dict(key_antiquant_scale=chan(), value_antiquant_scale=chan())),
+        (k8, dict(key_antiquant_scale=chan(), value_antiquant_scale=chan(),
+                  key_antiquant_offset=chan(), value_antiquant_offset=chan())),
+        (k8, dict(key_antiquant_scale=T((1,)), value_antiquant_scale=T((1,)))),
+        (k8, dict(key_antiquant_scale=T((1, KVN, 1, D)), value_antiquant_scale=T((KVN * D,)))),
+        (f8, dict(kmode=1, vmode=1, key_antiquant_scale=tok(), value_antiquant_scale=tok(304))),
+        (k8, dict(kmode=1, vmode=1, key_antiquant_scale=T((1, B, 300), fia.DT_FP32),
+                  value_antiquant_scale=tok(), key_antiquant_offset=T((1, B, 300), fia.DT_FP32),
+                  value_antiquant_offset=tok())),
+        (k8, dict(kmode=0, vmode=1, key_antiquant_scale=chan(fia.DT_FP32), value_antiquant_scale=tok())),
+    ]
+    for kv, kw in ok:
+        st, kind, _, msg = plan(P(num_kv_heads=KVN, **kw), q, kv, kv, o)
+        assert st == 0 and kind == "decode", (kw.keys(), msg)
+    bad = [
+        (k8, dict(key_antiquant_scale=chan())),                                   # value scale missing
+        (k8, dict(kmode=1, vmode=0, key_antiquant_scale=tok(), value_antiquant_scale=chan())),
+        (k8, dict(kmode=7, vmode=7, key_antiquant_scale=chan(), value_antiquant_scale=chan())),
+        (k8, dict(key_antiquant_scale=chan(fia.DT_FP32), value_antiquant_scale=chan(fia.DT_FP32))),
+        (k8, dict(kmode=1, vmode=1, key_antiquant_scale=tok(296), value_antiquant_scale=tok())),
+        (k8, dict(kmode=1, vmode=1, key_antiquant_scale=T((B, 300)), value_antiquant_scale=tok())),
+        (k8, dict(key_antiquant_scale=chan(), value_antiquant_scale=chan(), key_antiquant_offset=chan())),
+        (f8, dict(key_antiquant_scale=chan(), value_antiquant_scale=chan(),
+                  key_antiquant_offset=chan(), value_antiquant_offset=chan())),
+        (f8, dict(key_antiquant_scale=T((1,)), value_antiquant_scale=T((1,)))),
+        (k8, dict(key_antiquant_scale=T((KVN, D + 1)), value_antiquant_scale=chan())),
+        (k8, dict(kmode=0, vmode=1, key_antiquant_scale=chan(), value_antiquant_scale=tok())),
+    ]
+    for kv, kw in bad:
+        st, _, _, msg = plan(P(num_kv_heads=KVN, **kw), q, kv, kv, o)
+        assert st == BAD, (kw.keys(), msg)
+    good = dict(key_antiquant_scale=chan(), value_antiquant_scale=chan())
+    st, _, _, msg = plan(P(num_kv_heads=KVN, kmode=2, vmode=2, **good), q, k8, k8, o)
+    assert st == UNS, msg
+    q2, o2 = T((B, 4, 4, D)), T((B, 4, 4, D))
+    st, _, _, msg = plan(P(num_kv_heads=KVN, **good), q2, k8, k8, o2)
+    assert st == UNS and "query length 1" in msg
+    st, _, _, msg = plan(P(num_kv_heads=KVN, learnable_sink=T((4,)), **good), q, k8, k8, o)
+    assert st == UNS
+    st, _, _, msg = plan(P(num_kv_heads=KVN, kmode=1, vmode=1, key_antiquant_scale=T((B, 302), fia.DT_FP32),
+                           value_antiquant_scale=T((B, 302), fia.DT_FP32)), q, k8, k8, o)
+    assert st == UNS and "aligned" in msg
+    st, _, _, msg = plan(P(num_kv_heads=KVN), q, k8, f8, o)
+    assert st == BAD
+    qb, kb, vb, ob = dense(S1=1, S2=300)
+    st, _, _, msg = plan(P(num_kv_heads=2, **good), qb, kb, vb, ob)
+    assert st == BAD and "int8 or fp8" in msg
+    pool = T((20, 16, KVN, D), fia.DT_INT8)
+    st, _, _, msg = plan(P(num_kv_heads=KVN, block_size=16, actual_seq_lengths_kv=[30, 40], **good), q, pool,
+                         pool, o, bt=T((B, 4), fia.DT_INT32))
+    assert st == BAD and "block_size" in msg
+    pool = T((20, 32, KVN, D), fia.DT_INT8)
+    st, kind, _, msg = plan(P(num_kv_heads=KVN, block_size=32, actual_seq_lengths_kv=[30, 40], **good), q,
+                            pool, pool, o, bt=T((B, 4), fia.DT_INT32))
+    assert st == 0 and kind == "decode", msg
 
 
 def test_tnd_rules():

@@ -280,6 +280,45 @@ def test_decode_learnable_sink():
     dense_parity(W.with_random_sink(case, 834, mean=2.0), "decode")
 
 
+FAKE_QUANT_CASES = [
+    # (name, kind, kmode, vmode, offsets, per_tensor, builder)
+    ("i8_chan_off_paged", "int8", 0, 0, True, False,
+     lambda: W.paged_decode_case("fq0", 850, B=3, Q_N=32, KV_N=8, D=128, kv_lens=[1, 700, 5000],
+                                 block_size=128, lse=True, poison_tail=True, extra_blocks=2)),
+    ("i8_token_off_dense_d64", "int8", 1, 1, True, False,
+     lambda: W.dense_case("fq1", 851, B=3, S1=1, S2=1030, Q_N=8, KV_N=2, D=64,
+                          kv_lens=[1030, 33, 512], lse=True, poison_pad=True)),
+    ("fp8_chan_bnnbsd", "fp8", 0, 0, False, False,
+     lambda: W.as_bnnbsd(W.paged_decode_case("fq2", 852, B=2, Q_N=16, KV_N=4, D=128,
+                                             kv_lens=[2049, 300], block_size=64, lse=True,
+                                             poison_tail=True))),
+    ("fp8_token_paged32", "fp8", 1, 1, False, False,
+     lambda: W.paged_decode_case("fq3", 853, B=2, Q_N=8, KV_N=1, D=128, kv_lens=[77, 1500],
+                                 block_size=32, lse=True, poison_tail=True, extra_blocks=1)),
+    ("i8_mixed_off", "int8", 0, 1, True, False,
+     lambda: W.paged_decode_case("fq4", 854, B=2, Q_N=64, KV_N=2, D=128, kv_lens=[900, 1800],
+                                 block_size=128, lse=True, poison_tail=True)),
+    ("i8_tensor", "int8", 0, 0, True, True,
+     lambda: W.dense_case("fq5", 855, B=2, S1=1, S2=640, Q_N=4, KV_N=4, D=128, kv_lens=[640, 7],
+                          lse=True, poison_pad=True)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(FAKE_QUANT_CASES)))
+def test_decode_fake_quant_kv(i):
+    """Fake-quantised int8 / e4m3fn key/value rows (scale * (code + offset))."""
+    name, kind, km, vm, off, pt, build = FAKE_QUANT_CASES[i]
+    case = W.with_kv_quant(build(), 860 + i, kind=kind, kmode=km, vmode=vm, offsets=off,
+                           per_tensor=pt)
+    dense_parity(case, "decode")
+
+
+def test_decode_fake_quant_tnd():
+    case = W.tnd_case("fqt", 870, q_lens=[1, 1, 0, 1], kv_lens=[600, 5, 100, 1029], Q_N=8, KV_N=2,
+                      D=128, lse=True)
+    dense_parity(W.with_kv_quant(case, 871, kind="fp8", kmode=1, vmode=1), "decode")
+
+
 BNNBSD_DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size)
     (3, 32, 8, 128, [1, 511, 1300], 128),

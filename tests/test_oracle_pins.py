@@ -578,6 +578,98 @@ def test_learnable_sink_empty_rows_give_zero_and_the_sink():
     assert np.all(out_e == 0) and np.all(np.isposinf(lse_e))
 
 
+def _quant_case(kind, kmode, vmode, offsets=False, per_tensor=False, seed=95):
+    c = W.dense_case("fq", seed, B=2, S1=1, S2=9, Q_N=4, KV_N=2, D=8, dtype="bf16", lse=True,
+                     kv_lens=[9, 5])
+    return W.with_kv_quant(c, seed + 1, kind=kind, kmode=kmode, vmode=vmode, offsets=offsets,
+                           per_tensor=per_tensor)
+
+
+def test_fake_quant_unit_scale_equals_plain_attention_on_the_codes():
+    """Scale 1 and no offset: the codes themselves are the key / value
+    values (int8 through numpy's integer conversion, e4m3fn through torch's
+    float8 cast)."""
+    for kind in ("int8", "fp8"):
+        c = _quant_case(kind, 0, 0)
+        one = W.f32_to_bf16_bits(np.ones((2, 8), np.float32))
+        aq = dict(c.kv_quant, kscale=one, vscale=one)
+        out, lse = O.fia_case(dataclasses.replace(c, kv_quant=aq))
+        if kind == "int8":
+            kf, vf = c.k.astype(np.float64), c.v.astype(np.float64)
+        else:
+            kf = torch.from_numpy(c.k).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            vf = torch.from_numpy(c.v).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+        for b, L in enumerate((9, 5)):
+            want = sdpa(O.decode_bf16(c.q[b]), kf[b, :L], vf[b, :L], c.scale, gqa=True)
+            np.testing.assert_allclose(out[b], want, rtol=1e-11, atol=1e-12)
+
+
+def test_fake_quant_offset_cancelling_the_codes_gives_uniform_softmax():
+    """Key codes constant per channel with offset = -code: every key
+    dequantises to 0, so the softmax is uniform (LSE = ln n) and the output
+    is the mean of the dequantised values.  Distinguishes scale * (c + o)
+    from scale * (c - o)."""
+    c = _quant_case("int8", 0, 0, offsets=True)
+    k = np.empty_like(c.k)
+    const = np.arange(-8, 8, dtype=np.int8).reshape(2, 8)
+    k[...] = const[None, None]
+    koff = W.f32_to_bf16_bits(-const.astype(np.float32))
+    aq = dict(c.kv_quant, koff=koff)
+    out, lse = O.fia_case(dataclasses.replace(c, k=k, kv_quant=aq))
+    vs = O.decode_bf16(aq["vscale"])
+    vo = O.decode_bf16(aq["voff"])
+    for b, L in enumerate((9, 5)):
+        vdq = vs[None] * (c.v[b, :L].astype(np.float64) + vo[None])       # [L, KV_N, D]
+        for h in range(4):
+            np.testing.assert_allclose(out[b, 0, h], vdq[:, h // 2].mean(axis=0), rtol=1e-12, atol=1e-13)
+            assert abs(lse[b, h, 0] - math.log(L)) < 1e-12
+
+
+def test_fake_quant_modes_agree_on_a_constant_scale():
+    """A scale (and offset) equal everywhere gives the same result per
+    tensor, per channel and per token."""
+    base = _quant_case("int8", 0, 0, offsets=True)
+    s, o = np.float32(0.046875), np.float32(-1.5)
+    bits = lambda x, shape: W.f32_to_bf16_bits(np.full(shape, x, np.float32))
+    variants = [
+        dict(kmode=0, vmode=0, kscale=bits(s, (1,)), vscale=bits(s, (1,)), koff=bits(o, (1,)),
+             voff=bits(o, (1,))),
+        dict(kmode=0, vmode=0, kscale=bits(s, (2, 8)), vscale=bits(s, (2, 8)), koff=bits(o, (2, 8)),
+             voff=bits(o, (2, 8))),
+        dict(kmode=1, vmode=1, kscale=np.full((2, 12), s), vscale=np.full((2, 12), s),
+             koff=np.full((2, 12), o), voff=np.full((2, 12), o)),
+        dict(kmode=0, vmode=1, kscale=np.full((2, 8), s), vscale=np.full((2, 12), s),
+             koff=np.full((2, 8), o), voff=np.full((2, 12), o)),
+    ]
+    res = [O.fia_case(dataclasses.replace(base, kv_quant=dict(base.kv_quant, **v))) for v in variants]
+    for out, lse in res[1:]:
+        np.testing.assert_allclose(out, res[0][0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(lse, res[0][1], rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("kmode,vmode", [(0, 0), (1, 1), (0, 1)])
+def test_fake_quant_axes_against_sdpa(kmode, vmode):
+    """Per-channel tables index [kv head][d], per-token tables [batch][key
+    position]: torch SDPA on tensors dequantised with torch broadcasting."""
+    c = _quant_case("int8", kmode, vmode, offsets=True, seed=97)
+    aq = c.kv_quant
+    out, lse = O.fia_case(c)
+
+    def deq(codes, mode, sc, of, b, L):
+        x = torch.from_numpy(codes[b, :L].astype(np.float64))          # [L, N, D]
+        sc = O._table_f64(sc)
+        of = O._table_f64(of)
+        if mode == 1:
+            return _t(sc[b, :L])[:, None, None] * (x + _t(of[b, :L])[:, None, None])
+        return _t(sc.reshape(2, 8))[None] * (x + _t(of.reshape(2, 8))[None])
+
+    for b, L in enumerate((9, 5)):
+        kd = deq(c.k, kmode, aq["kscale"], aq["koff"], b, L).numpy()
+        vd = deq(c.v, vmode, aq["vscale"], aq["voff"], b, L).numpy()
+        want = sdpa(O.decode_bf16(c.q[b]), kd, vd, c.scale, gqa=True)
+        np.testing.assert_allclose(out[b], want, rtol=1e-11, atol=1e-12)
+
+
 def test_split_keys_merge_by_lse_reproduces_full():
     """Partial results over disjoint key ranges combine through their LSE
     (V2 softmaxLse restrictions: the ring-attention composition)."""
