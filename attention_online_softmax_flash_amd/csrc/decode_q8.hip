@@ -55,6 +55,37 @@ __device__ __forceinline__ float code_f32(uint32_t w, int k) {
   }
 }
 
+// Bytes 2 i and 2 i + 1 of w as a packed bf16 pair (e4m3fn codes; the
+// conversion is exact).
+template <int I>
+__device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, I == 1));
+}
+
+// Key operand: 8 codes (words w0, w1, bytes in order) as 8 bf16.
+template <bool FP8>
+__device__ __forceinline__ u32x4 codes8_bf16(uint32_t w0, uint32_t w1) {
+  if constexpr (FP8) {
+    return u32x4{fp8_pair_bf16<0>(w0), fp8_pair_bf16<1>(w0), fp8_pair_bf16<0>(w1), fp8_pair_bf16<1>(w1)};
+  } else {
+    return u32x4{pack_bf16x2(code_byte<false, 0>(w0), code_byte<false, 1>(w0)),
+                 pack_bf16x2(code_byte<false, 2>(w0), code_byte<false, 3>(w0)),
+                 pack_bf16x2(code_byte<false, 0>(w1), code_byte<false, 1>(w1)),
+                 pack_bf16x2(code_byte<false, 2>(w1), code_byte<false, 3>(w1))};
+  }
+}
+
+// Byte k of x and byte k of y as a packed bf16 pair (x low).
+template <bool FP8>
+__device__ __forceinline__ uint32_t pair_bf16(uint32_t x, uint32_t y, int k) {
+  if constexpr (FP8) {
+    const uint32_t sel = (uint32_t)k | ((uint32_t)(4 + k) << 8) | 0x0c0c0000u;
+    return fp8_pair_bf16<0>(__builtin_amdgcn_perm(y, x, sel));
+  } else {
+    return pack_bf16x2(code_f32<false>(x, k), code_f32<false>(y, k));
+  }
+}
+
 // Split x into a bf16 high part and a bf16 low part (x - hi), as bits.
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
   const uint32_t h = pack_bf16x2(x, 0.f) & 0xffffu;
@@ -66,7 +97,7 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 
 // KPT / VPT: key / value scales per token (else per channel).
 template <int D, bool FP8, bool KPT, bool VPT>
-__global__ __launch_bounds__(256, 2) void decode_split_q8(AttnArgs a) {
+__global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide k-steps of the score product per 16-key half
   constexpr int DPL = D / 16;  // value columns per lane column
   constexpr int KB = D / 4;    // key bytes per lane and row
@@ -228,10 +259,7 @@ __global__ __launch_bounds__(256, 2) void decode_split_q8(AttnArgs a) {
           // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
           const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
           const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
-          const u32x4 kop8 = {pack_bf16x2(code_f32<FP8>(w0, 0), code_f32<FP8>(w0, 1)),
-                              pack_bf16x2(code_f32<FP8>(w0, 2), code_f32<FP8>(w0, 3)),
-                              pack_bf16x2(code_f32<FP8>(w1, 0), code_f32<FP8>(w1, 1)),
-                              pack_bf16x2(code_f32<FP8>(w1, 2), code_f32<FP8>(w1, 3))};
+          const u32x4 kop8 = codes8_bf16<FP8>(w0, w1);
           sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
           if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
         }
@@ -253,9 +281,19 @@ __global__ __launch_bounds__(256, 2) void decode_split_q8(AttnArgs a) {
         mx = fmaxf(mx, x[s]);
       }
       mx = pair32_max(pair16_max(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
+      // Lazy rescale: the running max moves only when a head's new max
+      // exceeds it by more than 8 (probabilities stay <= 2^8).
+      const bool grow = mx > m_run + 8.f;
+      if (__any(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+        t_run *= alpha;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+      }
+      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
       float p[8];
       float psum = 0.f, tsum = 0.f;
 #pragma unroll
@@ -271,20 +309,16 @@ __global__ __launch_bounds__(256, 2) void decode_split_q8(AttnArgs a) {
           p[s] = pv;
         }
       }
-      l_run = l_run * alpha + psum;
-      t_run = t_run * alpha + tsum;
-      m_run = m_new;
+      l_run += psum;
+      t_run += tsum;
       const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                         pack_bf16x2(p[6], p[7])};
 #pragma unroll
       for (int e = 0; e < DPL; ++e) {
-        o[e] *= alpha;
         // byte e of the lane's DPL value bytes of each of the 8 keys
         const int w = e >> 2, k = e & 3;
-        const u32x4 av = {pack_bf16x2(code_f32<FP8>(vr[0][w], k), code_f32<FP8>(vr[1][w], k)),
-                          pack_bf16x2(code_f32<FP8>(vr[2][w], k), code_f32<FP8>(vr[3][w], k)),
-                          pack_bf16x2(code_f32<FP8>(vr[4][w], k), code_f32<FP8>(vr[5][w], k)),
-                          pack_bf16x2(code_f32<FP8>(vr[6][w], k), code_f32<FP8>(vr[7][w], k))};
+        const u32x4 av = {pair_bf16<FP8>(vr[0][w], vr[1][w], k), pair_bf16<FP8>(vr[2][w], vr[3][w], k),
+                          pair_bf16<FP8>(vr[4][w], vr[5][w], k), pair_bf16<FP8>(vr[6][w], vr[7][w], k)};
         o[e] = mfma16(av, pb, o[e]);
       }
     }

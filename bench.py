@@ -66,7 +66,16 @@ def decode_bytes(case):
     D, kvn, qn = case.q.shape[-1], case.num_kv_heads, case.num_heads
     B = case.q.shape[0]
     L = case.actual_seq_lengths_kv
-    kv = sum(L) * kvn * D * 2 * 2
+    aq = getattr(case, "kv_quant", None)
+    if aq is None:
+        kv = sum(L) * kvn * D * 2 * 2
+    else:
+        # one byte per code; per-token tables are read once per visible key
+        # (shared by the KV heads), per-channel tables once
+        kv = sum(L) * kvn * D * 2
+        for mode, sc, of in ((aq["kmode"], aq["kscale"], aq["koff"]), (aq["vmode"], aq["vscale"], aq["voff"])):
+            per = (sum(L) * 4) if mode == 1 else sc.nbytes
+            kv += per * (2 if of is not None else 1)
     q = B * qn * D * 2
     o = q
     lse = B * qn * 4 if case.lse else 0
@@ -189,7 +198,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "next", "copy"], default="all",
+    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "next", "c3q", "copy"], default="all",
                     help="limit the run to one workload (profiling); 'copy' runs a plain 1 GiB "
                          "device copy, the calibration of the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -347,6 +356,29 @@ def main():
             "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
         del plan
+
+    if want("c3q"):
+        # The paged GQA decode with a fake-quantised KV cache (one byte per
+        # element): int8 codes with per-token scales and offsets, and e4m3fn
+        # codes with per-channel scales.
+        case = W.c3_paged_decode()
+        for key, kind, km, off in (("paged_decode_int8_per_token", "int8", 1, True),
+                                   ("paged_decode_fp8_per_channel", "fp8", 0, False)):
+            qc = W.with_kv_quant(case, 1007, kind=kind, kmode=km, vmode=km, offsets=off)
+            nbytes = decode_bytes(qc)
+            plan = TI.dense_plan(qc, dev)
+            _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
+            gbs = nbytes / (kern_ms / 1000.0) / 1e9
+            what = ("int8 codes, per-token fp32 scales and offsets" if kind == "int8"
+                    else "e4m3fn codes, per-channel bf16 scales")
+            components[key] = {
+                "workload": "the paged GQA decode above with a fake-quantised KV cache: " + what,
+                "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
+                "ms": round(kern_ms, 5), "kernels": "decode_split_q8<128> + decode_merge<128>",
+                "tokens_per_s": round(case.q.shape[0] / (kern_ms / 1000.0), 1),
+                "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+            del plan, qc
+        del case
 
     if line is None:
         line = {"metric": "decode attention HBM GB/s + prefill attention TFLOP/s, bf16, 1 MI355X",
