@@ -9,10 +9,13 @@
 // split-KV kernel, so the bf16 merge kernel folds the partials.  The scales
 // and offsets are moved out of the MFMA operands:
 //   * key, per channel:  s_j = sum_d (q_d ks_d) c_jd + sum_d q_d ks_d ko_d.  The
-//     first term is an MFMA of the codes (exact in bf16) against q * ks split
-//     into a bf16 high and low part (two products, so the scaled query keeps
-//     about 16 bits); the second is one constant per head.
-//   * key, per token:    s_j = ks_j (q . c_j + ko_j sum_d q_d).
+//     first term is a product of the raw codes against q * ks carried with
+//     about 16 bits: int8 codes go into the int8 MFMA as loaded, against
+//     q * ks = sq (qi + qj / 256) with int8 qi, qj; e4m3fn codes are
+//     converted to bf16 (exact) against a bf16 high and low part of q * ks.
+//     The second term is one constant per head.
+//   * key, per token:    s_j = ks_j (q . c_j + ko_j sum_d q_d), q . c_j the same
+//     product with ks = 1.
 //   * value, per channel: o_d = vs_d (sum_j p_j c_jd / l + vo_d), applied to the
 //     normalised chunk result (the merge is a convex combination, so it
 //     commutes with this per-channel affine map).
@@ -26,6 +29,8 @@
 namespace fia {
 
 namespace {
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 // Element i of a per-channel scale / offset (bf16 or fp32; one element for
 // the whole tensor when `scalar`), 0 without a tensor.
@@ -62,17 +67,11 @@ __device__ __forceinline__ uint32_t fp8_pair_bf16(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, I == 1));
 }
 
-// Key operand: 8 codes (words w0, w1, bytes in order) as 8 bf16.
+// Key operand: 8 e4m3fn codes (words w0, w1, bytes in order) as 8 bf16.
 template <bool FP8>
 __device__ __forceinline__ u32x4 codes8_bf16(uint32_t w0, uint32_t w1) {
-  if constexpr (FP8) {
-    return u32x4{fp8_pair_bf16<0>(w0), fp8_pair_bf16<1>(w0), fp8_pair_bf16<0>(w1), fp8_pair_bf16<1>(w1)};
-  } else {
-    return u32x4{pack_bf16x2(code_byte<false, 0>(w0), code_byte<false, 1>(w0)),
-                 pack_bf16x2(code_byte<false, 2>(w0), code_byte<false, 3>(w0)),
-                 pack_bf16x2(code_byte<false, 0>(w1), code_byte<false, 1>(w1)),
-                 pack_bf16x2(code_byte<false, 2>(w1), code_byte<false, 3>(w1))};
-  }
+  static_assert(FP8, "int8 key codes feed the int8 MFMA directly");
+  return u32x4{fp8_pair_bf16<0>(w0), fp8_pair_bf16<1>(w0), fp8_pair_bf16<0>(w1), fp8_pair_bf16<1>(w1)};
 }
 
 // Byte k of x and byte k of y as a packed bf16 pair (x low).
@@ -129,34 +128,53 @@ __global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(Att
   const bool hvalid = hl < a.G;
   const int h = kvh * a.G + (hvalid ? hl : 0);
 
-  // Query of head n at d = KB g + 8 cc + e, as the B operand: the bf16 query
-  // itself (key per token), or q * ks split into high and low parts (key per
-  // channel).  qc: the per-head constant of the scores (log2 units), or, per
-  // token, sum_d q_d.
+  // Query of head n at d = KB g + i (i < KB) -- the same permutation of d as
+  // the key codes -- times the per-channel key scale (key per channel).  qc:
+  // sum_d q_d ks_d ko_d (key per channel), or sum_d q_d (key per token).
   const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb + (int64_t)q_off * a.q_ss +
                        (int64_t)h * a.q_sh + KB * g;
-  u32x4 qh[NC], ql[NC];
+  float qf[KB];
   float qc = 0.f;
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     const u32x4 raw = hvalid ? ld16(qp + 8 * cc) : u32x4{0, 0, 0, 0};
-    if constexpr (KPT) {
-      qh[cc] = raw;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t w = raw[e >> 1];
-        qc += bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = raw[e >> 1];
+      const float qd = bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
+      if constexpr (KPT) {
+        qf[8 * cc + e] = qd;
+        qc += qd;
+      } else {
+        const int ch = kvh * D + KB * g + 8 * cc + e;
+        qf[8 * cc + e] = qd * chan_val(a.kq_scale, a.kq_f32, a.kq_scalar, ch);
+        qc += qf[8 * cc + e] * chan_val(a.kq_off, a.kq_f32, a.kq_scalar, ch);
       }
-    } else {
+    }
+  }
+  // Sum over the four lanes of head n (lanes n, n + 16, n + 32, n + 48).
+  qc += shfl_xor_f(qc, 16);
+  qc += shfl_xor_f(qc, 32);
+  // B operand of the score product.
+  //  e4m3fn keys: bf16 MFMA; the query (scaled query: high and low bf16
+  //    parts) as 8 bf16 per k-step cc.
+  //  int8 keys: int8 MFMA on the raw codes; the query as sq * (qi + qj / 256)
+  //    with int8 qi, qj (sq = max |q| / 127 per head), i.e. about 16 bits.
+  u32x4 qh[NC], ql[NC];
+  u32x4 qi[KB / 16], qj[KB / 16];
+  float sq = 0.f;
+  if constexpr (FP8) {
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc) {
       uint32_t hbits[8], lbits[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const uint32_t w = raw[e >> 1];
-        const float qd = bf16_to_f32((uint16_t)((e & 1) ? (w >> 16) : (w & 0xffffu)));
-        const int ch = kvh * D + KB * g + 8 * cc + e;
-        const float qs = qd * chan_val(a.kq_scale, a.kq_f32, a.kq_scalar, ch);
-        split_bf16(qs, hbits[e], lbits[e]);
-        qc += qs * chan_val(a.kq_off, a.kq_f32, a.kq_scalar, ch);
+        if constexpr (KPT) {
+          hbits[e] = pack_bf16x2(qf[8 * cc + e], 0.f) & 0xffffu;   // the bf16 query itself
+          lbits[e] = 0u;
+        } else {
+          split_bf16(qf[8 * cc + e], hbits[e], lbits[e]);
+        }
       }
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
@@ -164,10 +182,32 @@ __global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(Att
         ql[cc][w] = lbits[2 * w] | (lbits[2 * w + 1] << 16);
       }
     }
+  } else {
+    float mabs = 0.f;
+#pragma unroll
+    for (int i = 0; i < KB; ++i) mabs = fmaxf(mabs, fabsf(qf[i]));
+    mabs = fmaxf(mabs, shfl_xor_f(mabs, 16));
+    mabs = fmaxf(mabs, shfl_xor_f(mabs, 32));
+    sq = mabs > 0.f ? mabs * (1.f / 127.f) : 1.f;
+    const float rq = 1.f / sq;
+#pragma unroll
+    for (int c4 = 0; c4 < KB / 16; ++c4) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        uint32_t hw = 0u, lw = 0u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float x = qf[16 * c4 + 4 * w + k] * rq;
+          const float xh = __builtin_rintf(x);
+          const float xl = fminf(fmaxf(__builtin_rintf((x - xh) * 256.f), -127.f), 127.f);
+          hw |= ((uint32_t)(int32_t)xh & 0xffu) << (8 * k);
+          lw |= ((uint32_t)(int32_t)xl & 0xffu) << (8 * k);
+        }
+        qi[c4][w] = hw;
+        qj[c4][w] = lw;
+      }
+    }
   }
-  // Sum over the four lanes of head n (lanes n, n + 16, n + 32, n + 48).
-  qc += shfl_xor_f(qc, 16);
-  qc += shfl_xor_f(qc, 32);
   const float c_shift = KPT ? 0.f : qc * a.scale_log2;
 
   float m_run = kNegInf;
@@ -253,15 +293,28 @@ __global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(Att
       f32x4 sc[2];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (FP8) {
+          sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc) {
-          // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
-          const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
-          const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
-          const u32x4 kop8 = codes8_bf16<FP8>(w0, w1);
-          sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
-          if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
+          for (int cc = 0; cc < NC; ++cc) {
+            // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
+            const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
+            const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
+            const u32x4 kop8 = codes8_bf16<true>(w0, w1);
+            sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
+            if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
+          }
+        } else {
+          // 16 key bytes per lane and product: the loaded pieces as they are.
+          i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
+#pragma unroll
+          for (int c4 = 0; c4 < KB / 16; ++c4) {
+            const i32x4 kc = __builtin_bit_cast(i32x4, kw[hf][c4]);
+            ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qi[c4]), ah, 0, 0, 0);
+            al = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qj[c4]), al, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sc[hf][r] = sq * __builtin_fmaf((float)al[r], 1.f / 256.f, (float)ah[r]);
         }
       }
       float x[8];

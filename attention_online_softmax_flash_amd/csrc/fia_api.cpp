@@ -938,12 +938,15 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
       }
     }
   } else if (e->kind == KIND_DECODE) {
+    // Keys per chunk: one-byte codes move half the bytes per key, so their
+    // chunks are twice as long (the same bytes per work item).
+    const int64_t chunk = kvq ? 2 * kDecodeChunk : kDecodeChunk;
     int64_t total_chunks = 0;
     for (int64_t b = 0; b < B; ++b) {
       int32_t* r = &e->meta[(size_t)b * fia::BF_COUNT];
       int64_t lo = 0, hi = 0;
       if (qlen[b] >= 1) visible(mode, 0, qlen[b], kvlen[b], p->pre_tokens, p->next_tokens, &lo, &hi);
-      const int64_t nch = hi > lo ? (hi + kDecodeChunk - 1) / kDecodeChunk - lo / kDecodeChunk : 0;
+      const int64_t nch = hi > lo ? (hi + chunk - 1) / chunk - lo / chunk : 0;
       r[fia::BF_LO] = (int32_t)lo;
       r[fia::BF_HI] = (int32_t)hi;
       r[fia::BF_NCHUNK] = (int32_t)nch;
@@ -957,7 +960,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
         e->meta.push_back(c);
       }
     }
-    a.chunk = kDecodeChunk;
+    a.chunk = (int32_t)chunk;
     a.n_head_blocks = (a.G + 15) / 16;
     const int64_t n_items = total_chunks * KVn * a.n_head_blocks;
     if (n_items > INT32_MAX) {

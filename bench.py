@@ -362,15 +362,20 @@ def main():
         # element): int8 codes with per-token scales and offsets, and e4m3fn
         # codes with per-channel scales.
         case = W.c3_paged_decode()
-        for key, kind, km, off in (("paged_decode_int8_per_token", "int8", 1, True),
-                                   ("paged_decode_fp8_per_channel", "fp8", 0, False)):
+        for key, kind, km, off, bn in (("paged_decode_int8_per_token", "int8", 1, True, False),
+                                       ("paged_decode_fp8_per_channel", "fp8", 0, False, False),
+                                       ("paged_decode_int8_per_token_bnnbsd", "int8", 1, True, True)):
             qc = W.with_kv_quant(case, 1007, kind=kind, kmode=km, vmode=km, offsets=off)
+            if bn:
+                qc = W.as_bnnbsd(qc)
             nbytes = decode_bytes(qc)
             plan = TI.dense_plan(qc, dev)
             _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
             gbs = nbytes / (kern_ms / 1000.0) / 1e9
             what = ("int8 codes, per-token fp32 scales and offsets" if kind == "int8"
                     else "e4m3fn codes, per-channel bf16 scales")
+            if bn:
+                what += ", pools in BnNBsD order [n_blocks, KV_N, 128, D]"
             components[key] = {
                 "workload": "the paged GQA decode above with a fake-quantised KV cache: " + what,
                 "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
