@@ -188,6 +188,11 @@ def cpu_baseline(case, flops):
                       "heads), float64 numpy with materialised scores"}
 
 
+def progress(what):
+    """One line on stderr per workload, so a long run shows it is alive."""
+    print(f"[bench] {what} ...", file=sys.stderr, flush=True)
+
+
 def roofline(bound, achieved, peak, unit, traffic):
     return {"bound": bound, "achieved": round(achieved, 3), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic}
@@ -232,6 +237,7 @@ def main():
     line = None
 
     if want("c2"):
+        progress("c2")
         case = W.c2_causal_gqa()
         flops = dense_flops(case)
         t0 = time.perf_counter()
@@ -262,6 +268,7 @@ def main():
         del plan, tensors
 
     if want("c3"):
+        progress("c3")
         case = W.c3_paged_decode()
         nbytes = decode_bytes(case)
         plan = TI.dense_plan(case, dev)
@@ -291,6 +298,7 @@ def main():
         del plan, case_b
 
     if want("c4"):
+        progress("c4")
         case = W.c4_alibi_prefill()
         flops = dense_flops(case)
         plan = TI.dense_plan(case, dev)
@@ -304,6 +312,7 @@ def main():
         del plan
 
     if want("c5"):
+        progress("c5")
         case = W.c5_sparse_sharedkv()
         nbytes = sparse_bytes(case)
         plan = TI.sparse_plan(case, dev)
@@ -319,6 +328,7 @@ def main():
         del plan
 
     if want("next"):
+        progress("next")
         # The causal GQA prefill workload with the inputs of the mask / bias /
         # sink parameter groups, and the heavily compressed sparse mode.
         base = W.c2_causal_gqa()
@@ -358,6 +368,7 @@ def main():
         del plan
 
     if want("c3q"):
+        progress("c3q")
         # The paged GQA decode with a fake-quantised KV cache (one byte per
         # element): int8 codes with per-token scales and offsets, and e4m3fn
         # codes with per-channel scales.
