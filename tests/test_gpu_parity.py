@@ -2,6 +2,8 @@
 on identical seeded inputs, at the bar of the parity contract:
 bf16 outputs |gpu - ref| <= 1e-2 + 1e-2 |ref|, LSE within 1e-3 absolute with
 +inf matching exactly, gathers and sparse row selection bit-exact."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -311,6 +313,35 @@ def test_decode_fake_quant_kv(i):
     case = W.with_kv_quant(build(), 860 + i, kind=kind, kmode=km, vmode=vm, offsets=off,
                            per_tensor=pt)
     dense_parity(case, "decode")
+
+
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_decode_fake_quant_every_code_is_exact(kind):
+    """Every code, one per batch entry with a single key: the output is the
+    value code itself (exact in bf16) and the LSE is scale * key code (query
+    e_0, scale 1 tables), so a wrong or flushed conversion of any code shows.
+    e4m3fn NaN codes (0x7f, 0xff) are left out."""
+    codes = np.arange(256)
+    if kind == "fp8":
+        codes = codes[(codes & 0x7F) != 0x7F]
+    B, D = codes.size, 128
+    case = W.dense_case("fqx", 880, B=B, S1=1, S2=4, Q_N=1, KV_N=1, D=D, kv_lens=[1] * B, lse=True,
+                        scale=0.5)
+    q = np.zeros_like(case.q)
+    q[..., 0] = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    case = W.with_kv_quant(dataclasses.replace(case, q=q), 881, kind=kind, kmode=0, vmode=0)
+    dt = np.int8 if kind == "int8" else np.uint8
+    k = np.zeros(case.k.shape, dtype=dt)
+    v = np.zeros(case.v.shape, dtype=dt)
+    k[:, 0, 0, 0] = codes.astype(np.uint8).view(dt)
+    v[:, 0, 0, :] = codes.astype(np.uint8).view(dt)[:, None]
+    one = W.f32_to_bf16_bits(np.ones((1, D), np.float32))
+    case = dataclasses.replace(case, k=k, v=v, kv_quant=dict(case.kv_quant, kscale=one, vscale=one))
+    plan = run_plan(TI.dense_plan(case, DEV))
+    out, lse = gpu_results(plan)
+    want = O.decode_codes(codes.astype(np.uint8).view(dt), kind)
+    np.testing.assert_array_equal(out[:, 0, 0, :], np.repeat(want[:, None], D, axis=1))
+    np.testing.assert_allclose(lse[:, 0, 0], 0.5 * want, rtol=2e-6, atol=1e-9)
 
 
 def test_decode_fake_quant_tnd():
