@@ -1027,7 +1027,8 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   const int64_t B = q->shape[0], S1 = q->shape[1], N1 = q->shape[2];
   if (q->shape[3] != fia::kSparseD) return fail(FIA_ERR_PARAM_INVALID, "q head dim must be 512");
   if (N1 != 64 && N1 != 128) return fail(FIA_ERR_PARAM_INVALID, "q heads must be 64 or 128");
-  if (S1 != 1) return fail(FIA_ERR_UNSUPPORTED, "query length must be 1");
+  if (S1 < 1) return fail(FIA_ERR_PARAM_INVALID, "query length must be >= 1");
+  if (B * S1 > 65535) return fail(FIA_ERR_UNSUPPORTED, "B * S1 must be <= 65535");
   if (attention_out->dtype != FIA_DT_BF16 || attention_out->ndim != 4 ||
       attention_out->shape[0] != B || attention_out->shape[1] != S1 || attention_out->shape[2] != N1 ||
       attention_out->shape[3] != fia::kSparseD) {
@@ -1077,7 +1078,7 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
     if (cmp_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices needs cmp_kv");
     if (p->cmp_ratio != 1) return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 1 without compressed KV");
   }
-  int64_t K2 = 0, idx_sb = 0;
+  int64_t K2 = 0, idx_sb = 0, idx_ss = 0;
   if (cmp_sparse_indices != nullptr) {
     if ((st = check_tensor(cmp_sparse_indices, "cmp_sparse_indices")) != FIA_SUCCESS) return st;
     const fia_tensor* t = cmp_sparse_indices;
@@ -1088,6 +1089,8 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
     K2 = t->shape[3];
     if (K2 != 512 && K2 != 1024) return fail(FIA_ERR_PARAM_INVALID, "K2 must be 512 or 1024");
     idx_sb = t->stride[0];
+    idx_ss = t->stride[1];
+    if (t->stride[3] != 1) return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices rows must be contiguous");
   }
   auto check_bt = [&](const fia_tensor* t, const char* name, int64_t need) -> fia_status {
     fia_status s2 = check_tensor(t, name);
@@ -1137,9 +1140,11 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   SparseArgs& a = e->sp;
   a.q = static_cast<const uint16_t*>(q->data);
   a.q_sb = q->stride[0];
+  a.q_ss = q->stride[1];
   a.q_sh = q->stride[2];
   a.o = static_cast<uint16_t*>(attention_out->data);
   a.o_sb = attention_out->stride[0];
+  a.o_ss = attention_out->stride[1];
   a.o_sh = attention_out->stride[2];
   a.ori = static_cast<const uint8_t*>(ori_kv->data);
   a.ori_sb = osb;
@@ -1153,9 +1158,11 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   a.cmp_bt_sb = has_cmp ? cmp_block_table->stride[0] : 0;
   a.idx = cmp_sparse_indices ? static_cast<const int32_t*>(cmp_sparse_indices->data) : nullptr;
   a.idx_sb = idx_sb;
+  a.idx_ss = idx_ss;
   a.seqused = static_cast<const int32_t*>(seqused_kv->data);
   a.sinks = static_cast<const float*>(sinks->data);
   a.B = (int32_t)B;
+  a.S1 = (int32_t)S1;
   a.N1 = (int32_t)N1;
   a.K2 = (int32_t)K2;
   a.bs1 = (int32_t)bs1;
@@ -1174,8 +1181,9 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   a.scale_log2 = (float)(p->softmax_scale * 1.4426950408889634);
   const int64_t n_chunks = a.n_slots / fia::kSparseChunk;
   e->part_o_off = 0;
-  e->part_lse_off = align_up((size_t)B * n_chunks * N1 * fia::kSparseD * sizeof(float), kAlign);
-  e->ws_size = align_up(e->part_lse_off + (size_t)B * n_chunks * N1 * sizeof(float), kAlign);
+  const size_t rows = (size_t)B * S1;
+  e->part_lse_off = align_up(rows * n_chunks * N1 * fia::kSparseD * sizeof(float), kAlign);
+  e->ws_size = align_up(e->part_lse_off + rows * n_chunks * N1 * sizeof(float), kAlign);
   *workspace_size = e->ws_size;
   *executor = e;
   return FIA_SUCCESS;

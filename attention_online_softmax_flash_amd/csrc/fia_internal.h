@@ -105,10 +105,12 @@ struct AttnArgs {
 
 // Shared-KV sparse decode arguments.
 struct SparseArgs {
-  const uint16_t* q;                // bf16 [B, 1, N1, 512]
-  int64_t q_sb, q_sh;
-  uint16_t* o;                      // bf16 [B, 1, N1, 512]
-  int64_t o_sb, o_sh;
+  // Row r = b * S1 + t is query token t of batch entry b; partials and the
+  // grid run over the B * S1 rows.
+  const uint16_t* q;                // bf16 [B, S1, N1, 512]
+  int64_t q_sb, q_ss, q_sh;
+  uint16_t* o;                      // bf16 [B, S1, N1, 512]
+  int64_t o_sb, o_ss, o_sh;
   const uint8_t* ori;               // [nb1, bs1, 1, 640]
   int64_t ori_sb, ori_ss;           // bytes
   const uint8_t* cmp;
@@ -117,11 +119,11 @@ struct SparseArgs {
   int64_t ori_bt_sb;
   const int32_t* cmp_bt;
   int64_t cmp_bt_sb;
-  const int32_t* idx;               // [B, 1, 1, K2]
-  int64_t idx_sb;
+  const int32_t* idx;               // [B, S1, 1, K2]
+  int64_t idx_sb, idx_ss;
   const int32_t* seqused;           // [B]
   const float* sinks;               // [N1]
-  int32_t B, N1, K2;
+  int32_t B, S1, N1, K2;
   int32_t bs1, bs2, nb1, nb2;
   int32_t ori_bt_cols, cmp_bt_cols;
   int32_t cmp_ratio, win_left, win_right;
@@ -130,8 +132,8 @@ struct SparseArgs {
   int32_t has_cmp;
   int32_t cmp_direct;               // no indices: compressed slot k is row k
   float scale_log2;
-  float* part_o;                    // [B * n_chunks * N1 * 512]
-  float* part_lse;                  // [B * n_chunks * N1]
+  float* part_o;                    // [B * S1 * n_chunks * N1 * 512]
+  float* part_lse;                  // [B * S1 * n_chunks * N1]
 };
 
 // Launchers (defined next to their kernels).  Return hipGetLastError().

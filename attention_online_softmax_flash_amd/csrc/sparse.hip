@@ -3,13 +3,15 @@
 // original KV followed by the top-k selected rows of the compressed KV, plus a
 // per-head sink logit.
 //
-// Row list of batch b (query length 1, query at position p = Lk - 1), as fixed
-// slots so a batch's result never depends on the other batch entries:
+// Row list of query token t of batch b (the S1 tokens are the last S1
+// positions of the KV sequence: p = Lk - S1 + t), as fixed slots so a
+// result never depends on the other batch entries:
 //   slots [0, n_win_slots): window row j = p - win_left + s, used when
-//     0 <= j <= min(Lk - 1, p + win_right);
-//   slots [n_win_slots, n_win_slots + K2): compressed row c = idx[b][s - n_win]
+//     0 <= j <= min(Lk - 1, p + win_right) (band);
+//   slots [n_win_slots, n_win_slots + K2): compressed row c = idx[b][t][s - n_win]
 //     (compressed-sparse) or c = s - n_win (heavily compressed: the whole
-//     compressed sequence, no indices), used when 0 <= c < floor(Lk / cmp_ratio).
+//     compressed sequence, no indices), used when 0 <= c < Lc - (S1 - 1 - t),
+//     Lc = floor(Lk / cmp_ratio) (right-down causal over the compressed rows).
 // Each packed 640-byte row holds bf16 rope x64 | e4m3fn nope x448 | fp32
 // scale x7 (one per 64-wide nope tile); the logical 512-vector is
 // [rope | nope * scale].
@@ -45,18 +47,20 @@ __device__ __forceinline__ void e4m3fn_x4(uint32_t w, float* f) {
   f[3] = hi[1];
 }
 
-// Slots s[0..N) of batch b -> packed row addresses (nullptr for an unused
+// Slots s[0..N) of row r = b * S1 + t -> packed row addresses (nullptr for an unused
 // slot) and ids: j for window row j, (1 << 30) | c for compressed row c, -1
 // if unused.  Compressed slot k holds row idx[b][k] (compressed-sparse) or
 // row k itself (heavily compressed, no indices).  No read depends on a branch: every table read goes to an
 // in-bounds address (a clamped position), so the N index reads, then the N
 // block-table reads, are each in flight together.
 template <int N>
-__device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int b, const int* s, int Lk,
+__device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int r, const int* s, int Lk,
                                                  const uint8_t** row, int32_t* id) {
-  const int p = Lk - 1;
+  const int b = r / a.S1;
+  const int t = r - b * a.S1;
+  const int p = Lk - a.S1 + t;
   const int jmax = min(Lk - 1, p + a.win_right);
-  const int n_cmp = Lk / a.cmp_ratio;
+  const int n_cmp = Lk / a.cmp_ratio - (a.S1 - 1 - t);
   const bool cmp_on = a.has_cmp && a.K2 > 0;
   int c[N];
 #pragma unroll
@@ -65,7 +69,7 @@ __device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int b, con
     if (a.cmp_direct) {
       c[u] = cmp_on ? s[u] - a.n_win_slots : -1;
     } else {
-      c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + k] : -1;
+      c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + (int64_t)t * a.idx_ss + k] : -1;
     }
   }
   int raw[N], slot[N];
@@ -78,10 +82,10 @@ __device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int b, con
     const bool wok = s[u] <= a.win_left + a.win_right && j >= 0 && j <= jmax;
     const bool cok = cmp_on && k < a.K2 && c[u] >= 0 && c[u] < n_cmp;
     ok[u] = win[u] ? wok : cok;
-    const int r = ok[u] ? (win[u] ? j : c[u]) : 0;
+    const int rr = ok[u] ? (win[u] ? j : c[u]) : 0;
     const int bs = win[u] ? a.bs1 : a.bs2;
-    const int page = r / bs;
-    slot[u] = r - page * bs;
+    const int page = rr / bs;
+    slot[u] = rr - page * bs;
     // Compressed slots read the compressed table only when there is one.
     const bool use_cmp = !win[u] && cmp_on;
     const int cols = use_cmp ? a.cmp_bt_cols : a.ori_bt_cols;
@@ -91,13 +95,13 @@ __device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int b, con
   }
 #pragma unroll
   for (int u = 0; u < N; ++u) {
-    const uint8_t* r;
+    const uint8_t* rp;
     if (win[u]) {
-      r = a.ori + (int64_t)clamp_block(raw[u], a.nb1) * a.ori_sb + (int64_t)slot[u] * a.ori_ss;
+      rp = a.ori + (int64_t)clamp_block(raw[u], a.nb1) * a.ori_sb + (int64_t)slot[u] * a.ori_ss;
     } else {
-      r = a.cmp + (int64_t)clamp_block(raw[u], a.nb2) * a.cmp_sb + (int64_t)slot[u] * a.cmp_ss;
+      rp = a.cmp + (int64_t)clamp_block(raw[u], a.nb2) * a.cmp_sb + (int64_t)slot[u] * a.cmp_ss;
     }
-    row[u] = ok[u] ? r : nullptr;
+    row[u] = ok[u] ? rp : nullptr;
   }
 }
 
@@ -107,7 +111,7 @@ __device__ __forceinline__ int sparse_len(const SparseArgs& a, int b) {
   return Lk < 0 ? 0 : (Lk > cap ? cap : Lk);
 }
 
-// Grid: (n_slots / 64, N1 / 32, B); 256 threads.
+// Grid: (n_slots / 64, N1 / 32, B * S1); 256 threads.
 __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xs = lds;                         // [64][X_PITCH]
@@ -119,7 +123,9 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
 
   const int chunk = blockIdx.x;
   const int hb = blockIdx.y;
-  const int b = blockIdx.z;
+  const int r = blockIdx.z;   // row b * S1 + t
+  const int b = r / a.S1;
+  const int t = r - b * a.S1;
   const int n_chunks = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -136,7 +142,8 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   // the row gather: head n, d = 256 dh + 16 c + 8 hh .. +7.
   u32x4 qv[16];
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)head * a.q_sh + 256 * dh + 8 * hh;
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)t * a.q_ss + (int64_t)head * a.q_sh +
+                         256 * dh + 8 * hh;
 #pragma unroll
     for (int c = 0; c < 16; ++c) qv[c] = ld16(qp + 16 * c);
   }
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
     for (int u = 0; u < 4; ++u) sl[u] = s0 + 4 * rg + u;
     const uint8_t* rows[4];
     int32_t rid[4];
-    sparse_slot_rows<4>(a, b, sl, Lk, rows, rid);
+    sparse_slot_rows<4>(a, r, sl, Lk, rows, rid);
     if (pc0 == 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) ids[4 * rg + u] = rid[u];
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   }
   const float l_tot = l_s[n] + l_s[32 + n];
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t pi = ((int64_t)b * n_chunks + chunk) * a.N1 + head;
+  const int64_t pi = ((int64_t)r * n_chunks + chunk) * a.N1 + head;
   float* pp = a.part_o + pi * kSparseD + 128 * wave + 4 * hh;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
@@ -293,18 +300,20 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   if (wave == 0 && hh == 0) a.part_lse[pi] = l_tot > 0.f ? m_use + fast_log2(l_tot) : kNegInf;
 }
 
-// One wave per (b, head): fold the chunks in slot order with the sink logit.
+// One wave per (row, head): fold the chunks in slot order with the sink logit.
 // Lanes read the chunk log2-sum-exps in parallel; the weighted sum runs over
 // chunks in order.
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.B * a.N1) return;
-  const int b = row / a.N1;
-  const int h = row - b * a.N1;
+  if (row >= a.B * a.S1 * a.N1) return;
+  const int r = row / a.N1;   // b * S1 + t
+  const int h = row - r * a.N1;
+  const int b = r / a.S1;
+  const int t = r - b * a.S1;
   const int n_chunks = a.n_slots / kSparseChunk;   // <= 64 (K2 <= 1024)
   const float sink = a.sinks[h] * kLog2e;
-  const float lc = lane < n_chunks ? a.part_lse[((int64_t)b * n_chunks + lane) * a.N1 + h] : kNegInf;
+  const float lc = lane < n_chunks ? a.part_lse[((int64_t)r * n_chunks + lane) * a.N1 + h] : kNegInf;
   float M = fmaxf(lc, sink);
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
@@ -318,9 +327,9 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   for (; c + 2 <= n_chunks; c += 2) {
     const float w0 = __shfl(w, c, 64), w1 = __shfl(w, c + 1, 64);
     const f32x4* p0 = reinterpret_cast<const f32x4*>(
-        a.part_o + (((int64_t)b * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
+        a.part_o + (((int64_t)r * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
     const f32x4* p1 = reinterpret_cast<const f32x4*>(
-        a.part_o + (((int64_t)b * n_chunks + c + 1) * a.N1 + h) * kSparseD + 8 * lane);
+        a.part_o + (((int64_t)r * n_chunks + c + 1) * a.N1 + h) * kSparseD + 8 * lane);
     const f32x4 x0 = p0[0], x1 = p0[1], y0 = p1[0], y1 = p1[1];
     L += w0;
     L += w1;
@@ -338,7 +347,7 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   for (; c < n_chunks; ++c) {
     const float w0 = __shfl(w, c, 64);
     const f32x4* p0 = reinterpret_cast<const f32x4*>(
-        a.part_o + (((int64_t)b * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
+        a.part_o + (((int64_t)r * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
     const f32x4 x0 = p0[0], x1 = p0[1];
     L += w0;
 #pragma unroll
@@ -348,7 +357,7 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)h * a.o_sh + 8 * lane;
+  uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)t * a.o_ss + (int64_t)h * a.o_sh + 8 * lane;
   st16(op, u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                  pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)});
 }
@@ -360,13 +369,13 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
   const hipError_t attr = hipFuncSetAttribute(
       (const void*)sparse_chunk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
   if (attr != hipSuccess) return attr;
-  dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.B);
+  dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.B * a.S1);
   sparse_chunk<<<grid, 256, LDS_TOTAL, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
-  const int rows = a.B * a.N1;
+  const int rows = a.B * a.S1 * a.N1;
   if (rows > 0) sparse_merge<<<(rows + 3) / 4, 256, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -374,13 +383,13 @@ hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
 // Test support: slot ids and raw row bytes, through sparse_slot_rows.
 __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* ids, uint8_t* rows) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.n_slots;
+  const int64_t total = (int64_t)a.B * a.S1 * a.n_slots;
   if (t >= total) return;
-  const int b = (int)(t / a.n_slots);
+  const int r = (int)(t / a.n_slots);   // b * S1 + query token
   const int s = (int)(t % a.n_slots);
   int32_t id;
   const uint8_t* row;
-  sparse_slot_rows<1>(a, b, &s, sparse_len(a, b), &row, &id);
+  sparse_slot_rows<1>(a, r, &s, sparse_len(a, r / a.S1), &row, &id);
   ids[t] = id;
   uint32_t* dst = reinterpret_cast<uint32_t*>(rows + t * kRowBytes);
   for (int w = 0; w < kRowBytes / 4; ++w) {
@@ -390,7 +399,7 @@ __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* 
 
 hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* rows,
                                     hipStream_t s) {
-  const int64_t total = (int64_t)a.B * a.n_slots;
+  const int64_t total = (int64_t)a.B * a.S1 * a.n_slots;
   if (total > 0) debug_sparse_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a, ids, rows);
   return hipGetLastError();
 }

@@ -346,13 +346,14 @@ class SparsePlan(_Plan):
         self._alloc_workspace(q.device)
 
     def debug_rows(self, stream=None):
-        """(ids [B, n_slots] int32, rows [B, n_slots, 640] uint8) as the kernel gathers them."""
+        """(ids [B, S1, n_slots] int32, rows [B, S1, n_slots, 640] uint8) as the
+        kernel gathers them."""
         n = ctypes.c_int32(0)
         _check(lib().fia_debug_sparse_rows(self._exec, None, 0, None, None, ctypes.byref(n), None))
-        B = self.tensors[0].shape[0]
+        B, S1 = self.tensors[0].shape[0], self.tensors[0].shape[1]
         dev = self.tensors[0].device
-        ids = torch.empty((B, n.value), dtype=torch.int32, device=dev)
-        rows = torch.empty((B, n.value, 640), dtype=torch.uint8, device=dev)
+        ids = torch.empty((B, S1, n.value), dtype=torch.int32, device=dev)
+        rows = torch.empty((B, S1, n.value, 640), dtype=torch.uint8, device=dev)
         _check(lib().fia_debug_sparse_rows(self._exec, self.workspace.data_ptr(),
                                            self.workspace.numel(), ids.data_ptr(),
                                            rows.data_ptr(), ctypes.byref(n),

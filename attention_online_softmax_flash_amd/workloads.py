@@ -476,19 +476,20 @@ def _paged_pool_of_rows(rng, rows_per_batch, block_size, extra_blocks=0):
 
 def sparse_case(name, seed, *, B, N1, seqused_kv, K2=512, block_size1=128,
                 block_size2=128, cmp_ratio=4, n_valid=None,
-                materialise_all_ori=True, heavily_compressed=False) -> SparseCase:
-    """Shared-KV sparse decode inputs (S1 = 1).
+                materialise_all_ori=True, heavily_compressed=False, S1=1) -> SparseCase:
+    """Shared-KV sparse attention inputs, S1 query tokens per batch entry
+    (the last S1 positions of its KV sequence).
 
     ori rows: every logical row < L_b is materialised, or, when
     ``materialise_all_ori`` is False, only the last 128 (the rest are NaN);
-    cmp rows: floor(L_b / cmp_ratio) rows per batch; top-K2 indices drawn
-    uniformly without replacement from [0, n_cmp), padded with -1 when fewer
-    are valid (valid entries first).  ``heavily_compressed``: no indices
+    cmp rows: floor(L_b / cmp_ratio) rows per batch; per query token, top-K2
+    indices drawn uniformly without replacement from [0, n_cmp), padded with
+    -1 when fewer are valid (valid entries first).  ``heavily_compressed``: no indices
     (every compressed row is used), cmp_ratio 128."""
     if heavily_compressed:
         cmp_ratio = 128
     rng = rng_for(seed)
-    q = normal_bf16(rng, (B, 1, N1, SPARSE_D))
+    q = normal_bf16(rng, (B, S1, N1, SPARSE_D))
     ori_rows, cmp_rows = [], []
     for L in seqused_kv:
         L = int(L)
@@ -499,18 +500,19 @@ def sparse_case(name, seed, *, B, N1, seqused_kv, K2=512, block_size1=128,
             # query's window; every other row is 0xFF bytes (NaN in all three
             # fields) so that reading one would poison the output.
             rows = np.full((L, ROW_BYTES), 0xFF, dtype=np.uint8)
-            lo = max(0, L - 128)
+            lo = max(0, L - 128 - (S1 - 1))
             rows[lo:] = pack_rows(rng, L - lo)
             ori_rows.append(rows)
         cmp_rows.append(pack_rows(rng, L // cmp_ratio))
     ori_kv, ori_bt = _paged_pool_of_rows(rng, ori_rows, block_size1)
     cmp_kv, cmp_bt = _paged_pool_of_rows(rng, [r if r.shape[0] else np.zeros((0, ROW_BYTES), np.uint8) for r in cmp_rows], block_size2)
-    idx = np.full((B, 1, 1, K2), -1, dtype=np.int32)
+    idx = np.full((B, S1, 1, K2), -1, dtype=np.int32)
     for b, L in enumerate(seqused_kv):
         n_cmp = int(L) // cmp_ratio
         nv = min(K2, n_cmp) if n_valid is None else min(n_valid, K2, n_cmp)
-        if nv > 0:
-            idx[b, 0, 0, :nv] = rng.choice(n_cmp, size=nv, replace=False).astype(np.int32)
+        for t in range(S1):
+            if nv > 0:
+                idx[b, t, 0, :nv] = rng.choice(n_cmp, size=nv, replace=False).astype(np.int32)
     if heavily_compressed:
         idx = None
     sinks = rng.standard_normal(N1, dtype=np.float32)

@@ -85,18 +85,20 @@ def decode_bytes(case):
 
 def sparse_bytes(case):
     """640 selected rows per batch at 604 used bytes each, q, out, indices."""
-    B, _, N1, D = case.q.shape
+    B, S1, N1, D = case.q.shape
     rows = 0
     for b, Lk in enumerate(case.seqused_kv):
-        win = min(Lk, case.win_left + case.win_right + 1)
-        n_cmp = Lk // case.cmp_ratio
-        if case.cmp_sparse_indices is None:     # heavily compressed: every compressed row
-            rows += win + n_cmp
-        else:
-            idx = case.cmp_sparse_indices[b, 0, 0]
-            rows += win + int(((idx >= 0) & (idx < n_cmp)).sum())
+        for t in range(S1):
+            p = Lk - S1 + t
+            win = max(0, min(Lk - 1, p + case.win_right) - max(0, p - case.win_left) + 1)
+            n_cmp = max(0, Lk // case.cmp_ratio - (S1 - 1 - t))
+            if case.cmp_sparse_indices is None:     # heavily compressed: every visible row
+                rows += win + n_cmp
+            else:
+                idx = case.cmp_sparse_indices[b, t, 0]
+                rows += win + int(((idx >= 0) & (idx < n_cmp)).sum())
     idx_bytes = 0 if case.cmp_sparse_indices is None else case.cmp_sparse_indices.nbytes
-    return rows * 604 + 2 * B * N1 * D * 2 + idx_bytes
+    return rows * 604 + 2 * B * S1 * N1 * D * 2 + idx_bytes
 
 
 def time_plan(plan, steps, warmup, flush=None):
@@ -362,6 +364,21 @@ def main():
         components["sparse_heavily_compressed"] = {
             "workload": "shared-KV sparse decode, heavily compressed: B=16, Q_N=64, D=512, "
                         "window 128 + every row of the ratio-128 compressed KV (128 rows), sinks",
+            "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
+            "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+        del plan
+        # Two query tokens per batch entry (speculative decoding) at the
+        # shared-KV sparse decode shapes.
+        case = W.sparse_case("s1_2", SEEDS_HCA + 1, B=16, N1=64, seqused_kv=[16384] * 16, K2=512,
+                             S1=2, materialise_all_ori=False)
+        nbytes = sparse_bytes(case)
+        plan = TI.sparse_plan(case, dev)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["sparse_two_query_tokens"] = {
+            "workload": "shared-KV sparse attention, 2 query tokens per batch entry: B=16, Q_N=64, "
+                        "D=512, window 128 + top-512 of ratio-4 compressed KV per token, sinks",
             "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
             "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}

@@ -222,27 +222,31 @@ typedef struct {
   int32_t return_softmax_lse; /* must be 0 (reserved on the page) */
 } fia_sparse_params;
 
-/* Phase 1 of the shared-KV sparse decode (query length 1): attention over
- * the sliding window of ori_kv (SWA), plus the top-k selected rows of cmp_kv
- * (CSA), or plus every row of the compressed sequence (HCA).
- *   q                  bf16 [B,1,N1,512], N1 in {64,128}; logical dim order
- *                      [rope(64) | nope(448)].
+/* Phase 1 of the shared-KV sparse attention: attention over the sliding
+ * window of ori_kv (SWA), plus the top-k selected rows of cmp_kv (CSA), or
+ * plus every row of the compressed sequence (HCA).  The S1 query tokens of a
+ * batch entry are the last S1 positions of its KV sequence (token t at
+ * p = Lk - S1 + t): its window is rows max(0, p - 127) .. p, and it sees the
+ * compressed rows c < floor(Lk / cmp_ratio) - (S1 - 1 - t) (right-down
+ * causal over the compressed sequence).
+ *   q                  bf16 [B,S1,N1,512], N1 in {64,128}, B * S1 <= 65535;
+ *                      logical dim order [rope(64) | nope(448)].
  *   ori_kv, cmp_kv     uint8 (or fp8_e4m3fn) PA_ND pools [n_blk, bs, 1, 640]:
  *                      per row bf16 rope x64 | e4m3fn nope x448 | fp32 scale x7
  *                      (one per 64-wide tile) | zero pad to 640 bytes.
  *   ori_sparse_indices must be NULL (reserved on the page).
- *   cmp_sparse_indices int32 [B,1,1,K2], K2 in {512,1024}; entry c is used
- *                      iff 0 <= c < floor(Lk / cmp_ratio).  NULL with cmp_kv:
- *                      heavily compressed mode, rows 0 .. floor(Lk / 128) - 1
- *                      of the compressed sequence are all used (max_seqused_kv
- *                      / 128 + 128 <= 4096).
+ *   cmp_sparse_indices int32 [B,S1,1,K2], K2 in {512,1024}, rows contiguous;
+ *                      entry c of token t is used iff 0 <= c and c is visible
+ *                      to t (above).  NULL with cmp_kv: heavily compressed
+ *                      mode, every compressed row visible to t is used
+ *                      (max_seqused_kv / 128 + 128 <= 4096).
  *   ori_block_table    int32 [B, >= ceil(max Lk / bs1)].
  *   cmp_block_table    int32 [B, >= ceil(floor(max Lk / cmp_ratio) / bs2)].
  *   seqused_kv         int32 [B] device, KV length per batch (Lk).
  *   max_seqused_kv     host upper bound of seqused_kv, for table validation.
  *   sinks              fp32 [N1]: one extra logit per head with a zero value.
  *   metadata           ignored (the plan is built here), may be NULL.
- *   attention_out      bf16 [B,1,N1,512].
+ *   attention_out      bf16 [B,S1,N1,512].
  * K~ = V~ = window rows of ori_kv followed by the used cmp_kv rows. */
 fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
                                          const fia_tensor* q, const fia_tensor* ori_kv,
@@ -286,11 +290,11 @@ int32_t fia_executor_kind(const fia_executor* executor);
 fia_status fia_debug_gather_kv(fia_executor* executor, void* workspace, size_t workspace_size,
                                int32_t which, void* dst, void* stream);
 
-/* Test support for the sparse executor: for every batch, the row list the
- * kernel attends to, as fixed slots [B, n_slots]: ids_out[b, s] = j for window
- * row j of ori_kv, (1 << 30) | c for row c of cmp_kv, -1 for an unused slot;
- * rows_out[b, s, 0..639] = the raw packed bytes of that row (zero when
- * unused).  n_slots is returned through *n_slots_out (ids_out may be NULL to
+/* Test support for the sparse executor: for every batch entry b and query
+ * token t, the row list the kernel attends to, as fixed slots [B, S1,
+ * n_slots]: ids_out[b, t, s] = j for window row j of ori_kv, (1 << 30) | c
+ * for row c of cmp_kv, -1 for an unused slot; rows_out[b, t, s, 0..639] =
+ * the raw packed bytes of that row (zero when unused).  n_slots is returned through *n_slots_out (ids_out may be NULL to
  * query it). */
 fia_status fia_debug_sparse_rows(fia_executor* executor, void* workspace, size_t workspace_size,
                                  int32_t* ids_out, uint8_t* rows_out, int32_t* n_slots_out,

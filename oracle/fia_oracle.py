@@ -376,17 +376,21 @@ def sparse_rows(Lk: int, S1: int, t: int, idx_row, *, cmp_ratio: int,
     """The logical rows a query token attends to: window rows of ori_kv and
     selected rows of cmp_kv.
 
-    Window: p = Lk - S1 + t (the query sits at the end of its KV sequence),
-    rows max(0, p - win_left) .. min(Lk - 1, p + win_right).
-    Compressed: entries c of the index row with 0 <= c < floor(Lk / ratio),
-    in index order (compressed-sparse mode); with no index row (heavily
-    compressed mode, sparse_flash_mla HCA: the window plus the contiguous
-    compressed KV segment) every compressed row 0 .. floor(Lk / ratio) - 1.
+    Window (ori_mask_mode 4, band): p = Lk - S1 + t (the S1 query tokens
+    are the last S1 positions of the KV sequence), rows max(0, p - win_left)
+    .. min(Lk - 1, p + win_right).
+    Compressed (cmp_mask_mode 3, right-down causal on the S1 x Lc score
+    matrix of the Lc = floor(Lk / ratio) compressed rows): token t sees the
+    compressed rows c <= t + Lc - S1, i.e. c < Lc - (S1 - 1 - t).  Reading:
+    the mode-3 rule of the dense operator applied to the compressed sequence
+    as the key axis.  Compressed-sparse mode: the entries c of the index row
+    that are >= 0 and visible, in index order; heavily compressed mode
+    (sparse_flash_mla HCA, no index row): every visible compressed row.
     """
     p = Lk - S1 + t
     lo, hi = max(0, p - win_left), min(Lk - 1, p + win_right)
     window = list(range(lo, hi + 1)) if hi >= lo else []
-    n_cmp = Lk // cmp_ratio
+    n_cmp = max(0, Lk // cmp_ratio - (S1 - 1 - t))
     if idx_row is None:
         comp = list(range(n_cmp))
     else:
@@ -395,37 +399,37 @@ def sparse_rows(Lk: int, S1: int, t: int, idx_row, *, cmp_ratio: int,
 
 
 def sparse_sharedkv(case, *, batches=None):
-    """Shared-KV sparse decode output, float64 [B, 1, N1, 512].
+    """Shared-KV sparse attention output, float64 [B, S1, N1, 512].
 
-    For each (b, head h): X = rows (window ++ compressed), scores
+    For each (b, query token t, head h): X = rows (window ++ compressed) of
+    :func:`sparse_rows`, scores
     s_r = softmax_scale * (q_h . x_r), an extra sink logit sigma_h with a zero
     value vector, out = sum_r exp(s_r - m) x_r / (exp(sigma_h - m) + sum_r
     exp(s_r - m)).  K~ = V~ = X.
     """
     q = case.q
     B, S1, N1, Dq = q.shape
-    if S1 != 1:
-        raise NotImplementedError("the oracle covers query length 1")
     bs1 = case.ori_kv.shape[1]
     bs2 = case.cmp_kv.shape[1]
     out = np.full((B, S1, N1, Dq), np.nan)
     sinks = np.asarray(case.sinks, dtype=np.float32).astype(np.float64)
     for b in (range(B) if batches is None else batches):
         Lk = int(case.seqused_kv[b])
-        idx_row = None if case.cmp_sparse_indices is None else case.cmp_sparse_indices[b, 0, 0]
-        win, comp = sparse_rows(Lk, S1, 0, idx_row,
-                                cmp_ratio=case.cmp_ratio, win_left=case.win_left,
-                                win_right=case.win_right)
-        X = []
-        for j in win:
-            X.append(decode_packed_row(case.ori_kv[case.ori_block_table[b, j // bs1], j % bs1, 0]))
-        for c in comp:
-            X.append(decode_packed_row(case.cmp_kv[case.cmp_block_table[b, c // bs2], c % bs2, 0]))
-        X = np.stack(X) if X else np.zeros((0, Dq))
-        qb = decode_bf16(q[b, 0])                           # [N1, 512]
-        s = case.softmax_scale * (qb @ X.T)                 # [N1, R]
-        for h in range(N1):
-            o, _ = softmax_rows(s[h:h + 1], np.ones((1, X.shape[0]), bool), X,
-                                extra_logit=float(sinks[h]))
-            out[b, 0, h] = o[0]
+        for t in range(S1):
+            idx_row = None if case.cmp_sparse_indices is None else case.cmp_sparse_indices[b, t, 0]
+            win, comp = sparse_rows(Lk, S1, t, idx_row,
+                                    cmp_ratio=case.cmp_ratio, win_left=case.win_left,
+                                    win_right=case.win_right)
+            X = []
+            for j in win:
+                X.append(decode_packed_row(case.ori_kv[case.ori_block_table[b, j // bs1], j % bs1, 0]))
+            for c in comp:
+                X.append(decode_packed_row(case.cmp_kv[case.cmp_block_table[b, c // bs2], c % bs2, 0]))
+            X = np.stack(X) if X else np.zeros((0, Dq))
+            qb = decode_bf16(q[b, t])                           # [N1, 512]
+            s = case.softmax_scale * (qb @ X.T)                 # [N1, R]
+            for h in range(N1):
+                o, _ = softmax_rows(s[h:h + 1], np.ones((1, X.shape[0]), bool), X,
+                                    extra_logit=float(sinks[h]))
+                out[b, t, h] = o[0]
     return out

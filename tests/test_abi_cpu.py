@@ -575,7 +575,13 @@ def sparse_plan_status(**over):
     (dict(layout_q=b"TND"), UNS),
     (dict(layout_kv=b"BSND"), BAD),
     (dict(sinks=T((64,), fia.DT_BF16)), BAD),
-    (dict(q=T((2, 2, 64, 512)), out=T((2, 2, 64, 512)), idx=T((2, 2, 1, 512), fia.DT_INT32)), UNS),
+    (dict(q=T((2, 2, 64, 512)), out=T((2, 2, 64, 512)), idx=T((2, 2, 1, 512), fia.DT_INT32)), 0),
+    (dict(q=T((2, 4, 64, 512)), out=T((2, 4, 64, 512)), idx=None, cmp_ratio=128), 0),
+    (dict(q=T((2, 2, 64, 512)), out=T((2, 2, 64, 512))), BAD),        # indices [B, 1, ...] for S1 = 2
+    (dict(q=T((2, 2, 64, 512)), out=T((2, 1, 64, 512)), idx=T((2, 2, 1, 512), fia.DT_INT32)), BAD),
+    (dict(q=T((2, 0, 64, 512)), out=T((2, 0, 64, 512)), idx=T((2, 0, 1, 512), fia.DT_INT32)), BAD),
+    (dict(q=T((2, 40000, 64, 512)), out=T((2, 40000, 64, 512)),
+          idx=T((2, 40000, 1, 512), fia.DT_INT32)), UNS),
 ])
 def test_sparse_phase1(over, expect):
     st, msg = sparse_plan_status(**over)

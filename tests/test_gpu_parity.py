@@ -479,7 +479,7 @@ def test_sparse_heavily_compressed_rows_are_bit_exact():
     plan = TI.sparse_plan(case, DEV)
     ids, rows = plan.debug_rows()
     torch.cuda.synchronize()
-    ids, rows = ids.cpu().numpy(), rows.cpu().numpy()
+    ids, rows = ids.cpu().numpy()[:, 0], rows.cpu().numpy()[:, 0]
     n_win = 128
     for b, L in enumerate(case.seqused_kv):
         win, comp = O.sparse_rows(L, 1, 0, None, cmp_ratio=128, win_left=127, win_right=0)
@@ -493,6 +493,51 @@ def test_sparse_heavily_compressed_rows_are_bit_exact():
                 c = x & ((1 << 30) - 1)
                 want = case.cmp_kv[case.cmp_block_table[b, c // 16], c % 16, 0]
                 assert np.array_equal(rows[b, s], want)
+
+
+SPARSE_MULTI_CASES = [
+    # (B, S1, N1, seqused, K2, hca)
+    (2, 4, 64, [300, 5000], 512, False),
+    (3, 2, 128, [9, 700, 130], 1024, False),
+    (2, 3, 64, [1000, 4000], 0, True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SPARSE_MULTI_CASES)))
+def test_sparse_multi_token(i):
+    """S1 > 1: token t at p = Lk - S1 + t, window band [p - 127, p], compressed
+    rows right-down causal over the compressed sequence."""
+    B, S1, N1, L, K2, hca = SPARSE_MULTI_CASES[i]
+    case = W.sparse_case(f"smt{i}", 430 + i, B=B, N1=N1, seqused_kv=L, K2=K2 or 512, S1=S1,
+                         block_size1=64, block_size2=32, heavily_compressed=hca,
+                         materialise_all_ori=False)
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
+def test_sparse_multi_token_rows_are_bit_exact():
+    case = W.sparse_case("smr", 440, B=2, N1=64, seqused_kv=[40, 3000], K2=512, S1=5,
+                         block_size1=32, block_size2=16, materialise_all_ori=False)
+    plan = TI.sparse_plan(case, DEV)
+    ids, rows = plan.debug_rows()
+    torch.cuda.synchronize()
+    ids, rows = ids.cpu().numpy(), rows.cpu().numpy()
+    n_win = 128
+    for b, L in enumerate(case.seqused_kv):
+        for t in range(5):
+            win, comp = O.sparse_rows(L, 5, t, case.cmp_sparse_indices[b, t, 0], cmp_ratio=4,
+                                      win_left=127, win_right=0)
+            assert [int(x) for x in ids[b, t, :n_win] if x >= 0] == win, (b, t)
+            assert [int(x) & ((1 << 30) - 1) for x in ids[b, t, n_win:] if x >= 0] == comp, (b, t)
+            for s in range(ids.shape[2]):
+                x = int(ids[b, t, s])
+                if x < 0:
+                    assert not rows[b, t, s].any()
+                elif x >> 30:
+                    c = x & ((1 << 30) - 1)
+                    assert np.array_equal(rows[b, t, s], case.cmp_kv[case.cmp_block_table[b, c // 16], c % 16, 0])
+                else:
+                    assert np.array_equal(rows[b, t, s], case.ori_kv[case.ori_block_table[b, x // 32], x % 32, 0])
 
 
 # ---------------------------------------------------------------------------
@@ -520,7 +565,7 @@ def test_sparse_row_selection_is_bit_exact():
     plan = TI.sparse_plan(case, DEV)
     ids, rows = plan.debug_rows()
     torch.cuda.synchronize()
-    ids, rows = ids.cpu().numpy(), rows.cpu().numpy()
+    ids, rows = ids.cpu().numpy()[:, 0], rows.cpu().numpy()[:, 0]
     n_win = 128
     for b, L in enumerate(case.seqused_kv):
         win, comp = O.sparse_rows(L, 1, 0, case.cmp_sparse_indices[b, 0, 0], cmp_ratio=4,

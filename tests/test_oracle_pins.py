@@ -397,6 +397,26 @@ def test_heavily_compressed_rows_hand_values():
     assert comp == list(range(8))
 
 
+def test_sparse_multi_token_rows_hand_values():
+    """S1 = 3 tokens at the end of Lk = 20 keys (positions 17, 18, 19), ratio
+    4 (Lc = 5 compressed rows): the band window [p - 127, p] and the mode-3
+    triangle over the compressed rows (token t sees c <= t + Lc - S1), worked
+    by hand; the last token sees what a single-token call sees."""
+    idx = np.array([4, 0, 3, 2, 1, -1], dtype=np.int32)
+    want_comp = {0: [0, 2, 1], 1: [0, 3, 2, 1], 2: [4, 0, 3, 2, 1]}
+    for t in range(3):
+        win, comp = O.sparse_rows(20, 3, t, idx, cmp_ratio=4, win_left=127, win_right=0)
+        assert win == list(range(0, 18 + t))
+        assert comp == want_comp[t]
+    win, comp = O.sparse_rows(20, 3, 0, None, cmp_ratio=4, win_left=127, win_right=0)
+    assert comp == [0, 1, 2]
+    assert O.sparse_rows(20, 1, 0, idx, cmp_ratio=4, win_left=127, win_right=0) == \
+        O.sparse_rows(20, 3, 2, idx, cmp_ratio=4, win_left=127, win_right=0)
+    # a long sequence: the window of the first of 4 tokens ends 3 rows early
+    win, _ = O.sparse_rows(1000, 4, 0, None, cmp_ratio=128, win_left=127, win_right=0)
+    assert win == list(range(1000 - 3 - 128, 1000 - 3))
+
+
 def test_explicit_mask_reduces_to_analytic_modes():
     """An explicit mask equal to the left-up causal pattern reproduces mode 2,
     an all-zero mask reproduces mode 0, and a fully masked row is empty."""
