@@ -36,18 +36,32 @@ constexpr int BN = kPrefillKeys;  // 64
 
 template <int D>
 struct PrefillLds {
-  static constexpr int K_ROW = D * 2;           // bytes per key row (swizzled, no padding)
-  static constexpr int K_BYTES = BN * K_ROW;
-  static constexpr int V_PITCH = BN * 2 + 16;   // bytes per transposed value row
-  static constexpr int V_BYTES = D * V_PITCH;
+  static constexpr int ROW = D * 2;             // bytes per key / value row (swizzled, no padding)
+  static constexpr int BYTES = BN * ROW;        // one stage of one tile
 };
 
 template <int D>
 struct TileRegs {
-  static constexpr int NK = BN * D / 8 / 256;   // 16-byte key pieces per thread
+  static constexpr int NK = BN * D / 8 / 256;   // 16-byte pieces of a tile per thread
   u32x4 k[NK];
-  u32x4 v[4];
+  u32x4 v[NK];
 };
+
+// XOR swizzle of value rows in LDS: 16-byte piece q of row r sits in slot
+// q ^ val_swz<PR>(r).  The value product reads them with 8-byte transpose
+// reads in which one group of 16 lanes touches four consecutive rows
+// (r % 4 = 0..3) and 32 contiguous bytes of each, and two neighbouring
+// groups the next 32 bytes: the swizzle sends those 4 x 2 (or 4 x 4) pieces
+// to distinct slots of the 128-byte (or 256-byte) bank window.
+template <int PR>
+__device__ __forceinline__ int val_swz(int r) {
+  if constexpr (PR == 16) {
+    constexpr int f = (0 << 0) | (6 << 4) | (10 << 8) | (12 << 12);
+    return (f >> (4 * (r & 3))) & 15;
+  } else {
+    return 2 * (r & 3);
+  }
+}
 
 }  // namespace
 
@@ -81,10 +95,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   // bias or per-row paging, which compute each tile's scores up front).
   constexpr bool PIPE = !ALIBI && !EXT && KVM != 2;
   constexpr bool INTERLEAVE = PIPE;
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[L::K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[L::K_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[L::V_BYTES];
-  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[L::V_BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k0[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_k1[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v0[L::BYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_v1[L::BYTES];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -181,45 +195,54 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     const uint16_t* kbase0 = kg + (int64_t)b * a.k_sb + (int64_t)kv_off * a.k_ss + (int64_t)kvh * a.k_sh;
     const uint16_t* vbase0 = vg + (int64_t)b * a.v_sb + (int64_t)kv_off * a.v_ss + (int64_t)kvh * a.v_sh;
 
-    // Key staging.  Buffer-to-LDS load q of wave w fills rows RPI (4 q + w)
-    // .. + RPI - 1 of the tile (1 KiB, lane l -> slot l % DCH of row
-    // l / DCH), fetching the global piece that belongs in that slot.  With
-    // registers (KVM 2), thread u = tid + 256 q holds piece u % DCH of row
-    // u / DCH and stores it into its slot.
-    uint32_t koffs[NK];
-#pragma unroll
-    for (int q = 0; q < NK; ++q) {
-      if constexpr (DMA_K) {
-        const int r = RPI * (4 * q + wave) + lane / DCH;
-        const int gp = (lane % DCH) ^ key_swz<DCH>(r);
-        koffs[q] = (uint32_t)(r * a.k_ss + 8 * gp) * 2u;
-      } else {
-        const int u = tid + 256 * q;
-        const int r = u / DCH;
-        koffs[q] = (uint32_t)(r * L::K_ROW + 16 * ((u % DCH) ^ key_swz<DCH>(r)));
-      }
+    // Key / value staging.  Buffer-to-LDS load q of wave w fills rows
+    // RPI (4 q + w) .. + RPI - 1 of the tile (1 KiB, lane l -> slot l % DCH
+    // of row l / DCH), fetching the global piece that belongs in that slot.
+    // With registers (KVM 2), thread u = tid + 256 q holds piece u % DCH of
+    // row u / DCH and stores it into its slot.  Keys and values differ only
+    // in their swizzle.
+    // Consecutive q differ by a fixed number of rows with the same swizzle,
+    // so one offset per lane plus a uniform step per q covers them.
+    constexpr int QROWS = 256 / DCH;   // tile rows per q
+    uint32_t koff, voff;
+    if constexpr (DMA_K) {
+      const int r = RPI * wave + lane / DCH;
+      koff = (uint32_t)(r * a.k_ss + 8 * ((lane % DCH) ^ key_swz<DCH>(r))) * 2u;
+      voff = (uint32_t)(r * a.v_ss + 8 * ((lane % DCH) ^ val_swz<DCH>(r))) * 2u;
+    } else {
+      const int r = tid / DCH;
+      koff = (uint32_t)(r * L::ROW + 16 * ((tid % DCH) ^ key_swz<DCH>(r)));
+      voff = (uint32_t)(r * L::ROW + 16 * ((tid % DCH) ^ val_swz<DCH>(r)));
     }
+    const uint32_t kq_step = (uint32_t)(QROWS * a.k_ss) * 2u;
+    const uint32_t vq_step = (uint32_t)(QROWS * a.v_ss) * 2u;
     // Score-operand reads: lane (n, hh) reads piece 2 c + hh of key rows
     // 32 k2 + n, which all share the swizzle of row n.
     uint32_t kr_addr[NQ];
     {
       const int sw = key_swz<DCH>(n);
 #pragma unroll
-      for (int c = 0; c < NQ; ++c) kr_addr[c] = (uint32_t)(n * L::K_ROW + 16 * ((2 * c + hh) ^ sw));
+      for (int c = 0; c < NQ; ++c) kr_addr[c] = (uint32_t)(n * L::ROW + 16 * ((2 * c + hh) ^ sw));
     }
-    // Thread roles for the value tile.
-    const int va = tid & 15;   // keys 4 va .. 4 va + 3 of the value tile
-    const int vq = tid >> 4;   // 16-byte value column piece
-    uint32_t voffs[4];
+    // Value-operand reads (transpose reads of row-major value rows).  For
+    // k-step kk of the value product, lane (m, hh) needs V[key][32 mb + m]
+    // for the keys whose probabilities it holds in the score accumulators:
+    // 16 kk + 4 hh + (0..3), then 16 kk + 8 + 4 hh + (0..3).  In one
+    // transpose read, lane 4 t + r' of a 16-lane group addresses row
+    // 16 kk + 8 h + 4 hh + t at 8-byte column 8 mb + 4 (m / 16) + r', so
+    // lane i of the group receives V[row t][32 mb + 16 (m / 16) + i].
+    uint32_t vr_addr[NMB];
+    {
+      const int gi = lane & 15;
+      const int t = gi >> 2, rp = gi & 3;
+      const int half = (lane >> 4) & 1;
+      const int r = 4 * hh + t;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) voffs[q] = (uint32_t)((4 * va + q) * a.v_ss + 8 * vq) * 2u;
-    // Transposed value rows keep keys in the order the score accumulators
-    // hold them: inside each 16-key group, key 8 b3 + 4 b2 + (0..3) sits at
-    // 8 b2 + 4 b3 + (0..3), so the 8 keys one lane feeds to a k-step of the
-    // value product are one contiguous 16-byte piece.
-    const int va_pos = 4 * (va & ~3) + 4 * (((va & 1) << 1) | ((va >> 1) & 1));
-    const uint32_t vs_addr = (uint32_t)(8 * vq * L::V_PITCH + va_pos * 2);
-    const uint32_t vr_addr = (uint32_t)(n * L::V_PITCH + 16 * hh);
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int c8 = 8 * mb + 4 * half + rp;
+        vr_addr[mb] = (uint32_t)(r * L::ROW + 16 * ((c8 >> 1) ^ val_swz<DCH>(r)) + 8 * (c8 & 1));
+      }
+    }
     TileRegs<D> regs;
 
     // Resources (or, for KVM 2, register loads) of key / value tile kt.
@@ -242,66 +265,46 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       rk = make_rsrc(kp, (uint32_t)((nvalid - 1) * a.k_ss + D) * 2u);
       rv = make_rsrc(vp, (uint32_t)((nvalid - 1) * a.v_ss + D) * 2u);
     };
-    // Global loads of tile kt: keys straight into stage `kdst` (KVM 0 / 1)
-    // or into registers, values into registers.
-    auto load_tile = [&](int kt, uint8_t* kdst) FIA_INLINE {
-      const int j0 = kt * BN;
-      if constexpr (KVM == 2) {
-#pragma unroll
-        for (int q = 0; q < NK; ++q) {
-          const int u = tid + 256 * q;
-          const int j = j0 + u / DCH;
-          u32x4 val = {0, 0, 0, 0};
-          if (j < Lk) val = ld16(kg + kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, j, kvh, kv_off) + 8 * (u % DCH));
-          regs.k[q] = val;
-        }
-        if (vq < DCH) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int j = j0 + 4 * va + q;
-            u32x4 val = {0, 0, 0, 0};
-            if (j < Lk) val = ld16(vg + kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, j, kvh, kv_off) + 8 * vq);
-            regs.v[q] = val;
-          }
-        }
-      } else {
-        __amdgpu_buffer_rsrc_t rk, rv;
-        tile_rsrc(kt, rk, rv);
-        if (kdst != nullptr) {
-#pragma unroll
-          for (int q = 0; q < NK; ++q) buf_ld16_lds(rk, kdst + 1024 * (4 * q + wave), koffs[q]);
-        }
-        if (vq < DCH) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) regs.v[q] = buf_ld16(rv, voffs[q]);
-        }
-      }
-    };
-    // Keys of tile kt into stage `kdst` by buffer-to-LDS loads alone.
-    auto load_k_lds = [&](int kt, uint8_t* kdst) FIA_INLINE {
+    // Keys (or values) of tile kt straight into stage `dst` by buffer-to-LDS
+    // loads (KVM 0 / 1).
+    auto load_k_lds = [&](int kt, uint8_t* dst) FIA_INLINE {
       __amdgpu_buffer_rsrc_t rk, rv;
       tile_rsrc(kt, rk, rv);
 #pragma unroll
-      for (int q = 0; q < NK; ++q) buf_ld16_lds(rk, kdst + 1024 * (4 * q + wave), koffs[q]);
+      for (int q = 0; q < NK; ++q) buf_ld16_lds(rk, dst + 1024 * (4 * q + wave), koff + q * kq_step);
     };
-    // Register-staged parts of a tile into their stages.
-    auto store_tile = [&](uint8_t* kst, uint8_t* vst) FIA_INLINE {
-      if constexpr (KVM == 2) {
+    auto load_v_lds = [&](int kt, uint8_t* dst) FIA_INLINE {
+      __amdgpu_buffer_rsrc_t rk, rv;
+      tile_rsrc(kt, rk, rv);
 #pragma unroll
-        for (int q = 0; q < NK; ++q) *reinterpret_cast<u32x4*>(kst + koffs[q]) = regs.k[q];
+      for (int q = 0; q < NK; ++q) buf_ld16_lds(rv, dst + 1024 * (4 * q + wave), voff + q * vq_step);
+    };
+    // KVM 2: keys and values of tile kt into registers (per-row page
+    // lookups; rows >= Lk read as zero), then into their stages.
+    auto load_regs = [&](int kt) FIA_INLINE {
+      const int j0 = kt * BN;
+#pragma unroll
+      for (int q = 0; q < NK; ++q) {
+        const int u = tid + 256 * q;
+        const int j = j0 + u / DCH;
+        u32x4 val = {0, 0, 0, 0};
+        if (j < Lk) val = ld16(kg + kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, j, kvh, kv_off) + 8 * (u % DCH));
+        regs.k[q] = val;
       }
-      if (vq < DCH) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int w = e >> 1;
-          u32x2 pr;
-          if (e & 1) {
-            pr = u32x2{pick_hi(regs.v[0][w], regs.v[1][w]), pick_hi(regs.v[2][w], regs.v[3][w])};
-          } else {
-            pr = u32x2{pick_lo(regs.v[0][w], regs.v[1][w]), pick_lo(regs.v[2][w], regs.v[3][w])};
-          }
-          *reinterpret_cast<u32x2*>(vst + vs_addr + e * L::V_PITCH) = pr;
-        }
+      for (int q = 0; q < NK; ++q) {
+        const int u = tid + 256 * q;
+        const int j = j0 + u / DCH;
+        u32x4 val = {0, 0, 0, 0};
+        if (j < Lk) val = ld16(vg + kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, j, kvh, kv_off) + 8 * (u % DCH));
+        regs.v[q] = val;
+      }
+    };
+    auto store_regs = [&](uint8_t* kst, uint8_t* vst) FIA_INLINE {
+#pragma unroll
+      for (int q = 0; q < NK; ++q) {
+        *reinterpret_cast<u32x4*>(kst + koff + q * QROWS * L::ROW) = regs.k[q];
+        *reinterpret_cast<u32x4*>(vst + voff + q * QROWS * L::ROW) = regs.v[q];
       }
     };
 
@@ -325,14 +328,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       constexpr bool ACC = decltype(acc_tag)::value;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
-        sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[0] + 32 * k2 * L::K_ROW), qreg[0],
+        sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[0] + 32 * k2 * L::ROW), qreg[0],
                         ACC ? sv[k2] : f32x16{});
       }
 #pragma unroll
       for (int c = 1; c < NQ; ++c) {
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
-          sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[c] + 32 * k2 * L::K_ROW),
+          sv[k2] = mfma32(*reinterpret_cast<const u32x4*>(kst + kr_addr[c] + 32 * k2 * L::ROW),
                           qreg[c], sv[k2]);
         }
       }
@@ -421,13 +424,14 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
                        pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
       }
       l_run += psum;
-      const uint8_t* vb = vst + vr_addr;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) {
-          const uint8_t* vp = vb + 32 * mb * L::V_PITCH + 32 * kk;
-          o[mb] = mfma32(*reinterpret_cast<const u32x4*>(vp), pb[kk], o[mb]);
+          const uint8_t* vp = vst + vr_addr[mb] + 16 * kk * L::ROW;
+          const u32x2 lo = lds_tr16(vp);
+          const u32x2 hi = lds_tr16(vp + 8 * L::ROW);
+          o[mb] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kk], o[mb]);
         }
       }
       __builtin_amdgcn_s_setprio(0);
@@ -444,36 +448,55 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 
     // Software pipeline over key tiles, two stages (stage of tile kt:
     // (kt - kt0) & 1).  Step kt holds the scores of tile kt in registers
-    // (with PIPE), issues the loads of tile kt + 2 and computes softmax(kt) +
-    // PV(kt) together with the score product of tile kt + 1; one barrier
-    // ends it, after which tile kt + 2's register-staged parts are stored
-    // into the stage tile kt used.  With PIPE the keys of tile kt were
-    // consumed one step earlier, so their stage is refilled from the start of
-    // step kt; otherwise the key loads go out after the barrier.
+    // (with PIPE) and computes softmax(kt) + PV(kt) together with the score
+    // product of tile kt + 1; one barrier ends it.  Buffer-to-LDS loads
+    // (KVM 0 / 1) go out at the start of a step into stages no wave reads in
+    // that step: the values of tile kt + 1, and the keys of tile kt + 2
+    // (with PIPE the keys of tile kt were consumed one step earlier) or of
+    // tile kt + 1.  The barrier ending the step waits for them.  With
+    // registers (KVM 2) tile kt + 2 is loaded at the start of step kt and
+    // stored after its barrier into the stages tile kt used.
     const int kt0 = klo / BN;
     const int kt1 = (khi + BN - 1) / BN;
     const bool has1 = kt0 + 1 < kt1;
-    load_tile(kt0, lds_k0);
-    if (PIPE && DMA_K && has1) load_k_lds(kt0 + 1, lds_k1);
-    barrier_after_loads();
-    store_tile(lds_k0, lds_v0);
-    if (has1) load_tile(kt0 + 1, (!PIPE && DMA_K) ? lds_k1 : nullptr);
-    barrier_after_loads();
+    if constexpr (DMA_K) {
+      load_k_lds(kt0, lds_k0);
+      load_v_lds(kt0, lds_v0);
+      if (PIPE && has1) load_k_lds(kt0 + 1, lds_k1);
+      barrier_after_loads();
+    } else {
+      load_regs(kt0);
+      store_regs(lds_k0, lds_v0);
+      if (has1) {
+        load_regs(kt0 + 1);
+        store_regs(lds_k1, lds_v1);
+      }
+      __syncthreads();
+    }
     f32x16 s_a[2], s_b[2];
     bool cur_skip = wave_skip(kt0);
     if (PIPE && !cur_skip) compute_s(std::false_type{}, lds_k0, s_a);
     if (EXT && !cur_skip) load_ext(kt0);
-    if (has1) store_tile(lds_k1, lds_v1);
-    __syncthreads();
+    if (PIPE) __syncthreads();   // step kt0 refills lds_k0
 
     auto step = [&](auto stage_tag, int kt, f32x16* sc, f32x16* sn) FIA_INLINE {
       constexpr int S = decltype(stage_tag)::value;
       uint8_t* kst = S ? lds_k1 : lds_k0;
       uint8_t* vst = S ? lds_v1 : lds_v0;
       uint8_t* knx = S ? lds_k0 : lds_k1;
+      uint8_t* vnx = S ? lds_v0 : lds_v1;
       const bool has_next = kt + 1 < kt1;
       const bool has_next2 = kt + 2 < kt1;
-      if (has_next2) load_tile(kt + 2, (PIPE && DMA_K) ? kst : nullptr);
+      if constexpr (DMA_K) {
+        if constexpr (PIPE) {
+          if (has_next2) load_k_lds(kt + 2, kst);
+        } else {
+          if (has_next) load_k_lds(kt + 1, knx);
+        }
+        if (has_next) load_v_lds(kt + 1, vnx);
+      } else {
+        if (has_next2) load_regs(kt + 2);
+      }
       const bool next_skip = has_next ? wave_skip(kt + 1) : true;
       // The next tile's keys are always read from the other stage array
       // itself (not through a pointer chosen at run time), so the compiler
@@ -499,10 +522,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         compute_s(std::false_type{}, knx, sn);
       }
       cur_skip = next_skip;
-      barrier_after_loads();   // loads of tile kt + 2 landed; every wave is done with tile kt
-      if (has_next2) {
-        if constexpr (!PIPE && DMA_K) load_k_lds(kt + 2, kst);
-        store_tile(kst, vst);
+      barrier_after_loads();   // this step's loads landed; every wave is done with tile kt
+      if constexpr (!DMA_K) {
+        if (has_next2) store_regs(kst, vst);
       }
       if (EXT && !next_skip) load_ext(kt + 1);
     };
