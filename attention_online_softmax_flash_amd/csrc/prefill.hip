@@ -346,12 +346,13 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     };
 
     // Softmax of tile kt (scores in sc), then O += V^T P^T from `vst`.  With
-    // `do_next` the score product of the next tile (keys in stage `knx`) is
+    // DO_NEXT the score product of the next tile (keys in stage `knx`) is
     // issued inside the same straight-line block, so its MFMAs overlap this
     // tile's VALU work.
     auto tile_body = [&](auto masked_tag, int kt, const uint8_t* vst, f32x16* sc,
-                         bool do_next, const uint8_t* knx, f32x16* sn) FIA_INLINE {
+                         auto next_tag, const uint8_t* knx, f32x16* sn) FIA_INLINE {
       constexpr bool MASKED = decltype(masked_tag)::value;
+      constexpr bool DO_NEXT = decltype(next_tag)::value;
       constexpr bool PLAIN = !ALIBI && !MASKED;
       const int j0 = kt * BN;
       float mx = kNegInf;
@@ -368,8 +369,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         // is c_al * (base + koff), not c_al * base + c_al * koff, so no
         // loop-invariant products need registers.
         const float base = (float)(jb - i + a.alibi_delta);
-        const int rel_lo = my_lo - jb;   // visible iff rel_lo <= koff < rel_hi
-        const int rel_hi = my_hi - jb;
+        // visible iff rel_lo <= koff < rel_hi, tested as one unsigned compare
+        const uint32_t nlo = (uint32_t)(jb - my_lo);
+        const uint32_t span = (uint32_t)(my_hi - my_lo);
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
             float x = ALIBI ? __builtin_fmaf(sc[k2][r], a.scale_log2, c_al * (base + (float)koff))
                             : sc[k2][r] * a.scale_log2;
             if constexpr (MASKED) {
-              bool keep = koff >= rel_lo && koff < rel_hi;
+              bool keep = (uint32_t)koff + nlo < span;
               if constexpr (EXT) keep = keep && sc[k2][r] != kNegInf;   // masked-out key
               x = keep ? x : kNegInf;
             }
@@ -405,7 +407,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       // VALU work of the other wave on the SIMD.
       __builtin_amdgcn_s_setprio(1);
       if constexpr (PIPE) {
-        if (do_next) compute_s(std::false_type{}, knx, sn);
+        if constexpr (DO_NEXT) compute_s(std::false_type{}, knx, sn);
       }
       float psum = 0.f;
       u32x4 pb[4];
@@ -514,9 +516,17 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         const int j0 = kt * BN;
         const bool need_mask = EXT || !(j0 >= wlo_max && j0 + BN <= whi_min);
         if (need_mask) {
-          tile_body(std::true_type{}, kt, vst, sc, do_next, knx, sn);
+          if (do_next) {
+            tile_body(std::true_type{}, kt, vst, sc, std::true_type{}, knx, sn);
+          } else {
+            tile_body(std::true_type{}, kt, vst, sc, std::false_type{}, knx, sn);
+          }
         } else {
-          tile_body(std::false_type{}, kt, vst, sc, do_next, knx, sn);
+          if (do_next) {
+            tile_body(std::false_type{}, kt, vst, sc, std::true_type{}, knx, sn);
+          } else {
+            tile_body(std::false_type{}, kt, vst, sc, std::false_type{}, knx, sn);
+          }
         }
       } else if (do_next) {
         compute_s(std::false_type{}, knx, sn);
