@@ -990,6 +990,7 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
                                          const fia_tensor* cmp_sparse_indices,
                                          const fia_tensor* ori_block_table,
                                          const fia_tensor* cmp_block_table,
+                                         const fia_tensor* cu_seqlens_q,
                                          const fia_tensor* seqused_kv, int64_t max_seqused_kv,
                                          const fia_tensor* sinks, const fia_tensor* metadata,
                                          const fia_tensor* attention_out, size_t* workspace_size,
@@ -1010,8 +1011,8 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   }
   const std::string lq = p->layout_q ? p->layout_q : "BSND";
   const std::string lkv = p->layout_kv ? p->layout_kv : "PA_ND";
-  if (lq == "TND") return fail(FIA_ERR_UNSUPPORTED, "layout_q TND is not supported");
-  if (lq != "BSND") return fail(FIA_ERR_PARAM_INVALID, "layout_q must be BSND or TND");
+  if (lq != "BSND" && lq != "TND") return fail(FIA_ERR_PARAM_INVALID, "layout_q must be BSND or TND");
+  const bool tnd = lq == "TND";
   if (lkv != "PA_ND") return fail(FIA_ERR_PARAM_INVALID, "layout_kv must be PA_ND");
   if (p->kv_quant_mode != 1) return fail(FIA_ERR_PARAM_INVALID, "kv_quant_mode must be 1 (per-tile)");
   if (p->tile_size != 64) return fail(FIA_ERR_PARAM_INVALID, "tile_size must be 64");
@@ -1023,16 +1024,35 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   if (p->return_softmax_lse) return fail(FIA_ERR_PARAM_INVALID, "return_softmax_lse is reserved");
   if (ori_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "ori_sparse_indices is reserved");
   if (q->dtype != FIA_DT_BF16) return fail(FIA_ERR_PARAM_INVALID, "q must be bf16");
-  if (q->ndim != 4) return fail(FIA_ERR_PARAM_INVALID, "q must be [B, S1, N1, 512]");
-  const int64_t B = q->shape[0], S1 = q->shape[1], N1 = q->shape[2];
-  if (q->shape[3] != fia::kSparseD) return fail(FIA_ERR_PARAM_INVALID, "q head dim must be 512");
+  // TND packs the query tokens of all batch entries into T1 rows; the batch
+  // count then comes from seqused_kv and the row split from cu_seqlens_q.
+  if (q->ndim != (tnd ? 3 : 4)) {
+    return fail(FIA_ERR_PARAM_INVALID, tnd ? "q must be [T1, N1, 512] for TND" : "q must be [B, S1, N1, 512]");
+  }
+  if (seqused_kv->dtype != FIA_DT_INT32 || seqused_kv->ndim != 1) {
+    return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
+  }
+  const int64_t B = tnd ? seqused_kv->shape[0] : q->shape[0];
+  const int64_t S1 = tnd ? 1 : q->shape[1];
+  const int64_t n_rows = tnd ? q->shape[0] : B * S1;
+  const int64_t N1 = q->shape[tnd ? 1 : 2];
+  if (q->shape[q->ndim - 1] != fia::kSparseD) return fail(FIA_ERR_PARAM_INVALID, "q head dim must be 512");
   if (N1 != 64 && N1 != 128) return fail(FIA_ERR_PARAM_INVALID, "q heads must be 64 or 128");
-  if (S1 < 1) return fail(FIA_ERR_PARAM_INVALID, "query length must be >= 1");
-  if (B * S1 > 65535) return fail(FIA_ERR_UNSUPPORTED, "B * S1 must be <= 65535");
-  if (attention_out->dtype != FIA_DT_BF16 || attention_out->ndim != 4 ||
-      attention_out->shape[0] != B || attention_out->shape[1] != S1 || attention_out->shape[2] != N1 ||
-      attention_out->shape[3] != fia::kSparseD) {
-    return fail(FIA_ERR_PARAM_INVALID, "attention_out must be bf16 with the shape of q");
+  if (B < 1) return fail(FIA_ERR_PARAM_INVALID, "batch must be >= 1");
+  if (!tnd && S1 < 1) return fail(FIA_ERR_PARAM_INVALID, "query length must be >= 1");
+  if (n_rows > 65535) return fail(FIA_ERR_UNSUPPORTED, "B * S1 (or T1) must be <= 65535");
+  bool out_ok = attention_out->dtype == FIA_DT_BF16 && attention_out->ndim == q->ndim;
+  for (int d = 0; out_ok && d < q->ndim; ++d) out_ok = attention_out->shape[d] == q->shape[d];
+  if (!out_ok) return fail(FIA_ERR_PARAM_INVALID, "attention_out must be bf16 with the shape of q");
+  if (tnd) {
+    if (cu_seqlens_q == nullptr) return fail(FIA_ERR_PARAM_INVALID, "TND requires cu_seqlens_q");
+    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q")) != FIA_SUCCESS) return st;
+    if (cu_seqlens_q->dtype != FIA_DT_INT32 || cu_seqlens_q->ndim != 1 ||
+        cu_seqlens_q->shape[0] != B + 1 || cu_seqlens_q->stride[0] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_q must be contiguous int32 [B + 1]");
+    }
+  } else if (cu_seqlens_q != nullptr) {
+    return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_q is only for layout_q TND");
   }
   auto check_pool = [&](const fia_tensor* t, const char* name, int64_t* nb, int64_t* bs,
                         int64_t* sb, int64_t* ss) -> fia_status {
@@ -1082,15 +1102,19 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   if (cmp_sparse_indices != nullptr) {
     if ((st = check_tensor(cmp_sparse_indices, "cmp_sparse_indices")) != FIA_SUCCESS) return st;
     const fia_tensor* t = cmp_sparse_indices;
-    if (t->dtype != FIA_DT_INT32 || t->ndim != 4 || t->shape[0] != B || t->shape[1] != S1 ||
-        t->shape[2] != 1) {
-      return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices must be int32 [B, S1, 1, K2]");
+    const bool shape_ok = tnd ? (t->ndim == 3 && t->shape[0] == n_rows && t->shape[1] == 1)
+                              : (t->ndim == 4 && t->shape[0] == B && t->shape[1] == S1 && t->shape[2] == 1);
+    if (t->dtype != FIA_DT_INT32 || !shape_ok) {
+      return fail(FIA_ERR_PARAM_INVALID, tnd ? "cmp_sparse_indices must be int32 [T1, 1, K2]"
+                                             : "cmp_sparse_indices must be int32 [B, S1, 1, K2]");
     }
-    K2 = t->shape[3];
+    K2 = t->shape[t->ndim - 1];
     if (K2 != 512 && K2 != 1024) return fail(FIA_ERR_PARAM_INVALID, "K2 must be 512 or 1024");
-    idx_sb = t->stride[0];
-    idx_ss = t->stride[1];
-    if (t->stride[3] != 1) return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices rows must be contiguous");
+    idx_sb = tnd ? 0 : t->stride[0];
+    idx_ss = tnd ? t->stride[0] : t->stride[1];
+    if (t->stride[t->ndim - 1] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices rows must be contiguous");
+    }
   }
   auto check_bt = [&](const fia_tensor* t, const char* name, int64_t need) -> fia_status {
     fia_status s2 = check_tensor(t, name);
@@ -1123,15 +1147,17 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
       }
     }
   }
-  if (seqused_kv->dtype != FIA_DT_INT32 || seqused_kv->ndim != 1 || seqused_kv->shape[0] != B) {
-    return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
-  }
+  if (seqused_kv->shape[0] != B) return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
   if (sinks->dtype != FIA_DT_FP32 || sinks->ndim != 1 || sinks->shape[0] != N1) {
     return fail(FIA_ERR_PARAM_INVALID, "sinks must be fp32 [N1]");
   }
-  if (q->stride[1] % 8 || q->stride[2] % 8 || q->stride[0] % 8 || attention_out->stride[0] % 8 ||
-      attention_out->stride[2] % 8 || reinterpret_cast<uintptr_t>(q->data) % 16 ||
-      reinterpret_cast<uintptr_t>(attention_out->data) % 16) {
+  for (int d = 0; d + 1 < q->ndim; ++d) {
+    if (q->stride[d] % 8 || attention_out->stride[d] % 8) {
+      return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
+    }
+  }
+  if (q->stride[q->ndim - 1] != 1 || attention_out->stride[q->ndim - 1] != 1 ||
+      reinterpret_cast<uintptr_t>(q->data) % 16 || reinterpret_cast<uintptr_t>(attention_out->data) % 16) {
     return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
   }
 
@@ -1139,13 +1165,15 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   e->kind = KIND_SPARSE;
   SparseArgs& a = e->sp;
   a.q = static_cast<const uint16_t*>(q->data);
-  a.q_sb = q->stride[0];
-  a.q_ss = q->stride[1];
-  a.q_sh = q->stride[2];
+  a.q_sb = tnd ? 0 : q->stride[0];
+  a.q_ss = q->stride[tnd ? 0 : 1];
+  a.q_sh = q->stride[tnd ? 1 : 2];
   a.o = static_cast<uint16_t*>(attention_out->data);
-  a.o_sb = attention_out->stride[0];
-  a.o_ss = attention_out->stride[1];
-  a.o_sh = attention_out->stride[2];
+  a.o_sb = tnd ? 0 : attention_out->stride[0];
+  a.o_ss = attention_out->stride[tnd ? 0 : 1];
+  a.o_sh = attention_out->stride[tnd ? 1 : 2];
+  a.cu_q = tnd ? static_cast<const int32_t*>(cu_seqlens_q->data) : nullptr;
+  a.n_rows = (int32_t)n_rows;
   a.ori = static_cast<const uint8_t*>(ori_kv->data);
   a.ori_sb = osb;
   a.ori_ss = oss;
@@ -1181,7 +1209,7 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   a.scale_log2 = (float)(p->softmax_scale * 1.4426950408889634);
   const int64_t n_chunks = a.n_slots / fia::kSparseChunk;
   e->part_o_off = 0;
-  const size_t rows = (size_t)B * S1;
+  const size_t rows = (size_t)n_rows;
   e->part_lse_off = align_up(rows * n_chunks * N1 * fia::kSparseD * sizeof(float), kAlign);
   e->ws_size = align_up(e->part_lse_off + rows * n_chunks * N1 * sizeof(float), kAlign);
   *workspace_size = e->ws_size;

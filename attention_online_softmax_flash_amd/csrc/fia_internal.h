@@ -105,12 +105,16 @@ struct AttnArgs {
 
 // Shared-KV sparse decode arguments.
 struct SparseArgs {
-  // Row r = b * S1 + t is query token t of batch entry b; partials and the
-  // grid run over the B * S1 rows.
-  const uint16_t* q;                // bf16 [B, S1, N1, 512]
+  // BSND: row r = b * S1 + t is query token t of batch entry b.  TND: row r
+  // is token r of [T1, N1, 512]; its batch entry b satisfies
+  // cu_q[b] <= r < cu_q[b + 1] (batch strides are 0, token strides address
+  // the row).  Partials and the grid run over the n_rows rows.
+  const uint16_t* q;                // bf16 [B, S1, N1, 512] or [T1, N1, 512]
   int64_t q_sb, q_ss, q_sh;
-  uint16_t* o;                      // bf16 [B, S1, N1, 512]
+  uint16_t* o;                      // bf16, the shape of q
   int64_t o_sb, o_ss, o_sh;
+  const int32_t* cu_q;              // TND: int32 [B + 1] on the device; BSND: nullptr
+  int32_t n_rows;                   // B * S1 (BSND) or T1 (TND)
   const uint8_t* ori;               // [nb1, bs1, 1, 640]
   int64_t ori_sb, ori_ss;           // bytes
   const uint8_t* cmp;
@@ -119,7 +123,7 @@ struct SparseArgs {
   int64_t ori_bt_sb;
   const int32_t* cmp_bt;
   int64_t cmp_bt_sb;
-  const int32_t* idx;               // [B, S1, 1, K2]
+  const int32_t* idx;               // [B, S1, 1, K2] or [T1, 1, K2]
   int64_t idx_sb, idx_ss;
   const int32_t* seqused;           // [B]
   const float* sinks;               // [N1]
@@ -132,8 +136,8 @@ struct SparseArgs {
   int32_t has_cmp;
   int32_t cmp_direct;               // no indices: compressed slot k is row k
   float scale_log2;
-  float* part_o;                    // [B * S1 * n_chunks * N1 * 512]
-  float* part_lse;                  // [B * S1 * n_chunks * N1]
+  float* part_o;                    // [n_rows * n_chunks * N1 * 512]
+  float* part_lse;                  // [n_rows * n_chunks * N1]
 };
 
 // Launchers (defined next to their kernels).  Return hipGetLastError().

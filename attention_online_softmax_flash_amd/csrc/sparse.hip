@@ -3,9 +3,10 @@
 // original KV followed by the top-k selected rows of the compressed KV, plus a
 // per-head sink logit.
 //
-// Row list of query token t of batch b (the S1 tokens are the last S1
-// positions of the KV sequence: p = Lk - S1 + t), as fixed slots so a
-// result never depends on the other batch entries:
+// Row list of query token t of batch b (the S1 tokens of the entry are the
+// last S1 positions of its KV sequence: p = Lk - S1 + t; with the TND layout
+// S1 is the entry's own count cu_seqlens_q[b + 1] - cu_seqlens_q[b]), as
+// fixed slots so a result never depends on the other batch entries:
 //   slots [0, n_win_slots): window row j = p - win_left + s, used when
 //     0 <= j <= min(Lk - 1, p + win_right) (band);
 //   slots [n_win_slots, n_win_slots + K2): compressed row c = idx[b][t][s - n_win]
@@ -47,20 +48,58 @@ __device__ __forceinline__ void e4m3fn_x4(uint32_t w, float* f) {
   f[3] = hi[1];
 }
 
-// Slots s[0..N) of row r = b * S1 + t -> packed row addresses (nullptr for an unused
+// Batch entry, token position and query count of row r.  BSND: b = r / S1.
+// TND: the entry b with cu_q[b] <= r < cu_q[b + 1], by binary search over the
+// cumulative counts (values as read; a row outside every entry, possible
+// only with inconsistent counts, is dead: no key rows, output 0).  tq is the
+// token index the query, output and index rows are addressed with (their
+// batch strides are 0 with TND).
+struct SparseRow {
+  int b, t, s1, tq;
+  bool live;
+};
+__device__ __forceinline__ SparseRow sparse_row(const SparseArgs& a, int r) {
+  SparseRow w;
+  if (a.cu_q == nullptr) {
+    w.b = r / a.S1;
+    w.t = r - w.b * a.S1;
+    w.s1 = a.S1;
+    w.tq = w.t;
+    w.live = true;
+    return w;
+  }
+  int lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_q[mid] <= r) {
+      lo = mid;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  const int c0 = a.cu_q[lo], c1 = a.cu_q[lo + 1];
+  w.b = lo;
+  w.tq = r;
+  w.live = c0 <= r && r < c1;
+  w.t = w.live ? r - c0 : 0;
+  w.s1 = w.live ? c1 - c0 : 1;
+  return w;
+}
+
+// Slots s[0..N) of query row w -> packed row addresses (nullptr for an unused
 // slot) and ids: j for window row j, (1 << 30) | c for compressed row c, -1
 // if unused.  Compressed slot k holds row idx[b][k] (compressed-sparse) or
 // row k itself (heavily compressed, no indices).  No read depends on a branch: every table read goes to an
 // in-bounds address (a clamped position), so the N index reads, then the N
 // block-table reads, are each in flight together.
 template <int N>
-__device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int r, const int* s, int Lk,
-                                                 const uint8_t** row, int32_t* id) {
-  const int b = r / a.S1;
-  const int t = r - b * a.S1;
-  const int p = Lk - a.S1 + t;
+__device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, const SparseRow& w, const int* s,
+                                                 int Lk, const uint8_t** row, int32_t* id) {
+  const int b = w.b;
+  const int t = w.t;
+  const int p = Lk - w.s1 + t;
   const int jmax = min(Lk - 1, p + a.win_right);
-  const int n_cmp = Lk / a.cmp_ratio - (a.S1 - 1 - t);
+  const int n_cmp = Lk / a.cmp_ratio - (w.s1 - 1 - t);
   const bool cmp_on = a.has_cmp && a.K2 > 0;
   int c[N];
 #pragma unroll
@@ -69,7 +108,7 @@ __device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int r, con
     if (a.cmp_direct) {
       c[u] = cmp_on ? s[u] - a.n_win_slots : -1;
     } else {
-      c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + (int64_t)t * a.idx_ss + k] : -1;
+      c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + (int64_t)w.tq * a.idx_ss + k] : -1;
     }
   }
   int raw[N], slot[N];
@@ -105,13 +144,14 @@ __device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, int r, con
   }
 }
 
-__device__ __forceinline__ int sparse_len(const SparseArgs& a, int b) {
-  int Lk = a.seqused[b];
+__device__ __forceinline__ int sparse_len(const SparseArgs& a, const SparseRow& w) {
+  if (!w.live) return 0;
+  int Lk = a.seqused[w.b];
   const int cap = a.ori_bt_cols * a.bs1;
   return Lk < 0 ? 0 : (Lk > cap ? cap : Lk);
 }
 
-// Grid: (n_slots / 64, N1 / 32, B * S1); 256 threads.
+// Grid: (n_slots / 64, N1 / 32, n_rows); 256 threads.
 __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xs = lds;                         // [64][X_PITCH]
@@ -123,16 +163,16 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
 
   const int chunk = blockIdx.x;
   const int hb = blockIdx.y;
-  const int r = blockIdx.z;   // row b * S1 + t
-  const int b = r / a.S1;
-  const int t = r - b * a.S1;
+  const int r = blockIdx.z;   // query row
+  const SparseRow qr = sparse_row(a, r);
+  const int b = qr.b;
   const int n_chunks = gridDim.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = uniform(tid >> 6);   // wave-uniform: scalar bookkeeping
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int Lk = sparse_len(a, b);
+  const int Lk = sparse_len(a, qr);
   const int s0 = chunk * kSparseChunk;
   const int sb = wave & 1;
   const int dh = wave >> 1;
@@ -142,7 +182,7 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
   // the row gather: head n, d = 256 dh + 16 c + 8 hh .. +7.
   u32x4 qv[16];
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)t * a.q_ss + (int64_t)head * a.q_sh +
+    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss + (int64_t)head * a.q_sh +
                          256 * dh + 8 * hh;
 #pragma unroll
     for (int c = 0; c < 16; ++c) qv[c] = ld16(qp + 16 * c);
@@ -162,7 +202,7 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
     for (int u = 0; u < 4; ++u) sl[u] = s0 + 4 * rg + u;
     const uint8_t* rows[4];
     int32_t rid[4];
-    sparse_slot_rows<4>(a, r, sl, Lk, rows, rid);
+    sparse_slot_rows<4>(a, qr, sl, Lk, rows, rid);
     if (pc0 == 0) {
 #pragma unroll
       for (int u = 0; u < 4; ++u) ids[4 * rg + u] = rid[u];
@@ -306,11 +346,10 @@ __global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   const int lane = threadIdx.x & 63;
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.B * a.S1 * a.N1) return;
-  const int r = row / a.N1;   // b * S1 + t
+  if (row >= a.n_rows * a.N1) return;
+  const int r = row / a.N1;   // query row
   const int h = row - r * a.N1;
-  const int b = r / a.S1;
-  const int t = r - b * a.S1;
+  const SparseRow qr = sparse_row(a, r);
   const int n_chunks = a.n_slots / kSparseChunk;   // <= 64 (K2 <= 1024)
   const float sink = a.sinks[h] * kLog2e;
   const float lc = lane < n_chunks ? a.part_lse[((int64_t)r * n_chunks + lane) * a.N1 + h] : kNegInf;
@@ -357,25 +396,25 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)t * a.o_ss + (int64_t)h * a.o_sh + 8 * lane;
+  uint16_t* op = a.o + (int64_t)qr.b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)h * a.o_sh + 8 * lane;
   st16(op, u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
                  pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)});
 }
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
-  if (a.B == 0) return hipSuccess;
+  if (a.n_rows == 0) return hipSuccess;
   // Dynamic LDS above the default limit must be enabled for the kernel (on
   // the current device); the call is cheap, so it is made on every launch.
   const hipError_t attr = hipFuncSetAttribute(
       (const void*)sparse_chunk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
   if (attr != hipSuccess) return attr;
-  dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.B * a.S1);
+  dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.n_rows);
   sparse_chunk<<<grid, 256, LDS_TOTAL, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
-  const int rows = a.B * a.S1 * a.N1;
+  const int rows = a.n_rows * a.N1;
   if (rows > 0) sparse_merge<<<(rows + 3) / 4, 256, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -383,13 +422,14 @@ hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
 // Test support: slot ids and raw row bytes, through sparse_slot_rows.
 __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* ids, uint8_t* rows) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)a.B * a.S1 * a.n_slots;
+  const int64_t total = (int64_t)a.n_rows * a.n_slots;
   if (t >= total) return;
-  const int r = (int)(t / a.n_slots);   // b * S1 + query token
+  const int r = (int)(t / a.n_slots);   // query row
   const int s = (int)(t % a.n_slots);
   int32_t id;
   const uint8_t* row;
-  sparse_slot_rows<1>(a, r, &s, sparse_len(a, r / a.S1), &row, &id);
+  const SparseRow qr = sparse_row(a, r);
+  sparse_slot_rows<1>(a, qr, &s, sparse_len(a, qr), &row, &id);
   ids[t] = id;
   uint32_t* dst = reinterpret_cast<uint32_t*>(rows + t * kRowBytes);
   for (int w = 0; w < kRowBytes / 4; ++w) {
@@ -399,7 +439,7 @@ __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* 
 
 hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* rows,
                                     hipStream_t s) {
-  const int64_t total = (int64_t)a.B * a.S1 * a.n_slots;
+  const int64_t total = (int64_t)a.n_rows * a.n_slots;
   if (total > 0) debug_sparse_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a, ids, rows);
   return hipGetLastError();
 }

@@ -118,8 +118,8 @@ def lib():
                                          _TP, _TP, ctypes.POINTER(sz), ctypes.POINTER(vp)]
     L.fia_sparse_get_workspace_size.restype = ctypes.c_int
     L.fia_sparse_get_workspace_size.argtypes = [ctypes.POINTER(FiaSparseParams), _TP, _TP, _TP, _TP,
-                                                _TP, _TP, _TP, _TP, ctypes.c_int64, _TP, _TP, _TP,
-                                                ctypes.POINTER(sz), ctypes.POINTER(vp)]
+                                                _TP, _TP, _TP, _TP, _TP, ctypes.c_int64, _TP, _TP,
+                                                _TP, ctypes.POINTER(sz), ctypes.POINTER(vp)]
     L.fia_run.restype = ctypes.c_int
     L.fia_run.argtypes = [vp, sz, vp, vp]
     L.fia_executor_destroy.restype = None
@@ -311,12 +311,12 @@ class SparsePlan(_Plan):
                  ori_win_left=127, ori_win_right=0, ori_mask_mode=4, cmp_mask_mode=3,
                  kv_quant_mode=1, tile_size=64, rope_head_dim=64, layout_q="BSND",
                  layout_kv="PA_ND", return_softmax_lse=False, ori_sparse_indices=None,
-                 attention_out=None):
+                 cu_seqlens_q=None, attention_out=None):
         L = lib()
         if attention_out is None:
             attention_out = torch.empty_like(q)
         self.tensors = (q, ori_kv, cmp_kv, cmp_sparse_indices, ori_block_table, cmp_block_table,
-                        seqused_kv, sinks, ori_sparse_indices)
+                        seqused_kv, sinks, ori_sparse_indices, cu_seqlens_q)
         self.out = attention_out
         p = FiaSparseParams()
         p.softmax_scale = softmax_scale
@@ -333,7 +333,7 @@ class SparsePlan(_Plan):
         p.return_softmax_lse = 1 if return_softmax_lse else 0
         self._params = p
         d = [describe(t) for t in (q, ori_kv, cmp_kv, ori_sparse_indices, cmp_sparse_indices,
-                                   ori_block_table, cmp_block_table, seqused_kv)]
+                                   ori_block_table, cmp_block_table, cu_seqlens_q, seqused_kv)]
         ds, dout = describe(sinks), describe(attention_out)
         self._descs = d + [ds, dout]
         ws = ctypes.c_size_t(0)
@@ -347,13 +347,13 @@ class SparsePlan(_Plan):
 
     def debug_rows(self, stream=None):
         """(ids [B, S1, n_slots] int32, rows [B, S1, n_slots, 640] uint8) as the
-        kernel gathers them."""
+        kernel gathers them; [T1, n_slots] and [T1, n_slots, 640] with TND."""
         n = ctypes.c_int32(0)
         _check(lib().fia_debug_sparse_rows(self._exec, None, 0, None, None, ctypes.byref(n), None))
-        B, S1 = self.tensors[0].shape[0], self.tensors[0].shape[1]
+        lead = tuple(self.tensors[0].shape[:-2])
         dev = self.tensors[0].device
-        ids = torch.empty((B, S1, n.value), dtype=torch.int32, device=dev)
-        rows = torch.empty((B, S1, n.value, 640), dtype=torch.uint8, device=dev)
+        ids = torch.empty(lead + (n.value,), dtype=torch.int32, device=dev)
+        rows = torch.empty(lead + (n.value, 640), dtype=torch.uint8, device=dev)
         _check(lib().fia_debug_sparse_rows(self._exec, self.workspace.data_ptr(),
                                            self.workspace.numel(), ids.data_ptr(),
                                            rows.data_ptr(), ctypes.byref(n),

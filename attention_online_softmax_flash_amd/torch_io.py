@@ -96,6 +96,8 @@ def sparse_tensors(case: SparseCase, device="cuda"):
         cmp_block_table=torch.from_numpy(case.cmp_block_table).to(device),
         seqused_kv=torch.tensor(case.seqused_kv, dtype=torch.int32, device=device),
         sinks=torch.from_numpy(case.sinks).to(device),
+        cu_seqlens_q=(None if case.cu_seqlens_q is None
+                      else torch.tensor(case.cu_seqlens_q, dtype=torch.int32, device=device)),
     )
 
 
@@ -105,7 +107,9 @@ def sparse_plan(case: SparseCase, device="cuda", tensors=None) -> fia.SparsePlan
                           t["ori_block_table"], t["cmp_block_table"], t["seqused_kv"],
                           t["sinks"], softmax_scale=case.softmax_scale,
                           max_seqused_kv=max(case.seqused_kv), cmp_ratio=case.cmp_ratio,
-                          ori_win_left=case.win_left, ori_win_right=case.win_right)
+                          ori_win_left=case.win_left, ori_win_right=case.win_right,
+                          layout_q="BSND" if case.cu_seqlens_q is None else "TND",
+                          cu_seqlens_q=t["cu_seqlens_q"])
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -418,12 +418,12 @@ def c4_alibi_prefill(seed=SEEDS["c4"], S=8192, lse=False) -> DenseCase:
 @dataclasses.dataclass
 class SparseCase:
     name: str
-    q: np.ndarray                  # bf16 bits [B, S1, N1, 512]
+    q: np.ndarray                  # bf16 bits [B, S1, N1, 512], or [T1, N1, 512] with cu_seqlens_q
     ori_kv: np.ndarray             # uint8 [nb1, bs1, 1, 640]
     cmp_kv: np.ndarray             # uint8 [nb2, bs2, 1, 640]
     ori_block_table: np.ndarray    # int32 [B, >= ceil(max S2 / bs1)]
     cmp_block_table: np.ndarray    # int32 [B, >= ceil(floor(max S2 / ratio) / bs2)]
-    cmp_sparse_indices: Optional[np.ndarray]  # int32 [B, S1, 1, K2]; -1 = invalid; None: every compressed row
+    cmp_sparse_indices: Optional[np.ndarray]  # int32 [B, S1, 1, K2] or [T1, 1, K2]; -1 = invalid; None: every compressed row
     seqused_kv: list
     sinks: np.ndarray              # float32 [N1]
     softmax_scale: float
@@ -431,6 +431,7 @@ class SparseCase:
     win_left: int = 127
     win_right: int = 0
     seed: int = 0
+    cu_seqlens_q: Optional[list] = None   # TND: cumulative query-token counts [B + 1]
 
 
 def pack_rows(rng, n_rows: int) -> np.ndarray:
@@ -521,6 +522,29 @@ def sparse_case(name, seed, *, B, N1, seqused_kv, K2=512, block_size1=128,
                       cmp_sparse_indices=idx, seqused_kv=[int(x) for x in seqused_kv],
                       sinks=sinks, softmax_scale=1.0 / math.sqrt(SPARSE_D),
                       cmp_ratio=cmp_ratio, seed=seed)
+
+
+def sparse_tnd_case(name, seed, *, q_counts, **kw) -> SparseCase:
+    """The TND form of :func:`sparse_case`: batch entry b has q_counts[b]
+    query tokens (possibly 0), packed into T1 = sum(q_counts) rows, with
+    cu_seqlens_q = [0, q_counts[0], q_counts[0] + q_counts[1], ...].
+
+    Drawn as a BSND case with S1 = max(q_counts) whose entry b keeps its last
+    q_counts[b] tokens: those sit at the same KV positions (the last
+    q_counts[b] of the sequence) as the TND tokens of entry b."""
+    s1max = max(1, max(q_counts))
+    base = sparse_case(name, seed, S1=s1max, **kw)
+    keep = [slice(s1max - c, s1max) for c in q_counts]
+    q = np.concatenate([base.q[b, keep[b]] for b in range(len(q_counts))], axis=0)
+    idx = None
+    if base.cmp_sparse_indices is not None:
+        idx = np.ascontiguousarray(np.concatenate(
+            [base.cmp_sparse_indices[b, keep[b]] for b in range(len(q_counts))], axis=0))
+    cu = [0]
+    for c in q_counts:
+        cu.append(cu[-1] + int(c))
+    return dataclasses.replace(base, q=np.ascontiguousarray(q), cmp_sparse_indices=idx,
+                               cu_seqlens_q=cu)
 
 
 def c5_sparse_sharedkv(seed=SEEDS["c5"], materialise_all_ori=False) -> SparseCase:

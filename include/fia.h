@@ -217,7 +217,7 @@ typedef struct {
   int32_t cmp_mask_mode;   /* 3 (right-down causal) */
   int32_t ori_win_left;    /* 127 */
   int32_t ori_win_right;   /* 0 */
-  const char* layout_q;    /* "BSND" */
+  const char* layout_q;    /* "BSND" (default) or "TND" */
   const char* layout_kv;   /* "PA_ND" */
   int32_t return_softmax_lse; /* must be 0 (reserved on the page) */
 } fia_sparse_params;
@@ -228,25 +228,34 @@ typedef struct {
  * batch entry are the last S1 positions of its KV sequence (token t at
  * p = Lk - S1 + t): its window is rows max(0, p - 127) .. p, and it sees the
  * compressed rows c < floor(Lk / cmp_ratio) - (S1 - 1 - t) (right-down
- * causal over the compressed sequence).
- *   q                  bf16 [B,S1,N1,512], N1 in {64,128}, B * S1 <= 65535;
+ * causal over the compressed sequence).  With layout_q "TND" the query
+ * tokens of all entries are packed into T1 rows and entry b owns rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b + 1] - 1 (its S1 is their count).
+ *   q                  bf16 [B,S1,N1,512] (BSND, B * S1 <= 65535) or
+ *                      [T1,N1,512] (TND, T1 <= 65535), N1 in {64,128};
  *                      logical dim order [rope(64) | nope(448)].
  *   ori_kv, cmp_kv     uint8 (or fp8_e4m3fn) PA_ND pools [n_blk, bs, 1, 640]:
  *                      per row bf16 rope x64 | e4m3fn nope x448 | fp32 scale x7
  *                      (one per 64-wide tile) | zero pad to 640 bytes.
  *   ori_sparse_indices must be NULL (reserved on the page).
- *   cmp_sparse_indices int32 [B,S1,1,K2], K2 in {512,1024}, rows contiguous;
+ *   cmp_sparse_indices int32 [B,S1,1,K2] (BSND) or [T1,1,K2] (TND), K2 in
+ *                      {512,1024}, rows contiguous;
  *                      entry c of token t is used iff 0 <= c and c is visible
  *                      to t (above).  NULL with cmp_kv: heavily compressed
  *                      mode, every compressed row visible to t is used
  *                      (max_seqused_kv / 128 + 128 <= 4096).
  *   ori_block_table    int32 [B, >= ceil(max Lk / bs1)].
  *   cmp_block_table    int32 [B, >= ceil(floor(max Lk / cmp_ratio) / bs2)].
+ *   cu_seqlens_q       TND only (NULL with BSND): int32 [B+1] device,
+ *                      cumulative query-token counts, non-decreasing, first
+ *                      0 and last T1 (SharedKV cu_seqlens_q).  Read on the
+ *                      device only; a row outside every entry (inconsistent
+ *                      counts) is written as 0.
  *   seqused_kv         int32 [B] device, KV length per batch (Lk).
  *   max_seqused_kv     host upper bound of seqused_kv, for table validation.
  *   sinks              fp32 [N1]: one extra logit per head with a zero value.
  *   metadata           ignored (the plan is built here), may be NULL.
- *   attention_out      bf16 [B,S1,N1,512].
+ *   attention_out      bf16, the shape of q.
  * K~ = V~ = window rows of ori_kv followed by the used cmp_kv rows. */
 fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
                                          const fia_tensor* q, const fia_tensor* ori_kv,
@@ -255,6 +264,7 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
                                          const fia_tensor* cmp_sparse_indices,
                                          const fia_tensor* ori_block_table,
                                          const fia_tensor* cmp_block_table,
+                                         const fia_tensor* cu_seqlens_q,
                                          const fia_tensor* seqused_kv, int64_t max_seqused_kv,
                                          const fia_tensor* sinks, const fia_tensor* metadata,
                                          const fia_tensor* attention_out,
@@ -290,10 +300,10 @@ int32_t fia_executor_kind(const fia_executor* executor);
 fia_status fia_debug_gather_kv(fia_executor* executor, void* workspace, size_t workspace_size,
                                int32_t which, void* dst, void* stream);
 
-/* Test support for the sparse executor: for every batch entry b and query
- * token t, the row list the kernel attends to, as fixed slots [B, S1,
- * n_slots]: ids_out[b, t, s] = j for window row j of ori_kv, (1 << 30) | c
- * for row c of cmp_kv, -1 for an unused slot; rows_out[b, t, s, 0..639] =
+/* Test support for the sparse executor: for every query row (BSND: batch
+ * entry b, token t; TND: packed token r), the row list the kernel attends
+ * to, as fixed slots [B, S1, n_slots] or [T1, n_slots]: ids_out[.., s] = j for window row j of ori_kv, (1 << 30) | c
+ * for row c of cmp_kv, -1 for an unused slot; rows_out[.., s, 0..639] =
  * the raw packed bytes of that row (zero when unused).  n_slots is returned through *n_slots_out (ids_out may be NULL to
  * query it). */
 fia_status fia_debug_sparse_rows(fia_executor* executor, void* workspace, size_t workspace_size,

@@ -399,25 +399,42 @@ def sparse_rows(Lk: int, S1: int, t: int, idx_row, *, cmp_ratio: int,
 
 
 def sparse_sharedkv(case, *, batches=None):
-    """Shared-KV sparse attention output, float64 [B, S1, N1, 512].
+    """Shared-KV sparse attention output, float64 [B, S1, N1, 512] (BSND) or
+    [T1, N1, 512] (TND: ``case.cu_seqlens_q`` set).
 
     For each (b, query token t, head h): X = rows (window ++ compressed) of
     :func:`sparse_rows`, scores
     s_r = softmax_scale * (q_h . x_r), an extra sink logit sigma_h with a zero
     value vector, out = sum_r exp(s_r - m) x_r / (exp(sigma_h - m) + sum_r
     exp(s_r - m)).  K~ = V~ = X.
+
+    TND (SharedKV layout_q TND, cu_seqlens_q): entry b owns packed rows
+    cu[b] .. cu[b + 1] - 1, its S1 is their count and its token t is row
+    cu[b] + t.  Reading: a packed row outside every entry (possible only with
+    inconsistent counts) is 0.
     """
     q = case.q
-    B, S1, N1, Dq = q.shape
+    Dq = q.shape[-1]
+    N1 = q.shape[-2]
     bs1 = case.ori_kv.shape[1]
     bs2 = case.cmp_kv.shape[1]
-    out = np.full((B, S1, N1, Dq), np.nan)
     sinks = np.asarray(case.sinks, dtype=np.float32).astype(np.float64)
+    B = len(case.seqused_kv)
+    if case.cu_seqlens_q is None:
+        S1 = q.shape[1]
+        out = np.full((B, S1, N1, Dq), np.nan)
+        rows_of = lambda b: [(t, S1, (b, t)) for t in range(S1)]
+        idx_of = lambda key: case.cmp_sparse_indices[key[0], key[1], 0]
+    else:
+        cu = [int(x) for x in case.cu_seqlens_q]
+        out = np.zeros((q.shape[0], N1, Dq))
+        rows_of = lambda b: [(t, cu[b + 1] - cu[b], cu[b] + t) for t in range(cu[b + 1] - cu[b])]
+        idx_of = lambda key: case.cmp_sparse_indices[key, 0]
     for b in (range(B) if batches is None else batches):
         Lk = int(case.seqused_kv[b])
-        for t in range(S1):
-            idx_row = None if case.cmp_sparse_indices is None else case.cmp_sparse_indices[b, t, 0]
-            win, comp = sparse_rows(Lk, S1, t, idx_row,
+        for t, S1b, key in rows_of(b):
+            idx_row = None if case.cmp_sparse_indices is None else idx_of(key)
+            win, comp = sparse_rows(Lk, S1b, t, idx_row,
                                     cmp_ratio=case.cmp_ratio, win_left=case.win_left,
                                     win_right=case.win_right)
             X = []
@@ -426,10 +443,10 @@ def sparse_sharedkv(case, *, batches=None):
             for c in comp:
                 X.append(decode_packed_row(case.cmp_kv[case.cmp_block_table[b, c // bs2], c % bs2, 0]))
             X = np.stack(X) if X else np.zeros((0, Dq))
-            qb = decode_bf16(q[b, t])                           # [N1, 512]
+            qb = decode_bf16(q[key])                            # [N1, 512]
             s = case.softmax_scale * (qb @ X.T)                 # [N1, R]
             for h in range(N1):
                 o, _ = softmax_rows(s[h:h + 1], np.ones((1, X.shape[0]), bool), X,
                                     extra_logit=float(sinks[h]))
-                out[b, t, h] = o[0]
+                out[key][h] = o[0]
     return out

@@ -521,7 +521,7 @@ def sparse_plan_status(**over):
              cmp=T((16, 128, 1, 640), fia.DT_UINT8), idx=T((B, 1, 1, 512), fia.DT_INT32),
              obt=T((B, 16), fia.DT_INT32), cbt=T((B, 4), fia.DT_INT32),
              seq=T((B,), fia.DT_INT32), sinks=T((N1,), fia.DT_FP32), out=T((B, 1, N1, 512)),
-             oidx=None, max_seq=2048)
+             oidx=None, cu=None, max_seq=2048)
     p = fia.FiaSparseParams()
     p.softmax_scale = 0.0441941738
     p.kv_quant_mode, p.tile_size, p.rope_head_dim, p.cmp_ratio = 1, 64, 64, 4
@@ -537,7 +537,7 @@ def sparse_plan_status(**over):
     ptr = lambda d: ctypes.pointer(d) if d is not None else None
     st = fia.lib().fia_sparse_get_workspace_size(
         ctypes.byref(p), ptr(t["q"]), ptr(t["ori"]), ptr(t["cmp"]), ptr(t["oidx"]), ptr(t["idx"]),
-        ptr(t["obt"]), ptr(t["cbt"]), ptr(t["seq"]), t["max_seq"], ptr(t["sinks"]), None,
+        ptr(t["obt"]), ptr(t["cbt"]), ptr(t["cu"]), ptr(t["seq"]), t["max_seq"], ptr(t["sinks"]), None,
         ptr(t["out"]), ctypes.byref(ws), ctypes.byref(ex))
     msg = fia.lib().fia_last_error().decode()
     if st == 0:
@@ -572,7 +572,24 @@ def sparse_plan_status(**over):
     (dict(obt=T((2, 15), fia.DT_INT32)), BAD),
     (dict(cbt=T((2, 3), fia.DT_INT32)), BAD),
     (dict(return_softmax_lse=1), BAD),
-    (dict(layout_q=b"TND"), UNS),
+    (dict(layout_q=b"TND"), BAD),                     # TND needs [T1, N1, 512] and cu_seqlens_q
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), idx=T((5, 1, 512), fia.DT_INT32),
+          cu=T((3,), fia.DT_INT32)), 0),
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), idx=None, cmp_ratio=128,
+          cu=T((3,), fia.DT_INT32)), 0),
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), idx=T((5, 1, 512), fia.DT_INT32)),
+     BAD),                                            # cu_seqlens_q missing
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), idx=T((5, 1, 512), fia.DT_INT32),
+          cu=T((2,), fia.DT_INT32)), BAD),            # cu_seqlens_q must be [B + 1]
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), idx=T((5, 1, 512), fia.DT_INT32),
+          cu=T((3,), fia.DT_INT64)), BAD),
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), idx=T((2, 1, 1, 512), fia.DT_INT32),
+          cu=T((3,), fia.DT_INT32)), BAD),            # indices [T1, 1, K2] with TND
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((4, 64, 512)), idx=T((5, 1, 512), fia.DT_INT32),
+          cu=T((3,), fia.DT_INT32)), BAD),
+    (dict(layout_q=b"TND", q=T((70000, 64, 512)), out=T((70000, 64, 512)),
+          idx=T((70000, 1, 512), fia.DT_INT32), cu=T((3,), fia.DT_INT32)), UNS),
+    (dict(cu=T((3,), fia.DT_INT32)), BAD),            # cu_seqlens_q only with TND
     (dict(layout_kv=b"BSND"), BAD),
     (dict(sinks=T((64,), fia.DT_BF16)), BAD),
     (dict(q=T((2, 2, 64, 512)), out=T((2, 2, 64, 512)), idx=T((2, 2, 1, 512), fia.DT_INT32)), 0),

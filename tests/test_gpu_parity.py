@@ -540,6 +540,68 @@ def test_sparse_multi_token_rows_are_bit_exact():
                     assert np.array_equal(rows[b, t, s], case.ori_kv[case.ori_block_table[b, x // 32], x % 32, 0])
 
 
+SPARSE_TND_CASES = [
+    # (q_counts, N1, seqused, K2, hca)
+    ([1, 3, 0, 2], 64, [300, 5000, 77, 1000], 512, False),
+    ([2, 1], 128, [9, 4000], 1024, False),
+    ([3, 1, 2], 64, [1000, 4000, 130], 0, True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(SPARSE_TND_CASES)))
+def test_sparse_tnd(i):
+    """layout_q TND: entry b owns packed rows cu[b] .. cu[b + 1] - 1 of q
+    [T1, N1, 512]; the row-to-entry map is read from cu_seqlens_q on the device."""
+    counts, N1, L, K2, hca = SPARSE_TND_CASES[i]
+    case = W.sparse_tnd_case(f"stnd{i}", 450 + i, q_counts=counts, B=len(counts), N1=N1,
+                             seqused_kv=L, K2=K2 or 512, block_size1=64, block_size2=32,
+                             heavily_compressed=hca, materialise_all_ori=False)
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    assert tuple(plan.out.shape) == (sum(counts), N1, 512)
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
+def test_sparse_tnd_rows_are_bit_exact():
+    counts = [2, 0, 4, 1]
+    case = W.sparse_tnd_case("stndr", 460, q_counts=counts, B=4, N1=64, seqused_kv=[40, 9, 3000, 700],
+                             K2=512, block_size1=32, block_size2=16, materialise_all_ori=False)
+    plan = TI.sparse_plan(case, DEV)
+    ids, rows = plan.debug_rows()
+    torch.cuda.synchronize()
+    ids, rows = ids.cpu().numpy(), rows.cpu().numpy()
+    assert ids.shape[0] == sum(counts)
+    n_win = 128
+    cu = case.cu_seqlens_q
+    for b, L in enumerate(case.seqused_kv):
+        for t in range(counts[b]):
+            r = cu[b] + t
+            win, comp = O.sparse_rows(L, counts[b], t, case.cmp_sparse_indices[r, 0], cmp_ratio=4,
+                                      win_left=127, win_right=0)
+            assert [int(x) for x in ids[r, :n_win] if x >= 0] == win, (b, t)
+            assert [int(x) & ((1 << 30) - 1) for x in ids[r, n_win:] if x >= 0] == comp, (b, t)
+            for s in range(ids.shape[1]):
+                x = int(ids[r, s])
+                if x < 0:
+                    assert not rows[r, s].any()
+                elif x >> 30:
+                    c = x & ((1 << 30) - 1)
+                    assert np.array_equal(rows[r, s], case.cmp_kv[case.cmp_block_table[b, c // 16], c % 16, 0])
+                else:
+                    assert np.array_equal(rows[r, s], case.ori_kv[case.ori_block_table[b, x // 32], x % 32, 0])
+
+
+def test_sparse_tnd_rows_outside_every_entry_are_zero():
+    """cu_seqlens_q ending before T1 (inconsistent counts): the rows past the
+    last entry are written as 0, the others as usual."""
+    case = W.sparse_tnd_case("stndz", 470, q_counts=[1, 2], B=2, N1=64, seqused_kv=[300, 80],
+                             K2=512, block_size1=32, block_size2=16, materialise_all_ori=False)
+    case.cu_seqlens_q = [0, 1, 2]
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    got = to_f64(plan.out)
+    assert np.all(got[2] == 0)
+    check_out(got, O.sparse_sharedkv(case))
+
+
 # ---------------------------------------------------------------------------
 # Bit-exact gathers and row selection.
 # ---------------------------------------------------------------------------
@@ -654,7 +716,7 @@ def test_sparse_batch_invariance():
                          materialise_all_ori=False)
     t = TI.sparse_tensors(case, DEV)
     full = run_plan(TI.sparse_plan(case, DEV, tensors=t))
-    sub = {k: (v[1:2].contiguous() if k not in ("ori_kv", "cmp_kv", "sinks") else v)
+    sub = {k: (v[1:2].contiguous() if v is not None and k not in ("ori_kv", "cmp_kv", "sinks") else v)
            for k, v in t.items()}
     one = run_plan(fia.SparsePlan(sub["q"], sub["ori_kv"], sub["cmp_kv"],
                                   sub["cmp_sparse_indices"], sub["ori_block_table"],

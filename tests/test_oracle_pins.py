@@ -797,6 +797,46 @@ def test_sparse_zero_query_closed_form_and_sink_limit():
         np.testing.assert_allclose(out[b, 0, 0], np.mean(X, axis=0), rtol=1e-12, atol=1e-14)
 
 
+def test_sparse_tnd_equals_bsnd_suffix():
+    """TND (SharedKV layout_q TND, cu_seqlens_q): entry b owns packed rows
+    cu[b] .. cu[b + 1] - 1 and its S1 is their count, so its tokens sit at the
+    last q_counts[b] KV positions -- the same positions as the last
+    q_counts[b] tokens of the BSND form with S1 = max(q_counts).  Row for row
+    the two results are the same; an entry with no token owns no row."""
+    counts = [2, 0, 3, 1]
+    kw = dict(B=4, N1=4, seqused_kv=[300, 50, 700, 9], K2=16, block_size1=32, block_size2=16,
+              materialise_all_ori=False)
+    tnd = W.sparse_tnd_case("t", 63, q_counts=counts, **kw)
+    base = W.sparse_case("t", 63, S1=3, **kw)
+    assert tnd.cu_seqlens_q == [0, 2, 2, 5, 6] and tnd.q.shape == (6, 4, 512)
+    out_t, out_b = O.sparse_sharedkv(tnd), O.sparse_sharedkv(base)
+    assert out_t.shape == (6, 4, 512)
+    r = 0
+    for b, c in enumerate(counts):
+        for t in range(c):
+            np.testing.assert_array_equal(out_t[r], out_b[b, 3 - c + t])
+            r += 1
+    # heavily compressed mode, no indices
+    tnd = W.sparse_tnd_case("h", 64, q_counts=[1, 2], B=2, N1=4, seqused_kv=[700, 1500],
+                            block_size1=32, block_size2=16, heavily_compressed=True,
+                            materialise_all_ori=False)
+    base = W.sparse_case("h", 64, S1=2, B=2, N1=4, seqused_kv=[700, 1500], block_size1=32,
+                         block_size2=16, heavily_compressed=True, materialise_all_ori=False)
+    out_t, out_b = O.sparse_sharedkv(tnd), O.sparse_sharedkv(base)
+    np.testing.assert_array_equal(out_t[0], out_b[0, 1])
+    np.testing.assert_array_equal(out_t[1:], out_b[1])
+
+
+def test_sparse_tnd_rows_outside_every_entry_are_zero():
+    """Reading for inconsistent counts (cu[B] < T1): packed rows past the last
+    entry belong to no batch entry and are 0."""
+    c = W.sparse_tnd_case("z", 65, q_counts=[1, 2], B=2, N1=4, seqused_kv=[300, 80], K2=16,
+                          block_size1=32, block_size2=16, materialise_all_ori=False)
+    c.cu_seqlens_q = [0, 1, 2]
+    out = O.sparse_sharedkv(c)
+    assert np.all(out[2] == 0) and np.all(np.isfinite(out[:2])) and np.any(out[:2] != 0)
+
+
 def test_sparse_poisoned_rows_are_never_read():
     c = _small_sparse(seed=62, lens=(1000, 129))
     out = O.sparse_sharedkv(c)
