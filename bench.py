@@ -310,7 +310,7 @@ def main():
             "workload": "causal ALiBi prefill: B=1, Q_N=KV_N=16, S=8192, D=128",
             "unit": "TFLOP/s", "value": round(tf, 3), "algorithmic_flop": flops,
             "ms": round(kern_ms, 5), "kernels": "prefill_bf16<128, true>",
-            "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", None)}
+            "roofline": roofline("mfma", tf, PEAK_BF16_TFLOPS, "TFLOP/s", measured_traffic("prefill_bf16_alibi"))}
         del plan
 
     if want("c5"):
