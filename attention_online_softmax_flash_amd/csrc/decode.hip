@@ -38,6 +38,7 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
   item /= a.n_head_blocks;
   const int kvh = item % a.KVn;
   const int cg = item / a.KVn;
+  if (a.n_chunks_dev != nullptr && cg >= *a.n_chunks_dev) return;   // past the device plan's chunks
   const int b = a.work[2 * cg];
   const int c = a.work[2 * cg + 1];
   const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
@@ -388,6 +389,64 @@ hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s)
       else decode_split_bf16<64, false><<<n_items, 256, 0, s>>>(a);
     }
   }
+  return hipGetLastError();
+}
+
+// Device-side partitioner (the device counterpart of the host planner's
+// decode branch, for KV lengths that live on the device): one workgroup
+// walks the batch entries 1024 at a time.  Entry b gets Lk = its length
+// clamped into [0, kvlen_bound], its visible range for query row 0 (the same
+// rule as the kernels), nch = the 0-aligned chunks that range touches, and
+// its first chunk index from an exclusive prefix sum of nch in batch order;
+// the chunk list holds (b, c) for c < nch in that order, and the total goes
+// to meta[B * BF_COUNT].  The result is the plan the host would build for
+// the same lengths, so results are bitwise the same.
+__global__ __launch_bounds__(1024) void decode_partition(AttnArgs a, int32_t* meta, int32_t* work) {
+  __shared__ int32_t scan[1024];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < a.B; base += 1024) {
+    const int b = base + tid;
+    int Lk = 0, lo = 0, hi = 0, nch = 0;
+    if (b < a.B) {
+      Lk = a.dev_kvlen[b];
+      Lk = Lk < 0 ? 0 : (Lk > a.kvlen_bound ? a.kvlen_bound : Lk);
+      visible_range(a, 0, 1, Lk, lo, hi);
+      nch = hi > lo ? (hi + a.chunk - 1) / a.chunk - lo / a.chunk : 0;
+    }
+    scan[tid] = nch;
+    __syncthreads();
+    // inclusive scan over the 1024 entries of this round
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int add = tid >= off ? scan[tid - off] : 0;
+      __syncthreads();
+      scan[tid] += add;
+      __syncthreads();
+    }
+    const int first = carry + scan[tid] - nch;
+    if (b < a.B) {
+      int32_t* r = meta + (int64_t)b * BF_COUNT;
+      r[BF_QLEN] = 1;
+      r[BF_KVLEN] = Lk;
+      r[BF_QOFF] = 0;
+      r[BF_KVOFF] = 0;
+      r[BF_LO] = lo;
+      r[BF_HI] = hi;
+      r[BF_NCHUNK] = nch;
+      r[BF_CHUNK0] = first;
+      for (int c = 0; c < nch; ++c) {
+        work[2 * (first + c)] = b;
+        work[2 * (first + c) + 1] = c;
+      }
+    }
+    carry += scan[1023];
+    __syncthreads();
+  }
+  if (tid == 0) meta[(int64_t)a.B * BF_COUNT] = carry;
+}
+
+hipError_t launch_decode_partition(const AttnArgs& a, int32_t* meta, int32_t* work, hipStream_t s) {
+  if (a.B > 0) decode_partition<<<1, 1024, 0, s>>>(a, meta, work);
   return hipGetLastError();
 }
 

@@ -110,6 +110,7 @@ __global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(Att
   item /= a.n_head_blocks;
   const int kvh = item % a.KVn;
   const int cg = item / a.KVn;
+  if (a.n_chunks_dev != nullptr && cg >= *a.n_chunks_dev) return;   // past the device plan's chunks
   const int b = a.work[2 * cg];
   const int c = a.work[2 * cg + 1];
   const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;

@@ -146,6 +146,11 @@ struct fia_executor {
   size_t ws_size = 0;
   int32_t n_items = 0;        // decode workgroups
   int32_t s2max = 0;
+  // Decode with KV lengths on the device: the plan (per-batch records, the
+  // chunk count and the chunk list) is written into the workspace at
+  // dev_meta_off by the partitioner kernel on every run.
+  bool dev_len = false;
+  size_t dev_meta_off = 0, dev_work_off = 0;
   bool noop = false;
   // Device copy of `meta`, made by the first run on a device and reused by
   // every later run there (the plan never changes after phase 1).
@@ -177,8 +182,15 @@ fia_status upload_plan(fia_executor* e) {
 
 void bind_workspace(fia_executor* e, void* ws) {
   uint8_t* base = static_cast<uint8_t*>(ws);
-  e->a.meta = static_cast<const int32_t*>(e->dplan);
-  e->a.work = static_cast<const int32_t*>(e->dplan) + e->work_off;
+  if (e->dev_len) {
+    int32_t* m = reinterpret_cast<int32_t*>(base + e->dev_meta_off);
+    e->a.meta = m;
+    e->a.work = reinterpret_cast<const int32_t*>(base + e->dev_work_off);
+    e->a.n_chunks_dev = m + (size_t)e->a.B * fia::BF_COUNT;
+  } else {
+    e->a.meta = static_cast<const int32_t*>(e->dplan);
+    e->a.work = static_cast<const int32_t*>(e->dplan) + e->work_off;
+  }
   e->a.part_o = reinterpret_cast<float*>(base + e->part_o_off);
   e->a.part_lse = reinterpret_cast<float*>(base + e->part_lse_off);
   e->sp.part_o = reinterpret_cast<float*>(base + e->part_o_off);
@@ -351,6 +363,24 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
                          "actual_seq_lengths", &qlen)) != FIA_SUCCESS) {
     return st;
   }
+  // KV lengths on the device: an int32 [B] tensor read by the partitioner
+  // kernel at run time; the host sizes everything for the bound.
+  const bool dev_len = p->actual_seq_lengths_kv_device != nullptr;
+  const int64_t len_bound = p->max_actual_seq_length_kv;
+  if (dev_len) {
+    const fia_tensor* t = p->actual_seq_lengths_kv_device;
+    if ((st = check_tensor(t, "actual_seq_lengths_kv_device")) != FIA_SUCCESS) return st;
+    if (t->dtype != FIA_DT_INT32 || t->ndim != 1 || t->shape[0] != B || t->stride[0] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "actual_seq_lengths_kv_device must be contiguous int32 [B]");
+    }
+    if (p->actual_seq_lengths_kv != nullptr) {
+      return fail(FIA_ERR_PARAM_INVALID, "give actual_seq_lengths_kv or actual_seq_lengths_kv_device, not both");
+    }
+    if (tnd) return fail(FIA_ERR_PARAM_INVALID, "actual_seq_lengths_kv_device is not supported with TND");
+    if (len_bound < 0 || len_bound > kMaxLen) {
+      return fail(FIA_ERR_PARAM_INVALID, "max_actual_seq_length_kv must be in [0, 20971520]");
+    }
+  }
   int64_t max_q = 0;
   for (auto v : qlen) max_q = std::max(max_q, v);
 
@@ -373,7 +403,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     if (!d_64_128 && max_q == 1 && bs > 512) {
       return fail(FIA_ERR_PARAM_INVALID, "block_size must be <= 512 when Q_S == 1");
     }
-    if (!p->actual_seq_lengths_kv) {
+    if (!p->actual_seq_lengths_kv && !dev_len) {
       return fail(FIA_ERR_PARAM_INVALID, "paged attention requires actual_seq_lengths_kv");
     }
     const std::string kvl = p->kv_layout ? p->kv_layout : "PA_ND";
@@ -417,8 +447,13 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     pool_view(key, &ck);
     pool_view(value, &cv);
     std::vector<int64_t> kl;
-    if ((st = lengths_from(p->actual_seq_lengths_kv, p->actual_seq_lengths_kv_len, B,
-                           bt_cols * bs, false, 0, "actual_seq_lengths_kv", &kl)) != FIA_SUCCESS) {
+    if (dev_len) {
+      if (len_bound > bt_cols * bs) {
+        return fail(FIA_ERR_PARAM_INVALID, "max_actual_seq_length_kv exceeds block_table cols * block_size");
+      }
+      kl.assign((size_t)B, len_bound);
+    } else if ((st = lengths_from(p->actual_seq_lengths_kv, p->actual_seq_lengths_kv_len, B,
+                                  bt_cols * bs, false, 0, "actual_seq_lengths_kv", &kl)) != FIA_SUCCESS) {
       return st;
     }
     kvlen = kl;
@@ -440,8 +475,11 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     }
     if (ck.S != cv.S || ck.B != cv.B) return fail(FIA_ERR_PARAM_INVALID, "key and value shapes differ");
     if (!tnd && ck.B != B) return fail(FIA_ERR_PARAM_INVALID, "key batch must equal query batch");
-    if ((st = lengths_from(p->actual_seq_lengths_kv, p->actual_seq_lengths_kv_len, B, ck.S, tnd,
-                           ck.S, "actual_seq_lengths_kv", &kvlen)) != FIA_SUCCESS) {
+    if (dev_len) {
+      if (len_bound > ck.S) return fail(FIA_ERR_PARAM_INVALID, "max_actual_seq_length_kv exceeds KV_S");
+      kvlen.assign((size_t)B, len_bound);
+    } else if ((st = lengths_from(p->actual_seq_lengths_kv, p->actual_seq_lengths_kv_len, B, ck.S, tnd,
+                                  ck.S, "actual_seq_lengths_kv", &kvlen)) != FIA_SUCCESS) {
       return st;
     }
   }
@@ -774,6 +812,15 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   }
 
   // Build the executor.
+  if (dev_len) {
+    if (!(max_q <= 1 && cq.S == 1)) {
+      return fail(FIA_ERR_PARAM_INVALID, "actual_seq_lengths_kv_device needs query length 1 (decode)");
+    }
+    if (f32 || kvq) return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device needs bf16 query, key and value");
+    if (explicit_mask || pse_tensor) {
+      return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device does not take atten_mask or pse_shift tensors");
+    }
+  }
   fia_executor* e = new fia_executor();
   AttnArgs& a = e->a;
   a.q = query->data;
@@ -937,6 +984,32 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
         return fail(FIA_ERR_UNSUPPORTED, "query too long for the prefill work encoding");
       }
     }
+  } else if (e->kind == KIND_DECODE && dev_len) {
+    // Lengths on the device: size the grid and the workspace for the bound
+    // (every entry at the bound, plus one chunk for a band that starts
+    // inside a chunk); the partitioner kernel writes the real plan into the
+    // workspace on every run.
+    const int64_t chunk = kDecodeChunk;
+    const int64_t per_b = (len_bound + chunk - 1) / chunk + (mode == 4 ? 1 : 0);
+    const int64_t total_max = B * per_b;
+    a.chunk = (int32_t)chunk;
+    a.n_head_blocks = (a.G + 15) / 16;
+    const int64_t n_items = total_max * KVn * a.n_head_blocks;
+    if (n_items > INT32_MAX) {
+      delete e;
+      return fail(FIA_ERR_UNSUPPORTED, "too many decode work items");
+    }
+    e->dev_len = true;
+    e->n_items = (int32_t)n_items;
+    a.n_work = (int32_t)total_max;
+    a.dev_kvlen = static_cast<const int32_t*>(p->actual_seq_lengths_kv_device->data);
+    a.kvlen_bound = (int32_t)len_bound;
+    e->meta_bytes = 0;   // nothing to upload
+    e->dev_meta_off = 0;
+    e->dev_work_off = align_up(((size_t)B * fia::BF_COUNT + 4) * sizeof(int32_t), kAlign);
+    e->part_o_off = align_up(e->dev_work_off + (size_t)total_max * 2 * sizeof(int32_t), kAlign);
+    e->part_lse_off = align_up(e->part_o_off + (size_t)total_max * Qn * D * sizeof(float), kAlign);
+    e->ws_size = align_up(e->part_lse_off + (size_t)total_max * Qn * sizeof(float), kAlign);
   } else if (e->kind == KIND_DECODE) {
     // Keys per chunk: one-byte codes move half the bytes per key, so their
     // chunks are twice as long (the same bytes per work item).
@@ -1231,6 +1304,12 @@ fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void
     case KIND_FP32: err = fia::launch_attn_fp32(e->a, s); break;
     case KIND_PREFILL: err = fia::launch_prefill_bf16(e->a, s); break;
     case KIND_DECODE:
+      if (e->dev_len) {
+        uint8_t* base = static_cast<uint8_t*>(workspace);
+        err = fia::launch_decode_partition(e->a, reinterpret_cast<int32_t*>(base + e->dev_meta_off),
+                                           reinterpret_cast<int32_t*>(base + e->dev_work_off), s);
+        if (err != hipSuccess) break;
+      }
       err = e->a.kvq ? fia::launch_decode_q8(e->a, e->n_items, s)
                      : fia::launch_decode_bf16(e->a, e->n_items, s);
       if (err == hipSuccess) err = fia::launch_decode_merge(e->a, s);
@@ -1251,6 +1330,7 @@ fia_status fia_debug_gather_kv(fia_executor* e, void* workspace, size_t workspac
   if (e->noop || e->kind == KIND_SPARSE || e->kind == KIND_FILL) {
     return fail(FIA_ERR_PARAM_INVALID, "executor has no key/value rows to gather");
   }
+  if (e->dev_len) return fail(FIA_ERR_PARAM_INVALID, "executor reads its KV lengths on the device");
   if (which != 0 && which != 1) return fail(FIA_ERR_PARAM_INVALID, "which must be 0 or 1");
   fia_status st = check_ws(e, workspace, workspace_size);
   if (st != FIA_SUCCESS) return st;

@@ -101,6 +101,14 @@ struct AttnArgs {
   int32_t n_head_blocks;            // ceil(G / 16)
   float* part_o;                    // [total_chunks * Qn * D]
   float* part_lse;                  // [total_chunks * Qn]
+  // Decode with KV lengths on the device: dev_kvlen int32 [B] is read by
+  // decode_partition, which writes the per-batch records, the chunk count
+  // (*n_chunks_dev) and the chunk list into the workspace (meta / work point
+  // there); lengths are clamped into [0, kvlen_bound].  The split kernels are
+  // launched for the bound's chunk count and return early past *n_chunks_dev.
+  const int32_t* dev_kvlen;         // nullptr: the plan was built on the host
+  int32_t kvlen_bound;
+  const int32_t* n_chunks_dev;
 };
 
 // Shared-KV sparse decode arguments.
@@ -144,6 +152,7 @@ struct SparseArgs {
 hipError_t launch_prefill_bf16(const AttnArgs& a, hipStream_t s);
 hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s);
 hipError_t launch_decode_merge(const AttnArgs& a, hipStream_t s);
+hipError_t launch_decode_partition(const AttnArgs& a, int32_t* meta, int32_t* work, hipStream_t s);
 hipError_t launch_decode_q8(const AttnArgs& a, int32_t n_items, hipStream_t s);
 hipError_t launch_attn_fp32(const AttnArgs& a, hipStream_t s);
 hipError_t launch_fill_empty(const AttnArgs& a, hipStream_t s);

@@ -80,6 +80,8 @@ class FiaParams(ctypes.Structure):
         ("value_antiquant_scale", ctypes.POINTER(FiaTensor)),
         ("key_antiquant_offset", ctypes.POINTER(FiaTensor)),
         ("value_antiquant_offset", ctypes.POINTER(FiaTensor)),
+        ("actual_seq_lengths_kv_device", ctypes.POINTER(FiaTensor)),
+        ("max_actual_seq_length_kv", ctypes.c_int64),
     ]
 
 
@@ -220,7 +222,8 @@ class AttentionPlan(_Plan):
                  actual_seq_lengths_kv=None, attention_out=None, softmax_lse=None,
                  kv_layout="PA_ND", learnable_sink=None, key_antiquant_mode=0,
                  value_antiquant_mode=0, key_antiquant_scale=None, value_antiquant_scale=None,
-                 key_antiquant_offset=None, value_antiquant_offset=None):
+                 key_antiquant_offset=None, value_antiquant_offset=None,
+                 actual_seq_lengths_kv_device=None, max_actual_seq_length_kv=0):
         L = lib()
         if attention_out is None:
             attention_out = torch.empty_like(query)
@@ -271,6 +274,14 @@ class AttentionPlan(_Plan):
         if self._lens_kv[0] is not None:
             p.actual_seq_lengths_kv = ctypes.cast(self._lens_kv[0], ctypes.POINTER(ctypes.c_int64))
             p.actual_seq_lengths_kv_len = self._lens_kv[1]
+        # KV lengths on the device (int32 [B]): read by the partitioner kernel
+        # at every run, so they may change between runs without a new plan.
+        self.lengths_kv_device = actual_seq_lengths_kv_device
+        self._dev_len_desc = (describe(actual_seq_lengths_kv_device)
+                              if actual_seq_lengths_kv_device is not None else None)
+        if self._dev_len_desc is not None:
+            p.actual_seq_lengths_kv_device = ctypes.pointer(self._dev_len_desc)
+        p.max_actual_seq_length_kv = int(max_actual_seq_length_kv)
         self._params = p
         self.batch = (len(actual_seq_lengths) if input_layout == "TND" else query.shape[0])
         descs = [describe(t) for t in (query, key, value, pse_shift, atten_mask, block_table,

@@ -75,6 +75,11 @@ def P(**kw):
     if sink is not None:
         keep.append(sink)
         p.learnable_sink = ctypes.pointer(sink)
+    dl = kw.pop("dev_lens", None)
+    if dl is not None:
+        keep.append(dl)
+        p.actual_seq_lengths_kv_device = ctypes.pointer(dl)
+    p.max_actual_seq_length_kv = kw.pop("len_bound", 0)
     p.key_antiquant_mode = kw.pop("kmode", 0)
     p.value_antiquant_mode = kw.pop("vmode", 0)
     for name in ("key_antiquant_scale", "value_antiquant_scale", "key_antiquant_offset",
@@ -603,3 +608,43 @@ def sparse_plan_status(**over):
 def test_sparse_phase1(over, expect):
     st, msg = sparse_plan_status(**over)
     assert st == expect, (over, msg)
+
+
+def test_device_kv_lengths_phase1():
+    """KV lengths on the device (decode only): int32 [B] tensor plus a host
+    bound that sizes the grid and the workspace."""
+    i32 = fia.DT_INT32
+    q, k, v, o = dense(S1=1, S2=3000)
+    st, kind, ws, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=3000), q, k, v, o)
+    assert st == 0 and kind == "decode" and ws > 0, msg
+    # the workspace grows with the bound (one chunk list and partials per bound chunk)
+    st2, _, ws2, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=600), q, k, v, o)
+    assert st2 == 0 and ws2 < ws, msg
+    cases = [
+        (dict(dev_lens=T((2,), i32), len_bound=3001), BAD),            # above KV_S
+        (dict(dev_lens=T((2,), i32), len_bound=-1), BAD),
+        (dict(dev_lens=T((3,), i32), len_bound=100), BAD),             # not [B]
+        (dict(dev_lens=T((2,), fia.DT_INT64), len_bound=100), BAD),
+        (dict(dev_lens=T((2,), i32), len_bound=100, actual_seq_lengths_kv=[5, 6]), BAD),
+    ]
+    for kw, expect in cases:
+        st, _, _, msg = plan(P(num_kv_heads=2, **kw), q, k, v, o)
+        assert st == expect, (kw, msg)
+    # query length > 1 is not a decode
+    q2, k2, v2, o2 = dense(S1=4, S2=3000)
+    st, _, _, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=100), q2, k2, v2, o2)
+    assert st == BAD, msg
+    # fp32 inputs are not taken
+    q3, k3, v3, o3 = dense(S1=1, S2=300, D=64, dt=fia.DT_FP32)
+    st, _, _, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=100), q3, k3, v3, o3)
+    assert st == UNS, msg
+    # paged: the bound must fit the block table
+    qp = T((2, 1, 4, 128))
+    pool = T((40, 128, 2, 128))
+    bt = T((2, 8), i32)
+    st, kind, _, msg = plan(P(num_kv_heads=2, block_size=128, dev_lens=T((2,), i32), len_bound=1024),
+                            qp, pool, pool, qp, bt=bt)
+    assert st == 0 and kind == "decode", msg
+    st, _, _, msg = plan(P(num_kv_heads=2, block_size=128, dev_lens=T((2,), i32), len_bound=1025),
+                         qp, pool, pool, qp, bt=bt)
+    assert st == BAD, msg

@@ -603,6 +603,72 @@ def test_sparse_tnd_rows_outside_every_entry_are_zero():
 
 
 # ---------------------------------------------------------------------------
+# Decode with KV lengths on the device (device-side partitioner).
+# ---------------------------------------------------------------------------
+def _dev_len_plan(case, lens_dev, bound, **kw):
+    q, k, v, bt, _ = TI.dense_tensors(case, DEV)
+    return fia.AttentionPlan(q, k, v, num_heads=case.num_heads,
+                             num_key_value_heads=case.num_kv_heads, scale_value=case.scale,
+                             sparse_mode=case.sparse_mode, pre_tokens=case.pre_tokens,
+                             next_tokens=case.next_tokens, block_table=bt,
+                             block_size=case.block_size if bt is not None else 0,
+                             softmax_lse_flag=case.lse, actual_seq_lengths_kv_device=lens_dev,
+                             max_actual_seq_length_kv=bound, **kw)
+
+
+DEV_LEN_CASES = [
+    # (mode, pre, next, sink)
+    (0, 2147483647, 2147483647, False),
+    (3, 2147483647, 2147483647, True),
+    (4, 700, 0, False),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DEV_LEN_CASES)))
+def test_decode_device_lengths_match_host_plan(i):
+    """The partitioner kernel builds the plan the host builds for the same
+    lengths: outputs and LSE equal the host-planned run bit for bit, and
+    match the oracle.  The lengths then change on the device and the same
+    executor runs again (no new plan), against a host plan of the new
+    lengths; lengths past the bound are clamped to it."""
+    mode, pre, nxt, sink = DEV_LEN_CASES[i]
+    lens = [1, 700, 5000, 4097, 129, 2048]
+    lens2 = [3000, 0, 1, 6000, 6001, 511]
+    bound = 6000
+    # the pool holds real rows for the longer of the two lengths of each entry
+    alloc = [max(a, min(b, bound)) for a, b in zip(lens, lens2)]
+    base = W.paged_decode_case(f"dl{i}", 480 + i, B=6, Q_N=32, KV_N=8, D=128, kv_lens=alloc,
+                               block_size=128, sparse_mode=mode, lse=True)
+    assert base.block_table.shape[1] * 128 >= bound
+    case = dataclasses.replace(base, actual_seq_lengths_kv=lens, pre_tokens=pre, next_tokens=nxt)
+    extra = {}
+    if sink:
+        case = W.with_random_sink(case, 481)
+        extra["learnable_sink"] = TI.to_device(case.learnable_sink, "bf16", DEV)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    plan = run_plan(_dev_len_plan(case, lens_dev, bound, **extra))
+    assert plan.kind == "decode"
+    host = run_plan(TI.dense_plan(case, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host.out.view(torch.int16))
+    assert torch.equal(plan.lse, host.lse)
+    out, lse = gpu_results(plan)
+    ref_o, ref_l = O.fia_case(case)
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+    # new lengths, same executor: shorter, longer, zero and one past the bound
+    lens_dev.copy_(torch.tensor(lens2, dtype=torch.int32))
+    run_plan(plan)
+    case2 = dataclasses.replace(case, actual_seq_lengths_kv=[min(x, bound) for x in lens2])
+    host2 = run_plan(TI.dense_plan(case2, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host2.out.view(torch.int16))
+    assert torch.equal(plan.lse, host2.lse)
+    out2, lse2 = gpu_results(plan)
+    ref_o2, ref_l2 = O.fia_case(case2)
+    check_out(out2, ref_o2)
+    check_lse(lse2, ref_l2)
+
+
+# ---------------------------------------------------------------------------
 # Bit-exact gathers and row selection.
 # ---------------------------------------------------------------------------
 def test_paged_gather_is_bit_exact():
