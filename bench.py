@@ -298,6 +298,21 @@ def main():
             "kernels": "decode_split_bf16<128> + decode_merge<128>",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
         del plan, case_b
+        # The same decode with the KV lengths on the device: the partitioner
+        # kernel builds the chunk list on every run, the grid is sized for
+        # the 8192 bound.
+        lens_dev = torch.tensor(case.actual_seq_lengths_kv, dtype=torch.int32, device=dev)
+        plan = TI.dense_plan(case, dev, actual_seq_lengths_kv=None,
+                             actual_seq_lengths_kv_device=lens_dev, max_actual_seq_length_kv=8192)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["paged_decode_device_lengths"] = {
+            "workload": "the paged GQA decode above with its KV lengths on the device (int32 [64]), "
+                        "plan bound 8192", "unit": "GB/s", "value": round(gbs, 2),
+            "algorithmic_bytes": nbytes, "ms": round(kern_ms, 5),
+            "kernels": "decode_partition + decode_split_bf16<128> + decode_merge<128>",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+        del plan, lens_dev
 
     if want("c4"):
         progress("c4")
