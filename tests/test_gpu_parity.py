@@ -668,6 +668,37 @@ def test_decode_device_lengths_match_host_plan(i):
     check_lse(lse2, ref_l2)
 
 
+def test_decode_device_lengths_graph_replay():
+    """The decode with device-resident lengths captured once into a HIP graph
+    (after one eager run) and replayed with new lengths written between the
+    replays, with eager work in between: every replay equals the host-planned
+    run of its lengths bit for bit."""
+    lens_sets = [[700, 5000, 1, 2048], [6000, 0, 129, 3000], [1, 1, 4097, 5999]]
+    bound = 6000
+    alloc = [max(x) for x in zip(*lens_sets)]
+    base = W.paged_decode_case("dlg", 490, B=4, Q_N=32, KV_N=8, D=128, kv_lens=alloc,
+                               block_size=128, sparse_mode=3, lse=True)
+    lens_dev = torch.tensor(lens_sets[0], dtype=torch.int32, device=DEV)
+    plan = run_plan(_dev_len_plan(base, lens_dev, bound))   # eager run first
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(stream):
+        with torch.cuda.graph(graph, stream=stream):
+            plan.run(stream)
+    torch.cuda.synchronize()
+    for rep in range(2):
+        for lens in lens_sets:
+            lens_dev.copy_(torch.tensor(lens, dtype=torch.int32))
+            scratch = torch.randn(1 << 20, device=DEV).sum()   # eager work between replays
+            graph.replay()
+            torch.cuda.synchronize()
+            host = run_plan(TI.dense_plan(dataclasses.replace(base, actual_seq_lengths_kv=lens), DEV))
+            assert torch.equal(plan.out.view(torch.int16), host.out.view(torch.int16)), (rep, lens)
+            assert torch.equal(plan.lse, host.lse), (rep, lens)
+            del scratch
+
+
 # ---------------------------------------------------------------------------
 # Bit-exact gathers and row selection.
 # ---------------------------------------------------------------------------
