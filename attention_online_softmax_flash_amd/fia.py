@@ -34,7 +34,8 @@ KIND_NAMES = {0: "fill", 1: "prefill", 2: "decode", 3: "sparse", 4: "fp32"}
 
 EXPORTED = ["fia_get_workspace_size", "fia_sparse_get_workspace_size", "fia_run",
             "fia_executor_destroy", "fia_last_error", "fia_executor_kind",
-            "fia_debug_gather_kv", "fia_debug_sparse_rows"]
+            "fia_debug_gather_kv", "fia_debug_sparse_rows", "fia_peak_mfma_bf16",
+            "fia_peak_hbm_read"]
 
 
 class FiaNotBuilt(RuntimeError):
@@ -134,6 +135,10 @@ def lib():
     L.fia_debug_gather_kv.argtypes = [vp, vp, sz, ctypes.c_int32, vp, vp]
     L.fia_debug_sparse_rows.restype = ctypes.c_int
     L.fia_debug_sparse_rows.argtypes = [vp, vp, sz, vp, vp, ctypes.POINTER(ctypes.c_int32), vp]
+    L.fia_peak_mfma_bf16.restype = ctypes.c_int
+    L.fia_peak_mfma_bf16.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
+    L.fia_peak_hbm_read.restype = ctypes.c_int
+    L.fia_peak_hbm_read.argtypes = [vp, sz, ctypes.c_int32, vp, vp]
     _LIB = L
     return L
 

@@ -190,6 +190,67 @@ def cpu_baseline(case, flops):
                       "heads), float64 numpy with materialised scores"}
 
 
+def measure_peaks(dev):
+    """Rates measured on this machine (the second roofline denominators):
+    a loop of independent bf16 MFMAs on register operands, and a streaming
+    read of a 2 GiB device buffer with 16-byte non-temporal loads; each the
+    best of 5 timed launches after one warm-up."""
+    import torch
+
+    from attention_online_softmax_flash_amd import fia
+
+    L = fia.lib()
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    n_wg, iters = 2048, 2000                  # 8 waves per CU, 2 per SIMD
+    out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
+    buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
+    out32 = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+
+    def best(launch):
+        launch()
+        ms = []
+        for _ in range(5):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            launch()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return min(ms)
+
+    def mfma():
+        fia._check(L.fia_peak_mfma_bf16(n_wg, iters, out.data_ptr(), h))
+
+    def read():
+        fia._check(L.fia_peak_hbm_read(buf.data_ptr(), buf.numel(), 2048, out32.data_ptr(), h))
+
+    t_mfma = best(mfma)
+    t_read = best(read)
+    flops = n_wg * 4 * iters * 8 * 32768
+    res = {"mfma_bf16_tflops": round(flops / (t_mfma / 1e3) / 1e12, 1),
+           "hbm_read_gbs": round(buf.numel() / (t_read / 1e3) / 1e9, 1),
+           "how": "fia_peak_mfma_bf16 (2048 workgroups x 4 waves, 2000 iterations of 8 independent "
+                  "32x32x16 bf16 MFMAs on registers) and fia_peak_hbm_read (2 GiB read once with "
+                  "16-byte non-temporal loads); best of 5 launches"}
+    del out, buf, out32
+    return res
+
+
+def add_measured_fracs(line, peaks):
+    """Beside each roofline's fraction of the published peak, its fraction of
+    the rate measured on this machine."""
+    def one(r):
+        if r is None:
+            return
+        m = peaks["mfma_bf16_tflops"] if r["unit"] == "TFLOP/s" else peaks["hbm_read_gbs"]
+        r["measured_peak"] = m
+        r["frac_measured"] = round(r["achieved"] / m, 4)
+    one(line.get("roofline"))
+    for c in line.get("components", {}).values():
+        one(c.get("roofline"))
+
+
 def progress(what):
     """One line on stderr per workload, so a long run shows it is alive."""
     print(f"[bench] {what} ...", file=sys.stderr, flush=True)
@@ -205,7 +266,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "next", "c3q", "copy"], default="all",
+    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "next", "c3q", "copy", "peaks"],
+                    default="all",
                     help="limit the run to one workload (profiling); 'copy' runs a plain 1 GiB "
                          "device copy, the calibration of the HBM traffic counters")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -237,6 +299,11 @@ def main():
     flush = lambda: flush_buf.zero_()
     components = {}
     line = None
+
+    peaks = None
+    if args.workload in ("all", "peaks"):
+        progress("peaks")
+        peaks = measure_peaks(dev)
 
     if want("c2"):
         progress("c2")
@@ -433,6 +500,9 @@ def main():
                 "value": None, "unit": None, "n_gpus": 1, "steps": args.steps,
                 "warmup": args.warmup, "note": f"partial run: --workload {args.workload}"}
     line["components"] = components
+    if peaks is not None:
+        line["measured_peaks"] = peaks
+        add_measured_fracs(line, peaks)
     print(json.dumps(line), flush=True)
 
 

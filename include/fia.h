@@ -317,6 +317,20 @@ int32_t fia_executor_kind(const fia_executor* executor);
 fia_status fia_debug_gather_kv(fia_executor* executor, void* workspace, size_t workspace_size,
                                int32_t which, void* dst, void* stream);
 
+/* Machine-peak probes, the measured roofline denominators beside the
+ * published peaks (each returns after enqueueing on `stream`):
+ *   fia_peak_mfma_bf16: n_workgroups x 4 waves, each running `iters`
+ *     iterations of 8 independent v_mfma_f32_32x32x16_bf16 on register
+ *     operands (n_workgroups * 4 * iters * 8 * 32768 flops, no memory
+ *     traffic); writes one float per thread to out[n_workgroups * 256].
+ *   fia_peak_hbm_read: streams `bytes` (a multiple of 16, 16-byte aligned
+ *     device memory) once with 16-byte non-temporal loads over n_workgroups
+ *     x 256 threads; writes one uint32 per thread to out[n_workgroups * 256].
+ * PARAM_INVALID for non-positive counts or misaligned sizes. */
+fia_status fia_peak_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out, void* stream);
+fia_status fia_peak_hbm_read(const void* buf, size_t bytes, int32_t n_workgroups, uint32_t* out,
+                             void* stream);
+
 /* Test support for the sparse executor: for every query row (BSND: batch
  * entry b, token t; TND: packed token r), the row list the kernel attends
  * to, as fixed slots [B, S1, n_slots] or [T1, n_slots]: ids_out[.., s] = j for window row j of ori_kv, (1 << 30) | c
