@@ -17,7 +17,7 @@ FAKE = 0x7F0000000000
 def header_functions():
     src = open(os.path.join(ROOT, "include", "fia.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(fia_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(fia_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_library_exports_every_declared_function():
