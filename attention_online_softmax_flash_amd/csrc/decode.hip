@@ -302,6 +302,9 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
   const int nchunk = bm[BF_NCHUNK];
   if (nchunk == 1) return;
+  // A TND batch entry without a query token owns no output row (its offset
+  // is the next entry's first row): nothing to write.
+  if (a.tnd && bm[BF_QLEN] == 0) return;
   const int q_off = bm[BF_QOFF];
   uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
                  (int64_t)h * a.o_sh + lane * PL;

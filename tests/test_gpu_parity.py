@@ -406,6 +406,16 @@ def test_decode_tnd():
     dense_parity(case, "decode")
 
 
+def test_decode_tnd_entry_without_query_writes_nothing():
+    """A TND entry with no query token owns no output row; the row at its
+    offset belongs to the next entry, here written directly by the split
+    kernel (one chunk) before the merge runs, so a stray empty-row write by
+    the merge would always show."""
+    case = W.tnd_case("dtnd0", 241, q_lens=[1, 0, 1, 0], kv_lens=[600, 100, 300, 7], Q_N=8,
+                      KV_N=2, D=128, lse=True)
+    dense_parity(case, "decode")
+
+
 FP32_CASES = [
     (2, 70, 70, 4, 2, 64, 3, None, None, [70, 33], [70, 33], True),
     (1, 40, 90, 2, 1, 128, 4, 10, 2, None, None, False),
