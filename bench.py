@@ -291,7 +291,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["all", "c2", "c3", "c4", "c5", "next", "c3q", "copy", "peaks"],
+    ap.add_argument("--workload", choices=["all", "c1", "c2", "c3", "c4", "c5", "next", "c3q", "copy", "peaks"],
                     default="all",
                     help="limit the run to one workload (profiling); 'copy' runs a plain 1 GiB "
                          "device copy, the calibration of the HBM traffic counters")
@@ -406,6 +406,19 @@ def main():
             "kernels": "decode_partition + decode_split_bf16<128> + decode_merge<128>",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
         del plan, lens_dev
+
+    if want("c1"):
+        progress("c1")
+        # Correctness-sized fp32 workload: kernel time only (launch-bound; its
+        # accuracy against the oracle is checked by the tests).
+        case = W.c1_tiny_dense()
+        plan = TI.dense_plan(case, dev)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup)
+        components["tiny_dense_fp32"] = {
+            "workload": "tiny dense attention: B=1, N=2, S1=S2=64, D=64, fp32, no mask, LSE",
+            "unit": "us", "value": round(kern_ms * 1000.0, 2), "kernels": "attn_fp32",
+            "algorithmic_flop": dense_flops(case)}
+        del plan
 
     if want("c4"):
         progress("c4")
