@@ -678,6 +678,39 @@ def test_decode_device_lengths_match_host_plan(i):
     check_lse(lse2, ref_l2)
 
 
+DEV_LEN_DENSE_CASES = [
+    # (Q_N, KV_N, D, lse): dense BSND KV, group sizes 1 / 16 / 64, head dims 64 / 128
+    (8, 8, 128, False),
+    (32, 2, 64, True),
+    (64, 1, 128, True),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DEV_LEN_DENSE_CASES)))
+def test_decode_device_lengths_dense_kv(i):
+    """Device-resident lengths with a dense (non-paged) KV cache: equal to the
+    host-planned run bit for bit and to the oracle; the bound is KV_S."""
+    Qn, KVn, D, lse = DEV_LEN_DENSE_CASES[i]
+    lens = [0, 1, 513, 1500, 2048]
+    case = W.dense_case(f"dld{i}", 495 + i, B=5, S1=1, S2=2048, Q_N=Qn, KV_N=KVn, D=D,
+                        kv_lens=lens, lse=lse)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    q, k, v, _, _ = TI.dense_tensors(case, DEV)
+    plan = run_plan(fia.AttentionPlan(q, k, v, num_heads=Qn, num_key_value_heads=KVn,
+                                      scale_value=case.scale, softmax_lse_flag=lse,
+                                      actual_seq_lengths_kv_device=lens_dev,
+                                      max_actual_seq_length_kv=2048))
+    host = run_plan(TI.dense_plan(case, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host.out.view(torch.int16))
+    if lse:
+        assert torch.equal(plan.lse, host.lse)
+    out, lse_v = gpu_results(plan)
+    ref_o, ref_l = O.fia_case(case)
+    check_out(out, ref_o)
+    if lse:
+        check_lse(lse_v, ref_l)
+
+
 def test_decode_device_lengths_graph_replay():
     """The decode with device-resident lengths captured once into a HIP graph
     (after one eager run) and replayed with new lengths written between the
