@@ -29,7 +29,7 @@ fia_status fail(fia_status st, const std::string& msg) {
 
 enum Kind { KIND_FILL = 0, KIND_PREFILL = 1, KIND_DECODE = 2, KIND_SPARSE = 3, KIND_FP32 = 4 };
 
-constexpr int kDecodeChunk = 512;     // keys per split-KV chunk (multiple of 128)
+constexpr int kDecodeChunk = 1024;    // keys per split-KV chunk (multiple of 128)
 constexpr int64_t kMaxLen = 20971520; // S <= 20M (V2 restrictions when Q_S > 1)
 constexpr size_t kAlign = 256;
 
@@ -1011,9 +1011,9 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     e->part_lse_off = align_up(e->part_o_off + (size_t)total_max * Qn * D * sizeof(float), kAlign);
     e->ws_size = align_up(e->part_lse_off + (size_t)total_max * Qn * sizeof(float), kAlign);
   } else if (e->kind == KIND_DECODE) {
-    // Keys per chunk: one-byte codes move half the bytes per key, so their
-    // chunks are twice as long (the same bytes per work item).
-    const int64_t chunk = kvq ? 2 * kDecodeChunk : kDecodeChunk;
+    // Keys per chunk (the same for one-byte codes, which measured best at
+    // this length too).
+    const int64_t chunk = kDecodeChunk;
     int64_t total_chunks = 0;
     for (int64_t b = 0; b < B; ++b) {
       int32_t* r = &e->meta[(size_t)b * fia::BF_COUNT];

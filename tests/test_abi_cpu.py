@@ -132,12 +132,13 @@ def test_paged_decode_plan_and_workspace_grows_with_lengths():
     q = T((3, 1, 8, 128))
     o = T((3, 1, 8, 128))
     pool = T((20, 128, 2, 128))
-    bt = T((3, 8), fia.DT_INT32)
+    bt = T((3, 16), fia.DT_INT32)
     st, kind, ws1, msg = plan(P(num_heads=8, num_kv_heads=2, block_size=128,
                                 actual_seq_lengths_kv=[100, 200, 300]), q, pool, pool, o, bt=bt)
     assert st == 0 and kind == "decode", msg
+    # past one split-KV chunk per row: partials for every chunk
     st, kind, ws2, msg = plan(P(num_heads=8, num_kv_heads=2, block_size=128,
-                                actual_seq_lengths_kv=[1000, 1000, 1000]), q, pool, pool, o, bt=bt)
+                                actual_seq_lengths_kv=[2000, 2000, 2000]), q, pool, pool, o, bt=bt)
     assert st == 0 and ws2 > ws1, msg
 
 

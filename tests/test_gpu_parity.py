@@ -354,6 +354,7 @@ BNNBSD_DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size)
     (3, 32, 8, 128, [1, 511, 1300], 128),
     (2, 8, 8, 128, [512, 513], 16),
+    (2, 8, 8, 128, [1024, 1025], 16),     # one chunk / two chunks at the 1024-key boundary
     (2, 4, 2, 64, [999, 40], 32),
     (2, 16, 1, 128, [2048 + 7, 100], 64),
 ]
@@ -372,6 +373,7 @@ DECODE_CASES = [
     # (B, Qn, KVn, D, kv_lens, block_size or None (dense), mode, pre, nxt)
     (3, 32, 8, 128, [1, 511, 1300], 128, 0, None, None),
     (2, 8, 8, 128, [512, 513], 16, 3, None, None),
+    (2, 8, 8, 128, [1024, 1025], 16, 3, None, None),
     (2, 16, 1, 128, [2048 + 7, 100], 64, 0, None, None),
     (2, 32, 1, 128, [700, 3], 512, 0, None, None),
     (1, 64, 1, 128, [1500], 128, 0, None, None),
