@@ -31,21 +31,24 @@ __global__ __launch_bounds__(256, 2) void peak_mfma_bf16(int32_t iters, float* o
   out[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
-// Grid-stride read of `bytes` (a multiple of 16) with non-temporal 16-byte
-// loads; each thread stores the XOR of what it read.
+// Streaming read of `bytes` (a multiple of 16): workgroups take contiguous
+// 32 KiB blocks in turn, each thread 8 non-temporal 16-byte loads in flight
+// (a wave reads 1 KiB runs), then the tail past the last whole block; each
+// thread stores the XOR of what it read.
 __global__ __launch_bounds__(256) void peak_hbm_read(const u32x4* buf, int64_t n16, uint32_t* out) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int BLK = 8 * 256;   // 16-byte units per block
+  const int64_t n_blk = n16 / BLK;
   uint32_t acc = 0;
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const u32x4 v0 = __builtin_nontemporal_load(buf + i);
-    const u32x4 v1 = __builtin_nontemporal_load(buf + i + stride);
-    const u32x4 v2 = __builtin_nontemporal_load(buf + i + 2 * stride);
-    const u32x4 v3 = __builtin_nontemporal_load(buf + i + 3 * stride);
-    acc ^= v0[0] ^ v0[1] ^ v0[2] ^ v0[3] ^ v1[0] ^ v1[1] ^ v1[2] ^ v1[3];
-    acc ^= v2[0] ^ v2[1] ^ v2[2] ^ v2[3] ^ v3[0] ^ v3[1] ^ v3[2] ^ v3[3];
+  for (int64_t blk = blockIdx.x; blk < n_blk; blk += gridDim.x) {
+    const u32x4* p = buf + blk * BLK + threadIdx.x;
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(p + u * 256);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
-  for (; i < n16; i += stride) {
+  for (int64_t i = n_blk * BLK + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x) {
     const u32x4 v = __builtin_nontemporal_load(buf + i);
     acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
   }

@@ -230,7 +230,7 @@ def measure_peaks(dev):
     n_wg, iters = 2048, 2000                  # 8 waves per CU, 2 per SIMD
     out = torch.empty(n_wg * 256, dtype=torch.float32, device=dev)
     buf = torch.ones(2 << 30, dtype=torch.uint8, device=dev)
-    out32 = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    out32 = torch.empty(4096 * 256, dtype=torch.int32, device=dev)
 
     def best(launch):
         launch()
@@ -248,7 +248,7 @@ def measure_peaks(dev):
         fia._check(L.fia_peak_mfma_bf16(n_wg, iters, out.data_ptr(), h))
 
     def read():
-        fia._check(L.fia_peak_hbm_read(buf.data_ptr(), buf.numel(), 2048, out32.data_ptr(), h))
+        fia._check(L.fia_peak_hbm_read(buf.data_ptr(), buf.numel(), 4096, out32.data_ptr(), h))
 
     t_mfma = best(mfma)
     t_read = best(read)
@@ -257,7 +257,7 @@ def measure_peaks(dev):
            "hbm_read_gbs": round(buf.numel() / (t_read / 1e3) / 1e9, 1),
            "how": "fia_peak_mfma_bf16 (2048 workgroups x 4 waves, 2000 iterations of 8 independent "
                   "32x32x16 bf16 MFMAs on registers) and fia_peak_hbm_read (2 GiB read once with "
-                  "16-byte non-temporal loads); best of 5 launches"}
+                  "16-byte non-temporal loads, 4096 workgroups taking contiguous 32 KiB blocks, 8 loads in flight per thread); best of 5 launches"}
     del out, buf, out32
     return res
 

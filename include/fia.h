@@ -324,8 +324,9 @@ fia_status fia_debug_gather_kv(fia_executor* executor, void* workspace, size_t w
  *     operands (n_workgroups * 4 * iters * 8 * 32768 flops, no memory
  *     traffic); writes one float per thread to out[n_workgroups * 256].
  *   fia_peak_hbm_read: streams `bytes` (a multiple of 16, 16-byte aligned
- *     device memory) once with 16-byte non-temporal loads over n_workgroups
- *     x 256 threads; writes one uint32 per thread to out[n_workgroups * 256].
+ *     device memory) once with 16-byte non-temporal loads, n_workgroups x 256
+ *     threads taking contiguous 32 KiB blocks in turn; writes one uint32 per
+ *     thread to out[n_workgroups * 256].
  * PARAM_INVALID for non-positive counts or misaligned sizes. */
 fia_status fia_peak_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out, void* stream);
 fia_status fia_peak_hbm_read(const void* buf, size_t bytes, int32_t n_workgroups, uint32_t* out,
