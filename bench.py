@@ -84,10 +84,21 @@ def decode_bytes(case):
 
 
 def sparse_bytes(case):
-    """640 selected rows per batch at 604 used bytes each, q, out, indices."""
-    B, S1, N1, D = case.q.shape
+    """Selected rows at 604 used bytes each, q, out, indices (BSND or TND)."""
+    N1, D = case.q.shape[-2], case.q.shape[-1]
+    B = len(case.seqused_kv)
+    if case.cu_seqlens_q is None:
+        S1 = case.q.shape[1]
+        counts = [S1] * B
+        key = lambda b, t: (b, t)
+    else:
+        cu = case.cu_seqlens_q
+        counts = [cu[b + 1] - cu[b] for b in range(B)]
+        key = lambda b, t: cu[b] + t
+    n_q = sum(counts)
     rows = 0
     for b, Lk in enumerate(case.seqused_kv):
+        S1 = counts[b]
         for t in range(S1):
             p = Lk - S1 + t
             win = max(0, min(Lk - 1, p + case.win_right) - max(0, p - case.win_left) + 1)
@@ -95,10 +106,10 @@ def sparse_bytes(case):
             if case.cmp_sparse_indices is None:     # heavily compressed: every visible row
                 rows += win + n_cmp
             else:
-                idx = case.cmp_sparse_indices[b, t, 0]
+                idx = case.cmp_sparse_indices[key(b, t)][0]
                 rows += win + int(((idx >= 0) & (idx < n_cmp)).sum())
     idx_bytes = 0 if case.cmp_sparse_indices is None else case.cmp_sparse_indices.nbytes
-    return rows * 604 + 2 * B * S1 * N1 * D * 2 + idx_bytes
+    return rows * 604 + 2 * n_q * N1 * D * 2 + idx_bytes + (4 * (B + 1) if case.cu_seqlens_q else 0)
 
 
 def time_plan(plan, steps, warmup, flush=None):
@@ -501,6 +512,22 @@ def main():
         components["sparse_two_query_tokens"] = {
             "workload": "shared-KV sparse attention, 2 query tokens per batch entry: B=16, Q_N=64, "
                         "D=512, window 128 + top-512 of ratio-4 compressed KV per token, sinks",
+            "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
+            "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
+            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
+        del plan
+        # TND: ragged query-token counts (1..4 per batch entry, seeded) packed
+        # into T1 rows, the row-to-entry map read from cu_seqlens_q on the device.
+        counts = [int(x) for x in W.rng_for(SEEDS_HCA + 2).integers(1, 5, size=16)]
+        case = W.sparse_tnd_case("tnd", SEEDS_HCA + 3, q_counts=counts, B=16, N1=64,
+                                 seqused_kv=[16384] * 16, K2=512, materialise_all_ori=False)
+        nbytes = sparse_bytes(case)
+        plan = TI.sparse_plan(case, dev)
+        _, kern_ms = time_plan(plan, min(args.steps, 20), args.warmup, flush=flush)
+        gbs = nbytes / (kern_ms / 1000.0) / 1e9
+        components["sparse_tnd_ragged"] = {
+            "workload": f"shared-KV sparse attention, TND with query counts {counts} (T1 = {sum(counts)}): "
+                        "Q_N=64, D=512, window 128 + top-512 of ratio-4 compressed KV per token, sinks",
             "unit": "GB/s", "value": round(gbs, 2), "algorithmic_bytes": nbytes,
             "ms": round(kern_ms, 5), "kernels": "sparse_chunk + sparse_merge",
             "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", None)}
