@@ -76,7 +76,7 @@ __device__ __forceinline__ int val_swz(int r) {
 // outstanding buffer-to-LDS load only guards reads of that stage.
 //
 // EXT: an explicit mask tensor (modes 0 / 1) and / or a bias tensor (pse
-// type 0); every tile takes the per-element path.  Both enter through the
+// type 0).  Both enter through the
 // initial value of the score accumulators: -inf for a masked key, bias /
 // scale otherwise (the scaled score is then q.k * scale + bias).  Their
 // loads for tile t + 1 go out at the end of step t, so they are in
@@ -514,7 +514,10 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       }
       if (!cur_skip) {
         const int j0 = kt * BN;
-        const bool need_mask = EXT || !(j0 >= wlo_max && j0 + BN <= whi_min);
+        // Tiles inside every row's visible range skip the per-element test;
+        // with a mask / bias tensor too: masked keys already hold -inf in the
+        // score accumulators, which the plain path maps to probability 0.
+        const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min);
         if (need_mask) {
           if (do_next) {
             tile_body(std::true_type{}, kt, vst, sc, std::true_type{}, knx, sn);
