@@ -774,7 +774,9 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
 
   // Kernel-specific requirements.
   if (f32) {
-    if (D % 32 != 0 || D > 256) return fail(FIA_ERR_UNSUPPORTED, "fp32 path needs D % 32 == 0 and D <= 256");
+    if (D != 32 && D != 64 && D != 128 && D != 256) {
+      return fail(FIA_ERR_UNSUPPORTED, "fp32 path needs D in {32, 64, 128, 256}");
+    }
   } else if (D != 64 && D != 128) {
     return fail(FIA_ERR_UNSUPPORTED, "bf16 kernels support head dim 64 and 128");
   }

@@ -516,8 +516,12 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         const int j0 = kt * BN;
         // Tiles inside every row's visible range skip the per-element test;
         // with a mask / bias tensor too: masked keys already hold -inf in the
-        // score accumulators, which the plain path maps to probability 0.
-        const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min);
+        // score accumulators, which the plain path maps to probability 0 as
+        // long as the scale is positive.  With scale 0 the plain path would
+        // form -inf * 0 = NaN, so such calls keep the per-element test, which
+        // replaces a masked key's score by -inf after scaling.
+        const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min) ||
+                               (EXT && !(a.scale_log2 > 0.f));
         if (need_mask) {
           if (do_next) {
             tile_body(std::true_type{}, kt, vst, sc, std::true_type{}, knx, sn);

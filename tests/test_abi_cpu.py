@@ -484,6 +484,16 @@ def test_shape_limits_and_unsupported():
     q, k, v, o = dense(N=257, KVN=257)
     st, _, _, msg = plan(P(num_heads=257, num_kv_heads=257), q, k, v, o)
     assert st == BAD
+    # The fp32 path is built for D in {32, 64, 128, 256}; any other D is
+    # refused in phase 1, so a successful phase 1 always has a kernel to run.
+    for D in (32, 64, 128, 256):
+        q, k, v, o = dense(D=D, dt=fia.DT_FP32)
+        st, kind, _, msg = plan(P(num_kv_heads=2), q, k, v, o)
+        assert st == 0 and kind == "fp32", (D, msg)
+    for D in (96, 160, 192, 224):
+        q, k, v, o = dense(D=D, dt=fia.DT_FP32)
+        st, _, _, msg = plan(P(num_kv_heads=2), q, k, v, o)
+        assert st == UNS and "fp32" in msg, (D, msg)
     q, k, v, o = dense()
     st, _, _, msg = plan(P(num_kv_heads=2, layout="NSD"), q, k, v, o)
     assert st == BAD
