@@ -60,6 +60,21 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32))
 
 
+def f32_to_f16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to IEEE binary16 (numpy's round to nearest even);
+    return bits."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def normal_f16(rng: np.random.Generator, shape) -> np.ndarray:
+    return f32_to_f16_bits(rng.standard_normal(shape, dtype=np.float32))
+
+
+# 0xFFFF is a NaN both as bfloat16 and as binary16: poison for rows that must
+# never be read.
+HALF_NAN_BITS = np.uint16(0xFFFF)
+
+
 @dataclasses.dataclass
 class DenseCase:
     """Inputs of one dense / paged attention call (query layout BSND or TND).
@@ -554,3 +569,167 @@ def c5_sparse_sharedkv(seed=SEEDS["c5"], materialise_all_ori=False) -> SparseCas
     return sparse_case("c5_sparse_sharedkv_decode", seed, B=16, N1=64,
                        seqused_kv=[16384] * 16, K2=512,
                        materialise_all_ori=materialise_all_ori)
+
+
+# ---------------------------------------------------------------------------
+# sparse_flash_mla: the same shared-KV sparse attention over unquantised fp16 /
+# bf16 rows of 512 values (sparse_flash_mla common and spec constraints).
+# ---------------------------------------------------------------------------
+SFMLA_MODES = {"SWA": 1, "CSA": 4, "HCA": 128}
+
+
+@dataclasses.dataclass
+class SfmlaCase:
+    """Inputs of one sparse_flash_mla call.
+
+    q: [B, S1, N1, 512] (BSND) or [T1, N1, 512] (TND, ``cu_seqlens_q`` set),
+    bits of ``dtype``.  ori_kv / cmp_kv (same dtype), by ``kv_layout``:
+    "PA_BBND" pools [n_blocks, block_size, 1, 512] addressed through
+    ori_block_table / cmp_block_table; "BSND" [B, S2, 1, 512]; "TND" packed
+    [T2, 1, 512] with entry b's rows starting at cu_seqlens_*_kv[b].
+    cmp_kv is None in the SWA mode; cmp_sparse_indices (int32 [B, S1, 1, K2]
+    or [T1, 1, K2], -1 = unused) only in the CSA mode.  sinks: None or
+    float32 [N1]."""
+    name: str
+    dtype: str                       # "bf16" | "fp16"
+    q: np.ndarray
+    kv_layout: str                   # "PA_BBND" | "BSND" | "TND"
+    ori_kv: np.ndarray
+    cmp_kv: Optional[np.ndarray]
+    ori_block_table: Optional[np.ndarray]
+    cmp_block_table: Optional[np.ndarray]
+    cu_seqlens_ori_kv: Optional[list]
+    cu_seqlens_cmp_kv: Optional[list]
+    cmp_sparse_indices: Optional[np.ndarray]
+    seqused_kv: list
+    sinks: Optional[np.ndarray]
+    softmax_scale: float
+    cmp_ratio: int = 4
+    win_left: int = 127
+    win_right: int = 0
+    cu_seqlens_q: Optional[list] = None
+    return_lse: bool = True
+    seed: int = 0
+
+    @property
+    def mode(self) -> str:
+        if self.cmp_kv is None:
+            return "SWA"
+        return "CSA" if self.cmp_sparse_indices is not None else "HCA"
+
+
+def _paged_half_pool(rng, rows_per_batch, block_size, extra_blocks=0):
+    """Place per-batch rows [L_b, 512] (uint16 bits) into a [n_blocks, bs, 1,
+    512] pool with randomly permuted physical blocks; slots past a batch's
+    rows hold NaN.  Unused table entries are -1.  Returns (pool, table)."""
+    pages = [-(-r.shape[0] // block_size) for r in rows_per_batch]
+    n_blocks = max(1, sum(pages) + extra_blocks)
+    perm = rng.permutation(n_blocks).astype(np.int32)
+    table = np.full((len(rows_per_batch), max(1, max(pages))), -1, dtype=np.int32)
+    pool = np.full((n_blocks, block_size, 1, SPARSE_D), HALF_NAN_BITS, dtype=np.uint16)
+    cursor = 0
+    for b, rows in enumerate(rows_per_batch):
+        for p in range(pages[b]):
+            blk = int(perm[cursor])
+            cursor += 1
+            table[b, p] = blk
+            lo, hi = p * block_size, min(rows.shape[0], (p + 1) * block_size)
+            pool[blk, : hi - lo, 0] = rows[lo:hi]
+    return pool, table
+
+
+def _place_half_rows(rng, rows_per_batch, kv_layout, block_size, extra_blocks=0):
+    """(kv, block_table, cu) of per-batch rows in the given KV layout."""
+    if kv_layout == "PA_BBND":
+        pool, table = _paged_half_pool(rng, rows_per_batch, block_size, extra_blocks)
+        return pool, table, None
+    if kv_layout == "BSND":
+        S2 = max(1, max(r.shape[0] for r in rows_per_batch))
+        kv = np.full((len(rows_per_batch), S2, 1, SPARSE_D), HALF_NAN_BITS, dtype=np.uint16)
+        for b, r in enumerate(rows_per_batch):
+            kv[b, : r.shape[0], 0] = r
+        return kv, None, None
+    if kv_layout == "TND":
+        cu = [0]
+        for r in rows_per_batch:
+            cu.append(cu[-1] + r.shape[0])
+        kv = np.concatenate(rows_per_batch, axis=0)[:, None, :] if cu[-1] else \
+            np.zeros((0, 1, SPARSE_D), dtype=np.uint16)
+        return np.ascontiguousarray(kv), None, cu
+    raise ValueError(kv_layout)
+
+
+def sfmla_case(name, seed, *, B, N1, seqused_kv, mode="CSA", K2=512, dtype="bf16",
+               kv_layout="PA_BBND", block_size1=128, block_size2=128, S1=1, n_valid=None,
+               sinks=True, lse=True, window_only_ori=False, extra_blocks=0) -> SfmlaCase:
+    """sparse_flash_mla inputs with S1 query tokens per batch entry (the last
+    S1 positions of its KV sequence).  Values N(0,1) rounded to ``dtype``.
+
+    SWA: window rows of ori_kv only.  CSA (ratio 4): plus the top-K2 rows of
+    cmp_kv, indices drawn uniformly without replacement from the
+    floor(L / 4) compressed rows and padded with -1 (valid entries first).
+    HCA (ratio 128): plus every compressed row.  ``window_only_ori``: only
+    the rows a query window can reach are drawn, every other ori row is NaN
+    (a read of one would poison the output)."""
+    ratio = SFMLA_MODES[mode]
+    rng = rng_for(seed)
+    draw = normal_bf16 if dtype == "bf16" else normal_f16
+    q = draw(rng, (B, S1, N1, SPARSE_D))
+    ori_rows, cmp_rows = [], []
+    for L in seqused_kv:
+        L = int(L)
+        if window_only_ori:
+            rows = np.full((L, SPARSE_D), HALF_NAN_BITS, dtype=np.uint16)
+            lo = max(0, L - 128 - (S1 - 1))
+            rows[lo:] = draw(rng, (L - lo, SPARSE_D))
+        else:
+            rows = draw(rng, (L, SPARSE_D))
+        ori_rows.append(rows)
+        if mode != "SWA":
+            cmp_rows.append(draw(rng, (L // ratio, SPARSE_D)))
+    ori_kv, ori_bt, ori_cu = _place_half_rows(rng, ori_rows, kv_layout, block_size1, extra_blocks)
+    cmp_kv = cmp_bt = cmp_cu = None
+    if mode != "SWA":
+        cmp_kv, cmp_bt, cmp_cu = _place_half_rows(rng, cmp_rows, kv_layout, block_size2, extra_blocks)
+    idx = None
+    if mode == "CSA":
+        idx = np.full((B, S1, 1, K2), -1, dtype=np.int32)
+        for b, L in enumerate(seqused_kv):
+            n_cmp = int(L) // ratio
+            nv = min(K2, n_cmp) if n_valid is None else min(n_valid, K2, n_cmp)
+            for t in range(S1):
+                if nv > 0:
+                    idx[b, t, 0, :nv] = rng.choice(n_cmp, size=nv, replace=False).astype(np.int32)
+    sk = rng.standard_normal(N1, dtype=np.float32) if sinks else None
+    return SfmlaCase(name=name, dtype=dtype, q=q, kv_layout=kv_layout, ori_kv=ori_kv,
+                     cmp_kv=cmp_kv, ori_block_table=ori_bt, cmp_block_table=cmp_bt,
+                     cu_seqlens_ori_kv=ori_cu, cu_seqlens_cmp_kv=cmp_cu,
+                     cmp_sparse_indices=idx, seqused_kv=[int(x) for x in seqused_kv],
+                     sinks=sk, softmax_scale=1.0 / math.sqrt(SPARSE_D), cmp_ratio=ratio,
+                     return_lse=lse, seed=seed)
+
+
+def sfmla_tnd_case(name, seed, *, q_counts, **kw) -> SfmlaCase:
+    """The TND-query form of :func:`sfmla_case` (as :func:`sparse_tnd_case`):
+    entry b keeps its last q_counts[b] tokens, packed in entry order."""
+    s1max = max(1, max(q_counts))
+    base = sfmla_case(name, seed, S1=s1max, **kw)
+    keep = [slice(s1max - c, s1max) for c in q_counts]
+    q = np.concatenate([base.q[b, keep[b]] for b in range(len(q_counts))], axis=0)
+    idx = None
+    if base.cmp_sparse_indices is not None:
+        idx = np.ascontiguousarray(np.concatenate(
+            [base.cmp_sparse_indices[b, keep[b]] for b in range(len(q_counts))], axis=0))
+    cu = [0]
+    for c in q_counts:
+        cu.append(cu[-1] + int(c))
+    return dataclasses.replace(base, q=np.ascontiguousarray(q), cmp_sparse_indices=idx,
+                               cu_seqlens_q=cu)
+
+
+def sfmla_decode_bf16(seed=SEEDS["c5"] + 100) -> SfmlaCase:
+    """The shared-KV sparse decode shape with unquantised bf16 rows: B=16,
+    N1=64, D=512, KV length 16384, window 127/0, ratio 4, top-512 indices,
+    PA_BBND pools of block 128, fp32 sinks, LSE."""
+    return sfmla_case("sfmla_csa_decode_bf16", seed, B=16, N1=64, seqused_kv=[16384] * 16,
+                      K2=512, window_only_ori=True)

@@ -51,6 +51,10 @@ What it computes, and where each step is stated on the pages:
   holds for a query row whose visible key set is empty (invalid-row
   correction, V2 innerPrecise restrictions) and for padded query rows
   i >= Lq; "inf" is taken as +inf.
+* sparse_flash_mla (function description, common / spec constraints): the
+  same row sets over unquantised fp16 / bf16 rows of 512 values, in PA_BBND
+  pools (addressed like PA_ND), BSND or packed TND KV, with an optional
+  softmax_lse output (shared-KV LSE shape, N2 = 1).
 * Shared-KV sparse decode (KvQuantSparseAttnSharedkv formula and
   constraints; sparse_flash_mla CSA mode): K~ = V~ = [window rows of ori_kv ;
   top-k selected rows of cmp_kv], each packed row = bf16 rope(64) |
@@ -98,9 +102,29 @@ def decode_e4m3fn(codes: np.ndarray) -> np.ndarray:
     return np.where((e == 15) & (m == 7), np.nan, val)
 
 
+def decode_fp16(bits: np.ndarray) -> np.ndarray:
+    """IEEE 754 binary16 bit patterns (uint16) -> float64, in closed form.
+
+    sign = b15, exponent = b14..b10 (bias 15), mantissa = b9..b0.
+    exponent 0 -> subnormal (m/1024) * 2^-14; exponent 31 -> +-inf for
+    m = 0, NaN otherwise; else (1 + m/1024) * 2^(e-15)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    s = (b >> 15) & 1
+    e = (b >> 10) & 31
+    m = b & 1023
+    sign = np.where(s == 1, -1.0, 1.0)
+    normal = (1.0 + m / 1024.0) * np.exp2(e.astype(np.float64) - 15.0)
+    sub = (m / 1024.0) * 2.0 ** -14
+    val = sign * np.where(e == 0, sub, normal)
+    val = np.where(e == 31, np.where(m == 0, sign * np.inf, np.nan), val)
+    return val
+
+
 def to_f64(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return decode_bf16(x)
+    if dtype == "fp16":
+        return decode_fp16(x)
     if dtype == "fp32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "fp64":
@@ -450,3 +474,84 @@ def sparse_sharedkv(case, *, batches=None):
                                     extra_logit=float(sinks[h]))
                 out[key][h] = o[0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# sparse_flash_mla: shared-KV sparse attention over unquantised rows.
+# ---------------------------------------------------------------------------
+def sparse_flash_mla(case):
+    """sparse_flash_mla (SWA / CSA / HCA modes) over fp16 / bf16 rows of 512,
+    float64.  Returns (out, lse).
+
+    Page: sparse_flash_mla, function description (O = softmax(Q K~^T *
+    softmax_scale) V~ with K~ = V~ the window part of ori_kv and the
+    compressed part of cmp_kv), common constraints (q, ori_kv and cmp_kv share
+    one dtype, fp16 or bf16; layouts BSND / TND for q and BSND / TND /
+    PA_BBND for the KV) and spec constraints (D 512, KV_N 1, window 127 / 0).
+    The row set of every query token is :func:`sparse_rows` (the same rules as
+    the shared-KV operator): SWA uses no compressed rows, CSA the valid
+    visible entries of the index row, HCA every visible compressed row.
+
+    Rows: "PA_BBND" pools are addressed through the block tables like the
+    PA_ND pools (row r of batch b at pool[table[b][r // bs], r % bs]);
+    "BSND" row r of batch b is kv[b, r]; "TND" row r of batch b is
+    kv[cu[b] + r] with cu = cu_seqlens_ori_kv / cu_seqlens_cmp_kv.
+
+    LSE (softmax_lse output, fp32 log-sum-exp, natural log) in the shared-KV
+    shape with N2 = 1: [B, 1, S1, N1] (BSND) or [1, T1, N1] (TND).  Readings:
+    with ``case.sinks`` (optional here) the sink is one extra logit with a
+    zero value vector, as for the shared-KV operator, and the LSE includes
+    it; a query token with no row and no sink gives 0 and +inf; a packed TND
+    row outside every entry is 0 / +inf.
+    """
+    dec = decode_bf16 if case.dtype == "bf16" else decode_fp16
+    q = case.q
+    N1, Dq = q.shape[-2], q.shape[-1]
+    B = len(case.seqused_kv)
+    sinks = None if case.sinks is None else np.asarray(case.sinks, np.float32).astype(np.float64)
+
+    def row(which, b, r):
+        kv = case.ori_kv if which == 0 else case.cmp_kv
+        if case.kv_layout == "PA_BBND":
+            table = case.ori_block_table if which == 0 else case.cmp_block_table
+            bs = kv.shape[1]
+            return kv[int(table[b, r // bs]), r % bs, 0]
+        if case.kv_layout == "BSND":
+            return kv[b, r, 0]
+        if case.kv_layout == "TND":
+            cu = case.cu_seqlens_ori_kv if which == 0 else case.cu_seqlens_cmp_kv
+            return kv[int(cu[b]) + r, 0]
+        raise ValueError(case.kv_layout)
+
+    if case.cu_seqlens_q is None:
+        S1 = q.shape[1]
+        out = np.full((B, S1, N1, Dq), np.nan)
+        lse = np.full((B, 1, S1, N1), np.nan)
+        rows_of = lambda b: [(t, S1, (b, t)) for t in range(S1)]
+        idx_of = lambda key: case.cmp_sparse_indices[key[0], key[1], 0]
+        lse_at = lambda key: (key[0], 0, key[1])
+    else:
+        cu = [int(x) for x in case.cu_seqlens_q]
+        out = np.zeros((q.shape[0], N1, Dq))
+        lse = np.full((1, q.shape[0], N1), POS_INF)
+        rows_of = lambda b: [(t, cu[b + 1] - cu[b], cu[b] + t) for t in range(cu[b + 1] - cu[b])]
+        idx_of = lambda key: case.cmp_sparse_indices[key, 0]
+        lse_at = lambda key: (0, key)
+    for b in range(B):
+        Lk = int(case.seqused_kv[b])
+        for t, S1b, key in rows_of(b):
+            idx_row = None if case.cmp_sparse_indices is None else idx_of(key)
+            win, comp = sparse_rows(Lk, S1b, t, idx_row, cmp_ratio=case.cmp_ratio,
+                                    win_left=case.win_left, win_right=case.win_right)
+            if case.cmp_kv is None:
+                comp = []
+            X = [dec(row(0, b, j)) for j in win] + [dec(row(1, b, c)) for c in comp]
+            X = np.stack(X) if X else np.zeros((0, Dq))
+            qb = dec(q[key])                                    # [N1, 512]
+            s = case.softmax_scale * (qb @ X.T)                 # [N1, R]
+            for h in range(N1):
+                o, l = softmax_rows(s[h:h + 1], np.ones((1, X.shape[0]), bool), X,
+                                    extra_logit=None if sinks is None else float(sinks[h]))
+                out[key][h] = o[0]
+                lse[lse_at(key)][h] = l[0]
+    return out, lse

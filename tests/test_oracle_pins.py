@@ -844,6 +844,196 @@ def test_sparse_poisoned_rows_are_never_read():
 
 
 # ---------------------------------------------------------------------------
+# sparse_flash_mla (unquantised fp16 / bf16 rows)
+# ---------------------------------------------------------------------------
+def test_fp16_decode_anchors_and_torch_table():
+    """IEEE binary16 anchors from the definition, then all 65536 codes
+    against torch's float16."""
+    anchors = {0x3C00: 1.0, 0x7BFF: 65504.0, 0x0400: 2.0 ** -14, 0x0001: 2.0 ** -24,
+               0x03FF: 1023 * 2.0 ** -24, 0xC000: -2.0, 0x3555: 1365 / 4096, 0x7C00: np.inf,
+               0xFC00: -np.inf}
+    for code, val in anchors.items():
+        assert O.decode_fp16(np.array([code], np.uint16))[0] == val, hex(code)
+    assert np.isnan(O.decode_fp16(np.array([0x7E00, 0xFFFF, 0x7C01], np.uint16))).all()
+    z = O.decode_fp16(np.array([0x8000], np.uint16))[0]
+    assert z == 0.0 and np.signbit(z)
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.float16).double().numpy()
+    got = O.decode_fp16(bits)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    assert np.array_equal(np.signbit(ref[ok]), np.signbit(got[ok]))
+
+
+def _small_sfmla(seed=70, **kw):
+    base = dict(B=2, N1=4, seqused_kv=[300, 77], K2=16, block_size1=32, block_size2=16)
+    base.update(kw)
+    return W.sfmla_case("f", seed, **base)
+
+
+def _sfmla_rows(c, b, t=0, S1=1):
+    """The logical rows of query token t of entry b, gathered by hand from
+    the pools: window (band [p - 127, p]) then the valid selected rows."""
+    L = c.seqused_kv[b]
+    p = L - S1 + t
+    dec = O.decode_bf16 if c.dtype == "bf16" else O.decode_fp16
+    bs1 = c.ori_kv.shape[1]
+    rows = [c.ori_kv[c.ori_block_table[b, j // bs1], j % bs1, 0] for j in range(max(0, p - 127), p + 1)]
+    if c.cmp_kv is not None:
+        bs2 = c.cmp_kv.shape[1]
+        n_cmp = L // c.cmp_ratio - (S1 - 1 - t)
+        sel = (c.cmp_sparse_indices[b, t, 0] if c.cmp_sparse_indices is not None
+               else range(max(0, n_cmp)))
+        rows += [c.cmp_kv[c.cmp_block_table[b, x // bs2], x % bs2, 0] for x in sel
+                 if 0 <= x < n_cmp]
+    return np.stack([dec(r) for r in rows])
+
+
+@pytest.mark.parametrize("mode,dtype", [("CSA", "bf16"), ("CSA", "fp16"), ("HCA", "bf16"),
+                                        ("SWA", "fp16")])
+def test_sfmla_matches_sdpa_and_logsumexp(mode, dtype):
+    """No sink: the output is SDPA over the hand-gathered rows and the LSE is
+    torch's logsumexp of the scaled scores."""
+    c = _small_sfmla(71, mode=mode, dtype=dtype, sinks=False,
+                     seqused_kv=[300, 77] if mode != "HCA" else [1500, 400])
+    out, lse = O.sparse_flash_mla(c)
+    dec = O.decode_bf16 if dtype == "bf16" else O.decode_fp16
+    for b in range(2):
+        X = _sfmla_rows(c, b)
+        q = dec(c.q[b, 0])
+        ref = sdpa(q[None], X[:, None], X[:, None], c.softmax_scale, gqa=True)
+        np.testing.assert_allclose(out[b, 0], ref[0], rtol=1e-11, atol=1e-13)
+        want = torch.logsumexp(_t(c.softmax_scale * (q @ X.T)), dim=1).numpy()
+        np.testing.assert_allclose(lse[b, 0, 0], want, rtol=1e-13, atol=1e-13)
+
+
+def test_sfmla_sink_matches_sdpa_with_zero_key():
+    c = _small_sfmla(72)
+    out, lse = O.sparse_flash_mla(c)
+    for b in range(2):
+        X = _sfmla_rows(c, b)
+        Xs = np.concatenate([X, np.zeros((1, 512))])
+        q = O.decode_bf16(c.q[b, 0])
+        mask = np.zeros((4, 1, X.shape[0] + 1))
+        mask[:, 0, -1] = c.sinks.astype(np.float64)
+        ref = sdpa(q[None], Xs[:, None], Xs[:, None], c.softmax_scale, mask=mask, gqa=True)
+        np.testing.assert_allclose(out[b, 0], ref[0], rtol=1e-11, atol=1e-13)
+        s = np.concatenate([c.softmax_scale * (q @ X.T), c.sinks.astype(np.float64)[:, None]], 1)
+        np.testing.assert_allclose(lse[b, 0, 0], torch.logsumexp(_t(s), dim=1).numpy(),
+                                   rtol=1e-13, atol=1e-13)
+
+
+def test_sfmla_zero_query_closed_form():
+    """Q = 0: every score is 0, so out = sum x / (n + e^sigma) and
+    LSE = ln(n + e^sigma); without a sink the mean and ln n."""
+    for sinks in (True, False):
+        c = _small_sfmla(73, sinks=sinks)
+        c.q[...] = 0
+        out, lse = O.sparse_flash_mla(c)
+        for b in range(2):
+            X = _sfmla_rows(c, b)
+            n = X.shape[0]
+            for h in range(4):
+                z = math.exp(float(c.sinks[h])) if sinks else 0.0
+                np.testing.assert_allclose(out[b, 0, h], X.sum(0) / (n + z), rtol=1e-12, atol=1e-14)
+                assert abs(lse[b, 0, 0, h] - math.log(n + z)) < 1e-12
+
+
+def test_sfmla_equals_sharedkv_on_representable_rows():
+    """A packed fp8 row decodes to values bf16 holds exactly (3-bit mantissa
+    times a power of two; bf16 rope), so the same rows written as bf16 give
+    the shared-KV operator's result."""
+    sk = _small_sparse(seed=74)
+    rows_o = np.stack([O.decode_packed_row(r) for r in sk.ori_kv.reshape(-1, 640)])
+    rows_c = np.stack([O.decode_packed_row(r) for r in sk.cmp_kv.reshape(-1, 640)])
+    bits_o = W.f32_to_bf16_bits(rows_o.astype(np.float32))
+    bits_c = W.f32_to_bf16_bits(rows_c.astype(np.float32))
+    fin = np.isfinite(rows_o)
+    assert np.array_equal(O.decode_bf16(bits_o)[fin], rows_o[fin])
+    assert np.array_equal(O.decode_bf16(bits_c), rows_c)
+    c = W.SfmlaCase(name="x", dtype="bf16", q=sk.q, kv_layout="PA_BBND",
+                    ori_kv=bits_o.reshape(sk.ori_kv.shape[:3] + (512,)),
+                    cmp_kv=bits_c.reshape(sk.cmp_kv.shape[:3] + (512,)),
+                    ori_block_table=sk.ori_block_table, cmp_block_table=sk.cmp_block_table,
+                    cu_seqlens_ori_kv=None, cu_seqlens_cmp_kv=None,
+                    cmp_sparse_indices=sk.cmp_sparse_indices, seqused_kv=sk.seqused_kv,
+                    sinks=sk.sinks, softmax_scale=sk.softmax_scale, cmp_ratio=4)
+    out, _ = O.sparse_flash_mla(c)
+    np.testing.assert_allclose(out, O.sparse_sharedkv(sk), rtol=1e-13, atol=1e-15)
+
+
+def test_sfmla_kv_layouts_agree():
+    """The same logical rows stored as PA_BBND pools, as BSND [B, S2, 1, 512]
+    or packed TND [T2, 1, 512] with cumulative offsets give the same result."""
+    c = _small_sfmla(75)
+    out, lse = O.sparse_flash_mla(c)
+
+    def logical(pool, row, L):
+        bs = pool.shape[1]
+        return np.stack([pool[row[j // bs], j % bs, 0] for j in range(L)]) if L else \
+            np.zeros((0, 512), np.uint16)
+
+    ori = [logical(c.ori_kv, c.ori_block_table[b], L) for b, L in enumerate(c.seqused_kv)]
+    cmp = [logical(c.cmp_kv, c.cmp_block_table[b], L // 4) for b, L in enumerate(c.seqused_kv)]
+    S2 = max(len(r) for r in ori)
+    S2c = max(len(r) for r in cmp)
+    bsnd_o = np.full((2, S2, 1, 512), W.HALF_NAN_BITS, np.uint16)
+    bsnd_c = np.full((2, S2c, 1, 512), W.HALF_NAN_BITS, np.uint16)
+    for b in range(2):
+        bsnd_o[b, :len(ori[b]), 0] = ori[b]
+        bsnd_c[b, :len(cmp[b]), 0] = cmp[b]
+    bs = dataclasses.replace(c, kv_layout="BSND", ori_kv=bsnd_o, cmp_kv=bsnd_c,
+                             ori_block_table=None, cmp_block_table=None)
+    o2, l2 = O.sparse_flash_mla(bs)
+    np.testing.assert_array_equal(o2, out)
+    np.testing.assert_array_equal(l2, lse)
+    cu_o = [0, len(ori[0]), len(ori[0]) + len(ori[1])]
+    cu_c = [0, len(cmp[0]), len(cmp[0]) + len(cmp[1])]
+    tnd = dataclasses.replace(bs, kv_layout="TND",
+                              ori_kv=np.concatenate(ori)[:, None], cmp_kv=np.concatenate(cmp)[:, None],
+                              cu_seqlens_ori_kv=cu_o, cu_seqlens_cmp_kv=cu_c)
+    o3, l3 = O.sparse_flash_mla(tnd)
+    np.testing.assert_array_equal(o3, out)
+    np.testing.assert_array_equal(l3, lse)
+
+
+def test_sfmla_tnd_query_and_empty_rows():
+    """TND queries equal the BSND suffix tokens (as for the shared-KV
+    operator); a packed row outside every entry is 0 / +inf; a batch entry
+    with no KV row gives 0 and +inf without a sink, 0 and sigma with one."""
+    counts = [2, 0, 3]
+    kw = dict(B=3, N1=4, seqused_kv=[300, 50, 700], K2=16, block_size1=32, block_size2=16)
+    tnd = W.sfmla_tnd_case("t", 76, q_counts=counts, **kw)
+    base = W.sfmla_case("t", 76, S1=3, **kw)
+    ot, lt = O.sparse_flash_mla(tnd)
+    ob, lb = O.sparse_flash_mla(base)
+    assert ot.shape == (5, 4, 512) and lt.shape == (1, 5, 4)
+    r = 0
+    for b, n in enumerate(counts):
+        for t in range(n):
+            np.testing.assert_array_equal(ot[r], ob[b, 3 - n + t])
+            np.testing.assert_array_equal(lt[0, r], lb[b, 0, 3 - n + t])
+            r += 1
+    tnd.cu_seqlens_q = [0, 2, 2, 4]
+    ot, lt = O.sparse_flash_mla(tnd)
+    assert np.all(ot[4] == 0) and np.all(np.isposinf(lt[0, 4]))
+    for sinks in (False, True):
+        c = _small_sfmla(77, sinks=sinks, seqused_kv=[0, 77])
+        out, lse = O.sparse_flash_mla(c)
+        assert np.all(out[0] == 0)
+        want = c.sinks.astype(np.float64) if sinks else np.full(4, np.inf)
+        np.testing.assert_array_equal(lse[0, 0, 0], want)
+        assert np.all(np.isfinite(out[1])) and np.all(np.isfinite(lse[1]))
+
+
+def test_sfmla_poisoned_rows_are_never_read():
+    c = _small_sfmla(78, seqused_kv=[1000, 129], window_only_ori=True)
+    out, lse = O.sparse_flash_mla(c)
+    assert np.all(np.isfinite(out)) and np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------------------
 # Generators: determinism and shapes
 # ---------------------------------------------------------------------------
 def test_generators_are_deterministic():
