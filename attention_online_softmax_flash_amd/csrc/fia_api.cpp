@@ -1059,6 +1059,162 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   return FIA_SUCCESS;
 }
 
+namespace {
+
+// Sub-chunks of 64 slots per sparse workgroup.  Fixed (not derived from the
+// batch), so that a row's chunk boundaries, and with them its result, depend
+// only on its own slot count.
+constexpr int kSparseSubPerChunk = 2;
+
+// Query, output and index checks shared by both sparse operators.  Fills the
+// query / output / index / length fields of `a`.
+struct SparseShape {
+  bool tnd = false;
+  int64_t B = 0, S1 = 0, n_rows = 0, N1 = 0;
+};
+
+fia_status sparse_query(const fia_tensor* q, const fia_tensor* attention_out,
+                        const fia_tensor* cu_seqlens_q, const fia_tensor* seqused_kv, bool tnd,
+                        int want_dtype, SparseShape* sh, SparseArgs* a) {
+  fia_status st;
+  // TND packs the query tokens of all batch entries into T1 rows; the batch
+  // count then comes from seqused_kv and the row split from cu_seqlens_q.
+  if (q->ndim != (tnd ? 3 : 4)) {
+    return fail(FIA_ERR_PARAM_INVALID, tnd ? "q must be [T1, N1, 512] for TND" : "q must be [B, S1, N1, 512]");
+  }
+  if (seqused_kv->dtype != FIA_DT_INT32 || seqused_kv->ndim != 1) {
+    return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
+  }
+  sh->tnd = tnd;
+  sh->B = tnd ? seqused_kv->shape[0] : q->shape[0];
+  sh->S1 = tnd ? 1 : q->shape[1];
+  sh->n_rows = tnd ? q->shape[0] : sh->B * sh->S1;
+  sh->N1 = q->shape[tnd ? 1 : 2];
+  if (q->shape[q->ndim - 1] != fia::kSparseD) return fail(FIA_ERR_PARAM_INVALID, "q head dim must be 512");
+  if (sh->B < 1) return fail(FIA_ERR_PARAM_INVALID, "batch must be >= 1");
+  if (!tnd && sh->S1 < 1) return fail(FIA_ERR_PARAM_INVALID, "query length must be >= 1");
+  if (sh->n_rows > 65535) return fail(FIA_ERR_UNSUPPORTED, "B * S1 (or T1) must be <= 65535");
+  if (seqused_kv->shape[0] != sh->B) return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
+  bool out_ok = attention_out->dtype == want_dtype && attention_out->ndim == q->ndim;
+  for (int d = 0; out_ok && d < q->ndim; ++d) out_ok = attention_out->shape[d] == q->shape[d];
+  if (!out_ok) {
+    return fail(FIA_ERR_PARAM_INVALID, std::string("attention_out must be ") + dtype_name(want_dtype) +
+                                           " with the shape of q");
+  }
+  if (tnd) {
+    if (cu_seqlens_q == nullptr) return fail(FIA_ERR_PARAM_INVALID, "TND requires cu_seqlens_q");
+    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q")) != FIA_SUCCESS) return st;
+    if (cu_seqlens_q->dtype != FIA_DT_INT32 || cu_seqlens_q->ndim != 1 ||
+        cu_seqlens_q->shape[0] != sh->B + 1 || cu_seqlens_q->stride[0] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_q must be contiguous int32 [B + 1]");
+    }
+  } else if (cu_seqlens_q != nullptr) {
+    return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_q is only for layout_q TND");
+  }
+  for (int d = 0; d + 1 < q->ndim; ++d) {
+    if (q->stride[d] % 8 || attention_out->stride[d] % 8) {
+      return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
+    }
+  }
+  if (q->stride[q->ndim - 1] != 1 || attention_out->stride[q->ndim - 1] != 1 ||
+      reinterpret_cast<uintptr_t>(q->data) % 16 || reinterpret_cast<uintptr_t>(attention_out->data) % 16) {
+    return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
+  }
+  a->q = static_cast<const uint16_t*>(q->data);
+  a->q_sb = tnd ? 0 : q->stride[0];
+  a->q_ss = q->stride[tnd ? 0 : 1];
+  a->q_sh = q->stride[tnd ? 1 : 2];
+  a->o = static_cast<uint16_t*>(attention_out->data);
+  a->o_sb = tnd ? 0 : attention_out->stride[0];
+  a->o_ss = attention_out->stride[tnd ? 0 : 1];
+  a->o_sh = attention_out->stride[tnd ? 1 : 2];
+  a->cu_q = tnd ? static_cast<const int32_t*>(cu_seqlens_q->data) : nullptr;
+  a->n_rows = (int32_t)sh->n_rows;
+  a->seqused = static_cast<const int32_t*>(seqused_kv->data);
+  a->B = (int32_t)sh->B;
+  a->S1 = (int32_t)sh->S1;
+  a->N1 = (int32_t)sh->N1;
+  return FIA_SUCCESS;
+}
+
+// cmp_sparse_indices: int32 [B, S1, 1, K2] (BSND) or [T1, 1, K2] (TND), rows
+// contiguous.  Returns K2 through *K2.
+fia_status sparse_indices(const fia_tensor* t, const SparseShape& sh, int64_t* K2, SparseArgs* a) {
+  fia_status st = check_tensor(t, "cmp_sparse_indices");
+  if (st != FIA_SUCCESS) return st;
+  const bool shape_ok = sh.tnd ? (t->ndim == 3 && t->shape[0] == sh.n_rows && t->shape[1] == 1)
+                               : (t->ndim == 4 && t->shape[0] == sh.B && t->shape[1] == sh.S1 &&
+                                  t->shape[2] == 1);
+  if (t->dtype != FIA_DT_INT32 || !shape_ok) {
+    return fail(FIA_ERR_PARAM_INVALID, sh.tnd ? "cmp_sparse_indices must be int32 [T1, 1, K2]"
+                                              : "cmp_sparse_indices must be int32 [B, S1, 1, K2]");
+  }
+  if (t->stride[t->ndim - 1] != 1) {
+    return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices rows must be contiguous");
+  }
+  *K2 = t->shape[t->ndim - 1];
+  a->idx = static_cast<const int32_t*>(t->data);
+  a->idx_sb = sh.tnd ? 0 : t->stride[0];
+  a->idx_ss = sh.tnd ? t->stride[0] : t->stride[1];
+  return FIA_SUCCESS;
+}
+
+// Block table of a paged pool: int32 [B, cols], cols >= `need`.
+fia_status sparse_block_table(const fia_tensor* t, const char* name, int64_t B, int64_t need,
+                              fia::SparsePool* pd) {
+  fia_status st = check_tensor(t, name);
+  if (st != FIA_SUCCESS) return st;
+  if (t->dtype != FIA_DT_INT32 || t->ndim != 2 || t->shape[0] != B || t->shape[1] == 0) {
+    return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be int32 [B, cols]");
+  }
+  if (t->shape[1] < need) {
+    return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " has fewer columns than the longest "
+                                                          "sequence needs");
+  }
+  if (t->shape[1] > INT32_MAX) return fail(FIA_ERR_UNSUPPORTED, std::string(name) + " too wide");
+  pd->bt = static_cast<const int32_t*>(t->data);
+  pd->bt_sb = t->stride[0];
+  pd->bt_cols = (int32_t)t->shape[1];
+  return FIA_SUCCESS;
+}
+
+// Slots, work split and workspace of a planned sparse executor (the
+// per-row slot count is n_win_slots + K2).
+fia_status sparse_finish(fia_executor* e, int64_t K2, size_t* workspace_size, fia_executor** executor) {
+  SparseArgs& a = e->sp;
+  a.K2 = (int32_t)K2;
+  a.n_win_slots = (int32_t)align_up((size_t)(a.win_left + a.win_right + 1), fia::kSparseSub);
+  a.n_slots = a.n_win_slots + a.K2;
+  a.sub_per_chunk = kSparseSubPerChunk;
+  const int64_t per_chunk = (int64_t)fia::kSparseSub * a.sub_per_chunk;
+  const int64_t n_chunks = (a.n_slots + per_chunk - 1) / per_chunk;
+  if (n_chunks > fia::kSparseMaxChunks) {
+    delete e;
+    return fail(FIA_ERR_UNSUPPORTED, "too many key rows per query token (window + K2 must be <= " +
+                                         std::to_string(fia::kSparseMaxChunks * per_chunk) + ")");
+  }
+  a.n_chunks = (int32_t)n_chunks;
+  a.n_hb = (a.N1 + fia::kSparseHeads - 1) / fia::kSparseHeads;
+  a.xcd_rows = (a.n_rows % 8 == 0) ? 1 : 0;
+  if ((int64_t)a.n_rows * a.n_hb * a.n_chunks > INT32_MAX) {
+    delete e;
+    return fail(FIA_ERR_UNSUPPORTED, "too many sparse work items");
+  }
+  const size_t rows = (size_t)a.n_rows;
+  e->part_o_off = 0;
+  e->part_lse_off = 0;
+  e->ws_size = 0;
+  if (n_chunks > 1) {
+    e->part_lse_off = align_up(rows * n_chunks * a.N1 * fia::kSparseD * sizeof(float), kAlign);
+    e->ws_size = align_up(e->part_lse_off + rows * n_chunks * a.N1 * sizeof(float), kAlign);
+  }
+  *workspace_size = e->ws_size;
+  *executor = e;
+  return FIA_SUCCESS;
+}
+
+}  // namespace
+
 fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_tensor* q,
                                          const fia_tensor* ori_kv, const fia_tensor* cmp_kv,
                                          const fia_tensor* ori_sparse_indices,
@@ -1099,38 +1255,14 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
   if (p->return_softmax_lse) return fail(FIA_ERR_PARAM_INVALID, "return_softmax_lse is reserved");
   if (ori_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "ori_sparse_indices is reserved");
   if (q->dtype != FIA_DT_BF16) return fail(FIA_ERR_PARAM_INVALID, "q must be bf16");
-  // TND packs the query tokens of all batch entries into T1 rows; the batch
-  // count then comes from seqused_kv and the row split from cu_seqlens_q.
-  if (q->ndim != (tnd ? 3 : 4)) {
-    return fail(FIA_ERR_PARAM_INVALID, tnd ? "q must be [T1, N1, 512] for TND" : "q must be [B, S1, N1, 512]");
+  SparseArgs a{};
+  SparseShape sh;
+  if ((st = sparse_query(q, attention_out, cu_seqlens_q, seqused_kv, tnd, FIA_DT_BF16, &sh, &a)) !=
+      FIA_SUCCESS) {
+    return st;
   }
-  if (seqused_kv->dtype != FIA_DT_INT32 || seqused_kv->ndim != 1) {
-    return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
-  }
-  const int64_t B = tnd ? seqused_kv->shape[0] : q->shape[0];
-  const int64_t S1 = tnd ? 1 : q->shape[1];
-  const int64_t n_rows = tnd ? q->shape[0] : B * S1;
-  const int64_t N1 = q->shape[tnd ? 1 : 2];
-  if (q->shape[q->ndim - 1] != fia::kSparseD) return fail(FIA_ERR_PARAM_INVALID, "q head dim must be 512");
-  if (N1 != 64 && N1 != 128) return fail(FIA_ERR_PARAM_INVALID, "q heads must be 64 or 128");
-  if (B < 1) return fail(FIA_ERR_PARAM_INVALID, "batch must be >= 1");
-  if (!tnd && S1 < 1) return fail(FIA_ERR_PARAM_INVALID, "query length must be >= 1");
-  if (n_rows > 65535) return fail(FIA_ERR_UNSUPPORTED, "B * S1 (or T1) must be <= 65535");
-  bool out_ok = attention_out->dtype == FIA_DT_BF16 && attention_out->ndim == q->ndim;
-  for (int d = 0; out_ok && d < q->ndim; ++d) out_ok = attention_out->shape[d] == q->shape[d];
-  if (!out_ok) return fail(FIA_ERR_PARAM_INVALID, "attention_out must be bf16 with the shape of q");
-  if (tnd) {
-    if (cu_seqlens_q == nullptr) return fail(FIA_ERR_PARAM_INVALID, "TND requires cu_seqlens_q");
-    if ((st = check_tensor(cu_seqlens_q, "cu_seqlens_q")) != FIA_SUCCESS) return st;
-    if (cu_seqlens_q->dtype != FIA_DT_INT32 || cu_seqlens_q->ndim != 1 ||
-        cu_seqlens_q->shape[0] != B + 1 || cu_seqlens_q->stride[0] != 1) {
-      return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_q must be contiguous int32 [B + 1]");
-    }
-  } else if (cu_seqlens_q != nullptr) {
-    return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_q is only for layout_q TND");
-  }
-  auto check_pool = [&](const fia_tensor* t, const char* name, int64_t* nb, int64_t* bs,
-                        int64_t* sb, int64_t* ss) -> fia_status {
+  if (sh.N1 != 64 && sh.N1 != 128) return fail(FIA_ERR_PARAM_INVALID, "q heads must be 64 or 128");
+  auto check_pool = [&](const fia_tensor* t, const char* name, fia::SparsePool* pd) -> fia_status {
     if (t->dtype != FIA_DT_UINT8 && t->dtype != FIA_DT_FP8_E4M3FN && t->dtype != FIA_DT_INT8) {
       return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be a byte tensor (fp8 packed rows)");
     }
@@ -1139,24 +1271,28 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
     if (!four && !three) {
       return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be [n_blocks, block_size, 1, 640]");
     }
-    *nb = t->shape[0];
-    *bs = t->shape[1];
-    *sb = t->stride[0];
-    *ss = t->stride[1];
-    if (*bs % 16 != 0 || *bs > 1024 || *bs <= 0) {
+    if (t->shape[1] % 16 != 0 || t->shape[1] > 1024 || t->shape[1] <= 0) {
       return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": block_size must be a multiple of 16, <= 1024");
     }
-    if (*sb % 16 != 0 || *ss % 16 != 0 || reinterpret_cast<uintptr_t>(t->data) % 16 != 0) {
+    if (t->stride[0] % 16 != 0 || t->stride[1] % 16 != 0 || reinterpret_cast<uintptr_t>(t->data) % 16 != 0) {
       return fail(FIA_ERR_UNSUPPORTED, std::string(name) + ": rows must be 16-byte aligned");
     }
+    if (t->shape[0] < 1 || t->shape[0] > INT32_MAX) {
+      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + ": bad block count");
+    }
+    pd->base = static_cast<const uint8_t*>(t->data);
+    pd->paged = 1;
+    pd->nb = (int32_t)t->shape[0];
+    pd->bs = (int32_t)t->shape[1];
+    pd->sb = t->stride[0];
+    pd->ss = t->stride[1];
     return FIA_SUCCESS;
   };
-  int64_t nb1, bs1, osb, oss, nb2 = 0, bs2 = 16, csb = 0, css = 0;
-  if ((st = check_pool(ori_kv, "ori_kv", &nb1, &bs1, &osb, &oss)) != FIA_SUCCESS) return st;
+  if ((st = check_pool(ori_kv, "ori_kv", &a.ori)) != FIA_SUCCESS) return st;
   const bool has_cmp = cmp_kv != nullptr;
   if (has_cmp) {
     if ((st = check_tensor(cmp_kv, "cmp_kv")) != FIA_SUCCESS) return st;
-    if ((st = check_pool(cmp_kv, "cmp_kv", &nb2, &bs2, &csb, &css)) != FIA_SUCCESS) return st;
+    if ((st = check_pool(cmp_kv, "cmp_kv", &a.cmp)) != FIA_SUCCESS) return st;
     if (cmp_kv->dtype != ori_kv->dtype) return fail(FIA_ERR_PARAM_INVALID, "ori_kv and cmp_kv dtypes differ");
     // CSA: top-k indices into a ratio-4 compressed sequence; HCA: no indices,
     // every row of a ratio-128 compressed sequence.
@@ -1173,123 +1309,225 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* p, const fia_t
     if (cmp_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices needs cmp_kv");
     if (p->cmp_ratio != 1) return fail(FIA_ERR_PARAM_INVALID, "cmp_ratio must be 1 without compressed KV");
   }
-  int64_t K2 = 0, idx_sb = 0, idx_ss = 0;
+  int64_t K2 = 0;
   if (cmp_sparse_indices != nullptr) {
-    if ((st = check_tensor(cmp_sparse_indices, "cmp_sparse_indices")) != FIA_SUCCESS) return st;
-    const fia_tensor* t = cmp_sparse_indices;
-    const bool shape_ok = tnd ? (t->ndim == 3 && t->shape[0] == n_rows && t->shape[1] == 1)
-                              : (t->ndim == 4 && t->shape[0] == B && t->shape[1] == S1 && t->shape[2] == 1);
-    if (t->dtype != FIA_DT_INT32 || !shape_ok) {
-      return fail(FIA_ERR_PARAM_INVALID, tnd ? "cmp_sparse_indices must be int32 [T1, 1, K2]"
-                                             : "cmp_sparse_indices must be int32 [B, S1, 1, K2]");
-    }
-    K2 = t->shape[t->ndim - 1];
+    if ((st = sparse_indices(cmp_sparse_indices, sh, &K2, &a)) != FIA_SUCCESS) return st;
     if (K2 != 512 && K2 != 1024) return fail(FIA_ERR_PARAM_INVALID, "K2 must be 512 or 1024");
-    idx_sb = tnd ? 0 : t->stride[0];
-    idx_ss = tnd ? t->stride[0] : t->stride[1];
-    if (t->stride[t->ndim - 1] != 1) {
-      return fail(FIA_ERR_PARAM_INVALID, "cmp_sparse_indices rows must be contiguous");
-    }
   }
-  auto check_bt = [&](const fia_tensor* t, const char* name, int64_t need) -> fia_status {
-    fia_status s2 = check_tensor(t, name);
-    if (s2 != FIA_SUCCESS) return s2;
-    if (t->dtype != FIA_DT_INT32 || t->ndim != 2 || t->shape[0] != B || t->shape[1] == 0) {
-      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " must be int32 [B, cols]");
-    }
-    if (t->shape[1] < need) {
-      return fail(FIA_ERR_PARAM_INVALID, std::string(name) + " has fewer columns than the longest "
-                                                            "sequence needs");
-    }
-    return FIA_SUCCESS;
-  };
   if (max_seqused_kv < 0) return fail(FIA_ERR_PARAM_INVALID, "max_seqused_kv must be >= 0");
-  if ((st = check_bt(ori_block_table, "ori_block_table", (max_seqused_kv + bs1 - 1) / bs1)) != FIA_SUCCESS) {
+  if ((st = sparse_block_table(ori_block_table, "ori_block_table", sh.B,
+                               (max_seqused_kv + a.ori.bs - 1) / a.ori.bs, &a.ori)) != FIA_SUCCESS) {
     return st;
   }
   const bool hca = has_cmp && cmp_sparse_indices == nullptr;
   if (has_cmp) {
     const int64_t ncmp = max_seqused_kv / p->cmp_ratio;
-    if ((st = check_bt(cmp_block_table, "cmp_block_table", (ncmp + bs2 - 1) / bs2)) != FIA_SUCCESS) {
+    if ((st = sparse_block_table(cmp_block_table, "cmp_block_table", sh.B,
+                                 (ncmp + a.cmp.bs - 1) / a.cmp.bs, &a.cmp)) != FIA_SUCCESS) {
       return st;
     }
-    if (hca) {
-      // One slot per compressed row of the longest sequence; the merge folds
-      // at most 64 chunks of 64 slots.
-      K2 = (int64_t)align_up((size_t)ncmp, fia::kSparseChunk);
-      if (K2 + 128 > 64 * fia::kSparseChunk) {
-        return fail(FIA_ERR_UNSUPPORTED, "max_seqused_kv too large for the heavily compressed mode");
-      }
-    }
+    // Heavily compressed: one slot per compressed row of the longest sequence.
+    if (hca) K2 = (int64_t)align_up((size_t)ncmp, fia::kSparseSub);
   }
-  if (seqused_kv->shape[0] != B) return fail(FIA_ERR_PARAM_INVALID, "seqused_kv must be int32 [B]");
-  if (sinks->dtype != FIA_DT_FP32 || sinks->ndim != 1 || sinks->shape[0] != N1) {
+  if (sinks->dtype != FIA_DT_FP32 || sinks->ndim != 1 || sinks->shape[0] != sh.N1) {
     return fail(FIA_ERR_PARAM_INVALID, "sinks must be fp32 [N1]");
   }
-  for (int d = 0; d + 1 < q->ndim; ++d) {
-    if (q->stride[d] % 8 || attention_out->stride[d] % 8) {
-      return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
-    }
-  }
-  if (q->stride[q->ndim - 1] != 1 || attention_out->stride[q->ndim - 1] != 1 ||
-      reinterpret_cast<uintptr_t>(q->data) % 16 || reinterpret_cast<uintptr_t>(attention_out->data) % 16) {
-    return fail(FIA_ERR_UNSUPPORTED, "q / attention_out rows must be 16-byte aligned");
-  }
-
   fia_executor* e = new fia_executor();
   e->kind = KIND_SPARSE;
-  SparseArgs& a = e->sp;
-  a.q = static_cast<const uint16_t*>(q->data);
-  a.q_sb = tnd ? 0 : q->stride[0];
-  a.q_ss = q->stride[tnd ? 0 : 1];
-  a.q_sh = q->stride[tnd ? 1 : 2];
-  a.o = static_cast<uint16_t*>(attention_out->data);
-  a.o_sb = tnd ? 0 : attention_out->stride[0];
-  a.o_ss = attention_out->stride[tnd ? 0 : 1];
-  a.o_sh = attention_out->stride[tnd ? 1 : 2];
-  a.cu_q = tnd ? static_cast<const int32_t*>(cu_seqlens_q->data) : nullptr;
-  a.n_rows = (int32_t)n_rows;
-  a.ori = static_cast<const uint8_t*>(ori_kv->data);
-  a.ori_sb = osb;
-  a.ori_ss = oss;
-  a.cmp = has_cmp ? static_cast<const uint8_t*>(cmp_kv->data) : nullptr;
-  a.cmp_sb = csb;
-  a.cmp_ss = css;
-  a.ori_bt = static_cast<const int32_t*>(ori_block_table->data);
-  a.ori_bt_sb = ori_block_table->stride[0];
-  a.cmp_bt = has_cmp ? static_cast<const int32_t*>(cmp_block_table->data) : nullptr;
-  a.cmp_bt_sb = has_cmp ? cmp_block_table->stride[0] : 0;
-  a.idx = cmp_sparse_indices ? static_cast<const int32_t*>(cmp_sparse_indices->data) : nullptr;
-  a.idx_sb = idx_sb;
-  a.idx_ss = idx_ss;
-  a.seqused = static_cast<const int32_t*>(seqused_kv->data);
+  a.fmt = fia::SF_FP8_PACKED;
   a.sinks = static_cast<const float*>(sinks->data);
-  a.B = (int32_t)B;
-  a.S1 = (int32_t)S1;
-  a.N1 = (int32_t)N1;
-  a.K2 = (int32_t)K2;
-  a.bs1 = (int32_t)bs1;
-  a.bs2 = (int32_t)bs2;
-  a.nb1 = (int32_t)nb1;
-  a.nb2 = (int32_t)nb2;
-  a.ori_bt_cols = (int32_t)ori_block_table->shape[1];
-  a.cmp_bt_cols = has_cmp ? (int32_t)cmp_block_table->shape[1] : 0;
   a.cmp_ratio = p->cmp_ratio;
   a.win_left = p->ori_win_left;
   a.win_right = p->ori_win_right;
-  a.n_win_slots = (int32_t)align_up((size_t)(a.win_left + a.win_right + 1), fia::kSparseChunk);
-  a.n_slots = a.n_win_slots + a.K2;
   a.has_cmp = has_cmp ? 1 : 0;
   a.cmp_direct = hca ? 1 : 0;
   a.scale_log2 = (float)(p->softmax_scale * 1.4426950408889634);
-  const int64_t n_chunks = a.n_slots / fia::kSparseChunk;
-  e->part_o_off = 0;
-  const size_t rows = (size_t)n_rows;
-  e->part_lse_off = align_up(rows * n_chunks * N1 * fia::kSparseD * sizeof(float), kAlign);
-  e->ws_size = align_up(e->part_lse_off + rows * n_chunks * N1 * sizeof(float), kAlign);
-  *workspace_size = e->ws_size;
-  *executor = e;
-  return FIA_SUCCESS;
+  e->sp = a;
+  return sparse_finish(e, K2, workspace_size, executor);
+}
+
+fia_status fia_sparse_flash_mla_get_workspace_size(
+    const fia_sfmla_params* p, const fia_tensor* q, const fia_tensor* ori_kv,
+    const fia_tensor* cmp_kv, const fia_tensor* ori_sparse_indices,
+    const fia_tensor* cmp_sparse_indices, const fia_tensor* ori_block_table,
+    const fia_tensor* cmp_block_table, const fia_tensor* cu_seqlens_q,
+    const fia_tensor* cu_seqlens_ori_kv, const fia_tensor* cu_seqlens_cmp_kv,
+    const fia_tensor* seqused_q, const fia_tensor* seqused_kv, int64_t max_seqused_kv,
+    const fia_tensor* sinks, const fia_tensor* metadata, const fia_tensor* attention_out,
+    const fia_tensor* softmax_lse, size_t* workspace_size, fia_executor** executor) {
+  (void)metadata;
+  if (!p || !q || !ori_kv || !seqused_kv || !attention_out || !workspace_size || !executor) {
+    return fail(FIA_ERR_NULLPTR, "params, q, ori_kv, seqused_kv, attention_out, workspace_size "
+                                 "and executor must not be NULL");
+  }
+  *executor = nullptr;
+  *workspace_size = 0;
+  fia_status st;
+  const fia_tensor* must[] = {q, ori_kv, seqused_kv, attention_out};
+  const char* names[] = {"q", "ori_kv", "seqused_kv", "attention_out"};
+  for (int i = 0; i < 4; ++i) {
+    if ((st = check_tensor(must[i], names[i])) != FIA_SUCCESS) return st;
+  }
+  const std::string lq = p->layout_q ? p->layout_q : "BSND";
+  const std::string lkv = p->layout_kv ? p->layout_kv : "PA_BBND";
+  if (lq != "BSND" && lq != "TND") return fail(FIA_ERR_PARAM_INVALID, "layout_q must be BSND or TND");
+  const bool tnd = lq == "TND";
+  // Layout pairs: BSND / BSND, TND / TND, BSND / PA_BBND, TND / PA_BBND.
+  const bool paged = lkv == "PA_BBND";
+  if (!paged && lkv != lq) {
+    return fail(FIA_ERR_PARAM_INVALID, "layout_kv must be PA_BBND or equal layout_q");
+  }
+  if (p->ori_mask_mode != 4) return fail(FIA_ERR_PARAM_INVALID, "ori_mask_mode must be 4 (band)");
+  if (p->ori_win_left != 127 || p->ori_win_right != 0) {
+    return fail(FIA_ERR_PARAM_INVALID, "ori_win_left must be 127 and ori_win_right 0");
+  }
+  if (ori_sparse_indices != nullptr) return fail(FIA_ERR_PARAM_INVALID, "ori_sparse_indices is reserved");
+  if (seqused_q != nullptr) return fail(FIA_ERR_PARAM_INVALID, "seqused_q is reserved");
+  if (q->dtype != FIA_DT_BF16 && q->dtype != FIA_DT_FP16) {
+    return fail(FIA_ERR_PARAM_INVALID, "q must be fp16 or bf16");
+  }
+  SparseArgs a{};
+  SparseShape sh;
+  if ((st = sparse_query(q, attention_out, cu_seqlens_q, seqused_kv, tnd, q->dtype, &sh, &a)) !=
+      FIA_SUCCESS) {
+    return st;
+  }
+  if (sh.N1 < 1 || sh.N1 > 128 || (sh.N1 & (sh.N1 - 1)) != 0) {
+    return fail(FIA_ERR_PARAM_INVALID, "q heads must be a power of two in 1..128");
+  }
+  const bool has_cmp = cmp_kv != nullptr;
+  // Modes (sparse_flash_mla SWA / CSA / HCA constraints).
+  if (!has_cmp) {
+    if (p->cmp_ratio != 1) return fail(FIA_ERR_PARAM_INVALID, "SWA (no cmp_kv) needs cmp_ratio 1");
+    if (cmp_sparse_indices || cmp_block_table || cu_seqlens_cmp_kv) {
+      return fail(FIA_ERR_PARAM_INVALID, "SWA takes no cmp_sparse_indices, cmp_block_table or "
+                                         "cu_seqlens_cmp_kv");
+    }
+    if (p->cmp_mask_mode != 0) return fail(FIA_ERR_PARAM_INVALID, "SWA needs cmp_mask_mode 0");
+  } else {
+    if (p->cmp_mask_mode != 3) return fail(FIA_ERR_PARAM_INVALID, "cmp_mask_mode must be 3");
+    if (cmp_sparse_indices != nullptr && p->cmp_ratio != 4) {
+      return fail(FIA_ERR_PARAM_INVALID, "CSA (cmp_sparse_indices) needs cmp_ratio 4");
+    }
+    if (cmp_sparse_indices == nullptr && p->cmp_ratio != 128) {
+      return fail(FIA_ERR_PARAM_INVALID, "HCA (cmp_kv without indices) needs cmp_ratio 128");
+    }
+  }
+  // One pool: PA_BBND [n_blocks, block_size, 1, 512], BSND [B, S2, 1, 512]
+  // or TND [T2, 1, 512] (cumulative row offsets in cu).
+  auto check_pool = [&](const fia_tensor* t, const fia_tensor* bt, const fia_tensor* cu,
+                        const char* name, int64_t max_rows, fia::SparsePool* pd) -> fia_status {
+    fia_status s2 = check_tensor(t, name);
+    if (s2 != FIA_SUCCESS) return s2;
+    const std::string nm = name;
+    if (t->dtype != q->dtype) return fail(FIA_ERR_PARAM_INVALID, nm + " must have the dtype of q");
+    const int nd = tnd && !paged ? 3 : 4;
+    if (t->ndim != nd || t->shape[nd - 2] != 1 || t->shape[nd - 1] != fia::kSparseD) {
+      return fail(FIA_ERR_PARAM_INVALID,
+                  nm + (paged ? " must be [n_blocks, block_size, 1, 512]"
+                              : (tnd ? " must be [T2, 1, 512]" : " must be [B, S2, 1, 512]")));
+    }
+    for (int d = 0; d + 2 < nd; ++d) {
+      if (t->stride[d] % 8 != 0) return fail(FIA_ERR_UNSUPPORTED, nm + ": rows must be 16-byte aligned");
+    }
+    if (reinterpret_cast<uintptr_t>(t->data) % 16 != 0) {
+      return fail(FIA_ERR_UNSUPPORTED, nm + ": rows must be 16-byte aligned");
+    }
+    pd->base = static_cast<const uint8_t*>(t->data);
+    pd->paged = paged ? 1 : 0;
+    if (paged) {
+      if (bt == nullptr) return fail(FIA_ERR_PARAM_INVALID, nm + " in PA_BBND needs its block table");
+      if (cu != nullptr) return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_*_kv is only for layout_kv TND");
+      if (t->shape[1] < 1 || t->shape[1] > 1024) {
+        return fail(FIA_ERR_PARAM_INVALID, nm + ": block_size must be 1..1024");
+      }
+      if (t->shape[0] < 1 || t->shape[0] > INT32_MAX) return fail(FIA_ERR_PARAM_INVALID, nm + ": bad block count");
+      pd->nb = (int32_t)t->shape[0];
+      pd->bs = (int32_t)t->shape[1];
+      pd->sb = t->stride[0] * 2;
+      pd->ss = t->stride[1] * 2;
+      return sparse_block_table(bt, (nm == "ori_kv") ? "ori_block_table" : "cmp_block_table", sh.B,
+                                (max_rows + pd->bs - 1) / pd->bs, pd);
+    }
+    if (bt != nullptr) return fail(FIA_ERR_PARAM_INVALID, "block tables are only for layout_kv PA_BBND");
+    if (tnd) {
+      if (cu == nullptr) return fail(FIA_ERR_PARAM_INVALID, nm + " in TND needs its cu_seqlens");
+      if ((s2 = check_tensor(cu, "cu_seqlens_kv")) != FIA_SUCCESS) return s2;
+      if (cu->dtype != FIA_DT_INT32 || cu->ndim != 1 || cu->shape[0] != sh.B + 1 || cu->stride[0] != 1) {
+        return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_ori_kv / cu_seqlens_cmp_kv must be contiguous "
+                                           "int32 [B + 1]");
+      }
+      if (t->shape[0] < 1) return fail(FIA_ERR_PARAM_INVALID, nm + " holds no rows");
+      pd->cu = static_cast<const int32_t*>(cu->data);
+      pd->sb = 0;
+      pd->ss = t->stride[0] * 2;
+      pd->n_rows = t->shape[0];
+      return FIA_SUCCESS;
+    }
+    if (cu != nullptr) return fail(FIA_ERR_PARAM_INVALID, "cu_seqlens_*_kv is only for layout_kv TND");
+    if (t->shape[0] != sh.B || t->shape[1] < 1) {
+      return fail(FIA_ERR_PARAM_INVALID, nm + " must be [B, S2, 1, 512] with S2 >= 1");
+    }
+    pd->sb = t->stride[0] * 2;
+    pd->ss = t->stride[1] * 2;
+    pd->n_rows = t->shape[1];
+    return FIA_SUCCESS;
+  };
+  if (max_seqused_kv < 0) return fail(FIA_ERR_PARAM_INVALID, "max_seqused_kv must be >= 0");
+  if ((st = check_pool(ori_kv, ori_block_table, cu_seqlens_ori_kv, "ori_kv", max_seqused_kv, &a.ori)) !=
+      FIA_SUCCESS) {
+    return st;
+  }
+  int64_t K2 = 0;
+  if (has_cmp) {
+    const int64_t ncmp = max_seqused_kv / p->cmp_ratio;
+    if ((st = check_pool(cmp_kv, cmp_block_table, cu_seqlens_cmp_kv, "cmp_kv", ncmp, &a.cmp)) !=
+        FIA_SUCCESS) {
+      return st;
+    }
+    if (cmp_sparse_indices != nullptr) {
+      if ((st = sparse_indices(cmp_sparse_indices, sh, &K2, &a)) != FIA_SUCCESS) return st;
+      if (K2 < 1) return fail(FIA_ERR_PARAM_INVALID, "K2 must be >= 1");
+    } else {
+      K2 = (int64_t)align_up((size_t)ncmp, fia::kSparseSub);
+    }
+  }
+  if (sinks != nullptr) {
+    if ((st = check_tensor(sinks, "sinks")) != FIA_SUCCESS) return st;
+    if (sinks->dtype != FIA_DT_FP32 || sinks->ndim != 1 || sinks->shape[0] != sh.N1 || sinks->stride[0] != 1) {
+      return fail(FIA_ERR_PARAM_INVALID, "sinks must be contiguous fp32 [N1]");
+    }
+    a.sinks = static_cast<const float*>(sinks->data);
+  }
+  if (p->return_softmax_lse) {
+    if (softmax_lse == nullptr) return fail(FIA_ERR_NULLPTR, "return_softmax_lse needs softmax_lse");
+    if ((st = check_tensor(softmax_lse, "softmax_lse")) != FIA_SUCCESS) return st;
+    // softmax_lse [B, N2, S1, N1 / N2] (BSND) or [N2, T1, N1 / N2] (TND), N2 = 1.
+    const fia_tensor* t = softmax_lse;
+    const bool ok = t->dtype == FIA_DT_FP32 &&
+                    (tnd ? (t->ndim == 3 && t->shape[0] == 1 && t->shape[1] == sh.n_rows && t->shape[2] == sh.N1)
+                         : (t->ndim == 4 && t->shape[0] == sh.B && t->shape[1] == 1 && t->shape[2] == sh.S1 &&
+                            t->shape[3] == sh.N1));
+    if (!ok) {
+      return fail(FIA_ERR_PARAM_INVALID, tnd ? "softmax_lse must be fp32 [1, T1, N1]"
+                                             : "softmax_lse must be fp32 [B, 1, S1, N1]");
+    }
+    a.lse = static_cast<float*>(t->data);
+    a.lse_sb = tnd ? 0 : t->stride[0];
+    a.lse_ss = tnd ? t->stride[1] : t->stride[2];
+    a.lse_sh = t->stride[t->ndim - 1];
+  }
+  fia_executor* e = new fia_executor();
+  e->kind = KIND_SPARSE;
+  a.fmt = q->dtype == FIA_DT_FP16 ? fia::SF_FP16 : fia::SF_BF16;
+  a.cmp_ratio = p->cmp_ratio;
+  a.win_left = p->ori_win_left;
+  a.win_right = p->ori_win_right;
+  a.has_cmp = has_cmp ? 1 : 0;
+  a.cmp_direct = (has_cmp && cmp_sparse_indices == nullptr) ? 1 : 0;
+  a.scale_log2 = (float)(p->softmax_scale * 1.4426950408889634);
+  e->sp = a;
+  return sparse_finish(e, K2, workspace_size, executor);
 }
 
 fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void* stream) {

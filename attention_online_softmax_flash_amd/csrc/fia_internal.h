@@ -111,41 +111,64 @@ struct AttnArgs {
   const int32_t* n_chunks_dev;
 };
 
-// Shared-KV sparse decode arguments.
+// One key / value pool of the sparse operators (ori_kv or cmp_kv).  Row rr
+// of batch entry b lives at
+//   paged: base + clamp(bt[b * bt_sb + min(rr / bs, bt_cols - 1)]) * sb + (rr % bs) * ss
+//   dense: base + b * sb + clamp(off_b + rr) * ss, off_b = cu[b] (packed TND
+//          rows, sb = 0) or 0 (BSND), clamped into [0, n_rows)
+// (block ids clamped into [0, nb)).  Strides in bytes.
+struct SparsePool {
+  const uint8_t* base;
+  int64_t sb, ss;
+  const int32_t* bt;                // paged: block table [B, bt_cols]
+  int64_t bt_sb;
+  int32_t bt_cols, bs, nb;
+  int32_t paged;
+  const int32_t* cu;                // dense TND: first row of each entry [B + 1]
+  int64_t n_rows;                   // dense: rows per batch (BSND) or in total (TND)
+};
+
+// Row formats of the sparse operators.
+enum SparseFmt {
+  SF_FP8_PACKED = 0,   // 640-byte rows: bf16 rope x64 | e4m3fn nope x448 | fp32 scale x7
+  SF_BF16 = 1,         // 512 bf16 values
+  SF_FP16 = 2          // 512 fp16 values
+};
+
+// Shared-KV sparse attention arguments (both sparse operators).
 struct SparseArgs {
   // BSND: row r = b * S1 + t is query token t of batch entry b.  TND: row r
   // is token r of [T1, N1, 512]; its batch entry b satisfies
   // cu_q[b] <= r < cu_q[b + 1] (batch strides are 0, token strides address
   // the row).  Partials and the grid run over the n_rows rows.
-  const uint16_t* q;                // bf16 [B, S1, N1, 512] or [T1, N1, 512]
+  int32_t fmt;                      // SparseFmt (query / output are fp16 with SF_FP16, else bf16)
+  const uint16_t* q;                // [B, S1, N1, 512] or [T1, N1, 512]
   int64_t q_sb, q_ss, q_sh;
-  uint16_t* o;                      // bf16, the shape of q
+  uint16_t* o;                      // the shape of q
   int64_t o_sb, o_ss, o_sh;
+  float* lse;                       // nullptr, or fp32 at b * lse_sb + tq * lse_ss + h * lse_sh
+  int64_t lse_sb, lse_ss, lse_sh;
   const int32_t* cu_q;              // TND: int32 [B + 1] on the device; BSND: nullptr
   int32_t n_rows;                   // B * S1 (BSND) or T1 (TND)
-  const uint8_t* ori;               // [nb1, bs1, 1, 640]
-  int64_t ori_sb, ori_ss;           // bytes
-  const uint8_t* cmp;
-  int64_t cmp_sb, cmp_ss;
-  const int32_t* ori_bt;
-  int64_t ori_bt_sb;
-  const int32_t* cmp_bt;
-  int64_t cmp_bt_sb;
+  SparsePool ori, cmp;
   const int32_t* idx;               // [B, S1, 1, K2] or [T1, 1, K2]
   int64_t idx_sb, idx_ss;
   const int32_t* seqused;           // [B]
-  const float* sinks;               // [N1]
+  const float* sinks;               // [N1] or nullptr
   int32_t B, S1, N1, K2;
-  int32_t bs1, bs2, nb1, nb2;
-  int32_t ori_bt_cols, cmp_bt_cols;
   int32_t cmp_ratio, win_left, win_right;
   int32_t n_win_slots;              // window slots (multiple of 64)
   int32_t n_slots;                  // window slots + K2
   int32_t has_cmp;
   int32_t cmp_direct;               // no indices: compressed slot k is row k
   float scale_log2;
-  float* part_o;                    // [n_rows * n_chunks * N1 * 512]
-  float* part_lse;                  // [n_rows * n_chunks * N1]
+  // Work split: every query row's slots are cut into n_chunks chunks of
+  // sub_per_chunk 64-slot sub-chunks; head blocks of 64 heads.  A workgroup
+  // takes one (row, head block, chunk).  xcd_rows: the workgroups of one
+  // row run on one XCD (row r on XCD r % 8; needs n_rows % 8 == 0).
+  int32_t sub_per_chunk, n_chunks, n_hb, xcd_rows;
+  float* part_o;                    // [n_rows * n_chunks * N1 * 512] (n_chunks > 1)
+  float* part_lse;                  // [n_rows * n_chunks * N1], log2 domain
 };
 
 // Launchers (defined next to their kernels).  Return hipGetLastError().
@@ -167,8 +190,11 @@ hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* 
 constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
 constexpr int kPrefillKeys = 64;    // keys per prefill tile
 constexpr int kDecodeStep = 32;     // keys per decode wave step
-constexpr int kSparseChunk = 64;    // row slots per sparse workgroup
-constexpr int kSparseHeads = 32;    // heads per sparse workgroup
+constexpr int kSparseSub = 64;      // row slots per sparse sub-chunk
+constexpr int kSparseHeads = 64;    // heads per sparse workgroup
+constexpr int kSparseMaxSub = 8;    // sub-chunks per sparse workgroup, at most
+constexpr int kSparseMaxChunks = 64;  // chunks per sparse query row, at most
+constexpr int kSparseBtCache = 512;   // block-table entries a sparse workgroup caches in LDS
 constexpr int kSparseD = 512;       // logical row width (64 rope + 448 nope)
 constexpr int kRowBytes = 640;
 

@@ -1,7 +1,7 @@
-// Shared-KV sparse decode (KvQuantSparseAttnSharedkv; sparse_flash_mla CSA
-// and HCA modes): O = softmax(Q K~^T * scale) V~ with K~ = V~ = the window rows of the
-// original KV followed by the top-k selected rows of the compressed KV, plus a
-// per-head sink logit.
+// Shared-KV sparse attention (KvQuantSparseAttnSharedkv; sparse_flash_mla SWA,
+// CSA and HCA modes): O = softmax(Q K~^T * scale) V~ with K~ = V~ = the window
+// rows of the original KV followed by the selected rows of the compressed KV,
+// plus an optional per-head sink logit.
 //
 // Row list of query token t of batch b (the S1 tokens of the entry are the
 // last S1 positions of its KV sequence: p = Lk - S1 + t; with the TND layout
@@ -13,27 +13,52 @@
 //     (compressed-sparse) or c = s - n_win (heavily compressed: the whole
 //     compressed sequence, no indices), used when 0 <= c < Lc - (S1 - 1 - t),
 //     Lc = floor(Lk / cmp_ratio) (right-down causal over the compressed rows).
-// Each packed 640-byte row holds bf16 rope x64 | e4m3fn nope x448 | fp32
-// scale x7 (one per 64-wide nope tile); the logical 512-vector is
-// [rope | nope * scale].
+// Row formats: packed 640-byte rows (bf16 rope x64 | e4m3fn nope x448 | fp32
+// scale x7, one per 64-wide nope tile; the logical 512-vector is
+// [rope | nope * scale]), or plain bf16 / fp16 rows of 512 values.
 //
-// One workgroup takes 64 slots x 32 heads of one batch entry: it gathers the
-// rows through the block tables, dequantises them into LDS once (row-major),
-// runs both products on 32x32x16 bf16 MFMA (the value product reads its
-// transposed operand with LDS transpose reads) and writes a normalised
-// partial with its log2-sum-exp.  The merge kernel folds the chunks in slot order together with
-// the sink: an extra logit sigma_h whose value vector is zero.
+// Work split.  A workgroup of 8 waves takes one query row, a block of 64
+// heads and one chunk of its slots (sub_per_chunk sub-chunks of 64 slots), so
+// every gathered row is converted once for all the heads that read it.  It
+//   1. loads its query rows into registers and caches the batch entry's block
+//      table rows and its index entries in LDS (all in flight together);
+//   2. resolves a sub-chunk's 64 slots to row addresses from those LDS copies
+//      (the row loads are then the only dependent trip to memory);
+//   3. loads the rows (the next sub-chunk's loads are in flight while the
+//      current one is computed), converts them to bf16 / fp16 in LDS
+//      row-major, runs S^T = X Q^T and O^T = X^T P^T on 32x32x16 MFMA (the
+//      value product reads its transposed operand with LDS transpose reads)
+//      with an online softmax across the sub-chunks;
+//   4. writes the final output (and LSE) when the row has one chunk, else a
+//      normalised fp32 partial with its log2-sum-exp, which the merge kernel
+//      folds in chunk order together with the sink.
 #include "fia_device.h"
 
 namespace fia {
 
 namespace {
 
-constexpr int X_PITCH = kSparseD * 2 + 16;   // bytes per row-major row
-constexpr int X_BYTES = kSparseChunk * X_PITCH;
-constexpr int P_BYTES = 4 * 64 * 16;
-constexpr int SX_BYTES = 2 * 64 * 16 * 4;
-constexpr int LDS_TOTAL = X_BYTES + P_BYTES + SX_BYTES + 64 * 4 + 2 * 32 * 4 * 2;
+constexpr int kThreads = 512;
+constexpr int X_PITCH = kSparseD * 2 + 16;          // bytes per row-major row in LDS
+constexpr int X_BYTES = kSparseSub * X_PITCH;        // 66560
+constexpr int Q_BYTES = kSparseHeads * X_PITCH;      // the workgroup's query rows, row-major
+constexpr int SX_BYTES = 4 * 64 * 16 * 4;            // score halves of the dh = 1 waves
+constexpr int RP_BYTES = 2 * kSparseSub * 8;         // row addresses, two sub-chunks
+constexpr int BT_BYTES = 2 * kSparseBtCache * 4;     // ori / cmp block-table rows
+constexpr int IX_BYTES = kSparseMaxSub * kSparseSub * 4;
+constexpr int ST_BYTES = 4 * 64 * 4;                 // row max / sum per (slot half, head)
+constexpr int LM_BYTES = 2 * 8;                      // live-slot masks, two sub-chunks
+constexpr int OFF_Q = X_BYTES;
+constexpr int OFF_SX = OFF_Q + Q_BYTES;
+// The probabilities [head block][k step][lane] (8 KB) share the score
+// exchange area: they are written after its last read in a step.
+constexpr int OFF_P = OFF_SX;
+constexpr int OFF_RP = OFF_SX + SX_BYTES;
+constexpr int OFF_BT = OFF_RP + RP_BYTES;
+constexpr int OFF_IX = OFF_BT + BT_BYTES;
+constexpr int OFF_ST = OFF_IX + IX_BYTES;
+constexpr int OFF_LM = OFF_ST + ST_BYTES;
+constexpr int LDS_TOTAL = OFF_LM + LM_BYTES;
 
 }  // namespace
 
@@ -46,6 +71,42 @@ __device__ __forceinline__ void e4m3fn_x4(uint32_t w, float* f) {
   f[1] = lo[1];
   f[2] = hi[0];
   f[3] = hi[1];
+}
+
+// Loads through a row address that was kept in LDS: the address is known to
+// be global memory, so the load is a global (not a generic / flat) load, which
+// would otherwise also hold up every later wait for LDS traffic.
+typedef const __attribute__((address_space(1))) u32x4* gptr_u32x4;
+typedef const __attribute__((address_space(1))) float* gptr_f32;
+__device__ __forceinline__ u32x4 ld16_global(const uint8_t* p) {
+  return *(gptr_u32x4)(p);
+}
+__device__ __forceinline__ float ldf_global(const uint8_t* p) {
+  return *(gptr_f32)(p);
+}
+
+// 32x32x16 MFMA on bf16 or fp16 operands (the 16-bit type of the rows).
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32h(u32x4 a, u32x4 b, f32x16 c) {
+  if constexpr (F16) {
+    typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  } else {
+    return mfma32(a, b, c);
+  }
+}
+
+// Two floats -> one packed pair of the 16-bit type (round to nearest even).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack_h2(float lo, float hi) {
+  if constexpr (F16) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, f16x2));
+  } else {
+    return pack_bf16x2(lo, hi);
+  }
 }
 
 // Batch entry, token position and query count of row r.  BSND: b = r / S1.
@@ -86,353 +147,508 @@ __device__ __forceinline__ SparseRow sparse_row(const SparseArgs& a, int r) {
   return w;
 }
 
-// Slots s[0..N) of query row w -> packed row addresses (nullptr for an unused
-// slot) and ids: j for window row j, (1 << 30) | c for compressed row c, -1
-// if unused.  Compressed slot k holds row idx[b][k] (compressed-sparse) or
-// row k itself (heavily compressed, no indices).  No read depends on a branch: every table read goes to an
-// in-bounds address (a clamped position), so the N index reads, then the N
-// block-table reads, are each in flight together.
-template <int N>
-__device__ __forceinline__ void sparse_slot_rows(const SparseArgs& a, const SparseRow& w, const int* s,
-                                                 int Lk, const uint8_t** row, int32_t* id) {
-  const int b = w.b;
-  const int t = w.t;
-  const int p = Lk - w.s1 + t;
-  const int jmax = min(Lk - 1, p + a.win_right);
-  const int n_cmp = Lk / a.cmp_ratio - (w.s1 - 1 - t);
-  const bool cmp_on = a.has_cmp && a.K2 > 0;
-  int c[N];
-#pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const int k = min(max(s[u] - a.n_win_slots, 0), a.K2 > 0 ? a.K2 - 1 : 0);
-    if (a.cmp_direct) {
-      c[u] = cmp_on ? s[u] - a.n_win_slots : -1;
-    } else {
-      c[u] = cmp_on ? a.idx[(int64_t)b * a.idx_sb + (int64_t)w.tq * a.idx_ss + k] : -1;
-    }
-  }
-  int raw[N], slot[N];
-  bool win[N], ok[N];
-#pragma unroll
-  for (int u = 0; u < N; ++u) {
-    win[u] = s[u] < a.n_win_slots;
-    const int j = p - a.win_left + s[u];
-    const int k = s[u] - a.n_win_slots;
-    const bool wok = s[u] <= a.win_left + a.win_right && j >= 0 && j <= jmax;
-    const bool cok = cmp_on && k < a.K2 && c[u] >= 0 && c[u] < n_cmp;
-    ok[u] = win[u] ? wok : cok;
-    const int rr = ok[u] ? (win[u] ? j : c[u]) : 0;
-    const int bs = win[u] ? a.bs1 : a.bs2;
-    const int page = rr / bs;
-    slot[u] = rr - page * bs;
-    // Compressed slots read the compressed table only when there is one.
-    const bool use_cmp = !win[u] && cmp_on;
-    const int cols = use_cmp ? a.cmp_bt_cols : a.ori_bt_cols;
-    const int32_t* bt = use_cmp ? a.cmp_bt + (int64_t)b * a.cmp_bt_sb : a.ori_bt + (int64_t)b * a.ori_bt_sb;
-    raw[u] = bt[min(page, cols - 1)];
-    id[u] = ok[u] ? (win[u] ? j : ((1 << 30) | c[u])) : -1;
-  }
-#pragma unroll
-  for (int u = 0; u < N; ++u) {
-    const uint8_t* rp;
-    if (win[u]) {
-      rp = a.ori + (int64_t)clamp_block(raw[u], a.nb1) * a.ori_sb + (int64_t)slot[u] * a.ori_ss;
-    } else {
-      rp = a.cmp + (int64_t)clamp_block(raw[u], a.nb2) * a.cmp_sb + (int64_t)slot[u] * a.cmp_ss;
-    }
-    row[u] = ok[u] ? rp : nullptr;
-  }
-}
-
+// KV length of the row's entry, clamped to what its pool can address.
 __device__ __forceinline__ int sparse_len(const SparseArgs& a, const SparseRow& w) {
   if (!w.live) return 0;
-  int Lk = a.seqused[w.b];
-  const int cap = a.ori_bt_cols * a.bs1;
-  return Lk < 0 ? 0 : (Lk > cap ? cap : Lk);
+  const int Lk = a.seqused[w.b];
+  const int64_t cap = a.ori.paged ? (int64_t)a.ori.bt_cols * a.ori.bs : a.ori.n_rows;
+  return Lk < 0 ? 0 : (int)((int64_t)Lk > cap ? cap : Lk);
 }
 
-// Grid: (n_slots / 64, N1 / 32, n_rows); 256 threads.
-__global__ __launch_bounds__(256, 2) void sparse_chunk(SparseArgs a) {
-  extern __shared__ __align__(16) uint8_t lds[];
-  uint8_t* xs = lds;                         // [64][X_PITCH]
-  u32x4* ps = reinterpret_cast<u32x4*>(xs + X_BYTES);        // [4][64]
-  float* sx = reinterpret_cast<float*>(xs + X_BYTES + P_BYTES);  // [2][64][16]
-  int32_t* ids = reinterpret_cast<int32_t*>(xs + X_BYTES + P_BYTES + SX_BYTES);  // [64]
-  float* mx_s = reinterpret_cast<float*>(ids + 64);          // [2][32]
-  float* l_s = mx_s + 64;                                    // [2][32]
+// Row rr of pool `pd` for batch entry b.  `bt(col)` returns the raw block id
+// of block-table column col of the entry (col < bt_cols); `off` is the
+// entry's first row in a packed (TND) pool.
+template <class BT>
+__device__ __forceinline__ const uint8_t* pool_row(const SparsePool& pd, int b, int rr, int64_t off,
+                                                   BT bt) {
+  if (pd.paged) {
+    const int page = rr / pd.bs;
+    const int slot = rr - page * pd.bs;
+    const int blk = clamp_block(bt(min(page, pd.bt_cols - 1)), pd.nb);
+    return pd.base + (int64_t)blk * pd.sb + (int64_t)slot * pd.ss;
+  }
+  int64_t row = off + rr;
+  row = row < 0 ? 0 : (row >= pd.n_rows ? pd.n_rows - 1 : row);
+  return pd.base + (int64_t)b * pd.sb + row * pd.ss;
+}
 
-  const int chunk = blockIdx.x;
-  const int hb = blockIdx.y;
-  const int r = blockIdx.z;   // query row
-  const SparseRow qr = sparse_row(a, r);
-  const int b = qr.b;
-  const int n_chunks = gridDim.x;
+// What a query row needs to resolve its slots.
+struct SlotCtx {
+  int b, p, jmax, n_cmp;
+  int64_t ori_off, cmp_off;   // first row of the entry in packed (TND) pools
+  bool live;
+};
+__device__ __forceinline__ SlotCtx slot_ctx(const SparseArgs& a, const SparseRow& w, int Lk) {
+  SlotCtx c;
+  c.b = w.b;
+  c.live = w.live;
+  c.p = Lk - w.s1 + w.t;
+  c.jmax = min(Lk - 1, c.p + a.win_right);
+  c.n_cmp = Lk / a.cmp_ratio - (w.s1 - 1 - w.t);
+  c.ori_off = a.ori.cu ? a.ori.cu[w.b] : 0;
+  c.cmp_off = (a.has_cmp && a.cmp.cu) ? a.cmp.cu[w.b] : 0;
+  return c;
+}
+
+// Slot s of a query row -> packed row address (nullptr for an unused slot)
+// and id: j for window row j, (1 << 30) | c for compressed row c, -1 if
+// unused.  `ori_bt` / `cmp_bt` read block-table columns of the entry and
+// `idx(k)` index entry k of the row (the kernel reads them from its LDS
+// copies, the test export from global memory).
+template <class OBT, class CBT, class IDX>
+__device__ __forceinline__ const uint8_t* slot_row(const SparseArgs& a, const SlotCtx& c, int s,
+                                                   OBT ori_bt, CBT cmp_bt, IDX idx, int32_t* id) {
+  *id = -1;
+  if (!c.live || s < 0 || s >= a.n_slots) return nullptr;
+  if (s < a.n_win_slots) {
+    const int j = c.p - a.win_left + s;
+    if (s > a.win_left + a.win_right || j < 0 || j > c.jmax) return nullptr;
+    *id = j;
+    return pool_row(a.ori, c.b, j, c.ori_off, ori_bt);
+  }
+  const int k = s - a.n_win_slots;
+  if (!a.has_cmp || k >= a.K2) return nullptr;
+  const int cr = a.cmp_direct ? k : idx(k);
+  if (cr < 0 || cr >= c.n_cmp) return nullptr;
+  *id = (1 << 30) | cr;
+  return pool_row(a.cmp, c.b, cr, c.cmp_off, cmp_bt);
+}
+
+// Grid: n_rows * n_hb * n_chunks workgroups of 512 threads (8 waves).
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
+  constexpr bool F16 = FMT == SF_FP16;
+  extern __shared__ __align__(16) uint8_t lds[];
+  uint8_t* xs = lds;                                                   // [64][X_PITCH]
+  u32x4* ps = reinterpret_cast<u32x4*>(lds + OFF_P);                   // [2][4][64]
+  float* sx = reinterpret_cast<float*>(lds + OFF_SX);                  // [4][64][16]
+  const uint8_t** rowp = reinterpret_cast<const uint8_t**>(lds + OFF_RP);   // [2][64]
+  int32_t* bt_o = reinterpret_cast<int32_t*>(lds + OFF_BT);            // [kSparseBtCache]
+  int32_t* bt_c = bt_o + kSparseBtCache;                               // [kSparseBtCache]
+  int32_t* ixc = reinterpret_cast<int32_t*>(lds + OFF_IX);             // [64 * sub_per_chunk]
+  float* mx_s = reinterpret_cast<float*>(lds + OFF_ST);                // [2][64]
+  float* l_s = mx_s + 128;                                             // [2][64]
+  uint64_t* live_m = reinterpret_cast<uint64_t*>(lds + OFF_LM);       // [2]: bit s = slot s used
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = uniform(tid >> 6);   // wave-uniform: scalar bookkeeping
+  const int wave = uniform(tid >> 6);
   const int n = lane & 31;
   const int hh = lane >> 5;
-  const int Lk = sparse_len(a, qr);
-  const int s0 = chunk * kSparseChunk;
+
+  // Workgroup -> (row, head block, chunk).
+  const int parts = a.n_hb * a.n_chunks;
+  int r, part;
+  {
+    const int L = blockIdx.x;
+    if (a.xcd_rows) {
+      const int k = L >> 3;
+      r = (L & 7) + 8 * (k / parts);
+      part = k % parts;
+    } else {
+      r = L / parts;
+      part = L - r * parts;
+    }
+  }
+  const int hb = part / a.n_chunks;
+  const int chunk = part - hb * a.n_chunks;
+  const int sub_n = a.sub_per_chunk;
+  const int s_begin = chunk * kSparseSub * sub_n;
+
+  // Roles.  Scores: slot half sb, head half hq, d half dh.  Values: head half
+  // hq, d quarter dq.  Lane (n, hh) owns head 64 hb + 32 hq + n.
   const int sb = wave & 1;
-  const int dh = wave >> 1;
-  const int head = hb * kSparseHeads + n;
+  const int hq = (wave >> 1) & 1;
+  const int dh = wave >> 2;
+  const int dq = (wave & 1) + 2 * (wave >> 2);
+  const int head = kSparseHeads * hb + 32 * hq + n;
+  const bool head_ok = head < a.N1;
 
-  // Query operand for the score product, loaded first so its latency overlaps
-  // the row gather: head n, d = 256 dh + 16 c + 8 hh .. +7.
-  u32x4 qv[16];
+  const SparseRow qr = sparse_row(a, r);
+  const int b = qr.b;
+
+  // 1. The workgroup's 64 query rows into LDS (row-major; heads past N1 are
+  // zero), then the LDS copies of the entry's block tables and index entries.
+  uint8_t* qs = lds + OFF_Q;
   {
-    const uint16_t* qp = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss + (int64_t)head * a.q_sh +
-                         256 * dh + 8 * hh;
+    const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss;
+    u32x4 qv[8];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) qv[c] = ld16(qp + 16 * c);
-  }
-
-  // 1. Gather and dequantise: thread owns rows 4 rg .. 4 rg + 3 and the
-  // 16-byte pieces pc = tid/16 + 16 q of their bf16 form (pieces 0..7 rope,
-  // 8..63 nope: 8 fp8 codes and their tile scale).  Every load is issued
-  // before the first conversion; unused slots read row 0 of the original KV
-  // (in bounds) and are zeroed.
-  {
-    const int rg = tid & 15;
-    const int pc0 = tid >> 4;
-    const bool rope0 = pc0 < 8;   // wave-uniform: waves 0, 1
-    int sl[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) sl[u] = s0 + 4 * rg + u;
-    const uint8_t* rows[4];
-    int32_t rid[4];
-    sparse_slot_rows<4>(a, qr, sl, Lk, rows, rid);
-    if (pc0 == 0) {
-#pragma unroll
-      for (int u = 0; u < 4; ++u) ids[4 * rg + u] = rid[u];
+    for (int v = 0; v < 8; ++v) {
+      const int p = tid + kThreads * v;   // 16-byte piece p % 64 of head p / 64
+      const int hd = kSparseHeads * hb + (p >> 6);
+      qv[v] = hd < a.N1 ? ld16(qrow + (int64_t)hd * a.q_sh + 8 * (p & 63)) : u32x4{0u, 0u, 0u, 0u};
     }
-    u32x4 raw0[4];
-    float sc0[4];
-    u32x2 codes[3][4];
-    float scl[3][4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const uint8_t* rp = rows[u] != nullptr ? rows[u] : a.ori;
-      if (rope0) {
-        raw0[u] = ld16(rp + 16 * pc0);
-        sc0[u] = 0.f;
-      } else {
-        const u32x2 cw = ld8(rp + 128 + 8 * (pc0 - 8));
-        raw0[u] = u32x4{cw.x, cw.y, 0u, 0u};
-        sc0[u] = *reinterpret_cast<const float*>(rp + 576 + 4 * ((pc0 - 8) >> 3));
-      }
-#pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        const int np = pc0 + 16 * q - 8;
-        codes[q - 1][u] = ld8(rp + 128 + 8 * np);
-        scl[q - 1][u] = *reinterpret_cast<const float*>(rp + 576 + 4 * (np >> 3));
-      }
-    }
-    auto dequant = [&](u32x2 cw, float sc) FIA_INLINE {
-      float f[8];
-      e4m3fn_x4(cw.x, f);
-      e4m3fn_x4(cw.y, f + 4);
-      return u32x4{pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
-                   pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)};
-    };
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      uint8_t* xr = xs + (4 * rg + u) * X_PITCH;
-      const bool live = rows[u] != nullptr;
-      const u32x4 w0 = rope0 ? raw0[u] : dequant(u32x2{raw0[u].x, raw0[u].y}, sc0[u]);
-      *reinterpret_cast<u32x4*>(xr + 16 * pc0) = live ? w0 : zero;
-#pragma unroll
-      for (int q = 1; q < 4; ++q) {
-        const u32x4 w = dequant(codes[q - 1][u], scl[q - 1][u]);
-        *reinterpret_cast<u32x4*>(xr + 16 * (pc0 + 16 * q)) = live ? w : zero;
-      }
+    for (int v = 0; v < 8; ++v) {
+      const int p = tid + kThreads * v;
+      *reinterpret_cast<u32x4*>(qs + (p >> 6) * X_PITCH + 16 * (p & 63)) = qv[v];
     }
   }
+  const bool cache_o = a.ori.paged && a.ori.bt_cols <= kSparseBtCache;
+  const bool cache_c = a.has_cmp && a.cmp.paged && a.cmp.bt_cols <= kSparseBtCache;
+  if (cache_o) {
+    const int32_t* src = a.ori.bt + (int64_t)b * a.ori.bt_sb;
+    for (int i = tid; i < a.ori.bt_cols; i += kThreads) bt_o[i] = src[i];
+  }
+  if (cache_c) {
+    const int32_t* src = a.cmp.bt + (int64_t)b * a.cmp.bt_sb;
+    for (int i = tid; i < a.cmp.bt_cols; i += kThreads) bt_c[i] = src[i];
+  }
+  const int k_begin = s_begin - a.n_win_slots;   // index entry of the chunk's first slot
+  const bool use_idx = a.has_cmp && !a.cmp_direct;
+  if (use_idx) {
+    const int32_t* src = a.idx + (int64_t)b * a.idx_sb + (int64_t)qr.tq * a.idx_ss;
+    for (int i = tid; i < kSparseSub * sub_n; i += kThreads) {
+      const int k = k_begin + i;
+      ixc[i] = (k >= 0 && k < a.K2) ? src[k] : -1;
+    }
+  }
+  const int Lk = sparse_len(a, qr);
+  const SlotCtx ctx = slot_ctx(a, qr, Lk);
   __syncthreads();
 
-  // 2. Scores S^T[slot][head]: wave (sb, dh) = slot block 32 sb, d half dh.
-  f32x16 s;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) s[r] = 0.f;
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH +
-                                                     (256 * dh + 16 * c + 8 * hh) * 2);
-    s = mfma32(av, qv[c], s);
-  }
-  if (dh == 1) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) sx[(sb * 64 + lane) * 16 + r] = s[r];
-  }
-  __syncthreads();
-  float m_loc = kNegInf;
-  if (dh == 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int slot = 32 * sb + 8 * (r >> 2) + 4 * hh + (r & 3);
-      const float x = (s[r] + sx[(sb * 64 + lane) * 16 + r]) * a.scale_log2;
-      s[r] = ids[slot] >= 0 ? x : kNegInf;
-      m_loc = fmaxf(m_loc, s[r]);
+  auto ori_bt = [&](int col) FIA_INLINE {
+    return cache_o ? bt_o[col] : a.ori.bt[(int64_t)b * a.ori.bt_sb + col];
+  };
+  auto cmp_bt = [&](int col) FIA_INLINE {
+    return cache_c ? bt_c[col] : a.cmp.bt[(int64_t)b * a.cmp.bt_sb + col];
+  };
+  auto idx_at = [&](int k) FIA_INLINE { return ixc[k - k_begin]; };
+  // Row addresses of sub-chunk u and the mask of its used slots into buffer
+  // u & 1 (wave 0: one slot per lane).
+  auto resolve = [&](int u) FIA_INLINE {
+    if (wave == 0) {
+      int32_t id;
+      const uint8_t* src = slot_row(a, ctx, s_begin + kSparseSub * u + lane, ori_bt, cmp_bt, idx_at, &id);
+      rowp[(u & 1) * kSparseSub + lane] = src;
+      const uint64_t m = __ballot(src != nullptr);
+      if (lane == 0) live_m[u & 1] = m;
     }
-    m_loc = pair32_max(m_loc);
-    if (hh == 0) mx_s[sb * 32 + n] = m_loc;
-  }
-  __syncthreads();
-  const float m_all = fmaxf(mx_s[n], mx_s[32 + n]);
-  const float m_use = (m_all == kNegInf) ? 0.f : m_all;
-  if (dh == 0) {
-    float l = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      float p[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        p[t] = fast_exp2(s[8 * kk + t] - m_use);
-        l += p[t];
-      }
-      ps[(2 * sb + kk) * 64 + lane] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
-                                           pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    }
-    l = pair32_sum(l);
-    if (hh == 0) l_s[sb * 32 + n] = l;
-  }
-  __syncthreads();
+  };
 
-  // 3. O^T[d][head] for d in [128 wave, 128 wave + 128).  Lane (n, hh)
-  // feeds k-step kk the slots 16 kk + 8 r + 4 hh + (0..3), r = 0, 1 (the
-  // order of the score accumulators) of column d = n: in 16-lane group g,
-  // lane j addresses slot 16 kk + 8 r + 4 (g / 2) + j / 4 at columns
-  // 16 (g % 2) + 4 (j % 4) .. + 3 of the 32-wide d block.
-  f32x16 o[4];
+  // Row pieces of one sub-chunk in registers.  Packed rows: piece p = tid +
+  // 512 v (p < 64 * 36) is 16 bytes of row p / 36: pieces 0..7 rope, 8..35
+  // 16 nope codes each (with their tile scale).  16-bit rows: piece p = tid +
+  // 512 v is 16 bytes (8 values) of row p / 64.
+  constexpr int NP = FMT == SF_FP8_PACKED ? 5 : 8;
+  constexpr int PPR = FMT == SF_FP8_PACKED ? 36 : 64;   // pieces per row
+  u32x4 raw[NP];
+  float scl[NP];
+  auto load_rows = [&](int u) FIA_INLINE {
+    const uint8_t* const* rp = rowp + (u & 1) * kSparseSub;
+#pragma unroll
+    for (int v = 0; v < NP; ++v) {
+      const int p = tid + kThreads * v;
+      raw[v] = u32x4{0u, 0u, 0u, 0u};
+      scl[v] = 0.f;
+      if (p < kSparseSub * PPR) {
+        const int row = p / PPR;
+        const int pc = p - row * PPR;
+        const uint8_t* src = rp[row];
+        if (src != nullptr) {
+          raw[v] = ld16_global(src + 16 * pc);
+          if (FMT == SF_FP8_PACKED && pc >= 8) scl[v] = ldf_global(src + 576 + 4 * ((pc - 8) >> 2));
+        }
+      }
+    }
+  };
+  auto store_rows = [&]() FIA_INLINE {
+#pragma unroll
+    for (int v = 0; v < NP; ++v) {
+      const int p = tid + kThreads * v;
+      if (p < kSparseSub * PPR) {
+        const int row = p / PPR;
+        const int pc = p - row * PPR;
+        uint8_t* xr = xs + row * X_PITCH;
+        if (FMT != SF_FP8_PACKED || pc < 8) {
+          *reinterpret_cast<u32x4*>(xr + 16 * pc) = raw[v];
+        } else {
+          const float sc = scl[v];
+          float f[16];
+          e4m3fn_x4(raw[v].x, f);
+          e4m3fn_x4(raw[v].y, f + 4);
+          e4m3fn_x4(raw[v].z, f + 8);
+          e4m3fn_x4(raw[v].w, f + 12);
+          u32x4* dst = reinterpret_cast<u32x4*>(xr + 128 + 32 * (pc - 8));
+          dst[0] = u32x4{pack_bf16x2(f[0] * sc, f[1] * sc), pack_bf16x2(f[2] * sc, f[3] * sc),
+                         pack_bf16x2(f[4] * sc, f[5] * sc), pack_bf16x2(f[6] * sc, f[7] * sc)};
+          dst[1] = u32x4{pack_bf16x2(f[8] * sc, f[9] * sc), pack_bf16x2(f[10] * sc, f[11] * sc),
+                         pack_bf16x2(f[12] * sc, f[13] * sc), pack_bf16x2(f[14] * sc, f[15] * sc)};
+        }
+      }
+    }
+  };
+
+  // Transposed value operand: in 16-lane group g, lane j addresses slot
+  // 16 kk + 8 r + 4 (g / 2) + j / 4 at columns 16 (g % 2) + 4 (j % 4) .. + 3
+  // of the 32-wide d block (the order of the score accumulators).
+  const uint8_t* tb;
   {
     const int g16 = lane >> 4;
     const int j = lane & 15;
-    const uint8_t* tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH +
-                        (128 * wave + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
+    tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH + (128 * dq + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
+  }
+
+  float m_run = kNegInf;   // running max (log2 domain) of this lane's head
+  float l_run = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) o[mb][q] = 0.f;
+  }
+
+  int n_sub = 0;
+  while (n_sub < sub_n && s_begin + kSparseSub * n_sub < a.n_slots) ++n_sub;
+  if (n_sub > 0) {
+    resolve(0);
+    __syncthreads();
+    load_rows(0);
+  }
+  for (int u = 0; u < n_sub; ++u) {
+    store_rows();
+    const bool has_next = u + 1 < n_sub;
+    if (has_next) resolve(u + 1);
+    __syncthreads();
+    if (has_next) load_rows(u + 1);
+    const uint64_t live = live_m[u & 1];
+
+    // 2. Scores S^T[slot][head] for slots 32 sb + (0..31), heads of hq, d half dh.
+    f32x16 s;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) s[q] = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const int off = (256 * dh + 16 * c + 8 * hh) * 2;
+      const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH + off);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(qs + (32 * hq + n) * X_PITCH + off);
+      s = mfma32h<F16>(av, bv, s);
+    }
+    float* sxw = sx + ((sb * 2 + hq) * 64 + lane) * 16;
+    if (dh == 1) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) sxw[q] = s[q];
+    }
+    __syncthreads();
+    if (dh == 0) {
+      float m_loc = kNegInf;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int slot = 32 * sb + 8 * (q >> 2) + 4 * hh + (q & 3);
+        const float x = (s[q] + sxw[q]) * a.scale_log2;
+        s[q] = ((live >> slot) & 1u) ? x : kNegInf;
+        m_loc = fmaxf(m_loc, s[q]);
+      }
+      m_loc = pair32_max(m_loc);
+      if (hh == 0) mx_s[sb * 64 + 32 * hq + n] = m_loc;
+    }
+    __syncthreads();
+    const float m_new = fmaxf(m_run, fmaxf(mx_s[32 * hq + n], mx_s[64 + 32 * hq + n]));
+    const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+    const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+    m_run = m_new;
+    if (dh == 0) {
+      float l = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float pr[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+          pr[t] = fast_exp2(s[8 * kk + t] - m_use);
+          l += pr[t];
+        }
+        ps[(hq * 4 + 2 * sb + kk) * 64 + lane] =
+            u32x4{pack_h2<F16>(pr[0], pr[1]), pack_h2<F16>(pr[2], pr[3]),
+                  pack_h2<F16>(pr[4], pr[5]), pack_h2<F16>(pr[6], pr[7])};
+      }
+      l = pair32_sum(l);
+      if (hh == 0) l_s[sb * 64 + 32 * hq + n] = l;
+    }
+    __syncthreads();
+    l_run = l_run * alpha + l_s[32 * hq + n] + l_s[64 + 32 * hq + n];
+
+    // 3. O^T[d][head] += X^T P^T for d in [128 dq, 128 dq + 128).
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+      o[mb] *= alpha;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const uint8_t* vp = tb + 16 * kk * X_PITCH + 64 * mb;
         const u32x2 lo2 = lds_tr16(vp);
         const u32x2 hi2 = lds_tr16(vp + 8 * X_PITCH);
-        o[mb] = mfma32(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[kk * 64 + lane], o[mb]);
+        o[mb] = mfma32h<F16>(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[(hq * 4 + kk) * 64 + lane], o[mb]);
       }
     }
+    __syncthreads();   // every wave is done with xs, ps and the statistics
   }
-  const float l_tot = l_s[n] + l_s[32 + n];
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const int64_t pi = ((int64_t)r * n_chunks + chunk) * a.N1 + head;
-  float* pp = a.part_o + pi * kSparseD + 128 * wave + 4 * hh;
+
+  // 4. Lane (n, hh) holds O^T[d][head] at d = 128 dq + 32 mb + 8 (q / 4) +
+  // 4 hh + q % 4.
+  if (!head_ok) return;
+  if (a.n_chunks == 1) {
+    float m = m_run, L = l_run, osc = 1.f;
+    bool has = L > 0.f;
+    if (a.sinks != nullptr && qr.live) {
+      // The sink: one more softmax term with a zero value vector.
+      const float z = a.sinks[head] * kLog2e;
+      const float mf = fmaxf(m, z);
+      osc = (m == kNegInf) ? 0.f : fast_exp2(m - mf);
+      L = L * osc + fast_exp2(z - mf);
+      m = mf;
+      has = true;
+    }
+    const float inv = has ? osc / L : 0.f;
+    uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)head * a.o_sh +
+                   128 * dq + 4 * hh;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        st8(op + 32 * mb + 8 * q4,
+            u32x2{pack_h2<F16>(o[mb][4 * q4] * inv, o[mb][4 * q4 + 1] * inv),
+                  pack_h2<F16>(o[mb][4 * q4 + 2] * inv, o[mb][4 * q4 + 3] * inv)});
+      }
+    }
+    if (a.lse != nullptr && dq == 0 && hh == 0) {
+      a.lse[(int64_t)b * a.lse_sb + (int64_t)qr.tq * a.lse_ss + (int64_t)head * a.lse_sh] =
+          has ? (m + fast_log2(L)) * kLn2 : kPosInf;
+    }
+    return;
+  }
+  // Partial of chunk `chunk`: part_o[row][chunk][d][head] (heads innermost,
+  // so each store writes whole runs of 32 heads), part_lse[row][chunk][head].
+  const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+  const int64_t rc = (int64_t)r * a.n_chunks + chunk;
+  float* pp = a.part_o + (rc * kSparseD + 128 * dq + 4 * hh) * a.N1 + head;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      *reinterpret_cast<f32x4*>(pp + 32 * mb + 8 * q4) =
-          f32x4{o[mb][4 * q4] * inv, o[mb][4 * q4 + 1] * inv, o[mb][4 * q4 + 2] * inv,
-                o[mb][4 * q4 + 3] * inv};
-    }
+    for (int q = 0; q < 16; ++q) pp[(int64_t)(32 * mb + 8 * (q >> 2) + (q & 3)) * a.N1] = o[mb][q] * inv;
   }
-  if (wave == 0 && hh == 0) a.part_lse[pi] = l_tot > 0.f ? m_use + fast_log2(l_tot) : kNegInf;
+  if (dq == 0 && hh == 0) a.part_lse[rc * a.N1 + head] = l_run > 0.f ? m_run + fast_log2(l_run) : kNegInf;
 }
 
-// One wave per (row, head): fold the chunks in slot order with the sink logit.
-// Lanes read the chunk log2-sum-exps in parallel; the weighted sum runs over
-// chunks in order.
+// Fold the chunk partials of one query row in chunk order with the sink
+// logit.  Workgroup (row, 32-wide d block, 64-head block): the 64 threads of
+// each wave take consecutive heads (coalesced partial reads), the 4 waves 8 d
+// values each.  Each thread computes its head's chunk weights itself; the
+// first 8 chunks' partials are requested before the log-sum-exps are read,
+// so both arrive in one trip to memory.
+template <bool F16>
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= a.n_rows * a.N1) return;
-  const int r = row / a.N1;   // query row
-  const int h = row - r * a.N1;
+  constexpr int G = 8;   // chunks per group of loads in flight
+  const int tid = threadIdx.x;
+  const int hl = tid & 63;
+  const int r = blockIdx.x;
+  const int d0 = 32 * blockIdx.y + 8 * (tid >> 6);
+  const int h = kSparseHeads * blockIdx.z + hl;
+  if (h >= a.N1) return;
   const SparseRow qr = sparse_row(a, r);
-  const int n_chunks = a.n_slots / kSparseChunk;   // <= 64 (K2 <= 1024)
-  const float sink = a.sinks[h] * kLog2e;
-  const float lc = lane < n_chunks ? a.part_lse[((int64_t)r * n_chunks + lane) * a.N1 + h] : kNegInf;
-  float M = fmaxf(lc, sink);
+  const int nc = a.n_chunks;
+  const int64_t rc0 = (int64_t)r * nc;
+  const float* base = a.part_o + (rc0 * kSparseD + d0) * a.N1 + h;
+  const int64_t cstride = (int64_t)kSparseD * a.N1;
+  float x[G][8];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
+  for (int i = 0; i < G; ++i) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) x[i][u] = i < nc ? base[i * cstride + (int64_t)u * a.N1] : 0.f;
+  }
+  const bool sink_on = a.sinks != nullptr && qr.live;
+  const float sink = sink_on ? a.sinks[h] * kLog2e : kNegInf;
+  const float* lp = a.part_lse + rc0 * a.N1 + h;
+  float M = sink;
+  for (int c = 0; c < nc; ++c) M = fmaxf(M, lp[(int64_t)c * a.N1]);
   const float m_use = (M == kNegInf) ? 0.f : M;
-  const float w = (lc == kNegInf) ? 0.f : fast_exp2(lc - m_use);
-  float L = fast_exp2(sink - m_use);
+  float L = sink_on ? fast_exp2(sink - m_use) : 0.f;
   float acc[8];
 #pragma unroll
   for (int u = 0; u < 8; ++u) acc[u] = 0.f;
-  int c = 0;
-  for (; c + 2 <= n_chunks; c += 2) {
-    const float w0 = __shfl(w, c, 64), w1 = __shfl(w, c + 1, 64);
-    const f32x4* p0 = reinterpret_cast<const f32x4*>(
-        a.part_o + (((int64_t)r * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
-    const f32x4* p1 = reinterpret_cast<const f32x4*>(
-        a.part_o + (((int64_t)r * n_chunks + c + 1) * a.N1 + h) * kSparseD + 8 * lane);
-    const f32x4 x0 = p0[0], x1 = p0[1], y0 = p1[0], y1 = p1[1];
-    L += w0;
-    L += w1;
+  for (int c0 = 0; c0 < nc; c0 += G) {
+    if (c0 > 0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[u] += w0 * x0[u];
-      acc[4 + u] += w0 * x1[u];
+      for (int i = 0; i < G; ++i) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          x[i][u] = c0 + i < nc ? base[(c0 + i) * cstride + (int64_t)u * a.N1] : 0.f;
+        }
+      }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[u] += w1 * y0[u];
-      acc[4 + u] += w1 * y1[u];
-    }
-  }
-  for (; c < n_chunks; ++c) {
-    const float w0 = __shfl(w, c, 64);
-    const f32x4* p0 = reinterpret_cast<const f32x4*>(
-        a.part_o + (((int64_t)r * n_chunks + c) * a.N1 + h) * kSparseD + 8 * lane);
-    const f32x4 x0 = p0[0], x1 = p0[1];
-    L += w0;
+    for (int i = 0; i < G; ++i) {
+      if (c0 + i < nc) {
+        const float lc = lp[(int64_t)(c0 + i) * a.N1];
+        const float wc = (lc == kNegInf) ? 0.f : fast_exp2(lc - m_use);
+        L += wc;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      acc[u] += w0 * x0[u];
-      acc[4 + u] += w0 * x1[u];
+        for (int u = 0; u < 8; ++u) acc[u] += wc * x[i][u];
+      }
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
-  uint16_t* op = a.o + (int64_t)qr.b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)h * a.o_sh + 8 * lane;
-  st16(op, u32x4{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv),
-                 pack_bf16x2(acc[4] * inv, acc[5] * inv), pack_bf16x2(acc[6] * inv, acc[7] * inv)});
+  uint16_t* op = a.o + (int64_t)qr.b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)h * a.o_sh + d0;
+  st16(op, u32x4{pack_h2<F16>(acc[0] * inv, acc[1] * inv), pack_h2<F16>(acc[2] * inv, acc[3] * inv),
+                 pack_h2<F16>(acc[4] * inv, acc[5] * inv), pack_h2<F16>(acc[6] * inv, acc[7] * inv)});
+  if (a.lse != nullptr && blockIdx.y == 0 && tid < 64) {
+    a.lse[(int64_t)qr.b * a.lse_sb + (int64_t)qr.tq * a.lse_ss + (int64_t)h * a.lse_sh] =
+        L > 0.f ? (m_use + fast_log2(L)) * kLn2 : kPosInf;
+  }
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const SparseArgs& a, hipStream_t s) {
+  // Dynamic LDS above the default limit must be enabled for the kernel (on
+  // the current device); the call is cheap, so it is made on every launch.
+  const hipError_t attr = hipFuncSetAttribute(
+      (const void*)sparse_attn<FMT>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+  if (attr != hipSuccess) return attr;
+  const unsigned grid = (unsigned)a.n_rows * a.n_hb * a.n_chunks;
+  sparse_attn<FMT><<<grid, kThreads, LDS_TOTAL, s>>>(a);
+  return hipGetLastError();
 }
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
   if (a.n_rows == 0) return hipSuccess;
-  // Dynamic LDS above the default limit must be enabled for the kernel (on
-  // the current device); the call is cheap, so it is made on every launch.
-  const hipError_t attr = hipFuncSetAttribute(
-      (const void*)sparse_chunk, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
-  if (attr != hipSuccess) return attr;
-  dim3 grid(a.n_slots / kSparseChunk, a.N1 / kSparseHeads, a.n_rows);
-  sparse_chunk<<<grid, 256, LDS_TOTAL, s>>>(a);
-  return hipGetLastError();
+  switch (a.fmt) {
+    case SF_FP8_PACKED: return launch_fmt<SF_FP8_PACKED>(a, s);
+    case SF_BF16: return launch_fmt<SF_BF16>(a, s);
+    case SF_FP16: return launch_fmt<SF_FP16>(a, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
-  const int rows = a.n_rows * a.N1;
-  if (rows > 0) sparse_merge<<<(rows + 3) / 4, 256, 0, s>>>(a);
+  if (a.n_rows == 0 || a.n_chunks <= 1) return hipSuccess;
+  const dim3 grid(a.n_rows, kSparseD / 32, a.n_hb);
+  if (a.fmt == SF_FP16) {
+    sparse_merge<true><<<grid, 256, 0, s>>>(a);
+  } else {
+    sparse_merge<false><<<grid, 256, 0, s>>>(a);
+  }
   return hipGetLastError();
 }
 
-// Test support: slot ids and raw row bytes, through sparse_slot_rows.
-__global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* ids, uint8_t* rows) {
+// Test support: slot ids and raw row bytes, through slot_row with the block
+// tables and index rows read from global memory.
+__global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* ids, uint8_t* rows,
+                                                         int row_bytes) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int64_t total = (int64_t)a.n_rows * a.n_slots;
   if (t >= total) return;
   const int r = (int)(t / a.n_slots);   // query row
   const int s = (int)(t % a.n_slots);
-  int32_t id;
-  const uint8_t* row;
   const SparseRow qr = sparse_row(a, r);
-  sparse_slot_rows<1>(a, qr, &s, sparse_len(a, qr), &row, &id);
+  const SlotCtx ctx = slot_ctx(a, qr, sparse_len(a, qr));
+  const int b = qr.b;
+  auto ori_bt = [&](int col) { return a.ori.bt[(int64_t)b * a.ori.bt_sb + col]; };
+  auto cmp_bt = [&](int col) { return a.cmp.bt[(int64_t)b * a.cmp.bt_sb + col]; };
+  auto idx_at = [&](int k) { return a.idx[(int64_t)b * a.idx_sb + (int64_t)qr.tq * a.idx_ss + k]; };
+  int32_t id;
+  const uint8_t* row = slot_row(a, ctx, s, ori_bt, cmp_bt, idx_at, &id);
   ids[t] = id;
-  uint32_t* dst = reinterpret_cast<uint32_t*>(rows + t * kRowBytes);
-  for (int w = 0; w < kRowBytes / 4; ++w) {
+  uint32_t* dst = reinterpret_cast<uint32_t*>(rows + t * row_bytes);
+  for (int w = 0; w < row_bytes / 4; ++w) {
     dst[w] = row ? reinterpret_cast<const uint32_t*>(row)[w] : 0u;
   }
 }
@@ -440,7 +656,10 @@ __global__ __launch_bounds__(256) void debug_sparse_rows(SparseArgs a, int32_t* 
 hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* rows,
                                     hipStream_t s) {
   const int64_t total = (int64_t)a.n_rows * a.n_slots;
-  if (total > 0) debug_sparse_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a, ids, rows);
+  const int row_bytes = a.fmt == SF_FP8_PACKED ? kRowBytes : 2 * kSparseD;
+  if (total > 0) {
+    debug_sparse_rows<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a, ids, rows, row_bytes);
+  }
   return hipGetLastError();
 }
 

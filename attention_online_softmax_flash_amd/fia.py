@@ -32,7 +32,8 @@ _TORCH_DT = {
 
 KIND_NAMES = {0: "fill", 1: "prefill", 2: "decode", 3: "sparse", 4: "fp32"}
 
-EXPORTED = ["fia_get_workspace_size", "fia_sparse_get_workspace_size", "fia_run",
+EXPORTED = ["fia_get_workspace_size", "fia_sparse_get_workspace_size",
+            "fia_sparse_flash_mla_get_workspace_size", "fia_run",
             "fia_executor_destroy", "fia_last_error", "fia_executor_kind",
             "fia_debug_gather_kv", "fia_debug_sparse_rows", "fia_peak_mfma_bf16",
             "fia_peak_hbm_read"]
@@ -103,6 +104,20 @@ class FiaSparseParams(ctypes.Structure):
     ]
 
 
+class FiaSfmlaParams(ctypes.Structure):
+    _fields_ = [
+        ("softmax_scale", ctypes.c_double),
+        ("cmp_ratio", ctypes.c_int32),
+        ("ori_mask_mode", ctypes.c_int32),
+        ("cmp_mask_mode", ctypes.c_int32),
+        ("ori_win_left", ctypes.c_int32),
+        ("ori_win_right", ctypes.c_int32),
+        ("layout_q", ctypes.c_char_p),
+        ("layout_kv", ctypes.c_char_p),
+        ("return_softmax_lse", ctypes.c_int32),
+    ]
+
+
 _LIB = None
 _TP = ctypes.POINTER(FiaTensor)
 
@@ -123,6 +138,10 @@ def lib():
     L.fia_sparse_get_workspace_size.argtypes = [ctypes.POINTER(FiaSparseParams), _TP, _TP, _TP, _TP,
                                                 _TP, _TP, _TP, _TP, _TP, ctypes.c_int64, _TP, _TP,
                                                 _TP, ctypes.POINTER(sz), ctypes.POINTER(vp)]
+    L.fia_sparse_flash_mla_get_workspace_size.restype = ctypes.c_int
+    L.fia_sparse_flash_mla_get_workspace_size.argtypes = (
+        [ctypes.POINTER(FiaSfmlaParams)] + [_TP] * 12 + [ctypes.c_int64] + [_TP] * 4 +
+        [ctypes.POINTER(sz), ctypes.POINTER(vp)])
     L.fia_run.restype = ctypes.c_int
     L.fia_run.argtypes = [vp, sz, vp, vp]
     L.fia_executor_destroy.restype = None
@@ -361,15 +380,18 @@ class SparsePlan(_Plan):
         self.workspace_size = ws.value
         self._alloc_workspace(q.device)
 
+    row_bytes = 640
+
     def debug_rows(self, stream=None):
-        """(ids [B, S1, n_slots] int32, rows [B, S1, n_slots, 640] uint8) as the
-        kernel gathers them; [T1, n_slots] and [T1, n_slots, 640] with TND."""
+        """(ids [B, S1, n_slots] int32, rows [B, S1, n_slots, row bytes] uint8)
+        as the kernel gathers them; [T1, n_slots] and [T1, n_slots, row bytes]
+        with TND (640 bytes per packed row, 1024 per fp16 / bf16 row)."""
         n = ctypes.c_int32(0)
         _check(lib().fia_debug_sparse_rows(self._exec, None, 0, None, None, ctypes.byref(n), None))
         lead = tuple(self.tensors[0].shape[:-2])
         dev = self.tensors[0].device
         ids = torch.empty(lead + (n.value,), dtype=torch.int32, device=dev)
-        rows = torch.empty(lead + (n.value, 640), dtype=torch.uint8, device=dev)
+        rows = torch.empty(lead + (n.value, self.row_bytes), dtype=torch.uint8, device=dev)
         _check(lib().fia_debug_sparse_rows(self._exec, self.workspace.data_ptr(),
                                            self.workspace.numel(), ids.data_ptr(),
                                            rows.data_ptr(), ctypes.byref(n),
@@ -384,3 +406,66 @@ def kv_quant_sparse_attn_sharedkv(q, ori_kv, cmp_kv, cmp_sparse_indices, ori_blo
                       seqused_kv, sinks, **kw)
     plan.run()
     return plan.out
+
+
+class SparseFlashMlaPlan(SparsePlan):
+    """Phase 1 of sparse_flash_mla (fp16 / bf16 rows) on torch tensors (see
+    fia.h).  Allocates ``attention_out`` and, with ``return_softmax_lse``,
+    ``softmax_lse`` ([B, 1, S1, N1] or [1, T1, N1]) when not given."""
+
+    row_bytes = 1024
+
+    def __init__(self, q, ori_kv, *, seqused_kv, softmax_scale, max_seqused_kv, cmp_kv=None,
+                 cmp_sparse_indices=None, ori_block_table=None, cmp_block_table=None,
+                 cu_seqlens_q=None, cu_seqlens_ori_kv=None, cu_seqlens_cmp_kv=None, sinks=None,
+                 cmp_ratio=1, ori_mask_mode=4, cmp_mask_mode=None, ori_win_left=127,
+                 ori_win_right=0, layout_q="BSND", layout_kv="PA_BBND",
+                 return_softmax_lse=False, ori_sparse_indices=None, seqused_q=None,
+                 attention_out=None, softmax_lse=None):
+        L = lib()
+        if attention_out is None:
+            attention_out = torch.empty_like(q)
+        if return_softmax_lse and softmax_lse is None:
+            if layout_q == "TND":
+                shape = (1, q.shape[0], q.shape[1])
+            else:
+                shape = (q.shape[0], 1, q.shape[1], q.shape[2])
+            softmax_lse = torch.empty(shape, dtype=torch.float32, device=q.device)
+        if cmp_mask_mode is None:
+            cmp_mask_mode = 0 if cmp_kv is None else 3
+        self.tensors = (q, ori_kv, cmp_kv, cmp_sparse_indices, ori_block_table, cmp_block_table,
+                        cu_seqlens_q, cu_seqlens_ori_kv, cu_seqlens_cmp_kv, seqused_kv, sinks,
+                        ori_sparse_indices, seqused_q)
+        self.out, self.lse = attention_out, softmax_lse if return_softmax_lse else None
+        p = FiaSfmlaParams()
+        p.softmax_scale = softmax_scale
+        p.cmp_ratio = cmp_ratio
+        p.ori_mask_mode = ori_mask_mode
+        p.cmp_mask_mode = cmp_mask_mode
+        p.ori_win_left = ori_win_left
+        p.ori_win_right = ori_win_right
+        p.layout_q = layout_q.encode()
+        p.layout_kv = layout_kv.encode()
+        p.return_softmax_lse = 1 if return_softmax_lse else 0
+        self._params = p
+        d = [describe(t) for t in (q, ori_kv, cmp_kv, ori_sparse_indices, cmp_sparse_indices,
+                                   ori_block_table, cmp_block_table, cu_seqlens_q,
+                                   cu_seqlens_ori_kv, cu_seqlens_cmp_kv, seqused_q, seqused_kv)]
+        tail = [describe(sinks), None, describe(attention_out),
+                describe(softmax_lse) if return_softmax_lse else None]
+        self._descs = d + tail
+        ws = ctypes.c_size_t(0)
+        ex = ctypes.c_void_p(None)
+        _check(L.fia_sparse_flash_mla_get_workspace_size(
+            ctypes.byref(p), *[_ptr(x) for x in d], int(max_seqused_kv), *[_ptr(x) for x in tail],
+            ctypes.byref(ws), ctypes.byref(ex)))
+        self._exec = ex
+        self.workspace_size = ws.value
+        self._alloc_workspace(q.device)
+
+
+def sparse_flash_mla(q, ori_kv, **kw):
+    """One-shot call of sparse_flash_mla; returns (attention_out, softmax_lse or None)."""
+    plan = SparseFlashMlaPlan(q, ori_kv, **kw)
+    plan.run()
+    return plan.out, plan.lse

@@ -6,7 +6,7 @@ import numpy as np
 import torch
 
 from . import fia
-from .workloads import DenseCase, SparseCase
+from .workloads import DenseCase, SfmlaCase, SparseCase
 
 
 def to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
@@ -110,6 +110,43 @@ def sparse_plan(case: SparseCase, device="cuda", tensors=None) -> fia.SparsePlan
                           ori_win_left=case.win_left, ori_win_right=case.win_right,
                           layout_q="BSND" if case.cu_seqlens_q is None else "TND",
                           cu_seqlens_q=t["cu_seqlens_q"])
+
+
+def half_to_device(arr: np.ndarray, dtype: str, device) -> torch.Tensor:
+    """fp16 / bf16 bit patterns (uint16) -> torch.float16 / torch.bfloat16."""
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16))
+    return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16).to(device)
+
+
+def sfmla_tensors(case: SfmlaCase, device="cuda"):
+    i32 = lambda x: None if x is None else torch.tensor(list(x), dtype=torch.int32, device=device)
+    arr = lambda x: None if x is None else torch.from_numpy(np.ascontiguousarray(x)).to(device)
+    return dict(
+        q=half_to_device(case.q, case.dtype, device),
+        ori_kv=half_to_device(case.ori_kv, case.dtype, device),
+        cmp_kv=None if case.cmp_kv is None else half_to_device(case.cmp_kv, case.dtype, device),
+        cmp_sparse_indices=arr(case.cmp_sparse_indices),
+        ori_block_table=arr(case.ori_block_table),
+        cmp_block_table=arr(case.cmp_block_table),
+        cu_seqlens_q=i32(case.cu_seqlens_q),
+        cu_seqlens_ori_kv=i32(case.cu_seqlens_ori_kv),
+        cu_seqlens_cmp_kv=i32(case.cu_seqlens_cmp_kv),
+        seqused_kv=i32(case.seqused_kv),
+        sinks=arr(case.sinks),
+    )
+
+
+def sfmla_plan(case: SfmlaCase, device="cuda", tensors=None) -> fia.SparseFlashMlaPlan:
+    t = tensors if tensors is not None else sfmla_tensors(case, device)
+    return fia.SparseFlashMlaPlan(
+        t["q"], t["ori_kv"], seqused_kv=t["seqused_kv"], softmax_scale=case.softmax_scale,
+        max_seqused_kv=max(case.seqused_kv), cmp_kv=t["cmp_kv"],
+        cmp_sparse_indices=t["cmp_sparse_indices"], ori_block_table=t["ori_block_table"],
+        cmp_block_table=t["cmp_block_table"], cu_seqlens_q=t["cu_seqlens_q"],
+        cu_seqlens_ori_kv=t["cu_seqlens_ori_kv"], cu_seqlens_cmp_kv=t["cu_seqlens_cmp_kv"],
+        sinks=t["sinks"], cmp_ratio=case.cmp_ratio, ori_win_left=case.win_left,
+        ori_win_right=case.win_right, layout_q="BSND" if case.cu_seqlens_q is None else "TND",
+        layout_kv=case.kv_layout, return_softmax_lse=case.return_lse)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -287,6 +287,69 @@ fia_status fia_sparse_get_workspace_size(const fia_sparse_params* params,
                                          const fia_tensor* attention_out,
                                          size_t* workspace_size, fia_executor** executor);
 
+/* Attributes of sparse_flash_mla (sparse_flash_mla parameter list: the same
+ * shared-KV sparse attention over unquantised fp16 / bf16 rows). */
+typedef struct {
+  double softmax_scale;
+  /* Mode (sparse_flash_mla function description and SWA / CSA / HCA
+   * constraints):
+   *   1: SWA, sliding window over ori_kv only (no cmp_kv, cmp_mask_mode 0);
+   *   4: CSA, plus the cmp_sparse_indices rows of cmp_kv;
+   *   128: HCA, plus every row of cmp_kv (no indices).
+   * With cmp_kv, cmp_mask_mode must be 3 (right-down causal). */
+  int32_t cmp_ratio;
+  int32_t ori_mask_mode;   /* 4 (band) */
+  int32_t cmp_mask_mode;   /* 3 with cmp_kv, 0 without */
+  int32_t ori_win_left;    /* 127 */
+  int32_t ori_win_right;   /* 0 */
+  const char* layout_q;    /* "BSND" (default) or "TND" */
+  /* "PA_BBND" (default): paged pools [n_blocks, block_size, 1, 512],
+   * block_size 1..1024, through ori_block_table / cmp_block_table; or equal
+   * to layout_q: "BSND" [B, S2, 1, 512] / "TND" [T2, 1, 512] with entry b's
+   * rows starting at cu_seqlens_ori_kv[b] / cu_seqlens_cmp_kv[b]. */
+  const char* layout_kv;
+  int32_t return_softmax_lse;   /* 1: write softmax_lse */
+} fia_sfmla_params;
+
+/* Phase 1 of sparse_flash_mla: the operator of fia_sparse_get_workspace_size
+ * (same row sets, same S1 / TND rules) over unquantised rows.
+ *   q                  fp16 or bf16 [B,S1,N1,512] (BSND, B * S1 <= 65535) or
+ *                      [T1,N1,512] (TND, T1 <= 65535), N1 a power of two in
+ *                      1..128.
+ *   ori_kv, cmp_kv     the dtype of q, rows of 512 values (KV_N = 1) in
+ *                      params->layout_kv; cmp_kv NULL in the SWA mode.
+ *   ori_sparse_indices, seqused_q   must be NULL (reserved on the page).
+ *   cmp_sparse_indices CSA only: int32 [B,S1,1,K2] or [T1,1,K2], K2 >= 1,
+ *                      rows contiguous; entry c of token t is used iff
+ *                      0 <= c and c is visible to t.
+ *   ori_block_table, cmp_block_table   PA_BBND only: int32 [B, >= ceil(max
+ *                      Lk / bs1)] and [B, >= ceil(floor(max Lk / cmp_ratio)
+ *                      / bs2)].
+ *   cu_seqlens_q       TND query only: int32 [B+1] device (as above).
+ *   cu_seqlens_ori_kv, cu_seqlens_cmp_kv   TND KV only: int32 [B+1] device,
+ *                      first packed row of each entry (non-decreasing).
+ *   seqused_kv         int32 [B] device, KV length per batch (Lk).
+ *   max_seqused_kv     host upper bound of seqused_kv.
+ *   sinks              NULL, or fp32 [N1]: one extra logit per head with a
+ *                      zero value vector (the shared-KV reading).
+ *   metadata           ignored, may be NULL.
+ *   attention_out      the dtype and shape of q.
+ *   softmax_lse        with return_softmax_lse: fp32 [B,1,S1,N1] (BSND) or
+ *                      [1,T1,N1] (TND), natural-log LSE of each (token, head)
+ *                      row including the sink; a row with no key row and no
+ *                      sink gives 0 and +inf.  Otherwise ignored.
+ * The window plus the K2 (or compressed) slots must not exceed 8192 per
+ * query token (FIA_ERR_UNSUPPORTED). */
+fia_status fia_sparse_flash_mla_get_workspace_size(
+    const fia_sfmla_params* params, const fia_tensor* q, const fia_tensor* ori_kv,
+    const fia_tensor* cmp_kv, const fia_tensor* ori_sparse_indices,
+    const fia_tensor* cmp_sparse_indices, const fia_tensor* ori_block_table,
+    const fia_tensor* cmp_block_table, const fia_tensor* cu_seqlens_q,
+    const fia_tensor* cu_seqlens_ori_kv, const fia_tensor* cu_seqlens_cmp_kv,
+    const fia_tensor* seqused_q, const fia_tensor* seqused_kv, int64_t max_seqused_kv,
+    const fia_tensor* sinks, const fia_tensor* metadata, const fia_tensor* attention_out,
+    const fia_tensor* softmax_lse, size_t* workspace_size, fia_executor** executor);
+
 /* Phase 2: enqueue the planned work on `stream` (a hipStream_t; NULL is the
  * default stream).  `workspace` is device memory of at least the size phase 1
  * returned (may be NULL when that size is 0); it is scratch and its contents
@@ -306,8 +369,8 @@ void fia_executor_destroy(fia_executor* executor);
 const char* fia_last_error(void);
 
 /* Which kernel path an executor takes: 0 fill-only (empty input),
- * 1 prompt (prefill), 2 incremental decode (split-KV), 3 shared-KV sparse,
- * 4 fp32 reference-precision path. */
+ * 1 prompt (prefill), 2 incremental decode (split-KV), 3 shared-KV sparse
+ * (both sparse operators), 4 fp32 reference-precision path. */
 int32_t fia_executor_kind(const fia_executor* executor);
 
 /* Test support: gather through the same device address function the decode
@@ -332,12 +395,13 @@ fia_status fia_peak_mfma_bf16(int32_t n_workgroups, int32_t iters, float* out, v
 fia_status fia_peak_hbm_read(const void* buf, size_t bytes, int32_t n_workgroups, uint32_t* out,
                              void* stream);
 
-/* Test support for the sparse executor: for every query row (BSND: batch
+/* Test support for the sparse executors: for every query row (BSND: batch
  * entry b, token t; TND: packed token r), the row list the kernel attends
- * to, as fixed slots [B, S1, n_slots] or [T1, n_slots]: ids_out[.., s] = j for window row j of ori_kv, (1 << 30) | c
- * for row c of cmp_kv, -1 for an unused slot; rows_out[.., s, 0..639] =
- * the raw packed bytes of that row (zero when unused).  n_slots is returned through *n_slots_out (ids_out may be NULL to
- * query it). */
+ * to, as fixed slots [B, S1, n_slots] or [T1, n_slots]: ids_out[.., s] = j
+ * for window row j of ori_kv, (1 << 30) | c for row c of cmp_kv, -1 for an
+ * unused slot; rows_out[.., s, :] = the raw bytes of that row (640 per
+ * packed row, 1024 per fp16 / bf16 row; zero when unused).  n_slots is
+ * returned through *n_slots_out (ids_out may be NULL to query it). */
 fia_status fia_debug_sparse_rows(fia_executor* executor, void* workspace, size_t workspace_size,
                                  int32_t* ids_out, uint8_t* rows_out, int32_t* n_slots_out,
                                  void* stream);

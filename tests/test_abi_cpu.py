@@ -579,7 +579,9 @@ def sparse_plan_status(**over):
     (dict(idx=None), BAD),                            # no indices needs ratio 128
     (dict(idx=None, cmp_ratio=128, cmp_mask_mode=4), BAD),
     (dict(idx=None, cmp_ratio=128, max_seq=600000, obt=T((2, 4688), fia.DT_INT32),
-          cbt=T((2, 40), fia.DT_INT32)), UNS),        # too many compressed rows
+          cbt=T((2, 40), fia.DT_INT32)), 0),          # 128 + 4736 slots per token
+    (dict(idx=None, cmp_ratio=128, max_seq=1100000, obt=T((2, 8594), fia.DT_INT32),
+          cbt=T((2, 68), fia.DT_INT32)), UNS),        # more than 8192 slots per token
     (dict(cmp_ratio=2), BAD),
     (dict(idx=T((2, 1, 1, 256), fia.DT_INT32)), BAD),
     (dict(oidx=T((2, 1, 1, 512), fia.DT_INT32)), BAD),
@@ -619,6 +621,112 @@ def sparse_plan_status(**over):
 def test_sparse_phase1(over, expect):
     st, msg = sparse_plan_status(**over)
     assert st == expect, (over, msg)
+
+
+def sfmla_plan_status(**over):
+    """Phase 1 of sparse_flash_mla on fake descriptors (CSA, BSND q, PA_BBND
+    bf16 pools by default)."""
+    B, N1 = 2, 64
+    dt = over.pop("dt", fia.DT_BF16)
+    t = dict(q=T((B, 1, N1, 512), dt), ori=T((32, 128, 1, 512), dt), cmp=T((16, 128, 1, 512), dt),
+             idx=T((B, 1, 1, 512), fia.DT_INT32), obt=T((B, 16), fia.DT_INT32),
+             cbt=T((B, 4), fia.DT_INT32), cuq=None, cuo=None, cuc=None, sq=None,
+             seq=T((B,), fia.DT_INT32), sinks=None, out=T((B, 1, N1, 512), dt),
+             lse=T((B, 1, 1, N1), fia.DT_FP32), oidx=None, max_seq=2048)
+    p = fia.FiaSfmlaParams()
+    p.softmax_scale = 0.0441941738
+    p.cmp_ratio, p.ori_mask_mode, p.cmp_mask_mode, p.ori_win_left, p.ori_win_right = 4, 4, 3, 127, 0
+    p.layout_q, p.layout_kv, p.return_softmax_lse = b"BSND", b"PA_BBND", 1
+    for key, val in over.items():
+        if hasattr(p, key) and key not in t:
+            setattr(p, key, val)
+        else:
+            t[key] = val
+    ws = ctypes.c_size_t(0)
+    ex = ctypes.c_void_p(None)
+    ptr = lambda d: ctypes.pointer(d) if d is not None else None
+    st = fia.lib().fia_sparse_flash_mla_get_workspace_size(
+        ctypes.byref(p), ptr(t["q"]), ptr(t["ori"]), ptr(t["cmp"]), ptr(t["oidx"]), ptr(t["idx"]),
+        ptr(t["obt"]), ptr(t["cbt"]), ptr(t["cuq"]), ptr(t["cuo"]), ptr(t["cuc"]), ptr(t["sq"]),
+        ptr(t["seq"]), t["max_seq"], ptr(t["sinks"]), None, ptr(t["out"]), ptr(t["lse"]),
+        ctypes.byref(ws), ctypes.byref(ex))
+    msg = fia.lib().fia_last_error().decode()
+    if st == 0:
+        assert fia.KIND_NAMES[fia.lib().fia_executor_kind(ex)] == "sparse"
+        fia.lib().fia_executor_destroy(ex)
+    return st, msg, ws.value
+
+
+I32, F32, F16 = fia.DT_INT32, fia.DT_FP32, fia.DT_FP16
+
+
+@pytest.mark.parametrize("over,expect", [
+    ({}, 0),
+    (dict(dt=F16), 0),
+    (dict(sinks=T((64,), F32)), 0),
+    (dict(return_softmax_lse=0, lse=None), 0),
+    (dict(return_softmax_lse=1, lse=None), fia.FIA_ERR_NULLPTR),
+    (dict(lse=T((2, 64, 1, 1), F32)), BAD),                  # [B, N2, S1, N1 / N2]
+    (dict(lse=T((2, 1, 1, 64), fia.DT_BF16)), BAD),
+    (dict(dt=fia.DT_FP32), BAD),                              # fp16 / bf16 only
+    (dict(ori=T((32, 128, 1, 512), F16)), BAD),               # dtypes must agree
+    (dict(out=T((2, 1, 64, 512), F16)), BAD),
+    (dict(ori=T((32, 128, 1, 640), fia.DT_UINT8)), BAD),      # packed rows are the other operator
+    (dict(ori=T((32, 128, 2, 512))), BAD),                    # KV_N must be 1
+    (dict(ori=T((32, 1025, 1, 512))), BAD),                   # block_size 1..1024
+    (dict(ori=T((2048, 1, 1, 512)), obt=T((2, 2048), I32)), 0),   # block_size 1
+    (dict(ori=T((700, 3, 1, 512)), obt=T((2, 683), I32)), 0),     # block_size 3
+    (dict(obt=T((2, 15), I32)), BAD),                         # too few columns
+    (dict(obt=None), BAD),
+    (dict(q=T((2, 1, 48, 512)), out=T((2, 1, 48, 512)), lse=T((2, 1, 1, 48), F32)), BAD),
+    (dict(q=T((2, 1, 1, 512)), out=T((2, 1, 1, 512)), lse=T((2, 1, 1, 1), F32)), 0),
+    (dict(q=T((2, 1, 256, 512)), out=T((2, 1, 256, 512)), lse=T((2, 1, 1, 256), F32)), BAD),
+    (dict(q=T((2, 1, 64, 576)), out=T((2, 1, 64, 576))), BAD),
+    (dict(idx=T((2, 1, 1, 100), I32)), 0),                    # any K2 >= 1
+    (dict(idx=T((2, 1, 1, 8200), I32)), UNS),                 # window + K2 > 8192
+    (dict(cmp_ratio=128), BAD),                               # CSA needs ratio 4
+    (dict(idx=None, cmp_ratio=128), 0),                       # HCA
+    (dict(idx=None), BAD),                                    # HCA needs ratio 128
+    (dict(cmp=None, idx=None, cbt=None, cmp_ratio=1, cmp_mask_mode=0), 0),   # SWA
+    (dict(cmp=None, idx=None, cbt=None, cmp_ratio=1, cmp_mask_mode=3), BAD),
+    (dict(cmp=None, idx=None, cmp_ratio=1, cmp_mask_mode=0), BAD),            # SWA: no cmp table
+    (dict(cmp_mask_mode=4), BAD),
+    (dict(ori_win_left=63), BAD),
+    (dict(ori_mask_mode=3), BAD),
+    (dict(oidx=T((2, 1, 1, 512), I32)), BAD),                 # reserved
+    (dict(sq=T((2,), I32)), BAD),                             # reserved
+    (dict(sinks=T((64,), fia.DT_BF16)), BAD),
+    (dict(sinks=T((32,), F32)), BAD),
+    (dict(layout_kv=b"BSND", ori=T((2, 3000, 1, 512)), cmp=T((2, 700, 1, 512)), obt=None, cbt=None), 0),
+    (dict(layout_kv=b"BSND", ori=T((3, 3000, 1, 512)), cmp=T((2, 700, 1, 512)), obt=None, cbt=None), BAD),
+    (dict(layout_kv=b"BSND", ori=T((2, 3000, 1, 512)), cmp=T((2, 700, 1, 512))), BAD),   # no tables
+    (dict(layout_kv=b"TND"), BAD),                            # TND KV needs TND q
+    (dict(layout_q=b"TND", layout_kv=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)),
+          lse=T((1, 5, 64), F32), idx=T((5, 1, 512), I32), cuq=T((3,), I32),
+          ori=T((4000, 1, 512)), cmp=T((1000, 1, 512)), obt=None, cbt=None,
+          cuo=T((3,), I32), cuc=T((3,), I32)), 0),
+    (dict(layout_q=b"TND", layout_kv=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)),
+          lse=T((1, 5, 64), F32), idx=T((5, 1, 512), I32), cuq=T((3,), I32),
+          ori=T((4000, 1, 512)), cmp=T((1000, 1, 512)), obt=None, cbt=None,
+          cuo=T((3,), I32)), BAD),                            # cu_seqlens_cmp_kv missing
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), lse=T((1, 5, 64), F32),
+          idx=T((5, 1, 512), I32), cuq=T((3,), I32)), 0),     # TND q, PA_BBND KV
+    (dict(layout_q=b"TND", q=T((5, 64, 512)), out=T((5, 64, 512)), lse=T((2, 1, 5, 64), F32),
+          idx=T((5, 1, 512), I32), cuq=T((3,), I32)), BAD),   # LSE [1, T1, N1] with TND
+    (dict(cuo=T((3,), I32)), BAD),                            # cu_seqlens_ori_kv only with TND KV
+])
+def test_sfmla_phase1(over, expect):
+    st, msg, _ = sfmla_plan_status(**over)
+    assert st == expect, (over, msg)
+
+
+def test_sfmla_workspace():
+    """Partials only when a query row spans several chunks of 128 slots: the
+    window alone (SWA) needs no workspace, CSA with K2 = 512 does."""
+    st, msg, ws = sfmla_plan_status(cmp=None, idx=None, cbt=None, cmp_ratio=1, cmp_mask_mode=0)
+    assert st == 0 and ws == 0, msg
+    st, msg, ws = sfmla_plan_status()
+    assert st == 0 and ws >= 2 * 64 * 5 * 512 * 4, msg
 
 
 def test_device_kv_lengths_phase1():
