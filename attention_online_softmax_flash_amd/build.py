@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libfia.so")
 SOURCES = ["fia_api.cpp", "prefill.hip", "decode.hip", "decode_q8.hip", "sparse.hip", "misc.hip",
-           "peaks.hip"]
+           "peaks.hip", "noalloc.hip"]
 ARCH = "gfx950"
 
 

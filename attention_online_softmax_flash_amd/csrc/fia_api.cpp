@@ -1530,14 +1530,10 @@ fia_status fia_sparse_flash_mla_get_workspace_size(
   return sparse_finish(e, K2, workspace_size, executor);
 }
 
-fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void* stream) {
-  if (e == nullptr) return fail(FIA_ERR_NULLPTR, "executor is NULL");
-  if (e->noop) return FIA_SUCCESS;
-  fia_status st = check_ws(e, workspace, workspace_size);
-  if (st != FIA_SUCCESS) return st;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  if ((st = upload_plan(e)) != FIA_SUCCESS) return st;
-  bind_workspace(e, workspace);
+namespace {
+
+// Enqueue the kernels of a bound executor (plan and workspace pointers set).
+fia_status launch_all(fia_executor* e, void* workspace, hipStream_t s) {
   hipError_t err = hipSuccess;
   switch (e->kind) {
     case KIND_FILL: err = fia::launch_fill_empty(e->a, s); break;
@@ -1563,6 +1559,20 @@ fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void
   if (err != hipSuccess) return fail(FIA_ERR_HIP, std::string("kernel launch failed: ") + hipGetErrorString(err));
   return FIA_SUCCESS;
 }
+
+}  // namespace
+
+fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* e, void* stream) {
+  if (e == nullptr) return fail(FIA_ERR_NULLPTR, "executor is NULL");
+  if (e->noop) return FIA_SUCCESS;
+  fia_status st = check_ws(e, workspace, workspace_size);
+  if (st != FIA_SUCCESS) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if ((st = upload_plan(e)) != FIA_SUCCESS) return st;
+  bind_workspace(e, workspace);
+  return launch_all(e, workspace, s);
+}
+
 
 fia_status fia_debug_gather_kv(fia_executor* e, void* workspace, size_t workspace_size,
                                int32_t which, void* dst, void* stream) {
@@ -1599,3 +1609,42 @@ fia_status fia_debug_sparse_rows(fia_executor* e, void* workspace, size_t worksp
 }
 
 }  // extern "C"
+
+namespace fia {
+
+void set_last_error(const char* msg) { g_last_error = msg; }
+
+// fia_run with the plan and the workspace in caller-given device scratch:
+// the plan (per-batch records and work list) is copied to `plan` on the
+// stream, the workspace is `ws`.  Nothing is allocated.
+fia_status run_on_scratch(fia_executor* e, void* plan, size_t plan_cap, void* ws, size_t ws_cap,
+                          void* stream) {
+  if (e == nullptr) return fail(FIA_ERR_NULLPTR, "executor is NULL");
+  if (e->noop) return FIA_SUCCESS;
+  if (e->meta_bytes > plan_cap) {
+    return fail(FIA_ERR_UNSUPPORTED, "the executor's plan (" + std::to_string(e->meta_bytes) +
+                                         " bytes) exceeds the no-allocation plan area of " +
+                                         std::to_string(plan_cap) + " bytes");
+  }
+  if (e->ws_size > ws_cap) {
+    return fail(FIA_ERR_UNSUPPORTED, "the executor's workspace (" + std::to_string(e->ws_size) +
+                                         " bytes) exceeds the no-allocation scratch of " +
+                                         std::to_string(ws_cap) + " bytes");
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (e->meta_bytes > 0) {
+    if (hipMemcpyAsync(plan, e->meta.data(), e->meta_bytes, hipMemcpyHostToDevice, s) != hipSuccess) {
+      return fail(FIA_ERR_HIP, "copy of the plan into the scratch failed");
+    }
+  }
+  bind_workspace(e, ws);
+  if (!e->dev_len) {
+    e->a.meta = static_cast<const int32_t*>(plan);
+    e->a.work = static_cast<const int32_t*>(plan) + e->work_off;
+  }
+  const fia_status st = launch_all(e, ws, s);
+  // Later fia_run calls bind their own plan copy again.
+  return st;
+}
+
+}  // namespace fia

@@ -33,7 +33,7 @@ _TORCH_DT = {
 KIND_NAMES = {0: "fill", 1: "prefill", 2: "decode", 3: "sparse", 4: "fp32"}
 
 EXPORTED = ["fia_get_workspace_size", "fia_sparse_get_workspace_size",
-            "fia_sparse_flash_mla_get_workspace_size", "fia_run",
+            "fia_sparse_flash_mla_get_workspace_size", "fia_run", "fia_run_no_alloc",
             "fia_executor_destroy", "fia_last_error", "fia_executor_kind",
             "fia_debug_gather_kv", "fia_debug_sparse_rows", "fia_peak_mfma_bf16",
             "fia_peak_hbm_read"]
@@ -144,6 +144,8 @@ def lib():
         [ctypes.POINTER(sz), ctypes.POINTER(vp)])
     L.fia_run.restype = ctypes.c_int
     L.fia_run.argtypes = [vp, sz, vp, vp]
+    L.fia_run_no_alloc.restype = ctypes.c_int
+    L.fia_run_no_alloc.argtypes = [vp, vp]
     L.fia_executor_destroy.restype = None
     L.fia_executor_destroy.argtypes = [vp]
     L.fia_last_error.restype = ctypes.c_char_p
@@ -217,6 +219,12 @@ class _Plan:
         """Enqueue the planned attention on ``stream`` (default: current)."""
         _check(lib().fia_run(self.workspace.data_ptr(), self.workspace.numel(), self._exec,
                              _stream_handle(stream)))
+        return self
+
+    def run_no_alloc(self, stream=None):
+        """Enqueue the planned attention without the plan's own workspace:
+        fia_run_no_alloc, on the library's static device scratch."""
+        _check(lib().fia_run_no_alloc(self._exec, _stream_handle(stream)))
         return self
 
     def close(self):
@@ -353,6 +361,7 @@ class SparsePlan(_Plan):
         self.tensors = (q, ori_kv, cmp_kv, cmp_sparse_indices, ori_block_table, cmp_block_table,
                         seqused_kv, sinks, ori_sparse_indices, cu_seqlens_q)
         self.out = attention_out
+        self.lse = None   # reserved on the page: not produced
         p = FiaSparseParams()
         p.softmax_scale = softmax_scale
         p.kv_quant_mode = kv_quant_mode

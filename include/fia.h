@@ -362,6 +362,25 @@ fia_status fia_sparse_flash_mla_get_workspace_size(
 fia_status fia_run(void* workspace, size_t workspace_size, fia_executor* executor,
                    void* stream);
 
+/* Phase 2 for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ * Runs `executor` exactly as fia_run does (same kernels, bitwise-identical
+ * results), but takes no workspace: the executor's plan (copied there on
+ * `stream` with hipMemcpyAsync) and its workspace live in a static device
+ * array of 64 MiB that the library holds on every GPU it runs on until the
+ * process ends (1 MiB for the plan, 63 MiB for the workspace).  Allocates
+ * nothing (no hipMalloc / hipFree, no allocating library call).
+ *   - FIA_ERR_UNSUPPORTED when the executor's plan exceeds 1 MiB or the
+ *     workspace size phase 1 returned exceeds 63 MiB (fia_last_error()
+ *     names the sizes); fia_run has no such limit.
+ *   - Every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents; calls that overlap on one GPU (other streams, other
+ *     threads) race and must be serialised by the caller.
+ *   - The first call on a device looks up the array's device address
+ *     (hipGetSymbolAddress, with that device current); FIA_ERR_HIP if that
+ *     fails. */
+fia_status fia_run_no_alloc(fia_executor* executor, void* stream);
+
 /* Release an executor (NULL is ignored). */
 void fia_executor_destroy(fia_executor* executor);
 
