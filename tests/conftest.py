@@ -8,6 +8,14 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 
+# A host-only build of the planner (the sanitizer test builds one) can stand
+# in for libfia.so: FIA_HOSTCHECK_LIB names it.
+if os.environ.get("FIA_HOSTCHECK_LIB"):
+    from attention_online_softmax_flash_amd import fia as _fia
+
+    _fia.LIB_PATH = os.environ["FIA_HOSTCHECK_LIB"]
+
+
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
 
