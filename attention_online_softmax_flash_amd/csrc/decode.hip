@@ -92,6 +92,7 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
 
   if (t_hi > t_lo) {
     const int first = ws + ((t_lo - ws) & ~31);
+    const WavePages wp = wave_pages(a, b, first, hi - 1, lane);
     for (int ts = first; ts < t_hi; ts += kDecodeStep) {
       // The two 16-key halves each lie inside one page (block sizes are
       // multiples of 16 and halves are 16-aligned): one bounds-checked
@@ -105,8 +106,8 @@ __global__ __launch_bounds__(256, 4) void decode_split_bf16(AttnArgs a) {
         int64_t ko = 0, vo = 0;
         uint32_t kbytes = 0, vbytes = 0;
         if (nv > 0) {
-          ko = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
-          vo = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
+          ko = kv_row_offset_w(a, wp, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
+          vo = kv_row_offset_w(a, wp, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
           kbytes = (uint32_t)((nv - 1) * a.k_ss + D) * 2u;
           vbytes = (uint32_t)((nv - 1) * a.v_ss + D) * 2u;
         }

@@ -96,7 +96,7 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 
 // KPT / VPT: key / value scales per token (else per channel).
 template <int D, bool FP8, bool KPT, bool VPT>
-__global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(AttnArgs a) {
+__global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split_q8(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide k-steps of the score product per 16-key half
   constexpr int DPL = D / 16;  // value columns per lane column
   constexpr int KB = D / 4;    // key bytes per lane and row
@@ -225,166 +225,240 @@ __global__ __launch_bounds__(256, (KPT || VPT) ? 3 : 4) void decode_split_q8(Att
   const float* vsp = VPT ? (const float*)a.vq_scale + (int64_t)b * a.vq_sb : nullptr;
   const float* vop = VPT && a.vq_off ? (const float*)a.vq_off + (int64_t)b * a.vq_sb : nullptr;
 
+  // Per-wave staging inside the combine buffer (used after the loop): one
+  // iteration's 64 key rows (row-major, 16-byte pieces XOR-swizzled so that
+  // the 16 rows one operand read touches fall in distinct bank groups) and
+  // its per-token tables (64 keys each).  All loads of an iteration -- keys,
+  // values and tables of two 32-key steps -- go out before its first wait.
+  constexpr int PR = D / 16;                 // 16-byte pieces per key row
+  constexpr int RPI = 64 / PR;               // rows per 64-lane buffer-to-LDS load
+  constexpr int STAGE = 64 * D + 1024;       // bytes of one wave's stage
+  constexpr int COMBINE = 4 * 16 * (D + 4) * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t sm_raw[COMBINE > 4 * STAGE ? COMBINE : 4 * STAGE];
+  float(*sm_o)[16][D + 4] = reinterpret_cast<float(*)[16][D + 4]>(sm_raw);
+  uint8_t* kst = sm_raw + wave * STAGE;
+  float* tst = reinterpret_cast<float*>(kst + 64 * D);   // [4 tables][64 keys]
+  // Lane l of buffer-to-LDS load `inst` fills slot l % PR of row
+  // RPI inst + l / PR of a 32-key step, fetching the global piece that
+  // belongs in that slot.
+  uint32_t k_lds_off[PR / 2];
+#pragma unroll
+  for (int inst = 0; inst < PR / 2; ++inst) {
+    const int r = RPI * inst + lane / PR;
+    k_lds_off[inst] = (uint32_t)((r % 16) * a.k_ss + 16 * ((lane % PR) ^ key_swz<PR>(r)));
+  }
+  // Score operand reads: lane (n, g) reads piece (KB / 16) g + c4 of row
+  // 16 hf + n of a step.
+  uint32_t k_rd[2][KB / 16];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+    for (int c4 = 0; c4 < KB / 16; ++c4) {
+      const int r = 16 * hf + n;
+      k_rd[hf][c4] = (uint32_t)(r * D + 16 * (((KB / 16) * g + c4) ^ key_swz<PR>(r)));
+    }
+  }
+  // Per-token table rows of the batch (no table: empty range, reads zero).
+  const __amdgpu_buffer_rsrc_t r_ks = make_rsrc(ksp, ksp ? (uint32_t)a.kq_cols * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t r_ko = make_rsrc(kop, kop ? (uint32_t)a.kq_cols * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t r_vs = make_rsrc(vsp, vsp ? (uint32_t)a.vq_cols * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t r_vo = make_rsrc(vop, vop ? (uint32_t)a.vq_cols * 4u : 0u);
+  auto lds_ptr = [](void* p) FIA_INLINE { return (__attribute__((address_space(3))) void*)p; };
+
   if (t_hi > t_lo) {
     const int first = ws + ((t_lo - ws) & ~31);
-    for (int ts = first; ts < t_hi; ts += kDecodeStep) {
-      // The two 16-key halves each lie inside one page (block sizes are
+    const WavePages wp = wave_pages(a, b, first, hi - 1, lane);
+    for (int ti = first; ti < t_hi; ti += 2 * kDecodeStep) {
+      // The four 16-key quarters each lie inside one page (block sizes are
       // multiples of 32); rows at or past `hi` read as zero.
-      __amdgpu_buffer_rsrc_t rk[2], rv[2];
+      __amdgpu_buffer_rsrc_t rk[4], rv[4];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int jb = ts + 16 * hf;
+      for (int qq = 0; qq < 4; ++qq) {
+        const int jb = ti + 16 * qq;
         const int nv = min(16, hi - jb);
         int64_t ko = 0, vo = 0;
         uint32_t kbytes = 0, vbytes = 0;
         if (nv > 0) {
-          ko = kv_row_offset(a, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
-          vo = kv_row_offset(a, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
+          ko = kv_row_offset_w(a, wp, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
+          vo = kv_row_offset_w(a, wp, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
           kbytes = (uint32_t)((nv - 1) * a.k_ss + D);
           vbytes = (uint32_t)((nv - 1) * a.v_ss + D);
         }
-        rk[hf] = make_rsrc(kbase + ko, kbytes);
-        rv[hf] = make_rsrc(vbase + vo, vbytes);
+        rk[qq] = make_rsrc(kbase + ko, kbytes);
+        rv[qq] = make_rsrc(vbase + vo, vbytes);
       }
-      // Key codes: row 16 hf + n, bytes KB g .. KB g + KB - 1.
-      u32x4 kw[2][KB / 16];
+      // Key codes of both steps, whole rows, into this wave's stage (the
+      // previous iteration's reads of it were consumed by its products).
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
-        for (int i = 0; i < KB / 16; ++i) {
-          kw[hf][i] = buf_ld16_nt(rk[hf], (uint32_t)(n * a.k_ss + KB * g + 16 * i));
+        for (int inst = 0; inst < PR / 2; ++inst) {
+          buf_ld16_lds_nt(rk[2 * sub + (RPI * inst) / 16], kst + 32 * D * sub + 1024 * inst,
+                          k_lds_off[inst]);
         }
       }
-      // Value codes for k-slot s: key 16 (s / 4) + 4 g + s % 4, columns DPL n ..
-      uint32_t vr[8][DPL / 4];
+      // Value codes for step sub, k-slot s: key 32 sub + 16 (s / 4) + 4 g +
+      // s % 4, columns DPL n ..
+      uint32_t vr[2][8][DPL / 4];
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int hf = s >> 2;
-        const int t = 4 * g + (s & 3);
-        const uint32_t off = (uint32_t)(t * a.v_ss + DPL * n);
-        if constexpr (DPL == 8) {
-          const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[hf], off, 0, 2));
-          vr[s][0] = w.x;
-          vr[s][1] = w.y;
-        } else {
-          vr[s][0] = __builtin_amdgcn_raw_buffer_load_b32(rv[hf], off, 0, 2);
-        }
-      }
-      // Per-token scales / offsets of the lane's keys ts + 16 hf + 4 g + r
-      // (4-aligned groups; a group past the tensor's width lies past every
-      // visible key, so its index is clamped).
-      f32x4 ks[2], kq[2], vs[2], vq[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int j4 = ts + 16 * hf + 4 * g;
-        ks[hf] = kq[hf] = vs[hf] = vq[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if constexpr (KPT) {
-          const int jk = min(j4, a.kq_cols - 4);
-          ks[hf] = *reinterpret_cast<const f32x4*>(ksp + jk);
-          if (kop != nullptr) kq[hf] = *reinterpret_cast<const f32x4*>(kop + jk);
-        }
-        if constexpr (VPT) {
-          const int jv = min(j4, a.vq_cols - 4);
-          vs[hf] = *reinterpret_cast<const f32x4*>(vsp + jv);
-          if (vop != nullptr) vq[hf] = *reinterpret_cast<const f32x4*>(vop + jv);
-        }
-      }
-
-      // Scores S^T[key 16 hf + 4 g + r][head n].
-      f32x4 sc[2];
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        if constexpr (FP8) {
-          sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int cc = 0; cc < NC; ++cc) {
-            // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
-            const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
-            const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
-            const u32x4 kop8 = codes8_bf16<true>(w0, w1);
-            sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
-            if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
-          }
-        } else {
-          // 16 key bytes per lane and product: the loaded pieces as they are.
-          i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
-#pragma unroll
-          for (int c4 = 0; c4 < KB / 16; ++c4) {
-            const i32x4 kc = __builtin_bit_cast(i32x4, kw[hf][c4]);
-            ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qi[c4]), ah, 0, 0, 0);
-            al = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qj[c4]), al, 0, 0, 0);
-          }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) sc[hf][r] = sq * __builtin_fmaf((float)al[r], 1.f / 256.f, (float)ah[r]);
-        }
-      }
-      float x[8];
-      float mx = kNegInf;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        const int hf = s >> 2, r = s & 3;
-        const int j = ts + 16 * hf + 4 * g + r;
-        const bool ok = j >= t_lo && j < t_hi;
-        float v;
-        if constexpr (KPT) {
-          v = ks[hf][r] * __builtin_fmaf(kq[hf][r], qc, sc[hf][r]) * a.scale_log2;
-        } else {
-          v = __builtin_fmaf(sc[hf][r], a.scale_log2, c_shift);
-        }
-        x[s] = ok ? v : kNegInf;
-        mx = fmaxf(mx, x[s]);
-      }
-      mx = pair32_max(pair16_max(mx));
-      // Lazy rescale: the running max moves only when a head's new max
-      // exceeds it by more than 8 (probabilities stay <= 2^8).
-      const bool grow = mx > m_run + 8.f;
-      if (__any(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_run *= alpha;
-        t_run *= alpha;
-#pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] *= alpha;
-      }
-      const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-      float p[8];
-      float psum = 0.f, tsum = 0.f;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        p[s] = fast_exp2(x[s] - m_use);
-        psum += p[s];
-      }
-      if constexpr (VPT) {
+      for (int sub = 0; sub < 2; ++sub) {
 #pragma unroll
         for (int s = 0; s < 8; ++s) {
-          const float pv = p[s] * vs[s >> 2][s & 3];
-          tsum = __builtin_fmaf(pv, vq[s >> 2][s & 3], tsum);
-          p[s] = pv;
+          const int qq = 2 * sub + (s >> 2);
+          const int t = 4 * g + (s & 3);
+          const uint32_t off = (uint32_t)(t * a.v_ss + DPL * n);
+          if constexpr (DPL == 8) {
+            const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[qq], off, 0, 2));
+            vr[sub][s][0] = w.x;
+            vr[sub][s][1] = w.y;
+          } else {
+            vr[sub][s][0] = __builtin_amdgcn_raw_buffer_load_b32(rv[qq], off, 0, 2);
+          }
         }
       }
-      l_run += psum;
-      t_run += tsum;
-      const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
-                        pack_bf16x2(p[6], p[7])};
+      // Per-token scales / offsets of keys ti .. ti + 63: one 4-byte load per
+      // key and table straight into the stage; keys past a table's width
+      // read as zero (they lie past every visible key).
+      if constexpr (KPT || VPT) {
+        const uint32_t toff = (uint32_t)(ti + lane) * 4u;
+        if constexpr (KPT) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ks, lds_ptr(tst), 4, toff, 0, 0, 0);
+          if (kop != nullptr) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_ko, lds_ptr(tst + 64), 4, toff, 0, 0, 0);
+        }
+        if constexpr (VPT) {
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(r_vs, lds_ptr(tst + 128), 4, toff, 0, 0, 0);
+          if (vop != nullptr) __builtin_amdgcn_raw_ptr_buffer_load_lds(r_vo, lds_ptr(tst + 192), 4, toff, 0, 0, 0);
+        }
+      }
+      // The stage is complete once this wave's loads have landed (only this
+      // wave reads its stage).
+      __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
+
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) {
-        // byte e of the lane's DPL value bytes of each of the 8 keys
-        const int w = e >> 2, k = e & 3;
-        const u32x4 av = {pair_bf16<FP8>(vr[0][w], vr[1][w], k), pair_bf16<FP8>(vr[2][w], vr[3][w], k),
-                          pair_bf16<FP8>(vr[4][w], vr[5][w], k), pair_bf16<FP8>(vr[6][w], vr[7][w], k)};
-        o[e] = mfma16(av, pb, o[e]);
+      for (int sub = 0; sub < 2; ++sub) {
+        const int ts = ti + 32 * sub;
+        if (ts >= t_hi) break;
+        const uint8_t* ks_rows = kst + 32 * D * sub;
+        u32x4 kw[2][KB / 16];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+          for (int c4 = 0; c4 < KB / 16; ++c4) kw[hf][c4] = *reinterpret_cast<const u32x4*>(ks_rows + k_rd[hf][c4]);
+        }
+        // Tables of the lane's keys 16 hf + 4 g + r of this step.
+        f32x4 ks[2], kq[2], vs[2], vq[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int j4 = 32 * sub + 16 * hf + 4 * g;
+          ks[hf] = kq[hf] = vs[hf] = vq[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if constexpr (KPT) {
+            ks[hf] = *reinterpret_cast<const f32x4*>(tst + j4);
+            if (kop != nullptr) kq[hf] = *reinterpret_cast<const f32x4*>(tst + 64 + j4);
+          }
+          if constexpr (VPT) {
+            vs[hf] = *reinterpret_cast<const f32x4*>(tst + 128 + j4);
+            if (vop != nullptr) vq[hf] = *reinterpret_cast<const f32x4*>(tst + 192 + j4);
+          }
+        }
+
+        // Scores S^T[key 16 hf + 4 g + r][head n].
+        f32x4 sc[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          if constexpr (FP8) {
+            sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc) {
+              // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
+              const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
+              const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
+              const u32x4 kop8 = codes8_bf16<true>(w0, w1);
+              sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
+              if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
+            }
+          } else {
+            // 16 key bytes per lane and product: the loaded pieces as they are.
+            i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
+#pragma unroll
+            for (int c4 = 0; c4 < KB / 16; ++c4) {
+              const i32x4 kc = __builtin_bit_cast(i32x4, kw[hf][c4]);
+              ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qi[c4]), ah, 0, 0, 0);
+              al = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qj[c4]), al, 0, 0, 0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[hf][r] = sq * __builtin_fmaf((float)al[r], 1.f / 256.f, (float)ah[r]);
+          }
+        }
+        float x[8];
+        float mx = kNegInf;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          const int hf = s >> 2, r = s & 3;
+          const int j = ts + 16 * hf + 4 * g + r;
+          const bool ok = j >= t_lo && j < t_hi;
+          float v;
+          if constexpr (KPT) {
+            v = ks[hf][r] * __builtin_fmaf(kq[hf][r], qc, sc[hf][r]) * a.scale_log2;
+          } else {
+            v = __builtin_fmaf(sc[hf][r], a.scale_log2, c_shift);
+          }
+          x[s] = ok ? v : kNegInf;
+          mx = fmaxf(mx, x[s]);
+        }
+        mx = pair32_max(pair16_max(mx));
+        // Lazy rescale: the running max moves only when a head's new max
+        // exceeds it by more than 8 (probabilities stay <= 2^8).
+        const bool grow = mx > m_run + 8.f;
+        if (__any(grow)) {
+          const float m_new = grow ? mx : m_run;
+          const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
+          m_run = m_new;
+          l_run *= alpha;
+          t_run *= alpha;
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+        }
+        const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+        float p[8];
+        float psum = 0.f, tsum = 0.f;
+#pragma unroll
+        for (int s = 0; s < 8; ++s) {
+          p[s] = fast_exp2(x[s] - m_use);
+          psum += p[s];
+        }
+        if constexpr (VPT) {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const float pv = p[s] * vs[s >> 2][s & 3];
+            tsum = __builtin_fmaf(pv, vq[s >> 2][s & 3], tsum);
+            p[s] = pv;
+          }
+        }
+        l_run += psum;
+        t_run += tsum;
+        const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
+                          pack_bf16x2(p[6], p[7])};
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) {
+          // byte e of the lane's DPL value bytes of each of the 8 keys
+          const int w = e >> 2, k = e & 3;
+          const uint32_t(&v8)[8][DPL / 4] = vr[sub];
+          const u32x4 av = {pair_bf16<FP8>(v8[0][w], v8[1][w], k), pair_bf16<FP8>(v8[2][w], v8[3][w], k),
+                            pair_bf16<FP8>(v8[4][w], v8[5][w], k), pair_bf16<FP8>(v8[6][w], v8[7][w], k)};
+          o[e] = mfma16(av, pb, o[e]);
+        }
       }
     }
   }
   l_run = pair32_sum(pair16_sum(l_run));
   t_run = pair32_sum(pair16_sum(t_run));
 
-  // Combine the four waves through LDS in wave order.
+  // Combine the four waves through LDS in wave order (every wave is done
+  // with its stage first).
   __shared__ float sm_m[4][16];
   __shared__ float sm_l[4][16];
   __shared__ float sm_t[4][16];
-  __shared__ __attribute__((aligned(16))) float sm_o[4][16][D + 4];
+  __syncthreads();
   if (g == 0) {
     sm_m[wave][n] = m_run;
     sm_l[wave][n] = l_run;

@@ -114,6 +114,42 @@ __device__ __forceinline__ int64_t kv_row_offset(const AttnArgs& a, int64_t sb, 
   return (int64_t)b * sb + (int64_t)(kv_off + j) * ss + (int64_t)g * sh;
 }
 
+// Paged key / value, decode: the block ids of the pages a wave reads, looked
+// up once before its key loop.  Lane l holds the block id of page p0 + l
+// (p0 = page of key j0), the column clamped to the page of key jmax (the
+// batch's last visible key) and the id into [0, n_blocks).  The wave's keys
+// must span fewer than 64 pages.  Zero when not paged.
+struct WavePages {
+  int btv;
+  int p0;
+};
+
+__device__ __forceinline__ WavePages wave_pages(const AttnArgs& a, int b, int j0, int jmax, int lane) {
+  WavePages w{0, 0};
+  if (a.paged) {
+    w.p0 = (int)fast_div((uint32_t)j0, a.bs_div);
+    const int pmax = (int)fast_div((uint32_t)jmax, a.bs_div);
+    const int col = min(w.p0 + lane, pmax);
+    const int blk = a.block_table[(int64_t)b * a.bt_sb + col];
+    w.btv = blk < 0 ? 0 : (blk >= a.n_blocks ? a.n_blocks - 1 : blk);
+  }
+  return w;
+}
+
+// kv_row_offset with the page's block id taken from the wave's WavePages
+// (no memory access): j must lie in pages p0 .. p0 + 63, at most jmax.
+__device__ __forceinline__ int64_t kv_row_offset_w(const AttnArgs& a, const WavePages& w, int64_t sb,
+                                                   int64_t ss, int64_t sh, int b, int j, int g,
+                                                   int kv_off) {
+  if (a.paged) {
+    const uint32_t page = fast_div((uint32_t)j, a.bs_div);
+    const int slot = j - (int)page * a.block_size;
+    const int blk = __builtin_amdgcn_readlane(w.btv, (int)page - w.p0);
+    return (int64_t)blk * sb + (int64_t)slot * ss + (int64_t)g * sh;
+  }
+  return (int64_t)b * sb + (int64_t)(kv_off + j) * ss + (int64_t)g * sh;
+}
+
 // Same, for a run of rows known to share one page (paged) -- the block id is
 // looked up once by the caller.
 __device__ __forceinline__ int64_t paged_row_offset(int blk, int slot, int g, int64_t sb,
