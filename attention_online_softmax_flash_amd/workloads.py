@@ -733,3 +733,64 @@ def sfmla_decode_bf16(seed=SEEDS["c5"] + 100) -> SfmlaCase:
     PA_BBND pools of block 128, fp32 sinks, LSE."""
     return sfmla_case("sfmla_csa_decode_bf16", seed, B=16, N1=64, seqused_kv=[16384] * 16,
                       K2=512, window_only_ori=True)
+
+
+# ---------------------------------------------------------------------------
+# The timed variants of the workloads above (each with its own seed), shared
+# by the benchmark and the full-size parity tests.
+# ---------------------------------------------------------------------------
+SEEDS_SPARSE_MODES = 1006
+
+
+def mask_prefill() -> DenseCase:
+    """Causal GQA prefill shapes with an explicit uint8 mask [4, 2048, 2048],
+    Bernoulli(0.1) masked, mode 0."""
+    return with_random_mask(c2_causal_gqa(), 41, p_masked=0.1, mode=0)
+
+
+def bias_prefill() -> DenseCase:
+    """Causal GQA prefill with a bf16 pse_shift bias [1, 32, 2048, 2048]."""
+    return with_random_bias(c2_causal_gqa(), 42, per_batch=False)
+
+
+def sink_prefill() -> DenseCase:
+    """Causal GQA prefill with a bf16 learnable sink [32]."""
+    return with_random_sink(c2_causal_gqa(), 43)
+
+
+Q8_DECODES = {
+    # name: (code kind, table mode (0 per channel, 1 per token), offsets, BnNBsD pools)
+    "q8_int8": ("int8", 1, True, False),
+    "q8_fp8": ("fp8", 0, False, False),
+    "q8_int8_bnnbsd": ("int8", 1, True, True),
+}
+
+
+def q8_decode(name) -> DenseCase:
+    """The paged GQA decode with a fake-quantised KV cache (Q8_DECODES)."""
+    kind, mode, off, bn = Q8_DECODES[name]
+    case = with_kv_quant(c3_paged_decode(), 1007, kind=kind, kmode=mode, vmode=mode, offsets=off)
+    return as_bnnbsd(case) if bn else case
+
+
+def sparse_hca_decode() -> SparseCase:
+    """Shared-KV sparse decode, heavily compressed: B=16, N1=64, KV length
+    16384, window 128 + every row of the ratio-128 compressed KV."""
+    return sparse_case("hca", SEEDS_SPARSE_MODES, B=16, N1=64, seqused_kv=[16384] * 16,
+                       materialise_all_ori=False, heavily_compressed=True)
+
+
+def sparse_two_tokens() -> SparseCase:
+    """Shared-KV sparse attention with 2 query tokens per batch entry."""
+    return sparse_case("s1_2", SEEDS_SPARSE_MODES + 1, B=16, N1=64, seqused_kv=[16384] * 16, K2=512,
+                       S1=2, materialise_all_ori=False)
+
+
+def sparse_tnd_counts():
+    return [int(x) for x in rng_for(SEEDS_SPARSE_MODES + 2).integers(1, 5, size=16)]
+
+
+def sparse_tnd_ragged() -> SparseCase:
+    """Shared-KV sparse attention, TND queries with 1-4 tokens per entry."""
+    return sparse_tnd_case("tnd", SEEDS_SPARSE_MODES + 3, q_counts=sparse_tnd_counts(), B=16, N1=64,
+                           seqused_kv=[16384] * 16, K2=512, materialise_all_ori=False)

@@ -38,7 +38,6 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters.json")
-SEEDS_HCA = 1006
 METRIC = "decode attention HBM GB/s + prefill attention TFLOP/s, bf16, 1 MI355X"
 LLC_BYTES = 256 << 20          # MI355X last-level (Infinity) cache
 
@@ -408,7 +407,7 @@ def qkvo_bytes(case):
 
 def _prefill_variant(ctx, key, make, text, kernel, extra):
     TI, W, O = _mods()
-    case = make(W.c2_causal_gqa())
+    case = make()
     out, _, _ = prefill_component(
         ctx, case, key, text, kernel,
         cpu_fn=lambda: O.fia_case(case, heads=list(range(4))), cpu_work=dense_flops(case) * 4 / 32,
@@ -420,7 +419,7 @@ def _prefill_variant(ctx, key, make, text, kernel, extra):
 def comp_mask(ctx):
     TI, W, O = _mods()
     return _prefill_variant(
-        ctx, "mask", lambda b: W.with_random_mask(b, 41, p_masked=0.1, mode=0),
+        ctx, "mask", W.mask_prefill,
         "causal GQA prefill shapes, sparse_mode 0 with a uint8 mask [4, 2048, 2048] (10 % of keys "
         "masked out, every key of the actual lengths otherwise)", "prefill_bf16<128, false, 0, true>",
         # one mask byte per (i, j) of every batch's [Lq, Lk] corner, shared by the heads
@@ -430,7 +429,7 @@ def comp_mask(ctx):
 def comp_bias(ctx):
     TI, W, O = _mods()
     return _prefill_variant(
-        ctx, "bias", lambda b: W.with_random_bias(b, 42, per_batch=False),
+        ctx, "bias", W.bias_prefill,
         "causal GQA prefill with a bf16 pse_shift bias [1, 32, 2048, 2048]",
         "prefill_bf16<128, false, 0, true>",
         # 2 bytes of bias per visible (i, j) pair and query head; a bias
@@ -442,7 +441,7 @@ def comp_bias(ctx):
 
 def comp_sink(ctx):
     TI, W, O = _mods()
-    return _prefill_variant(ctx, "sink", lambda b: W.with_random_sink(b, 43),
+    return _prefill_variant(ctx, "sink", W.sink_prefill,
                             "causal GQA prefill with a bf16 learnable sink [32]",
                             "prefill_bf16<128, false, 0, false>", None)
 
@@ -498,9 +497,7 @@ def comp_c3_devlen(ctx):
 
 def _q8(ctx, key, kind, km, off, bn, text):
     TI, W, O = _mods()
-    qc = W.with_kv_quant(W.c3_paged_decode(), 1007, kind=kind, kmode=km, vmode=km, offsets=off)
-    if bn:
-        qc = W.as_bnnbsd(qc)
+    qc = W.q8_decode(key)
     return decode_component(ctx, qc, key, "the paged GQA decode with a fake-quantised KV cache: " + text,
                             "decode_split_q8<128> + decode_merge<128>", cpu=(key == "q8_int8"))
 
@@ -563,8 +560,7 @@ def comp_sfmla(ctx):
 
 def comp_hca(ctx):
     TI, W, O = _mods()
-    case = W.sparse_case("hca", SEEDS_HCA, B=16, N1=64, seqused_kv=[16384] * 16,
-                         materialise_all_ori=False, heavily_compressed=True)
+    case = W.sparse_hca_decode()
     return sparse_component(ctx, case, "hca",
                             "shared-KV sparse decode, heavily compressed: B=16, Q_N=64, D=512, window "
                             "128 + every row of the ratio-128 compressed KV (128 rows), sinks")
@@ -572,8 +568,7 @@ def comp_hca(ctx):
 
 def comp_s1_2(ctx):
     TI, W, O = _mods()
-    case = W.sparse_case("s1_2", SEEDS_HCA + 1, B=16, N1=64, seqused_kv=[16384] * 16, K2=512,
-                         S1=2, materialise_all_ori=False)
+    case = W.sparse_two_tokens()
     return sparse_component(ctx, case, "s1_2",
                             "shared-KV sparse attention, 2 query tokens per batch entry: B=16, Q_N=64, "
                             "D=512, window 128 + top-512 of ratio-4 compressed KV per token, sinks")
@@ -581,9 +576,8 @@ def comp_s1_2(ctx):
 
 def comp_tnd(ctx):
     TI, W, O = _mods()
-    counts = [int(x) for x in W.rng_for(SEEDS_HCA + 2).integers(1, 5, size=16)]
-    case = W.sparse_tnd_case("tnd", SEEDS_HCA + 3, q_counts=counts, B=16, N1=64,
-                             seqused_kv=[16384] * 16, K2=512, materialise_all_ori=False)
+    counts = W.sparse_tnd_counts()
+    case = W.sparse_tnd_ragged()
     return sparse_component(ctx, case, "tnd",
                             f"shared-KV sparse attention, TND with query counts {counts} "
                             f"(T1 = {sum(counts)}): Q_N=64, D=512, window 128 + top-512 of ratio-4 "
