@@ -530,69 +530,86 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
 }
 
 // Fold the chunk partials of one query row in chunk order with the sink
-// logit.  Workgroup (row, 32-wide d block, 64-head block): the 64 threads of
-// each wave take consecutive heads (coalesced partial reads), the 4 waves 8 d
-// values each.  Each thread computes its head's chunk weights itself; the
-// first 8 chunks' partials are requested before the log-sum-exps are read,
-// so both arrive in one trip to memory.
+// logit.  Workgroup (row, 16-wide d block, 64-head block): the 64 threads of
+// each wave take consecutive heads (coalesced partial reads), the 4 waves 4 d
+// values each.  Chunks are folded in groups of G: every log-sum-exp and
+// partial of a group is requested before the first is used (addresses
+// clamped to the last chunk, so the loads are unconditional), and the group
+// is folded into the running sum with the usual rescale by the new maximum;
+// the sink's term joins at the end.
+constexpr int kMergeD = 4;   // d values per thread
 template <bool F16>
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   constexpr int G = 8;   // chunks per group of loads in flight
   const int tid = threadIdx.x;
   const int hl = tid & 63;
   const int r = blockIdx.x;
-  const int d0 = 32 * blockIdx.y + 8 * (tid >> 6);
+  const int d0 = 4 * kMergeD * blockIdx.y + kMergeD * (tid >> 6);
   const int h = kSparseHeads * blockIdx.z + hl;
   if (h >= a.N1) return;
   const SparseRow qr = sparse_row(a, r);
   const int nc = a.n_chunks;
   const int64_t rc0 = (int64_t)r * nc;
   const float* base = a.part_o + (rc0 * kSparseD + d0) * a.N1 + h;
-  const int64_t cstride = (int64_t)kSparseD * a.N1;
-  float x[G][8];
-#pragma unroll
-  for (int i = 0; i < G; ++i) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u) x[i][u] = i < nc ? base[i * cstride + (int64_t)u * a.N1] : 0.f;
-  }
-  const bool sink_on = a.sinks != nullptr && qr.live;
-  const float sink = sink_on ? a.sinks[h] * kLog2e : kNegInf;
   const float* lp = a.part_lse + rc0 * a.N1 + h;
-  float M = sink;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, lp[(int64_t)c * a.N1]);
-  const float m_use = (M == kNegInf) ? 0.f : M;
-  float L = sink_on ? fast_exp2(sink - m_use) : 0.f;
-  float acc[8];
+  const int64_t cstride = (int64_t)kSparseD * a.N1;
+  // The sink logit (a buffer load, zero without sinks: no branch, so the
+  // load stays in flight through the fold that follows).
+  const bool sink_on = a.sinks != nullptr && qr.live;
+  const __amdgpu_buffer_rsrc_t r_sink = make_rsrc(a.sinks, a.sinks != nullptr ? (uint32_t)a.N1 * 4u : 0u);
+  const float z = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r_sink, (uint32_t)h * 4u, 0, 0)) * kLog2e;
+  // Running maximum M and sum L of 2^(lse_c - M) over the chunks so far.
+  float M = kNegInf;
+  float L = 0.f;
+  float acc[kMergeD];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) acc[u] = 0.f;
+  for (int u = 0; u < kMergeD; ++u) acc[u] = 0.f;
   for (int c0 = 0; c0 < nc; c0 += G) {
-    if (c0 > 0) {
-#pragma unroll
-      for (int i = 0; i < G; ++i) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          x[i][u] = c0 + i < nc ? base[(c0 + i) * cstride + (int64_t)u * a.N1] : 0.f;
-        }
-      }
-    }
+    float lv[G];
+    float x[G][kMergeD];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
-      if (c0 + i < nc) {
-        const float lc = lp[(int64_t)(c0 + i) * a.N1];
-        const float wc = (lc == kNegInf) ? 0.f : fast_exp2(lc - m_use);
-        L += wc;
+      const int64_t c = min(c0 + i, nc - 1);
+      lv[i] = lp[c * a.N1];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) acc[u] += wc * x[i][u];
-      }
+      for (int u = 0; u < kMergeD; ++u) x[i][u] = base[c * cstride + (int64_t)u * a.N1];
     }
+    // Branch-free from here (a branch would let the compiler sink the
+    // partial loads past the wait for the log-sum-exps).
+    float gm = M;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if (c0 + i >= nc) lv[i] = kNegInf;
+      gm = fmaxf(gm, lv[i]);
+    }
+    const float gmu = (gm == kNegInf) ? 0.f : gm;
+    const float sc = (M == kNegInf) ? 0.f : fast_exp2(M - gmu);
+    L *= sc;
+#pragma unroll
+    for (int u = 0; u < kMergeD; ++u) acc[u] *= sc;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float wc = (lv[i] == kNegInf) ? 0.f : fast_exp2(lv[i] - gmu);
+      L += wc;
+#pragma unroll
+      for (int u = 0; u < kMergeD; ++u) acc[u] = __builtin_fmaf(wc, x[i][u], acc[u]);
+    }
+    M = gm;
+  }
+  if (sink_on) {
+    const float mf = fmaxf(M, z);
+    const float sc = (M == kNegInf) ? 0.f : fast_exp2(M - mf);
+    L = L * sc + fast_exp2(z - mf);
+#pragma unroll
+    for (int u = 0; u < kMergeD; ++u) acc[u] *= sc;
+    M = mf;
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* op = a.o + (int64_t)qr.b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)h * a.o_sh + d0;
-  st16(op, u32x4{pack_h2<F16>(acc[0] * inv, acc[1] * inv), pack_h2<F16>(acc[2] * inv, acc[3] * inv),
-                 pack_h2<F16>(acc[4] * inv, acc[5] * inv), pack_h2<F16>(acc[6] * inv, acc[7] * inv)});
+  st8(op, u32x2{pack_h2<F16>(acc[0] * inv, acc[1] * inv), pack_h2<F16>(acc[2] * inv, acc[3] * inv)});
   if (a.lse != nullptr && blockIdx.y == 0 && tid < 64) {
     a.lse[(int64_t)qr.b * a.lse_sb + (int64_t)qr.tq * a.lse_ss + (int64_t)h * a.lse_sh] =
-        L > 0.f ? (m_use + fast_log2(L)) * kLn2 : kPosInf;
+        L > 0.f ? (M + fast_log2(L)) * kLn2 : kPosInf;
   }
 }
 
@@ -620,7 +637,7 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
 
 hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
   if (a.n_rows == 0 || a.n_chunks <= 1) return hipSuccess;
-  const dim3 grid(a.n_rows, kSparseD / 32, a.n_hb);
+  const dim3 grid(a.n_rows, kSparseD / (4 * kMergeD), a.n_hb);
   if (a.fmt == SF_FP16) {
     sparse_merge<true><<<grid, 256, 0, s>>>(a);
   } else {
