@@ -296,81 +296,90 @@ template <int D>
 __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
   constexpr int PL = D / 64;
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + uniform(threadIdx.x >> 6);   // one row per wave
   if (row >= a.B * a.Qn) return;
   const int b = row / a.Qn;
   const int h = row - b * a.Qn;
+  // The batch record, read whole (one scalar load).
   const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
-  const int nchunk = bm[BF_NCHUNK];
+  int32_t rec[BF_COUNT];
+#pragma unroll
+  for (int f = 0; f < BF_COUNT; ++f) rec[f] = bm[f];
+  const int nchunk = rec[BF_NCHUNK];
   if (nchunk == 1) return;
   // A TND batch entry without a query token owns no output row (its offset
   // is the next entry's first row): nothing to write.
-  if (a.tnd && bm[BF_QLEN] == 0) return;
-  const int q_off = bm[BF_QOFF];
+  if (a.tnd && rec[BF_QLEN] == 0) return;
+  const int q_off = rec[BF_QOFF];
   uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)q_off * a.o_ss +
                  (int64_t)h * a.o_sh + lane * PL;
   float* lp = a.lse + (int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)q_off * a.lse_ss;
   // Learnable sink (log2 units): one more term with a zero value vector.
-  const float z = a.sink != nullptr ? bf16_to_f32(a.sink[h]) * kLog2e : kNegInf;
-  if (nchunk == 0) {
-#pragma unroll
-    for (int u = 0; u < PL; ++u) op[u] = 0;
-    if (a.write_lse && lane == 0) *lp = a.sink != nullptr ? z * kLn2 : kPosInf;
-    return;
-  }
-  const int chunk0 = bm[BF_CHUNK0];
+  // Loaded through a buffer resource (reads zero without a sink), so no
+  // branch holds the chunk loads below behind it.
+  const __amdgpu_buffer_rsrc_t r_sink =
+      make_rsrc(a.sink, a.sink != nullptr ? (uint32_t)a.Qn * 2u : 0u);
+  const float z = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r_sink, (uint32_t)h * 2u, 0, 0)) * kLog2e;
+  // A row with no chunk (no visible key) takes the same path: the fold
+  // leaves M = -inf and L = 0, and the end writes 0 with LSE +inf (or the
+  // sink's).
+  const int chunk0 = rec[BF_CHUNK0];
+  // Chunks are folded in fixed order, in groups of G: every log-sum-exp and
+  // partial of a group is requested before the first is used (addresses
+  // clamped to the last chunk, so the loads are unconditional and nothing
+  // branches before they are used), with a running-maximum rescale.
+  constexpr int G = 8;
   float M = kNegInf;
-  for (int c0 = 0; c0 < nchunk; c0 += 64) {
-    const int c = c0 + lane;
-    const float lc = c < nchunk ? a.part_lse[(int64_t)(chunk0 + c) * a.Qn + h] : kNegInf;
-    M = fmaxf(M, lc);
-  }
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor_f(M, m));
-  if (M == kNegInf) {   // every chunk empty (explicit mask): 0 and LSE +inf, or the sink's
-#pragma unroll
-    for (int u = 0; u < PL; ++u) op[u] = 0;
-    if (a.write_lse && lane == 0) *lp = a.sink != nullptr ? z * kLn2 : kPosInf;
-    return;
-  }
-  M = fmaxf(M, z);
   float L = 0.f;
   float acc[PL];
 #pragma unroll
   for (int u = 0; u < PL; ++u) acc[u] = 0.f;
-  for (int c0 = 0; c0 < nchunk; c0 += 64) {
-    const int c = c0 + lane;
-    const float lc = c < nchunk ? a.part_lse[(int64_t)(chunk0 + c) * a.Qn + h] : kNegInf;
-    const float w = fast_exp2(lc - M);
-    const int cnt = min(64, nchunk - c0);
-    int k = 0;
-    for (; k + 4 <= cnt; k += 4) {
-      float x[4][PL];
-      float wk[4];
+  for (int c0 = 0; c0 < nchunk; c0 += G) {
+    // Lane i < G loads the log-sum-exp of chunk c0 + i (a vector load: the
+    // address is wave-uniform per chunk, and scalar loads would each be
+    // waited for on their own); every lane loads its d values of all G.
+    const float lvl = a.part_lse[((int64_t)chunk0 + min(c0 + (lane & (G - 1)), nchunk - 1)) * a.Qn + h];
+    float x[G][PL];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        wk[t] = __shfl(w, k + t, 64);
-        const float* pp = a.part_o + ((int64_t)(chunk0 + c0 + k + t) * a.Qn + h) * D + lane * PL;
+    for (int i = 0; i < G; ++i) {
+      const int64_t pc = (int64_t)chunk0 + min(c0 + i, nchunk - 1);
+      const float* pp = a.part_o + (pc * a.Qn + h) * D + lane * PL;
 #pragma unroll
-        for (int u = 0; u < PL; ++u) x[t][u] = pp[u];
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        L += wk[t];
-#pragma unroll
-        for (int u = 0; u < PL; ++u) acc[u] += wk[t] * x[t][u];
-      }
+      for (int u = 0; u < PL; ++u) x[i][u] = pp[u];
     }
-    for (; k < cnt; ++k) {
-      const float wk = __shfl(w, k, 64);
-      const float* pp = a.part_o + ((int64_t)(chunk0 + c0 + k) * a.Qn + h) * D + lane * PL;
-      L += wk;
+    float lv[G];
+    float gm = M;
 #pragma unroll
-      for (int u = 0; u < PL; ++u) acc[u] += wk * pp[u];
+    for (int i = 0; i < G; ++i) {
+      lv[i] = (c0 + i < nchunk) ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lvl), i))
+                                : kNegInf;
+      gm = fmaxf(gm, lv[i]);
     }
+    const float gmu = (gm == kNegInf) ? 0.f : gm;
+    const float sc = (M == kNegInf) ? 0.f : fast_exp2(M - gmu);
+    L *= sc;
+#pragma unroll
+    for (int u = 0; u < PL; ++u) acc[u] *= sc;
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const float wc = (lv[i] == kNegInf) ? 0.f : fast_exp2(lv[i] - gmu);
+      L += wc;
+#pragma unroll
+      for (int u = 0; u < PL; ++u) acc[u] = __builtin_fmaf(wc, x[i][u], acc[u]);
+    }
+    M = gm;
   }
-  if (a.sink != nullptr) L += fast_exp2(z - M);
-  const float inv = 1.f / L;
+  if (a.sink != nullptr) {
+    // every chunk empty: output 0, LSE the sink's
+    const float mf = fmaxf(M, z);
+    const float sc = (M == kNegInf) ? 0.f : fast_exp2(M - mf);
+    L = L * sc + fast_exp2(z - mf);
+#pragma unroll
+    for (int u = 0; u < PL; ++u) acc[u] *= sc;
+    M = mf;
+  }
+  // every chunk empty and no sink: output 0, LSE +inf
+  const float inv = L > 0.f ? 1.f / L : 0.f;
   if constexpr (PL == 2) {
     *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[1] * inv);
   } else {
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(256) void decode_merge(AttnArgs a) {
       op[u] = (uint16_t)(pack_bf16x2(acc[u] * inv, 0.f) & 0xffffu);
     }
   }
-  if (a.write_lse && lane == 0) *lp = (M + fast_log2(L)) * kLn2;
+  if (a.write_lse && lane == 0) *lp = L > 0.f ? (M + fast_log2(L)) * kLn2 : kPosInf;
 }
 
 hipError_t launch_decode_bf16(const AttnArgs& a, int32_t n_items, hipStream_t s) {
