@@ -147,6 +147,24 @@ __device__ __forceinline__ SparseRow sparse_row(const SparseArgs& a, int r) {
   return w;
 }
 
+// Same, for a row index r that is uniform over the calling wave (every
+// lane active): with B + 1 <= 64 the wave loads the cumulative counts in one
+// vector load (lane i: cu_q[i]) and counts the entries that start at or
+// before r, instead of a chain of dependent loads.
+__device__ __forceinline__ SparseRow sparse_row_wave(const SparseArgs& a, int r, int lane) {
+  if (a.cu_q == nullptr || a.B + 1 > 64) return sparse_row(a, r);
+  const int v = a.cu_q[min(lane, a.B)];
+  const int lo = __popcll(__ballot(lane >= 1 && lane < a.B && v <= r));
+  const int c0 = __builtin_amdgcn_readlane(v, lo), c1 = __builtin_amdgcn_readlane(v, lo + 1);
+  SparseRow w;
+  w.b = lo;
+  w.tq = r;
+  w.live = c0 <= r && r < c1;
+  w.t = w.live ? r - c0 : 0;
+  w.s1 = w.live ? c1 - c0 : 1;
+  return w;
+}
+
 // KV length of the row's entry, clamped to what its pool can address.
 __device__ __forceinline__ int sparse_len(const SparseArgs& a, const SparseRow& w) {
   if (!w.live) return 0;
@@ -264,48 +282,54 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   const int head = kSparseHeads * hb + 32 * hq + n;
   const bool head_ok = head < a.N1;
 
-  const SparseRow qr = sparse_row(a, r);
+  const SparseRow qr = sparse_row_wave(a, r, lane);
   const int b = qr.b;
 
   // 1. The workgroup's 64 query rows into LDS (row-major; heads past N1 are
-  // zero), then the LDS copies of the entry's block tables and index entries.
+  // zero), and LDS copies of the entry's block-table rows and of the chunk's
+  // index entries.  Every load is issued before the first store: each is
+  // unconditional (heads past N1 and absent tables lie outside their buffer
+  // resources and read as zero; positions are clamped), so they are in
+  // flight together, one trip to memory.
   uint8_t* qs = lds + OFF_Q;
-  {
-    const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss;
-    u32x4 qv[8];
+  const int nh = min(kSparseHeads, a.N1 - kSparseHeads * hb);
+  const __amdgpu_buffer_rsrc_t rq =
+      make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss + (int64_t)kSparseHeads * hb * a.q_sh,
+                (uint32_t)(((int64_t)(nh - 1) * a.q_sh + kSparseD) * 2));
+  u32x4 qv[8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int p = tid + kThreads * v;   // 16-byte piece p % 64 of head p / 64
-      const int hd = kSparseHeads * hb + (p >> 6);
-      qv[v] = hd < a.N1 ? ld16(qrow + (int64_t)hd * a.q_sh + 8 * (p & 63)) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-      const int p = tid + kThreads * v;
-      *reinterpret_cast<u32x4*>(qs + (p >> 6) * X_PITCH + 16 * (p & 63)) = qv[v];
-    }
+  for (int v = 0; v < 8; ++v) {
+    const int p = tid + kThreads * v;   // 16-byte piece p % 64 of head p / 64
+    qv[v] = buf_ld16(rq, (uint32_t)(((int64_t)(p >> 6) * a.q_sh + 8 * (p & 63)) * 2));
   }
   const bool cache_o = a.ori.paged && a.ori.bt_cols <= kSparseBtCache;
   const bool cache_c = a.has_cmp && a.cmp.paged && a.cmp.bt_cols <= kSparseBtCache;
-  if (cache_o) {
-    const int32_t* src = a.ori.bt + (int64_t)b * a.ori.bt_sb;
-    for (int i = tid; i < a.ori.bt_cols; i += kThreads) bt_o[i] = src[i];
-  }
-  if (cache_c) {
-    const int32_t* src = a.cmp.bt + (int64_t)b * a.cmp.bt_sb;
-    for (int i = tid; i < a.cmp.bt_cols; i += kThreads) bt_c[i] = src[i];
-  }
+  // One entry per thread: the caches hold at most kThreads entries, the
+  // index slice 64 * sub_per_chunk <= kThreads.
+  static_assert(kSparseBtCache <= kThreads && kSparseSub * kSparseMaxSub <= kThreads, "one entry per thread");
   const int k_begin = s_begin - a.n_win_slots;   // index entry of the chunk's first slot
   const bool use_idx = a.has_cmp && !a.cmp_direct;
-  if (use_idx) {
-    const int32_t* src = a.idx + (int64_t)b * a.idx_sb + (int64_t)qr.tq * a.idx_ss;
-    for (int i = tid; i < kSparseSub * sub_n; i += kThreads) {
-      const int k = k_begin + i;
-      ixc[i] = (k >= 0 && k < a.K2) ? src[k] : -1;
-    }
-  }
+  const int k_own = k_begin + tid;
+  const __amdgpu_buffer_rsrc_t r_bto =
+      make_rsrc(cache_o ? a.ori.bt + (int64_t)b * a.ori.bt_sb : nullptr, cache_o ? (uint32_t)a.ori.bt_cols * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t r_btc =
+      make_rsrc(cache_c ? a.cmp.bt + (int64_t)b * a.cmp.bt_sb : nullptr, cache_c ? (uint32_t)a.cmp.bt_cols * 4u : 0u);
+  const __amdgpu_buffer_rsrc_t r_ix =
+      make_rsrc(use_idx ? a.idx + (int64_t)b * a.idx_sb + (int64_t)qr.tq * a.idx_ss : nullptr,
+                use_idx ? (uint32_t)a.K2 * 4u : 0u);
+  const int32_t bto = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_bto, (uint32_t)tid * 4u, 0, 0);
+  const int32_t btc = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_btc, (uint32_t)tid * 4u, 0, 0);
+  const int32_t ixv = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(r_ix, (uint32_t)max(k_own, 0) * 4u, 0, 0);
   const int Lk = sparse_len(a, qr);
   const SlotCtx ctx = slot_ctx(a, qr, Lk);
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int p = tid + kThreads * v;
+    *reinterpret_cast<u32x4*>(qs + (p >> 6) * X_PITCH + 16 * (p & 63)) = qv[v];
+  }
+  if (cache_o && tid < a.ori.bt_cols) bt_o[tid] = bto;
+  if (cache_c && tid < a.cmp.bt_cols) bt_c[tid] = btc;
+  if (use_idx && tid < kSparseSub * sub_n) ixc[tid] = (k_own >= 0 && k_own < a.K2) ? ixv : -1;
   __syncthreads();
 
   auto ori_bt = [&](int col) FIA_INLINE {
@@ -546,8 +570,8 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   const int r = blockIdx.x;
   const int d0 = 4 * kMergeD * blockIdx.y + kMergeD * (tid >> 6);
   const int h = kSparseHeads * blockIdx.z + hl;
+  const SparseRow qr = sparse_row_wave(a, r, hl);   // every lane still active
   if (h >= a.N1) return;
-  const SparseRow qr = sparse_row(a, r);
   const int nc = a.n_chunks;
   const int64_t rc0 = (int64_t)r * nc;
   const float* base = a.part_o + (rc0 * kSparseD + d0) * a.N1 + h;
