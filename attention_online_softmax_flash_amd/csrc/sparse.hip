@@ -288,19 +288,20 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   // 1. The workgroup's 64 query rows into LDS (row-major; heads past N1 are
   // zero), and LDS copies of the entry's block-table rows and of the chunk's
   // index entries.  Every load is issued before the first store: each is
-  // unconditional (heads past N1 and absent tables lie outside their buffer
-  // resources and read as zero; positions are clamped), so they are in
+  // unconditional (positions are clamped into range, absent tables lie
+  // outside their empty buffer resources and read as zero), so they are in
   // flight together, one trip to memory.
   uint8_t* qs = lds + OFF_Q;
-  const int nh = min(kSparseHeads, a.N1 - kSparseHeads * hb);
-  const __amdgpu_buffer_rsrc_t rq =
-      make_rsrc(a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss + (int64_t)kSparseHeads * hb * a.q_sh,
-                (uint32_t)(((int64_t)(nh - 1) * a.q_sh + kSparseD) * 2));
+  const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss;
   u32x4 qv[8];
 #pragma unroll
   for (int v = 0; v < 8; ++v) {
-    const int p = tid + kThreads * v;   // 16-byte piece p % 64 of head p / 64
-    qv[v] = buf_ld16(rq, (uint32_t)(((int64_t)(p >> 6) * a.q_sh + 8 * (p & 63)) * 2));
+    // 16-byte piece p % 64 of head p / 64; heads past N1 load the last head
+    // (a valid address) and are zeroed.
+    const int p = tid + kThreads * v;
+    const int hd = kSparseHeads * hb + (p >> 6);
+    const u32x4 w = ld16(qrow + (int64_t)min(hd, a.N1 - 1) * a.q_sh + 8 * (p & 63));
+    qv[v] = hd < a.N1 ? w : u32x4{0u, 0u, 0u, 0u};
   }
   const bool cache_o = a.ori.paged && a.ori.bt_cols <= kSparseBtCache;
   const bool cache_c = a.has_cmp && a.cmp.paged && a.cmp.bt_cols <= kSparseBtCache;

@@ -539,6 +539,24 @@ def test_sparse_multi_token(i):
     check_out(to_f64(plan.out), O.sparse_sharedkv(case))
 
 
+def test_sparse_strided_query_and_output():
+    """q and attention_out as strided views (heads outermost in memory, so the
+    head stride is S1 * 512), N1 = 128 (two head blocks)."""
+    case = W.sparse_case("sstr", 445, B=2, N1=128, seqused_kv=[900, 3000], K2=512, S1=3,
+                         block_size1=64, block_size2=32, materialise_all_ori=False)
+    t = TI.sparse_tensors(case, DEV)
+    q = t["q"]
+    t["q"] = q.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)   # [B, S1, N1, 512] view
+    assert t["q"].stride(2) == 3 * 512
+    out = torch.zeros(q.shape[0], q.shape[2], q.shape[1], q.shape[3], dtype=q.dtype, device=DEV)
+    plan = fia.SparsePlan(t["q"], t["ori_kv"], t["cmp_kv"], t["cmp_sparse_indices"],
+                          t["ori_block_table"], t["cmp_block_table"], t["seqused_kv"], t["sinks"],
+                          softmax_scale=case.softmax_scale, max_seqused_kv=max(case.seqused_kv),
+                          cmp_ratio=case.cmp_ratio, attention_out=out.permute(0, 2, 1, 3))
+    run_plan(plan)
+    check_out(to_f64(out.permute(0, 2, 1, 3)), O.sparse_sharedkv(case))
+
+
 def test_sparse_multi_token_rows_are_bit_exact():
     case = W.sparse_case("smr", 440, B=2, N1=64, seqused_kv=[40, 3000], K2=512, S1=5,
                          block_size1=32, block_size2=16, materialise_all_ori=False)
