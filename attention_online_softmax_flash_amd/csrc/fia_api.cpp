@@ -1592,6 +1592,34 @@ fia_status fia_debug_gather_kv(fia_executor* e, void* workspace, size_t workspac
   return FIA_SUCCESS;
 }
 
+fia_status fia_debug_read_kv(fia_executor* e, void* workspace, size_t workspace_size, int32_t order,
+                             uint32_t* out, int64_t* out_len, void* stream) {
+  if (e == nullptr || out_len == nullptr) return fail(FIA_ERR_NULLPTR, "executor and out_len must not be NULL");
+  if (e->noop || e->kind != KIND_DECODE || e->dev_len) {
+    return fail(FIA_ERR_PARAM_INVALID, "fia_debug_read_kv needs a split-KV decode executor planned on the host");
+  }
+  if (order != 0 && order != 1) return fail(FIA_ERR_PARAM_INVALID, "order must be 0 or 1");
+  const int64_t grid = fia::decode_read_grid(e->a, order);
+  if (grid < 0) {
+    return fail(FIA_ERR_UNSUPPORTED, order == 0 ? "read order 0 needs D * element size of 128 or 256 bytes"
+                                                : "read order 1 needs adjacent heads and KV_N * D * element "
+                                                  "size of 1024 or 2048 bytes");
+  }
+  if (out == nullptr) {
+    *out_len = grid;
+    return FIA_SUCCESS;
+  }
+  if (*out_len < grid) return fail(FIA_ERR_PARAM_INVALID, "out holds fewer words than the read writes");
+  fia_status st = check_ws(e, workspace, workspace_size);
+  if (st != FIA_SUCCESS) return st;
+  if ((st = upload_plan(e)) != FIA_SUCCESS) return st;
+  bind_workspace(e, workspace);
+  hipError_t err = fia::launch_decode_read(e->a, order, out, static_cast<hipStream_t>(stream));
+  if (err != hipSuccess) return fail(FIA_ERR_HIP, std::string("read launch failed: ") + hipGetErrorString(err));
+  *out_len = grid;
+  return FIA_SUCCESS;
+}
+
 fia_status fia_debug_sparse_rows(fia_executor* e, void* workspace, size_t workspace_size,
                                  int32_t* ids_out, uint8_t* rows_out, int32_t* n_slots_out,
                                  void* stream) {

@@ -183,8 +183,26 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t s);
 hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s);
 hipError_t launch_debug_gather(const AttnArgs& a, int32_t which, void* dst, int32_t s2max,
                                hipStream_t s);
+hipError_t launch_decode_read(const AttnArgs& a, int32_t order, uint32_t* out, hipStream_t s);
 hipError_t launch_debug_sparse_rows(const SparseArgs& a, int32_t* ids, uint8_t* rows,
                                     hipStream_t s);
+
+// Workgroups of the decode read pass (the length of its output), or -1 when
+// the plan's shape has no instantiation: order 0 needs rows of D * esz bytes
+// in {128, 256} (esz: bytes per key / value element, 1 for fake-quant
+// codes), order 1 KV_N * D * esz in {1024, 2048} with the heads of a token
+// adjacent.
+inline int64_t decode_read_grid(const AttnArgs& a, int32_t order) {
+  const int64_t esz = a.kvq ? 1 : a.esz;   // bytes per key / value element
+  const int64_t row = (int64_t)a.D * esz;
+  if (order == 0) {
+    if (row != 128 && row != 256) return -1;
+    return (int64_t)a.n_work * a.KVn;
+  }
+  const int64_t span = row * a.KVn;
+  if ((span != 1024 && span != 2048) || a.k_sh * esz != row || a.v_sh * esz != row) return -1;
+  return (int64_t)a.n_work * 8;
+}
 
 // Constants shared by planner and kernels.
 constexpr int kPrefillRows = 128;   // query rows per prefill workgroup

@@ -201,10 +201,107 @@ __global__ __launch_bounds__(256) void debug_gather(AttnArgs a, int which, uint8
 
 hipError_t launch_debug_gather(const AttnArgs& a, int32_t which, void* dst, int32_t s2max,
                                hipStream_t s) {
-  const int esz = a.esz;
+  const int esz = a.kvq ? 1 : a.esz;   // bytes per key / value element (1: fake-quant codes)
   const int64_t total = (int64_t)a.B * s2max * a.KVn * (a.D * esz / 4);
   if (total > 0) {
     debug_gather<<<(unsigned)((total + 255) / 256), 256, 0, s>>>(a, which, (uint8_t*)dst, s2max, esz);
+  }
+  return hipGetLastError();
+}
+
+// Read-only pass over a split-KV decode plan's key / value rows, the
+// measured ceiling of its access pattern: every visible key and value row of
+// every chunk is loaded once (16-byte non-temporal loads through per-run
+// buffer resources, 8 KB of keys and 8 KB of values per wave and step, all in
+// flight before one wait) and folded by XOR; nothing else.
+//   ORDER 0: a workgroup per (chunk, KV head), its waves over quarters of
+//     the chunk, SPAN = D * esz bytes per key and request: the order the
+//     decode kernels read in.
+//   ORDER 1: a workgroup per (chunk, eighth of it), its waves over 32 keys,
+//     SPAN = KV_N * D * esz contiguous bytes of a token row per request
+//     (pools whose heads of one token are adjacent: PA_ND, BSND).
+// out[blockIdx.x] receives the workgroup's XOR of every 32-bit word read.
+template <int ORDER, int SPAN>
+__global__ __launch_bounds__(256) void decode_read(AttnArgs a, uint32_t* out) {
+  constexpr int KS = 8192 / SPAN;   // keys per step (64, 32, 8 or 4)
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int parts = ORDER == 0 ? a.KVn : 8;
+  const int cg = blockIdx.x / parts;
+  const int part = blockIdx.x - cg * parts;
+  const int b = a.work[2 * cg], c = a.work[2 * cg + 1];
+  const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
+  const int lo = bm[BF_LO], hi = bm[BF_HI], kv_off = bm[BF_KVOFF];
+  const int C = a.chunk;
+  const int cbase = (lo / C + c) * C;
+  const int wlen = ORDER == 0 ? C / 4 : C / 32;
+  const int ws = ORDER == 0 ? cbase + wave * wlen : cbase + (4 * part + wave) * wlen;
+  const int t_lo = max(ws, lo), t_hi = min(ws + wlen, hi);
+  const int kvh = ORDER == 0 ? part : 0;
+  const int esz = a.kvq ? 1 : a.esz;   // bytes per key / value element
+  const uint8_t* kb = (const uint8_t*)a.k;
+  const uint8_t* vb = (const uint8_t*)a.v;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  if (t_hi > t_lo) {
+    const int first = ws + ((t_lo - ws) & ~(KS - 1));
+    const WavePages wp = wave_pages(a, b, first, hi - 1, lane);
+    for (int ti = first; ti < t_hi; ti += KS) {
+      // The step's keys in 16-key runs (each inside one page); keys at or
+      // past t_hi lie outside a run's resources and read as zero.
+      constexpr int NR = KS > 16 ? KS / 16 : 1;
+      constexpr int RK = KS > 16 ? 16 : KS;   // keys per run
+      __amdgpu_buffer_rsrc_t rk[NR], rv[NR];
+#pragma unroll
+      for (int q = 0; q < NR; ++q) {
+        const int jb = ti + RK * q;
+        const int nv = min(RK, t_hi - jb);
+        int64_t ko = 0, vo = 0;
+        uint32_t kbytes = 0, vbytes = 0;
+        if (nv > 0) {
+          ko = kv_row_offset_w(a, wp, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off) * esz;
+          vo = kv_row_offset_w(a, wp, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off) * esz;
+          kbytes = (uint32_t)((int64_t)(nv - 1) * a.k_ss * esz + SPAN);
+          vbytes = (uint32_t)((int64_t)(nv - 1) * a.v_ss * esz + SPAN);
+        }
+        rk[q] = make_rsrc(kb + ko, kbytes);
+        rv[q] = make_rsrc(vb + vo, vbytes);
+      }
+      // Load i, lane l: byte 1024 i + 16 l of the step's KS x SPAN bytes.
+      u32x4 v[16];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int byte = 1024 * i + 16 * lane;
+        const int kk = byte / SPAN;            // key within the step
+        const int q = (1024 * i / SPAN) / RK;  // its run (the same for every lane)
+        const int kr = kk - RK * q;            // key within the run
+        const int pc = byte - kk * SPAN;
+        v[2 * i] = buf_ld16_nt(rk[q], (uint32_t)((int64_t)kr * a.k_ss * esz + pc));
+        v[2 * i + 1] = buf_ld16_nt(rv[q], (uint32_t)((int64_t)kr * a.v_ss * esz + pc));
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc ^= v[i];
+    }
+  }
+  uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int m = 32; m >= 1; m >>= 1) x ^= (uint32_t)__shfl_xor((int)x, m, 64);
+  __shared__ uint32_t red[4];
+  if (lane == 0) red[wave] = x;
+  __syncthreads();
+  if (tid == 0) out[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
+
+hipError_t launch_decode_read(const AttnArgs& a, int32_t order, uint32_t* out, hipStream_t s) {
+  const int64_t grid = decode_read_grid(a, order);
+  if (grid <= 0) return hipSuccess;
+  const int64_t row = (int64_t)a.D * (a.kvq ? 1 : a.esz);
+  const unsigned g = (unsigned)grid;
+  if (order == 0) {
+    if (row == 128) decode_read<0, 128><<<g, 256, 0, s>>>(a, out);
+    else decode_read<0, 256><<<g, 256, 0, s>>>(a, out);
+  } else {
+    if (row * a.KVn == 1024) decode_read<1, 1024><<<g, 256, 0, s>>>(a, out);
+    else decode_read<1, 2048><<<g, 256, 0, s>>>(a, out);
   }
   return hipGetLastError();
 }

@@ -35,7 +35,7 @@ KIND_NAMES = {0: "fill", 1: "prefill", 2: "decode", 3: "sparse", 4: "fp32"}
 EXPORTED = ["fia_get_workspace_size", "fia_sparse_get_workspace_size",
             "fia_sparse_flash_mla_get_workspace_size", "fia_run", "fia_run_no_alloc",
             "fia_executor_destroy", "fia_last_error", "fia_executor_kind",
-            "fia_debug_gather_kv", "fia_debug_sparse_rows", "fia_peak_mfma_bf16",
+            "fia_debug_gather_kv", "fia_debug_read_kv", "fia_debug_sparse_rows", "fia_peak_mfma_bf16",
             "fia_peak_hbm_read"]
 
 
@@ -154,6 +154,8 @@ def lib():
     L.fia_executor_kind.argtypes = [vp]
     L.fia_debug_gather_kv.restype = ctypes.c_int
     L.fia_debug_gather_kv.argtypes = [vp, vp, sz, ctypes.c_int32, vp, vp]
+    L.fia_debug_read_kv.restype = ctypes.c_int
+    L.fia_debug_read_kv.argtypes = [vp, vp, sz, ctypes.c_int32, vp, ctypes.POINTER(ctypes.c_int64), vp]
     L.fia_debug_sparse_rows.restype = ctypes.c_int
     L.fia_debug_sparse_rows.argtypes = [vp, vp, sz, vp, vp, ctypes.POINTER(ctypes.c_int32), vp]
     L.fia_peak_mfma_bf16.restype = ctypes.c_int
@@ -337,6 +339,20 @@ class AttentionPlan(_Plan):
                                          self.workspace.numel(), which, dst.data_ptr(),
                                          _stream_handle(stream)))
         return dst
+
+    def read_kv(self, order, out=None, stream=None):
+        """fia_debug_read_kv: read every visible key / value row once in the
+        given order (0: per KV head, 1: whole token rows); returns the
+        per-workgroup XOR words (a uint32 tensor on the device, viewed as
+        int32)."""
+        n = ctypes.c_int64(0)
+        _check(lib().fia_debug_read_kv(self._exec, None, 0, order, None, ctypes.byref(n), None))
+        if out is None or out.numel() < n.value:
+            out = torch.empty(max(1, n.value), dtype=torch.int32, device=self.workspace.device)
+        n = ctypes.c_int64(out.numel())
+        _check(lib().fia_debug_read_kv(self._exec, self.workspace.data_ptr(), self.workspace.numel(),
+                                       order, out.data_ptr(), ctypes.byref(n), _stream_handle(stream)))
+        return out[: n.value]
 
 
 def fused_infer_attention_score(query, key, value, **kw):

@@ -458,12 +458,49 @@ def decode_component(ctx, case, key, workload, kernels, plan_kw=None, cpu=True):
            "ms": round(kern_ms, 5), "kernels": kernels,
            "tokens_per_s": round(case.q.shape[0] / (kern_ms / 1000.0), 1),
            "roofline": roofline("hbm", gbs, PEAK_HBM_GBS, "GB/s", measured_traffic(key))}
+    if plan_kw is None:
+        out["read_ceiling"] = read_ceiling(plan, case, kern_ms, ctx)
     if ctx.cpu and cpu:
         out["cpu_baseline"] = cpu_baseline(lambda: O.fia_case(case), nbytes, "GB/s",
                                            "whole passes of this decode workload (every batch and "
                                            "head), float64 numpy with materialised scores")
     del plan
     return out
+
+
+def read_ceiling(plan, case, kern_ms, ctx):
+    """The decode against a pure read of its own key / value rows
+    (fia_debug_read_kv): the same rows, block-table lookups and request sizes,
+    no arithmetic, timed back to back like the decode.  Order 0 reads one KV
+    head's row per request (the decode kernels' order), order 1 a token's
+    whole row of KV_N heads (where the pool keeps them adjacent)."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    res = {"how": "fia_debug_read_kv, back to back; kv_bytes = every visible key and value row once"}
+    L = case.actual_seq_lengths_kv
+    esz = 1 if getattr(case, "kv_quant", None) else 2
+    kv_bytes = sum(L) * case.num_kv_heads * case.q.shape[-1] * esz * 2
+    res["kv_bytes"] = kv_bytes
+    for order in (0, 1):
+        try:
+            out = plan.read_kv(order)
+        except Exception as e:   # no instantiation for this shape / layout
+            res[f"order{order}"] = f"n/a ({e.__class__.__name__})"
+            continue
+        n = min(ctx.steps, 20)
+        for _ in range(ctx.warmup):
+            plan.read_kv(order, out=out, stream=stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(n):
+            plan.read_kv(order, out=out, stream=stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / n
+        res[f"order{order}"] = {"ms": round(ms, 5), "gbs": round(kv_bytes / (ms / 1000.0) / 1e9, 1),
+                                "decode_vs_read": round(ms / kern_ms, 3)}
+    return res
 
 
 def comp_c3(ctx):

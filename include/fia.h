@@ -399,6 +399,23 @@ int32_t fia_executor_kind(const fia_executor* executor);
 fia_status fia_debug_gather_kv(fia_executor* executor, void* workspace, size_t workspace_size,
                                int32_t which, void* dst, void* stream);
 
+/* Measurement support: the read-rate ceiling of a split-KV decode plan's
+ * access pattern.  Reads every visible key and value row of the plan's
+ * chunks once, as the decode kernels would (16-byte non-temporal loads, the
+ * same block-table lookups), computes nothing but an XOR of the words read,
+ * and writes one uint32 per workgroup to out.
+ *   order 0: a workgroup per (chunk, KV head), one head's row (D * element
+ *            size bytes, 128 or 256) per request: the decode kernels' order.
+ *   order 1: a workgroup per (chunk, 128 keys), a token's whole row of KV_N
+ *            heads (1024 or 2048 contiguous bytes) per request; pools whose
+ *            heads of one token are adjacent (PA_ND, dense BSND).
+ * *out_len: in, the capacity of out (words); out, the number written.  With
+ * out == NULL only *out_len is set (to the number the call would write).
+ * PARAM_INVALID for executors other than a host-planned split-KV decode,
+ * UNSUPPORTED for shapes outside the two orders' sizes. */
+fia_status fia_debug_read_kv(fia_executor* executor, void* workspace, size_t workspace_size,
+                             int32_t order, uint32_t* out, int64_t* out_len, void* stream);
+
 /* Machine-peak probes, the measured roofline denominators beside the
  * published peaks (each returns after enqueueing on `stream`):
  *   fia_peak_mfma_bf16: n_workgroups x 4 waves, each running `iters`

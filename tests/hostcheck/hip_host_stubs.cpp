@@ -43,6 +43,7 @@ hipError_t launch_attn_fp32(const AttnArgs&, hipStream_t) { return hipErrorNoDev
 hipError_t launch_fill_empty(const AttnArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_sparse(const SparseArgs&, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_sparse_merge(const SparseArgs&, hipStream_t) { return hipErrorNoDevice; }
+hipError_t launch_decode_read(const AttnArgs&, int32_t, uint32_t*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_debug_gather(const AttnArgs&, int32_t, void*, int32_t, hipStream_t) {
   return hipErrorNoDevice;
 }

@@ -767,3 +767,64 @@ def test_device_kv_lengths_phase1():
     st, _, _, msg = plan(P(num_kv_heads=2, block_size=128, dev_lens=T((2,), i32), len_bound=1025),
                          qp, pool, pool, qp, bt=bt)
     assert st == BAD, msg
+
+
+def _executor(p, q, k, v, out, bt=None):
+    ws = ctypes.c_size_t(0)
+    ex = ctypes.c_void_p(None)
+    ptr = lambda d: ctypes.pointer(d) if d is not None else None
+    st = fia.lib().fia_get_workspace_size(ctypes.byref(p), ptr(q), ptr(k), ptr(v), None, None,
+                                          ptr(bt), ptr(out), None, ctypes.byref(ws), ctypes.byref(ex))
+    assert st == 0, fia.lib().fia_last_error().decode()
+    return ex
+
+
+def _read_len(ex, order):
+    n = ctypes.c_int64(-7)
+    st = fia.lib().fia_debug_read_kv(ex, None, 0, order, None, ctypes.byref(n), None)
+    return st, n.value
+
+
+def test_decode_read_probe_sizes():
+    """fia_debug_read_kv without an output only reports how many words it
+    would write (no device access): chunks x KV heads for order 0, chunks x 8
+    for order 1, and refuses shapes and executors it has no form for."""
+    lens = dict(actual_seq_lengths_kv=[1000, 2048, 3000])   # 1 + 2 + 3 chunks of 1024 keys
+    q, o = T((3, 1, 32, 128)), T((3, 1, 32, 128))
+    bt = T((3, 24), fia.DT_INT32)
+    ex = _executor(P(num_heads=32, num_kv_heads=4, block_size=128, **lens), q,
+                   T((80, 128, 4, 128)), T((80, 128, 4, 128)), o, bt=bt)
+    try:
+        assert _read_len(ex, 0) == (0, 6 * 4)
+        assert _read_len(ex, 1) == (0, 6 * 8)       # 4 heads x 256 B = 1 KB token rows
+        assert _read_len(ex, 2)[0] == BAD
+        assert fia.lib().fia_debug_read_kv(ex, None, 0, 0, None, None, None) == fia.FIA_ERR_NULLPTR
+        small = ctypes.c_int64(3)
+        assert fia.lib().fia_debug_read_kv(ex, None, 0, 0, ctypes.c_void_p(16), ctypes.byref(small),
+                                           None) == BAD
+    finally:
+        fia.lib().fia_executor_destroy(ex)
+    # BnNBsD: a head's rows are contiguous, a token's heads are not
+    ex = _executor(P(num_heads=32, num_kv_heads=4, block_size=128, kv_layout="BnNBsD", **lens), q,
+                   T((80, 4, 128, 128)), T((80, 4, 128, 128)), o, bt=bt)
+    try:
+        assert _read_len(ex, 0) == (0, 6 * 4)
+        assert _read_len(ex, 1)[0] == UNS
+    finally:
+        fia.lib().fia_executor_destroy(ex)
+    # D = 64 bf16: 128-byte head rows, 512-byte token rows (order 1 has no form)
+    q64, o64 = T((3, 1, 32, 64)), T((3, 1, 32, 64))
+    ex = _executor(P(num_heads=32, num_kv_heads=4, block_size=128, **lens), q64,
+                   T((80, 128, 4, 64)), T((80, 128, 4, 64)), o64, bt=bt)
+    try:
+        assert _read_len(ex, 0) == (0, 6 * 4)
+        assert _read_len(ex, 1)[0] == UNS
+    finally:
+        fia.lib().fia_executor_destroy(ex)
+    # not a decode executor
+    qp, kp, vp, op = dense()
+    ex = _executor(P(num_kv_heads=2, sparse_mode=3), qp, kp, vp, op)
+    try:
+        assert _read_len(ex, 0)[0] == BAD
+    finally:
+        fia.lib().fia_executor_destroy(ex)

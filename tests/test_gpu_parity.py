@@ -792,6 +792,23 @@ def test_paged_gather_is_bit_exact():
             assert np.array_equal(got[b, :L], want), (which, b)
 
 
+def test_paged_gather_of_fake_quant_codes_is_bit_exact():
+    """One-byte key / value codes are gathered as bytes (the row of a code is
+    D bytes long), through the same row-address function."""
+    case = W.with_kv_quant(W.paged_decode_case("gq", 505, B=2, Q_N=8, KV_N=2, D=128,
+                                               kv_lens=[77, 700], block_size=32, poison_tail=True),
+                           506, kind="int8", kmode=1, vmode=1, offsets=True)
+    plan = TI.dense_plan(case, DEV)
+    s2 = max(case.actual_seq_lengths_kv)
+    for which, pool in ((0, case.k_pool), (1, case.v_pool)):
+        got = plan.debug_gather(which, s2)
+        torch.cuda.synchronize()
+        got = got.cpu().numpy().view(np.uint8)
+        for b, L in enumerate(case.actual_seq_lengths_kv):
+            want = O.gather_paged(pool, case.block_table[b], L, 32).view(np.uint8)
+            assert np.array_equal(got[b, :L], want), (which, b)
+
+
 def test_sparse_row_selection_is_bit_exact():
     case = W.sparse_case("sr", 510, B=3, N1=64, seqused_kv=[5, 300, 4000], K2=512, n_valid=100,
                          block_size1=32, block_size2=16, materialise_all_ori=False)
@@ -895,3 +912,29 @@ def test_sparse_batch_invariance():
                                   sub["cmp_block_table"], sub["seqused_kv"], sub["sinks"],
                                   softmax_scale=case.softmax_scale, max_seqused_kv=600))
     assert torch.equal(one.out[0], full.out[1])
+
+
+@pytest.mark.parametrize("kind", ["bf16", "int8", "bf16_bnnbsd"])
+def test_decode_read_probe_reads_exactly_the_visible_rows(kind):
+    """fia_debug_read_kv (the access-pattern read ceiling the benchmark
+    reports) reads every visible key and value row once and nothing else:
+    the XOR of the words it read, in either order, equals the XOR of the
+    visible rows gathered on the host (tail slots past each length hold NaN)."""
+    case = W.paged_decode_case("rdp", 470, B=3, Q_N=32, KV_N=8, D=128, kv_lens=[1, 1500, 3000],
+                               block_size=128, lse=True, poison_tail=True)
+    if kind == "int8":
+        case = W.with_kv_quant(case, 471, kind="int8", kmode=1, vmode=1, offsets=True)
+    if kind.endswith("bnnbsd"):
+        case = W.as_bnnbsd(case)
+    want = np.uint32(0)
+    for pool in (case.k_pool, case.v_pool):
+        for b, L in enumerate(case.actual_seq_lengths_kv):
+            rows = O.gather_paged(pool, case.block_table[b], L, case.block_size, case.kv_layout)
+            want ^= np.bitwise_xor.reduce(np.ascontiguousarray(rows).view(np.uint32), axis=None)
+    plan = TI.dense_plan(case, DEV)
+    orders = [0] if kind.endswith("bnnbsd") else [0, 1]
+    for order in orders:
+        words = plan.read_kv(order)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(words.cpu().numpy().view(np.uint32), axis=None)
+        assert got == want, (order, hex(int(got)), hex(int(want)))
