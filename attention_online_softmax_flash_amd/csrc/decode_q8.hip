@@ -32,12 +32,28 @@ namespace {
 
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
-// Element i of a per-channel scale / offset (bf16 or fp32; one element for
-// the whole tensor when `scalar`), 0 without a tensor.
-__device__ __forceinline__ float chan_val(const void* p, int is_f32, int scalar, int i) {
-  if (p == nullptr) return 0.f;
-  const int k = scalar ? 0 : i;
-  return is_f32 ? static_cast<const float*>(p)[k] : bf16_to_f32(static_cast<const uint16_t*>(p)[k]);
+// Elements i0 .. i0 + N - 1 of a per-channel scale / offset table (bf16 or
+// fp32; every element is element 0 when `scalar`; zero without a table),
+// every load issued before any is used: one trip to memory.  `count` is the
+// table's element count (KV_N * D, or 1 when scalar).
+template <int N>
+__device__ __forceinline__ void chan_run(const void* p, int is_f32, int scalar, int64_t count, int i0,
+                                         float (&out)[N]) {
+  const uint32_t esz = is_f32 ? 4u : 2u;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(p, p != nullptr ? (uint32_t)(count * esz) : 0u);
+  if (is_f32) {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint32_t i = scalar ? 0u : (uint32_t)(i0 + k);
+      out[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, i * 4u, 0, 0));
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+      const uint32_t i = scalar ? 0u : (uint32_t)(i0 + k);
+      out[k] = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, i * 2u, 0, 0));
+    }
+  }
 }
 
 // Byte K of the 4-byte word w as a float (int8 or e4m3fn code, exact).
@@ -136,6 +152,14 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
                        (int64_t)h * a.q_sh + KB * g;
   float qf[KB];
   float qc = 0.f;
+  // Key per channel: the lane's KB scales and offsets (channels kvh D +
+  // KB g ..), all requested together.
+  float kcs[KPT ? 1 : KB], kco[KPT ? 1 : KB];
+  if constexpr (!KPT) {
+    const int64_t cnt = a.kq_scalar ? 1 : (int64_t)a.KVn * D;
+    chan_run(a.kq_scale, a.kq_f32, a.kq_scalar, cnt, kvh * D + KB * g, kcs);
+    chan_run(a.kq_off, a.kq_f32, a.kq_scalar, cnt, kvh * D + KB * g, kco);
+  }
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
     const u32x4 raw = hvalid ? ld16(qp + 8 * cc) : u32x4{0, 0, 0, 0};
@@ -147,9 +171,8 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
         qf[8 * cc + e] = qd;
         qc += qd;
       } else {
-        const int ch = kvh * D + KB * g + 8 * cc + e;
-        qf[8 * cc + e] = qd * chan_val(a.kq_scale, a.kq_f32, a.kq_scalar, ch);
-        qc += qf[8 * cc + e] * chan_val(a.kq_off, a.kq_f32, a.kq_scalar, ch);
+        qf[8 * cc + e] = qd * kcs[8 * cc + e];
+        qc += qf[8 * cc + e] * kco[8 * cc + e];
       }
     }
   }
@@ -491,6 +514,14 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   const float inv = any ? 1.f / L : 0.f;
   const float lse2 = any ? M + fast_log2(L) : kNegInf;
   float val[PER];
+  // Value per channel: this thread's PER scales and offsets, requested
+  // together.
+  float vcs[VPT ? 1 : PER], vco[VPT ? 1 : PER];
+  if constexpr (!VPT) {
+    const int64_t cnt = a.vq_scalar ? 1 : (int64_t)a.KVn * D;
+    chan_run(a.vq_scale, a.vq_f32, a.vq_scalar, cnt, kvh * D + d0, vcs);
+    chan_run(a.vq_off, a.vq_f32, a.vq_scalar, cnt, kvh * D + d0, vco);
+  }
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
     float s = 0.f;
@@ -499,10 +530,7 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
     if constexpr (VPT) {
       val[u] = (s + T) * inv;
     } else {
-      const int ch = kvh * D + d0 + u;
-      val[u] = any ? chan_val(a.vq_scale, a.vq_f32, a.vq_scalar, ch) *
-                         (s * inv + chan_val(a.vq_off, a.vq_f32, a.vq_scalar, ch))
-                   : 0.f;
+      val[u] = any ? vcs[u] * (s * inv + vco[u]) : 0.f;
     }
   }
   if (nchunk == 1) {
