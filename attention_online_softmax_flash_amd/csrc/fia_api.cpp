@@ -920,8 +920,15 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     for (int64_t b = 0; b < B; ++b) {
       const int64_t rows = tnd ? qlen[b] : cq.S;
       const int64_t nqt = (rows + fia::kPrefillRows - 1) / fia::kPrefillRows;
-      for (int64_t qt = 0; qt < nqt; ++qt) {
+      // Padded layouts: the tiles wholly past the actual query length get
+      // no item; item qt of the nl live tiles (at least one) also writes the
+      // rows of tiles nl + qt, nl + qt + nl, ... (zeros, LSE +inf).
+      const int64_t nl = tnd ? nqt
+                             : std::min(nqt, std::max<int64_t>(
+                                                 (qlen[b] + fia::kPrefillRows - 1) / fia::kPrefillRows, 1));
+      for (int64_t qt = 0; qt < nl; ++qt) {
         int64_t cost = 0;
+        if (!tnd && nl + qt < nqt) cost += ((nqt - 1 - (nl + qt)) / nl + 1 + 3) / 4;
         const int64_t i0 = qt * fia::kPrefillRows;
         const int64_t i1 = std::min(i0 + fia::kPrefillRows, qlen[b]);
         if (i1 > i0) {
@@ -929,7 +936,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
           visible(mode, i0, qlen[b], kvlen[b], p->pre_tokens, p->next_tokens, &l0, &h0);
           visible(mode, i1 - 1, qlen[b], kvlen[b], p->pre_tokens, p->next_tokens, &l1, &h1);
           if (h1 > l0) {
-            cost = (h1 + fia::kPrefillKeys - 1) / fia::kPrefillKeys - l0 / fia::kPrefillKeys;
+            cost += (h1 + fia::kPrefillKeys - 1) / fia::kPrefillKeys - l0 / fia::kPrefillKeys;
           }
         }
         for (int64_t h = 0; h < Qn; ++h) items.push_back({cost, (int32_t)b, (int32_t)h, (int32_t)qt});

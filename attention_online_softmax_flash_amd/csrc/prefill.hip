@@ -583,6 +583,30 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           has ? (m_run + fast_log2(l_tot)) * kLn2 : kPosInf;
     }
   }
+
+  // Padded query layouts: tiles wholly past the actual query length get no
+  // work item; the items of the live tiles write their rows (0, LSE +inf),
+  // item qt taking tiles nl + qt, nl + qt + nl, ... (nl live tiles, at
+  // least 1).
+  if (!a.tnd) {
+    const int nqt = (a.Sq + BM - 1) / BM;
+    const int nl = max((Lq + BM - 1) / BM, 1);
+    const int dp = tid % DCH;
+    for (int t = nl + qt; t < nqt; t += nl) {
+#pragma unroll
+      for (int r0 = 0; r0 < BM; r0 += 256 / DCH) {
+        const int row = t * BM + r0 + tid / DCH;
+        if (row < a.Sq) {
+          uint16_t* op = (uint16_t*)a.o + (int64_t)b * a.o_sb + (int64_t)row * a.o_ss +
+                         (int64_t)h * a.o_sh + 8 * dp;
+          st16(op, u32x4{0u, 0u, 0u, 0u});
+          if (a.write_lse && dp == 0) {
+            a.lse[(int64_t)b * a.lse_sb + (int64_t)h * a.lse_sh + (int64_t)row * a.lse_ss] = kPosInf;
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int D, bool ALIBI, int KVM>

@@ -145,6 +145,33 @@ def test_prefill_other_layouts(layout):
     check_lse(to_f64(plan.lse)[..., 0], ref_l)
 
 
+@pytest.mark.parametrize("D,layout", [(64, "BSND"), (128, "BSND"), (128, "BNSD")])
+def test_prefill_padded_tiles_are_written(D, layout):
+    """Query tiles wholly past the actual length get no work item of their
+    own; the live tiles' items write them.  Outputs start as NaN, so a row
+    nobody writes fails; S1 = 1000 leaves a partial last tile and batch 1
+    (length 130) has 2 live tiles for 6 padded ones."""
+    case = W.dense_case("padtiles", 145, B=3, S1=1000, S2=900, Q_N=4, KV_N=2, D=D,
+                        sparse_mode=3, q_lens=[0, 130, 999], kv_lens=[50, 900, 777], lse=True,
+                        poison_pad=True)
+    q, k, v, bt, slopes = TI.dense_tensors(case, DEV)
+    if layout == "BNSD":
+        q, k, v = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full((3, 4, 1000, 1), float("nan"), dtype=torch.float32, device=DEV)
+    plan = run_plan(fia.AttentionPlan(q, k, v, num_heads=4, num_key_value_heads=2,
+                                      scale_value=case.scale, input_layout=layout,
+                                      sparse_mode=3, softmax_lse_flag=True,
+                                      actual_seq_lengths=[0, 130, 999],
+                                      actual_seq_lengths_kv=[50, 900, 777],
+                                      attention_out=out, softmax_lse=lse))
+    assert plan.kind == "prefill"
+    got = plan.out.permute(0, 2, 1, 3) if layout == "BNSD" else plan.out
+    ref_o, ref_l = O.fia_case(case)
+    check_out(to_f64(got), ref_o)
+    check_lse(to_f64(plan.lse)[..., 0], ref_l)
+
+
 def test_prefill_tnd():
     case = W.tnd_case("tnd", 140, q_lens=[100, 0, 257, 1], kv_lens=[100, 3, 300, 50],
                       Q_N=8, KV_N=4, D=128, sparse_mode=3, lse=True)
