@@ -92,7 +92,8 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   constexpr bool DMA_K = KVM != 2;
   // PIPE: the score product of tile t+1 is issued together with the softmax
   // of tile t (needs a second score buffer; too many registers with the ALiBi
-  // bias or per-row paging, which compute each tile's scores up front).
+  // bias, mask / bias tensors or per-row paging, which compute each tile's
+  // scores up front).
   constexpr bool PIPE = !ALIBI && !EXT && KVM != 2;
   constexpr bool INTERLEAVE = PIPE;
   __shared__ __attribute__((aligned(16))) uint8_t lds_k0[L::BYTES];
@@ -155,10 +156,20 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     u32x4 qreg[NQ];
     const uint16_t* qp = (const uint16_t*)a.q + (int64_t)b * a.q_sb +
                          (int64_t)(q_off + i) * a.q_ss + (int64_t)h * a.q_sh + 8 * hh;
+    // ALiBi enters through the initial value of the score accumulators,
+    // slope ((kv_start + j) - (q_start + i)) / scale, so that the scaled
+    // score q.k scale + bias comes out of the product; the softmax is then
+    // the plain one.  With scale 0 the score is the bias alone: the query
+    // operand is zero and the accumulators start at the bias in log2 units
+    // (scaled by 1).
+    const bool alibi_s0 = ALIBI && !(a.scale_log2 > 0.f);
+    const float scl = alibi_s0 ? 1.f : a.scale_log2;
+    const float c_al = ALIBI ? (alibi_s0 ? a.slopes[h] * kLog2e : a.slopes[h] / a.scale) : 0.f;
 #pragma unroll
-    for (int c = 0; c < NQ; ++c) qreg[c] = row_live ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
+    for (int c = 0; c < NQ; ++c) {
+      qreg[c] = (row_live && !alibi_s0) ? ld16(qp + 16 * c) : u32x4{0, 0, 0, 0};
+    }
 
-    const float c_al = ALIBI ? a.slopes[h] * kLog2e : 0.f;
     // Explicit mask and bias rows of this lane's query row (rows past Q_S
     // are dead; their index is clamped into the tensor).
     const bool has_mask = EXT && a.mask != nullptr;
@@ -308,17 +319,27 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       }
     };
 
-    // Score accumulators of tile kt with the mask and bias folded in (from
-    // the mask words / bias values loaded by load_ext).
-    auto init_ext = [&](f32x16* sv) FIA_INLINE {
+    // Initial score accumulators of tile kt: the mask and bias tensors
+    // (from the mask words / bias values loaded by load_ext) and the ALiBi
+    // bias.  Accumulator r of key block k2 holds key 32 k2 + 8 (r / 4) +
+    // r % 4 of the lane's 4 hh group; the ALiBi term is an fma with that
+    // constant offset (an fma is not split, so no 32 loop-invariant products
+    // are kept in registers).
+    auto init_acc = [&](int kt, f32x16* sv) FIA_INLINE {
+      const float cb = ALIBI ? c_al * (float)(kt * BN + 4 * hh - i + a.alibi_delta) : 0.f;
 #pragma unroll
       for (int k2 = 0; k2 < 2; ++k2) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const uint32_t pv = pw[4 * k2 + (r >> 2)][(r >> 1) & 1];
-          const float bias = __builtin_bit_cast(float, (r & 1) ? (pv & 0xffff0000u) : (pv << 16));
-          const bool off = ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) != 0u;
-          sv[k2][r] = off ? kNegInf : bias * inv_scale;
+          float x = 0.f;
+          if constexpr (ALIBI) x = __builtin_fmaf(c_al, (float)(32 * k2 + 8 * (r >> 2) + (r & 3)), cb);
+          if constexpr (EXT) {
+            const uint32_t pv = pw[4 * k2 + (r >> 2)][(r >> 1) & 1];
+            const float bias = __builtin_bit_cast(float, (r & 1) ? (pv & 0xffff0000u) : (pv << 16));
+            const bool off = ((mw[4 * k2 + (r >> 2)] >> (8 * (r & 3))) & 0xffu) != 0u;
+            x = off ? kNegInf : __builtin_fmaf(bias, inv_scale, x);
+          }
+          sv[k2][r] = x;
         }
       }
     };
@@ -340,6 +361,15 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         }
       }
     };
+    // Scores of tile kt into sv (keys in stage kst).
+    auto scores = [&](int kt, const uint8_t* kst, f32x16* sv) FIA_INLINE {
+      if constexpr (ALIBI || EXT) {
+        init_acc(kt, sv);
+        compute_s(std::true_type{}, kst, sv);
+      } else {
+        compute_s(std::false_type{}, kst, sv);
+      }
+    };
     auto wave_skip = [&](int kt) FIA_INLINE {
       const int j0 = kt * BN;
       return (wrows_end <= iw0) || (j0 + BN <= wlo_min) || (j0 >= whi_max);
@@ -353,7 +383,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
                          auto next_tag, const uint8_t* knx, f32x16* sn) FIA_INLINE {
       constexpr bool MASKED = decltype(masked_tag)::value;
       constexpr bool DO_NEXT = decltype(next_tag)::value;
-      constexpr bool PLAIN = !ALIBI && !MASKED;
+      constexpr bool PLAIN = !MASKED;
       const int j0 = kt * BN;
       float mx = kNegInf;
       if constexpr (PLAIN) {
@@ -362,13 +392,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[k2][r]);
         }
-        mx *= a.scale_log2;
+        mx *= scl;
       } else {
         const int jb = j0 + 4 * hh;
-        // ALiBi distance (kv_start + j) - (q_start + i) = base + koff.  The bias
-        // is c_al * (base + koff), not c_al * base + c_al * koff, so no
-        // loop-invariant products need registers.
-        const float base = (float)(jb - i + a.alibi_delta);
         // visible iff rel_lo <= koff < rel_hi, tested as one unsigned compare
         const uint32_t nlo = (uint32_t)(jb - my_lo);
         const uint32_t span = (uint32_t)(my_hi - my_lo);
@@ -377,8 +403,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int koff = 32 * k2 + 8 * (r >> 2) + (r & 3);
-            float x = ALIBI ? __builtin_fmaf(sc[k2][r], a.scale_log2, c_al * (base + (float)koff))
-                            : sc[k2][r] * a.scale_log2;
+            float x = sc[k2][r] * scl;
             if constexpr (MASKED) {
               bool keep = (uint32_t)koff + nlo < span;
               if constexpr (EXT) keep = keep && sc[k2][r] != kNegInf;   // masked-out key
@@ -407,7 +432,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       // VALU work of the other wave on the SIMD.
       __builtin_amdgcn_s_setprio(1);
       if constexpr (PIPE) {
-        if constexpr (DO_NEXT) compute_s(std::false_type{}, knx, sn);
+        if constexpr (DO_NEXT) scores(kt + 1, knx, sn);
       }
       float psum = 0.f;
       u32x4 pb[4];
@@ -418,7 +443,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         float p[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-          p[t] = PLAIN ? fast_exp2(__builtin_fmaf(sc[k2][rb + t], a.scale_log2, -m_sub))
+          p[t] = PLAIN ? fast_exp2(__builtin_fmaf(sc[k2][rb + t], scl, -m_sub))
                        : fast_exp2(sc[k2][rb + t] - m_sub);
           psum += p[t];
         }
@@ -477,7 +502,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
     }
     f32x16 s_a[2], s_b[2];
     bool cur_skip = wave_skip(kt0);
-    if (PIPE && !cur_skip) compute_s(std::false_type{}, lds_k0, s_a);
+    if (PIPE && !cur_skip) scores(kt0, lds_k0, s_a);
     if (EXT && !cur_skip) load_ext(kt0);
     if (PIPE) __syncthreads();   // step kt0 refills lds_k0
 
@@ -504,14 +529,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
       // itself (not through a pointer chosen at run time), so the compiler
       // sees that they cannot alias this step's buffer-to-LDS loads.
       const bool do_next = PIPE && !next_skip;
-      if constexpr (EXT) {
-        if (!cur_skip) {
-          init_ext(sc);
-          compute_s(std::true_type{}, kst, sc);
-        }
-      } else if (!PIPE && !cur_skip) {
-        compute_s(std::false_type{}, kst, sc);
-      }
+      if (!PIPE && !cur_skip) scores(kt, kst, sc);
       if (!cur_skip) {
         const int j0 = kt * BN;
         // Tiles inside every row's visible range skip the per-element test;
@@ -521,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
         // form -inf * 0 = NaN, so such calls keep the per-element test, which
         // replaces a masked key's score by -inf after scaling.
         const bool need_mask = !(j0 >= wlo_max && j0 + BN <= whi_min) ||
-                               (EXT && !(a.scale_log2 > 0.f));
+                               (EXT && !(scl > 0.f));
         if (need_mask) {
           if (do_next) {
             tile_body(std::true_type{}, kt, vst, sc, std::true_type{}, knx, sn);
@@ -536,7 +554,7 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           }
         }
       } else if (do_next) {
-        compute_s(std::false_type{}, knx, sn);
+        scores(kt + 1, knx, sn);
       }
       cur_skip = next_skip;
       barrier_after_loads();   // this step's loads landed; every wave is done with tile kt

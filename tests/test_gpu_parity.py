@@ -127,6 +127,37 @@ def test_prefill_alibi_start_offsets():
     dense_parity(case, "prefill")
 
 
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_alibi_scale_zero(D):
+    # scale_value 0 with ALiBi: every score is its bias alone.
+    case = W.dense_case(f"als0_{D}", 125 + D, B=2, S1=260, S2=260, Q_N=4, KV_N=2, D=D,
+                        scale=0.0, sparse_mode=3, alibi=True, q_lens=[260, 70],
+                        kv_lens=[260, 70], lse=True, poison_pad=True)
+    dense_parity(case, "prefill")
+
+
+@pytest.mark.parametrize("scale", [None, 0.0])
+def test_prefill_alibi_with_mask(scale):
+    # ALiBi together with an explicit mask tensor (both in the score
+    # accumulators' initial value), a fully masked row included.
+    case = W.dense_case("almask", 127, B=2, S1=200, S2=200, Q_N=4, KV_N=4, D=128, scale=scale,
+                        alibi=True, q_lens=[200, 150], kv_lens=[200, 150], lse=True,
+                        poison_pad=True)
+    case = W.with_random_mask(case, 128, p_masked=0.2, dead_rows=(3,))
+    dense_parity(case, "prefill")
+
+
+@pytest.mark.parametrize("bs", [32, 128])
+def test_prefill_alibi_paged(bs):
+    # ALiBi over a paged cache: whole-tile pages (128) and per-row lookups (32).
+    case = W.paged_decode_case("alpg", 129, B=2, Q_N=8, KV_N=2, D=128, kv_lens=[200, 131],
+                               block_size=bs, S1=200, sparse_mode=3, lse=True, poison_tail=True,
+                               extra_blocks=2)
+    case.actual_seq_lengths = [200, 131]   # ALiBi: query and key lengths agree
+    case.alibi_slopes = W.alibi_slopes(8)
+    dense_parity(case, "prefill")
+
+
 @pytest.mark.parametrize("layout", ["BNSD", "BSH"])
 def test_prefill_other_layouts(layout):
     case = W.dense_case("lay", 130, B=2, S1=150, S2=150, Q_N=8, KV_N=2, D=128, sparse_mode=3,
