@@ -14,14 +14,16 @@
 // With queries on the MFMA column axis, lane l owns query row l%32 of its
 // wave: its running max and sum live in that lane plus its partner l^32, so a
 // row reduction is one cross-lane step.  The key order inside each 16-key
-// k-step follows the accumulator layout of S^T; V^T is read from LDS in the
-// same order, so P needs no shuffling.  V is transposed into LDS on the way in.
+// k-step follows the accumulator layout of S^T; V^T is read from the
+// row-major value tile in LDS in the same order by transposing 8-byte LDS
+// reads, so P needs no shuffling.
 //
 // Masks (aclnnFusedInferAttentionScoreV5 Attention Mask group): per query row
 // i the visible keys are [lo(i), hi(i)); tiles wholly inside every row's range
 // of a wave skip the per-element test, tiles outside are skipped.  ALiBi
 // (pse type 2) adds slope * ((kv_start + j) - (q_start + i)) after scaling
-// (aclnnFusedInferAttentionScoreV4 formula).  Rows with no visible key and
+// (aclnnFusedInferAttentionScoreV4 formula); it enters the score product as
+// the accumulators' initial value.  Rows with no visible key and
 // rows past the actual query length are written as 0 with LSE +inf.
 #include <type_traits>
 
@@ -70,10 +72,10 @@ __device__ __forceinline__ int val_swz(int r) {
 // block_size a multiple of 64 (a tile lies in one page, one table lookup per
 // tile), 2 any paged layout (per-row lookup).
 //
-// Key tiles go global -> LDS by buffer-to-LDS loads (KVM 0 / 1) or through
-// registers (KVM 2); value tiles go through registers, transposed on the way
-// in.  Each stage is its own LDS array, so the compiler's wait for an
-// outstanding buffer-to-LDS load only guards reads of that stage.
+// Key and value tiles go global -> LDS by buffer-to-LDS loads (KVM 0 / 1) or
+// through registers (KVM 2), row-major with an XOR swizzle.  Each stage is
+// its own LDS array, so the compiler's wait for an outstanding buffer-to-LDS
+// load only guards reads of that stage.
 //
 // EXT: an explicit mask tensor (modes 0 / 1) and / or a bias tensor (pse
 // type 0).  Both enter through the
