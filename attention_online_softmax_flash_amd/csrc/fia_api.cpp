@@ -818,7 +818,7 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     if (!(max_q <= 1 && cq.S == 1)) {
       return fail(FIA_ERR_PARAM_INVALID, "actual_seq_lengths_kv_device needs query length 1 (decode)");
     }
-    if (f32 || kvq) return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device needs bf16 query, key and value");
+    if (f32) return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device needs a bf16 query (fp32 is not taken)");
     if (explicit_mask || pse_tensor) {
       return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device does not take atten_mask or pse_shift tensors");
     }

@@ -173,8 +173,9 @@ typedef struct {
    * [0, max_actual_seq_length_kv]; the bound (host, >= 0) sizes the grid and
    * the workspace and must fit the key extent (KV_S, or block_table cols *
    * block_size).  Requires actual_seq_lengths_kv == NULL, query length 1
-   * (BSND / BSH / BNSD, no TND), a bf16 query with bf16 key / value, and no
-   * atten_mask or pse_shift tensor (PARAM_INVALID / UNSUPPORTED otherwise).
+   * (BSND / BSH / BNSD, no TND), a bf16 query with bf16 or fake-quantised
+   * (int8 / e4m3fn) key / value, and no atten_mask or pse_shift tensor
+   * (PARAM_INVALID / UNSUPPORTED otherwise).
    * Results equal those of the host-planned executor for the same lengths,
    * bit for bit.  NULL: lengths from actual_seq_lengths_kv as above. */
   const fia_tensor* actual_seq_lengths_kv_device;

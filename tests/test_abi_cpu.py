@@ -445,6 +445,12 @@ def test_fake_quant_kv_rules():
     st, kind, _, msg = plan(P(num_kv_heads=KVN, block_size=32, actual_seq_lengths_kv=[30, 40], **good), q,
                             pool, pool, o, bt=T((B, 4), fia.DT_INT32))
     assert st == 0 and kind == "decode", msg
+    # KV lengths on the device: per-channel and per-token tables (the tables
+    # cover the padded S2, so any length up to the bound reads inside them)
+    dl = dict(dev_lens=T((B,), fia.DT_INT32), len_bound=300)
+    for kv, kw in ((k8, good), (f8, dict(kmode=1, vmode=1, key_antiquant_scale=tok(), value_antiquant_scale=tok()))):
+        st, kind, ws, msg = plan(P(num_kv_heads=KVN, **dl, **kw), q, kv, kv, o)
+        assert st == 0 and kind == "decode" and ws > 0, msg
 
 
 def test_tnd_rules():

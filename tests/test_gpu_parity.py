@@ -712,8 +712,9 @@ def _dev_len_plan(case, lens_dev, bound, **kw):
                              sparse_mode=case.sparse_mode, pre_tokens=case.pre_tokens,
                              next_tokens=case.next_tokens, block_table=bt,
                              block_size=case.block_size if bt is not None else 0,
-                             softmax_lse_flag=case.lse, actual_seq_lengths_kv_device=lens_dev,
-                             max_actual_seq_length_kv=bound, **kw)
+                             kv_layout=case.kv_layout, softmax_lse_flag=case.lse,
+                             actual_seq_lengths_kv_device=lens_dev, max_actual_seq_length_kv=bound,
+                             **TI.antiquant_kwargs(case, DEV), **kw)
 
 
 DEV_LEN_CASES = [
@@ -799,6 +800,54 @@ def test_decode_device_lengths_dense_kv(i):
     check_out(out, ref_o)
     if lse:
         check_lse(lse_v, ref_l)
+
+
+DEV_LEN_QUANT_CASES = [
+    # (kind, kmode, vmode, offsets, builder(kv_lens))
+    ("int8", 1, 1, True,
+     lambda kl: W.paged_decode_case("dlq0", 520, B=4, Q_N=32, KV_N=8, D=128, kv_lens=kl,
+                                    block_size=128, lse=True)),
+    ("fp8", 0, 0, False,
+     lambda kl: W.as_bnnbsd(W.paged_decode_case("dlq1", 521, B=4, Q_N=16, KV_N=4, D=128,
+                                                kv_lens=kl, block_size=64, lse=True))),
+    ("int8", 0, 1, True,
+     lambda kl: W.dense_case("dlq2", 522, B=4, S1=1, S2=3000, Q_N=8, KV_N=2, D=64, kv_lens=kl,
+                             lse=True)),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DEV_LEN_QUANT_CASES)))
+def test_decode_fake_quant_device_lengths(i):
+    """Fake-quantised key / value with device-resident lengths: equal to the
+    host-planned run bit for bit and to the oracle, then again after the
+    lengths change on the device (zero, one, the bound and one past it)."""
+    kind, km, vm, off, build = DEV_LEN_QUANT_CASES[i]
+    lens = [1, 700, 2999, 129]
+    lens2 = [3000, 0, 1, 3001]
+    bound = 3000
+    alloc = [max(a, min(b, bound)) for a, b in zip(lens, lens2)]
+    base = W.with_kv_quant(build(alloc), 530 + i, kind=kind, kmode=km, vmode=vm, offsets=off)
+    case = dataclasses.replace(base, actual_seq_lengths_kv=lens)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    plan = run_plan(_dev_len_plan(case, lens_dev, bound))
+    assert plan.kind == "decode"
+    host = run_plan(TI.dense_plan(case, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host.out.view(torch.int16))
+    assert torch.equal(plan.lse, host.lse)
+    out, lse = gpu_results(plan)
+    ref_o, ref_l = O.fia_case(case)
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+    lens_dev.copy_(torch.tensor(lens2, dtype=torch.int32))
+    run_plan(plan)
+    case2 = dataclasses.replace(base, actual_seq_lengths_kv=[min(x, bound) for x in lens2])
+    host2 = run_plan(TI.dense_plan(case2, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host2.out.view(torch.int16))
+    assert torch.equal(plan.lse, host2.lse)
+    out2, lse2 = gpu_results(plan)
+    ref_o2, ref_l2 = O.fia_case(case2)
+    check_out(out2, ref_o2)
+    check_lse(lse2, ref_l2)
 
 
 def test_decode_device_lengths_graph_replay():
