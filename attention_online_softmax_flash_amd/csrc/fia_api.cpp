@@ -377,6 +377,10 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
       return fail(FIA_ERR_PARAM_INVALID, "give actual_seq_lengths_kv or actual_seq_lengths_kv_device, not both");
     }
     if (tnd) return fail(FIA_ERR_PARAM_INVALID, "actual_seq_lengths_kv_device is not supported with TND");
+    if (p->pse_type == 2) {
+      return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device does not take ALiBi (its equal-length "
+                                       "rule cannot be checked on the host)");
+    }
     if (len_bound < 0 || len_bound > kMaxLen) {
       return fail(FIA_ERR_PARAM_INVALID, "max_actual_seq_length_kv must be in [0, 20971520]");
     }
@@ -815,9 +819,6 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
 
   // Build the executor.
   if (dev_len) {
-    if (!(max_q <= 1 && cq.S == 1)) {
-      return fail(FIA_ERR_PARAM_INVALID, "actual_seq_lengths_kv_device needs query length 1 (decode)");
-    }
     if (f32) return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device needs a bf16 query (fp32 is not taken)");
     if (explicit_mask || pse_tensor) {
       return fail(FIA_ERR_UNSUPPORTED, "actual_seq_lengths_kv_device does not take atten_mask or pse_shift tensors");
@@ -915,6 +916,13 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
   }
 
   if (e->kind == KIND_PREFILL) {
+    if (dev_len) {
+      // KV lengths on the device: the items are planned (and costed) for the
+      // bound; the kernel reads each entry's length, clamped into
+      // [0, bound], and derives its visible key ranges from it.
+      a.dev_kvlen = static_cast<const int32_t*>(p->actual_seq_lengths_kv_device->data);
+      a.kvlen_bound = (int32_t)len_bound;
+    }
     struct Item { int64_t cost; int32_t b, h, qt; };
     std::vector<Item> items;
     for (int64_t b = 0; b < B; ++b) {

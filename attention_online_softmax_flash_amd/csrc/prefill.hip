@@ -116,7 +116,9 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
   const int qt = w1 >> 8;
   const int kvh = h / a.G;
   const int32_t* bm = a.meta + (int64_t)b * BF_COUNT;
-  const int Lq = bm[BF_QLEN], Lk = bm[BF_KVLEN];
+  const int Lq = bm[BF_QLEN];
+  // Key length: the plan's, or read on the device and clamped into [0, bound].
+  const int Lk = a.dev_kvlen != nullptr ? min(max(a.dev_kvlen[b], 0), a.kvlen_bound) : bm[BF_KVLEN];
   const int q_off = bm[BF_QOFF], kv_off = bm[BF_KVOFF];
   const int write_rows = a.tnd ? Lq : a.Sq;
 

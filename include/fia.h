@@ -162,20 +162,23 @@ typedef struct {
   const fia_tensor* value_antiquant_scale;
   const fia_tensor* key_antiquant_offset;
   const fia_tensor* value_antiquant_offset;
-  /* KV lengths resident on the device (incremental decode only; the SharedKV
-   * and sparse_flash_mla metadata operators likewise balance the work on the
-   * device before the main kernels): int32 [B], contiguous, device memory,
-   * read at run time by a partitioner kernel that writes the per-batch
-   * records and the split-KV chunk list into the workspace.  A caller whose
+  /* KV lengths resident on the device (the SharedKV and sparse_flash_mla
+   * metadata operators likewise balance the work on the device before the
+   * main kernels): int32 [B], contiguous, device memory.  Decode (query
+   * length 1): read at run time by a partitioner kernel that writes the
+   * per-batch records and the split-KV chunk list into the workspace.
+   * Prompt (query length > 1, e.g. a chunk of prompt against a paged
+   * cache): the work items are planned for the bound and each reads its
+   * entry's length on the device.  A caller whose
    * lengths live on the GPU then needs no host copy and no synchronisation
    * per step, and one executor serves any lengths up to the bound (also
    * under HIP graph replay).  Each length is clamped into
    * [0, max_actual_seq_length_kv]; the bound (host, >= 0) sizes the grid and
    * the workspace and must fit the key extent (KV_S, or block_table cols *
-   * block_size).  Requires actual_seq_lengths_kv == NULL, query length 1
-   * (BSND / BSH / BNSD, no TND), a bf16 query with bf16 or fake-quantised
-   * (int8 / e4m3fn) key / value, and no atten_mask or pse_shift tensor
-   * (PARAM_INVALID / UNSUPPORTED otherwise).
+   * block_size).  Requires actual_seq_lengths_kv == NULL, BSND / BSH /
+   * BNSD (no TND), a bf16 query with bf16 key / value (or, in decode,
+   * fake-quantised int8 / e4m3fn key / value), no ALiBi and no atten_mask or
+   * pse_shift tensor (PARAM_INVALID / UNSUPPORTED otherwise).
    * Results equal those of the host-planned executor for the same lengths,
    * bit for bit.  NULL: lengths from actual_seq_lengths_kv as above. */
   const fia_tensor* actual_seq_lengths_kv_device;

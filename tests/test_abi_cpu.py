@@ -755,10 +755,15 @@ def test_device_kv_lengths_phase1():
     for kw, expect in cases:
         st, _, _, msg = plan(P(num_kv_heads=2, **kw), q, k, v, o)
         assert st == expect, (kw, msg)
-    # query length > 1 is not a decode
+    # query length > 1: a prompt whose items are planned for the bound (no
+    # workspace); ALiBi is not taken (its equal-length rule needs the lengths)
     q2, k2, v2, o2 = dense(S1=4, S2=3000)
-    st, _, _, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=100), q2, k2, v2, o2)
-    assert st == BAD, msg
+    st, kind, ws, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=100), q2, k2, v2, o2)
+    assert st == 0 and kind == "prefill" and ws == 0, msg
+    q4, k4, v4, o4 = dense(S1=3000, S2=3000)
+    st, _, _, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=3000, pse_type=2), q4, k4,
+                         v4, o4, pse=T((4,), fia.DT_FP32))
+    assert st == UNS and "ALiBi" in msg, msg
     # fp32 inputs are not taken
     q3, k3, v3, o3 = dense(S1=1, S2=300, D=64, dt=fia.DT_FP32)
     st, _, _, msg = plan(P(num_kv_heads=2, dev_lens=T((2,), i32), len_bound=100), q3, k3, v3, o3)

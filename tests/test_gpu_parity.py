@@ -850,6 +850,56 @@ def test_decode_fake_quant_device_lengths(i):
     check_lse(lse2, ref_l2)
 
 
+DEV_LEN_PREFILL_CASES = [
+    # (mask mode, paged block size (0: dense KV), D)
+    (3, 128, 128),
+    (0, 32, 128),
+    (3, 0, 64),
+]
+
+
+@pytest.mark.parametrize("i", range(len(DEV_LEN_PREFILL_CASES)))
+def test_prefill_device_lengths(i):
+    """A 40-row prompt chunk against a cache whose lengths live on the
+    device (items planned for the bound): equal to the host-planned run bit
+    for bit and to the oracle, then again after the lengths change on the
+    device (zero, one, the bound and one past it; with right-down causality
+    rows with no visible key come out as 0 / +inf)."""
+    mode, bs, D = DEV_LEN_PREFILL_CASES[i]
+    lens = [40, 700, 2999, 129]
+    lens2 = [3000, 0, 1, 3001]
+    bound = 3000
+    alloc = [max(a, min(b, bound)) for a, b in zip(lens, lens2)]
+    if bs:
+        base = W.paged_decode_case(f"dlp{i}", 540 + i, B=4, Q_N=8, KV_N=2, D=D, kv_lens=alloc,
+                                   block_size=bs, S1=40, sparse_mode=mode, lse=True)
+        assert base.block_table.shape[1] * bs >= bound
+    else:
+        base = W.dense_case(f"dlp{i}", 540 + i, B=4, S1=40, S2=bound, Q_N=8, KV_N=2, D=D,
+                            kv_lens=alloc, sparse_mode=mode, lse=True)
+    case = dataclasses.replace(base, actual_seq_lengths_kv=lens)
+    lens_dev = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    plan = run_plan(_dev_len_plan(case, lens_dev, bound))
+    assert plan.kind == "prefill"
+    host = run_plan(TI.dense_plan(case, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host.out.view(torch.int16))
+    assert torch.equal(plan.lse, host.lse)
+    out, lse = gpu_results(plan)
+    ref_o, ref_l = O.fia_case(case)
+    check_out(out, ref_o)
+    check_lse(lse, ref_l)
+    lens_dev.copy_(torch.tensor(lens2, dtype=torch.int32))
+    run_plan(plan)
+    case2 = dataclasses.replace(base, actual_seq_lengths_kv=[min(x, bound) for x in lens2])
+    host2 = run_plan(TI.dense_plan(case2, DEV))
+    assert torch.equal(plan.out.view(torch.int16), host2.out.view(torch.int16))
+    assert torch.equal(plan.lse, host2.lse)
+    out2, lse2 = gpu_results(plan)
+    ref_o2, ref_l2 = O.fia_case(case2)
+    check_out(out2, ref_o2)
+    check_lse(lse2, ref_l2)
+
+
 def test_decode_device_lengths_graph_replay():
     """The decode with device-resident lengths captured once into a HIP graph
     (after one eager run) and replayed with new lengths written between the
