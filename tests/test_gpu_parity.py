@@ -176,7 +176,7 @@ def test_prefill_other_layouts(layout):
     check_lse(to_f64(plan.lse)[..., 0], ref_l)
 
 
-@pytest.mark.parametrize("D,layout", [(64, "BSND"), (128, "BSND"), (128, "BNSD")])
+@pytest.mark.parametrize("D,layout", [(64, "BSND"), (128, "BSND"), (128, "BNSD"), (64, "BSH")])
 def test_prefill_padded_tiles_are_written(D, layout):
     """Query tiles wholly past the actual length get no work item of their
     own; the live tiles' items write them.  Outputs start as NaN, so a row
@@ -188,6 +188,8 @@ def test_prefill_padded_tiles_are_written(D, layout):
     q, k, v, bt, slopes = TI.dense_tensors(case, DEV)
     if layout == "BNSD":
         q, k, v = (x.permute(0, 2, 1, 3).contiguous() for x in (q, k, v))
+    elif layout == "BSH":
+        q, k, v = (x.reshape(x.shape[0], x.shape[1], -1).contiguous() for x in (q, k, v))
     out = torch.full_like(q, float("nan"))
     lse = torch.full((3, 4, 1000, 1), float("nan"), dtype=torch.float32, device=DEV)
     plan = run_plan(fia.AttentionPlan(q, k, v, num_heads=4, num_key_value_heads=2,
@@ -198,6 +200,8 @@ def test_prefill_padded_tiles_are_written(D, layout):
                                       attention_out=out, softmax_lse=lse))
     assert plan.kind == "prefill"
     got = plan.out.permute(0, 2, 1, 3) if layout == "BNSD" else plan.out
+    if layout == "BSH":
+        got = got.reshape(3, 1000, 4, D)
     ref_o, ref_l = O.fia_case(case)
     check_out(to_f64(got), ref_o)
     check_lse(to_f64(plan.lse)[..., 0], ref_l)
