@@ -209,7 +209,7 @@ constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
 constexpr int kPrefillKeys = 64;    // keys per prefill tile
 constexpr int kDecodeStep = 32;     // keys per decode wave step
 constexpr int kSparseSub = 64;      // row slots per sparse sub-chunk
-constexpr int kSparseHeads = 64;    // heads per sparse workgroup
+constexpr int kSparseHeads = 32;    // heads per sparse workgroup
 constexpr int kSparseMaxSub = 8;    // sub-chunks per sparse workgroup, at most
 constexpr int kSparseMaxChunks = 64;  // chunks per sparse query row, at most
 constexpr int kSparseBtCache = 512;   // block-table entries a sparse workgroup caches in LDS

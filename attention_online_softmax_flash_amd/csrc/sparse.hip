@@ -17,9 +17,11 @@
 // scale x7, one per 64-wide nope tile; the logical 512-vector is
 // [rope | nope * scale]), or plain bf16 / fp16 rows of 512 values.
 //
-// Work split.  A workgroup of 8 waves takes one query row, a block of 64
+// Work split.  A workgroup of 8 waves takes one query row, a block of 32
 // heads and one chunk of its slots (sub_per_chunk sub-chunks of 64 slots), so
-// every gathered row is converted once for all the heads that read it.  It
+// every gathered row is converted once for the 32 heads of the block (the
+// workgroups of the other head blocks of the row run on the same XCD and
+// find the rows in its L2).  It
 //   1. loads its query rows into registers and caches the batch entry's block
 //      table rows and its index entries in LDS (all in flight together);
 //   2. resolves a sub-chunk's 64 slots to row addresses from those LDS copies
@@ -42,7 +44,7 @@ constexpr int kThreads = 512;
 constexpr int X_PITCH = kSparseD * 2 + 16;          // bytes per row-major row in LDS
 constexpr int X_BYTES = kSparseSub * X_PITCH;        // 66560
 constexpr int Q_BYTES = kSparseHeads * X_PITCH;      // the workgroup's query rows, row-major
-constexpr int SX_BYTES = 4 * 64 * 16 * 4;            // score halves of the dh = 1 waves
+constexpr int SX_BYTES = 3 * 2 * 64 * 16 * 4;        // score partials of the d quarters 1..3
 constexpr int RP_BYTES = 2 * kSparseSub * 8;         // row addresses, two sub-chunks
 constexpr int BT_BYTES = 2 * kSparseBtCache * 4;     // ori / cmp block-table rows
 constexpr int IX_BYTES = kSparseMaxSub * kSparseSub * 4;
@@ -50,8 +52,8 @@ constexpr int ST_BYTES = 4 * 64 * 4;                 // row max / sum per (slot 
 constexpr int LM_BYTES = 2 * 8;                      // live-slot masks, two sub-chunks
 constexpr int OFF_Q = X_BYTES;
 constexpr int OFF_SX = OFF_Q + Q_BYTES;
-// The probabilities [head block][k step][lane] (8 KB) share the score
-// exchange area: they are written after its last read in a step.
+// The probabilities [k step][lane] (4 KB) share the score exchange area:
+// they are written after its last read in a step.
 constexpr int OFF_P = OFF_SX;
 constexpr int OFF_RP = OFF_SX + SX_BYTES;
 constexpr int OFF_BT = OFF_RP + RP_BYTES;
@@ -273,13 +275,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   const int sub_n = a.sub_per_chunk;
   const int s_begin = chunk * kSparseSub * sub_n;
 
-  // Roles.  Scores: slot half sb, head half hq, d half dh.  Values: head half
-  // hq, d quarter dq.  Lane (n, hh) owns head 64 hb + 32 hq + n.
+  // Roles.  Scores: slot half sb, d quarter dq (128 values).  Values: d
+  // block of 64 (the wave index).  Lane (n, hh) owns head 32 hb + n.
   const int sb = wave & 1;
-  const int hq = (wave >> 1) & 1;
-  const int dh = wave >> 2;
-  const int dq = (wave & 1) + 2 * (wave >> 2);
-  const int head = kSparseHeads * hb + 32 * hq + n;
+  const int dq = wave >> 1;
+  const int head = kSparseHeads * hb + n;
   const bool head_ok = head < a.N1;
 
   const SparseRow qr = sparse_row_wave(a, r, lane);
@@ -293,9 +293,10 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   // flight together, one trip to memory.
   uint8_t* qs = lds + OFF_Q;
   const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss;
-  u32x4 qv[8];
+  constexpr int QV = kSparseHeads * 64 / kThreads;   // 16-byte query pieces per thread
+  u32x4 qv[QV];
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
+  for (int v = 0; v < QV; ++v) {
     // 16-byte piece p % 64 of head p / 64; heads past N1 load the last head
     // (a valid address) and are zeroed.
     const int p = tid + kThreads * v;
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   const int Lk = sparse_len(a, qr);
   const SlotCtx ctx = slot_ctx(a, qr, Lk);
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
+  for (int v = 0; v < QV; ++v) {
     const int p = tid + kThreads * v;
     *reinterpret_cast<u32x4*>(qs + (p >> 6) * X_PITCH + 16 * (p & 63)) = qv[v];
   }
@@ -412,14 +413,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   {
     const int g16 = lane >> 4;
     const int j = lane & 15;
-    tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH + (128 * dq + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
+    tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH + (64 * wave + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
   }
 
   float m_run = kNegInf;   // running max (log2 domain) of this lane's head
   float l_run = 0.f;
-  f32x16 o[4];
+  constexpr int NOB = 2;   // 32-wide d blocks of the wave's 64 values
+  f32x16 o[NOB];
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < NOB; ++mb) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) o[mb][q] = 0.f;
   }
@@ -439,41 +441,46 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
     if (has_next) load_rows(u + 1);
     const uint64_t live = live_m[u & 1];
 
-    // 2. Scores S^T[slot][head] for slots 32 sb + (0..31), heads of hq, d half dh.
+    // 2. Scores S^T[slot][head] for slots 32 sb + (0..31), d quarter dq; the
+    // quarters 1..3 hand their partial sums to the quarter-0 wave of their
+    // slot half through LDS.
     f32x16 s;
 #pragma unroll
     for (int q = 0; q < 16; ++q) s[q] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const int off = (256 * dh + 16 * c + 8 * hh) * 2;
+    for (int c = 0; c < 8; ++c) {
+      const int off = (128 * dq + 16 * c + 8 * hh) * 2;
       const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH + off);
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(qs + (32 * hq + n) * X_PITCH + off);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(qs + n * X_PITCH + off);
       s = mfma32h<F16>(av, bv, s);
     }
-    float* sxw = sx + ((sb * 2 + hq) * 64 + lane) * 16;
-    if (dh == 1) {
+    if (dq > 0) {
+      float* sxw = sx + (((dq - 1) * 2 + sb) * 64 + lane) * 16;
 #pragma unroll
       for (int q = 0; q < 16; ++q) sxw[q] = s[q];
     }
     __syncthreads();
-    if (dh == 0) {
+    if (dq == 0) {
+      const float* sx1 = sx + ((0 * 2 + sb) * 64 + lane) * 16;
+      const float* sx2 = sx + ((1 * 2 + sb) * 64 + lane) * 16;
+      const float* sx3 = sx + ((2 * 2 + sb) * 64 + lane) * 16;
       float m_loc = kNegInf;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int slot = 32 * sb + 8 * (q >> 2) + 4 * hh + (q & 3);
-        const float x = (s[q] + sxw[q]) * a.scale_log2;
+        const float x = ((s[q] + sx1[q]) + (sx2[q] + sx3[q])) * a.scale_log2;
         s[q] = ((live >> slot) & 1u) ? x : kNegInf;
         m_loc = fmaxf(m_loc, s[q]);
       }
       m_loc = pair32_max(m_loc);
-      if (hh == 0) mx_s[sb * 64 + 32 * hq + n] = m_loc;
+      if (hh == 0) mx_s[sb * 32 + n] = m_loc;
     }
     __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(mx_s[32 * hq + n], mx_s[64 + 32 * hq + n]));
+    const float m_new = fmaxf(m_run, fmaxf(mx_s[n], mx_s[32 + n]));
     const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     m_run = m_new;
-    if (dh == 0) {
+    if (dq == 0) {
       float l = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -483,32 +490,32 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
           pr[t] = fast_exp2(s[8 * kk + t] - m_use);
           l += pr[t];
         }
-        ps[(hq * 4 + 2 * sb + kk) * 64 + lane] =
+        ps[(2 * sb + kk) * 64 + lane] =
             u32x4{pack_h2<F16>(pr[0], pr[1]), pack_h2<F16>(pr[2], pr[3]),
                   pack_h2<F16>(pr[4], pr[5]), pack_h2<F16>(pr[6], pr[7])};
       }
       l = pair32_sum(l);
-      if (hh == 0) l_s[sb * 64 + 32 * hq + n] = l;
+      if (hh == 0) l_s[sb * 32 + n] = l;
     }
     __syncthreads();
-    l_run = l_run * alpha + l_s[32 * hq + n] + l_s[64 + 32 * hq + n];
+    l_run = l_run * alpha + l_s[n] + l_s[32 + n];
 
-    // 3. O^T[d][head] += X^T P^T for d in [128 dq, 128 dq + 128).
+    // 3. O^T[d][head] += X^T P^T for d in [64 wave, 64 wave + 64).
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < NOB; ++mb) {
       o[mb] *= alpha;
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const uint8_t* vp = tb + 16 * kk * X_PITCH + 64 * mb;
         const u32x2 lo2 = lds_tr16(vp);
         const u32x2 hi2 = lds_tr16(vp + 8 * X_PITCH);
-        o[mb] = mfma32h<F16>(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[(hq * 4 + kk) * 64 + lane], o[mb]);
+        o[mb] = mfma32h<F16>(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[kk * 64 + lane], o[mb]);
       }
     }
     __syncthreads();   // every wave is done with xs, ps and the statistics
   }
 
-  // 4. Lane (n, hh) holds O^T[d][head] at d = 128 dq + 32 mb + 8 (q / 4) +
+  // 4. Lane (n, hh) holds O^T[d][head] at d = 64 wave + 32 mb + 8 (q / 4) +
   // 4 hh + q % 4.
   if (!head_ok) return;
   if (a.n_chunks == 1) {
@@ -525,9 +532,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
     }
     const float inv = has ? osc / L : 0.f;
     uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)head * a.o_sh +
-                   128 * dq + 4 * hh;
+                   64 * wave + 4 * hh;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int mb = 0; mb < NOB; ++mb) {
 #pragma unroll
       for (int q4 = 0; q4 < 4; ++q4) {
         st8(op + 32 * mb + 8 * q4,
@@ -535,7 +542,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
                   pack_h2<F16>(o[mb][4 * q4 + 2] * inv, o[mb][4 * q4 + 3] * inv)});
       }
     }
-    if (a.lse != nullptr && dq == 0 && hh == 0) {
+    if (a.lse != nullptr && wave == 0 && hh == 0) {
       a.lse[(int64_t)b * a.lse_sb + (int64_t)qr.tq * a.lse_ss + (int64_t)head * a.lse_sh] =
           has ? (m + fast_log2(L)) * kLn2 : kPosInf;
     }
@@ -545,13 +552,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   // so each store writes whole runs of 32 heads), part_lse[row][chunk][head].
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const int64_t rc = (int64_t)r * a.n_chunks + chunk;
-  float* pp = a.part_o + (rc * kSparseD + 128 * dq + 4 * hh) * a.N1 + head;
+  float* pp = a.part_o + (rc * kSparseD + 64 * wave + 4 * hh) * a.N1 + head;
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb) {
+  for (int mb = 0; mb < NOB; ++mb) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) pp[(int64_t)(32 * mb + 8 * (q >> 2) + (q & 3)) * a.N1] = o[mb][q] * inv;
   }
-  if (dq == 0 && hh == 0) a.part_lse[rc * a.N1 + head] = l_run > 0.f ? m_run + fast_log2(l_run) : kNegInf;
+  if (wave == 0 && hh == 0) a.part_lse[rc * a.N1 + head] = l_run > 0.f ? m_run + fast_log2(l_run) : kNegInf;
 }
 
 // Fold the chunk partials of one query row in chunk order with the sink
@@ -563,6 +570,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
 // is folded into the running sum with the usual rescale by the new maximum;
 // the sink's term joins at the end.
 constexpr int kMergeD = 4;   // d values per thread
+constexpr int kMergeHeads = 64;   // heads per merge workgroup (one per lane)
 template <bool F16>
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   constexpr int G = 8;   // chunks per group of loads in flight
@@ -570,7 +578,7 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   const int hl = tid & 63;
   const int r = blockIdx.x;
   const int d0 = 4 * kMergeD * blockIdx.y + kMergeD * (tid >> 6);
-  const int h = kSparseHeads * blockIdx.z + hl;
+  const int h = kMergeHeads * blockIdx.z + hl;
   const SparseRow qr = sparse_row_wave(a, r, hl);   // every lane still active
   if (h >= a.N1) return;
   const int nc = a.n_chunks;
@@ -662,7 +670,7 @@ hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
 
 hipError_t launch_sparse_merge(const SparseArgs& a, hipStream_t s) {
   if (a.n_rows == 0 || a.n_chunks <= 1) return hipSuccess;
-  const dim3 grid(a.n_rows, kSparseD / (4 * kMergeD), a.n_hb);
+  const dim3 grid(a.n_rows, kSparseD / (4 * kMergeD), (a.N1 + kMergeHeads - 1) / kMergeHeads);
   if (a.fmt == SF_FP16) {
     sparse_merge<true><<<grid, 256, 0, s>>>(a);
   } else {
