@@ -1209,7 +1209,12 @@ fia_status sparse_finish(fia_executor* e, int64_t K2, size_t* workspace_size, fi
                                          std::to_string(fia::kSparseMaxChunks * per_chunk) + ")");
   }
   a.n_chunks = (int32_t)n_chunks;
-  a.n_hb = (a.N1 + fia::kSparseHeads - 1) / fia::kSparseHeads;
+  {
+    const int64_t hs = fia::kSparseHeadsSmall;
+    const int64_t wg_small = (int64_t)a.n_rows * n_chunks * ((a.N1 + hs - 1) / hs);
+    a.hb_heads = (a.N1 <= hs || wg_small <= fia::kSparseCUs) ? fia::kSparseHeadsSmall : fia::kSparseHeadsLarge;
+  }
+  a.n_hb = (a.N1 + a.hb_heads - 1) / a.hb_heads;
   a.xcd_rows = (a.n_rows % 8 == 0) ? 1 : 0;
   if ((int64_t)a.n_rows * a.n_hb * a.n_chunks > INT32_MAX) {
     delete e;

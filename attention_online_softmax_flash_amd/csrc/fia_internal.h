@@ -167,6 +167,7 @@ struct SparseArgs {
   // takes one (row, head block, chunk).  xcd_rows: the workgroups of one
   // row run on one XCD (row r on XCD r % 8; needs n_rows % 8 == 0).
   int32_t sub_per_chunk, n_chunks, n_hb, xcd_rows;
+  int32_t hb_heads;                 // heads per workgroup (kSparseHeadsSmall or kSparseHeadsLarge)
   float* part_o;                    // [n_rows * n_chunks * N1 * 512] (n_chunks > 1)
   float* part_lse;                  // [n_rows * n_chunks * N1], log2 domain
 };
@@ -209,7 +210,11 @@ constexpr int kPrefillRows = 128;   // query rows per prefill workgroup
 constexpr int kPrefillKeys = 64;    // keys per prefill tile
 constexpr int kDecodeStep = 32;     // keys per decode wave step
 constexpr int kSparseSub = 64;      // row slots per sparse sub-chunk
-constexpr int kSparseHeads = 32;    // heads per sparse workgroup
+// Heads per sparse workgroup: 32, or 64 when the launch with 32 would need
+// more workgroups than the CUs of a 256-CU MI355X (one workgroup per CU).
+constexpr int kSparseHeadsSmall = 32;
+constexpr int kSparseHeadsLarge = 64;
+constexpr int kSparseCUs = 256;
 constexpr int kSparseMaxSub = 8;    // sub-chunks per sparse workgroup, at most
 constexpr int kSparseMaxChunks = 64;  // chunks per sparse query row, at most
 constexpr int kSparseBtCache = 512;   // block-table entries a sparse workgroup caches in LDS

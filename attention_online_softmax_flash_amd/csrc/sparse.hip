@@ -17,11 +17,12 @@
 // scale x7, one per 64-wide nope tile; the logical 512-vector is
 // [rope | nope * scale]), or plain bf16 / fp16 rows of 512 values.
 //
-// Work split.  A workgroup of 8 waves takes one query row, a block of 32
-// heads and one chunk of its slots (sub_per_chunk sub-chunks of 64 slots), so
-// every gathered row is converted once for the 32 heads of the block (the
-// workgroups of the other head blocks of the row run on the same XCD and
-// find the rows in its L2).  It
+// Work split.  A workgroup of 8 waves takes one query row, a block of HB
+// heads (32, or 64 when the launch would not fit the CUs otherwise) and one
+// chunk of its slots (sub_per_chunk sub-chunks of 64 slots), so every
+// gathered row is converted once for the heads of the block (the workgroups
+// of the other head blocks of the row run on the same XCD and find the rows
+// in its L2).  It
 //   1. loads its query rows into registers and caches the batch entry's block
 //      table rows and its index entries in LDS (all in flight together);
 //   2. resolves a sub-chunk's 64 slots to row addresses from those LDS copies
@@ -43,24 +44,33 @@ namespace {
 constexpr int kThreads = 512;
 constexpr int X_PITCH = kSparseD * 2 + 16;          // bytes per row-major row in LDS
 constexpr int X_BYTES = kSparseSub * X_PITCH;        // 66560
-constexpr int Q_BYTES = kSparseHeads * X_PITCH;      // the workgroup's query rows, row-major
-constexpr int SX_BYTES = 3 * 2 * 64 * 16 * 4;        // score partials of the d quarters 1..3
 constexpr int RP_BYTES = 2 * kSparseSub * 8;         // row addresses, two sub-chunks
 constexpr int BT_BYTES = 2 * kSparseBtCache * 4;     // ori / cmp block-table rows
 constexpr int IX_BYTES = kSparseMaxSub * kSparseSub * 4;
 constexpr int ST_BYTES = 4 * 64 * 4;                 // row max / sum per (slot half, head)
 constexpr int LM_BYTES = 2 * 8;                      // live-slot masks, two sub-chunks
-constexpr int OFF_Q = X_BYTES;
-constexpr int OFF_SX = OFF_Q + Q_BYTES;
-// The probabilities [k step][lane] (4 KB) share the score exchange area:
-// they are written after its last read in a step.
-constexpr int OFF_P = OFF_SX;
-constexpr int OFF_RP = OFF_SX + SX_BYTES;
-constexpr int OFF_BT = OFF_RP + RP_BYTES;
-constexpr int OFF_IX = OFF_BT + BT_BYTES;
-constexpr int OFF_ST = OFF_IX + IX_BYTES;
-constexpr int OFF_LM = OFF_ST + ST_BYTES;
-constexpr int LDS_TOTAL = OFF_LM + LM_BYTES;
+// LDS layout of a workgroup of HB heads (32 or 64).  HQ 32-head halves; the
+// score product is split over DS d ranges, whose partial sums meet through
+// the exchange area SX.
+template <int HB>
+struct SparseLds {
+  static constexpr int HQ = HB / 32;
+  static constexpr int DS = 4 / HQ;
+  static constexpr int Q_BYTES = HB * X_PITCH;                        // query rows, row-major
+  static constexpr int SX_BYTES = (DS - 1) * 2 * HQ * 64 * 16 * 4;    // score partials
+  static constexpr int OFF_Q = X_BYTES;
+  static constexpr int OFF_SX = OFF_Q + Q_BYTES;
+  // The probabilities [head half][k step][lane] (HQ x 4 KB) share the score
+  // exchange area: they are written after its last read in a step.
+  static constexpr int OFF_P = OFF_SX;
+  static constexpr int OFF_RP = OFF_SX + SX_BYTES;
+  static constexpr int OFF_BT = OFF_RP + RP_BYTES;
+  static constexpr int OFF_IX = OFF_BT + BT_BYTES;
+  static constexpr int OFF_ST = OFF_IX + IX_BYTES;
+  static constexpr int OFF_LM = OFF_ST + ST_BYTES;
+  static constexpr int TOTAL = OFF_LM + LM_BYTES;
+  static_assert(HQ * 4 * 64 * 16 <= SX_BYTES, "probabilities fit the exchange area");
+};
 
 }  // namespace
 
@@ -235,20 +245,26 @@ __device__ __forceinline__ const uint8_t* slot_row(const SparseArgs& a, const Sl
 }
 
 // Grid: n_rows * n_hb * n_chunks workgroups of 512 threads (8 waves).
-template <int FMT>
+template <int FMT, int HB>
 __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   constexpr bool F16 = FMT == SF_FP16;
+  using SL = SparseLds<HB>;
+  constexpr int HQ = SL::HQ;
+  constexpr int DS = SL::DS;
+  constexpr int DSW = kSparseD / DS;       // d values per score split (128 or 256)
+  constexpr int DVW = kSparseD * HQ / 8;   // d values per wave in the value product (64 or 128)
+  constexpr int NOB = DVW / 32;            // its 32-wide d blocks
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xs = lds;                                                   // [64][X_PITCH]
-  u32x4* ps = reinterpret_cast<u32x4*>(lds + OFF_P);                   // [2][4][64]
-  float* sx = reinterpret_cast<float*>(lds + OFF_SX);                  // [4][64][16]
-  const uint8_t** rowp = reinterpret_cast<const uint8_t**>(lds + OFF_RP);   // [2][64]
-  int32_t* bt_o = reinterpret_cast<int32_t*>(lds + OFF_BT);            // [kSparseBtCache]
+  u32x4* ps = reinterpret_cast<u32x4*>(lds + SL::OFF_P);                   // [HQ][4][64]
+  float* sx = reinterpret_cast<float*>(lds + SL::OFF_SX);                  // [DS - 1][2][HQ][64][16]
+  const uint8_t** rowp = reinterpret_cast<const uint8_t**>(lds + SL::OFF_RP);   // [2][64]
+  int32_t* bt_o = reinterpret_cast<int32_t*>(lds + SL::OFF_BT);            // [kSparseBtCache]
   int32_t* bt_c = bt_o + kSparseBtCache;                               // [kSparseBtCache]
-  int32_t* ixc = reinterpret_cast<int32_t*>(lds + OFF_IX);             // [64 * sub_per_chunk]
-  float* mx_s = reinterpret_cast<float*>(lds + OFF_ST);                // [2][64]
-  float* l_s = mx_s + 128;                                             // [2][64]
-  uint64_t* live_m = reinterpret_cast<uint64_t*>(lds + OFF_LM);       // [2]: bit s = slot s used
+  int32_t* ixc = reinterpret_cast<int32_t*>(lds + SL::OFF_IX);             // [64 * sub_per_chunk]
+  float* mx_s = reinterpret_cast<float*>(lds + SL::OFF_ST);                // [2][HB]
+  float* l_s = mx_s + 128;                                             // [2][HB]
+  uint64_t* live_m = reinterpret_cast<uint64_t*>(lds + SL::OFF_LM);       // [2]: bit s = slot s used
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -275,11 +291,14 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   const int sub_n = a.sub_per_chunk;
   const int s_begin = chunk * kSparseSub * sub_n;
 
-  // Roles.  Scores: slot half sb, d quarter dq (128 values).  Values: d
-  // block of 64 (the wave index).  Lane (n, hh) owns head 32 hb + n.
+  // Roles.  Scores: slot half sb, head half hq, d range ds (DSW values).
+  // Values: head half hq, d block dv (DVW values).  Lane (n, hh) owns head
+  // HB hb + 32 hq + n.
   const int sb = wave & 1;
-  const int dq = wave >> 1;
-  const int head = kSparseHeads * hb + n;
+  const int hq = HQ == 2 ? ((wave >> 1) & 1) : 0;
+  const int ds = HQ == 2 ? (wave >> 2) : (wave >> 1);
+  const int dv = HQ == 2 ? ((wave & 1) + 2 * (wave >> 2)) : wave;
+  const int head = HB * hb + 32 * hq + n;
   const bool head_ok = head < a.N1;
 
   const SparseRow qr = sparse_row_wave(a, r, lane);
@@ -291,16 +310,16 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   // unconditional (positions are clamped into range, absent tables lie
   // outside their empty buffer resources and read as zero), so they are in
   // flight together, one trip to memory.
-  uint8_t* qs = lds + OFF_Q;
+  uint8_t* qs = lds + SL::OFF_Q;
   const uint16_t* qrow = a.q + (int64_t)b * a.q_sb + (int64_t)qr.tq * a.q_ss;
-  constexpr int QV = kSparseHeads * 64 / kThreads;   // 16-byte query pieces per thread
+  constexpr int QV = HB * 64 / kThreads;   // 16-byte query pieces per thread
   u32x4 qv[QV];
 #pragma unroll
   for (int v = 0; v < QV; ++v) {
     // 16-byte piece p % 64 of head p / 64; heads past N1 load the last head
     // (a valid address) and are zeroed.
     const int p = tid + kThreads * v;
-    const int hd = kSparseHeads * hb + (p >> 6);
+    const int hd = HB * hb + (p >> 6);
     const u32x4 w = ld16(qrow + (int64_t)min(hd, a.N1 - 1) * a.q_sh + 8 * (p & 63));
     qv[v] = hd < a.N1 ? w : u32x4{0u, 0u, 0u, 0u};
   }
@@ -413,12 +432,11 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   {
     const int g16 = lane >> 4;
     const int j = lane & 15;
-    tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH + (64 * wave + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
+    tb = xs + (4 * (g16 >> 1) + (j >> 2)) * X_PITCH + (DVW * dv + 16 * (g16 & 1) + 4 * (j & 3)) * 2;
   }
 
   float m_run = kNegInf;   // running max (log2 domain) of this lane's head
   float l_run = 0.f;
-  constexpr int NOB = 2;   // 32-wide d blocks of the wave's 64 values
   f32x16 o[NOB];
 #pragma unroll
   for (int mb = 0; mb < NOB; ++mb) {
@@ -441,46 +459,52 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
     if (has_next) load_rows(u + 1);
     const uint64_t live = live_m[u & 1];
 
-    // 2. Scores S^T[slot][head] for slots 32 sb + (0..31), d quarter dq; the
-    // quarters 1..3 hand their partial sums to the quarter-0 wave of their
-    // slot half through LDS.
+    // 2. Scores S^T[slot][head] for slots 32 sb + (0..31), heads of hq, d
+    // range ds; ranges 1 .. DS - 1 hand their partial sums to the range-0
+    // wave through LDS.
     f32x16 s;
 #pragma unroll
     for (int q = 0; q < 16; ++q) s[q] = 0.f;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int off = (128 * dq + 16 * c + 8 * hh) * 2;
+    for (int c = 0; c < DSW / 16; ++c) {
+      const int off = (DSW * ds + 16 * c + 8 * hh) * 2;
       const u32x4 av = *reinterpret_cast<const u32x4*>(xs + (32 * sb + n) * X_PITCH + off);
-      const u32x4 bv = *reinterpret_cast<const u32x4*>(qs + n * X_PITCH + off);
+      const u32x4 bv = *reinterpret_cast<const u32x4*>(qs + (32 * hq + n) * X_PITCH + off);
       s = mfma32h<F16>(av, bv, s);
     }
-    if (dq > 0) {
-      float* sxw = sx + (((dq - 1) * 2 + sb) * 64 + lane) * 16;
+    auto part = [&](int k) FIA_INLINE {   // partial of d range k >= 1, this (sb, hq, lane)
+      return sx + ((((k - 1) * 2 + sb) * HQ + hq) * 64 + lane) * 16;
+    };
+    if (ds > 0) {
+      float* sxw = part(ds);
 #pragma unroll
       for (int q = 0; q < 16; ++q) sxw[q] = s[q];
     }
     __syncthreads();
-    if (dq == 0) {
-      const float* sx1 = sx + ((0 * 2 + sb) * 64 + lane) * 16;
-      const float* sx2 = sx + ((1 * 2 + sb) * 64 + lane) * 16;
-      const float* sx3 = sx + ((2 * 2 + sb) * 64 + lane) * 16;
+    if (ds == 0) {
       float m_loc = kNegInf;
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int slot = 32 * sb + 8 * (q >> 2) + 4 * hh + (q & 3);
-        const float x = ((s[q] + sx1[q]) + (sx2[q] + sx3[q])) * a.scale_log2;
+        float sum;
+        if constexpr (DS == 2) {
+          sum = s[q] + part(1)[q];
+        } else {
+          sum = (s[q] + part(1)[q]) + (part(2)[q] + part(3)[q]);
+        }
+        const float x = sum * a.scale_log2;
         s[q] = ((live >> slot) & 1u) ? x : kNegInf;
         m_loc = fmaxf(m_loc, s[q]);
       }
       m_loc = pair32_max(m_loc);
-      if (hh == 0) mx_s[sb * 32 + n] = m_loc;
+      if (hh == 0) mx_s[sb * HB + 32 * hq + n] = m_loc;
     }
     __syncthreads();
-    const float m_new = fmaxf(m_run, fmaxf(mx_s[n], mx_s[32 + n]));
+    const float m_new = fmaxf(m_run, fmaxf(mx_s[32 * hq + n], mx_s[HB + 32 * hq + n]));
     const float alpha = (m_new == kNegInf) ? 1.f : fast_exp2(m_run - m_new);
     const float m_use = (m_new == kNegInf) ? 0.f : m_new;
     m_run = m_new;
-    if (dq == 0) {
+    if (ds == 0) {
       float l = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 2; ++kk) {
@@ -490,17 +514,17 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
           pr[t] = fast_exp2(s[8 * kk + t] - m_use);
           l += pr[t];
         }
-        ps[(2 * sb + kk) * 64 + lane] =
+        ps[(hq * 4 + 2 * sb + kk) * 64 + lane] =
             u32x4{pack_h2<F16>(pr[0], pr[1]), pack_h2<F16>(pr[2], pr[3]),
                   pack_h2<F16>(pr[4], pr[5]), pack_h2<F16>(pr[6], pr[7])};
       }
       l = pair32_sum(l);
-      if (hh == 0) l_s[sb * 32 + n] = l;
+      if (hh == 0) l_s[sb * HB + 32 * hq + n] = l;
     }
     __syncthreads();
-    l_run = l_run * alpha + l_s[n] + l_s[32 + n];
+    l_run = l_run * alpha + l_s[32 * hq + n] + l_s[HB + 32 * hq + n];
 
-    // 3. O^T[d][head] += X^T P^T for d in [64 wave, 64 wave + 64).
+    // 3. O^T[d][head] += X^T P^T for d in [DVW dv, DVW dv + DVW).
 #pragma unroll
     for (int mb = 0; mb < NOB; ++mb) {
       o[mb] *= alpha;
@@ -509,13 +533,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
         const uint8_t* vp = tb + 16 * kk * X_PITCH + 64 * mb;
         const u32x2 lo2 = lds_tr16(vp);
         const u32x2 hi2 = lds_tr16(vp + 8 * X_PITCH);
-        o[mb] = mfma32h<F16>(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[kk * 64 + lane], o[mb]);
+        o[mb] = mfma32h<F16>(u32x4{lo2.x, lo2.y, hi2.x, hi2.y}, ps[(hq * 4 + kk) * 64 + lane], o[mb]);
       }
     }
     __syncthreads();   // every wave is done with xs, ps and the statistics
   }
 
-  // 4. Lane (n, hh) holds O^T[d][head] at d = 64 wave + 32 mb + 8 (q / 4) +
+  // 4. Lane (n, hh) holds O^T[d][head] at d = DVW dv + 32 mb + 8 (q / 4) +
   // 4 hh + q % 4.
   if (!head_ok) return;
   if (a.n_chunks == 1) {
@@ -532,7 +556,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
     }
     const float inv = has ? osc / L : 0.f;
     uint16_t* op = a.o + (int64_t)b * a.o_sb + (int64_t)qr.tq * a.o_ss + (int64_t)head * a.o_sh +
-                   64 * wave + 4 * hh;
+                   DVW * dv + 4 * hh;
 #pragma unroll
     for (int mb = 0; mb < NOB; ++mb) {
 #pragma unroll
@@ -542,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
                   pack_h2<F16>(o[mb][4 * q4 + 2] * inv, o[mb][4 * q4 + 3] * inv)});
       }
     }
-    if (a.lse != nullptr && wave == 0 && hh == 0) {
+    if (a.lse != nullptr && dv == 0 && hh == 0) {
       a.lse[(int64_t)b * a.lse_sb + (int64_t)qr.tq * a.lse_ss + (int64_t)head * a.lse_sh] =
           has ? (m + fast_log2(L)) * kLn2 : kPosInf;
     }
@@ -552,13 +576,13 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   // so each store writes whole runs of 32 heads), part_lse[row][chunk][head].
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const int64_t rc = (int64_t)r * a.n_chunks + chunk;
-  float* pp = a.part_o + (rc * kSparseD + 64 * wave + 4 * hh) * a.N1 + head;
+  float* pp = a.part_o + (rc * kSparseD + DVW * dv + 4 * hh) * a.N1 + head;
 #pragma unroll
   for (int mb = 0; mb < NOB; ++mb) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) pp[(int64_t)(32 * mb + 8 * (q >> 2) + (q & 3)) * a.N1] = o[mb][q] * inv;
   }
-  if (wave == 0 && hh == 0) a.part_lse[rc * a.N1 + head] = l_run > 0.f ? m_run + fast_log2(l_run) : kNegInf;
+  if (dv == 0 && hh == 0) a.part_lse[rc * a.N1 + head] = l_run > 0.f ? m_run + fast_log2(l_run) : kNegInf;
 }
 
 // Fold the chunk partials of one query row in chunk order with the sink
@@ -646,16 +670,24 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   }
 }
 
-template <int FMT>
-static hipError_t launch_fmt(const SparseArgs& a, hipStream_t s) {
+template <int FMT, int HB>
+static hipError_t launch_hb(const SparseArgs& a, hipStream_t s) {
   // Dynamic LDS above the default limit must be enabled for the kernel (on
   // the current device); the call is cheap, so it is made on every launch.
+  constexpr int lds = SparseLds<HB>::TOTAL;
   const hipError_t attr = hipFuncSetAttribute(
-      (const void*)sparse_attn<FMT>, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_TOTAL);
+      (const void*)sparse_attn<FMT, HB>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
   const unsigned grid = (unsigned)a.n_rows * a.n_hb * a.n_chunks;
-  sparse_attn<FMT><<<grid, kThreads, LDS_TOTAL, s>>>(a);
+  sparse_attn<FMT, HB><<<grid, kThreads, lds, s>>>(a);
   return hipGetLastError();
+}
+
+template <int FMT>
+static hipError_t launch_fmt(const SparseArgs& a, hipStream_t s) {
+  if (a.hb_heads == 32) return launch_hb<FMT, 32>(a, s);
+  if (a.hb_heads == 64) return launch_hb<FMT, 64>(a, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_sparse(const SparseArgs& a, hipStream_t s) {
