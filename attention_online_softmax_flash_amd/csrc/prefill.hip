@@ -465,16 +465,30 @@ __global__ __launch_bounds__(256, 2) void prefill_bf16(AttnArgs a) {
           o[mb] = mfma32(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[kk], o[mb]);
         }
       }
-      __builtin_amdgcn_s_setprio(0);
-      // Interleave: one MFMA, a few VALU, one LDS read, repeated.
+      // Order of the block's instructions (the hints have to come before the
+      // priority change: the scheduler does not move instructions across
+      // it).  The first key-operand reads of the next score product go out
+      // ahead; then each score MFMA is followed by one LDS read and a few
+      // softmax VALU instructions, and each value MFMA by two transpose reads
+      // and more VALU work, so no MFMA waits for a read issued just before it.
       if constexpr (INTERLEAVE) {
+        constexpr int SM = DO_NEXT ? 2 * NQ : 0;   // score MFMAs in the block
+        constexpr int VM = 4 * NMB;                // value MFMAs
+        if constexpr (DO_NEXT) __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);
 #pragma unroll
-        for (int g = 0; g < 24; ++g) {
+        for (int g = 0; g < SM; ++g) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+#pragma unroll
+        for (int g = 0; g < VM; ++g) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
         }
       }
+      __builtin_amdgcn_s_setprio(0);
     };
 
     // Software pipeline over key tiles, two stages (stage of tile kt:
