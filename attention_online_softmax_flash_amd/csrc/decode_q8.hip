@@ -110,22 +110,38 @@ __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) 
 
 }  // namespace
 
-// KPT / VPT: key / value scales per token (else per channel).
-template <int D, bool FP8, bool KPT, bool VPT>
-__global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split_q8(AttnArgs a) {
+// KPT / VPT: key / value scales per token (else per channel).  NH: KV heads
+// per wave.  With NH = 2 (heads of a token adjacent in memory, G <= 8) a wave
+// takes KV heads kvh and kvh + 1 of the same keys: their codes are one
+// 2 D-byte run per token, loaded as a whole, and the G query heads of each
+// fill columns [0, G) and [G, 2 G) of the 16-column MFMA tiles, so the
+// softmax work of a column serves a real head twice as often.
+template <int D, bool FP8, bool KPT, bool VPT, int NH>
+__global__ __launch_bounds__(256, (KPT || VPT || FP8 || NH == 2) ? 3 : 4) void decode_split_q8(AttnArgs a) {
   constexpr int NC = D / 32;   // 32-wide k-steps of the score product per 16-key half
   constexpr int DPL = D / 16;  // value columns per lane column
   constexpr int KB = D / 4;    // key bytes per lane and row
+  constexpr int NSUB = 2 / NH; // 32-key steps per load round (64 D bytes of key codes)
+  constexpr int RB = NH * D;   // staged bytes per key row
+  static_assert(NH == 1 || NH == 2, "one or two KV heads per wave");
   const int lane = threadIdx.x & 63;
   const int wave = uniform(threadIdx.x >> 6);
   const int n = lane & 15;
   const int g = lane >> 4;
 
   int item = blockIdx.x;
-  const int hb = item % a.n_head_blocks;
-  item /= a.n_head_blocks;
-  const int kvh = item % a.KVn;
-  const int cg = item / a.KVn;
+  int hb = 0, kvh;
+  if constexpr (NH == 1) {
+    hb = item % a.n_head_blocks;
+    item /= a.n_head_blocks;
+    kvh = item % a.KVn;
+    item /= a.KVn;
+  } else {
+    const int npair = a.KVn / 2;
+    kvh = 2 * (item % npair);
+    item /= npair;
+  }
+  const int cg = item;
   if (a.n_chunks_dev != nullptr && cg >= *a.n_chunks_dev) return;   // past the device plan's chunks
   const int b = a.work[2 * cg];
   const int c = a.work[2 * cg + 1];
@@ -141,9 +157,13 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   const int t_lo = max(ws, lo);
   const int t_hi = min(ws + wlen, hi);
 
-  const int hl = hb * 16 + n;
+  // Column n: query head hl of KV head kvl (with NH = 2 columns [G, 2 G)
+  // belong to kvh + 1; columns past the heads are dead and carry a zero query).
+  const int hs = (NH == 2 && n >= a.G) ? 1 : 0;
+  const int hl = NH == 2 ? n - hs * a.G : hb * 16 + n;
   const bool hvalid = hl < a.G;
-  const int h = kvh * a.G + (hvalid ? hl : 0);
+  const int kvl = kvh + hs;
+  const int h = kvl * a.G + (hvalid ? hl : 0);
 
   // Query of head n at d = KB g + i (i < KB) -- the same permutation of d as
   // the key codes -- times the per-channel key scale (key per channel).  qc:
@@ -157,8 +177,8 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   float kcs[KPT ? 1 : KB], kco[KPT ? 1 : KB];
   if constexpr (!KPT) {
     const int64_t cnt = a.kq_scalar ? 1 : (int64_t)a.KVn * D;
-    chan_run(a.kq_scale, a.kq_f32, a.kq_scalar, cnt, kvh * D + KB * g, kcs);
-    chan_run(a.kq_off, a.kq_f32, a.kq_scalar, cnt, kvh * D + KB * g, kco);
+    chan_run(a.kq_scale, a.kq_f32, a.kq_scalar, cnt, kvl * D + KB * g, kcs);
+    chan_run(a.kq_off, a.kq_f32, a.kq_scalar, cnt, kvl * D + KB * g, kco);
   }
 #pragma unroll
   for (int cc = 0; cc < NC; ++cc) {
@@ -249,11 +269,12 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   const float* vop = VPT && a.vq_off ? (const float*)a.vq_off + (int64_t)b * a.vq_sb : nullptr;
 
   // Per-wave staging inside the combine buffer (used after the loop): one
-  // iteration's 64 key rows (row-major, 16-byte pieces XOR-swizzled so that
-  // the 16 rows one operand read touches fall in distinct bank groups) and
-  // its per-token tables (64 keys each).  All loads of an iteration -- keys,
-  // values and tables of two 32-key steps -- go out before its first wait.
-  constexpr int PR = D / 16;                 // 16-byte pieces per key row
+  // iteration's key rows (64 rows of D bytes, or 32 rows of the two heads'
+  // 2 D bytes; row-major, 16-byte pieces XOR-swizzled so that the 16 rows
+  // one operand read touches fall in distinct bank groups) and its
+  // per-token tables (64 keys each).  All loads of an iteration -- keys,
+  // values and tables of its 32-key steps -- go out before its first wait.
+  constexpr int PR = RB / 16;                // 16-byte pieces per staged row
   constexpr int RPI = 64 / PR;               // rows per 64-lane buffer-to-LDS load
   constexpr int STAGE = 64 * D + 1024;       // bytes of one wave's stage
   constexpr int COMBINE = 4 * 16 * (D + 4) * 4;
@@ -270,15 +291,18 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
     const int r = RPI * inst + lane / PR;
     k_lds_off[inst] = (uint32_t)((r % 16) * a.k_ss + 16 * ((lane % PR) ^ key_swz<PR>(r)));
   }
-  // Score operand reads: lane (n, g) reads piece (KB / 16) g + c4 of row
-  // 16 hf + n of a step.
-  uint32_t k_rd[2][KB / 16];
+  // Score operand reads: lane (n, g) reads piece (D / 16) x + (KB / 16) g + c4
+  // of row 16 hf + n of a step (head x of the row).
+  uint32_t k_rd[NH][2][KB / 16];
 #pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
+  for (int x = 0; x < NH; ++x) {
 #pragma unroll
-    for (int c4 = 0; c4 < KB / 16; ++c4) {
-      const int r = 16 * hf + n;
-      k_rd[hf][c4] = (uint32_t)(r * D + 16 * (((KB / 16) * g + c4) ^ key_swz<PR>(r)));
+    for (int hf = 0; hf < 2; ++hf) {
+#pragma unroll
+      for (int c4 = 0; c4 < KB / 16; ++c4) {
+        const int r = 16 * hf + n;
+        k_rd[x][hf][c4] = (uint32_t)(r * RB + 16 * (((D / 16) * x + (KB / 16) * g + c4) ^ key_swz<PR>(r)));
+      }
     }
   }
   // Per-token table rows of the batch (no table: empty range, reads zero).
@@ -291,12 +315,12 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   if (t_hi > t_lo) {
     const int first = ws + ((t_lo - ws) & ~31);
     const WavePages wp = wave_pages(a, b, first, hi - 1, lane);
-    for (int ti = first; ti < t_hi; ti += 2 * kDecodeStep) {
-      // The four 16-key quarters each lie inside one page (block sizes are
+    for (int ti = first; ti < t_hi; ti += NSUB * kDecodeStep) {
+      // The 16-key quarters each lie inside one page (block sizes are
       // multiples of 32); rows at or past `hi` read as zero.
-      __amdgpu_buffer_rsrc_t rk[4], rv[4];
+      __amdgpu_buffer_rsrc_t rk[2 * NSUB], rv[2 * NSUB];
 #pragma unroll
-      for (int qq = 0; qq < 4; ++qq) {
+      for (int qq = 0; qq < 2 * NSUB; ++qq) {
         const int jb = ti + 16 * qq;
         const int nv = min(16, hi - jb);
         int64_t ko = 0, vo = 0;
@@ -304,38 +328,42 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
         if (nv > 0) {
           ko = kv_row_offset_w(a, wp, a.k_sb, a.k_ss, a.k_sh, b, jb, kvh, kv_off);
           vo = kv_row_offset_w(a, wp, a.v_sb, a.v_ss, a.v_sh, b, jb, kvh, kv_off);
-          kbytes = (uint32_t)((nv - 1) * a.k_ss + D);
-          vbytes = (uint32_t)((nv - 1) * a.v_ss + D);
+          kbytes = (uint32_t)((nv - 1) * a.k_ss + RB);
+          vbytes = (uint32_t)((nv - 1) * a.v_ss + RB);
         }
         rk[qq] = make_rsrc(kbase + ko, kbytes);
         rv[qq] = make_rsrc(vbase + vo, vbytes);
       }
-      // Key codes of both steps, whole rows, into this wave's stage (the
-      // previous iteration's reads of it were consumed by its products).
+      // Key codes of the iteration's steps, whole rows, into this wave's
+      // stage (the previous iteration's reads of it were consumed by its
+      // products).
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
         for (int inst = 0; inst < PR / 2; ++inst) {
-          buf_ld16_lds_nt(rk[2 * sub + (RPI * inst) / 16], kst + 32 * D * sub + 1024 * inst,
+          buf_ld16_lds_nt(rk[2 * sub + (RPI * inst) / 16], kst + 32 * RB * sub + 1024 * inst,
                           k_lds_off[inst]);
         }
       }
-      // Value codes for step sub, k-slot s: key 32 sub + 16 (s / 4) + 4 g +
-      // s % 4, columns DPL n ..
-      uint32_t vr[2][8][DPL / 4];
+      // Value codes for step sub, head x, k-slot s: key 32 sub + 16 (s / 4) +
+      // 4 g + s % 4, columns DPL n ..
+      uint32_t vr[NSUB][NH][8][DPL / 4];
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < NSUB; ++sub) {
 #pragma unroll
-        for (int s = 0; s < 8; ++s) {
-          const int qq = 2 * sub + (s >> 2);
-          const int t = 4 * g + (s & 3);
-          const uint32_t off = (uint32_t)(t * a.v_ss + DPL * n);
-          if constexpr (DPL == 8) {
-            const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[qq], off, 0, 2));
-            vr[sub][s][0] = w.x;
-            vr[sub][s][1] = w.y;
-          } else {
-            vr[sub][s][0] = __builtin_amdgcn_raw_buffer_load_b32(rv[qq], off, 0, 2);
+        for (int x = 0; x < NH; ++x) {
+#pragma unroll
+          for (int s = 0; s < 8; ++s) {
+            const int qq = 2 * sub + (s >> 2);
+            const int t = 4 * g + (s & 3);
+            const uint32_t off = (uint32_t)(t * a.v_ss + x * D + DPL * n);
+            if constexpr (DPL == 8) {
+              const u32x2 w = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rv[qq], off, 0, 2));
+              vr[sub][x][s][0] = w.x;
+              vr[sub][x][s][1] = w.y;
+            } else {
+              vr[sub][x][s][0] = __builtin_amdgcn_raw_buffer_load_b32(rv[qq], off, 0, 2);
+            }
           }
         }
       }
@@ -358,16 +386,14 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
       __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
 
 #pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
+      for (int sub = 0; sub < NSUB; ++sub) {
         const int ts = ti + 32 * sub;
         if (ts >= t_hi) break;
-        const uint8_t* ks_rows = kst + 32 * D * sub;
-        u32x4 kw[2][KB / 16];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-#pragma unroll
-          for (int c4 = 0; c4 < KB / 16; ++c4) kw[hf][c4] = *reinterpret_cast<const u32x4*>(ks_rows + k_rd[hf][c4]);
-        }
+        const uint8_t* ks_rows = kst + 32 * RB * sub;
+        // Key operand pieces of head x, half hf (read where they are used).
+        auto kwr = [&](int x, int hf, int c4) FIA_INLINE {
+          return *reinterpret_cast<const u32x4*>(ks_rows + k_rd[x][hf][c4]);
+        };
         // Tables of the lane's keys 16 hf + 4 g + r of this step.
         f32x4 ks[2], kq[2], vs[2], vq[2];
 #pragma unroll
@@ -384,32 +410,47 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
           }
         }
 
-        // Scores S^T[key 16 hf + 4 g + r][head n].
+        // Scores S^T[key 16 hf + 4 g + r][column n]: one product per head of
+        // the row against every column's query; a column keeps its own
+        // head's.
         f32x4 sc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           if constexpr (FP8) {
-            sc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 sx[NH];
 #pragma unroll
-            for (int cc = 0; cc < NC; ++cc) {
-              // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
-              const uint32_t w0 = kw[hf][cc >> 1][2 * (cc & 1)];
-              const uint32_t w1 = kw[hf][cc >> 1][2 * (cc & 1) + 1];
-              const u32x4 kop8 = codes8_bf16<true>(w0, w1);
-              sc[hf] = mfma16(kop8, qh[cc], sc[hf]);
-              if constexpr (!KPT) sc[hf] = mfma16(kop8, ql[cc], sc[hf]);
+            for (int x = 0; x < NH; ++x) {
+              sx[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int cc = 0; cc < NC; ++cc) {
+                // bytes 8 cc .. 8 cc + 7 of the lane's KB key bytes
+                const u32x4 kp = kwr(x, hf, cc >> 1);
+                const uint32_t w0 = kp[2 * (cc & 1)];
+                const uint32_t w1 = kp[2 * (cc & 1) + 1];
+                const u32x4 kop8 = codes8_bf16<true>(w0, w1);
+                sx[x] = mfma16(kop8, qh[cc], sx[x]);
+                if constexpr (!KPT) sx[x] = mfma16(kop8, ql[cc], sx[x]);
+              }
             }
+            sc[hf] = (NH == 2 && hs) ? sx[NH - 1] : sx[0];
           } else {
             // 16 key bytes per lane and product: the loaded pieces as they are.
-            i32x4 ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
+            i32x4 ah[NH], al[NH];
 #pragma unroll
-            for (int c4 = 0; c4 < KB / 16; ++c4) {
-              const i32x4 kc = __builtin_bit_cast(i32x4, kw[hf][c4]);
-              ah = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qi[c4]), ah, 0, 0, 0);
-              al = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qj[c4]), al, 0, 0, 0);
+            for (int x = 0; x < NH; ++x) {
+              ah[x] = i32x4{0, 0, 0, 0};
+              al[x] = i32x4{0, 0, 0, 0};
+#pragma unroll
+              for (int c4 = 0; c4 < KB / 16; ++c4) {
+                const i32x4 kc = __builtin_bit_cast(i32x4, kwr(x, hf, c4));
+                ah[x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qi[c4]), ah[x], 0, 0, 0);
+                al[x] = __builtin_amdgcn_mfma_i32_16x16x64_i8(kc, __builtin_bit_cast(i32x4, qj[c4]), al[x], 0, 0, 0);
+              }
             }
+            const i32x4 ahs = (NH == 2 && hs) ? ah[NH - 1] : ah[0];
+            const i32x4 als = (NH == 2 && hs) ? al[NH - 1] : al[0];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) sc[hf][r] = sq * __builtin_fmaf((float)al[r], 1.f / 256.f, (float)ah[r]);
+            for (int r = 0; r < 4; ++r) sc[hf][r] = sq * __builtin_fmaf((float)als[r], 1.f / 256.f, (float)ahs[r]);
           }
         }
         float x[8];
@@ -461,14 +502,20 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
         t_run += tsum;
         const u32x4 pb = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]), pack_bf16x2(p[4], p[5]),
                           pack_bf16x2(p[6], p[7])};
+        // Head x's values against the probabilities of its own columns only
+        // (the other head's columns enter as zero), into the shared output.
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) {
-          // byte e of the lane's DPL value bytes of each of the 8 keys
-          const int w = e >> 2, k = e & 3;
-          const uint32_t(&v8)[8][DPL / 4] = vr[sub];
-          const u32x4 av = {pair_bf16<FP8>(v8[0][w], v8[1][w], k), pair_bf16<FP8>(v8[2][w], v8[3][w], k),
-                            pair_bf16<FP8>(v8[4][w], v8[5][w], k), pair_bf16<FP8>(v8[6][w], v8[7][w], k)};
-          o[e] = mfma16(av, pb, o[e]);
+        for (int x = 0; x < NH; ++x) {
+          const u32x4 pbx = (NH == 1 || hs == x) ? pb : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) {
+            // byte e of the lane's DPL value bytes of each of the 8 keys
+            const int w = e >> 2, k = e & 3;
+            const uint32_t(&v8)[8][DPL / 4] = vr[sub][x];
+            const u32x4 av = {pair_bf16<FP8>(v8[0][w], v8[1][w], k), pair_bf16<FP8>(v8[2][w], v8[3][w], k),
+                              pair_bf16<FP8>(v8[4][w], v8[5][w], k), pair_bf16<FP8>(v8[6][w], v8[7][w], k)};
+            o[e] = mfma16(av, pbx, o[e]);
+          }
         }
       }
     }
@@ -497,8 +544,17 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   constexpr int PER = 16 * D / 256;  // outputs per thread
   const int hh = threadIdx.x / (D / PER);
   const int d0 = (threadIdx.x % (D / PER)) * PER;
-  if (hb * 16 + hh >= a.G) return;
-  const int hout = kvh * a.G + hb * 16 + hh;
+  int hout, kvo;
+  if constexpr (NH == 1) {
+    if (hb * 16 + hh >= a.G) return;
+    hout = kvh * a.G + hb * 16 + hh;
+    kvo = kvh;
+  } else {
+    if (hh >= 2 * a.G) return;
+    const int hso = hh >= a.G ? 1 : 0;
+    kvo = kvh + hso;
+    hout = kvo * a.G + hh - hso * a.G;
+  }
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < 4; ++w) M = fmaxf(M, sm_m[w][hh]);
@@ -519,8 +575,8 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   float vcs[VPT ? 1 : PER], vco[VPT ? 1 : PER];
   if constexpr (!VPT) {
     const int64_t cnt = a.vq_scalar ? 1 : (int64_t)a.KVn * D;
-    chan_run(a.vq_scale, a.vq_f32, a.vq_scalar, cnt, kvh * D + d0, vcs);
-    chan_run(a.vq_off, a.vq_f32, a.vq_scalar, cnt, kvh * D + d0, vco);
+    chan_run(a.vq_scale, a.vq_f32, a.vq_scalar, cnt, kvo * D + d0, vcs);
+    chan_run(a.vq_off, a.vq_f32, a.vq_scalar, cnt, kvo * D + d0, vco);
   }
 #pragma unroll
   for (int u = 0; u < PER; ++u) {
@@ -553,26 +609,29 @@ __global__ __launch_bounds__(256, (KPT || VPT || FP8) ? 3 : 4) void decode_split
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int NH>
 static void launch_q8_modes(const AttnArgs& a, int32_t n_items, hipStream_t s) {
   if (a.kq_mode == 1) {
-    decode_split_q8<D, FP8, true, true><<<n_items, 256, 0, s>>>(a);
+    decode_split_q8<D, FP8, true, true, NH><<<n_items, 256, 0, s>>>(a);
   } else if (a.vq_mode == 1) {
-    decode_split_q8<D, FP8, false, true><<<n_items, 256, 0, s>>>(a);
+    decode_split_q8<D, FP8, false, true, NH><<<n_items, 256, 0, s>>>(a);
   } else {
-    decode_split_q8<D, FP8, false, false><<<n_items, 256, 0, s>>>(a);
+    decode_split_q8<D, FP8, false, false, NH><<<n_items, 256, 0, s>>>(a);
   }
 }
 
 hipError_t launch_decode_q8(const AttnArgs& a, int32_t n_items, hipStream_t s) {
   if (n_items > 0) {
     const bool fp8 = a.kvq == 2;
-    if (a.D == 128) {
-      if (fp8) launch_q8_modes<128, true>(a, n_items, s);
-      else launch_q8_modes<128, false>(a, n_items, s);
+    if (a.D == 128 && a.kv_pair) {
+      if (fp8) launch_q8_modes<128, true, 2>(a, n_items, s);
+      else launch_q8_modes<128, false, 2>(a, n_items, s);
+    } else if (a.D == 128) {
+      if (fp8) launch_q8_modes<128, true, 1>(a, n_items, s);
+      else launch_q8_modes<128, false, 1>(a, n_items, s);
     } else {
-      if (fp8) launch_q8_modes<64, true>(a, n_items, s);
-      else launch_q8_modes<64, false>(a, n_items, s);
+      if (fp8) launch_q8_modes<64, true, 1>(a, n_items, s);
+      else launch_q8_modes<64, false, 1>(a, n_items, s);
     }
   }
   return hipGetLastError();

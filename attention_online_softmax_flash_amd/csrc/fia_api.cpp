@@ -248,6 +248,16 @@ fia_status lengths_from(const int64_t* arr, int64_t len, int64_t B, int64_t def,
   return FIA_SUCCESS;
 }
 
+// Heads per decode work item: blocks of 16 query heads of one KV head, or
+// (fake-quantised codes, D = 128, G <= 8, KV_N even, the heads of a token
+// adjacent in both caches) two KV heads per wave, whose codes then form one
+// 2 D-byte run per token.
+void set_head_split(AttnArgs& a, int64_t KVn) {
+  a.kv_pair = (a.kvq != 0 && a.D == 128 && a.G <= 8 && KVn % 2 == 0 && a.k_sh == a.D &&
+               a.v_sh == a.D) ? 1 : 0;
+  a.n_head_blocks = a.kv_pair ? 1 : (a.G + 15) / 16;
+}
+
 void visible(int mode, int64_t i, int64_t Lq, int64_t Lk, int64_t pre, int64_t next, int64_t* lo,
              int64_t* hi) {
   const int64_t d = Lk - Lq;
@@ -1010,8 +1020,8 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
     const int64_t per_b = (len_bound + chunk - 1) / chunk + (mode == 4 ? 1 : 0);
     const int64_t total_max = B * per_b;
     a.chunk = (int32_t)chunk;
-    a.n_head_blocks = (a.G + 15) / 16;
-    const int64_t n_items = total_max * KVn * a.n_head_blocks;
+    set_head_split(a, KVn);
+    const int64_t n_items = total_max * (a.kv_pair ? KVn / 2 : KVn) * a.n_head_blocks;
     if (n_items > INT32_MAX) {
       delete e;
       return fail(FIA_ERR_UNSUPPORTED, "too many decode work items");
@@ -1051,8 +1061,8 @@ fia_status fia_get_workspace_size(const fia_params* p, const fia_tensor* query,
       }
     }
     a.chunk = (int32_t)chunk;
-    a.n_head_blocks = (a.G + 15) / 16;
-    const int64_t n_items = total_chunks * KVn * a.n_head_blocks;
+    set_head_split(a, KVn);
+    const int64_t n_items = total_chunks * (a.kv_pair ? KVn / 2 : KVn) * a.n_head_blocks;
     if (n_items > INT32_MAX) {
       delete e;
       return fail(FIA_ERR_UNSUPPORTED, "too many decode work items");

@@ -98,7 +98,11 @@ struct AttnArgs {
   int32_t write_lse;
   // decode split-KV
   int32_t chunk;                    // tokens per chunk (multiple of 128)
-  int32_t n_head_blocks;            // ceil(G / 16)
+  int32_t n_head_blocks;            // ceil(G / 16); 1 with kv_pair
+  // Fake-quantised decode: two adjacent KV heads per wave (heads of a token
+  // adjacent in memory, G <= 8, KV_N even, D = 128); work items then run
+  // over KV head pairs.
+  int32_t kv_pair;
   float* part_o;                    // [total_chunks * Qn * D]
   float* part_lse;                  // [total_chunks * Qn]
   // Decode with KV lengths on the device: dev_kvlen int32 [B] is read by

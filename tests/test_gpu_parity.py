@@ -377,6 +377,17 @@ FAKE_QUANT_CASES = [
     ("i8_tensor", "int8", 0, 0, True, True,
      lambda: W.dense_case("fq5", 855, B=2, S1=1, S2=640, Q_N=4, KV_N=4, D=128, kv_lens=[640, 7],
                           lse=True, poison_pad=True)),
+    # two KV heads per wave (adjacent heads, G <= 8): every column used (G = 8),
+    # an odd group size with KV_N = 6, a dense BSND cache with mixed modes
+    ("i8_token_pair_g8", "int8", 1, 1, True, False,
+     lambda: W.paged_decode_case("fq6", 856, B=3, Q_N=64, KV_N=8, D=128, kv_lens=[1, 1500, 3000],
+                                 block_size=64, lse=True, poison_tail=True, extra_blocks=1)),
+    ("fp8_chan_pair_g3", "fp8", 0, 0, False, False,
+     lambda: W.paged_decode_case("fq7", 857, B=2, Q_N=18, KV_N=6, D=128, kv_lens=[2100, 33],
+                                 block_size=128, lse=True, poison_tail=True)),
+    ("i8_mixed_pair_dense", "int8", 0, 1, True, False,
+     lambda: W.dense_case("fq8", 858, B=2, S1=1, S2=1100, Q_N=16, KV_N=4, D=128,
+                          kv_lens=[1100, 260], lse=True, poison_pad=True)),
 ]
 
 
