@@ -5,9 +5,10 @@
 // ([KV_N, D], or one value for the whole tensor) or per token ([B, S2],
 // shared by the KV heads).
 //
-// Same work split, chunking, wave combine and partial format as the bf16
-// split-KV kernel, so the bf16 merge kernel folds the partials.  The scales
-// and offsets are moved out of the MFMA operands:
+// Same chunking, wave combine and partial format as the bf16 split-KV
+// kernel, so the bf16 merge kernel folds the partials; work items run over
+// KV heads, or over pairs of adjacent KV heads (one wave takes both: NH = 2).
+// The scales and offsets are moved out of the MFMA operands:
 //   * key, per channel:  s_j = sum_d (q_d ks_d) c_jd + sum_d q_d ks_d ko_d.  The
 //     first term is a product of the raw codes against q * ks carried with
 //     about 16 bits: int8 codes go into the int8 MFMA as loaded, against
