@@ -429,6 +429,38 @@ def test_decode_fake_quant_every_code_is_exact(kind):
     np.testing.assert_allclose(lse[:, 0, 0], 0.5 * want, rtol=2e-6, atol=1e-9)
 
 
+@pytest.mark.parametrize("kind", ["int8", "fp8"])
+def test_decode_fake_quant_every_code_two_heads_per_wave(kind):
+    """The every-code check through the kernel that takes two adjacent KV
+    heads per wave (dense BSND, KV_N = 2, G = 1): head 0 carries each code,
+    head 1 the codes in reverse order, so both heads' key and value
+    conversions and their output columns are checked bit-exactly."""
+    codes = np.arange(256)
+    if kind == "fp8":
+        codes = codes[(codes & 0x7F) != 0x7F]
+    rev = codes[::-1].copy()
+    B, D = codes.size, 128
+    case = W.dense_case("fqx2", 882, B=B, S1=1, S2=4, Q_N=2, KV_N=2, D=D, kv_lens=[1] * B, lse=True,
+                        scale=0.5)
+    q = np.zeros_like(case.q)
+    q[..., 0] = W.f32_to_bf16_bits(np.ones(1, np.float32))[0]
+    case = W.with_kv_quant(dataclasses.replace(case, q=q), 883, kind=kind, kmode=0, vmode=0)
+    dt = np.int8 if kind == "int8" else np.uint8
+    k = np.zeros(case.k.shape, dtype=dt)
+    v = np.zeros(case.v.shape, dtype=dt)
+    for h, cs in ((0, codes), (1, rev)):
+        k[:, 0, h, 0] = cs.astype(np.uint8).view(dt)
+        v[:, 0, h, :] = cs.astype(np.uint8).view(dt)[:, None]
+    one = W.f32_to_bf16_bits(np.ones((2, D), np.float32))
+    case = dataclasses.replace(case, k=k, v=v, kv_quant=dict(case.kv_quant, kscale=one, vscale=one))
+    plan = run_plan(TI.dense_plan(case, DEV))
+    out, lse = gpu_results(plan)
+    for h, cs in ((0, codes), (1, rev)):
+        want = O.decode_codes(cs.astype(np.uint8).view(dt), kind)
+        np.testing.assert_array_equal(out[:, 0, h, :], np.repeat(want[:, None], D, axis=1))
+        np.testing.assert_allclose(lse[:, h, 0], 0.5 * want, rtol=2e-6, atol=1e-9)
+
+
 def test_decode_fake_quant_tnd():
     case = W.tnd_case("fqt", 870, q_lens=[1, 1, 0, 1], kv_lens=[600, 5, 100, 1029], Q_N=8, KV_N=2,
                       D=128, lse=True)
