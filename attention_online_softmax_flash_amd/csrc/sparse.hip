@@ -42,8 +42,11 @@ namespace fia {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int X_PITCH = kSparseD * 2 + 16;          // bytes per row-major row in LDS
-constexpr int X_BYTES = kSparseSub * X_PITCH;        // 66560
+// Bytes per row-major row in LDS: consecutive rows start 32 bytes (8 banks)
+// apart, so the 4 rows x 32 bytes one 16-lane group of transposed value
+// reads touches fall in distinct banks.
+constexpr int X_PITCH = kSparseD * 2 + 32;
+constexpr int X_BYTES = kSparseSub * X_PITCH;        // 67584
 constexpr int RP_BYTES = 2 * kSparseSub * 8;         // row addresses, two sub-chunks
 constexpr int BT_BYTES = 2 * kSparseBtCache * 4;     // ori / cmp block-table rows
 constexpr int IX_BYTES = kSparseMaxSub * kSparseSub * 4;
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
   extern __shared__ __align__(16) uint8_t lds[];
   uint8_t* xs = lds;                                                   // [64][X_PITCH]
   u32x4* ps = reinterpret_cast<u32x4*>(lds + SL::OFF_P);                   // [HQ][4][64]
-  float* sx = reinterpret_cast<float*>(lds + SL::OFF_SX);                  // [DS - 1][2][HQ][64][16]
+  float* sx = reinterpret_cast<float*>(lds + SL::OFF_SX);                  // [DS - 1][2][HQ][4][64][4]
   const uint8_t** rowp = reinterpret_cast<const uint8_t**>(lds + SL::OFF_RP);   // [2][64]
   int32_t* bt_o = reinterpret_cast<int32_t*>(lds + SL::OFF_BT);            // [kSparseBtCache]
   int32_t* bt_c = bt_o + kSparseBtCache;                               // [kSparseBtCache]
@@ -472,13 +475,15 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
       const u32x4 bv = *reinterpret_cast<const u32x4*>(qs + (32 * hq + n) * X_PITCH + off);
       s = mfma32h<F16>(av, bv, s);
     }
-    auto part = [&](int k) FIA_INLINE {   // partial of d range k >= 1, this (sb, hq, lane)
-      return sx + ((((k - 1) * 2 + sb) * HQ + hq) * 64 + lane) * 16;
+    // Element q of the partial of d range k >= 1, this (sb, hq, lane): four
+    // floats per lane and quarter, lanes adjacent (16-byte stores, no bank
+    // conflicts).
+    auto part = [&](int k, int q) FIA_INLINE -> float& {
+      return sx[(((((k - 1) * 2 + sb) * HQ + hq) * 4 + (q >> 2)) * 64 + lane) * 4 + (q & 3)];
     };
     if (ds > 0) {
-      float* sxw = part(ds);
 #pragma unroll
-      for (int q = 0; q < 16; ++q) sxw[q] = s[q];
+      for (int q = 0; q < 16; ++q) part(ds, q) = s[q];
     }
     __syncthreads();
     if (ds == 0) {
@@ -488,9 +493,9 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
         const int slot = 32 * sb + 8 * (q >> 2) + 4 * hh + (q & 3);
         float sum;
         if constexpr (DS == 2) {
-          sum = s[q] + part(1)[q];
+          sum = s[q] + part(1, q);
         } else {
-          sum = (s[q] + part(1)[q]) + (part(2)[q] + part(3)[q]);
+          sum = (s[q] + part(1, q)) + (part(2, q) + part(3, q));
         }
         const float x = sum * a.scale_log2;
         s[q] = ((live >> slot) & 1u) ? x : kNegInf;
