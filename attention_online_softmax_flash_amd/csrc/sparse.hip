@@ -577,15 +577,19 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
     }
     return;
   }
-  // Partial of chunk `chunk`: part_o[row][chunk][d][head] (heads innermost,
-  // so each store writes whole runs of 32 heads), part_lse[row][chunk][head].
+  // Partial of chunk `chunk`: part_o[row][chunk][d / 4][head][d % 4] (four
+  // consecutive d values of a head per 16-byte store, heads adjacent, so a
+  // store writes whole runs of 32 heads), part_lse[row][chunk][head].
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
   const int64_t rc = (int64_t)r * a.n_chunks + chunk;
-  float* pp = a.part_o + (rc * kSparseD + DVW * dv + 4 * hh) * a.N1 + head;
+  f32x4* pp = reinterpret_cast<f32x4*>(a.part_o) + (rc * (kSparseD / 4) + (DVW * dv) / 4 + hh) * a.N1 + head;
 #pragma unroll
   for (int mb = 0; mb < NOB; ++mb) {
 #pragma unroll
-    for (int q = 0; q < 16; ++q) pp[(int64_t)(32 * mb + 8 * (q >> 2) + (q & 3)) * a.N1] = o[mb][q] * inv;
+    for (int q4 = 0; q4 < 4; ++q4) {
+      pp[(int64_t)(8 * mb + 2 * q4) * a.N1] = f32x4{o[mb][4 * q4] * inv, o[mb][4 * q4 + 1] * inv,
+                                                    o[mb][4 * q4 + 2] * inv, o[mb][4 * q4 + 3] * inv};
+    }
   }
   if (dv == 0 && hh == 0) a.part_lse[rc * a.N1 + head] = l_run > 0.f ? m_run + fast_log2(l_run) : kNegInf;
 }
@@ -598,7 +602,7 @@ __global__ __launch_bounds__(kThreads, 1) void sparse_attn(SparseArgs a) {
 // clamped to the last chunk, so the loads are unconditional), and the group
 // is folded into the running sum with the usual rescale by the new maximum;
 // the sink's term joins at the end.
-constexpr int kMergeD = 4;   // d values per thread
+constexpr int kMergeD = 4;   // d values per thread (one 16-byte partial load)
 constexpr int kMergeHeads = 64;   // heads per merge workgroup (one per lane)
 template <bool F16>
 __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
@@ -612,9 +616,9 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
   if (h >= a.N1) return;
   const int nc = a.n_chunks;
   const int64_t rc0 = (int64_t)r * nc;
-  const float* base = a.part_o + (rc0 * kSparseD + d0) * a.N1 + h;
+  const f32x4* base = reinterpret_cast<const f32x4*>(a.part_o) + (rc0 * (kSparseD / 4) + d0 / 4) * a.N1 + h;
   const float* lp = a.part_lse + rc0 * a.N1 + h;
-  const int64_t cstride = (int64_t)kSparseD * a.N1;
+  const int64_t cstride = (int64_t)(kSparseD / 4) * a.N1;   // in 4-float units
   // The sink logit (a buffer load, zero without sinks: no branch, so the
   // load stays in flight through the fold that follows).
   const bool sink_on = a.sinks != nullptr && qr.live;
@@ -633,8 +637,9 @@ __global__ __launch_bounds__(256) void sparse_merge(SparseArgs a) {
     for (int i = 0; i < G; ++i) {
       const int64_t c = min(c0 + i, nc - 1);
       lv[i] = lp[c * a.N1];
+      const f32x4 v4 = base[c * cstride];
 #pragma unroll
-      for (int u = 0; u < kMergeD; ++u) x[i][u] = base[c * cstride + (int64_t)u * a.N1];
+      for (int u = 0; u < kMergeD; ++u) x[i][u] = v4[u];
     }
     // Branch-free from here (a branch would let the compiler sink the
     // partial loads past the wait for the log-sum-exps).
