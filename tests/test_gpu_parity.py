@@ -582,6 +582,21 @@ def test_sparse_sweep(i):
     check_out(to_f64(plan.out), O.sparse_sharedkv(case))
 
 
+def test_sparse_non_power_of_two_scales():
+    """Tile scales that are not powers of two (a random mix with powers of
+    two, so both conversions run within one wave: the exact fp32 product for
+    the former, the exponent-only hardware conversion for the latter)."""
+    case = W.sparse_case("spnp2", 430, B=3, N1=64, seqused_kv=[2000, 300, 4100], K2=512,
+                         block_size1=64, block_size2=32, materialise_all_ori=False)
+    rng = np.random.default_rng(431)
+    for pool in (case.ori_kv, case.cmp_kv):
+        sc = np.ascontiguousarray(pool[..., 576:604]).view(np.float32)
+        mult = rng.choice(np.array([1.0, 1.5, 0.75, 1.2345], np.float32), size=sc.shape)
+        pool[..., 576:604] = (sc * mult).view(np.uint8)
+    plan = run_plan(TI.sparse_plan(case, DEV))
+    check_out(to_f64(plan.out), O.sparse_sharedkv(case))
+
+
 def test_sparse_window_only():
     case = W.sparse_case("swa", 410, B=2, N1=64, seqused_kv=[300, 50], K2=512,
                          materialise_all_ori=False)
